@@ -1,0 +1,374 @@
+"""fp64 CPU oracle of the HySparse hybrid-block attention path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU
+baseline leg of the benchmark may import this module.  It shares no code with
+the HIP path (it imports numpy and nothing from the product package); inputs
+arrive as float64 arrays holding the exact stored values (fp8 codes are
+decoded here, by `decode_e4m3fn`).
+
+Every function is the plain definition from the pages, in float64, computed
+row by row (a query row only needs keys up to its own position), so sampled
+rows of a full-size workload cost seconds.  Nothing is blocked, fused or
+reordered beyond what the definitions state.
+
+Sources (cited by page title and section):
+  [X]  "HySparse: A Hybrid Sparse Attention Architecture with Oracle Token
+       Selection and KV Cache Sharing" -- explainer page (paper-graph-ui),
+       sections 3.4.1-3.4.3.
+  [P]  The same paper's own text (paperpeel page), sections 3.1-3.3.
+  [H2] HySparse2 explainer page (deep-reads), "Precise retrieval without a
+       separate indexer" and the decode_one_token pseudocode.
+
+Readings where the pages leave a step open (each one also listed in the
+design notes):
+  R1  The block score is the post-softmax maximum (eq. S_t^i of [X] 3.4.1);
+      the printed rescale of [X] "Modified FlashAttention Kernel" is read as
+      exp(S - m)/l, i.e. exp(raw - LSE), which is the only form that makes the
+      stored value equal eq. S_t^i.  An alternative block log-sum-exp score
+      (block probability mass) is offered as score='lse'.
+  R2  Candidate blocks: by default only fully-past blocks j < floor(t/B);
+      include_diag=True adds the (causally clipped) diagonal block, which is
+      the literal reading of B_i = {(i-1)B+1 .. min(iB, t)}.
+  R3  Fewer candidates than k: all are selected, the rest is padded with -1;
+      an empty selection gives a zero sparse-branch output.
+  R4  Ties: order by score descending, then block index ascending; the index
+      list is emitted in ascending order.
+  R5  Gates are per (token, head) logits; gates=None means both gates are 1.
+  R6  The window holds the min(t+1, W) keys [t-W+1, t], the query's own
+      position included.
+  R7  Query head h belongs to kv group floor(h / G) (contiguous grouping).
+  R8  Decode: the new token is already in the cache, so the query sits at
+      position L-1 of an L-token context.  The window ring keeps position p in
+      slot p mod W.
+  R9  Token-level selection ([H2]): block size 1, candidates are the tokens
+      older than the newest n_recent, which are always added and do not use
+      the k budget; no window branch and no gate.  The group score is the
+      same group-wise maximum of post-softmax weights.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 64
+
+
+# ----------------------------------------------------------------- helpers
+def softmax_scale(d: int) -> float:
+    """tau = 1/sqrt(d) ([X] 3.4.1, "Standard Attention Formulation")."""
+    return 1.0 / np.sqrt(d)
+
+
+def _attend(logits: np.ndarray, values: np.ndarray):
+    """Softmax over the last axis of `logits` ([..., n]) applied to values [n, d].
+
+    Returns (o [..., d], lse [...]).  An empty key set (n == 0, or every logit
+    -inf) gives o = 0 and lse = -inf (reading R3).
+    """
+    lead = logits.shape[:-1]
+    d = values.shape[-1]
+    if logits.shape[-1] == 0:
+        return np.zeros((*lead, d)), np.full(lead, -np.inf)
+    m = logits.max(axis=-1, keepdims=True)
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    e = np.exp(logits - m_safe)
+    l = e.sum(axis=-1, keepdims=True)
+    l_safe = np.where(l > 0, l, 1.0)
+    o = (e @ values) / l_safe
+    lse = np.where(finite & (l > 0), m_safe + np.log(l_safe), -np.inf)[..., 0]
+    o = np.where(finite & (l > 0), o, 0.0)
+    return o, lse
+
+
+def group_of(h: int, G: int) -> int:
+    """Reading R7: query head h uses kv head floor(h/G)."""
+    return h // G
+
+
+# ------------------------------------------------------- full attention layer
+def full_attention_rows(q_rows: np.ndarray, pos: np.ndarray, k: np.ndarray,
+                        v: np.ndarray, scale: float | None = None,
+                        block: int = BLOCK, score: str = "max"):
+    """Causal GQA attention of the full layer plus its block scores, for a set of rows.
+
+    q_rows [R, Hq, d]: the queries at positions `pos` [R]; k, v [Hkv, >=max(pos)+1, d].
+    o_t = sum_{i<=t} softmax_i(tau q_t.k_i) v_i   ([X] 3.4.1 eq. o_t; [P] 3.2)
+    LSE_t = log sum_{i<=t} exp(tau q_t.k_i)
+    raw[h, r, j] = max_{i in B_j, i<=t} tau q.k_i  (score='max'), i.e. the
+        pre-softmax block maximum that the modified FlashAttention pass stores
+        ([X] "Modified FlashAttention Kernel", first pass), or the block
+        log-sum-exp (score='lse').  Only j <= t//block is defined; later
+        entries are NaN.
+    Returns o [R, Hq, d], lse [Hq, R], raw [Hq, R, nblk] with nblk = ceil((max(pos)+1)/block).
+    """
+    R, Hq, d = q_rows.shape
+    Hkv = k.shape[0]
+    G = Hq // Hkv
+    tau = softmax_scale(d) if scale is None else scale
+    n = int(pos.max()) + 1
+    nblk = (n + block - 1) // block
+    o = np.zeros((R, Hq, d))
+    lse = np.zeros((Hq, R))
+    raw = np.full((Hq, R, nblk), np.nan)
+    for g in range(Hkv):
+        heads = slice(g * G, (g + 1) * G)
+        for r in range(R):
+            t = int(pos[r])
+            s = tau * (q_rows[r, heads] @ k[g, : t + 1].T)          # [G, t+1]
+            o[r, heads], lse[heads, r] = _attend(s, v[g, : t + 1])
+            nb = t // block + 1
+            padded = np.full((G, nb * block), -np.inf)
+            padded[:, : t + 1] = s
+            blocks = padded.reshape(G, nb, block)
+            if score == "max":
+                raw[heads, r, :nb] = blocks.max(axis=-1)
+            elif score == "lse":
+                mb = blocks.max(axis=-1, keepdims=True)
+                raw[heads, r, :nb] = mb[..., 0] + np.log(np.exp(blocks - mb).sum(axis=-1))
+            else:
+                raise ValueError(score)
+    return o, lse, raw
+
+
+def block_scores(raw: np.ndarray, lse: np.ndarray) -> np.ndarray:
+    """Post-softmax block scores S_{h,t,j} = exp(raw - LSE_t)  (reading R1).
+
+    With score='max' this is eq. S_t^i of [X] 3.4.1: the largest attention
+    weight that query t gives to any key of block j.  raw [Hq, R, nblk],
+    lse [Hq, R]; NaN entries (future blocks) stay NaN.
+    """
+    return np.exp(raw - lse[..., None])
+
+
+def group_max(S: np.ndarray, Hkv: int) -> np.ndarray:
+    """S_g = max over the heads h of group g of S_h  ([X] "Grouped-Query
+    Attention (GQA) Aggregation", eq. S_g; [P] 3.2).  S [Hq, ...] -> [Hkv, ...]."""
+    Hq = S.shape[0]
+    G = Hq // Hkv
+    return S.reshape(Hkv, G, *S.shape[1:]).max(axis=1)
+
+
+def candidates(t: int, block: int = BLOCK, include_diag: bool = False,
+               n_recent: int = 0) -> np.ndarray:
+    """Candidate key blocks (or tokens when block == 1) of query position t.
+
+    Block mode (reading R2): j < floor(t/block), plus j = floor(t/block) when
+    include_diag.  Token mode (reading R9): tokens i < t+1-n_recent.
+    """
+    if block == 1 and n_recent:
+        return np.arange(max(0, t + 1 - n_recent))
+    last = t // block
+    return np.arange(last + 1 if include_diag else last)
+
+
+def topk_select(scores_row: np.ndarray, cand: np.ndarray, k: int):
+    """TopK of [X] 3.4.2 / [P] 3.2 over one row: the k candidates with the
+    highest score, ties to the lower index (R4); returned ascending and padded
+    with -1 to length k (R3).  Also returns the candidates' scores sorted
+    descending (used for the near-tie rule of the parity tests)."""
+    s = scores_row[cand]
+    order = np.lexsort((cand, -s))
+    take = cand[order[: min(k, cand.size)]]
+    idx = np.full(k, -1, np.int64)
+    idx[: take.size] = np.sort(take)
+    return idx, s[order]
+
+
+def select_with_recent(scores_row: np.ndarray, t: int, k: int, n_recent: int):
+    """Token-level selection of [H2]: top-k of the old tokens united with the
+    n_recent newest visible tokens (which do not use the k budget), ascending.
+    Returns the selected token ids (length min(k, #old) + min(n_recent, t+1))
+    and the sorted scores of the old candidates."""
+    old = candidates(t, 1, n_recent=n_recent)
+    top, sorted_s = topk_select(scores_row, old, k)
+    top = top[top >= 0]
+    recent = np.arange(max(0, t + 1 - n_recent), t + 1)
+    return np.sort(np.concatenate([top, recent])), sorted_s
+
+
+# --------------------------------------------------------------- sparse layer
+def sparse_branch_rows(qs_rows: np.ndarray, pos: np.ndarray, k: np.ndarray,
+                       v: np.ndarray, idx: np.ndarray, block: int = BLOCK,
+                       scale: float | None = None) -> np.ndarray:
+    """Block-sparse attention branch over the full layer's own K/V.
+
+    K~, V~ = concat of the selected blocks (eq. K~,V~ of [X] 3.4.3, "Branch 1");
+    o~_t = softmax(tau q'_t . K~) V~ (eq. o~_t).  Keys after t inside a selected
+    diagonal block are excluded (causality).  idx [Hkv, R, n_sel] holds block
+    ids (or token ids with block=1), -1 = unused; the order of the list does
+    not matter.  Returns o~ [R, Hq, d].
+    """
+    R, Hq, d = qs_rows.shape
+    Hkv = k.shape[0]
+    G = Hq // Hkv
+    tau = softmax_scale(d) if scale is None else scale
+    out = np.zeros((R, Hq, d))
+    for g in range(Hkv):
+        heads = slice(g * G, (g + 1) * G)
+        for r in range(R):
+            t = int(pos[r])
+            sel = idx[g, r]
+            sel = np.unique(sel[sel >= 0])
+            keys = (sel[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+            keys = keys[keys <= t]
+            s = tau * (qs_rows[r, heads] @ k[g, keys].T)
+            out[r, heads], _ = _attend(s, v[g, keys])
+    return out
+
+
+def window_branch_rows(qs_rows: np.ndarray, pos: np.ndarray, ks: np.ndarray,
+                       vs: np.ndarray, W: int, scale: float | None = None) -> np.ndarray:
+    """Sliding-window branch with the layer's own K'/V' ([X] 3.4.3 "Branch 2",
+    eq. o'_t): keys [t-W+1, t] (reading R6).  W = 0 gives 0.
+    ks, vs [Hkv, >=max(pos)+1, d].  Returns o' [R, Hq, d]."""
+    R, Hq, d = qs_rows.shape
+    Hkv = ks.shape[0]
+    G = Hq // Hkv
+    tau = softmax_scale(d) if scale is None else scale
+    out = np.zeros((R, Hq, d))
+    for g in range(Hkv):
+        heads = slice(g * G, (g + 1) * G)
+        for r in range(R):
+            t = int(pos[r])
+            lo = max(0, t - W + 1)
+            keys = np.arange(lo, t + 1) if W > 0 else np.arange(0)
+            s = tau * (qs_rows[r, heads] @ ks[g, keys].T)
+            out[r, heads], _ = _attend(s, vs[g, keys])
+    return out
+
+
+def sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def gated_fusion(o_sparse: np.ndarray, o_window: np.ndarray,
+                 gate_logits: np.ndarray | None) -> np.ndarray:
+    """o_t = sigma(g~) o~_t + sigma(g') o'_t  ([X] 3.4.3 "Gated Fusion"; [P] 3.1).
+    Two independent sigmoids per (token, head) (R5); gate_logits [R, Hq, 2]
+    with [..., 0] for the sparse and [..., 1] for the window branch."""
+    if gate_logits is None:
+        return o_sparse + o_window
+    g = sigmoid(gate_logits)
+    return g[..., 0:1] * o_sparse + g[..., 1:2] * o_window
+
+
+# ------------------------------------------------------------- hybrid block
+def select_rows(raw: np.ndarray, lse: np.ndarray, pos: np.ndarray, Hkv: int, kb: int,
+                block: int = BLOCK, include_diag: bool = False):
+    """Finalise, group-aggregate and select for each row: returns
+    idx [Hkv, R, kb], S_g [Hkv, R, nblk] and the sorted candidate scores
+    (list over (g, r))."""
+    Sg = group_max(block_scores(raw, lse), Hkv)
+    R = pos.size
+    idx = np.full((Hkv, R, kb), -1, np.int64)
+    ranked = {}
+    for g in range(Hkv):
+        for r in range(R):
+            t = int(pos[r])
+            cand = candidates(t, block, include_diag)
+            idx[g, r], ranked[g, r] = topk_select(Sg[g, r], cand, kb)
+    return idx, Sg, ranked
+
+
+def sparse_layer_rows(qs_rows, pos, k, v, idx, ks, vs, W, gates_rows,
+                      block: int = BLOCK, scale: float | None = None):
+    """One sparse layer ([X] 3.4.3, [P] 3.1/3.3): block-sparse branch over the
+    shared K/V at the inherited indices, window branch over its own K'/V',
+    merged by the sigmoid gates."""
+    o_sp = sparse_branch_rows(qs_rows, pos, k, v, idx, block, scale)
+    o_sw = window_branch_rows(qs_rows, pos, ks, vs, W, scale)
+    return gated_fusion(o_sp, o_sw, gates_rows)
+
+
+def hybrid_block_rows(q, k, v, layers, pos, kb, W, block=BLOCK,
+                      include_diag=False, score="max", scale=None):
+    """The whole prefill hybrid block [Full, Sparse x N] for one sequence, at the
+    query positions `pos` ([X] 3.2 information flow; [P] 3.1).
+
+    q [T, Hq, d]; k, v [Hkv, T, d]; layers: list of dicts with q [T,Hq,d],
+    k, v [Hkv,T,d] (the layer's own window K'/V') and gates [T,Hq,2] or None.
+    Returns dict(o, lse, raw, Sg, idx, ranked, layer_out=[...]).
+    """
+    Hkv = k.shape[0]
+    o, lse, raw = full_attention_rows(q[pos], pos, k, v, scale, block, score)
+    idx, Sg, ranked = select_rows(raw, lse, pos, Hkv, kb, block, include_diag)
+    outs = []
+    for lay in layers:
+        gates = None if lay.get("gates") is None else lay["gates"][pos]
+        outs.append(sparse_layer_rows(lay["q"][pos], pos, k, v, idx, lay["k"], lay["v"],
+                                      W, gates, block, scale))
+    return dict(o=o, lse=lse, raw=raw, Sg=Sg, idx=idx, ranked=ranked, layer_out=outs)
+
+
+# -------------------------------------------------------------------- decode
+def decode_e4m3fn(codes: np.ndarray) -> np.ndarray:
+    """OCP fp8 e4m3fn code -> value (float64), from the bit fields: sign, 4-bit
+    exponent with bias 7, 3-bit mantissa; exponent 0 is subnormal
+    (m/8 * 2^-6); S.1111.111 is NaN; there is no infinity."""
+    c = np.asarray(codes).astype(np.int64)
+    s = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = np.where((e == 0xF) & (m == 0x7), np.nan, val)
+    return s * val
+
+
+def window_from_ring(k_ring: np.ndarray, v_ring: np.ndarray, L: int, W: int):
+    """Keys/values of the last min(L, W) positions, read from a W-slot ring
+    where position p sits in slot p mod W (reading R8).  Returns them in
+    position order, [Hkv, n, d] each."""
+    p = np.arange(max(0, L - W), L)
+    return k_ring[:, p % W], v_ring[:, p % W]
+
+
+def decode_step(q, k, v, L, layers, kb, W, block=BLOCK, n_recent=0,
+                kv_scale=None, scale=None):
+    """One decode step of a hybrid block for one sequence ([H2] decode_one_token:
+    exact scores of the full layer, selection, then the sparse followers).
+
+    q [Hq, d]; k, v [Hkv, >=L, d] float64 values, or fp8 codes when kv_scale
+    [2, Hkv] is given (value = decode_e4m3fn(code) * scale[K|V, g]).
+    layers: dicts with q [Hq,d], optional k_ring/v_ring [Hkv,W,d], gates [Hq,2].
+    block=64: block mode (top-kb blocks of the fully-past candidates, window
+    branch, gates).  block=1: token mode of [H2] (top-kb old tokens + n_recent
+    newest, no window, no gate).
+    """
+    Hkv = k.shape[0]
+    if kv_scale is not None:
+        k = decode_e4m3fn(k[:, :L]) * kv_scale[0][:, None, None]
+        v = decode_e4m3fn(v[:, :L]) * kv_scale[1][:, None, None]
+    pos = np.array([L - 1])
+    o, lse, raw = full_attention_rows(q[None], pos, k, v, scale, block)
+    Sg = group_max(block_scores(raw, lse), Hkv)          # [Hkv, 1, nblk]
+    if block == 1:
+        sel = []
+        ranked = []
+        for g in range(Hkv):
+            s, rk = select_with_recent(Sg[g, 0], L - 1, kb, n_recent)
+            sel.append(s)
+            ranked.append(rk)
+        n = max(len(s) for s in sel)
+        idx = np.full((Hkv, 1, n), -1, np.int64)
+        for g in range(Hkv):
+            idx[g, 0, : len(sel[g])] = sel[g]
+    else:
+        idx, Sg, ranked_d = select_rows(raw, lse, pos, Hkv, kb, block, False)
+        ranked = [ranked_d[g, 0] for g in range(Hkv)]
+    outs = []
+    for lay in layers:
+        qs = lay["q"][None]
+        o_sp = sparse_branch_rows(qs, pos, k, v, idx, block, scale)
+        if block == 1 or W == 0 or lay.get("k_ring") is None:
+            o_sw = np.zeros_like(o_sp)
+        else:
+            kw, vw = window_from_ring(lay["k_ring"], lay["v_ring"], L, W)
+            # window keys re-indexed 0..n-1 with the query at n-1
+            o_sw = window_branch_rows(qs, np.array([kw.shape[1] - 1]), kw, vw, W, scale)
+        gates = lay.get("gates")
+        if block == 1:
+            outs.append(o_sp[0])
+        else:
+            outs.append(gated_fusion(o_sp, o_sw, None if gates is None else gates[None])[0])
+    return dict(o=o[0], lse=lse[:, 0], raw=raw[:, 0], Sg=Sg[:, 0], idx=idx[:, 0],
+                ranked=ranked, layer_out=outs)
