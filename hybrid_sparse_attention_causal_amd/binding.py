@@ -1,0 +1,158 @@
+"""Thin ctypes binding of libhysparse.so (include/hysparse.h).
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the computation runs in the library's
+kernels.  A missing library raises immediately: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhysparse.so")
+
+HS_OK, HS_ERR_INVALID_ARG, HS_ERR_UNSUPPORTED, HS_ERR_WORKSPACE, HS_ERR_LAUNCH = range(5)
+HS_F32, HS_BF16, HS_FP8_E4M3 = 0, 1, 2
+HS_SCORE_MAX, HS_SCORE_LSE = 0, 1
+HS_SEL_FULLY_PAST, HS_SEL_INCLUDE_DIAG = 0, 2
+HS_FN_FULL_ATTN, HS_FN_BLOCK_TOPK, HS_FN_SPARSE_ATTN, HS_FN_DECODE_SELECT = range(4)
+
+EXPORTS = ("hs_full_attn_fwd_scores", "hs_block_topk", "hs_sparse_attn_fwd",
+           "hs_decode_select_attn", "hs_workspace_size", "hs_last_error", "hs_version")
+
+
+class HsError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"hysparse status {status}: {msg}")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("batch", ctypes.c_int), ("q_len", ctypes.c_int), ("kv_len", ctypes.c_int),
+        ("hq", ctypes.c_int), ("hkv", ctypes.c_int), ("head_dim", ctypes.c_int),
+        ("dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int),
+        ("scale", ctypes.c_float),
+        ("kv_lens", ctypes.c_void_p), ("kv_scale", ctypes.c_void_p),
+    ]
+
+
+def make_shape(batch, q_len, kv_len, hq, hkv, head_dim, dtype, kv_dtype=None, scale=0.0,
+               kv_lens=None, kv_scale=None) -> Shape:
+    s = Shape()
+    s.struct_size = ctypes.sizeof(Shape)
+    s.batch, s.q_len, s.kv_len = batch, q_len, kv_len
+    s.hq, s.hkv, s.head_dim = hq, hkv, head_dim
+    s.dtype = dtype
+    s.kv_dtype = dtype if kv_dtype is None else kv_dtype
+    s.scale = scale
+    s.kv_lens = _ptr(kv_lens)
+    s.kv_scale = _ptr(kv_scale)
+    return s
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libhysparse.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m hybrid_sparse_attention_causal_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, Z, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    SP = ctypes.POINTER(Shape)
+    lib.hs_full_attn_fwd_scores.argtypes = [SP, P, P, P, P, P, P, I, I, P, Z, P]
+    lib.hs_block_topk.argtypes = [SP, P, P, I, I, I, I, P, P, P, Z, P]
+    lib.hs_sparse_attn_fwd.argtypes = [SP, P, P, P, P, I, P, P, I, P, P, P]
+    lib.hs_decode_select_attn.argtypes = [SP, P, P, P, P, I, I, P, P, I, P, P, P, Z, P]
+    lib.hs_workspace_size.argtypes = [I, SP, I, I, I]
+    lib.hs_workspace_size.restype = Z
+    lib.hs_last_error.restype = ctypes.c_char_p
+    lib.hs_version.restype = I
+    for name in ("hs_full_attn_fwd_scores", "hs_block_topk", "hs_sparse_attn_fwd",
+                 "hs_decode_select_attn"):
+        getattr(lib, name).restype = I
+    del F
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status: int):
+    if status != HS_OK:
+        raise HsError(status, load().hs_last_error().decode())
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    return {torch.float32: HS_F32, torch.bfloat16: HS_BF16, torch.uint8: HS_FP8_E4M3,
+            torch.float8_e4m3fn: HS_FP8_E4M3}[t.dtype]
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors passed to hysparse must be contiguous")
+
+
+# ------------------------------------------------------------------ prefill
+def full_attn_fwd_scores(q, k, v_blk, o, lse, blk_raw, score=HS_SCORE_MAX, scale=0.0,
+                         stream=None):
+    """Prefill full layer.  q [B,T,Hq,d], k [B,Hkv,T,d], v_blk [B,Hkv,nblk,d,64];
+    outputs o [B,T,Hq,d], lse [B,Hq,T] fp32, blk_raw [B,Hq,T,nblk] fp32."""
+    _contig(q, k, v_blk, o, lse, blk_raw)
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    s = make_shape(B, T, T, Hq, Hkv, d, dtype_code(q), scale=scale)
+    _check(load().hs_full_attn_fwd_scores(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v_blk),
+                                          _ptr(o), _ptr(lse), _ptr(blk_raw), 64, score,
+                                          None, 0, _stream(stream)))
+
+
+def block_topk(q_shape, blk_raw, lse, topk, idx, grp_score=None, include_diag=False,
+               stream=None):
+    """Prefill selection.  q_shape = (B, T, Hq, Hkv, d, dtype_code);
+    idx [B,Hkv,T,topk] int32, grp_score [B,Hkv,T,nblk] fp32 or None."""
+    _contig(blk_raw, lse, idx, grp_score)
+    B, T, Hq, Hkv, d, dt = q_shape
+    s = make_shape(B, T, T, Hq, Hkv, d, dt)
+    flags = HS_SEL_INCLUDE_DIAG if include_diag else HS_SEL_FULLY_PAST
+    _check(load().hs_block_topk(ctypes.byref(s), _ptr(blk_raw), _ptr(lse), 64, topk, 0, flags,
+                                _ptr(grp_score), _ptr(idx), None, 0, _stream(stream)))
+
+
+def sparse_attn_fwd(q_sp, k, v_blk, idx, topk, k_swa, v_swa_blk, window, gate_logits, o,
+                    scale=0.0, stream=None):
+    """One prefill sparse layer.  q_sp/o [B,T,Hq,d]; k [B,Hkv,T,d]; v_blk, v_swa_blk
+    [B,Hkv,nblk,d,64]; idx [B,Hkv,T,topk]; k_swa [B,Hkv,T,d]; gates [B,T,Hq,2] or None."""
+    _contig(q_sp, k, v_blk, idx, k_swa, v_swa_blk, gate_logits, o)
+    B, T, Hq, d = q_sp.shape
+    Hkv = (k if k is not None else k_swa).shape[1]
+    s = make_shape(B, T, T, Hq, Hkv, d, dtype_code(q_sp), scale=scale)
+    _check(load().hs_sparse_attn_fwd(ctypes.byref(s), _ptr(q_sp), _ptr(k), _ptr(v_blk),
+                                     _ptr(idx), topk, _ptr(k_swa), _ptr(v_swa_blk), window,
+                                     _ptr(gate_logits), _ptr(o), _stream(stream)))
+
+
+def version() -> int:
+    return load().hs_version()

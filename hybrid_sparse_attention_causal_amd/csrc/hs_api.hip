@@ -1,0 +1,239 @@
+// hs_api.hip -- the extern "C" entry points declared in include/hysparse.h:
+// argument validation (before anything is launched), error reporting and
+// dispatch to the kernel launchers.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string>
+
+#include "hs_internal.h"
+#include "hysparse.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+hs_status fail(hs_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+hs_status ok() {
+  g_err.clear();
+  return HS_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+#define REQUIRE_PTR(p)                                                               \
+  do {                                                                               \
+    if (!(p)) return fail(HS_ERR_INVALID_ARG, "%s: %s is NULL", fn, #p);             \
+    if (!aligned16(p)) return fail(HS_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, #p); \
+  } while (0)
+
+// Common shape checks.  Returns HS_OK or an error (message set).
+hs_status check_shape(const char* fn, const hs_shape* s) {
+  if (!s) return fail(HS_ERR_INVALID_ARG, "%s: shape is NULL", fn);
+  if (s->struct_size < sizeof(hs_shape))
+    return fail(HS_ERR_INVALID_ARG, "%s: shape.struct_size %zu < %zu", fn, s->struct_size, sizeof(hs_shape));
+  if (s->batch < 0 || s->q_len < 0 || s->kv_len < 0)
+    return fail(HS_ERR_INVALID_ARG, "%s: negative batch/q_len/kv_len", fn);
+  if (s->hq <= 0 || s->hkv <= 0 || s->hq % s->hkv != 0)
+    return fail(HS_ERR_INVALID_ARG, "%s: hq=%d must be a positive multiple of hkv=%d", fn, s->hq, s->hkv);
+  const int G = s->hq / s->hkv;
+  if (!pow2(G) || G > 32)
+    return fail(HS_ERR_UNSUPPORTED, "%s: group size hq/hkv=%d must be a power of two <= 32", fn, G);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(HS_ERR_UNSUPPORTED, "%s: head_dim=%d (supported: 64, 128)", fn, s->head_dim);
+  if (!(s->scale >= 0.f) || isinf(s->scale))
+    return fail(HS_ERR_INVALID_ARG, "%s: scale must be finite and >= 0", fn);
+  if ((long long)s->batch * s->hq * (long long)(s->q_len > s->kv_len ? s->q_len : s->kv_len) * s->head_dim >
+      (1ll << 40))
+    return fail(HS_ERR_INVALID_ARG, "%s: problem too large", fn);
+  return HS_OK;
+}
+
+hs_status check_prefill(const char* fn, const hs_shape* s) {
+  hs_status st = check_shape(fn, s);
+  if (st) return st;
+  if (s->kv_lens) return fail(HS_ERR_INVALID_ARG, "%s: prefill call with kv_lens set", fn);
+  if (s->q_len != s->kv_len)
+    return fail(HS_ERR_INVALID_ARG, "%s: prefill needs q_len == kv_len (got %d, %d)", fn, s->q_len, s->kv_len);
+  if (s->dtype != HS_F32 && s->dtype != HS_BF16)
+    return fail(HS_ERR_UNSUPPORTED, "%s: prefill dtype %d (supported: HS_F32, HS_BF16)", fn, s->dtype);
+  if (s->kv_dtype != s->dtype)
+    return fail(HS_ERR_UNSUPPORTED, "%s: prefill needs kv_dtype == dtype", fn);
+  return HS_OK;
+}
+
+float scale_log2(const hs_shape* s) {
+  const float tau = s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)s->head_dim);
+  return tau * 1.4426950408889634f;
+}
+
+hs_status launched(const char* fn, hipError_t e) {
+  if (e != hipSuccess) return fail(HS_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int hs_version(void) { return 100; }
+
+const char* hs_last_error(void) { return g_err.c_str(); }
+
+size_t hs_workspace_size(int fn_id, const hs_shape* shape, int block, int topk, int window) {
+  (void)fn_id;
+  (void)shape;
+  (void)block;
+  (void)topk;
+  (void)window;
+  return 0;
+}
+
+hs_status hs_full_attn_fwd_scores(const hs_shape* s, const void* q, const void* k, const void* v,
+                                  void* o, float* lse, float* blk_raw, int block, int flags,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "hs_full_attn_fwd_scores";
+  (void)ws;
+  (void)ws_bytes;
+  hs_status st = check_shape(fn, s);
+  if (st) return st;
+  if (flags != HS_SCORE_MAX && flags != HS_SCORE_LSE)
+    return fail(HS_ERR_INVALID_ARG, "%s: flags=%d (HS_SCORE_MAX or HS_SCORE_LSE)", fn, flags);
+  if (s->kv_lens) return fail(HS_ERR_UNSUPPORTED, "%s: decode mode is not available in this build", fn);
+  st = check_prefill(fn, s);
+  if (st) return st;
+  if (block != 64) return fail(HS_ERR_UNSUPPORTED, "%s: prefill block=%d (only 64)", fn, block);
+  if (s->batch == 0 || s->q_len == 0) return ok();
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(o);
+  REQUIRE_PTR(lse);
+  REQUIRE_PTR(blk_raw);
+  hs::FullPrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.raw = blk_raw;
+  a.B = s->batch;
+  a.T = s->q_len;
+  a.Hq = s->hq;
+  a.Hkv = s->hkv;
+  a.nblk = (s->q_len + 63) / 64;
+  a.sc2 = scale_log2(s);
+  return launched(fn, hs::launch_full_prefill(a, s->dtype, s->head_dim, flags == HS_SCORE_LSE,
+                                              (hipStream_t)stream));
+}
+
+hs_status hs_block_topk(const hs_shape* s, const float* blk_raw, const float* lse, int block,
+                        int topk, int n_recent, int flags, float* grp_score, int32_t* idx,
+                        void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "hs_block_topk";
+  (void)ws;
+  (void)ws_bytes;
+  hs_status st = check_shape(fn, s);
+  if (st) return st;
+  if (flags != HS_SEL_FULLY_PAST && flags != HS_SEL_INCLUDE_DIAG)
+    return fail(HS_ERR_INVALID_ARG, "%s: flags=%d", fn, flags);
+  if (n_recent < 0) return fail(HS_ERR_INVALID_ARG, "%s: n_recent < 0", fn);
+  if (block != 64) return fail(HS_ERR_UNSUPPORTED, "%s: block=%d is not available in this build", fn, block);
+  if (topk < 1 || topk > 1024) return fail(HS_ERR_INVALID_ARG, "%s: topk=%d (1..1024 blocks)", fn, topk);
+  if (n_recent != 0) return fail(HS_ERR_INVALID_ARG, "%s: n_recent applies to token mode only", fn);
+  hs::TopkArgs a{};
+  if (s->kv_lens) {
+    return fail(HS_ERR_UNSUPPORTED, "%s: decode mode is not available in this build", fn);
+  } else {
+    st = check_prefill(fn, s);
+    if (st) return st;
+    a.R = s->q_len;
+    a.raw_stride = (s->q_len + 63) / 64;
+  }
+  if (a.raw_stride > 1024)
+    return fail(HS_ERR_UNSUPPORTED, "%s: more than 1024 candidate blocks per row", fn);
+  if (s->batch == 0 || a.R == 0) return ok();
+  REQUIRE_PTR(blk_raw);
+  REQUIRE_PTR(lse);
+  REQUIRE_PTR(idx);
+  if (grp_score && !aligned16(grp_score)) return fail(HS_ERR_INVALID_ARG, "%s: grp_score misaligned", fn);
+  a.raw = blk_raw;
+  a.lse = lse;
+  a.gs = grp_score;
+  a.idx = idx;
+  a.kv_lens = s->kv_lens;
+  a.B = s->batch;
+  a.Hq = s->hq;
+  a.Hkv = s->hkv;
+  a.kb = topk;
+  a.diag = flags == HS_SEL_INCLUDE_DIAG;
+  return launched(fn, hs::launch_block_topk(a, a.raw_stride, (hipStream_t)stream));
+}
+
+hs_status hs_sparse_attn_fwd(const hs_shape* s, const void* q_sp, const void* k, const void* v,
+                             const int32_t* idx, int topk, const void* k_swa, const void* v_swa,
+                             int window, const float* gate_logits, void* o, void* stream) {
+  const char* fn = "hs_sparse_attn_fwd";
+  hs_status st = check_prefill(fn, s);
+  if (st) return st;
+  if (topk < 0 || topk > 1024) return fail(HS_ERR_INVALID_ARG, "%s: topk=%d (0..1024)", fn, topk);
+  if (window < 0) return fail(HS_ERR_INVALID_ARG, "%s: window < 0", fn);
+  if (s->batch == 0 || s->q_len == 0) return ok();
+  if ((long long)(s->q_len + 63) / 64 > (1 << 16))
+    return fail(HS_ERR_UNSUPPORTED, "%s: more than 65536 blocks", fn);
+  REQUIRE_PTR(q_sp);
+  REQUIRE_PTR(o);
+  if (topk > 0) {
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(idx);
+  }
+  if (window > 0) {
+    REQUIRE_PTR(k_swa);
+    REQUIRE_PTR(v_swa);
+  }
+  if (gate_logits && ((uintptr_t)gate_logits & 7u))
+    return fail(HS_ERR_INVALID_ARG, "%s: gate_logits not 8-byte aligned", fn);
+  hs::SparsePrefillArgs a{};
+  a.q = q_sp;
+  a.k = k;
+  a.v = v;
+  a.idx = idx;
+  a.ks = k_swa;
+  a.vs = v_swa;
+  a.gates = gate_logits;
+  a.o = o;
+  a.B = s->batch;
+  a.T = s->q_len;
+  a.Hq = s->hq;
+  a.Hkv = s->hkv;
+  a.nblk = (s->q_len + 63) / 64;
+  a.topk = topk;
+  a.W = window;
+  a.sc2 = scale_log2(s);
+  return launched(fn, hs::launch_sparse_prefill(a, s->dtype, s->head_dim, (hipStream_t)stream));
+}
+
+hs_status hs_decode_select_attn(const hs_shape* s, const void* q_sp, const void* k, const void* v,
+                                const int32_t* idx, int n_sel, int block, const void* k_ring,
+                                const void* v_ring, int window, const float* gate_logits, void* o,
+                                void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "hs_decode_select_attn";
+  (void)q_sp; (void)k; (void)v; (void)idx; (void)n_sel; (void)block; (void)k_ring; (void)v_ring;
+  (void)window; (void)gate_logits; (void)o; (void)ws; (void)ws_bytes; (void)stream;
+  hs_status st = check_shape(fn, s);
+  if (st) return st;
+  return fail(HS_ERR_UNSUPPORTED, "%s: decode is not available in this build", fn);
+}
+
+}  // extern "C"

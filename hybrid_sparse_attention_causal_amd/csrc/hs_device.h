@@ -1,0 +1,261 @@
+// hs_device.h -- device building blocks shared by the HySparse kernels (gfx950).
+//
+// The attention "engine" works on one wavefront (64 lanes) and one tile of 64
+// keys at a time.  It computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (or
+// 8x v_mfma_f32_16x16x4f32 for fp32 inputs), so that a lane holds 16 logits of
+// ONE query column: the per-column softmax maximum and sum need only two
+// cross-lane exchanges (xor 16, xor 32), and the 64-key tile maximum is exactly
+// the per-block maximum of the modified FlashAttention pass (HySparse
+// explainer, section 3.4.1 "Modified FlashAttention Kernel": the row-wise
+// maximum of each key tile is stored as the block score).
+//
+// MFMA 16x16x32 operand layout (lane l, q = l/16, r = l%16):
+//   A (16 x 32): row r, k-slots 8q..8q+7        B (32 x 16): col r, k-slots 8q..8q+7
+//   C (16 x 16): col r, rows 4q..4q+3
+// S^T chunk c (c = 0..3, 16 keys each) row r holds key tile_key(c, r).  The map
+// is chosen so that, after the softmax, a lane's 8 probabilities of chunks
+// {2u, 2u+1} are exactly the k-slots 8q..8q+7 of keys 32u+8q..32u+8q+7 of the
+// P.V product: the P operand needs no shuffle, and the value operand is eight
+// consecutive keys of one head_dim row, i.e. 16 contiguous bytes of a
+// [head_dim][64] (block-major) value tile.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hysparse.h"
+
+namespace hs {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegBig = -1.0e30f;
+constexpr int kBlk = 64;
+constexpr int kNoKey = 0x7fffffff;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__host__ __device__ __forceinline__ int tile_key(int c, int r) {
+  return ((c >> 1) << 5) | ((r >> 2) << 3) | ((c & 1) << 2) | (r & 3);
+}
+// inverse of tile_key: the S^T row (16*c + r) that holds key kk of the tile
+__host__ __device__ __forceinline__ int tile_row(int kk) {
+  const int u = kk >> 5, q = (kk >> 3) & 3, e = (kk >> 2) & 1, i = kk & 3;
+  return ((2 * u + e) << 4) | (q << 2) | i;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// ----------------------------------------------------------- element traits
+template <int DT> struct Tr;
+
+template <> struct Tr<HS_BF16> {
+  static constexpr int ES = 2;  // bytes per element
+  struct Frag { uint4 u; };
+  __device__ __forceinline__ static Frag ld(const void* p) {
+    Frag f;
+    f.u = *reinterpret_cast<const uint4*>(p);
+    return f;
+  }
+  __device__ __forceinline__ static Frag zero() {
+    Frag f;
+    f.u = make_uint4(0u, 0u, 0u, 0u);
+    return f;
+  }
+  // keep elements e < n, zero the rest (n in 0..8)
+  __device__ __forceinline__ static Frag keep(Frag f, int n) {
+    uint32_t w[4] = {f.u.x, f.u.y, f.u.z, f.u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (2 * i >= n) w[i] = 0u;
+      else if (2 * i + 1 >= n) w[i] &= 0xffffu;
+    }
+    f.u = make_uint4(w[0], w[1], w[2], w[3]);
+    return f;
+  }
+  __device__ __forceinline__ static void mma(f32x4& acc, const Frag& a, const Frag& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a.u),
+                                                  __builtin_bit_cast(bf16x8_t, b.u), acc, 0, 0, 0);
+  }
+  __device__ __forceinline__ static Frag pack(const float* p) {
+    Frag f;
+    f.u = make_uint4(bf16_bits(p[0]) | (bf16_bits(p[1]) << 16), bf16_bits(p[2]) | (bf16_bits(p[3]) << 16),
+                     bf16_bits(p[4]) | (bf16_bits(p[5]) << 16), bf16_bits(p[6]) | (bf16_bits(p[7]) << 16));
+    return f;
+  }
+  __device__ __forceinline__ static void store4(void* dst, float a, float b, float c, float d) {
+    *reinterpret_cast<uint2*>(dst) =
+        make_uint2(bf16_bits(a) | (bf16_bits(b) << 16), bf16_bits(c) | (bf16_bits(d) << 16));
+  }
+};
+
+template <> struct Tr<HS_F32> {
+  static constexpr int ES = 4;
+  struct Frag { float4 a, b; };
+  __device__ __forceinline__ static Frag ld(const void* p) {
+    Frag f;
+    f.a = reinterpret_cast<const float4*>(p)[0];
+    f.b = reinterpret_cast<const float4*>(p)[1];
+    return f;
+  }
+  __device__ __forceinline__ static Frag zero() {
+    Frag f;
+    f.a = make_float4(0.f, 0.f, 0.f, 0.f);
+    f.b = f.a;
+    return f;
+  }
+  __device__ __forceinline__ static Frag keep(Frag f, int n) {
+    float v[8] = {f.a.x, f.a.y, f.a.z, f.a.w, f.b.x, f.b.y, f.b.z, f.b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i >= n) v[i] = 0.f;
+    f.a = make_float4(v[0], v[1], v[2], v[3]);
+    f.b = make_float4(v[4], v[5], v[6], v[7]);
+    return f;
+  }
+  __device__ __forceinline__ static void mma(f32x4& acc, const Frag& a, const Frag& b) {
+    // k-slot 8q+e of the 32-wide step is fed as k = q of sub-step e
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.x, b.a.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.y, b.a.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.z, b.a.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.w, b.a.w, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.x, b.b.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.y, b.b.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.z, b.b.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.w, b.b.w, acc, 0, 0, 0);
+  }
+  __device__ __forceinline__ static Frag pack(const float* p) {
+    Frag f;
+    f.a = make_float4(p[0], p[1], p[2], p[3]);
+    f.b = make_float4(p[4], p[5], p[6], p[7]);
+    return f;
+  }
+  __device__ __forceinline__ static void store4(void* dst, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
+  }
+};
+
+// ------------------------------------------------------------- the engine
+// One wavefront, NT column tiles of 16 query columns each, head_dim D.
+// Online softmax state per column tile: running maximum m (log2 units, already
+// scaled), per-lane partial denominator l, and O^T accumulators
+// (o[nt][mc]: head_dim rows 16*mc + 4q .. +3 of the lane's column).
+template <int DT, int D, int NT>
+struct WaveAttn {
+  using T = Tr<DT>;
+  using Frag = typename T::Frag;
+  static constexpr int NS = D / 32;  // k-steps of S^T = K Q^T
+  static constexpr int NM = D / 16;  // row chunks of O^T
+
+  Frag qf[NT][NS];
+  f32x4 o[NT][NM];
+  float m[NT], l[NT];
+
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      m[nt] = kNegBig;
+      l[nt] = 0.f;
+#pragma unroll
+      for (int mc = 0; mc < NM; ++mc) o[nt][mc] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  // Process one 64-key tile whose first key has absolute index kbase.
+  //   ldK(c, s)  -> A fragment of S^T chunk c, k-step s (key kbase+tile_key(c, r))
+  //   ldV(u, mc) -> A fragment of O^T chunk mc, key step u (keys kbase+32u+8q..+7)
+  //   lo[nt], hi[nt]: inclusive absolute key range valid for the lane's column
+  //   (lo = kNoKey disables the column for this tile).
+  //   sc2 = softmax scale * log2(e).
+  // Outputs per column tile: bmax = max scaled logit of the tile (log2 units,
+  // -inf when no key is valid) and, when WANT_SUM, bsum = sum over the tile of
+  // exp2(logit - m_new) (m_new = running max after this tile).
+  template <bool MASK, bool WANT_SUM, class LK, class LV>
+  __device__ __forceinline__ void tile(const LK& ldK, const LV& ldV, int kbase, const int* lo,
+                                       const int* hi, float sc2, float* bmax, float* bsum) {
+    const int lane = lane_id();
+    const int q4 = (lane >> 4) << 2;
+    f32x4 s[NT][4];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) s[nt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NS; ++ks) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const Frag a = ldK(c, ks);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) T::mma(s[nt][c], a, qf[nt][ks]);
+      }
+    }
+    Frag pf[NT][2];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float x[16];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = s[nt][c][i] * sc2;
+          if (MASK) {
+            const int key = kbase + tile_key(c, q4 + i);
+            if (key < lo[nt] || key > hi[nt]) v = -INFINITY;
+          }
+          x[4 * c + i] = v;
+          mx = fmaxf(mx, v);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      bmax[nt] = mx;
+      const float mn = fmaxf(m[nt], mx);
+      const float alpha = fast_exp2(m[nt] - mn);
+      m[nt] = mn;
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        x[e] = fast_exp2(x[e] - mn);
+        ps += x[e];
+      }
+      l[nt] = l[nt] * alpha + ps;
+      if (WANT_SUM) {
+        float bs = ps + __shfl_xor(ps, 16);
+        bs += __shfl_xor(bs, 32);
+        bsum[nt] = bs;
+      }
+#pragma unroll
+      for (int mc = 0; mc < NM; ++mc) o[nt][mc] *= alpha;
+      pf[nt][0] = T::pack(x);
+      pf[nt][1] = T::pack(x + 8);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int mc = 0; mc < NM; ++mc) {
+        const Frag a = ldV(u, mc);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) T::mma(o[nt][mc], a, pf[nt][u]);
+      }
+    }
+  }
+
+  // Column totals: 1/l (0 when the column saw no key) and the log2-domain LSE.
+  __device__ __forceinline__ void finish(int nt, float& inv_l, float& lse2) const {
+    float lt = l[nt] + __shfl_xor(l[nt], 16);
+    lt += __shfl_xor(lt, 32);
+    inv_l = lt > 0.f ? 1.f / lt : 0.f;
+    lse2 = lt > 0.f ? m[nt] + fast_log2(lt) : -INFINITY;
+  }
+};
+
+}  // namespace hs

@@ -1,0 +1,53 @@
+// hs_internal.h -- launcher interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hs {
+
+struct FullPrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* raw;
+  int B, T, Hq, Hkv, nblk;
+  float sc2;  // softmax scale * log2(e)
+};
+
+struct TopkArgs {
+  const float* raw;
+  const float* lse;
+  float* gs;
+  int32_t* idx;
+  const int32_t* kv_lens;  // decode: context lengths; NULL in prefill
+  int B, Hq, Hkv;
+  int R;           // query rows per sequence (T in prefill, 1 in decode)
+  int raw_stride;  // floats per (b, h, row) score row
+  int kb;          // top-k
+  int diag;        // include the diagonal block
+};
+
+struct SparsePrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* idx;
+  const void* ks;
+  const void* vs;
+  const float* gates;
+  void* o;
+  int B, T, Hq, Hkv, nblk, topk, W;
+  int nwg;  // work groups before the XCD remap
+  float sc2;
+};
+
+hipError_t launch_full_prefill(const FullPrefillArgs& a, int dtype, int D, int score_lse,
+                               hipStream_t s);
+hipError_t launch_block_topk(const TopkArgs& a, int max_blocks, hipStream_t s);
+hipError_t launch_sparse_prefill(const SparsePrefillArgs& a, int dtype, int D, hipStream_t s);
+
+}  // namespace hs

@@ -99,6 +99,30 @@ def _normal(rng: np.random.Generator, shape) -> np.ndarray:
     return out
 
 
+_CHUNK = 1 << 22  # elements per independently seeded chunk
+
+
+def _normal_big(cfg: "Config", stream: int, shape) -> np.ndarray:
+    """N(0,1) float32 array drawn in fixed 4M-element chunks, chunk i from
+    default_rng([seed, stream, 1000 + i]); filled by a thread pool, the result
+    does not depend on the thread count."""
+    out = np.empty(shape, np.float32)
+    flat = out.reshape(-1)
+    n = flat.size
+    nch = (n + _CHUNK - 1) // _CHUNK
+
+    def one(i):
+        seg = flat[i * _CHUNK: min(n, (i + 1) * _CHUNK)]
+        _rng(cfg, stream, 1000 + i).standard_normal(out=seg, dtype=np.float32)
+
+    if nch <= 1:
+        one(0) if n else None
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(one, range(nch)))
+    return out
+
+
 def _threads() -> int:
     try:
         n = len(os.sched_getaffinity(0))
@@ -108,11 +132,27 @@ def _threads() -> int:
 
 
 # ------------------------------------------------------------------ encodings
+def _bf16_chunk(u: np.ndarray, out: np.ndarray) -> None:
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= 16
+    out[...] = r
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 (or float64, first rounded to float32) to bf16, RNE."""
+    """Round float32 (or float64, first rounded to float32) to bf16, RNE.
+    Works in 1M-element chunks on a thread pool (numpy releases the GIL)."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    r = ((u >> 16) & 1) + np.uint32(0x7FFF)
-    return ((u + r) >> 16).astype(np.uint16)
+    out = np.empty(u.shape, np.uint16)
+    uf, of = u.reshape(-1), out.reshape(-1)
+    n, ch = uf.size, 1 << 20
+    if n <= ch:
+        _bf16_chunk(uf, of)
+        return out
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(lambda i: _bf16_chunk(uf[i:i + ch], of[i:i + ch]), range(0, n, ch)))
+    return out
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -188,7 +228,7 @@ def _salient(cfg: Config, L: int, b: int) -> np.ndarray:
 
 def _queries(cfg: Config, stream: int, c: np.ndarray, lead) -> np.ndarray:
     """Q ~ N(0,1)/d^(1/4) + 1.5 c_g, shape [*lead, Hq, d] (float32)."""
-    x = _normal(_rng(cfg, stream), (*lead, cfg.Hq, cfg.d))
+    x = _normal_big(cfg, stream, (*lead, cfg.Hq, cfg.d))
     x *= np.float32(cfg.d ** -0.25)
     x += (1.5 * np.repeat(c, cfg.G, axis=0)).astype(np.float32)
     return x
@@ -202,8 +242,8 @@ def make_prefill(cfg: Config, n_layers: int | None = None) -> PrefillInputs:
     c = _unit_vectors(cfg)
     s = np.float32(d ** -0.25)
     q = _queries(cfg, 0, c, (B, T))
-    k = _normal(_rng(cfg, 1), (B, Hkv, T, d)) * s
-    v = _normal(_rng(cfg, 2), (B, Hkv, T, d)) * s
+    k = _normal_big(cfg, 1, (B, Hkv, T, d)) * s
+    v = _normal_big(cfg, 2, (B, Hkv, T, d)) * s
     sal = []
     for b in range(B):
         pos = _salient(cfg, T, b)
@@ -212,9 +252,9 @@ def make_prefill(cfg: Config, n_layers: int | None = None) -> PrefillInputs:
     layers = []
     for l in range(nl):
         ql = _queries(cfg, 10 + l, c, (B, T))
-        kl = _normal(_rng(cfg, 30 + l), (B, Hkv, T, d))
-        vl = _normal(_rng(cfg, 50 + l), (B, Hkv, T, d))
-        gl = _normal(_rng(cfg, 70 + l), (B, T, cfg.Hq, 2))
+        kl = _normal_big(cfg, 30 + l, (B, Hkv, T, d))
+        vl = _normal_big(cfg, 50 + l, (B, Hkv, T, d))
+        gl = _normal_big(cfg, 70 + l, (B, T, cfg.Hq, 2))
         layers.append(dict(q=store(ql, cfg.dtype), k=store(kl, cfg.dtype),
                            v=store(vl, cfg.dtype), gates=gl))
     return PrefillInputs(cfg, store(q, cfg.dtype), store(k, cfg.dtype),

@@ -1,0 +1,200 @@
+/*
+ * hysparse.h -- C ABI of the HySparse hybrid-block attention hot path on AMD
+ * MI355X (gfx950).
+ *
+ * A hybrid block is one full causal attention layer followed by N sparse
+ * layers (HySparse paper, section 3.1 "HySparse Overview"; explainer page
+ * section 3.2 "Big-Picture Architecture").  The full layer computes ordinary
+ * causal GQA attention and, in the same pass, per-64-token-block scores
+ * (explainer section 3.4.1, "Block-Level Max Attention Scores" and "Modified
+ * FlashAttention Kernel"; paper section 3.2).  The scores are normalised,
+ * reduced over the query heads of each GQA group and turned into a per-query
+ * top-k block list (explainer 3.4.1 "Grouped-Query Attention (GQA)
+ * Aggregation", 3.4.2 "TopK Block Selection").  Every sparse layer then
+ * attends to those blocks of the full layer's own K/V plus a sliding window
+ * of its own K'/V', and merges the two with sigmoid gates (explainer 3.4.3;
+ * paper sections 3.1, 3.3).  Decode runs the same path for one new token per
+ * sequence; the token-level variant of the HySparse2 explainer ("Precise
+ * retrieval without a separate indexer") selects single tokens plus the
+ * newest ones instead of blocks.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller, 16-byte
+ *     aligned, densely packed in the layouts stated below (row-major, last
+ *     index fastest).  The library never allocates or frees device memory;
+ *     scratch space comes from a caller workspace of hs_workspace_size() bytes.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is only enqueued; nothing synchronises the host.
+ *   - Arguments are validated before anything is launched; on an error the
+ *     call returns a non-zero hs_status, writes nothing, and hs_last_error()
+ *     (thread-local) describes the problem.  HS_ERR_LAUNCH reports a failed
+ *     kernel launch.
+ *   - Query head h belongs to kv head floor(h / G), G = hq / hkv (contiguous
+ *     GQA grouping).  G must be a power of two <= 64; head_dim is 64 or 128.
+ *   - Value caches use a block-major layout: each run of 64 consecutive
+ *     positions of one kv head is stored as a [head_dim][64] tile, i.e. a
+ *     value tensor is [batch][hkv][ceil(len/64)][head_dim][64].  Key caches
+ *     are position-major [batch][hkv][len][head_dim].  Tail entries of the
+ *     last value tile (positions >= len) are never used and may hold anything.
+ *   - The softmax scale is shape.scale, or 1/sqrt(head_dim) when it is 0.
+ */
+#ifndef HYSPARSE_H
+#define HYSPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hs_status {
+  HS_OK = 0,
+  HS_ERR_INVALID_ARG = 1, /* a null pointer, a bad size or a misaligned pointer */
+  HS_ERR_UNSUPPORTED = 2, /* a valid but unimplemented combination            */
+  HS_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required       */
+  HS_ERR_LAUNCH = 4       /* the HIP runtime refused a launch                 */
+} hs_status;
+
+typedef enum hs_dtype {
+  HS_F32 = 0,      /* IEEE binary32                                   */
+  HS_BF16 = 1,     /* bfloat16                                        */
+  HS_FP8_E4M3 = 2  /* OCP fp8 e4m3fn codes (key/value caches only)    */
+} hs_dtype;
+
+/* flags of hs_full_attn_fwd_scores */
+#define HS_SCORE_MAX 0 /* block score = max logit of the block (the pages' rule) */
+#define HS_SCORE_LSE 1 /* block score = log-sum-exp of the block's logits        */
+/* flags of hs_block_topk */
+#define HS_SEL_FULLY_PAST 0   /* candidates j < floor(t/64)                      */
+#define HS_SEL_INCLUDE_DIAG 2 /* candidates j <= floor(t/64) (diagonal clipped)  */
+
+typedef struct hs_shape {
+  size_t struct_size;     /* = sizeof(hs_shape); lets the struct grow          */
+  int batch;              /* number of sequences                               */
+  int q_len;              /* prefill: T (queries = keys = T); decode: 1        */
+  int kv_len;             /* prefill: T; decode: cache capacity per sequence    */
+  int hq, hkv, head_dim;  /* query heads, kv heads, head dimension (64|128)    */
+  int dtype;              /* hs_dtype of queries/outputs (and K/V in prefill)  */
+  int kv_dtype;           /* decode: hs_dtype of the caches; prefill: = dtype  */
+  float scale;            /* softmax scale tau; 0 -> 1/sqrt(head_dim)          */
+  const int32_t* kv_lens; /* decode: device [batch] context lengths L_b (the
+                             query sits at position L_b-1); NULL = prefill     */
+  const float* kv_scale;  /* fp8 caches: device [2][hkv] scales (K, V); value
+                             = decoded code * scale.  NULL otherwise           */
+} hs_shape;
+
+/*
+ * Full causal attention layer with per-block scores in one pass
+ * (explainer 3.4.1 eq. o_t and eq. S_t^i; "Modified FlashAttention Kernel",
+ * first pass; paper 3.2).
+ *
+ * Prefill (kv_lens == NULL), T = q_len = kv_len, nblk = ceil(T/64):
+ *   q  [batch][T][hq][head_dim]          dtype
+ *   k  [batch][hkv][T][head_dim]         dtype
+ *   v  [batch][hkv][nblk][head_dim][64]  dtype (block-major)
+ *   o  [batch][T][hq][head_dim]          dtype (out)
+ *   lse     [batch][hq][T] fp32 (out): log sum_{i<=t} exp(tau q_t.k_i)
+ *   blk_raw [batch][hq][T][nblk] fp32 (out): for j <= floor(t/64) only,
+ *           HS_SCORE_MAX: max_{i in block j, i<=t} tau q_t.k_i
+ *           HS_SCORE_LSE: log sum_{i in block j, i<=t} exp(tau q_t.k_i)
+ *     Both are log-domain and independent of the row normaliser: the
+ *     post-softmax score of the pages is exp(blk_raw - lse).  Entries
+ *     j > floor(t/64) are not written.
+ * Decode (kv_lens != NULL, q_len == 1), capacity C = kv_len (multiple of 64):
+ *   q [batch][hq][head_dim] (dtype); k [batch][hkv][C][head_dim];
+ *   v [batch][hkv][C/64][head_dim][64] (kv_dtype; fp8 needs kv_scale);
+ *   o [batch][hq][head_dim]; lse [batch][hq];
+ *   blk_raw [batch][hq][C/block]: block = 64 gives block scores as above for
+ *   j <= floor((L_b-1)/64); block = 1 gives every token's logit tau q.k_i for
+ *   i < L_b (the token-level variant).  Needs a workspace.
+ * `block` must be 64 in prefill and 64 or 1 in decode.
+ */
+hs_status hs_full_attn_fwd_scores(const hs_shape* shape, const void* q, const void* k,
+                                  const void* v, void* o, float* lse, float* blk_raw,
+                                  int block, int flags, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/*
+ * Finalisation, GQA group maximum and top-k selection
+ * (explainer 3.4.1 "Modified FlashAttention Kernel" second pass, eq. S_g;
+ * 3.4.2 "TopK Block Selection"; paper 3.2).
+ *
+ * For each query row t and group g:
+ *   S_g[t][j] = max_{h in g} exp(blk_raw[h][t][j] - lse[h][t])
+ * and idx receives the `topk` candidates with the largest S_g, ties to the
+ * smaller index, written in ascending order and padded with -1 when there are
+ * fewer candidates.  Candidates: j < floor(t/64) (HS_SEL_FULLY_PAST) or
+ * j <= floor(t/64) (HS_SEL_INCLUDE_DIAG).
+ * Prefill: blk_raw/lse as produced above; idx [batch][hkv][T][topk] int32;
+ *   grp_score (nullable) [batch][hkv][T][nblk] fp32 receives S_g for
+ *   j <= floor(t/64).
+ * Decode, block = 64: t = L_b-1, idx [batch][hkv][topk].
+ * Decode, block = 1 (token mode): candidates are the tokens i < L_b-n_recent;
+ *   the n_recent newest tokens are always added and do not count against
+ *   topk; idx [batch][hkv][topk+n_recent] holds token ids, ascending, -1
+ *   padded.  grp_score (nullable) [batch][hkv][C] receives S_g for i < L_b.
+ * topk is 1..1024 in block mode and 1..4096 in token mode.
+ */
+hs_status hs_block_topk(const hs_shape* shape, const float* blk_raw, const float* lse,
+                        int block, int topk, int n_recent, int flags, float* grp_score,
+                        int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One sparse layer, prefill (explainer 3.4.3: "Branch 1: Block Sparse
+ * Attention" eq. K~,V~ and eq. o~_t, "Branch 2: Sliding Window Attention"
+ * eq. o'_t, "Gated Fusion"; paper 3.1 and 3.3).
+ *   q_sp  [batch][T][hq][head_dim]          the layer's own queries q'
+ *   k, v  the full layer's K (position-major) and V (block-major), shared
+ *   idx   [batch][hkv][T][topk] int32 block ids (any order, -1 = unused)
+ *   k_swa [batch][hkv][T][head_dim], v_swa [batch][hkv][nblk][head_dim][64]
+ *         the layer's own window cache (NULL together with window == 0)
+ *   window   W >= 0: keys t-W+1 .. t of k_swa/v_swa
+ *   gate_logits [batch][T][hq][2] fp32 (sparse, window) or NULL (both gates 1)
+ *   o     [batch][T][hq][head_dim] (out)
+ * o_t = sigmoid(G0) o~_t + sigmoid(G1) o'_t; an empty selection gives o~ = 0.
+ * Keys after t inside a selected block are excluded.
+ */
+hs_status hs_sparse_attn_fwd(const hs_shape* shape, const void* q_sp, const void* k,
+                             const void* v, const int32_t* idx, int topk,
+                             const void* k_swa, const void* v_swa, int window,
+                             const float* gate_logits, void* o, void* stream);
+
+/*
+ * One sparse layer at decode time, one query per sequence (explainer 3.4.3;
+ * HySparse2 explainer, decode_one_token pseudocode).
+ *   q_sp [batch][hq][head_dim]; k, v: the full layer's caches as in
+ *   hs_full_attn_fwd_scores decode mode; idx [batch][hkv][n_sel] from
+ *   hs_block_topk (block ids for block = 64, token ids for block = 1).
+ *   k_ring, v_ring: the layer's own window ring [batch][hkv][W][head_dim]
+ *   and [batch][hkv][ceil(W/64)][head_dim][64] (slot = position mod W), or
+ *   NULL with window == 0.  gate_logits [batch][hq][2] or NULL.
+ *   o [batch][hq][head_dim] (out).  Needs a workspace.
+ */
+hs_status hs_decode_select_attn(const hs_shape* shape, const void* q_sp, const void* k,
+                                const void* v, const int32_t* idx, int n_sel, int block,
+                                const void* k_ring, const void* v_ring, int window,
+                                const float* gate_logits, void* o, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/* Function ids for hs_workspace_size */
+#define HS_FN_FULL_ATTN 0
+#define HS_FN_BLOCK_TOPK 1
+#define HS_FN_SPARSE_ATTN 2
+#define HS_FN_DECODE_SELECT 3
+
+/* Workspace bytes the given entry point needs for this shape (0 if none).
+ * `block`, `topk` and `window` are the values that will be passed to it. */
+size_t hs_workspace_size(int fn_id, const hs_shape* shape, int block, int topk, int window);
+
+/* Thread-local description of the last error of this thread ("" if none). */
+const char* hs_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int hs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYSPARSE_H */

@@ -1,0 +1,93 @@
+"""The C-ABI library: it loads, exports every symbol include/hysparse.h
+declares, and rejects bad arguments before touching the GPU (so these run on a
+machine without one: validation happens before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from hybrid_sparse_attention_causal_amd import binding as hb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hysparse.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(hb.LIB_PATH),
+                                reason="libhysparse.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hs_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = hb.load()
+    names = declared_functions()
+    assert set(names) == set(hb.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert hb.version() >= 100
+
+
+def _shape(**kw):
+    args = dict(batch=1, q_len=128, kv_len=128, hq=8, hkv=2, head_dim=128, dtype=hb.HS_BF16)
+    args.update(kw)
+    return hb.make_shape(**args)
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null pointer value; never dereferenced
+
+
+def _full(s, block=64, flags=0, ptrs=FAKE):
+    lib = hb.load()
+    return lib.hs_full_attn_fwd_scores(ctypes.byref(s), ptrs, ptrs, ptrs, ptrs, ptrs, ptrs,
+                                       block, flags, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=6, hkv=4), hb.HS_ERR_INVALID_ARG),
+    (dict(hq=12, hkv=4), hb.HS_ERR_UNSUPPORTED),      # group of 3
+    (dict(head_dim=96), hb.HS_ERR_UNSUPPORTED),
+    (dict(dtype=hb.HS_FP8_E4M3), hb.HS_ERR_UNSUPPORTED),
+    (dict(q_len=-1), hb.HS_ERR_INVALID_ARG),
+    (dict(kv_len=64), hb.HS_ERR_INVALID_ARG),          # prefill needs q_len == kv_len
+    (dict(scale=float("nan")), hb.HS_ERR_INVALID_ARG),
+])
+def test_full_attn_rejects_bad_shapes(kw, status):
+    assert _full(_shape(**kw)) == status
+    assert hb.load().hs_last_error().decode()
+
+
+def test_full_attn_rejects_bad_args():
+    s = _shape()
+    assert _full(s, block=32) == hb.HS_ERR_UNSUPPORTED
+    assert _full(s, flags=7) == hb.HS_ERR_INVALID_ARG
+    assert _full(s, ptrs=None) == hb.HS_ERR_INVALID_ARG
+    assert _full(s, ptrs=FAKE + 4) == hb.HS_ERR_INVALID_ARG   # misaligned
+    bad = _shape()
+    bad.struct_size = 8
+    assert _full(bad) == hb.HS_ERR_INVALID_ARG
+    assert hb.load().hs_full_attn_fwd_scores(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 0,
+                                             None, 0, None) == hb.HS_ERR_INVALID_ARG
+
+
+def test_empty_problem_is_a_no_op():
+    assert _full(_shape(q_len=0, kv_len=0), ptrs=None) == hb.HS_OK
+    assert _full(_shape(batch=0), ptrs=None) == hb.HS_OK
+
+
+def test_topk_and_sparse_validation():
+    lib = hb.load()
+    s = _shape()
+    assert lib.hs_block_topk(ctypes.byref(s), FAKE, FAKE, 64, 0, 0, 0, None, FAKE, None, 0,
+                             None) == hb.HS_ERR_INVALID_ARG
+    assert lib.hs_block_topk(ctypes.byref(s), FAKE, FAKE, 64, 4, 0, 5, None, FAKE, None, 0,
+                             None) == hb.HS_ERR_INVALID_ARG
+    assert lib.hs_block_topk(ctypes.byref(s), None, FAKE, 64, 4, 0, 0, None, FAKE, None, 0,
+                             None) == hb.HS_ERR_INVALID_ARG
+    assert lib.hs_sparse_attn_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 4, None, None, 16,
+                                  None, FAKE, None) == hb.HS_ERR_INVALID_ARG   # window w/o cache
+    assert lib.hs_sparse_attn_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, -1, None, None, 0,
+                                  None, FAKE, None) == hb.HS_ERR_INVALID_ARG

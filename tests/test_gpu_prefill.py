@@ -1,0 +1,243 @@
+"""GPU parity of the prefill path (full layer + scores, selection, sparse
+layers) against the fp64 oracle, called through the C ABI.
+
+Small shapes are compared on every row; the full-size 7B-shaped (T=8192) and
+80B-shaped (T=32768) workloads on sampled rows.  Sparse-layer outputs are
+compared with the oracle evaluated on the GPU's own indices (a legal near-tie
+swap cannot fail an output check) and the indices themselves under the
+near-tie rule."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from hybrid_sparse_attention_causal_amd import binding as hb
+from hybrid_sparse_attention_causal_amd import inputs as gen
+from oracle import hs_oracle as ora
+from parity import SIDE_TOL, TOL, compare_indices, dev, host, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+class Run:
+    """One prefill hybrid block on the GPU, with its buffers."""
+
+    def __init__(self, inp, score=hb.HS_SCORE_MAX, include_diag=False, kb=None, W=None,
+                 gates=True):
+        cfg = inp.cfg
+        self.cfg, self.inp = cfg, inp
+        B, T, Hq, Hkv, d = cfg.B, cfg.T, cfg.Hq, cfg.Hkv, cfg.d
+        self.kb = cfg.kb if kb is None else kb
+        self.W = cfg.W if W is None else W
+        nblk = cfg.nblk
+        tdt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+        q, k = dev(inp.q, cfg.dtype), dev(inp.k, cfg.dtype)
+        vb = dev(gen.block_major(inp.v), cfg.dtype)
+        self.o = torch.full((B, T, Hq, d), float("nan"), dtype=tdt, device="cuda")
+        self.lse = torch.full((B, Hq, T), float("nan"), device="cuda")
+        self.raw = torch.full((B, Hq, T, nblk), float("nan"), device="cuda")
+        hb.full_attn_fwd_scores(q, k, vb, self.o, self.lse, self.raw, score=score)
+        self.idx = torch.full((B, Hkv, T, self.kb), -7, dtype=torch.int32, device="cuda")
+        self.gs = torch.full((B, Hkv, T, nblk), float("nan"), device="cuda")
+        dt = hb.HS_F32 if cfg.dtype == "f32" else hb.HS_BF16
+        hb.block_topk((B, T, Hq, Hkv, d, dt), self.raw, self.lse, self.kb, self.idx, self.gs,
+                      include_diag=include_diag)
+        self.outs = []
+        for lay in inp.layers:
+            qs, ks = dev(lay["q"], cfg.dtype), dev(lay["k"], cfg.dtype)
+            vsb = dev(gen.block_major(lay["v"]), cfg.dtype)
+            g = dev(lay["gates"]) if gates else None
+            o = torch.full((B, T, Hq, d), float("nan"), dtype=tdt, device="cuda")
+            hb.sparse_attn_fwd(qs, k, vb, self.idx, self.kb, ks if self.W else None,
+                               vsb if self.W else None, self.W, g, o)
+            self.outs.append(o)
+        torch.cuda.synchronize()
+
+
+def oracle_rows(inp, pos, kb, W, score="max", include_diag=False, gates=True, b=0):
+    layers = [dict(q=inp.f64("q", l)[b], k=inp.f64("k", l)[b], v=inp.f64("v", l)[b],
+                   gates=inp.f64("gates", l)[b] if gates else None)
+              for l in range(len(inp.layers))]
+    return ora.hybrid_block_rows(inp.f64("q")[b], inp.f64("k")[b], inp.f64("v")[b], layers,
+                                 pos, kb, W, include_diag=include_diag, score=score)
+
+
+def check_run(run, pos, score="max", include_diag=False, gates=True, layers=None):
+    cfg, inp = run.cfg, run.inp
+    tol = TOL[cfg.dtype]
+    ref = oracle_rows(inp, pos, run.kb, run.W, score, include_diag, gates)
+    o = host(run.o)[0][pos]
+    err_o = np.abs(o - ref["o"]).max()
+    lse = host(run.lse)[0][:, pos]
+    err_lse = np.abs(lse - ref["lse"]).max()
+    raw = host(run.raw)[0][:, pos]
+    valid = ~np.isnan(ref["raw"])
+    err_raw = np.abs(raw[valid] - ref["raw"][valid]).max()
+    say(f"  full layer: max|dO|={err_o:.3g} max|dLSE|={err_lse:.3g} max|draw|={err_raw:.3g}")
+    assert err_o <= tol and err_lse <= SIDE_TOL and err_raw <= SIDE_TOL
+    gs = host(run.gs)[0][:, pos]
+    vg = ~np.isnan(ref["Sg"])
+    rel_gs = np.abs(gs[vg] - ref["Sg"][vg]).max() / np.abs(ref["Sg"][vg]).max()
+    gidx = host(run.idx)[0][:, pos]
+    n, ties, fails = compare_indices(gidx, ref, pos, run.kb, include_diag)
+    say(f"  selection: rows={n} near-tie={ties} failures={len(fails)} rel|dSg|={rel_gs:.3g}")
+    assert not fails, fails[:5]
+    assert rel_gs < 1e-4
+    b = 0
+    k64, v64 = inp.f64("k")[b], inp.f64("v")[b]
+    for l in range(len(inp.layers)) if layers is None else layers:
+        gl = inp.f64("gates", l)[b][pos] if gates else None
+        want = ora.sparse_layer_rows(inp.f64("q", l)[b][pos], pos, k64, v64, gidx,
+                                     inp.f64("k", l)[b], inp.f64("v", l)[b], run.W, gl)
+        got = host(run.outs[l])[0][pos]
+        err = np.abs(got - want).max()
+        say(f"  sparse layer {l}: max|dO|={err:.3g}")
+        assert err <= tol
+
+
+SMALL = [
+    # T, Hq, Hkv, d, dtype, kb, W
+    (1, 4, 1, 64, "f32", 4, 128),
+    (63, 8, 2, 64, "bf16", 2, 16),
+    (65, 4, 4, 128, "f32", 1, 1),
+    (200, 8, 1, 128, "bf16", 2, 7),
+    (130, 16, 2, 64, "bf16", 3, 200),
+    (257, 2, 2, 64, "f32", 2, 64),
+    (333, 32, 4, 128, "bf16", 4, 100),
+    (640, 4, 1, 64, "f32", 8, 128),
+]
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,d,dtype,kb,W", SMALL)
+def test_small_shapes_all_rows(T, Hq, Hkv, d, dtype, kb, W):
+    say(f"[small] T={T} Hq={Hq} Hkv={Hkv} d={d} {dtype} kb={kb} W={W}")
+    cfg = gen.config(1, T=T, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, kb=kb, W=W, N=2)
+    inp = gen.make_prefill(cfg)
+    run = Run(inp)
+    check_run(run, np.arange(T))
+
+
+@pytest.mark.parametrize("score", ["max", "lse"])
+@pytest.mark.parametrize("include_diag", [False, True])
+def test_score_modes_and_candidates(score, include_diag):
+    say(f"[modes] score={score} include_diag={include_diag}")
+    cfg = gen.config(1, T=300, Hq=8, Hkv=2, d=64, dtype="f32", kb=3, W=50, N=1)
+    inp = gen.make_prefill(cfg)
+    run = Run(inp, score=hb.HS_SCORE_LSE if score == "lse" else hb.HS_SCORE_MAX,
+              include_diag=include_diag)
+    check_run(run, np.arange(300), score=score, include_diag=include_diag)
+
+
+def test_ungated_and_no_window():
+    say("[variants] gates=None, W=0")
+    cfg = gen.config(1, T=260, Hq=4, Hkv=1, d=128, dtype="bf16", kb=2, W=0, N=1)
+    inp = gen.make_prefill(cfg)
+    run = Run(inp, gates=False)
+    check_run(run, np.arange(260), gates=False)
+
+
+def test_dense_reduction_on_gpu():
+    """Every block selected (diagonal included), no window, no gate: each sparse
+    layer equals dense causal attention of its own queries over the shared K/V."""
+    say("[dense reduction]")
+    T = 256
+    cfg = gen.config(1, T=T, Hq=4, Hkv=2, d=64, dtype="f32", kb=4, W=0, N=1)
+    inp = gen.make_prefill(cfg)
+    run = Run(inp, include_diag=True, gates=False)
+    assert np.array_equal(host(run.idx)[0][:, 255], np.tile(np.arange(4), (2, 1)))
+    qs = inp.f64("q", 0)[0]
+    o, _, _ = ora.full_attention_rows(qs, np.arange(T), inp.f64("k")[0], inp.f64("v")[0])
+    got = host(run.outs[0])[0]
+    # rows t < 192 have fewer than 4 candidate blocks, so all of theirs are selected too
+    assert np.abs(got - o).max() < 1e-4
+
+
+def _golden_inputs(T):
+    """The hand-worked examples padded to d=64: q = 8 e (tau*q.k = k component)."""
+    d = 64
+    q = np.zeros((1, T, 2, d), np.float32)
+    q[0, :, 0, 0] = 8.0
+    q[0, :, 1, 1] = 8.0
+    k = np.zeros((1, 1, T, d), np.float32)
+    k[0, 0, 5, 0] = math.log(3.0)
+    k[0, 0, :64, 1] = math.log(2.0)
+    k[0, 0, 100, 1] = k[0, 0, 101, 1] = math.log(4.0)
+    v = np.zeros((1, 1, T, d), np.float32)
+    v[0, 0, 5, 0] = 1.0
+    v[0, 0, 100, 1] = v[0, 0, 101, 1] = 1.0
+    return q, k, v
+
+
+def test_hand_worked_examples_on_gpu():
+    from test_oracle_pins import _read_golden
+
+    say("[golden E1/E2]")
+    g1 = _read_golden("e1_two_blocks.txt")
+    q, k, v = _golden_inputs(128)
+    cfg = gen.config(1, T=128, Hq=2, Hkv=1, d=64, kb=1, W=0, N=0)
+    inp = gen.PrefillInputs(cfg, q, k, v, [], [])
+    run = Run(inp, include_diag=True)
+    S = np.exp(host(run.raw)[0][:, 127] - host(run.lse)[0][:, 127:128])
+    assert np.abs(S[0] - g1["S_A"]).max() < 1e-6 and np.abs(S[1] - g1["S_B"]).max() < 1e-6
+    assert np.abs(host(run.gs)[0][0, 127, :2] - g1["S_g"]).max() < 1e-6
+    assert host(run.idx)[0][0, 127, 0] == 0
+    o = host(run.o)[0][127]
+    assert np.abs(o[0, :2] - g1["o_A"]).max() < 1e-6 and np.abs(o[1, :2] - g1["o_B"]).max() < 1e-6
+    run = Run(inp, score=hb.HS_SCORE_LSE, include_diag=True)
+    assert np.abs(host(run.gs)[0][0, 127, :2] - g1["S_g_lse_mode"]).max() < 1e-6
+
+    g2 = _read_golden("e2_three_blocks_gated.txt")
+    T = 192
+    q, k, v = _golden_inputs(T)
+    vs = np.zeros((1, 1, T, 64), np.float32)
+    vs[0, 0, :, 0] = np.arange(T)
+    vs[0, 0, :, 1] = -np.arange(T)
+    gates = np.zeros((1, T, 2, 2), np.float32)
+    gates[..., 1] = math.log(3.0)
+    lay = dict(q=q, k=np.zeros((1, 1, T, 64), np.float32), v=vs, gates=gates)
+    cfg = gen.config(1, T=T, Hq=2, Hkv=1, d=64, kb=1, W=2, N=1)
+    inp = gen.PrefillInputs(cfg, q, k, v, [lay], [])
+    run = Run(inp)
+    assert np.abs(host(run.gs)[0][0, 191, :2] - g2["S_g"]).max() < 1e-6
+    assert host(run.idx)[0][0, 191, 0] == 0
+    o = host(run.outs[0])[0][191]
+    assert np.abs(o[0, :2] - g2["o_A"]).max() < 1e-4 * 143
+    assert np.abs(o[1, :2] - g2["o_B"]).max() < 1e-4 * 143
+
+
+def test_config1_tiny_block_all_rows():
+    say("[config 1] T=1024 Hq=4 Hkv=1 d=64 fp32, 3 sparse layers")
+    inp = gen.make_prefill(gen.config(1))
+    run = Run(inp)
+    check_run(run, np.arange(1024))
+
+
+def test_config2_7b_shaped_sampled():
+    say("[config 2] T=8192 Hq=32 Hkv=8 d=128 bf16, 3 sparse layers, sampled rows")
+    inp = gen.make_prefill(gen.config(2))
+    run = Run(inp)
+    pos = sample_rows(8192, every=101)
+    check_run(run, pos)
+
+
+def test_config3_80b_shaped_sampled():
+    say("[config 3] T=32768 Hq=32 Hkv=4 d=128 bf16, sampled rows, layers 0-1 of 11")
+    inp = gen.make_prefill(gen.config(3), n_layers=2)
+    run = Run(inp)
+    pos = sample_rows(32768, every=409, head=96, tail=32)
+    check_run(run, pos)
+
+
+def test_repeat_runs_are_bitwise_identical():
+    say("[determinism]")
+    inp = gen.make_prefill(gen.config(1, T=500, Hq=8, Hkv=2, d=128, dtype="bf16", N=1))
+    a, b = Run(inp), Run(inp)
+    for x, y in ((a.o, b.o), (a.raw, b.raw), (a.idx, b.idx), (a.outs[0], b.outs[0])):
+        assert torch.equal(torch.nan_to_num(x.float(), 123.0), torch.nan_to_num(y.float(), 123.0))
