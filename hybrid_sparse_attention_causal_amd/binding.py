@@ -154,5 +154,54 @@ def sparse_attn_fwd(q_sp, k, v_blk, idx, topk, k_swa, v_swa_blk, window, gate_lo
                                      _ptr(gate_logits), _ptr(o), _stream(stream)))
 
 
+# ------------------------------------------------------------------- decode
+def workspace_size(fn_id, shape: Shape, block=64, topk=0, window=0) -> int:
+    return load().hs_workspace_size(fn_id, ctypes.byref(shape), block, topk, window)
+
+
+def decode_shape(q, k, lens, kv_scale=None, scale=0.0) -> Shape:
+    """q [B,Hq,d]; k [B,Hkv,C,d] (the key cache); lens [B] int32 on the device."""
+    B, Hq, d = q.shape
+    Hkv, C = k.shape[1], k.shape[2]
+    return make_shape(B, 1, C, Hq, Hkv, d, dtype_code(q), dtype_code(k), scale, lens, kv_scale)
+
+
+def decode_full_attn_scores(q, k, v, lens, o, lse, raw, block=64, ws=None, kv_scale=None,
+                            scale=0.0, stream=None):
+    """Decode full layer.  q/o [B,Hq,d]; k [B,Hkv,C,d]; v [B,Hkv,C/64,d,64];
+    lse [B,Hq]; raw [B,Hq,C/block].  ws: uint8 device tensor (allocated here
+    when None)."""
+    _contig(q, k, v, lens, o, lse, raw)
+    s = decode_shape(q, k, lens, kv_scale, scale)
+    need = workspace_size(HS_FN_FULL_ATTN, s, block)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(load().hs_full_attn_fwd_scores(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                          _ptr(lse), _ptr(raw), block, HS_SCORE_MAX, _ptr(ws),
+                                          ws.numel(), _stream(stream)))
+    return ws
+
+
+def decode_block_topk(q, k, lens, raw, lse, topk, idx, grp_score=None, block=64, n_recent=0,
+                      kv_scale=None, stream=None):
+    """Decode selection; idx [B,Hkv,topk(+n_recent)] int32."""
+    _contig(raw, lse, idx, grp_score)
+    s = decode_shape(q, k, lens, kv_scale)
+    _check(load().hs_block_topk(ctypes.byref(s), _ptr(raw), _ptr(lse), block, topk, n_recent,
+                                HS_SEL_FULLY_PAST, _ptr(grp_score), _ptr(idx), None, 0,
+                                _stream(stream)))
+
+
+def decode_select_attn(q_sp, k, v, lens, idx, n_sel, k_ring, v_ring, window, gate_logits, o,
+                       block=64, kv_scale=None, scale=0.0, stream=None):
+    """One decode sparse layer.  q_sp/o [B,Hq,d]; idx [B,Hkv,n_sel];
+    k_ring [B,Hkv,W,d]; v_ring [B,Hkv,ceil(W/64),d,64]; gates [B,Hq,2] or None."""
+    _contig(q_sp, k, v, lens, idx, k_ring, v_ring, gate_logits, o)
+    s = decode_shape(q_sp, k, lens, kv_scale, scale)
+    _check(load().hs_decode_select_attn(ctypes.byref(s), _ptr(q_sp), _ptr(k), _ptr(v), _ptr(idx),
+                                        n_sel, block, _ptr(k_ring), _ptr(v_ring), window,
+                                        _ptr(gate_logits), _ptr(o), None, 0, _stream(stream)))
+
+
 def version() -> int:
     return load().hs_version()

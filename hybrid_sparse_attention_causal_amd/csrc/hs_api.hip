@@ -72,6 +72,32 @@ hs_status check_prefill(const char* fn, const hs_shape* s) {
   return HS_OK;
 }
 
+hs_status check_decode(const char* fn, const hs_shape* s) {
+  hs_status st = check_shape(fn, s);
+  if (st) return st;
+  if (!s->kv_lens) return fail(HS_ERR_INVALID_ARG, "%s: decode needs kv_lens", fn);
+  if (!aligned16(s->kv_lens)) return fail(HS_ERR_INVALID_ARG, "%s: kv_lens not 16-byte aligned", fn);
+  if (s->q_len != 1) return fail(HS_ERR_INVALID_ARG, "%s: decode needs q_len == 1", fn);
+  if (s->kv_len <= 0 || s->kv_len % 64)
+    return fail(HS_ERR_INVALID_ARG, "%s: cache capacity kv_len=%d must be a positive multiple of 64", fn,
+                s->kv_len);
+  if (s->dtype != HS_BF16) return fail(HS_ERR_UNSUPPORTED, "%s: decode query dtype must be HS_BF16", fn);
+  if (s->kv_dtype != HS_BF16)
+    return fail(HS_ERR_UNSUPPORTED, "%s: decode cache dtype %d is not available", fn, s->kv_dtype);
+  if (s->hq / s->hkv > 16) return fail(HS_ERR_UNSUPPORTED, "%s: decode group size > 16", fn);
+  return HS_OK;
+}
+
+// split-K chunking of the decode full layer: 16 blocks (1024 keys) per chunk
+constexpr int kDecodeChunkBlocks = 16;
+int decode_nch(const hs_shape* s) {
+  const int span = 64 * kDecodeChunkBlocks;
+  return (s->kv_len + span - 1) / span;
+}
+size_t decode_full_ws(const hs_shape* s) {
+  return (size_t)s->batch * s->hq * decode_nch(s) * (s->head_dim + 2) * sizeof(float);
+}
+
 float scale_log2(const hs_shape* s) {
   const float tau = s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)s->head_dim);
   return tau * 1.4426950408889634f;
@@ -91,11 +117,11 @@ int hs_version(void) { return 100; }
 const char* hs_last_error(void) { return g_err.c_str(); }
 
 size_t hs_workspace_size(int fn_id, const hs_shape* shape, int block, int topk, int window) {
-  (void)fn_id;
-  (void)shape;
   (void)block;
   (void)topk;
   (void)window;
+  if (!shape || shape->struct_size < sizeof(hs_shape) || !shape->kv_lens) return 0;
+  if (fn_id == HS_FN_FULL_ATTN) return decode_full_ws(shape);
   return 0;
 }
 
@@ -109,7 +135,41 @@ hs_status hs_full_attn_fwd_scores(const hs_shape* s, const void* q, const void* 
   if (st) return st;
   if (flags != HS_SCORE_MAX && flags != HS_SCORE_LSE)
     return fail(HS_ERR_INVALID_ARG, "%s: flags=%d (HS_SCORE_MAX or HS_SCORE_LSE)", fn, flags);
-  if (s->kv_lens) return fail(HS_ERR_UNSUPPORTED, "%s: decode mode is not available in this build", fn);
+  if (s->kv_lens) {
+    st = check_decode(fn, s);
+    if (st) return st;
+    if (block != 64 && block != 1) return fail(HS_ERR_INVALID_ARG, "%s: decode block=%d (64 or 1)", fn, block);
+    if (flags != HS_SCORE_MAX) return fail(HS_ERR_UNSUPPORTED, "%s: decode supports HS_SCORE_MAX only", fn);
+    if (s->batch == 0) return ok();
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(o);
+    REQUIRE_PTR(lse);
+    REQUIRE_PTR(blk_raw);
+    const size_t need = decode_full_ws(s);
+    if (!ws || ws_bytes < need)
+      return fail(HS_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, need, ws_bytes);
+    if (!aligned16(ws)) return fail(HS_ERR_INVALID_ARG, "%s: ws not 16-byte aligned", fn);
+    hs::DecodeFullArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.raw = blk_raw;
+    a.part = (float*)ws;
+    a.lens = s->kv_lens;
+    a.B = s->batch;
+    a.Hq = s->hq;
+    a.Hkv = s->hkv;
+    a.C = s->kv_len;
+    a.nch = decode_nch(s);
+    a.ch_blocks = kDecodeChunkBlocks;
+    a.token = block == 1;
+    a.sc2 = scale_log2(s);
+    return launched(fn, hs::launch_decode_full(a, s->head_dim, (hipStream_t)stream));
+  }
   st = check_prefill(fn, s);
   if (st) return st;
   if (block != 64) return fail(HS_ERR_UNSUPPORTED, "%s: prefill block=%d (only 64)", fn, block);
@@ -153,7 +213,10 @@ hs_status hs_block_topk(const hs_shape* s, const float* blk_raw, const float* ls
   if (n_recent != 0) return fail(HS_ERR_INVALID_ARG, "%s: n_recent applies to token mode only", fn);
   hs::TopkArgs a{};
   if (s->kv_lens) {
-    return fail(HS_ERR_UNSUPPORTED, "%s: decode mode is not available in this build", fn);
+    st = check_decode(fn, s);
+    if (st) return st;
+    a.R = 1;
+    a.raw_stride = s->kv_len / 64;
   } else {
     st = check_prefill(fn, s);
     if (st) return st;
@@ -229,11 +292,45 @@ hs_status hs_decode_select_attn(const hs_shape* s, const void* q_sp, const void*
                                 const void* v_ring, int window, const float* gate_logits, void* o,
                                 void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "hs_decode_select_attn";
-  (void)q_sp; (void)k; (void)v; (void)idx; (void)n_sel; (void)block; (void)k_ring; (void)v_ring;
-  (void)window; (void)gate_logits; (void)o; (void)ws; (void)ws_bytes; (void)stream;
-  hs_status st = check_shape(fn, s);
+  (void)ws;
+  (void)ws_bytes;
+  hs_status st = check_decode(fn, s);
   if (st) return st;
-  return fail(HS_ERR_UNSUPPORTED, "%s: decode is not available in this build", fn);
+  if (block != 64) return fail(HS_ERR_UNSUPPORTED, "%s: block=%d is not available", fn, block);
+  if (n_sel < 0 || n_sel > 4096) return fail(HS_ERR_INVALID_ARG, "%s: n_sel=%d (0..4096)", fn, n_sel);
+  if (window < 0 || window > s->kv_len) return fail(HS_ERR_INVALID_ARG, "%s: window=%d", fn, window);
+  if (s->batch == 0) return ok();
+  REQUIRE_PTR(q_sp);
+  REQUIRE_PTR(o);
+  if (n_sel > 0) {
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(idx);
+  }
+  if (window > 0) {
+    REQUIRE_PTR(k_ring);
+    REQUIRE_PTR(v_ring);
+  }
+  if (gate_logits && ((uintptr_t)gate_logits & 7u))
+    return fail(HS_ERR_INVALID_ARG, "%s: gate_logits not 8-byte aligned", fn);
+  hs::DecodeSparseArgs a{};
+  a.q = q_sp;
+  a.k = k;
+  a.v = v;
+  a.idx = idx;
+  a.kr = k_ring;
+  a.vr = v_ring;
+  a.gates = gate_logits;
+  a.o = o;
+  a.lens = s->kv_lens;
+  a.B = s->batch;
+  a.Hq = s->hq;
+  a.Hkv = s->hkv;
+  a.C = s->kv_len;
+  a.nsel = n_sel;
+  a.W = window;
+  a.sc2 = scale_log2(s);
+  return launched(fn, hs::launch_decode_sparse(a, s->head_dim, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -178,9 +178,16 @@ struct WaveAttn {
   // Outputs per column tile: bmax = max scaled logit of the tile (log2 units,
   // -inf when no key is valid) and, when WANT_SUM, bsum = sum over the tile of
   // exp2(logit - m_new) (m_new = running max after this tile).
-  template <bool MASK, bool WANT_SUM, class LK, class LV>
+  struct NoHook {
+    __device__ __forceinline__ void operator()(int, const float*) const {}
+  };
+
+  // `hook(nt, x)` sees the lane's 16 masked, scaled logits (log2 units; x[4c+i]
+  // belongs to key kbase + tile_key(c, 4q+i)) before the exponentials.
+  template <bool MASK, bool WANT_SUM, class LK, class LV, class HK = NoHook>
   __device__ __forceinline__ void tile(const LK& ldK, const LV& ldV, int kbase, const int* lo,
-                                       const int* hi, float sc2, float* bmax, float* bsum) {
+                                       const int* hi, float sc2, float* bmax, float* bsum,
+                                       const HK& hook = HK()) {
     const int lane = lane_id();
     const int q4 = (lane >> 4) << 2;
     f32x4 s[NT][4];
@@ -215,6 +222,7 @@ struct WaveAttn {
           mx = fmaxf(mx, v);
         }
       }
+      hook(nt, x);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       bmax[nt] = mx;

@@ -45,6 +45,40 @@ struct SparsePrefillArgs {
   float sc2;
 };
 
+struct DecodeFullArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* raw;
+  float* part;            // workspace: [B][Hq][nch][D+2] partial (o, m, l)
+  const int32_t* lens;
+  int B, Hq, Hkv;
+  int C;                  // cache capacity per sequence (multiple of 64)
+  int nch;                // chunks per sequence at capacity
+  int ch_blocks;          // 64-key blocks per chunk
+  int token;              // 1: raw holds per-token logits; 0: per-block maxima
+  float sc2;
+};
+
+struct DecodeSparseArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* idx;
+  const void* kr;
+  const void* vr;
+  const float* gates;
+  void* o;
+  const int32_t* lens;
+  int B, Hq, Hkv, C, nsel, W;
+  float sc2;
+};
+
+hipError_t launch_decode_full(const DecodeFullArgs& a, int D, hipStream_t s);
+hipError_t launch_decode_sparse(const DecodeSparseArgs& a, int D, hipStream_t s);
+
 hipError_t launch_full_prefill(const FullPrefillArgs& a, int dtype, int D, int score_lse,
                                hipStream_t s);
 hipError_t launch_block_topk(const TopkArgs& a, int max_blocks, hipStream_t s);

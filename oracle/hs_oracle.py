@@ -355,20 +355,30 @@ def decode_step(q, k, v, L, layers, kb, W, block=BLOCK, n_recent=0,
     else:
         idx, Sg, ranked_d = select_rows(raw, lse, pos, Hkv, kb, block, False)
         ranked = [ranked_d[g, 0] for g in range(Hkv)]
-    outs = []
-    for lay in layers:
-        qs = lay["q"][None]
-        o_sp = sparse_branch_rows(qs, pos, k, v, idx, block, scale)
-        if block == 1 or W == 0 or lay.get("k_ring") is None:
-            o_sw = np.zeros_like(o_sp)
-        else:
-            kw, vw = window_from_ring(lay["k_ring"], lay["v_ring"], L, W)
-            # window keys re-indexed 0..n-1 with the query at n-1
-            o_sw = window_branch_rows(qs, np.array([kw.shape[1] - 1]), kw, vw, W, scale)
-        gates = lay.get("gates")
-        if block == 1:
-            outs.append(o_sp[0])
-        else:
-            outs.append(gated_fusion(o_sp, o_sw, None if gates is None else gates[None])[0])
+    outs = [decode_sparse_layer(lay, k, v, L, idx[:, 0], W, block, scale=scale) for lay in layers]
     return dict(o=o[0], lse=lse[:, 0], raw=raw[:, 0], Sg=Sg[:, 0], idx=idx[:, 0],
                 ranked=ranked, layer_out=outs)
+
+
+def decode_sparse_layer(lay, k, v, L, idx, W, block=BLOCK, kv_scale=None, scale=None):
+    """One sparse layer at decode time for one sequence: the sparse branch over
+    the selected blocks (block=64) or tokens (block=1) of the full layer's
+    cache, the window branch over the layer's own ring, the sigmoid gates
+    ([X] 3.4.3; [H2] decode_one_token).  idx [Hkv, n] (-1 = unused).
+    Token mode has no window and no gate (reading R9).  Returns o [Hq, d]."""
+    if kv_scale is not None:
+        k = decode_e4m3fn(k[:, :L]) * kv_scale[0][:, None, None]
+        v = decode_e4m3fn(v[:, :L]) * kv_scale[1][:, None, None]
+    pos = np.array([L - 1])
+    qs = lay["q"][None]
+    o_sp = sparse_branch_rows(qs, pos, k, v, idx[:, None, :], block, scale)
+    if block == 1:
+        return o_sp[0]
+    if W == 0 or lay.get("k_ring") is None:
+        o_sw = np.zeros_like(o_sp)
+    else:
+        kw, vw = window_from_ring(lay["k_ring"], lay["v_ring"], L, W)
+        # window keys re-indexed 0..n-1 with the query at n-1
+        o_sw = window_branch_rows(qs, np.array([kw.shape[1] - 1]), kw, vw, W, scale)
+    gates = lay.get("gates")
+    return gated_fusion(o_sp, o_sw, None if gates is None else gates[None])[0]

@@ -1,0 +1,126 @@
+"""GPU parity of the decode path (block mode): split-K full layer with block
+scores, selection, sparse layers with the window ring and gates, against the
+fp64 oracle, through the C ABI.  Cache positions >= L_b hold NaN, so any read
+past a sequence's length shows up in the outputs."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from hybrid_sparse_attention_causal_amd import binding as hb
+from hybrid_sparse_attention_causal_amd import inputs as gen
+from oracle import hs_oracle as ora
+from parity import SIDE_TOL, TOL, check_index_row, check_index_set, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+class DecodeRun:
+    def __init__(self, inp, n_layers=None, gates=True, W=None):
+        cfg = inp.cfg
+        self.cfg, self.inp = cfg, inp
+        B, Hq, Hkv, C, d = cfg.B, cfg.Hq, cfg.Hkv, cfg.T, cfg.d
+        self.W = cfg.W if W is None else W
+        kc = np.empty((B, Hkv, C, d), np.uint16)
+        vc = np.empty((B, Hkv, C // 64, d, 64), np.uint16)
+        gen.fill_decode_cache(inp, kc, vc)
+        self.k, self.v = dev(kc), dev(vc)
+        del kc, vc
+        self.lens = torch.from_numpy(inp.lens.astype(np.int32)).cuda()
+        q = dev(inp.q)
+        self.o = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.full((B, Hq), float("nan"), device="cuda")
+        self.raw = torch.full((B, Hq, C // 64), float("nan"), device="cuda")
+        hb.decode_full_attn_scores(q, self.k, self.v, self.lens, self.o, self.lse, self.raw)
+        self.idx = torch.full((B, Hkv, cfg.kb), -7, dtype=torch.int32, device="cuda")
+        self.gs = torch.full((B, Hkv, C // 64), float("nan"), device="cuda")
+        hb.decode_block_topk(q, self.k, self.lens, self.raw, self.lse, cfg.kb, self.idx, self.gs)
+        self.outs = []
+        layers = inp.layers if n_layers is None else inp.layers[:n_layers]
+        for lay in layers:
+            o = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+            kr = dev(lay["k_ring"]) if self.W else None
+            vr = dev(gen.block_major(lay["v_ring"])) if self.W else None
+            g = dev(lay["gates"]) if gates else None
+            hb.decode_select_attn(dev(lay["q"]), self.k, self.v, self.lens, self.idx, cfg.kb,
+                                  kr, vr, self.W, g, o)
+            self.outs.append(o)
+        torch.cuda.synchronize()
+
+
+def f64_bf16(a):
+    return gen.bf16_bits_to_f32(a).astype(np.float64)
+
+
+def check_sequences(run, seqs, gates=True):
+    cfg, inp = run.cfg, run.inp
+    tol = TOL["bf16"]
+    o_g, lse_g, raw_g = host(run.o), host(run.lse), host(run.raw)
+    idx_g, gs_g = host(run.idx), host(run.gs)
+    outs_g = [host(o) for o in run.outs]
+    worst = dict(o=0.0, lse=0.0, raw=0.0, layer=0.0)
+    ties = 0
+    for b in seqs:
+        L = int(inp.lens[b])
+        ks, vs = zip(*(inp.kv_slab_f64(b, g) for g in range(cfg.Hkv)))
+        k, v = np.stack(ks), np.stack(vs)
+        layers = []
+        for lay in inp.layers[: len(run.outs)]:
+            layers.append(dict(q=f64_bf16(lay["q"][b]),
+                               k_ring=f64_bf16(lay["k_ring"][b]) if run.W else None,
+                               v_ring=f64_bf16(lay["v_ring"][b]) if run.W else None,
+                               gates=lay["gates"][b].astype(np.float64) if gates else None))
+        ref = ora.decode_step(f64_bf16(inp.q[b]), k, v, L, [], cfg.kb, run.W)
+        nb = (L - 1) // 64 + 1
+        worst["o"] = max(worst["o"], np.abs(o_g[b] - ref["o"]).max())
+        worst["lse"] = max(worst["lse"], np.abs(lse_g[b] - ref["lse"]).max())
+        worst["raw"] = max(worst["raw"], np.abs(raw_g[b][:, :nb] - ref["raw"][:, :nb]).max())
+        assert np.abs(gs_g[b][:, :nb] - ref["Sg"][:, :nb]).max() <= 1e-4 * ref["Sg"][:, :nb].max()
+        for g in range(cfg.Hkv):
+            ranked = ref["ranked"][g]
+            ok, tie = check_index_row(idx_g[b, g], ref["idx"][g], ranked, cfg.kb)
+            if tie:
+                ties += 1
+                cand = np.arange((L - 1) // 64)
+                ok = ok and check_index_set(idx_g[b, g], ref["Sg"][g], cand, cfg.kb, ranked)
+            assert ok, (b, g, idx_g[b, g], ref["idx"][g])
+        for l, lay in enumerate(layers):
+            want = ora.decode_sparse_layer(lay, k, v, L, idx_g[b].astype(np.int64), run.W)
+            worst["layer"] = max(worst["layer"], np.abs(outs_g[l][b] - want).max())
+    say(f"  seqs={list(seqs)} max|dO|={worst['o']:.3g} max|dLSE|={worst['lse']:.3g} "
+        f"max|draw|={worst['raw']:.3g} sparse max|dO|={worst['layer']:.3g} near-tie={ties}")
+    assert worst["o"] <= tol and worst["layer"] <= tol
+    assert worst["lse"] <= SIDE_TOL and worst["raw"] <= SIDE_TOL
+    # NaN poison beyond L must never leak into the outputs
+    assert not np.isnan(o_g).any() and all(not np.isnan(x).any() for x in outs_g)
+
+
+@pytest.mark.parametrize("W,gates", [(100, True), (64, False), (0, True), (300, True)])
+def test_small_ragged(W, gates):
+    say(f"[decode small] W={W} gates={gates}")
+    cfg = gen.config(4, B=6, T=1024, Hq=8, Hkv=2, d=128, kb=3, W=W, N=2, L_lo=1, L_hi=1024)
+    inp = gen.make_decode(cfg)
+    inp.lens = np.array([1, 63, 64, 65, 700, 1024], np.int32)
+    run = DecodeRun(inp, gates=gates)
+    check_sequences(run, range(6), gates=gates)
+
+
+def test_group_of_16_and_d64():
+    say("[decode G=16 d=64]")
+    cfg = gen.config(4, B=3, T=2048, Hq=16, Hkv=1, d=64, kb=5, W=128, N=1, L_lo=300, L_hi=2048)
+    inp = gen.make_decode(cfg)
+    run = DecodeRun(inp)
+    check_sequences(run, range(3))
+
+
+def test_config4_full_size_sampled():
+    say("[config 4] 64 seqs, capacity 65536, L ~ U[32768, 65536], kb=32, W=128 (layers 0-1 of 11)")
+    inp = gen.make_decode(gen.config(4), n_layers=2)
+    run = DecodeRun(inp)
+    check_sequences(run, [0, 21, 42, 63])
