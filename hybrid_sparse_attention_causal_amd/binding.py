@@ -187,9 +187,11 @@ def decode_block_topk(q, k, lens, raw, lse, topk, idx, grp_score=None, block=64,
     """Decode selection; idx [B,Hkv,topk(+n_recent)] int32."""
     _contig(raw, lse, idx, grp_score)
     s = decode_shape(q, k, lens, kv_scale)
+    need = workspace_size(HS_FN_BLOCK_TOPK, s, block, topk)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=raw.device) if need else None
     _check(load().hs_block_topk(ctypes.byref(s), _ptr(raw), _ptr(lse), block, topk, n_recent,
-                                HS_SEL_FULLY_PAST, _ptr(grp_score), _ptr(idx), None, 0,
-                                _stream(stream)))
+                                HS_SEL_FULLY_PAST, _ptr(grp_score), _ptr(idx), _ptr(ws),
+                                0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def decode_select_attn(q_sp, k, v, lens, idx, n_sel, k_ring, v_ring, window, gate_logits, o,

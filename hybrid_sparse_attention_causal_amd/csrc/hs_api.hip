@@ -82,8 +82,10 @@ hs_status check_decode(const char* fn, const hs_shape* s) {
     return fail(HS_ERR_INVALID_ARG, "%s: cache capacity kv_len=%d must be a positive multiple of 64", fn,
                 s->kv_len);
   if (s->dtype != HS_BF16) return fail(HS_ERR_UNSUPPORTED, "%s: decode query dtype must be HS_BF16", fn);
-  if (s->kv_dtype != HS_BF16)
+  if (s->kv_dtype != HS_BF16 && s->kv_dtype != HS_FP8_E4M3)
     return fail(HS_ERR_UNSUPPORTED, "%s: decode cache dtype %d is not available", fn, s->kv_dtype);
+  if (s->kv_dtype == HS_FP8_E4M3 && (!s->kv_scale || ((uintptr_t)s->kv_scale & 3u)))
+    return fail(HS_ERR_INVALID_ARG, "%s: fp8 caches need a 4-byte aligned kv_scale", fn);
   if (s->hq / s->hkv > 16) return fail(HS_ERR_UNSUPPORTED, "%s: decode group size > 16", fn);
   return HS_OK;
 }
@@ -96,6 +98,19 @@ int decode_nch(const hs_shape* s) {
 }
 size_t decode_full_ws(const hs_shape* s) {
   return (size_t)s->batch * s->hq * decode_nch(s) * (s->head_dim + 2) * sizeof(float);
+}
+size_t token_topk_ws(const hs_shape* s) {
+  return (size_t)s->batch * s->hkv * ((size_t)s->kv_len + 2048) * sizeof(uint32_t);
+}
+// Token mode (block = 1) runs on fp8 caches with position-major values; block
+// mode (block = 64) on bf16 caches with block-major values.
+hs_status check_decode_block(const char* fn, const hs_shape* s, int block) {
+  if (block != 64 && block != 1) return fail(HS_ERR_INVALID_ARG, "%s: decode block=%d (64 or 1)", fn, block);
+  if (block == 64 && s->kv_dtype != HS_BF16)
+    return fail(HS_ERR_UNSUPPORTED, "%s: block mode needs HS_BF16 caches", fn);
+  if (block == 1 && s->kv_dtype != HS_FP8_E4M3)
+    return fail(HS_ERR_UNSUPPORTED, "%s: token mode needs HS_FP8_E4M3 caches", fn);
+  return HS_OK;
 }
 
 float scale_log2(const hs_shape* s) {
@@ -122,6 +137,7 @@ size_t hs_workspace_size(int fn_id, const hs_shape* shape, int block, int topk, 
   (void)window;
   if (!shape || shape->struct_size < sizeof(hs_shape) || !shape->kv_lens) return 0;
   if (fn_id == HS_FN_FULL_ATTN) return decode_full_ws(shape);
+  if (fn_id == HS_FN_BLOCK_TOPK && block == 1) return token_topk_ws(shape);
   return 0;
 }
 
@@ -138,7 +154,8 @@ hs_status hs_full_attn_fwd_scores(const hs_shape* s, const void* q, const void* 
   if (s->kv_lens) {
     st = check_decode(fn, s);
     if (st) return st;
-    if (block != 64 && block != 1) return fail(HS_ERR_INVALID_ARG, "%s: decode block=%d (64 or 1)", fn, block);
+    st = check_decode_block(fn, s, block);
+    if (st) return st;
     if (flags != HS_SCORE_MAX) return fail(HS_ERR_UNSUPPORTED, "%s: decode supports HS_SCORE_MAX only", fn);
     if (s->batch == 0) return ok();
     REQUIRE_PTR(q);
@@ -167,6 +184,8 @@ hs_status hs_full_attn_fwd_scores(const hs_shape* s, const void* q, const void* 
     a.nch = decode_nch(s);
     a.ch_blocks = kDecodeChunkBlocks;
     a.token = block == 1;
+    a.kv_dtype = s->kv_dtype;
+    a.kv_scale = s->kv_scale;
     a.sc2 = scale_log2(s);
     return launched(fn, hs::launch_decode_full(a, s->head_dim, (hipStream_t)stream));
   }
@@ -208,12 +227,48 @@ hs_status hs_block_topk(const hs_shape* s, const float* blk_raw, const float* ls
   if (flags != HS_SEL_FULLY_PAST && flags != HS_SEL_INCLUDE_DIAG)
     return fail(HS_ERR_INVALID_ARG, "%s: flags=%d", fn, flags);
   if (n_recent < 0) return fail(HS_ERR_INVALID_ARG, "%s: n_recent < 0", fn);
-  if (block != 64) return fail(HS_ERR_UNSUPPORTED, "%s: block=%d is not available in this build", fn, block);
+  if (block == 1) {
+    // token-level selection (decode only)
+    st = check_decode(fn, s);
+    if (st) return st;
+    st = check_decode_block(fn, s, block);
+    if (st) return st;
+    if (flags != HS_SEL_FULLY_PAST) return fail(HS_ERR_INVALID_ARG, "%s: token mode takes no flags", fn);
+    if (topk < 1 || topk > 4096) return fail(HS_ERR_INVALID_ARG, "%s: topk=%d (1..4096 tokens)", fn, topk);
+    if (n_recent > 4096) return fail(HS_ERR_INVALID_ARG, "%s: n_recent=%d (0..4096)", fn, n_recent);
+    if (s->batch == 0) return ok();
+    REQUIRE_PTR(blk_raw);
+    REQUIRE_PTR(lse);
+    REQUIRE_PTR(idx);
+    if (grp_score && !aligned16(grp_score)) return fail(HS_ERR_INVALID_ARG, "%s: grp_score misaligned", fn);
+    const size_t need = token_topk_ws(s);
+    if (!ws || ws_bytes < need)
+      return fail(HS_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, need, ws_bytes);
+    if (!aligned16(ws)) return fail(HS_ERR_INVALID_ARG, "%s: ws not 16-byte aligned", fn);
+    hs::TokenTopkArgs a{};
+    a.raw = blk_raw;
+    a.lse = lse;
+    a.gs = grp_score;
+    a.idx = idx;
+    a.lens = s->kv_lens;
+    a.keys = (uint32_t*)ws;
+    a.hist = (uint32_t*)ws + (size_t)s->batch * s->hkv * s->kv_len;
+    a.B = s->batch;
+    a.Hq = s->hq;
+    a.Hkv = s->hkv;
+    a.C = s->kv_len;
+    a.kb = topk;
+    a.n_recent = n_recent;
+    return launched(fn, hs::launch_token_topk(a, (hipStream_t)stream));
+  }
+  if (block != 64) return fail(HS_ERR_INVALID_ARG, "%s: block=%d (64 or 1)", fn, block);
   if (topk < 1 || topk > 1024) return fail(HS_ERR_INVALID_ARG, "%s: topk=%d (1..1024 blocks)", fn, topk);
   if (n_recent != 0) return fail(HS_ERR_INVALID_ARG, "%s: n_recent applies to token mode only", fn);
   hs::TopkArgs a{};
   if (s->kv_lens) {
     st = check_decode(fn, s);
+    if (st) return st;
+    st = check_decode_block(fn, s, block);
     if (st) return st;
     a.R = 1;
     a.raw_stride = s->kv_len / 64;
@@ -296,8 +351,11 @@ hs_status hs_decode_select_attn(const hs_shape* s, const void* q_sp, const void*
   (void)ws_bytes;
   hs_status st = check_decode(fn, s);
   if (st) return st;
-  if (block != 64) return fail(HS_ERR_UNSUPPORTED, "%s: block=%d is not available", fn, block);
-  if (n_sel < 0 || n_sel > 4096) return fail(HS_ERR_INVALID_ARG, "%s: n_sel=%d (0..4096)", fn, n_sel);
+  st = check_decode_block(fn, s, block);
+  if (st) return st;
+  if (n_sel < 0 || n_sel > 8192) return fail(HS_ERR_INVALID_ARG, "%s: n_sel=%d (0..8192)", fn, n_sel);
+  if (block == 1 && (window != 0 || gate_logits))
+    return fail(HS_ERR_INVALID_ARG, "%s: token mode has no window branch and no gate", fn);
   if (window < 0 || window > s->kv_len) return fail(HS_ERR_INVALID_ARG, "%s: window=%d", fn, window);
   if (s->batch == 0) return ok();
   REQUIRE_PTR(q_sp);
@@ -329,7 +387,9 @@ hs_status hs_decode_select_attn(const hs_shape* s, const void* q_sp, const void*
   a.C = s->kv_len;
   a.nsel = n_sel;
   a.W = window;
+  a.kv_scale = s->kv_scale;
   a.sc2 = scale_log2(s);
+  if (block == 1) return launched(fn, hs::launch_decode_sparse_token(a, s->head_dim, (hipStream_t)stream));
   return launched(fn, hs::launch_decode_sparse(a, s->head_dim, (hipStream_t)stream));
 }
 

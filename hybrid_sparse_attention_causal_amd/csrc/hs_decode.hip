@@ -19,11 +19,16 @@ namespace hs {
 // ======================================================== split-K full layer
 // Unit (b, g, ch) covers keys [ch*CH*64, min(L, (ch+1)*CH*64)).  MFMA columns
 // 0..G-1 are the G query heads of kv group g (G <= 16).
-template <int D, int TOKEN>
+// KV = HS_BF16: key cache [C][D] and block-major value cache [C/64][D][64];
+// KV = HS_FP8_E4M3: position-major fp8 key and value caches [C][D] with one
+// scale per (K|V, kv head); the value fragments are byte-transposed in
+// registers (fp8_vfrag4), so their head_dim rows come in fp8_vrow_d order.
+template <int D, int TOKEN, int KV>
 __global__ __launch_bounds__(256) void decode_full_kernel(DecodeFullArgs a) {
   using Tt = Tr<HS_BF16>;
+  using Frag = Tt::Frag;
   using Eng = WaveAttn<HS_BF16, D, 1>;
-  constexpr int ES = 2;
+  constexpr int KES = KV == HS_FP8_E4M3 ? 1 : 2;  // cache bytes per element
   const int lane = threadIdx.x & 63;
   const long unit = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (unit >= (long)a.B * a.Hkv * a.nch) return;
@@ -39,6 +44,9 @@ __global__ __launch_bounds__(256) void decode_full_kernel(DecodeFullArgs a) {
   const int col = lane & 15;
   const int h = g * G + col;
   const int r16 = lane & 15, q8 = 8 * (lane >> 4);
+  const float sk = KV == HS_FP8_E4M3 ? a.kv_scale[g] : 1.f;
+  const float sv = KV == HS_FP8_E4M3 ? a.kv_scale[a.Hkv + g] : 1.f;
+  const float sc2 = a.sc2 * sk;
 
   Eng eng;
   eng.reset();
@@ -47,22 +55,38 @@ __global__ __launch_bounds__(256) void decode_full_kernel(DecodeFullArgs a) {
   hi[0] = L - 1;
 #pragma unroll
   for (int ks = 0; ks < Eng::NS; ++ks)
-    eng.qf[0][ks] = col < G ? Tt::ld((const char*)a.q + ((size_t)(b * a.Hq + h) * D + 32 * ks + q8) * ES)
+    eng.qf[0][ks] = col < G ? Tt::ld((const char*)a.q + ((size_t)(b * a.Hq + h) * D + 32 * ks + q8) * 2)
                             : Tt::zero();
-  const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * a.C * D * ES;
-  const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * (a.C / 64) * D * 64 * ES;
+  const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * a.C * D * KES;
+  const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * a.C * D * KES;
   float* rawrow = a.raw + (size_t)(b * a.Hq + h) * (TOKEN ? a.C : a.C / 64);
   const int q4 = (lane >> 4) << 2;
 
   for (int kb0 = kstart; kb0 < kend; kb0 += 64) {
     const bool partial = kb0 + 64 > L;
     const int j = kb0 >> 6;
+    Frag vc[4];
     auto ldK = [&](int c, int ks) {
       const int key = kb0 + tile_key(c, r16);
-      return (!partial || key < L) ? Tt::ld(kg + ((size_t)key * D + 32 * ks + q8) * ES) : Tt::zero();
+      if (partial && key >= L) return Tt::zero();
+      if (KV == HS_FP8_E4M3) return fp8x8_frag(*(const uint2*)(kg + (size_t)key * D + 32 * ks + q8));
+      return Tt::ld(kg + ((size_t)key * D + 32 * ks + q8) * 2);
     };
     auto ldV = [&](int u, int mc) {
-      const auto f = Tt::ld(vg + (((size_t)j * D + 16 * mc + r16) * 64 + 32 * u + q8) * ES);
+      if (KV == HS_FP8_E4M3) {
+        if ((mc & 3) == 0) {
+          uint32_t w[8];
+          const int key0 = kb0 + 32 * u + q8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            w[e] = (!partial || key0 + e < L)
+                       ? *(const uint32_t*)(vg + (size_t)(key0 + e) * D + 64 * (mc >> 2) + 4 * r16)
+                       : 0u;
+          fp8_vfrag4(w, vc);
+        }
+        return vc[mc & 3];
+      }
+      const auto f = Tt::ld(vg + (((size_t)j * D + 16 * mc + r16) * 64 + 32 * u + q8) * 2);
       return partial ? Tt::keep(f, L - (kb0 + 32 * u + q8)) : f;
     };
     float bmax[1], bsum[1];
@@ -83,20 +107,35 @@ __global__ __launch_bounds__(256) void decode_full_kernel(DecodeFullArgs a) {
           }
         }
       };
-      eng.template tile<true, false>(ldK, ldV, kb0, lo, hi, a.sc2, bmax, bsum, hook);
+      eng.template tile<true, false>(ldK, ldV, kb0, lo, hi, sc2, bmax, bsum, hook);
     } else {
-      eng.template tile<true, false>(ldK, ldV, kb0, lo, hi, a.sc2, bmax, bsum);
+      eng.template tile<true, false>(ldK, ldV, kb0, lo, hi, sc2, bmax, bsum);
       if (lane < 16 && col < G) rawrow[j] = bmax[0] * kLn2;
     }
   }
 
-  // partial state: unnormalised o (head_dim floats), m (log2 units), l
+  // partial state: unnormalised o (head_dim floats, natural order), m (log2), l
   float lt = eng.l[0] + __shfl_xor(eng.l[0], 16);
   lt += __shfl_xor(lt, 32);
   if (col < G) {
     float* pp = a.part + ((size_t)(b * a.Hq + h) * a.nch + ch) * (D + 2);
+    if (KV == HS_FP8_E4M3) {
+      // rows 4q+i of chunk mc hold head_dim 64*(mc>>2) + 16q + 4i + (mc&3)
 #pragma unroll
-    for (int mc = 0; mc < Eng::NM; ++mc) *(float4*)(pp + 16 * mc + q4) = *(const float4*)&eng.o[0][mc];
+      for (int hf = 0; hf < D / 64; ++hf) {
+        float v[16];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[4 * i + k] = eng.o[0][4 * hf + k][i] * sv;
+        float4* dst = (float4*)(pp + 64 * hf + 4 * q4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+      }
+    } else {
+#pragma unroll
+      for (int mc = 0; mc < Eng::NM; ++mc) *(float4*)(pp + 16 * mc + q4) = *(const float4*)&eng.o[0][mc];
+    }
     if (lane < 16) {
       pp[D] = eng.m[0];
       pp[D + 1] = lt;
@@ -270,17 +309,290 @@ __global__ __launch_bounds__(512) void decode_sparse_kernel(DecodeSparseArgs a) 
   }
 }
 
+// ========================================================= token-level top-k
+// HySparse2 explainer, "Precise retrieval without a separate indexer" and the
+// decode_one_token pseudocode: selected = newest n_recent tokens united with
+// the top-k older tokens by full-layer score.  The token score is the group
+// maximum of the post-softmax weights, x_i = max_h (logit_hi - LSE_h) in the
+// log domain.  Selection is a three-level radix select on the order-preserving
+// 32-bit key of x (11 + 11 + 10 bits), then one pass that emits the winners in
+// ascending token order, equal keys resolved towards the smaller token id.
+__device__ __forceinline__ uint32_t order_key_f(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* p, long n) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) p[i] = 0u;
+}
+
+// grid (rows, C/4096): keys for 4096 tokens and the level-1 histogram (top 11 bits)
+__global__ __launch_bounds__(256) void token_keys_kernel(TokenTopkArgs a) {
+  __shared__ uint32_t hist[2048];
+  const int row = blockIdx.x;
+  const int g = row % a.Hkv, b = row / a.Hkv;
+  const int L = a.lens[b];
+  const int ncand = max(0, L - a.n_recent);
+  const int G = a.Hq / a.Hkv;
+  for (int i = threadIdx.x; i < 2048; i += 256) hist[i] = 0u;
+  __syncthreads();
+  const int base = blockIdx.y * 4096;
+  float ls[16];
+  for (int hh = 0; hh < G; ++hh) ls[hh] = a.lse[(size_t)b * a.Hq + g * G + hh];
+  uint32_t* keys = a.keys + (size_t)row * a.C;
+  for (int n = 0; n < 16; ++n) {
+    const int i = base + threadIdx.x + 256 * n;
+    if (i >= a.C) break;
+    uint32_t key = 0u;
+    if (i < L) {
+      float x = -INFINITY;
+      for (int hh = 0; hh < G; ++hh)
+        x = fmaxf(x, a.raw[((size_t)b * a.Hq + g * G + hh) * a.C + i] - ls[hh]);
+      if (a.gs) a.gs[(size_t)row * a.C + i] = expf(x);
+      if (i < ncand) {
+        key = order_key_f(x);
+        atomicAdd(&hist[key >> 21], 1u);
+      }
+    }
+    keys[i] = key;
+  }
+  __syncthreads();
+  uint32_t* gh = a.hist + (size_t)row * 2048;
+  for (int i = threadIdx.x; i < 2048; i += 256)
+    if (hist[i]) atomicAdd(&gh[i], hist[i]);
+}
+
+// Block-wide search in a histogram of nb bins (nb = 1024 or 2048, 1024 threads):
+// the bin b with count(> b) < k <= count(>= b); returns b and count(> b).
+__device__ void find_bin(const uint32_t* h, int nb, int k, uint32_t* scan, int* res) {
+  const int t = threadIdx.x;
+  const int per = nb / 1024;
+  // thread t owns bins [nb - (t+1)*per, nb - t*per), i.e. descending order
+  uint32_t own = 0;
+  for (int e = 0; e < per; ++e) own += h[nb - t * per - 1 - e];
+  scan[t] = own;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const uint32_t v = t >= off ? scan[t - off] : 0u;
+    __syncthreads();
+    scan[t] += v;
+    __syncthreads();
+  }
+  const uint32_t incl = scan[t], excl = incl - own;
+  if (excl < (uint32_t)k && incl >= (uint32_t)k) {
+    uint32_t above = excl;
+    for (int e = 0; e < per; ++e) {
+      const int bin = nb - t * per - 1 - e;
+      if (above + h[bin] >= (uint32_t)k) {
+        res[0] = bin;
+        res[1] = (int)above;
+        break;
+      }
+      above += h[bin];
+    }
+  }
+  __syncthreads();
+}
+
+// one work group (1024 threads) per (sequence, kv group) row
+__global__ __launch_bounds__(1024) void token_select_kernel(TokenTopkArgs a) {
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t scan[1024];
+  __shared__ int res[2];
+  __shared__ uint32_t wsum[16];
+  const int row = blockIdx.x;
+  const int b = row / a.Hkv;
+  const int L = a.lens[b];
+  const int ncand = max(0, L - a.n_recent);
+  const int nrec = min(L, a.n_recent);
+  const int kb = a.kb;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const uint64_t lt_mask = lane ? (~0ull >> (64 - lane)) : 0ull;
+  const uint32_t* keys = a.keys + (size_t)row * a.C;
+  int32_t* out = a.idx + (size_t)row * (kb + a.n_recent);
+  int nsel;
+
+  if (ncand <= kb) {
+    for (int i = t; i < ncand; i += 1024) out[i] = i;
+    nsel = ncand;
+  } else {
+    // level 1: the global histogram of the top 11 bits
+    const uint32_t* gh = a.hist + (size_t)row * 2048;
+    for (int i = t; i < 2048; i += 1024) hist[i] = gh[i];
+    __syncthreads();
+    find_bin(hist, 2048, kb, scan, res);
+    const uint32_t b1 = (uint32_t)res[0];
+    int need = kb - res[1];
+    // level 2: bits 20..10 inside bin b1
+    for (int i = t; i < 2048; i += 1024) hist[i] = 0u;
+    __syncthreads();
+    for (int i = t; i < ncand; i += 1024) {
+      const uint32_t k = keys[i];
+      if ((k >> 21) == b1) atomicAdd(&hist[(k >> 10) & 2047u], 1u);
+    }
+    __syncthreads();
+    find_bin(hist, 2048, need, scan, res);
+    const uint32_t p2 = (b1 << 11) | (uint32_t)res[0];
+    need -= res[1];
+    // level 3: bits 9..0
+    for (int i = t; i < 1024; i += 1024) hist[i] = 0u;
+    __syncthreads();
+    for (int i = t; i < ncand; i += 1024) {
+      const uint32_t k = keys[i];
+      if ((k >> 10) == p2) atomicAdd(&hist[k & 1023u], 1u);
+    }
+    __syncthreads();
+    find_bin(hist, 1024, need, scan, res);
+    const uint32_t thr = (p2 << 10) | (uint32_t)res[0];
+    const int need_eq = need - res[1];  // >= 1 keys equal to thr are taken
+    // emit ascending: running counts of selected and of ties in token order
+    int sel_base = 0, tie_base = 0;
+    for (int c0 = 0; c0 < ncand; c0 += 1024) {
+      const int i = c0 + t;
+      const uint32_t k = i < ncand ? keys[i] : 0u;
+      const bool gt = i < ncand && k > thr;
+      const bool eq = i < ncand && k == thr;
+      const uint64_t em = __ballot(eq);
+      if (lane == 0) wsum[w] = (uint32_t)__popcll(em);
+      __syncthreads();
+      int tie_before = tie_base;
+      for (int x = 0; x < w; ++x) tie_before += wsum[x];
+      int tie_total = tie_base;
+      for (int x = 0; x < 16; ++x) tie_total += wsum[x];
+      const int rank = tie_before + __popcll(em & lt_mask);
+      const bool s = gt || (eq && rank < need_eq);
+      __syncthreads();
+      const uint64_t sm = __ballot(s);
+      if (lane == 0) wsum[w] = (uint32_t)__popcll(sm);
+      __syncthreads();
+      int pos = sel_base;
+      for (int x = 0; x < w; ++x) pos += wsum[x];
+      int sel_total = sel_base;
+      for (int x = 0; x < 16; ++x) sel_total += wsum[x];
+      if (s) out[pos + __popcll(sm & lt_mask)] = i;
+      sel_base = sel_total;
+      tie_base = tie_total;
+      __syncthreads();
+    }
+    nsel = kb;
+  }
+  for (int r = t; r < nrec; r += 1024) out[nsel + r] = L - nrec + r;
+  for (int r = nsel + nrec + t; r < kb + a.n_recent; r += 1024) out[r] = -1;
+}
+
+// ============================================ token-level sparse layer (fp8)
+// One work group (8 waves) per (b, g); work items are tiles of 64 consecutive
+// entries of the ascending token list (-1 padding at the end).  Keys and
+// values of the selected tokens are gathered straight from the fp8 caches;
+// no window branch and no gate (the newest tokens are part of the list).
+template <int D>
+__global__ __launch_bounds__(512) void decode_sparse_token_kernel(DecodeSparseArgs a) {
+  using Tt = Tr<HS_BF16>;
+  using Frag = Tt::Frag;
+  using Eng = WaveAttn<HS_BF16, D, 1>;
+  constexpr int NW = 8;
+  __shared__ float sm_m[NW][16], sm_l[NW][16];
+  __shared__ __attribute__((aligned(16))) float sm_o[NW][16][D];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int bg = blockIdx.x;
+  const int g = bg % a.Hkv, b = bg / a.Hkv;
+  const int L = a.lens[b];
+  const int G = a.Hq / a.Hkv;
+  const int col = lane & 15;
+  const int h = g * G + col;
+  const int r16 = lane & 15, q8 = 8 * (lane >> 4), q4 = (lane >> 4) << 2;
+  const float sk = a.kv_scale[g], sv = a.kv_scale[a.Hkv + g];
+  const float sc2 = a.sc2 * sk;
+
+  Eng eng;
+  eng.reset();
+#pragma unroll
+  for (int ks = 0; ks < Eng::NS; ++ks)
+    eng.qf[0][ks] = col < G ? Tt::ld((const char*)a.q + ((size_t)(b * a.Hq + h) * D + 32 * ks + q8) * 2)
+                            : Tt::zero();
+  const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * a.C * D;
+  const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * a.C * D;
+  const int32_t* il = a.idx + (size_t)(b * a.Hkv + g) * a.nsel;
+  const int ntile = (a.nsel + 63) / 64;
+  float bmax[1], bsum[1];
+  int lo[1], hi[1];
+
+  for (int it = w; it < ntile; it += NW) {
+    const int s0 = 64 * it;
+    int tok = s0 + lane < a.nsel ? il[s0 + lane] : -1;
+    if (tok >= L) tok = -1;
+    const int nvalid = __popcll(__ballot(tok >= 0));  // valid entries form a prefix
+    if (nvalid == 0) continue;
+    lo[0] = col < G ? 0 : kNoKey;
+    hi[0] = s0 + nvalid - 1;
+    Frag vc[4];
+    auto ldK = [&](int c, int ks) {
+      const int tk = __shfl(tok, tile_key(c, r16));
+      return tk >= 0 ? fp8x8_frag(*(const uint2*)(kg + (size_t)tk * D + 32 * ks + q8)) : Tt::zero();
+    };
+    auto ldV = [&](int u, int mc) {
+      if ((mc & 3) == 0) {
+        uint32_t wv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tk = __shfl(tok, 32 * u + q8 + e);
+          wv[e] = tk >= 0 ? *(const uint32_t*)(vg + (size_t)tk * D + 64 * (mc >> 2) + 4 * r16) : 0u;
+        }
+        fp8_vfrag4(wv, vc);
+      }
+      return vc[mc & 3];
+    };
+    eng.template tile<true, false>(ldK, ldV, s0, lo, hi, sc2, bmax, bsum);
+  }
+
+  float lt = eng.l[0] + __shfl_xor(eng.l[0], 16);
+  lt += __shfl_xor(lt, 32);
+  if (lane < 16) {
+    sm_m[w][col] = eng.m[0];
+    sm_l[w][col] = lt;
+  }
+#pragma unroll
+  for (int hf = 0; hf < D / 64; ++hf) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm_o[w][col][fp8_vrow_d(4 * hf + k, q4 + i)] = eng.o[0][4 * hf + k][i];
+  }
+  __syncthreads();
+  for (int el = threadIdx.x; el < G * D; el += 64 * NW) {
+    const int c = el / D, d = el % D;
+    float M = kNegBig;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww][c]);
+    float ls = 0.f, os = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float wt = fast_exp2(sm_m[ww][c] - M);
+      ls += wt * sm_l[ww][c];
+      os += wt * sm_o[ww][c][d];
+    }
+    ((uint16_t*)a.o)[((size_t)b * a.Hq + g * G + c) * D + d] = (uint16_t)bf16_bits(ls > 0.f ? sv * os / ls : 0.f);
+  }
+}
+
 // ================================================================ launchers
+template <int D>
+static void decode_full_dispatch(const DecodeFullArgs& a, dim3 grid, hipStream_t s) {
+  if (a.kv_dtype == HS_FP8_E4M3) {
+    if (a.token) hipLaunchKernelGGL((decode_full_kernel<D, 1, HS_FP8_E4M3>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((decode_full_kernel<D, 0, HS_FP8_E4M3>), grid, dim3(256), 0, s, a);
+  } else {
+    if (a.token) hipLaunchKernelGGL((decode_full_kernel<D, 1, HS_BF16>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((decode_full_kernel<D, 0, HS_BF16>), grid, dim3(256), 0, s, a);
+  }
+}
+
 hipError_t launch_decode_full(const DecodeFullArgs& a, int D, hipStream_t s) {
   const long units = (long)a.B * a.Hkv * a.nch;
   dim3 grid((unsigned)((units + 3) / 4));
-  if (D == 128) {
-    if (a.token) hipLaunchKernelGGL((decode_full_kernel<128, 1>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((decode_full_kernel<128, 0>), grid, dim3(256), 0, s, a);
-  } else {
-    if (a.token) hipLaunchKernelGGL((decode_full_kernel<64, 1>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((decode_full_kernel<64, 0>), grid, dim3(256), 0, s, a);
-  }
+  if (D == 128) decode_full_dispatch<128>(a, grid, s);
+  else decode_full_dispatch<64>(a, grid, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2((unsigned)(((long)a.B * a.Hq + 3) / 4));
@@ -293,6 +605,30 @@ hipError_t launch_decode_sparse(const DecodeSparseArgs& a, int D, hipStream_t s)
   dim3 grid((unsigned)(a.B * a.Hkv));
   if (D == 128) hipLaunchKernelGGL(decode_sparse_kernel<128>, grid, dim3(512), 0, s, a);
   else hipLaunchKernelGGL(decode_sparse_kernel<64>, grid, dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace hs
+
+namespace hs {
+
+hipError_t launch_token_topk(const TokenTopkArgs& a, hipStream_t s) {
+  const long rows = (long)a.B * a.Hkv;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(256), dim3(256), 0, s, a.hist, rows * 2048);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(token_keys_kernel, dim3((unsigned)rows, (unsigned)((a.C + 4095) / 4096)), dim3(256), 0,
+                     s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(token_select_kernel, dim3((unsigned)rows), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_sparse_token(const DecodeSparseArgs& a, int D, hipStream_t s) {
+  dim3 grid((unsigned)(a.B * a.Hkv));
+  if (D == 128) hipLaunchKernelGGL(decode_sparse_token_kernel<128>, grid, dim3(512), 0, s, a);
+  else hipLaunchKernelGGL(decode_sparse_token_kernel<64>, grid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -143,6 +143,55 @@ template <> struct Tr<HS_F32> {
   }
 };
 
+// ---------------------------------------------------------- fp8 e4m3 caches
+// v_cvt_pk_f32_fp8 decodes OCP e4m3fn exactly on gfx950 (every code checked
+// against an independent table); e4m3 values are exact in bf16, so a decoded
+// code feeds the bf16 MFMA without rounding.
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_bf16x2(uint32_t w) {
+  const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+  return bf16_bits(f[0]) | (bf16_bits(f[1]) << 16);
+}
+
+// 8 fp8 codes (byte e = element e) -> bf16 fragment of 8 elements
+__device__ __forceinline__ Tr<HS_BF16>::Frag fp8x8_frag(uint2 c) {
+  Tr<HS_BF16>::Frag f;
+  f.u = make_uint4(fp8x2_bf16x2<false>(c.x), fp8x2_bf16x2<true>(c.x), fp8x2_bf16x2<false>(c.y),
+                   fp8x2_bf16x2<true>(c.y));
+  return f;
+}
+
+// Value fragments from a position-major fp8 cache.  Lane (q, r) of key step u
+// loads the dword w[e] = V[key0 + e][dbase + 4r .. +3] of 8 consecutive keys
+// (key0 = kbase + 32u + 8q).  A 4x4 byte transpose of w[0..3] and of w[4..7]
+// yields, for k = 0..3, the 8 codes of head_dim row dbase + 4r + k over the 8
+// keys: the A fragment of O^T row chunk mc = 4*(dbase/64) + k, whose row r is
+// head_dim dbase + 4r + k (a permuted head_dim order, undone when storing).
+__device__ __forceinline__ void fp8_vfrag4(const uint32_t* w, Tr<HS_BF16>::Frag* out) {
+  uint32_t t[2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t w0 = w[4 * h], w1 = w[4 * h + 1], w2 = w[4 * h + 2], w3 = w[4 * h + 3];
+    const uint32_t p = __builtin_amdgcn_perm(w1, w0, 0x05010400u);  // w0.0 w1.0 w0.1 w1.1
+    const uint32_t q = __builtin_amdgcn_perm(w1, w0, 0x07030602u);  // w0.2 w1.2 w0.3 w1.3
+    const uint32_t r = __builtin_amdgcn_perm(w3, w2, 0x05010400u);  // w2.0 w3.0 w2.1 w3.1
+    const uint32_t s = __builtin_amdgcn_perm(w3, w2, 0x07030602u);  // w2.2 w3.2 w2.3 w3.3
+    t[h][0] = __builtin_amdgcn_perm(r, p, 0x05040100u);  // byte 0 of w0..w3
+    t[h][1] = __builtin_amdgcn_perm(r, p, 0x07060302u);  // byte 1
+    t[h][2] = __builtin_amdgcn_perm(s, q, 0x05040100u);  // byte 2
+    t[h][3] = __builtin_amdgcn_perm(s, q, 0x07060302u);  // byte 3
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) out[k] = fp8x8_frag(make_uint2(t[0][k], t[1][k]));
+}
+
+// head_dim index held in row m of O^T chunk mc under the fp8 value order
+__host__ __device__ __forceinline__ int fp8_vrow_d(int mc, int m) {
+  return 64 * (mc >> 2) + 4 * m + (mc & 3);
+}
+
 // ------------------------------------------------------------- the engine
 // One wavefront, NT column tiles of 16 query columns each, head_dim D.
 // Online softmax state per column tile: running maximum m (log2 units, already

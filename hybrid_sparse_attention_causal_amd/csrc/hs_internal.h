@@ -59,6 +59,8 @@ struct DecodeFullArgs {
   int nch;                // chunks per sequence at capacity
   int ch_blocks;          // 64-key blocks per chunk
   int token;              // 1: raw holds per-token logits; 0: per-block maxima
+  int kv_dtype;           // HS_BF16 (block-major V) or HS_FP8_E4M3 (position-major V)
+  const float* kv_scale;  // fp8: device [2][Hkv]
   float sc2;
 };
 
@@ -72,9 +74,24 @@ struct DecodeSparseArgs {
   const float* gates;
   void* o;
   const int32_t* lens;
+  const float* kv_scale;  // fp8 token mode: device [2][Hkv]
   int B, Hq, Hkv, C, nsel, W;
   float sc2;
 };
+
+struct TokenTopkArgs {
+  const float* raw;       // [B][Hq][C] per-token logits
+  const float* lse;       // [B][Hq]
+  float* gs;              // nullable [B][Hkv][C]
+  int32_t* idx;           // [B][Hkv][kb + n_recent]
+  const int32_t* lens;
+  uint32_t* keys;         // workspace [B*Hkv][C]
+  uint32_t* hist;         // workspace [B*Hkv][2048]
+  int B, Hq, Hkv, C, kb, n_recent;
+};
+
+hipError_t launch_token_topk(const TokenTopkArgs& a, hipStream_t s);
+hipError_t launch_decode_sparse_token(const DecodeSparseArgs& a, int D, hipStream_t s);
 
 hipError_t launch_decode_full(const DecodeFullArgs& a, int D, hipStream_t s);
 hipError_t launch_decode_sparse(const DecodeSparseArgs& a, int D, hipStream_t s);

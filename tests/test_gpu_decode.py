@@ -124,3 +124,118 @@ def test_config4_full_size_sampled():
     inp = gen.make_decode(gen.config(4), n_layers=2)
     run = DecodeRun(inp)
     check_sequences(run, [0, 21, 42, 63])
+
+
+# --------------------------------------------------------------- token level
+class TokenRun:
+    """Token-level decode (fp8 e4m3 caches, position-major): full layer with
+    per-token logits, top-k tokens + the newest n_recent, sparse layers."""
+
+    def __init__(self, inp, n_layers=None):
+        cfg = inp.cfg
+        self.cfg, self.inp = cfg, inp
+        B, Hq, Hkv, C, d = cfg.B, cfg.Hq, cfg.Hkv, cfg.T, cfg.d
+        R, kb = cfg.n_recent, cfg.kb
+        kc = np.empty((B, Hkv, C, d), np.uint8)
+        vc = np.empty((B, Hkv, C, d), np.uint8)
+        gen.fill_decode_cache(inp, kc, vc, v_block_major=False)
+        self.k, self.v = dev(kc), dev(vc)
+        del kc, vc
+        self.scale = dev(inp.kv_scale)
+        self.lens = torch.from_numpy(inp.lens.astype(np.int32)).cuda()
+        q = dev(inp.q)
+        self.o = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.full((B, Hq), float("nan"), device="cuda")
+        self.raw = torch.full((B, Hq, C), float("nan"), device="cuda")
+        hb.decode_full_attn_scores(q, self.k, self.v, self.lens, self.o, self.lse, self.raw,
+                                   block=1, kv_scale=self.scale)
+        self.idx = torch.full((B, Hkv, kb + R), -7, dtype=torch.int32, device="cuda")
+        self.gs = torch.full((B, Hkv, C), float("nan"), device="cuda")
+        hb.decode_block_topk(q, self.k, self.lens, self.raw, self.lse, kb, self.idx, self.gs,
+                             block=1, n_recent=R, kv_scale=self.scale)
+        self.outs = []
+        for lay in (inp.layers if n_layers is None else inp.layers[:n_layers]):
+            o = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+            hb.decode_select_attn(dev(lay["q"]), self.k, self.v, self.lens, self.idx, kb + R,
+                                  None, None, 0, None, o, block=1, kv_scale=self.scale)
+            self.outs.append(o)
+        torch.cuda.synchronize()
+
+
+def check_token_sequences(run, seqs, rel=1e-4):
+    cfg, inp = run.cfg, run.inp
+    R, kb = cfg.n_recent, cfg.kb
+    o_g, lse_g, raw_g = host(run.o), host(run.lse), host(run.raw)
+    idx_g, gs_g = host(run.idx), host(run.gs)
+    outs_g = [host(o) for o in run.outs]
+    worst = dict(o=0.0, lse=0.0, raw=0.0, layer=0.0, gs=0.0)
+    ties = 0
+    for b in seqs:
+        L = int(inp.lens[b])
+        ks, vs = zip(*(inp.kv_slab(b, g) for g in range(cfg.Hkv)))
+        k, v = np.stack(ks), np.stack(vs)
+        ref = ora.decode_step(f64_bf16(inp.q[b]), k, v, L, [], kb, 0, block=1, n_recent=R,
+                              kv_scale=inp.kv_scale.astype(np.float64))
+        worst["o"] = max(worst["o"], np.abs(o_g[b] - ref["o"]).max())
+        worst["lse"] = max(worst["lse"], np.abs(lse_g[b] - ref["lse"]).max())
+        worst["raw"] = max(worst["raw"], np.abs(raw_g[b][:, :L] - ref["raw"][:, :L]).max())
+        worst["gs"] = max(worst["gs"], (np.abs(gs_g[b][:, :L] - ref["Sg"][:, :L]) /
+                                        ref["Sg"][:, :L].max()).max())
+        ncand = max(0, L - R)
+        for g in range(cfg.Hkv):
+            row = idx_g[b, g]
+            want = ref["idx"][g]
+            n_out = min(kb, ncand) + min(R, L)
+            assert np.all(row[n_out:] == -1) and np.all(np.diff(row[:n_out]) > 0), (b, g)
+            assert np.array_equal(row[n_out - min(R, L):n_out], np.arange(L - min(R, L), L))
+            ranked = ref["ranked"][g]
+            if ncand > kb:
+                sk, sk1 = ranked[kb - 1], ranked[kb]
+                if (sk - sk1) / sk < rel:
+                    ties += 1
+                    got = row[: n_out - min(R, L)]
+                    Sg = ref["Sg"][g]
+                    cand = np.arange(ncand)
+                    must = cand[Sg[cand] > sk * (1 + rel)]
+                    banned = cand[Sg[cand] < sk * (1 - rel)]
+                    assert np.all(np.isin(must, got)) and not np.any(np.isin(banned, got)), (b, g)
+                    continue
+            assert np.array_equal(row[:n_out], want[:n_out]), (b, g)
+        for l in range(len(run.outs)):
+            lay = dict(q=f64_bf16(inp.layers[l]["q"][b]))
+            want = ora.decode_sparse_layer(lay, k, v, L, idx_g[b].astype(np.int64), 0, block=1,
+                                           kv_scale=inp.kv_scale.astype(np.float64))
+            worst["layer"] = max(worst["layer"], np.abs(outs_g[l][b] - want).max())
+    say(f"  seqs={list(seqs)} max|dO|={worst['o']:.3g} max|dLSE|={worst['lse']:.3g} "
+        f"max|draw|={worst['raw']:.3g} rel|dSg|={worst['gs']:.3g} "
+        f"sparse max|dO|={worst['layer']:.3g} near-tie={ties}")
+    tol = TOL["fp8"]
+    assert worst["o"] <= tol and worst["layer"] <= tol
+    assert worst["lse"] <= SIDE_TOL and worst["raw"] <= SIDE_TOL and worst["gs"] < 1e-4
+    assert not np.isnan(o_g).any() and all(not np.isnan(x).any() for x in outs_g)
+
+
+def test_token_small_ragged():
+    say("[token small] fp8, C=4096, top-256 + 16 recent")
+    cfg = gen.config(5, B=4, T=4096, Hq=8, Hkv=2, d=128, kb=256, n_recent=16, N=2,
+                     L_lo=1, L_hi=4096)
+    inp = gen.make_decode(cfg)
+    inp.lens = np.array([1, 200, 300, 4096], np.int32)
+    run = TokenRun(inp)
+    check_token_sequences(run, range(4))
+
+
+def test_token_d64_group16():
+    say("[token d=64 G=16]")
+    cfg = gen.config(5, B=2, T=8192, Hq=16, Hkv=1, d=64, kb=100, n_recent=128, N=1,
+                     L_lo=5000, L_hi=8192)
+    inp = gen.make_decode(cfg)
+    run = TokenRun(inp)
+    check_token_sequences(run, range(2))
+
+
+def test_config5_token_level_full_size_sampled():
+    say("[config 5] 16 seqs x 262144 fp8 tokens, top-2048 + 128 recent (layers 0-1 of 11)")
+    inp = gen.make_decode(gen.config(5), n_layers=2)
+    run = TokenRun(inp)
+    check_token_sequences(run, [0, 7, 15])
