@@ -120,7 +120,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_ref:
+        import torch
+
+        n = args.copy_ref << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_ref_bytes": n, "launches": 3}))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the kernels shard by kv group with no exchange, see the design notes)",

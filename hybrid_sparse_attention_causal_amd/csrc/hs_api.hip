@@ -307,8 +307,9 @@ hs_status hs_sparse_attn_fwd(const hs_shape* s, const void* q_sp, const void* k,
   if (topk < 0 || topk > 1024) return fail(HS_ERR_INVALID_ARG, "%s: topk=%d (0..1024)", fn, topk);
   if (window < 0) return fail(HS_ERR_INVALID_ARG, "%s: window < 0", fn);
   if (s->batch == 0 || s->q_len == 0) return ok();
-  if ((long long)(s->q_len + 63) / 64 > (1 << 16))
-    return fail(HS_ERR_UNSUPPORTED, "%s: more than 65536 blocks", fn);
+  if (s->hq / s->hkv > 16) return fail(HS_ERR_UNSUPPORTED, "%s: group size > 16", fn);
+  if (hs::sparse_prefill_lds_bytes(s->q_len, s->hq / s->hkv) > 48 * 1024)
+    return fail(HS_ERR_UNSUPPORTED, "%s: sequence too long for the selection bitsets", fn);
   REQUIRE_PTR(q_sp);
   REQUIRE_PTR(o);
   if (topk > 0) {

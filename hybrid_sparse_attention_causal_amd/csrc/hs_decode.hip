@@ -115,8 +115,7 @@ __global__ __launch_bounds__(256) void decode_full_kernel(DecodeFullArgs a) {
   }
 
   // partial state: unnormalised o (head_dim floats, natural order), m (log2), l
-  float lt = eng.l[0] + __shfl_xor(eng.l[0], 16);
-  lt += __shfl_xor(lt, 32);
+  const float lt = xlane_sum(eng.l[0]);
   if (col < G) {
     float* pp = a.part + ((size_t)(b * a.Hq + h) * a.nch + ch) * (D + 2);
     if (KV == HS_FP8_E4M3) {
@@ -270,8 +269,7 @@ __global__ __launch_bounds__(512) void decode_sparse_kernel(DecodeSparseArgs a) 
 #pragma unroll
   for (int br = 0; br < 2; ++br) {
     Eng& e = br ? sw : sp;
-    float lt = e.l[0] + __shfl_xor(e.l[0], 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = xlane_sum(e.l[0]);
     if (lane < 16) {
       sm_m[w][col] = e.m[0];
       sm_l[w][col] = lt;
@@ -546,8 +544,7 @@ __global__ __launch_bounds__(512) void decode_sparse_token_kernel(DecodeSparseAr
     eng.template tile<true, false>(ldK, ldV, s0, lo, hi, sc2, bmax, bsum);
   }
 
-  float lt = eng.l[0] + __shfl_xor(eng.l[0], 16);
-  lt += __shfl_xor(lt, 32);
+  const float lt = xlane_sum(eng.l[0]);
   if (lane < 16) {
     sm_m[w][col] = eng.m[0];
     sm_l[w][col] = lt;

@@ -28,6 +28,8 @@
 namespace hs {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -35,6 +37,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1.0e30f;
 constexpr int kBlk = 64;
 constexpr int kNoKey = 0x7fffffff;
+constexpr float kSlack = 8.f;  // see WaveAttn::tile
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
@@ -50,8 +53,28 @@ __host__ __device__ __forceinline__ int tile_row(int kk) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Reductions over the four lanes {l, l^16, l^32, l^48} that hold one MFMA
+// column, with the gfx950 row-swap instructions (no LDS traffic).  Every
+// lane of the group gets the same result.
+__device__ __forceinline__ float xlane_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float xlane_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+// two floats -> packed bf16 pair (RNE), one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // ----------------------------------------------------------- element traits
@@ -87,13 +110,12 @@ template <> struct Tr<HS_BF16> {
   }
   __device__ __forceinline__ static Frag pack(const float* p) {
     Frag f;
-    f.u = make_uint4(bf16_bits(p[0]) | (bf16_bits(p[1]) << 16), bf16_bits(p[2]) | (bf16_bits(p[3]) << 16),
-                     bf16_bits(p[4]) | (bf16_bits(p[5]) << 16), bf16_bits(p[6]) | (bf16_bits(p[7]) << 16));
+    f.u = make_uint4(bf16x2_bits(p[0], p[1]), bf16x2_bits(p[2], p[3]), bf16x2_bits(p[4], p[5]),
+                     bf16x2_bits(p[6], p[7]));
     return f;
   }
   __device__ __forceinline__ static void store4(void* dst, float a, float b, float c, float d) {
-    *reinterpret_cast<uint2*>(dst) =
-        make_uint2(bf16_bits(a) | (bf16_bits(b) << 16), bf16_bits(c) | (bf16_bits(d) << 16));
+    *reinterpret_cast<uint2*>(dst) = make_uint2(bf16x2_bits(a, b), bf16x2_bits(c, d));
   }
 };
 
@@ -152,7 +174,7 @@ typedef __attribute__((ext_vector_type(2))) float f32x2;
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_bf16x2(uint32_t w) {
   const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
-  return bf16_bits(f[0]) | (bf16_bits(f[1]) << 16);
+  return bf16x2_bits(f[0], f[1]);
 }
 
 // 8 fp8 codes (byte e = element e) -> bf16 fragment of 8 elements
@@ -191,6 +213,113 @@ __device__ __forceinline__ void fp8_vfrag4(const uint32_t* w, Tr<HS_BF16>::Frag*
 __host__ __device__ __forceinline__ int fp8_vrow_d(int mc, int m) {
   return 64 * (mc >> 2) + 4 * m + (mc & 3);
 }
+
+// ------------------------------------------------------ LDS tile staging
+// A 64-key tile (K rows + the matching [D][64] value tile) staged through LDS
+// by NTHR threads: `gload` issues the global loads into registers, `sstore`
+// writes them to one LDS buffer.  K rows are stored in S^T row order
+// (tile_row).  Both tiles are unpadded; the 16-byte chunk c of row r is
+// stored at chunk c ^ (r & SW), SW = min(chunks per row, 16) - 1.  Measured
+// with the LDS bank-conflict counter on gfx950, this swizzle makes the
+// fragment reads (16 rows x 4 chunks per wavefront) conflict-free, whereas
+// padded row strides of 272 and 144 bytes conflict.  Keys at or after `nk`
+// read as zero.
+template <int DT, int D, int NTHR>
+struct TileStage {
+  using T = Tr<DT>;
+  using Frag = typename T::Frag;
+  static constexpr int ES = T::ES;
+  static constexpr int KCH = D * ES / 16;   // 16-byte chunks per K row
+  static constexpr int VCH = 64 * ES / 16;  // chunks per value row
+  static constexpr int KS = D * ES;
+  static constexpr int VS = 64 * ES;
+  static constexpr int KSW = (KCH < 16 ? KCH : 16) - 1;
+  static constexpr int VSW = (VCH < 16 ? VCH : 16) - 1;
+  static constexpr int KB = 64 * KS;
+  static constexpr int VB = D * VS;
+  static constexpr int BYTES = KB + VB;
+  static constexpr int NK = 64 * KCH / NTHR;
+  static constexpr int NV = D * VCH / NTHR;
+  static_assert(NK * NTHR == 64 * KCH && NV * NTHR == D * VCH, "tile does not split evenly");
+  uint4 kr[NK], vr[NV];
+
+  __device__ __forceinline__ static int k_lds(int row, int chunk) {
+    return row * KS + ((chunk ^ (row & KSW)) << 4);
+  }
+  __device__ __forceinline__ static int v_lds(int row, int chunk) {
+    return KB + row * VS + ((chunk ^ (row & VSW)) << 4);
+  }
+
+  // krows: key row 0 of the tile (row stride D elements); vslab: [D][64] tile;
+  // nk: number of valid keys in the tile (>= 64 means all)
+  __device__ __forceinline__ void gload(const char* krows, const char* vslab, int nk) {
+#pragma unroll
+    for (int n = 0; n < NK; ++n) {
+      const int ci = threadIdx.x + NTHR * n;
+      const int kk = ci / KCH, col = ci % KCH;
+      kr[n] = kk < nk ? *(const uint4*)(krows + kk * KS + col * 16) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      const int ci = threadIdx.x + NTHR * n;
+      const int dd = ci / VCH, col = ci % VCH;
+      uint4 x = *(const uint4*)(vslab + dd * VS + col * 16);
+      const int k0 = col * (16 / ES);
+      if (k0 + 16 / ES > nk) {
+        uint32_t w[4] = {x.x, x.y, x.z, x.w};
+        const int keep = nk - k0;  // elements kept
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e0 = i * 4 / ES;  // first element of word i
+          if (e0 >= keep) w[i] = 0u;
+          else if (ES == 2 && e0 + 1 >= keep) w[i] &= 0xffffu;
+        }
+        x = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      vr[n] = x;
+    }
+  }
+  __device__ __forceinline__ void sstore(char* buf) const {
+#pragma unroll
+    for (int n = 0; n < NK; ++n) {
+      const int ci = threadIdx.x + NTHR * n;
+      *(uint4*)(buf + k_lds(tile_row(ci / KCH), ci % KCH)) = kr[n];
+    }
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      const int ci = threadIdx.x + NTHR * n;
+      *(uint4*)(buf + v_lds(ci / VCH, ci % VCH)) = vr[n];
+    }
+  }
+  // A fragment of S^T chunk c, k-step ks: row 16c + r, elements 32ks + 8q .. +7
+  __device__ __forceinline__ static Frag ldK(const char* buf, int c, int ks) {
+    const int lane = lane_id();
+    const int row = 16 * c + (lane & 15);
+    const int ch = (32 * ks + 8 * (lane >> 4)) * ES / 16;
+    if constexpr (ES == 2) {
+      return T::ld(buf + k_lds(row, ch));
+    } else {
+      Frag f;
+      f.a = *(const float4*)(buf + k_lds(row, ch));
+      f.b = *(const float4*)(buf + k_lds(row, ch + 1));
+      return f;
+    }
+  }
+  // A fragment of O^T chunk mc, key step u: value row 16mc + r, keys 32u + 8q .. +7
+  __device__ __forceinline__ static Frag ldV(const char* buf, int u, int mc) {
+    const int lane = lane_id();
+    const int row = 16 * mc + (lane & 15);
+    const int ch = (32 * u + 8 * (lane >> 4)) * ES / 16;
+    if constexpr (ES == 2) {
+      return T::ld(buf + v_lds(row, ch));
+    } else {
+      Frag f;
+      f.a = *(const float4*)(buf + v_lds(row, ch));
+      f.b = *(const float4*)(buf + v_lds(row, ch + 1));
+      return f;
+    }
+  }
+};
 
 // ------------------------------------------------------------- the engine
 // One wavefront, NT column tiles of 16 query columns each, head_dim D.
@@ -233,6 +362,8 @@ struct WaveAttn {
 
   // `hook(nt, x)` sees the lane's 16 masked, scaled logits (log2 units; x[4c+i]
   // belongs to key kbase + tile_key(c, 4q+i)) before the exponentials.
+  // Masking is decided per wavefront: only when some column's [lo, hi] does
+  // not cover the whole tile are keys compared one by one.
   template <bool MASK, bool WANT_SUM, class LK, class LV, class HK = NoHook>
   __device__ __forceinline__ void tile(const LK& ldK, const LV& ldV, int kbase, const int* lo,
                                        const int* hi, float sc2, float* bmax, float* bsum,
@@ -253,7 +384,24 @@ struct WaveAttn {
         for (int nt = 0; nt < NT; ++nt) T::mma(s[nt][c], a, qf[nt][ks]);
       }
     }
+    // masking: a column with lo == kNoKey is switched off (one select per
+    // value); key-by-key range checks only when some live column's [lo, hi]
+    // does not cover the tile
+    bool ranged = false, off = false;
+    if (MASK) {
+      bool part = false, dis = false;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const bool en = lo[nt] != kNoKey;
+        dis = dis || !en;
+        part = part || (en && (kbase < lo[nt] || kbase + 63 > hi[nt]));
+      }
+      ranged = __ballot(part) != 0ull;
+      off = __ballot(dis) != 0ull;
+    }
     Frag pf[NT][2];
+    bool rescale = false;
+    float alpha[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float x[16];
@@ -262,38 +410,50 @@ struct WaveAttn {
       for (int c = 0; c < 4; ++c) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float v = s[nt][c][i] * sc2;
-          if (MASK) {
+          float v = s[nt][c][i];
+          if (MASK && ranged) {
             const int key = kbase + tile_key(c, q4 + i);
             if (key < lo[nt] || key > hi[nt]) v = -INFINITY;
+          } else if (MASK && off) {
+            if (lo[nt] == kNoKey) v = -INFINITY;
           }
           x[4 * c + i] = v;
           mx = fmaxf(mx, v);
         }
       }
-      hook(nt, x);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if constexpr (!__is_same(HK, NoHook)) {
+        float xs[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xs[e] = x[e] * sc2;
+        hook(nt, xs);
+      }
+      mx = xlane_max(mx) * sc2;  // raw logits are unscaled; sc2 > 0
       bmax[nt] = mx;
-      const float mn = fmaxf(m[nt], mx);
-      const float alpha = fast_exp2(m[nt] - mn);
+      // The running maximum is only raised when the tile exceeds it by more
+      // than kSlack (log2 units): the exponentials then stay <= 2^kSlack, exact
+      // enough in fp32 and bf16, and the O rescale is rare.  m + log2(l) is
+      // the LSE whichever maximum is kept.
+      const bool up = mx > m[nt] + kSlack;
+      const float mn = up ? mx : m[nt];
+      alpha[nt] = up ? fast_exp2(m[nt] - mn) : 1.f;
+      rescale = rescale || up;
       m[nt] = mn;
       float ps = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        x[e] = fast_exp2(x[e] - mn);
+        x[e] = fast_exp2(__builtin_fmaf(x[e], sc2, -mn));
         ps += x[e];
       }
-      l[nt] = l[nt] * alpha + ps;
-      if (WANT_SUM) {
-        float bs = ps + __shfl_xor(ps, 16);
-        bs += __shfl_xor(bs, 32);
-        bsum[nt] = bs;
-      }
-#pragma unroll
-      for (int mc = 0; mc < NM; ++mc) o[nt][mc] *= alpha;
+      l[nt] = l[nt] * alpha[nt] + ps;
+      if (WANT_SUM) bsum[nt] = xlane_sum(ps);
       pf[nt][0] = T::pack(x);
       pf[nt][1] = T::pack(x + 8);
+    }
+    if (__ballot(rescale) != 0ull) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mc = 0; mc < NM; ++mc) o[nt][mc] *= alpha[nt];
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -308,8 +468,7 @@ struct WaveAttn {
 
   // Column totals: 1/l (0 when the column saw no key) and the log2-domain LSE.
   __device__ __forceinline__ void finish(int nt, float& inv_l, float& lse2) const {
-    float lt = l[nt] + __shfl_xor(l[nt], 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = xlane_sum(l[nt]);
     inv_l = lt > 0.f ? 1.f / lt : 0.f;
     lse2 = lt > 0.f ? m[nt] + fast_log2(lt) : -INFINITY;
   }

@@ -100,5 +100,7 @@ hipError_t launch_full_prefill(const FullPrefillArgs& a, int dtype, int D, int s
                                hipStream_t s);
 hipError_t launch_block_topk(const TopkArgs& a, int max_blocks, hipStream_t s);
 hipError_t launch_sparse_prefill(const SparsePrefillArgs& a, int dtype, int D, hipStream_t s);
+// dynamic LDS of the sparse prefill kernel (bitsets + block list)
+size_t sparse_prefill_lds_bytes(int T, int G);
 
 }  // namespace hs

@@ -13,19 +13,6 @@
 
 namespace hs {
 
-__device__ __forceinline__ uint4 keep_u4(uint4 v, int n_keep, int es) {
-  // zero the 16-byte chunk's elements with index >= n_keep (es = element bytes)
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  const int nb = n_keep * es;  // bytes kept
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int b0 = 4 * i;
-    if (b0 >= nb) w[i] = 0u;
-    else if (b0 + 4 > nb) w[i] &= (1u << (8 * (nb - b0))) - 1u;
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
 // ===================================================================== full
 // Work group = 4 wavefronts.  With Gw = min(G, 4) query heads of one kv group
 // per work group, wave w takes head hb*Gw + w%Gw and 16*NT consecutive query
@@ -38,14 +25,10 @@ template <int DT, int D, int NT, int SCORE_LSE>
 __global__ __launch_bounds__(256, (DT == HS_F32 && D == 128) ? 1 : 2) void full_prefill_kernel(FullPrefillArgs a) {
   using Tt = Tr<DT>;
   using Eng = WaveAttn<DT, D, NT>;
+  using St = TileStage<DT, D, 256>;
   constexpr int ES = Tt::ES;
-  constexpr int KS = D * ES + 16;   // LDS row stride (bytes) of the K tile
-  constexpr int VS = 64 * ES + 16;  // LDS row stride of the d-major V tile
-  constexpr int KB = 64 * KS, VB = D * VS;
-  constexpr int KCH = D * ES / 16, VCH = 64 * ES / 16;  // 16-byte chunks per row
-  constexpr int NK = 64 * KCH / 256, NV = D * VCH / 256;
   constexpr int PWAVE = 16 * NT;
-  __shared__ __attribute__((aligned(16))) char smem[2 * (KB + VB)];
+  __shared__ __attribute__((aligned(16))) char smem[2 * St::BYTES];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int G = a.Hq / a.Hkv;
@@ -65,42 +48,8 @@ __global__ __launch_bounds__(256, (DT == HS_F32 && D == 128) ? 1 : 2) void full_
 
   const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * T * D * ES;
   const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
-
-  uint4 kreg[NK], vreg[NV];
-  auto gload = [&](int j) {
-#pragma unroll
-    for (int n = 0; n < NK; ++n) {
-      const int ci = threadIdx.x + 256 * n;
-      const int kk = ci / KCH, col = ci % KCH;
-      const int key = 64 * j + kk;
-      kreg[n] = key < T ? *(const uint4*)(kg + (size_t)key * D * ES + col * 16) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int n = 0; n < NV; ++n) {
-      const int ci = threadIdx.x + 256 * n;
-      const int dd = ci / VCH, col = ci % VCH;
-      uint4 x = *(const uint4*)(vg + ((size_t)j * D + dd) * 64 * ES + col * 16);
-      const int k0 = 64 * j + col * (16 / ES);
-      if (k0 + 16 / ES > T) x = keep_u4(x, T - k0, ES);
-      vreg[n] = x;
-    }
-  };
-  auto sstore = [&](int buf) {
-    char* ksm = smem + buf * (KB + VB);
-    char* vsm = ksm + KB;
-#pragma unroll
-    for (int n = 0; n < NK; ++n) {
-      const int ci = threadIdx.x + 256 * n;
-      const int kk = ci / KCH, col = ci % KCH;
-      *(uint4*)(ksm + tile_row(kk) * KS + col * 16) = kreg[n];
-    }
-#pragma unroll
-    for (int n = 0; n < NV; ++n) {
-      const int ci = threadIdx.x + 256 * n;
-      const int dd = ci / VCH, col = ci % VCH;
-      *(uint4*)(vsm + dd * VS + col * 16) = vreg[n];
-    }
-  };
+  St st;
+  auto gload = [&](int j) { st.gload(kg + (size_t)64 * j * D * ES, vg + (size_t)j * D * 64 * ES, T - 64 * j); };
 
   Eng eng;
   eng.reset();
@@ -119,20 +68,14 @@ __global__ __launch_bounds__(256, (DT == HS_F32 && D == 128) ? 1 : 2) void full_
   }
 
   gload(0);
-  sstore(0);
+  st.sstore(smem);
   __syncthreads();
   for (int j = 0; j <= jmax; ++j) {
-    const int buf = j & 1;
+    const char* buf = smem + (j & 1) * St::BYTES;
     if (j < jmax) gload(j + 1);
     if (64 * j <= plast) {
-      const char* ksm = smem + buf * (KB + VB);
-      const char* vsm = ksm + KB;
-      auto ldK = [&](int c, int ks) {
-        return Tt::ld(ksm + (16 * c + (lane & 15)) * KS + (32 * ks + 8 * (lane >> 4)) * ES);
-      };
-      auto ldV = [&](int u, int mc) {
-        return Tt::ld(vsm + (16 * mc + (lane & 15)) * VS + (32 * u + 8 * (lane >> 4)) * ES);
-      };
+      auto ldK = [&](int c, int ks) { return St::ldK(buf, c, ks); };
+      auto ldV = [&](int u, int mc) { return St::ldV(buf, u, mc); };
       float bmax[NT], bsum[NT];
       if (64 * j + 63 > p0)
         eng.template tile<true, SCORE_LSE != 0>(ldK, ldV, 64 * j, lo, hi, a.sc2, bmax, bsum);
@@ -149,7 +92,7 @@ __global__ __launch_bounds__(256, (DT == HS_F32 && D == 128) ? 1 : 2) void full_
         }
       }
     }
-    if (j < jmax) sstore(buf ^ 1);
+    if (j < jmax) st.sstore(smem + ((j + 1) & 1) * St::BYTES);
     __syncthreads();
   }
 
@@ -263,21 +206,26 @@ __global__ __launch_bounds__(256) void block_topk_kernel(TopkArgs a) {
 }
 
 // ==================================================================== sparse
-// One wavefront per (sequence, kv group, P consecutive query positions) with
-// P = 16*NT/G, so its 16*NT MFMA columns are the G heads of P positions.  The
-// wave walks the union of its positions' selected blocks in ascending order
-// (a bitset in LDS), gathering each 64-key block of the shared K/V straight
-// from global memory into MFMA operands; columns whose position did not select
-// a block are masked.  The window branch then runs over keys
-// [t0-W+1, t0+P-1] of the layer's own K'/V' with per-column masks, and the
-// two normalised branches are merged by the sigmoid gates.
-template <int DT, int D, int NT>
-__global__ __launch_bounds__(256, 2) void sparse_prefill_kernel(SparsePrefillArgs a) {
+// One work group of NW wavefronts per (sequence, kv group, NW*P consecutive
+// query positions), P = 16/G: wave w owns positions t0 + wP .. t0 + wP + P-1,
+// and its 16 MFMA columns are the G heads of those P positions.
+// The work group walks, in ascending order, the union of the blocks its
+// positions selected (bitsets in LDS), then the 64-key blocks of the layer's
+// own K'/V' that cover its windows.  Each block is loaded once per work group
+// into a double-buffered LDS tile (the next block's global loads are in
+// flight while the current one is computed); a wave computes a block only if
+// one of its positions selected it (window: if it overlaps one of its
+// windows), masking the columns that did not.  The two normalised branches are
+// merged by the sigmoid gates.
+template <int DT, int D, int NW>
+__global__ __launch_bounds__(64 * NW, (DT == HS_F32 && D == 128) ? 1 : 2)
+void sparse_prefill_kernel(SparsePrefillArgs a) {
   using Tt = Tr<DT>;
-  using Eng = WaveAttn<DT, D, NT>;
-  using Frag = typename Tt::Frag;
+  using Eng = WaveAttn<DT, D, 1>;
+  using St = TileStage<DT, D, 64 * NW>;
   constexpr int ES = Tt::ES;
-  extern __shared__ uint32_t shbits[];
+  __shared__ __attribute__((aligned(16))) char tiles[2 * St::BYTES];
+  extern __shared__ uint32_t dyn[];
 
   // XCD-aware remap: consecutive ids go round-robin over the 8 XCDs; give each
   // XCD a contiguous range of work groups (same kv group -> shared L2).
@@ -288,151 +236,156 @@ __global__ __launch_bounds__(256, 2) void sparse_prefill_kernel(SparsePrefillArg
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int T = a.T;
   const int G = a.Hq / a.Hkv;
-  const int P = 16 * NT / G;
-  const int npg = (T + P - 1) / P;
-  const int npg4 = (npg + 3) >> 2;
-  const int bg = wgid / npg4;
+  const int P = 16 / G;
+  const int PWG = NW * P;
+  const int nwg_bg = (T + PWG - 1) / PWG;
+  const int bg = wgid / nwg_bg;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
-  const int pg = (wgid % npg4) * 4 + w;
-  const int t0 = pg * P;
+  const int t0 = (wgid % nwg_bg) * PWG;
+  const int tw0 = t0 + w * P;
   const int nw32 = (a.nblk + 31) >> 5;
-  uint32_t* U = shbits + w * (1 + P) * nw32;
-  uint32_t* S = U + nw32;
+  uint32_t* U = dyn;                      // union of the work group
+  uint32_t* Uw = U + nw32;                // union of each wave  [NW][nw32]
+  uint32_t* S = Uw + NW * nw32;           // selection of each position [PWG][nw32]
+  int* ulist = (int*)(S + PWG * nw32);    // ascending union, then its length
+  int* nu_p = ulist + a.nblk;
 
-  for (int i = lane; i < (1 + P) * nw32; i += 64) U[i] = 0u;
+  for (int i = threadIdx.x; i < (1 + NW + PWG) * nw32; i += 64 * NW) U[i] = 0u;
   __syncthreads();
   if (live) {
-    for (int e = lane; e < P * a.topk; e += 64) {
+    for (int e = threadIdx.x; e < PWG * a.topk; e += 64 * NW) {
       const int p = e / a.topk;
       const int t = t0 + p;
       if (t < T) {
         const int j = a.idx[((size_t)(b * a.Hkv + g) * T + t) * a.topk + (e % a.topk)];
-        if (j >= 0 && j < a.nblk) {
-          atomicOr(&U[j >> 5], 1u << (j & 31));
-          atomicOr(&S[p * nw32 + (j >> 5)], 1u << (j & 31));
+        if (j >= 0 && j < a.nblk && 64 * j <= t) {
+          const uint32_t bit = 1u << (j & 31);
+          atomicOr(&U[j >> 5], bit);
+          atomicOr(&Uw[(p / P) * nw32 + (j >> 5)], bit);
+          atomicOr(&S[p * nw32 + (j >> 5)], bit);
         }
       }
     }
   }
   __syncthreads();
-  if (!live || t0 >= T) return;
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int wi = 0; wi < nw32; ++wi) {
+      uint32_t word = U[wi];
+      while (word) {
+        ulist[n++] = wi * 32 + __builtin_ctz(word);
+        word &= word - 1;
+      }
+    }
+    *nu_p = n;
+  }
+  __syncthreads();
+  const int nu = live ? *nu_p : 0;
+  int jw0 = 0, nwin = 0;
+  if (live && a.W > 0) {
+    jw0 = max(0, t0 - a.W + 1) >> 6;
+    nwin = (min(T - 1, t0 + PWG - 1) >> 6) - jw0 + 1;
+  }
+  const int nitems = nu + nwin;
 
-  int tcol[NT], hcol[NT], pcol[NT];
+  // per-lane column: position tcol (of this wave), head hcol
+  const int col = lane & 15;
+  const int pcol = col / G;
+  const int tcol = tw0 + pcol;
+  const int hcol = g * G + col % G;
   Eng eng;
   eng.reset();
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int col = 16 * nt + (lane & 15);
-    pcol[nt] = col / G;
-    tcol[nt] = t0 + pcol[nt];
-    hcol[nt] = g * G + col % G;
-#pragma unroll
-    for (int ks = 0; ks < Eng::NS; ++ks) {
-      eng.qf[nt][ks] = tcol[nt] < T
-                           ? Tt::ld((const char*)a.q +
-                                    (((size_t)(b * T + tcol[nt]) * a.Hq + hcol[nt]) * D + 32 * ks + 8 * (lane >> 4)) * ES)
-                           : Tt::zero();
-    }
-  }
+  for (int ks = 0; ks < Eng::NS; ++ks)
+    eng.qf[0][ks] = (live && tcol < T)
+                        ? Tt::ld((const char*)a.q +
+                                 (((size_t)(b * T + tcol) * a.Hq + hcol) * D + 32 * ks + 8 * (lane >> 4)) * ES)
+                        : Tt::zero();
 
   const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * T * D * ES;
   const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
-  const int r16 = lane & 15, q8 = 8 * (lane >> 4);
-  int lo[NT], hi[NT];
-  float bmax[NT], bsum[NT];
+  const char* ksg = (const char*)a.ks + (size_t)(b * a.Hkv + g) * T * D * ES;
+  const char* vsg = (const char*)a.vs + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
+  // two register stages: the global loads of item i+2 are in flight while
+  // item i is computed and item i+1 is written to LDS
+  St st0, st1;
+  auto issue = [&](St& st, int i) {
+    const bool win = i >= nu;
+    const int j = win ? jw0 + (i - nu) : ulist[i];
+    st.gload((win ? ksg : kg) + (size_t)64 * j * D * ES, (win ? vsg : vg) + (size_t)j * D * 64 * ES,
+             T - 64 * j);
+  };
 
-  // ---- branch 1: gathered blocks of the shared K/V
-  for (int wi = 0; wi < nw32; ++wi) {
-    uint32_t word = __builtin_amdgcn_readfirstlane(U[wi]);
-    while (word) {
-      const int bit = __builtin_ctz(word);
-      word &= word - 1;
-      const int j = wi * 32 + bit;
-      const int kbase = 64 * j;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const bool sel = (S[pcol[nt] * nw32 + wi] >> bit) & 1u;
-        lo[nt] = sel ? 0 : kNoKey;
-        hi[nt] = tcol[nt] < T ? tcol[nt] : -1;
-      }
-      const bool full = kbase + 64 <= T;
-      auto ldK = [&](int c, int ks) {
-        const int key = kbase + tile_key(c, r16);
-        return (full || key < T) ? Tt::ld(kg + ((size_t)key * D + 32 * ks + q8) * ES) : Tt::zero();
-      };
-      auto ldV = [&](int u, int mc) {
-        const Frag f = Tt::ld(vg + (((size_t)j * D + 16 * mc + r16) * 64 + 32 * u + q8) * ES);
-        if (full) return f;
-        const int k0 = kbase + 32 * u + q8;
-        return Tt::keep(f, T - k0);
-      };
-      eng.template tile<true, false>(ldK, ldV, kbase, lo, hi, a.sc2, bmax, bsum);
-    }
+  f32x4 acc[Eng::NM];
+  float gate0 = 1.f, gate1 = 1.f;
+  if (a.gates && live && tcol < T) {
+    const float2 gl = *(const float2*)(a.gates + ((size_t)(b * T + tcol) * a.Hq + hcol) * 2);
+    gate0 = 1.f / (1.f + expf(-gl.x));
+    gate1 = 1.f / (1.f + expf(-gl.y));
   }
-
-  // normalise branch 1 and apply its gate
-  f32x4 acc[NT][Eng::NM];
-  float gw[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+  auto fold = [&](float gate, bool first) {
     float inv, l2;
-    eng.finish(nt, inv, l2);
-    float g0 = 1.f, g1 = 1.f;
-    if (a.gates && tcol[nt] < T) {
-      const float2 gl = *(const float2*)(a.gates + ((size_t)(b * T + tcol[nt]) * a.Hq + hcol[nt]) * 2);
-      g0 = 1.f / (1.f + expf(-gl.x));
-      g1 = 1.f / (1.f + expf(-gl.y));
-    }
-    gw[nt] = g1;
-    const float s0 = inv * g0;
+    eng.finish(0, inv, l2);
+    const float sc = inv * gate;
 #pragma unroll
-    for (int mc = 0; mc < Eng::NM; ++mc) acc[nt][mc] = eng.o[nt][mc] * s0;
-  }
+    for (int mc = 0; mc < Eng::NM; ++mc) acc[mc] = first ? eng.o[0][mc] * sc : acc[mc] + eng.o[0][mc] * sc;
+  };
 
-  // ---- branch 2: sliding window over the layer's own K'/V'
-  if (a.W > 0) {
-    eng.reset();
-    const char* ksg = (const char*)a.ks + (size_t)(b * a.Hkv + g) * T * D * ES;
-    const char* vsg = (const char*)a.vs + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
-    const int wlo = max(0, t0 - a.W + 1);
-    const int whi = min(T - 1, t0 + P - 1);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      lo[nt] = tcol[nt] - a.W + 1;
-      hi[nt] = tcol[nt] < T ? tcol[nt] : -1;
-    }
-    for (int kbase = wlo & ~7; kbase <= whi; kbase += 64) {
-      auto ldK = [&](int c, int ks) {
-        const int key = kbase + tile_key(c, r16);
-        return key < T ? Tt::ld(ksg + ((size_t)key * D + 32 * ks + q8) * ES) : Tt::zero();
-      };
-      auto ldV = [&](int u, int mc) {
-        const int k0 = kbase + 32 * u + q8;
-        if (k0 >= T) return Tt::zero();
-        const Frag f = Tt::ld(vsg + (((size_t)(k0 >> 6) * D + 16 * mc + r16) * 64 + (k0 & 63)) * ES);
-        return k0 + 8 <= T ? f : Tt::keep(f, T - k0);
-      };
-      eng.template tile<true, false>(ldK, ldV, kbase, lo, hi, a.sc2, bmax, bsum);
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float inv, l2;
-      eng.finish(nt, inv, l2);
-      const float s1 = inv * gw[nt];
-#pragma unroll
-      for (int mc = 0; mc < Eng::NM; ++mc) acc[nt][mc] += eng.o[nt][mc] * s1;
-    }
+  if (nitems > 0) {
+    issue(st0, 0);
+    st0.sstore(tiles);
   }
-
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    if (tcol[nt] < T) {
-      char* op = (char*)a.o + (((size_t)(b * T + tcol[nt]) * a.Hq + hcol[nt]) * D + 4 * (lane >> 4)) * ES;
-#pragma unroll
-      for (int mc = 0; mc < Eng::NM; ++mc) {
-        const f32x4 v = acc[nt][mc];
-        Tt::store4(op + 16 * mc * ES, v[0], v[1], v[2], v[3]);
+  if (nitems > 1) issue(st1, 1);
+  __syncthreads();
+  float bmax[1], bsum[1];
+  int lo[1], hi[1];
+  const int hicol = tcol < T ? tcol : -1;
+  auto step = [&](int i, St& ld_into, const St& store_from) {
+    if (i == nu) {
+      fold(gate0, true);
+      eng.reset();
+    }
+    if (i + 2 < nitems) issue(ld_into, i + 2);
+    const char* buf = tiles + (i & 1) * St::BYTES;
+    auto ldK = [&](int c, int ks) { return St::ldK(buf, c, ks); };
+    auto ldV = [&](int u, int mc) { return St::ldV(buf, u, mc); };
+    if (i < nu) {
+      const int j = ulist[i];
+      const bool mine = (__builtin_amdgcn_readfirstlane(Uw[w * nw32 + (j >> 5)]) >> (j & 31)) & 1u;
+      if (mine) {
+        const bool sel = (S[(w * P + pcol) * nw32 + (j >> 5)] >> (j & 31)) & 1u;
+        lo[0] = sel ? 0 : kNoKey;
+        hi[0] = hicol;
+        eng.template tile<true, false>(ldK, ldV, 64 * j, lo, hi, a.sc2, bmax, bsum);
       }
+    } else {
+      const int j = jw0 + (i - nu);
+      const bool mine = tw0 < T && 64 * j <= tw0 + P - 1 && 64 * j + 63 >= tw0 - a.W + 1;
+      if (mine) {
+        lo[0] = tcol - a.W + 1;
+        hi[0] = hicol;
+        eng.template tile<true, false>(ldK, ldV, 64 * j, lo, hi, a.sc2, bmax, bsum);
+      }
+    }
+    if (i + 1 < nitems) store_from.sstore(tiles + ((i + 1) & 1) * St::BYTES);
+    __syncthreads();
+  };
+  for (int i = 0; i < nitems; i += 2) {
+    step(i, st0, st1);
+    if (i + 1 < nitems) step(i + 1, st1, st0);
+  }
+  if (nu == nitems) {  // no window tiles: the sparse branch is still open
+    fold(gate0, true);
+  } else {
+    fold(gate1, false);
+  }
+
+  if (live && tcol < T) {
+    char* op = (char*)a.o + (((size_t)(b * T + tcol) * a.Hq + hcol) * D + 4 * (lane >> 4)) * ES;
+#pragma unroll
+    for (int mc = 0; mc < Eng::NM; ++mc) {
+      const f32x4 v = acc[mc];
+      Tt::store4(op + 16 * mc * ES, v[0], v[1], v[2], v[3]);
     }
   }
 }
@@ -470,27 +423,30 @@ hipError_t launch_block_topk(const TopkArgs& a, int max_blocks, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DT, int D, int NT>
+constexpr int kSparseWaves = 8;  // waves per work group of the sparse prefill kernel
+
+template <int DT, int D>
 static hipError_t sparse_dispatch(SparsePrefillArgs a, hipStream_t s) {
+  constexpr int NW = kSparseWaves;
   const int G = a.Hq / a.Hkv;
-  const int P = 16 * NT / G;
-  const int npg = (a.T + P - 1) / P;
-  const int npg4 = (npg + 3) / 4;
-  a.nwg = a.B * a.Hkv * npg4;
+  const int P = 16 / G;
+  const int PWG = NW * P;
+  a.nwg = a.B * a.Hkv * ((a.T + PWG - 1) / PWG);
   const int per = (a.nwg + 7) / 8;
-  const size_t lds = (size_t)4 * (1 + P) * ((a.nblk + 31) / 32) * sizeof(uint32_t);
-  hipLaunchKernelGGL((sparse_prefill_kernel<DT, D, NT>), dim3(8 * per), dim3(256), lds, s, a);
+  const int nw32 = (a.nblk + 31) / 32;
+  const size_t lds = ((size_t)(1 + NW + PWG) * nw32 + a.nblk + 1) * sizeof(uint32_t);
+  hipLaunchKernelGGL((sparse_prefill_kernel<DT, D, NW>), dim3(8 * per), dim3(64 * NW), lds, s, a);
   return hipGetLastError();
 }
 
+size_t sparse_prefill_lds_bytes(int T, int G) {
+  const int nblk = (T + 63) / 64, nw32 = (nblk + 31) / 32, PWG = kSparseWaves * (16 / G);
+  return ((size_t)(1 + kSparseWaves + PWG) * nw32 + nblk + 1) * sizeof(uint32_t);
+}
+
 hipError_t launch_sparse_prefill(const SparsePrefillArgs& a, int dtype, int D, hipStream_t s) {
-  const int G = a.Hq / a.Hkv;
-  if (G <= 16) {
-    if (dtype == HS_BF16) return D == 64 ? sparse_dispatch<HS_BF16, 64, 1>(a, s) : sparse_dispatch<HS_BF16, 128, 1>(a, s);
-    return D == 64 ? sparse_dispatch<HS_F32, 64, 1>(a, s) : sparse_dispatch<HS_F32, 128, 1>(a, s);
-  }
-  if (dtype == HS_BF16) return D == 64 ? sparse_dispatch<HS_BF16, 64, 2>(a, s) : sparse_dispatch<HS_BF16, 128, 2>(a, s);
-  return D == 64 ? sparse_dispatch<HS_F32, 64, 2>(a, s) : sparse_dispatch<HS_F32, 128, 2>(a, s);
+  if (dtype == HS_BF16) return D == 64 ? sparse_dispatch<HS_BF16, 64>(a, s) : sparse_dispatch<HS_BF16, 128>(a, s);
+  return D == 64 ? sparse_dispatch<HS_F32, 64>(a, s) : sparse_dispatch<HS_F32, 128>(a, s);
 }
 
 }  // namespace hs
