@@ -347,46 +347,41 @@ struct WaveAttn {
     }
   }
 
-  // Process one 64-key tile whose first key has absolute index kbase.
-  //   ldK(c, s)  -> A fragment of S^T chunk c, k-step s (key kbase+tile_key(c, r))
-  //   ldV(u, mc) -> A fragment of O^T chunk mc, key step u (keys kbase+32u+8q..+7)
-  //   lo[nt], hi[nt]: inclusive absolute key range valid for the lane's column
-  //   (lo = kNoKey disables the column for this tile).
-  //   sc2 = softmax scale * log2(e).
-  // Outputs per column tile: bmax = max scaled logit of the tile (log2 units,
-  // -inf when no key is valid) and, when WANT_SUM, bsum = sum over the tile of
-  // exp2(logit - m_new) (m_new = running max after this tile).
   struct NoHook {
     __device__ __forceinline__ void operator()(int, const float*) const {}
   };
 
-  // `hook(nt, x)` sees the lane's 16 masked, scaled logits (log2 units; x[4c+i]
-  // belongs to key kbase + tile_key(c, 4q+i)) before the exponentials.
-  // Masking is decided per wavefront: only when some column's [lo, hi] does
-  // not cover the whole tile are keys compared one by one.
-  template <bool MASK, bool WANT_SUM, class LK, class LV, class HK = NoHook>
-  __device__ __forceinline__ void tile(const LK& ldK, const LV& ldV, int kbase, const int* lo,
-                                       const int* hi, float sc2, float* bmax, float* bsum,
-                                       const HK& hook = HK()) {
-    const int lane = lane_id();
-    const int q4 = (lane >> 4) << 2;
-    f32x4 s[NT][4];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) s[nt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // S^T of one 64-key tile: s[nt][c] (rows = keys tile_key(c, 4q+i), column = lane's).
+  template <class LK>
+  __device__ __forceinline__ void qk(const LK& ldK, f32x4 (&s)[NT][4]) const {
 #pragma unroll
     for (int ks = 0; ks < NS; ++ks) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const Frag a = ldK(c, ks);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) T::mma(s[nt][c], a, qf[nt][ks]);
+        for (int nt = 0; nt < NT; ++nt) {
+          if (ks == 0) {
+            s[nt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+          T::mma(s[nt][c], a, qf[nt][ks]);
+        }
       }
     }
-    // masking: a column with lo == kNoKey is switched off (one select per
-    // value); key-by-key range checks only when some live column's [lo, hi]
-    // does not cover the tile
+  }
+
+  // Online-softmax update with the logits s of a tile, then O += P V.
+  // `hook(nt, x)` sees the lane's 16 masked, scaled logits (log2 units; x[4c+i]
+  // belongs to key kbase + tile_key(c, 4q+i)) before the exponentials.
+  // Masking is decided per wavefront: a column with lo == kNoKey is switched
+  // off (one select per value); key-by-key range checks only when some live
+  // column's [lo, hi] does not cover the whole tile.
+  template <bool MASK, bool WANT_SUM, class LV, class HK = NoHook>
+  __device__ __forceinline__ void softmax_pv(f32x4 (&s)[NT][4], const LV& ldV, int kbase, const int* lo,
+                                             const int* hi, float sc2, float* bmax, float* bsum,
+                                             const HK& hook = HK()) {
+    const int lane = lane_id();
+    const int q4 = (lane >> 4) << 2;
     bool ranged = false, off = false;
     if (MASK) {
       bool part = false, dis = false;
@@ -464,6 +459,23 @@ struct WaveAttn {
         for (int nt = 0; nt < NT; ++nt) T::mma(o[nt][mc], a, pf[nt][u]);
       }
     }
+  }
+
+  // One whole 64-key tile whose first key has absolute index kbase.
+  //   ldK(c, s)  -> A fragment of S^T chunk c, k-step s (key kbase+tile_key(c, r))
+  //   ldV(u, mc) -> A fragment of O^T chunk mc, key step u (keys kbase+32u+8q..+7)
+  //   lo[nt], hi[nt]: inclusive absolute key range valid for the lane's column
+  //   (lo = kNoKey disables the column for this tile); sc2 = scale * log2(e).
+  // Outputs per column tile: bmax = max scaled logit of the tile (log2 units,
+  // -inf when no key is valid) and, when WANT_SUM, bsum = sum over the tile of
+  // exp2(logit - m_new) (m_new = running max after this tile).
+  template <bool MASK, bool WANT_SUM, class LK, class LV, class HK = NoHook>
+  __device__ __forceinline__ void tile(const LK& ldK, const LV& ldV, int kbase, const int* lo,
+                                       const int* hi, float sc2, float* bmax, float* bsum,
+                                       const HK& hook = HK()) {
+    f32x4 s[NT][4];
+    qk(ldK, s);
+    softmax_pv<MASK, WANT_SUM>(s, ldV, kbase, lo, hi, sc2, bmax, bsum, hook);
   }
 
   // Column totals: 1/l (0 when the column saw no key) and the log2-domain LSE.

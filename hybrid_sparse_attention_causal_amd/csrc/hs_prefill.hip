@@ -206,22 +206,21 @@ __global__ __launch_bounds__(256) void block_topk_kernel(TopkArgs a) {
 }
 
 // ==================================================================== sparse
-// One work group of NW wavefronts per (sequence, kv group, NW*P consecutive
-// query positions), P = 16/G: wave w owns positions t0 + wP .. t0 + wP + P-1,
-// and its 16 MFMA columns are the G heads of those P positions.
+// One work group of NW wavefronts per (sequence, kv group, NW*PW consecutive
+// query positions), PW = 16*NT/G: wave w owns positions t0 + w*PW .. +PW-1,
+// and its 16*NT MFMA columns are the G heads of those positions.
 // The work group walks, in ascending order, the union of the blocks its
 // positions selected (bitsets in LDS), then the 64-key blocks of the layer's
 // own K'/V' that cover its windows.  Each block is loaded once per work group
-// into a double-buffered LDS tile (the next block's global loads are in
+// into a double-buffered LDS tile (the global loads of the next items are in
 // flight while the current one is computed); a wave computes a block only if
 // one of its positions selected it (window: if it overlaps one of its
 // windows), masking the columns that did not.  The two normalised branches are
 // merged by the sigmoid gates.
-template <int DT, int D, int NW>
-__global__ __launch_bounds__(64 * NW, (DT == HS_F32 && D == 128) ? 1 : 2)
-void sparse_prefill_kernel(SparsePrefillArgs a) {
+template <int DT, int D, int NT, int NW, int NSTAGE>
+__global__ __launch_bounds__(64 * NW, 2) void sparse_prefill_kernel(SparsePrefillArgs a) {
   using Tt = Tr<DT>;
-  using Eng = WaveAttn<DT, D, 1>;
+  using Eng = WaveAttn<DT, D, NT>;
   using St = TileStage<DT, D, 64 * NW>;
   constexpr int ES = Tt::ES;
   __shared__ __attribute__((aligned(16))) char tiles[2 * St::BYTES];
@@ -236,13 +235,13 @@ void sparse_prefill_kernel(SparsePrefillArgs a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int T = a.T;
   const int G = a.Hq / a.Hkv;
-  const int P = 16 / G;
-  const int PWG = NW * P;
+  const int PW = 16 * NT / G;
+  const int PWG = NW * PW;
   const int nwg_bg = (T + PWG - 1) / PWG;
   const int bg = wgid / nwg_bg;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
   const int t0 = (wgid % nwg_bg) * PWG;
-  const int tw0 = t0 + w * P;
+  const int tw0 = t0 + w * PW;
   const int nw32 = (a.nblk + 31) >> 5;
   uint32_t* U = dyn;                      // union of the work group
   uint32_t* Uw = U + nw32;                // union of each wave  [NW][nw32]
@@ -261,23 +260,34 @@ void sparse_prefill_kernel(SparsePrefillArgs a) {
         if (j >= 0 && j < a.nblk && 64 * j <= t) {
           const uint32_t bit = 1u << (j & 31);
           atomicOr(&U[j >> 5], bit);
-          atomicOr(&Uw[(p / P) * nw32 + (j >> 5)], bit);
+          atomicOr(&Uw[(p / PW) * nw32 + (j >> 5)], bit);
           atomicOr(&S[p * nw32 + (j >> 5)], bit);
         }
       }
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int n = 0;
-    for (int wi = 0; wi < nw32; ++wi) {
-      uint32_t word = U[wi];
-      while (word) {
-        ulist[n++] = wi * 32 + __builtin_ctz(word);
-        word &= word - 1;
+  if (threadIdx.x < 64) {
+    // compact the union: wave 0 scans the words in order with a running count
+    int base = 0;
+    for (int w0 = 0; w0 < nw32; w0 += 64) {
+      const uint32_t word = w0 + lane < nw32 ? U[w0 + lane] : 0u;
+      int cnt = __popc(word);
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
       }
+      int pos = base + incl - cnt;
+      uint32_t wd = word;
+      while (wd) {
+        ulist[pos++] = (w0 + lane) * 32 + __builtin_ctz(wd);
+        wd &= wd - 1;
+      }
+      base += __shfl(incl, 63);
     }
-    *nu_p = n;
+    if (lane == 0) *nu_p = base;
   }
   __syncthreads();
   const int nu = live ? *nu_p : 0;
@@ -288,11 +298,245 @@ void sparse_prefill_kernel(SparsePrefillArgs a) {
   }
   const int nitems = nu + nwin;
 
-  // per-lane column: position tcol (of this wave), head hcol
+  // per-lane columns: position tcol (of this wave), head hcol
+  int tcol[NT], hcol[NT], pcol[NT], hicol[NT];
+  Eng eng;
+  eng.reset();
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int col = 16 * nt + (lane & 15);
+    pcol[nt] = col / G;
+    tcol[nt] = tw0 + pcol[nt];
+    hcol[nt] = g * G + col % G;
+    hicol[nt] = tcol[nt] < T ? tcol[nt] : -1;
+#pragma unroll
+    for (int ks = 0; ks < Eng::NS; ++ks)
+      eng.qf[nt][ks] = (live && tcol[nt] < T)
+                           ? Tt::ld((const char*)a.q +
+                                    (((size_t)(b * T + tcol[nt]) * a.Hq + hcol[nt]) * D + 32 * ks + 8 * (lane >> 4)) * ES)
+                           : Tt::zero();
+  }
+
+  const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * T * D * ES;
+  const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
+  const char* ksg = (const char*)a.ks + (size_t)(b * a.Hkv + g) * T * D * ES;
+  const char* vsg = (const char*)a.vs + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
+  auto issue = [&](St& st, int i) {
+    const bool win = i >= nu;
+    const int j = win ? jw0 + (i - nu) : ulist[i];
+    st.gload((win ? ksg : kg) + (size_t)64 * j * D * ES, (win ? vsg : vg) + (size_t)j * D * 64 * ES,
+             T - 64 * j);
+  };
+
+  f32x4 acc[NT][Eng::NM];
+  float gate0[NT], gate1[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    gate0[nt] = 1.f;
+    gate1[nt] = 1.f;
+    if (a.gates && live && tcol[nt] < T) {
+      const float2 gl = *(const float2*)(a.gates + ((size_t)(b * T + tcol[nt]) * a.Hq + hcol[nt]) * 2);
+      gate0[nt] = 1.f / (1.f + expf(-gl.x));
+      gate1[nt] = 1.f / (1.f + expf(-gl.y));
+    }
+  }
+  auto fold = [&](const float* gate, bool first) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float inv, l2;
+      eng.finish(nt, inv, l2);
+      const float sc = inv * gate[nt];
+#pragma unroll
+      for (int mc = 0; mc < Eng::NM; ++mc)
+        acc[nt][mc] = first ? eng.o[nt][mc] * sc : acc[nt][mc] + eng.o[nt][mc] * sc;
+    }
+  };
+
+  float bmax[NT], bsum[NT];
+  int lo[NT], hi[NT];
+  auto compute = [&](int i) {
+    const char* buf = tiles + (i & 1) * St::BYTES;
+    auto ldK = [&](int c, int ks) { return St::ldK(buf, c, ks); };
+    auto ldV = [&](int u, int mc) { return St::ldV(buf, u, mc); };
+    if (i < nu) {
+      const int j = ulist[i];
+      const bool mine = (__builtin_amdgcn_readfirstlane(Uw[w * nw32 + (j >> 5)]) >> (j & 31)) & 1u;
+      if (mine) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const bool sel = (S[(w * PW + pcol[nt]) * nw32 + (j >> 5)] >> (j & 31)) & 1u;
+          lo[nt] = sel ? 0 : kNoKey;
+          hi[nt] = hicol[nt];
+        }
+        eng.template tile<true, false>(ldK, ldV, 64 * j, lo, hi, a.sc2, bmax, bsum);
+      }
+    } else {
+      const int j = jw0 + (i - nu);
+      const bool mine = tw0 < T && 64 * j <= tw0 + PW - 1 && 64 * j + 63 >= tw0 - a.W + 1;
+      if (mine) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          lo[nt] = tcol[nt] - a.W + 1;
+          hi[nt] = hicol[nt];
+        }
+        eng.template tile<true, false>(ldK, ldV, 64 * j, lo, hi, a.sc2, bmax, bsum);
+      }
+    }
+  };
+
+  if (NSTAGE == 2) {
+    // two register stages: the global loads of item i+2 are in flight while
+    // item i is computed and item i+1 is written to LDS
+    St st0, st1;
+    if (nitems > 0) {
+      issue(st0, 0);
+      st0.sstore(tiles);
+    }
+    if (nitems > 1) issue(st1, 1);
+    __syncthreads();
+    auto step = [&](int i, St& ld_into, const St& store_from) {
+      if (i == nu) {
+        fold(gate0, true);
+        eng.reset();
+      }
+      if (i + 2 < nitems) issue(ld_into, i + 2);
+      compute(i);
+      if (i + 1 < nitems) store_from.sstore(tiles + ((i + 1) & 1) * St::BYTES);
+      __syncthreads();
+    };
+    for (int i = 0; i < nitems; i += 2) {
+      step(i, st0, st1);
+      if (i + 1 < nitems) step(i + 1, st1, st0);
+    }
+  } else {
+    St st;
+    if (nitems > 0) {
+      issue(st, 0);
+      st.sstore(tiles);
+    }
+    __syncthreads();
+    for (int i = 0; i < nitems; ++i) {
+      if (i == nu) {
+        fold(gate0, true);
+        eng.reset();
+      }
+      if (i + 1 < nitems) issue(st, i + 1);
+      compute(i);
+      if (i + 1 < nitems) st.sstore(tiles + ((i + 1) & 1) * St::BYTES);
+      __syncthreads();
+    }
+  }
+  if (nu == nitems) {  // no window tiles: the sparse branch is still open
+    fold(gate0, true);
+  } else {
+    fold(gate1, false);
+  }
+
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    if (live && tcol[nt] < T) {
+      char* op = (char*)a.o + (((size_t)(b * T + tcol[nt]) * a.Hq + hcol[nt]) * D + 4 * (lane >> 4)) * ES;
+#pragma unroll
+      for (int mc = 0; mc < Eng::NM; ++mc) {
+        const f32x4 v = acc[nt][mc];
+        Tt::store4(op + 16 * mc * ES, v[0], v[1], v[2], v[3]);
+      }
+    }
+  }
+}
+
+// Ping-pong variant of the sparse kernel (NT = 1, 8 wavefronts).  The two
+// wavefronts that share a SIMD (w and w+4) work one half-tile out of phase:
+// waves 0-3 run QK^T -> softmax -> PV on item s, waves 4-7 run softmax -> PV
+// on item s-1 and then QK^T on item s, so one wave's exponentials overlap the
+// other's matrix instructions.  Three LDS tile buffers hold items s-1, s and
+// s+1; the loads of item s+2 are in flight during step s.  Work assignment,
+// masking and the two branches are as in sparse_prefill_kernel.
+template <int DT, int D>
+__global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefillArgs a) {
+  using Tt = Tr<DT>;
+  using Eng = WaveAttn<DT, D, 1>;
+  using St = TileStage<DT, D, 512>;
+  constexpr int ES = Tt::ES;
+  constexpr int NW = 8;
+  __shared__ __attribute__((aligned(16))) char tiles[3 * St::BYTES];
+  extern __shared__ uint32_t dyn[];
+
+  const int per = gridDim.x >> 3;
+  const int wgid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  const bool live = wgid < a.nwg;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const bool lag = w >= 4;  // waves 4-7 run half a tile behind
+  const int T = a.T;
+  const int G = a.Hq / a.Hkv;
+  const int PW = 16 / G;
+  const int PWG = NW * PW;
+  const int nwg_bg = (T + PWG - 1) / PWG;
+  const int bg = wgid / nwg_bg;
+  const int g = bg % a.Hkv, b = bg / a.Hkv;
+  const int t0 = (wgid % nwg_bg) * PWG;
+  const int tw0 = t0 + w * PW;
+  const int nw32 = (a.nblk + 31) >> 5;
+  uint32_t* U = dyn;
+  uint32_t* Uw = U + nw32;
+  uint32_t* S = Uw + NW * nw32;
+  int* ulist = (int*)(S + PWG * nw32);
+  int* nu_p = ulist + a.nblk;
+
+  for (int i = threadIdx.x; i < (1 + NW + PWG) * nw32; i += 64 * NW) U[i] = 0u;
+  __syncthreads();
+  if (live) {
+    for (int e = threadIdx.x; e < PWG * a.topk; e += 64 * NW) {
+      const int p = e / a.topk;
+      const int t = t0 + p;
+      if (t < T) {
+        const int j = a.idx[((size_t)(b * a.Hkv + g) * T + t) * a.topk + (e % a.topk)];
+        if (j >= 0 && j < a.nblk && 64 * j <= t) {
+          const uint32_t bit = 1u << (j & 31);
+          atomicOr(&U[j >> 5], bit);
+          atomicOr(&Uw[(p / PW) * nw32 + (j >> 5)], bit);
+          atomicOr(&S[p * nw32 + (j >> 5)], bit);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    int base = 0;
+    for (int w0 = 0; w0 < nw32; w0 += 64) {
+      const uint32_t word = w0 + lane < nw32 ? U[w0 + lane] : 0u;
+      const int cnt = __popc(word);
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+      }
+      int pos = base + incl - cnt;
+      uint32_t wd = word;
+      while (wd) {
+        ulist[pos++] = (w0 + lane) * 32 + __builtin_ctz(wd);
+        wd &= wd - 1;
+      }
+      base += __shfl(incl, 63);
+    }
+    if (lane == 0) *nu_p = base;
+  }
+  __syncthreads();
+  const int nu = live ? *nu_p : 0;
+  int jw0 = 0, nwin = 0;
+  if (live && a.W > 0) {
+    jw0 = max(0, t0 - a.W + 1) >> 6;
+    nwin = (min(T - 1, t0 + PWG - 1) >> 6) - jw0 + 1;
+  }
+  const int nitems = nu + nwin;
+
   const int col = lane & 15;
   const int pcol = col / G;
   const int tcol = tw0 + pcol;
   const int hcol = g * G + col % G;
+  const int hicol = tcol < T ? tcol : -1;
   Eng eng;
   eng.reset();
 #pragma unroll
@@ -306,10 +550,8 @@ void sparse_prefill_kernel(SparsePrefillArgs a) {
   const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
   const char* ksg = (const char*)a.ks + (size_t)(b * a.Hkv + g) * T * D * ES;
   const char* vsg = (const char*)a.vs + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
-  // two register stages: the global loads of item i+2 are in flight while
-  // item i is computed and item i+1 is written to LDS
-  St st0, st1;
-  auto issue = [&](St& st, int i) {
+  St st;
+  auto issue = [&](int i) {
     const bool win = i >= nu;
     const int j = win ? jw0 + (i - nu) : ulist[i];
     st.gload((win ? ksg : kg) + (size_t)64 * j * D * ES, (win ? vsg : vg) + (size_t)j * D * 64 * ES,
@@ -330,56 +572,77 @@ void sparse_prefill_kernel(SparsePrefillArgs a) {
 #pragma unroll
     for (int mc = 0; mc < Eng::NM; ++mc) acc[mc] = first ? eng.o[0][mc] * sc : acc[mc] + eng.o[0][mc] * sc;
   };
-
-  if (nitems > 0) {
-    issue(st0, 0);
-    st0.sstore(tiles);
-  }
-  if (nitems > 1) issue(st1, 1);
-  __syncthreads();
-  float bmax[1], bsum[1];
-  int lo[1], hi[1];
-  const int hicol = tcol < T ? tcol : -1;
-  auto step = [&](int i, St& ld_into, const St& store_from) {
-    if (i == nu) {
-      fold(gate0, true);
-      eng.reset();
-    }
-    if (i + 2 < nitems) issue(ld_into, i + 2);
-    const char* buf = tiles + (i & 1) * St::BYTES;
-    auto ldK = [&](int c, int ks) { return St::ldK(buf, c, ks); };
-    auto ldV = [&](int u, int mc) { return St::ldV(buf, u, mc); };
+  // item i: first key, mask, and whether this wave computes it
+  auto item = [&](int i, int& kbase, int& lo, int& hi) -> bool {
     if (i < nu) {
       const int j = ulist[i];
+      kbase = 64 * j;
       const bool mine = (__builtin_amdgcn_readfirstlane(Uw[w * nw32 + (j >> 5)]) >> (j & 31)) & 1u;
-      if (mine) {
-        const bool sel = (S[(w * P + pcol) * nw32 + (j >> 5)] >> (j & 31)) & 1u;
-        lo[0] = sel ? 0 : kNoKey;
-        hi[0] = hicol;
-        eng.template tile<true, false>(ldK, ldV, 64 * j, lo, hi, a.sc2, bmax, bsum);
+      const bool sel = (S[(w * PW + pcol) * nw32 + (j >> 5)] >> (j & 31)) & 1u;
+      lo = sel ? 0 : kNoKey;
+      hi = hicol;
+      return mine;
+    }
+    const int j = jw0 + (i - nu);
+    kbase = 64 * j;
+    lo = tcol - a.W + 1;
+    hi = hicol;
+    return tw0 < T && 64 * j <= tw0 + PW - 1 && 64 * j + 63 >= tw0 - a.W + 1;
+  };
+
+  if (nitems > 0) {
+    issue(0);
+    st.sstore(tiles);
+  }
+  if (nitems > 1) issue(1);
+  __syncthreads();
+
+  float bmax[1], bsum[1];
+  f32x4 sreg[1][4];
+  int p_kbase = 0, p_lo[1] = {0}, p_hi[1] = {0};
+  bool p_mine = false;
+  for (int st_i = 0; st_i <= nitems; ++st_i) {
+    if (st_i + 1 < nitems) st.sstore(tiles + ((st_i + 1) % 3) * St::BYTES);
+    if (st_i + 2 < nitems) issue(st_i + 2);
+    if (!lag) {
+      if (st_i < nitems) {
+        if (st_i == nu) {
+          fold(gate0, true);
+          eng.reset();
+        }
+        int kbase, lo[1], hi[1];
+        if (item(st_i, kbase, lo[0], hi[0])) {
+          const char* buf = tiles + (st_i % 3) * St::BYTES;
+          eng.template tile<true, false>([&](int c, int ks) { return St::ldK(buf, c, ks); },
+                                         [&](int u, int mc) { return St::ldV(buf, u, mc); }, kbase, lo, hi,
+                                         a.sc2, bmax, bsum);
+        }
       }
     } else {
-      const int j = jw0 + (i - nu);
-      const bool mine = tw0 < T && 64 * j <= tw0 + P - 1 && 64 * j + 63 >= tw0 - a.W + 1;
-      if (mine) {
-        lo[0] = tcol - a.W + 1;
-        hi[0] = hicol;
-        eng.template tile<true, false>(ldK, ldV, 64 * j, lo, hi, a.sc2, bmax, bsum);
+      if (st_i >= 1 && p_mine) {
+        const char* buf = tiles + ((st_i - 1) % 3) * St::BYTES;
+        eng.template softmax_pv<true, false>(sreg, [&](int u, int mc) { return St::ldV(buf, u, mc); }, p_kbase,
+                                             p_lo, p_hi, a.sc2, bmax, bsum);
+      }
+      if (st_i < nitems) {
+        if (st_i == nu) {
+          fold(gate0, true);
+          eng.reset();
+        }
+        p_mine = item(st_i, p_kbase, p_lo[0], p_hi[0]);
+        if (p_mine) {
+          const char* buf = tiles + (st_i % 3) * St::BYTES;
+          eng.qk([&](int c, int ks) { return St::ldK(buf, c, ks); }, sreg);
+        }
       }
     }
-    if (i + 1 < nitems) store_from.sstore(tiles + ((i + 1) & 1) * St::BYTES);
     __syncthreads();
-  };
-  for (int i = 0; i < nitems; i += 2) {
-    step(i, st0, st1);
-    if (i + 1 < nitems) step(i + 1, st1, st0);
   }
-  if (nu == nitems) {  // no window tiles: the sparse branch is still open
+  if (nu == nitems) {
     fold(gate0, true);
   } else {
     fold(gate1, false);
   }
-
   if (live && tcol < T) {
     char* op = (char*)a.o + (((size_t)(b * T + tcol) * a.Hq + hcol) * D + 4 * (lane >> 4)) * ES;
 #pragma unroll
@@ -423,24 +686,32 @@ hipError_t launch_block_topk(const TopkArgs& a, int max_blocks, hipStream_t s) {
   return hipGetLastError();
 }
 
-constexpr int kSparseWaves = 8;  // waves per work group of the sparse prefill kernel
+// sparse prefill launch shape: waves per work group, column tiles per wave,
+// register prefetch stages
+constexpr int kSparseWaves = 8;
+constexpr int kSparseNT = 1;
+constexpr int kSparseStages = 2;
 
 template <int DT, int D>
 static hipError_t sparse_dispatch(SparsePrefillArgs a, hipStream_t s) {
-  constexpr int NW = kSparseWaves;
+  constexpr int NW = kSparseWaves, NT = kSparseNT;
   const int G = a.Hq / a.Hkv;
-  const int P = 16 / G;
-  const int PWG = NW * P;
+  const int PWG = NW * (16 * NT / G);
   a.nwg = a.B * a.Hkv * ((a.T + PWG - 1) / PWG);
   const int per = (a.nwg + 7) / 8;
   const int nw32 = (a.nblk + 31) / 32;
   const size_t lds = ((size_t)(1 + NW + PWG) * nw32 + a.nblk + 1) * sizeof(uint32_t);
-  hipLaunchKernelGGL((sparse_prefill_kernel<DT, D, NW>), dim3(8 * per), dim3(64 * NW), lds, s, a);
+  constexpr bool pingpong = NW == 8 && NT == 1 && 3 * TileStage<DT, D, 512>::BYTES <= 100 * 1024;
+  if constexpr (pingpong)
+    hipLaunchKernelGGL((sparse_prefill_pp_kernel<DT, D>), dim3(8 * per), dim3(512), lds, s, a);
+  else
+    hipLaunchKernelGGL((sparse_prefill_kernel<DT, D, NT, NW, kSparseStages>), dim3(8 * per), dim3(64 * NW), lds,
+                       s, a);
   return hipGetLastError();
 }
 
 size_t sparse_prefill_lds_bytes(int T, int G) {
-  const int nblk = (T + 63) / 64, nw32 = (nblk + 31) / 32, PWG = kSparseWaves * (16 / G);
+  const int nblk = (T + 63) / 64, nw32 = (nblk + 31) / 32, PWG = kSparseWaves * (16 * kSparseNT / G);
   return ((size_t)(1 + kSparseWaves + PWG) * nw32 + nblk + 1) * sizeof(uint32_t);
 }
 
