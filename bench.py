@@ -1,6 +1,7 @@
 """Benchmark of the hybrid-block prefill hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--config 2] [--no-cpu]
+                    [--decode [4] [5]]
 
 One step = one whole hybrid block over one batch of synthetic input: the full
 causal GQA layer with block scores, the top-k selection, then the N sparse
@@ -113,6 +114,119 @@ def cpu_baseline(inp, budget_s: float = 12.0):
                       f"({done_w / total * 100:.2f}% of the block)"}
 
 
+def decode_bytes(inp) -> float:
+    """Algorithmic HBM bytes of one decode step: the full layer reads every
+    cached key and value once; each sparse layer reads its selected blocks (or
+    tokens) of the shared cache and its own window ring; plus queries, outputs,
+    gates and indices.  Score intermediates and workspace are not counted."""
+    cfg = inp.cfg
+    e = 1 if cfg.dtype == "fp8" else 2
+    L = inp.lens.astype(np.float64)
+    d, Hq, Hkv, N = cfg.d, cfg.Hq, cfg.Hkv, cfg.N
+    full = (L.sum() * Hkv * d * 2 * e) + cfg.B * Hq * d * 2 * 2
+    if cfg.kind == "decode_token":
+        ncand = np.maximum(0, L - cfg.n_recent)
+        nsel = np.minimum(cfg.kb, ncand) + np.minimum(cfg.n_recent, L)
+        per_layer = (nsel.sum() * Hkv * d * 2 * e + cfg.B * Hq * d * 2 * 2
+                     + cfg.B * Hkv * (cfg.kb + cfg.n_recent) * 4)
+    else:
+        nsel = np.minimum(cfg.kb, np.floor((L - 1) / 64))
+        ring = np.minimum(L, cfg.W)
+        per_layer = ((nsel.sum() * 64 + ring.sum()) * Hkv * d * 2 * e + cfg.B * Hq * d * 2 * 2
+                     + cfg.B * Hq * 2 * 4 + cfg.B * Hkv * cfg.kb * 4)
+    return float(full + N * per_layer)
+
+
+def bench_decode(cid: int, steps: int):
+    """Time full decode steps of the 1:11 decode workload (block or token mode)
+    on a cold cache; returns a dict for the JSON line."""
+    import torch
+
+    from hybrid_sparse_attention_causal_amd import binding as hb
+    from hybrid_sparse_attention_causal_amd import inputs as gen
+
+    cfg = gen.config(cid)
+    inp = gen.make_decode(cfg)
+    B, Hq, Hkv, C, d = cfg.B, cfg.Hq, cfg.Hkv, cfg.T, cfg.d
+    token = cfg.kind == "decode_token"
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    if token:
+        kc = np.empty((B, Hkv, C, d), np.uint8)
+        vc = np.empty((B, Hkv, C, d), np.uint8)
+        gen.fill_decode_cache(inp, kc, vc, v_block_major=False)
+    else:
+        kc = np.empty((B, Hkv, C, d), np.uint16)
+        vc = np.empty((B, Hkv, C // 64, d, 64), np.uint16)
+        gen.fill_decode_cache(inp, kc, vc)
+    k, v = dev(kc), dev(vc)
+    del kc, vc
+    scale = dev(inp.kv_scale) if token else None
+    lens = torch.from_numpy(inp.lens.astype(np.int32)).cuda()
+    q = dev(inp.q)
+    blk = 1 if token else 64
+    nsel = cfg.kb + cfg.n_recent if token else cfg.kb
+    o = torch.empty((B, Hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq), device="cuda")
+    raw = torch.empty((B, Hq, C // blk), device="cuda")
+    idx = torch.empty((B, Hkv, nsel), dtype=torch.int32, device="cuda")
+    shape = hb.decode_shape(q, k, lens, scale)
+    ws_full = torch.empty(max(16, hb.workspace_size(hb.HS_FN_FULL_ATTN, shape, blk)),
+                          dtype=torch.uint8, device="cuda")
+    layers = []
+    for lay in inp.layers:
+        ent = dict(q=dev(lay["q"]), o=torch.empty_like(o))
+        if not token:
+            ent.update(kr=dev(lay["k_ring"]), vr=dev(gen.block_major(lay["v_ring"])),
+                       g=dev(lay["gates"]))
+        layers.append(ent)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        hb.decode_full_attn_scores(q, k, v, lens, o, lse, raw, block=blk, ws=ws_full,
+                                   kv_scale=scale, stream=stream)
+        hb.decode_block_topk(q, k, lens, raw, lse, cfg.kb, idx, block=blk, n_recent=cfg.n_recent,
+                             kv_scale=scale, stream=stream)
+        for l in layers:
+            if token:
+                hb.decode_select_attn(l["q"], k, v, lens, idx, nsel, None, None, 0, None, l["o"],
+                                      block=1, kv_scale=scale, stream=stream)
+            else:
+                hb.decode_select_attn(l["q"], k, v, lens, idx, nsel, l["kr"], l["vr"], cfg.W, l["g"],
+                                      l["o"], stream=stream)
+
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        scrub.fill_(1)  # evicts L2 and the MALL; outside the timed events
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    warm0, warm1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    warm0.record(stream)
+    for _ in range(steps):
+        step()
+    warm1.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median(times))
+    nbytes = decode_bytes(inp)
+    return {"workload": {4: "1:11 hybrid block decode, 64 seqs, L~U[32768,65536], top-32 blocks, W=128",
+                         5: "token-level decode, 16 seqs x 262144, fp8 KV, top-2048 + 128 recent"}[cid],
+            "ms_per_step_cold": ms, "ms_per_step_warm": warm0.elapsed_time(warm1) / steps,
+            "algorithmic_bytes": nbytes, "GB_per_s": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +234,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--decode", type=int, nargs="*", default=[4], choices=[4, 5],
+                    help="decode workloads also measured (default: 4); pass none to skip")
     ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -234,6 +350,10 @@ def main():
         "roofline": {"kernel": dom_kernel, "bound": "mfma", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic},
     }
+    if args.decode:
+        del layers, q, k, vb, o, lse, raw, idx
+        torch.cuda.empty_cache()
+        out["decode"] = [bench_decode(c, max(3, min(args.steps, 10))) for c in args.decode]
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(out), flush=True)

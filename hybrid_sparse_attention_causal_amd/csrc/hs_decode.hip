@@ -11,6 +11,8 @@
 //  decode_sparse_kernel   one sparse layer: the selected blocks of the shared
 //                         cache plus the layer's own window ring, merged by the
 //                         sigmoid gates (explainer 3.4.3)
+#include <type_traits>
+
 #include "hs_device.h"
 #include "hs_internal.h"
 
@@ -24,7 +26,7 @@ namespace hs {
 // scale per (K|V, kv head); the value fragments are byte-transposed in
 // registers (fp8_vfrag4), so their head_dim rows come in fp8_vrow_d order.
 template <int D, int TOKEN, int KV>
-__global__ __launch_bounds__(256) void decode_full_kernel(DecodeFullArgs a) {
+__global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
   using Tt = Tr<HS_BF16>;
   using Frag = Tt::Frag;
   using Eng = WaveAttn<HS_BF16, D, 1>;
@@ -62,32 +64,78 @@ __global__ __launch_bounds__(256) void decode_full_kernel(DecodeFullArgs a) {
   float* rawrow = a.raw + (size_t)(b * a.Hq + h) * (TOKEN ? a.C : a.C / 64);
   const int q4 = (lane >> 4) << 2;
 
-  for (int kb0 = kstart; kb0 < kend; kb0 += 64) {
+  // Raw fragments of one tile: bf16: 16 K and 16 V fragments of 16 bytes;
+  // fp8: 16 K fragments of 8 bytes and 2x(D/64)x8 value dwords (decoded at
+  // use).  Two waves per SIMD keep two tiles in flight per SIMD.
+  constexpr bool F8 = KV == HS_FP8_E4M3;
+  struct RawB {
+    uint4 k[4][Eng::NS];
+    uint4 v[2][Eng::NM];
+  };
+  struct Raw8 {
+    uint2 k8[4][Eng::NS];
+    uint32_t v8[2][D / 64][8];
+  };
+  struct Raw : std::conditional_t<F8, Raw8, RawB> {};
+  auto load = [&](int kb0, Raw& r) {
     const bool partial = kb0 + 64 > L;
+    const int j = kb0 >> 6;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int key = kb0 + tile_key(c, r16);
+      const bool ok = !partial || key < L;
+#pragma unroll
+      for (int ks = 0; ks < Eng::NS; ++ks) {
+        if constexpr (F8) {
+          r.k8[c][ks] = ok ? *(const uint2*)(kg + (size_t)key * D + 32 * ks + q8) : make_uint2(0u, 0u);
+        } else {
+          r.k[c][ks] =
+              ok ? *(const uint4*)(kg + ((size_t)key * D + 32 * ks + q8) * 2) : make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int key0 = kb0 + 32 * u + q8;
+      if constexpr (F8) {
+#pragma unroll
+        for (int hf = 0; hf < D / 64; ++hf)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            r.v8[u][hf][e] = (!partial || key0 + e < L)
+                                 ? *(const uint32_t*)(vg + (size_t)(key0 + e) * D + 64 * hf + 4 * r16)
+                                 : 0u;
+      } else {
+#pragma unroll
+        for (int mc = 0; mc < Eng::NM; ++mc) {
+          Frag f = Tt::ld(vg + (((size_t)j * D + 16 * mc + r16) * 64 + 32 * u + q8) * 2);
+          if (partial) f = Tt::keep(f, L - key0);
+          r.v[u][mc] = f.u;
+        }
+      }
+    }
+  };
+  auto compute = [&](int kb0, const Raw& r) {
     const int j = kb0 >> 6;
     Frag vc[4];
     auto ldK = [&](int c, int ks) {
-      const int key = kb0 + tile_key(c, r16);
-      if (partial && key >= L) return Tt::zero();
-      if (KV == HS_FP8_E4M3) return fp8x8_frag(*(const uint2*)(kg + (size_t)key * D + 32 * ks + q8));
-      return Tt::ld(kg + ((size_t)key * D + 32 * ks + q8) * 2);
+      if constexpr (F8) {
+        return fp8x8_frag(r.k8[c][ks]);
+      } else {
+        Frag f;
+        f.u = r.k[c][ks];
+        return f;
+      }
     };
     auto ldV = [&](int u, int mc) {
-      if (KV == HS_FP8_E4M3) {
-        if ((mc & 3) == 0) {
-          uint32_t w[8];
-          const int key0 = kb0 + 32 * u + q8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            w[e] = (!partial || key0 + e < L)
-                       ? *(const uint32_t*)(vg + (size_t)(key0 + e) * D + 64 * (mc >> 2) + 4 * r16)
-                       : 0u;
-          fp8_vfrag4(w, vc);
-        }
+      if constexpr (F8) {
+        if ((mc & 3) == 0) fp8_vfrag4(r.v8[u][mc >> 2], vc);
         return vc[mc & 3];
+      } else {
+        Frag f;
+        f.u = r.v[u][mc];
+        return f;
       }
-      const auto f = Tt::ld(vg + (((size_t)j * D + 16 * mc + r16) * 64 + 32 * u + q8) * 2);
-      return partial ? Tt::keep(f, L - (kb0 + 32 * u + q8)) : f;
     };
     float bmax[1], bsum[1];
     if (TOKEN) {
@@ -112,6 +160,13 @@ __global__ __launch_bounds__(256) void decode_full_kernel(DecodeFullArgs a) {
       eng.template tile<true, false>(ldK, ldV, kb0, lo, hi, sc2, bmax, bsum);
       if (lane < 16 && col < G) rawrow[j] = bmax[0] * kLn2;
     }
+  };
+  // per tile, the key and value loads are issued together (one memory round
+  // trip per tile)
+  for (int kb0 = kstart; kb0 < kend; kb0 += 64) {
+    Raw r;
+    load(kb0, r);
+    compute(kb0, r);
   }
 
   // partial state: unnormalised o (head_dim floats, natural order), m (log2), l
@@ -168,11 +223,18 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeFullArgs a) {
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  for (int c = 0; c < nchb; ++c) {
-    const float* p = pp + (size_t)c * (D + 2);
-    const float w = fast_exp2(p[D] - M);
+  // lane c of a 64-chunk group holds that chunk's weight; the loads of the
+  // chunks are independent and unrolled
+  for (int c0 = 0; c0 < nchb; c0 += 64) {
+    const float wl = c0 + lane < nchb ? fast_exp2(pp[(size_t)(c0 + lane) * (D + 2) + D] - M) : 0.f;
+    const int n = min(64, nchb - c0);
+#pragma unroll 8
+    for (int c = 0; c < n; ++c) {
+      const float w = __shfl(wl, c);
+      const float* p = pp + (size_t)(c0 + c) * (D + 2);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += w * p[lane + 64 * i];
+      for (int i = 0; i < PER; ++i) acc[i] += w * p[lane + 64 * i];
+    }
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   uint16_t* o = (uint16_t*)a.o + (size_t)bh * D;
@@ -230,14 +292,24 @@ __global__ __launch_bounds__(512) void decode_sparse_kernel(DecodeSparseArgs a) 
       const bool partial = kb0 + 64 > L;
       lo[0] = col < G ? 0 : kNoKey;
       hi[0] = L - 1;
-      auto ldK = [&](int c, int ks) {
+      // key and value fragments are loaded together (one round trip)
+      typename Tt::Frag kf[4][Eng::NS], vf[2][Eng::NM];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
         const int key = kb0 + tile_key(c, r16);
-        return (!partial || key < L) ? Tt::ld(kg + ((size_t)key * D + 32 * ks + q8) * ES) : Tt::zero();
-      };
-      auto ldV = [&](int u, int mc) {
-        const auto f = Tt::ld(vg + (((size_t)j * D + 16 * mc + r16) * 64 + 32 * u + q8) * ES);
-        return partial ? Tt::keep(f, L - (kb0 + 32 * u + q8)) : f;
-      };
+#pragma unroll
+        for (int ks = 0; ks < Eng::NS; ++ks)
+          kf[c][ks] = (!partial || key < L) ? Tt::ld(kg + ((size_t)key * D + 32 * ks + q8) * ES) : Tt::zero();
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int mc = 0; mc < Eng::NM; ++mc) {
+          const auto f = Tt::ld(vg + (((size_t)j * D + 16 * mc + r16) * 64 + 32 * u + q8) * ES);
+          vf[u][mc] = partial ? Tt::keep(f, L - (kb0 + 32 * u + q8)) : f;
+        }
+      auto ldK = [&](int c, int ks) { return kf[c][ks]; };
+      auto ldV = [&](int u, int mc) { return vf[u][mc]; };
       sp.template tile<true, false>(ldK, ldV, kb0, lo, hi, a.sc2, bmax, bsum);
     } else {
       const int r = it - a.nsel;
@@ -397,7 +469,7 @@ __global__ __launch_bounds__(1024) void token_select_kernel(TokenTopkArgs a) {
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t scan[1024];
   __shared__ int res[2];
-  __shared__ uint32_t wsum[16];
+  __shared__ uint32_t wsum[32];
   const int row = blockIdx.x;
   const int b = row / a.Hkv;
   const int L = a.lens[b];
@@ -443,34 +515,41 @@ __global__ __launch_bounds__(1024) void token_select_kernel(TokenTopkArgs a) {
     find_bin(hist, 1024, need, scan, res);
     const uint32_t thr = (p2 << 10) | (uint32_t)res[0];
     const int need_eq = need - res[1];  // >= 1 keys equal to thr are taken
-    // emit ascending: running counts of selected and of ties in token order
-    int sel_base = 0, tie_base = 0;
-    for (int c0 = 0; c0 < ncand; c0 += 1024) {
-      const int i = c0 + t;
-      const uint32_t k = i < ncand ? keys[i] : 0u;
-      const bool gt = i < ncand && k > thr;
-      const bool eq = i < ncand && k == thr;
-      const uint64_t em = __ballot(eq);
-      if (lane == 0) wsum[w] = (uint32_t)__popcll(em);
-      __syncthreads();
-      int tie_before = tie_base;
-      for (int x = 0; x < w; ++x) tie_before += wsum[x];
-      int tie_total = tie_base;
-      for (int x = 0; x < 16; ++x) tie_total += wsum[x];
-      const int rank = tie_before + __popcll(em & lt_mask);
-      const bool s = gt || (eq && rank < need_eq);
-      __syncthreads();
-      const uint64_t sm = __ballot(s);
-      if (lane == 0) wsum[w] = (uint32_t)__popcll(sm);
-      __syncthreads();
-      int pos = sel_base;
-      for (int x = 0; x < w; ++x) pos += wsum[x];
-      int sel_total = sel_base;
-      for (int x = 0; x < 16; ++x) sel_total += wsum[x];
-      if (s) out[pos + __popcll(sm & lt_mask)] = i;
-      sel_base = sel_total;
-      tie_base = tie_total;
-      __syncthreads();
+    // emit ascending: wave w owns the contiguous candidates
+    // [w*wseg, (w+1)*wseg) and walks them 64 at a time; ballots give each
+    // lane its rank among the keys > thr and == thr of its wave, and one
+    // exclusive scan over the 16 waves' counts gives every wave its first
+    // output slot and its first tie rank.
+    const int wseg = ((ncand + 1023) / 1024) * 64;
+    const int i0 = min(ncand, w * wseg), i1 = min(ncand, i0 + wseg);
+    uint32_t ngt = 0, neq = 0;
+    for (int i = i0; i < i1; i += 64) {
+      const uint32_t k = i + lane < i1 ? keys[i + lane] : 0u;
+      const bool in = i + lane < i1;
+      ngt += __popcll(__ballot(in && k > thr));
+      neq += __popcll(__ballot(in && k == thr));
+    }
+    if (lane == 0) {
+      wsum[w] = ngt;
+      wsum[16 + w] = neq;
+    }
+    __syncthreads();
+    uint32_t gt_base = 0, eq_base = 0;
+    for (int v = 0; v < w; ++v) {
+      gt_base += wsum[v];
+      eq_base += wsum[16 + v];
+    }
+    uint32_t pos = gt_base + min(eq_base, (uint32_t)need_eq);
+    for (int i = i0; i < i1; i += 64) {
+      const bool in = i + lane < i1;
+      const uint32_t k = in ? keys[i + lane] : 0u;
+      const uint64_t eqm = __ballot(in && k == thr);
+      const uint32_t eq_rank = eq_base + __popcll(eqm & lt_mask);
+      const bool take = in && (k > thr || (k == thr && eq_rank < (uint32_t)need_eq));
+      const uint64_t tm = __ballot(take);
+      if (take) out[pos + __popcll(tm & lt_mask)] = i + lane;
+      pos += __popcll(tm);
+      eq_base += __popcll(eqm);
     }
     nsel = kb;
   }
