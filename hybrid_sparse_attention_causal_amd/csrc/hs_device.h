@@ -117,6 +117,11 @@ template <> struct Tr<HS_BF16> {
   __device__ __forceinline__ static void store4(void* dst, float a, float b, float c, float d) {
     *reinterpret_cast<uint2*>(dst) = make_uint2(bf16x2_bits(a, b), bf16x2_bits(c, d));
   }
+  __device__ __forceinline__ static f32x4 load4(const void* src) {
+    const uint2 w = *reinterpret_cast<const uint2*>(src);
+    return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                 __uint_as_float(w.y & 0xffff0000u)};
+  }
 };
 
 template <> struct Tr<HS_F32> {
@@ -162,6 +167,10 @@ template <> struct Tr<HS_F32> {
   }
   __device__ __forceinline__ static void store4(void* dst, float a, float b, float c, float d) {
     *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
+  }
+  __device__ __forceinline__ static f32x4 load4(const void* src) {
+    const float4 v = *reinterpret_cast<const float4*>(src);
+    return f32x4{v.x, v.y, v.z, v.w};
   }
 };
 
@@ -251,8 +260,12 @@ struct TileStage {
   }
 
   // krows: key row 0 of the tile (row stride D elements); vslab: [D][64] tile;
-  // nk: number of valid keys in the tile (>= 64 means all)
+  // nk: number of valid keys in the tile (>= 64 means all).  Key rows beyond
+  // nk are not read; value columns beyond nk are zeroed in sstore, after the
+  // data has arrived, so no wait is forced here.
+  int nk_;
   __device__ __forceinline__ void gload(const char* krows, const char* vslab, int nk) {
+    nk_ = nk;
 #pragma unroll
     for (int n = 0; n < NK; ++n) {
       const int ci = threadIdx.x + NTHR * n;
@@ -263,27 +276,30 @@ struct TileStage {
     for (int n = 0; n < NV; ++n) {
       const int ci = threadIdx.x + NTHR * n;
       const int dd = ci / VCH, col = ci % VCH;
-      uint4 x = *(const uint4*)(vslab + dd * VS + col * 16);
-      const int k0 = col * (16 / ES);
-      if (k0 + 16 / ES > nk) {
-        uint32_t w[4] = {x.x, x.y, x.z, x.w};
-        const int keep = nk - k0;  // elements kept
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e0 = i * 4 / ES;  // first element of word i
-          if (e0 >= keep) w[i] = 0u;
-          else if (ES == 2 && e0 + 1 >= keep) w[i] &= 0xffffu;
-        }
-        x = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-      vr[n] = x;
+      vr[n] = *(const uint4*)(vslab + dd * VS + col * 16);
     }
   }
-  __device__ __forceinline__ void sstore(char* buf) const {
+  __device__ __forceinline__ void sstore(char* buf) {
 #pragma unroll
     for (int n = 0; n < NK; ++n) {
       const int ci = threadIdx.x + NTHR * n;
       *(uint4*)(buf + k_lds(tile_row(ci / KCH), ci % KCH)) = kr[n];
+    }
+    if (nk_ < 64) {  // uniform: only a ragged last tile
+      constexpr int EPW = 4 / ES;  // elements per 32-bit word
+#pragma unroll
+      for (int n = 0; n < NV; ++n) {
+        const int ci = threadIdx.x + NTHR * n;
+        const int k0 = (ci % VCH) * (16 / ES);
+        uint32_t w[4] = {vr[n].x, vr[n].y, vr[n].z, vr[n].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = nk_ - (k0 + EPW * i);  // valid elements left from this word on
+          const uint32_t msk = r >= EPW ? 0xffffffffu : (r == 1 && EPW == 2 ? 0xffffu : 0u);
+          w[i] &= msk;
+        }
+        vr[n] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
     }
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
@@ -372,10 +388,12 @@ struct WaveAttn {
 
   // Online-softmax update with the logits s of a tile, then O += P V.
   // `hook(nt, x)` sees the lane's 16 masked, scaled logits (log2 units; x[4c+i]
-  // belongs to key kbase + tile_key(c, 4q+i)) before the exponentials.
+  // belongs to key kbase + tile_key(c, 4q+i)) before the exponentials; those
+  // of a switched-off column are not masked.
   // Masking is decided per wavefront: a column with lo == kNoKey is switched
-  // off (one select per value); key-by-key range checks only when some live
-  // column's [lo, hi] does not cover the whole tile.
+  // off (its maximum and exponent offset are replaced, two selects per lane);
+  // key-by-key range checks only when some live column's [lo, hi] does not
+  // cover the whole tile.
   template <bool MASK, bool WANT_SUM, class LV, class HK = NoHook>
   __device__ __forceinline__ void softmax_pv(f32x4 (&s)[NT][4], const LV& ldV, int kbase, const int* lo,
                                              const int* hi, float sc2, float* bmax, float* bsum,
@@ -400,22 +418,30 @@ struct WaveAttn {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float x[16];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[4 * c + i] = s[nt][c][i];
+      const bool en = !MASK || lo[nt] != kNoKey;
+      if (MASK && ranged) {
+        // the lane's keys are kbase + 8*(lane/16) + k, k = 32(c/2) + 4(c%2) + i
+        const int base = kbase + 8 * (lane >> 4);
+        const int klo = en ? lo[nt] - base : 64;
+        const int khi = hi[nt] - base;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int k = 32 * (c >> 1) + 4 * (c & 1) + i;
+            if (k < klo || k > khi) x[4 * c + i] = -INFINITY;
+          }
+      }
       float mx = -INFINITY;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = s[nt][c][i];
-          if (MASK && ranged) {
-            const int key = kbase + tile_key(c, q4 + i);
-            if (key < lo[nt] || key > hi[nt]) v = -INFINITY;
-          } else if (MASK && off) {
-            if (lo[nt] == kNoKey) v = -INFINITY;
-          }
-          x[4 * c + i] = v;
-          mx = fmaxf(mx, v);
-        }
-      }
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, x[e]);
+      // a switched-off column (lo == kNoKey) keeps its raw logits; its maximum
+      // is -inf and its exponentials are forced to 0 below
+      if (MASK && off) mx = en ? mx : -INFINITY;
       if constexpr (!__is_same(HK, NoHook)) {
         float xs[16];
 #pragma unroll
@@ -433,10 +459,11 @@ struct WaveAttn {
       alpha[nt] = up ? fast_exp2(m[nt] - mn) : 1.f;
       rescale = rescale || up;
       m[nt] = mn;
+      const float nmn = (MASK && off && !en) ? -INFINITY : -mn;
       float ps = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        x[e] = fast_exp2(__builtin_fmaf(x[e], sc2, -mn));
+        x[e] = fast_exp2(__builtin_fmaf(x[e], sc2, nmn));
         ps += x[e];
       }
       l[nt] = l[nt] * alpha[nt] + ps;

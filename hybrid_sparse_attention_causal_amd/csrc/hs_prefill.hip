@@ -394,7 +394,7 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_prefill_kernel(SparsePrefil
     }
     if (nitems > 1) issue(st1, 1);
     __syncthreads();
-    auto step = [&](int i, St& ld_into, const St& store_from) {
+    auto step = [&](int i, St& ld_into, St& store_from) {
       if (i == nu) {
         fold(gate0, true);
         eng.reset();
@@ -445,17 +445,19 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_prefill_kernel(SparsePrefil
   }
 }
 
-// Ping-pong variant of the sparse kernel (NT = 1, 8 wavefronts).  The two
-// wavefronts that share a SIMD (w and w+4) work one half-tile out of phase:
-// waves 0-3 run QK^T -> softmax -> PV on item s, waves 4-7 run softmax -> PV
-// on item s-1 and then QK^T on item s, so one wave's exponentials overlap the
-// other's matrix instructions.  Three LDS tile buffers hold items s-1, s and
-// s+1; the loads of item s+2 are in flight during step s.  Work assignment,
-// masking and the two branches are as in sparse_prefill_kernel.
-template <int DT, int D>
+// Ping-pong variant of the sparse kernel (8 wavefronts, NT column tiles of
+// 16 columns per wavefront).  The two wavefronts that share a SIMD (w and w+4)
+// work one half-tile out of phase: waves 0-3 run QK^T -> softmax -> PV on item
+// s, waves 4-7 run softmax -> PV on item s-1 and then QK^T on item s, so one
+// wave's exponentials overlap the other's matrix instructions.  Three LDS tile
+// buffers hold items s-1, s and s+1; the loads of item s+2 are in flight during
+// step s.  Work assignment, masking and the two branches are as in
+// sparse_prefill_kernel; column tile nt of wave w holds the G heads of the
+// 16/G positions tw0 + nt*16/G + col/G.
+template <int DT, int D, int NT>
 __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefillArgs a) {
   using Tt = Tr<DT>;
-  using Eng = WaveAttn<DT, D, 1>;
+  using Eng = WaveAttn<DT, D, NT>;
   using St = TileStage<DT, D, 512>;
   constexpr int ES = Tt::ES;
   constexpr int NW = 8;
@@ -470,7 +472,8 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
   const bool lag = w >= 4;  // waves 4-7 run half a tile behind
   const int T = a.T;
   const int G = a.Hq / a.Hkv;
-  const int PW = 16 / G;
+  const int PT = 16 / G;  // positions per column tile
+  const int PW = NT * PT;
   const int PWG = NW * PW;
   const int nwg_bg = (T + PWG - 1) / PWG;
   const int bg = wgid / nwg_bg;
@@ -533,18 +536,25 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
   const int nitems = nu + nwin;
 
   const int col = lane & 15;
-  const int pcol = col / G;
-  const int tcol = tw0 + pcol;
   const int hcol = g * G + col % G;
-  const int hicol = tcol < T ? tcol : -1;
+  int pcol[NT], tcol[NT], hicol[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    pcol[nt] = nt * PT + col / G;
+    tcol[nt] = tw0 + pcol[nt];
+    hicol[nt] = tcol[nt] < T ? tcol[nt] : -1;
+  }
   Eng eng;
   eng.reset();
 #pragma unroll
-  for (int ks = 0; ks < Eng::NS; ++ks)
-    eng.qf[0][ks] = (live && tcol < T)
-                        ? Tt::ld((const char*)a.q +
-                                 (((size_t)(b * T + tcol) * a.Hq + hcol) * D + 32 * ks + 8 * (lane >> 4)) * ES)
-                        : Tt::zero();
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < Eng::NS; ++ks)
+      eng.qf[nt][ks] =
+          (live && tcol[nt] < T)
+              ? Tt::ld((const char*)a.q +
+                       (((size_t)(b * T + tcol[nt]) * a.Hq + hcol) * D + 32 * ks + 8 * (lane >> 4)) * ES)
+              : Tt::zero();
 
   const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * T * D * ES;
   const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
@@ -558,35 +568,59 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
              T - 64 * j);
   };
 
-  f32x4 acc[Eng::NM];
-  float gate0 = 1.f, gate1 = 1.f;
-  if (a.gates && live && tcol < T) {
-    const float2 gl = *(const float2*)(a.gates + ((size_t)(b * T + tcol) * a.Hq + hcol) * 2);
-    gate0 = 1.f / (1.f + expf(-gl.x));
-    gate1 = 1.f / (1.f + expf(-gl.y));
-  }
-  auto fold = [&](float gate, bool first) {
-    float inv, l2;
-    eng.finish(0, inv, l2);
-    const float sc = inv * gate;
+  float gate0[NT], gate1[NT];
 #pragma unroll
-    for (int mc = 0; mc < Eng::NM; ++mc) acc[mc] = first ? eng.o[0][mc] * sc : acc[mc] + eng.o[0][mc] * sc;
+  for (int nt = 0; nt < NT; ++nt) {
+    gate0[nt] = 1.f;
+    gate1[nt] = 1.f;
+    if (a.gates && live && tcol[nt] < T) {
+      const float2 gl = *(const float2*)(a.gates + ((size_t)(b * T + tcol[nt]) * a.Hq + hcol) * 2);
+      gate0[nt] = 1.f / (1.f + expf(-gl.x));
+      gate1[nt] = 1.f / (1.f + expf(-gl.y));
+    }
+  }
+  // Close a branch.  The first branch's gated output is parked in the output
+  // rows themselves (in the output dtype) while the second branch runs and is
+  // added back when that one closes: no registers hold it in between.
+  auto fold = [&](const float* gate, bool first) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float inv, l2;
+      eng.finish(nt, inv, l2);
+      const float sc = inv * gate[nt];
+      if (live && tcol[nt] < T) {
+        char* op = (char*)a.o + (((size_t)(b * T + tcol[nt]) * a.Hq + hcol) * D + 4 * (lane >> 4)) * ES;
+#pragma unroll
+        for (int mc = 0; mc < Eng::NM; ++mc) {
+          f32x4 v = eng.o[nt][mc] * sc;
+          if (!first) v += Tt::load4(op + 16 * mc * ES);
+          Tt::store4(op + 16 * mc * ES, v[0], v[1], v[2], v[3]);
+        }
+      }
+    }
   };
-  // item i: first key, mask, and whether this wave computes it
-  auto item = [&](int i, int& kbase, int& lo, int& hi) -> bool {
+  // item i: first key, per-column-tile key range, and whether this wave
+  // computes it
+  auto item = [&](int i, int& kbase, int* lo, int* hi) -> bool {
     if (i < nu) {
       const int j = ulist[i];
       kbase = 64 * j;
       const bool mine = (__builtin_amdgcn_readfirstlane(Uw[w * nw32 + (j >> 5)]) >> (j & 31)) & 1u;
-      const bool sel = (S[(w * PW + pcol) * nw32 + (j >> 5)] >> (j & 31)) & 1u;
-      lo = sel ? 0 : kNoKey;
-      hi = hicol;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const bool sel = (S[(w * PW + pcol[nt]) * nw32 + (j >> 5)] >> (j & 31)) & 1u;
+        lo[nt] = sel ? 0 : kNoKey;
+        hi[nt] = hicol[nt];
+      }
       return mine;
     }
     const int j = jw0 + (i - nu);
     kbase = 64 * j;
-    lo = tcol - a.W + 1;
-    hi = hicol;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      lo[nt] = tcol[nt] - a.W + 1;
+      hi[nt] = hicol[nt];
+    }
     return tw0 < T && 64 * j <= tw0 + PW - 1 && 64 * j + 63 >= tw0 - a.W + 1;
   };
 
@@ -597,9 +631,9 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
   if (nitems > 1) issue(1);
   __syncthreads();
 
-  float bmax[1], bsum[1];
-  f32x4 sreg[1][4];
-  int p_kbase = 0, p_lo[1] = {0}, p_hi[1] = {0};
+  float bmax[NT], bsum[NT];
+  f32x4 sreg[NT][4];
+  int p_kbase = 0, p_lo[NT], p_hi[NT];
   bool p_mine = false;
   for (int st_i = 0; st_i <= nitems; ++st_i) {
     if (st_i + 1 < nitems) st.sstore(tiles + ((st_i + 1) % 3) * St::BYTES);
@@ -610,8 +644,8 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
           fold(gate0, true);
           eng.reset();
         }
-        int kbase, lo[1], hi[1];
-        if (item(st_i, kbase, lo[0], hi[0])) {
+        int kbase, lo[NT], hi[NT];
+        if (item(st_i, kbase, lo, hi)) {
           const char* buf = tiles + (st_i % 3) * St::BYTES;
           eng.template tile<true, false>([&](int c, int ks) { return St::ldK(buf, c, ks); },
                                          [&](int u, int mc) { return St::ldV(buf, u, mc); }, kbase, lo, hi,
@@ -629,7 +663,7 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
           fold(gate0, true);
           eng.reset();
         }
-        p_mine = item(st_i, p_kbase, p_lo[0], p_hi[0]);
+        p_mine = item(st_i, p_kbase, p_lo, p_hi);
         if (p_mine) {
           const char* buf = tiles + (st_i % 3) * St::BYTES;
           eng.qk([&](int c, int ks) { return St::ldK(buf, c, ks); }, sreg);
@@ -642,14 +676,6 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
     fold(gate0, true);
   } else {
     fold(gate1, false);
-  }
-  if (live && tcol < T) {
-    char* op = (char*)a.o + (((size_t)(b * T + tcol) * a.Hq + hcol) * D + 4 * (lane >> 4)) * ES;
-#pragma unroll
-    for (int mc = 0; mc < Eng::NM; ++mc) {
-      const f32x4 v = acc[mc];
-      Tt::store4(op + 16 * mc * ES, v[0], v[1], v[2], v[3]);
-    }
   }
 }
 
@@ -689,27 +715,31 @@ hipError_t launch_block_topk(const TopkArgs& a, int max_blocks, hipStream_t s) {
 // sparse prefill launch shape: waves per work group, column tiles per wave,
 // register prefetch stages
 constexpr int kSparseWaves = 8;
-constexpr int kSparseNT = 1;
+constexpr int kSparseNT = 2;
 constexpr int kSparseStages = 2;
 
 template <int DT, int D>
 static hipError_t sparse_dispatch(SparsePrefillArgs a, hipStream_t s) {
-  constexpr int NW = kSparseWaves, NT = kSparseNT;
+  constexpr int NW = kSparseWaves;
+  // the ping-pong kernel needs three tile buffers in LDS (f32 with d = 128
+  // does not fit and takes the one-column-tile kernel)
+  constexpr bool pingpong = NW == 8 && 3 * TileStage<DT, D, 512>::BYTES <= 100 * 1024;
+  constexpr int NT = pingpong ? kSparseNT : 1;
   const int G = a.Hq / a.Hkv;
   const int PWG = NW * (16 * NT / G);
   a.nwg = a.B * a.Hkv * ((a.T + PWG - 1) / PWG);
   const int per = (a.nwg + 7) / 8;
   const int nw32 = (a.nblk + 31) / 32;
   const size_t lds = ((size_t)(1 + NW + PWG) * nw32 + a.nblk + 1) * sizeof(uint32_t);
-  constexpr bool pingpong = NW == 8 && NT == 1 && 3 * TileStage<DT, D, 512>::BYTES <= 100 * 1024;
   if constexpr (pingpong)
-    hipLaunchKernelGGL((sparse_prefill_pp_kernel<DT, D>), dim3(8 * per), dim3(512), lds, s, a);
+    hipLaunchKernelGGL((sparse_prefill_pp_kernel<DT, D, NT>), dim3(8 * per), dim3(512), lds, s, a);
   else
     hipLaunchKernelGGL((sparse_prefill_kernel<DT, D, NT, NW, kSparseStages>), dim3(8 * per), dim3(64 * NW), lds,
                        s, a);
   return hipGetLastError();
 }
 
+// dynamic LDS of the widest sparse launch shape (an upper bound for all)
 size_t sparse_prefill_lds_bytes(int T, int G) {
   const int nblk = (T + 63) / 64, nw32 = (nblk + 31) / 32, PWG = kSparseWaves * (16 * kSparseNT / G);
   return ((size_t)(1 + kSparseWaves + PWG) * nw32 + nblk + 1) * sizeof(uint32_t);
