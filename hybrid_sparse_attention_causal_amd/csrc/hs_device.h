@@ -78,6 +78,12 @@ __device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
 }
 
 // ----------------------------------------------------------- element traits
+// Wait until every vector memory load of this wave has returned.  Issued once
+// after the prologue loads (queries, gates): the compiler otherwise cannot
+// tell them apart from the tile prefetches in flight inside the main loop and
+// waits for all of them at the first use of a query fragment.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int DT> struct Tr;
 
 template <> struct Tr<HS_BF16> {
@@ -413,15 +419,10 @@ struct WaveAttn {
       off = __ballot(dis) != 0ull;
     }
     Frag pf[NT][2];
-    bool rescale = false;
-    float alpha[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      float x[16];
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[4 * c + i] = s[nt][c][i];
+      // masking, exponentials and packing work in place on the logits
+      f32x4(&x)[4] = s[nt];
       const bool en = !MASK || lo[nt] != kNoKey;
       if (MASK && ranged) {
         // the lane's keys are kbase + 8*(lane/16) + k, k = 32(c/2) + 4(c%2) + i
@@ -433,19 +434,21 @@ struct WaveAttn {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int k = 32 * (c >> 1) + 4 * (c & 1) + i;
-            if (k < klo || k > khi) x[4 * c + i] = -INFINITY;
+            x[c][i] = (k < klo || k > khi) ? -INFINITY : x[c][i];
           }
       }
       float mx = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, x[e]);
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[c][i]);
       // a switched-off column (lo == kNoKey) keeps its raw logits; its maximum
       // is -inf and its exponentials are forced to 0 below
       if (MASK && off) mx = en ? mx : -INFINITY;
       if constexpr (!__is_same(HK, NoHook)) {
         float xs[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) xs[e] = x[e] * sc2;
+        for (int e = 0; e < 16; ++e) xs[e] = x[e >> 2][e & 3] * sc2;
         hook(nt, xs);
       }
       mx = xlane_max(mx) * sc2;  // raw logits are unscaled; sc2 > 0
@@ -456,26 +459,25 @@ struct WaveAttn {
       // the LSE whichever maximum is kept.
       const bool up = mx > m[nt] + kSlack;
       const float mn = up ? mx : m[nt];
-      alpha[nt] = up ? fast_exp2(m[nt] - mn) : 1.f;
-      rescale = rescale || up;
+      const float alpha = up ? fast_exp2(m[nt] - mn) : 1.f;
       m[nt] = mn;
       const float nmn = (MASK && off && !en) ? -INFINITY : -mn;
       float ps = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        x[e] = fast_exp2(__builtin_fmaf(x[e], sc2, nmn));
-        ps += x[e];
-      }
-      l[nt] = l[nt] * alpha[nt] + ps;
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[c][i] = fast_exp2(__builtin_fmaf(x[c][i], sc2, nmn));
+          ps += x[c][i];
+        }
+      l[nt] = l[nt] * alpha + ps;
       if (WANT_SUM) bsum[nt] = xlane_sum(ps);
-      pf[nt][0] = T::pack(x);
-      pf[nt][1] = T::pack(x + 8);
-    }
-    if (__ballot(rescale) != 0ull) {
+      pf[nt][0] = T::pack(reinterpret_cast<const float*>(&x[0]));
+      pf[nt][1] = T::pack(reinterpret_cast<const float*>(&x[2]));
+      if (__ballot(up) != 0ull) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int mc = 0; mc < NM; ++mc) o[nt][mc] *= alpha[nt];
+        for (int mc = 0; mc < NM; ++mc) o[nt][mc] *= alpha;
+      }
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {

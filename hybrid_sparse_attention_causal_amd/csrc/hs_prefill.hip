@@ -67,6 +67,7 @@ __global__ __launch_bounds__(256, (DT == HS_F32 && D == 128) ? 1 : 2) void full_
     }
   }
 
+  wait_vmem();
   gload(0);
   st.sstore(smem);
   __syncthreads();
@@ -624,6 +625,7 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
     return tw0 < T && 64 * j <= tw0 + PW - 1 && 64 * j + 63 >= tw0 - a.W + 1;
   };
 
+  wait_vmem();
   if (nitems > 0) {
     issue(0);
     st.sstore(tiles);
@@ -631,6 +633,8 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
   if (nitems > 1) issue(1);
   __syncthreads();
 
+  // one set of logits, key ranges and flags serves both roles (the lag
+  // waves carry them across the barrier)
   float bmax[NT], bsum[NT];
   f32x4 sreg[NT][4];
   int p_kbase = 0, p_lo[NT], p_hi[NT];
@@ -644,12 +648,11 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
           fold(gate0, true);
           eng.reset();
         }
-        int kbase, lo[NT], hi[NT];
-        if (item(st_i, kbase, lo, hi)) {
+        if (item(st_i, p_kbase, p_lo, p_hi)) {
           const char* buf = tiles + (st_i % 3) * St::BYTES;
-          eng.template tile<true, false>([&](int c, int ks) { return St::ldK(buf, c, ks); },
-                                         [&](int u, int mc) { return St::ldV(buf, u, mc); }, kbase, lo, hi,
-                                         a.sc2, bmax, bsum);
+          eng.qk([&](int c, int ks) { return St::ldK(buf, c, ks); }, sreg);
+          eng.template softmax_pv<true, false>(sreg, [&](int u, int mc) { return St::ldV(buf, u, mc); }, p_kbase,
+                                               p_lo, p_hi, a.sc2, bmax, bsum);
         }
       }
     } else {
