@@ -60,19 +60,24 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(kernel: str):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/sparse_prefill_7b_hbm_traffic.txt: FETCH_SIZE and WRITE_SIZE per
+    dispatch, scaled by a plain-copy calibration), if it was taken on the
+    current kernel sources and the same workload; else None."""
+    path = os.path.join(ROOT, "profiles", "sparse_prefill_7b_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
+    ent = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, _, val = line.partition(":")
+            ent[key.strip()] = val.strip()
+    if ent.get("kernel") != kernel or ent.get("source_hash") != kernel_source_hash():
+        return None
     try:
-        rec = json.load(open(path))
-    except ValueError:
+        return float(ent["bytes_per_launch"])
+    except (KeyError, ValueError):
         return None
-    ent = rec.get(kernel)
-    if not ent or ent.get("source_hash") != kernel_source_hash():
-        return None
-    return ent.get("bytes_per_launch")
 
 
 def cpu_baseline(inp, budget_s: float = 12.0):
@@ -324,7 +329,7 @@ def main():
     else:
         dom, dom_ms, dom_flops, dom_kernel = "sparse_layer", sparse_ms, fs, "sparse_prefill_kernel"
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
-    traffic = measured_traffic(dom_kernel)
+    traffic = measured_traffic(dom_kernel) if cfg.cid == 2 else None
     out = {
         "metric": METRIC,
         "value": B * T / (ms_step * 1e-3),
