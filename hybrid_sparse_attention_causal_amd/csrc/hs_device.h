@@ -123,6 +123,19 @@ template <> struct Tr<HS_BF16> {
   __device__ __forceinline__ static void store4(void* dst, float a, float b, float c, float d) {
     *reinterpret_cast<uint2*>(dst) = make_uint2(bf16x2_bits(a, b), bf16x2_bits(c, d));
   }
+  // a lane's 16 probabilities (four f32x4) -> its two P fragments, stored in
+  // place in x[0] and x[1]; p_frag reads fragment u back
+  __device__ __forceinline__ static void pack_p(f32x4 (&x)[4]) {
+    const Frag a = pack(reinterpret_cast<const float*>(&x[0]));
+    const Frag b = pack(reinterpret_cast<const float*>(&x[2]));
+    x[0] = __builtin_bit_cast(f32x4, a.u);
+    x[1] = __builtin_bit_cast(f32x4, b.u);
+  }
+  __device__ __forceinline__ static Frag p_frag(const f32x4 (&x)[4], int u) {
+    Frag f;
+    f.u = __builtin_bit_cast(uint4, x[u]);
+    return f;
+  }
   __device__ __forceinline__ static f32x4 load4(const void* src) {
     const uint2 w = *reinterpret_cast<const uint2*>(src);
     return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
@@ -173,6 +186,14 @@ template <> struct Tr<HS_F32> {
   }
   __device__ __forceinline__ static void store4(void* dst, float a, float b, float c, float d) {
     *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
+  }
+  // fp32 P fragments are the probabilities themselves
+  __device__ __forceinline__ static void pack_p(f32x4 (&)[4]) {}
+  __device__ __forceinline__ static Frag p_frag(const f32x4 (&x)[4], int u) {
+    Frag f;
+    f.a = make_float4(x[2 * u][0], x[2 * u][1], x[2 * u][2], x[2 * u][3]);
+    f.b = make_float4(x[2 * u + 1][0], x[2 * u + 1][1], x[2 * u + 1][2], x[2 * u + 1][3]);
+    return f;
   }
   __device__ __forceinline__ static f32x4 load4(const void* src) {
     const float4 v = *reinterpret_cast<const float4*>(src);
@@ -313,6 +334,67 @@ struct TileStage {
       *(uint4*)(buf + v_lds(ci / VCH, ci % VCH)) = vr[n];
     }
   }
+  // ---- direct global -> LDS staging (global_load_lds_dwordx4) ----------
+  // A wave instruction writes 1 KiB of LDS: lane l's 16 bytes land at
+  // base + 16 l.  Chunk q (1 KiB) of the tile goes to wave q % NW as its
+  // instruction q / NW; each lane fetches the 16 source bytes that belong at
+  // its LDS position under the row map and the chunk swizzle above.  Key rows
+  // past the valid count are clamped to the last valid row (their logits are
+  // masked); value columns past it are zeroed in LDS by dma_fix.
+  static constexpr int NWV = NTHR / 64;
+  static constexpr int NDMA = BYTES / 1024 / NWV;
+  static_assert(NDMA * NWV * 1024 == BYTES && (KB / 1024) % NWV == 0, "tile does not split into wave chunks");
+  static constexpr int NDK = KB / 1024 / NWV;  // instructions 0..NDK-1 are key rows
+  int dkey[NDK > 0 ? NDK : 1];
+  int doff[NDMA];
+  __device__ __forceinline__ void dma_init() {
+    const int lane = lane_id(), w = threadIdx.x >> 6;
+#pragma unroll
+    for (int n = 0; n < NDMA; ++n) {
+      const int off = (w + NWV * n) * 1024 + 16 * lane;
+      if (n < NDK) {
+        const int r = off / KS, c = ((off % KS) >> 4) ^ (r & KSW);
+        dkey[n] = tile_key(r >> 4, r & 15);
+        doff[n] = c * 16;
+      } else {
+        const int v = off - KB, dd = v / VS, c = ((v % VS) >> 4) ^ (dd & VSW);
+        doff[n] = dd * VS + c * 16;
+      }
+    }
+  }
+  __device__ __forceinline__ void dma(char* buf, const char* krows, const char* vslab, int nk) {
+    nk_ = nk;
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int n = 0; n < NDMA; ++n) {
+      const char* src = n < NDK ? krows + (size_t)min(dkey[n < NDK ? n : 0], nk - 1) * KS + doff[n] : vslab + doff[n];
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + (w + NWV * n) * 1024), 16,
+                                       0, 0);
+    }
+  }
+  // after this wave's transfers have landed (vmcnt 0): zero the value
+  // columns past the valid count in the chunks this lane fetched
+  __device__ __forceinline__ void dma_fix(char* buf) const {
+    if (nk_ >= 64) return;  // uniform
+    const int lane = lane_id(), w = threadIdx.x >> 6;
+    constexpr int EPW = 4 / ES;
+#pragma unroll
+    for (int n = NDK; n < NDMA; ++n) {
+      const int k0 = ((doff[n] % VS) >> 4) * (16 / ES);
+      if (k0 + 16 / ES > nk_) {
+        uint4* p = (uint4*)(buf + (w + NWV * n) * 1024 + 16 * lane);
+        const uint4 x = *p;
+        uint32_t wd[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = nk_ - (k0 + EPW * i);
+          wd[i] &= r >= EPW ? 0xffffffffu : (r == 1 && EPW == 2 ? 0xffffu : 0u);
+        }
+        *p = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      }
+    }
+  }
+
   // A fragment of S^T chunk c, k-step ks: row 16c + r, elements 32ks + 8q .. +7
   __device__ __forceinline__ static Frag ldK(const char* buf, int c, int ks) {
     const int lane = lane_id();
@@ -400,10 +482,9 @@ struct WaveAttn {
   // off (its maximum and exponent offset are replaced, two selects per lane);
   // key-by-key range checks only when some live column's [lo, hi] does not
   // cover the whole tile.
-  template <bool MASK, bool WANT_SUM, class LV, class HK = NoHook>
-  __device__ __forceinline__ void softmax_pv(f32x4 (&s)[NT][4], const LV& ldV, int kbase, const int* lo,
-                                             const int* hi, float sc2, float* bmax, float* bsum,
-                                             const HK& hook = HK()) {
+  template <bool MASK, bool WANT_SUM, class HK = NoHook>
+  __device__ __forceinline__ void softmax(f32x4 (&s)[NT][4], int kbase, const int* lo, const int* hi, float sc2,
+                                          float* bmax, float* bsum, const HK& hook = HK()) {
     const int lane = lane_id();
     const int q4 = (lane >> 4) << 2;
     bool ranged = false, off = false;
@@ -418,7 +499,6 @@ struct WaveAttn {
       ranged = __ballot(part) != 0ull;
       off = __ballot(dis) != 0ull;
     }
-    Frag pf[NT][2];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       // masking, exponentials and packing work in place on the logits
@@ -472,22 +552,34 @@ struct WaveAttn {
         }
       l[nt] = l[nt] * alpha + ps;
       if (WANT_SUM) bsum[nt] = xlane_sum(ps);
-      pf[nt][0] = T::pack(reinterpret_cast<const float*>(&x[0]));
-      pf[nt][1] = T::pack(reinterpret_cast<const float*>(&x[2]));
+      T::pack_p(x);
       if (__ballot(up) != 0ull) {
 #pragma unroll
         for (int mc = 0; mc < NM; ++mc) o[nt][mc] *= alpha;
       }
     }
+  }
+
+  // O += P V with the P fragments that softmax left in s.
+  template <class LV>
+  __device__ __forceinline__ void pv(const f32x4 (&s)[NT][4], const LV& ldV) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
       for (int mc = 0; mc < NM; ++mc) {
         const Frag a = ldV(u, mc);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) T::mma(o[nt][mc], a, pf[nt][u]);
+        for (int nt = 0; nt < NT; ++nt) T::mma(o[nt][mc], a, T::p_frag(s[nt], u));
       }
     }
+  }
+
+  template <bool MASK, bool WANT_SUM, class LV, class HK = NoHook>
+  __device__ __forceinline__ void softmax_pv(f32x4 (&s)[NT][4], const LV& ldV, int kbase, const int* lo,
+                                             const int* hi, float sc2, float* bmax, float* bsum,
+                                             const HK& hook = HK()) {
+    softmax<MASK, WANT_SUM>(s, kbase, lo, hi, sc2, bmax, bsum, hook);
+    pv(s, ldV);
   }
 
   // One whole 64-key tile whose first key has absolute index kbase.

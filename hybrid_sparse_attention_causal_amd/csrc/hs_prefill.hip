@@ -562,11 +562,12 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
   const char* ksg = (const char*)a.ks + (size_t)(b * a.Hkv + g) * T * D * ES;
   const char* vsg = (const char*)a.vs + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
   St st;
-  auto issue = [&](int i) {
+  st.dma_init();
+  auto issue = [&](int i) {  // item i -> LDS buffer i % 3, in flight until wait_vmem
     const bool win = i >= nu;
     const int j = win ? jw0 + (i - nu) : ulist[i];
-    st.gload((win ? ksg : kg) + (size_t)64 * j * D * ES, (win ? vsg : vg) + (size_t)j * D * 64 * ES,
-             T - 64 * j);
+    st.dma(tiles + (i % 3) * St::BYTES, (win ? ksg : kg) + (size_t)64 * j * D * ES,
+           (win ? vsg : vg) + (size_t)j * D * 64 * ES, T - 64 * j);
   };
 
   float gate0[NT], gate1[NT];
@@ -625,54 +626,43 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
     return tw0 < T && 64 * j <= tw0 + PW - 1 && 64 * j + 63 >= tw0 - a.W + 1;
   };
 
+  if (nitems > 0) issue(0);
   wait_vmem();
-  if (nitems > 0) {
-    issue(0);
-    st.sstore(tiles);
-  }
-  if (nitems > 1) issue(1);
+  if (nitems > 0) st.dma_fix(tiles);
   __syncthreads();
 
-  // one set of logits, key ranges and flags serves both roles (the lag
-  // waves carry them across the barrier)
+  // Per step s, wave A (0-3) runs  P(s-1)V | QK(s) | softmax(s)  and wave B
+  // (4-7) runs  softmax(s-1) | P(s-1)V | QK(s): one wave's matrix block
+  // (PV + QK, 64 MFMAs) overlaps its partner's exponentials.  Across the
+  // barrier A carries the packed P of item s, B its logits, both in sreg.
   float bmax[NT], bsum[NT];
   f32x4 sreg[NT][4];
   int p_kbase = 0, p_lo[NT], p_hi[NT];
   bool p_mine = false;
   for (int st_i = 0; st_i <= nitems; ++st_i) {
-    if (st_i + 1 < nitems) st.sstore(tiles + ((st_i + 1) % 3) * St::BYTES);
-    if (st_i + 2 < nitems) issue(st_i + 2);
-    if (!lag) {
-      if (st_i < nitems) {
-        if (st_i == nu) {
-          fold(gate0, true);
-          eng.reset();
-        }
-        if (item(st_i, p_kbase, p_lo, p_hi)) {
-          const char* buf = tiles + (st_i % 3) * St::BYTES;
-          eng.qk([&](int c, int ks) { return St::ldK(buf, c, ks); }, sreg);
-          eng.template softmax_pv<true, false>(sreg, [&](int u, int mc) { return St::ldV(buf, u, mc); }, p_kbase,
-                                               p_lo, p_hi, a.sc2, bmax, bsum);
-        }
+    // the buffer of item st_i + 1 held item st_i - 2, last read before the
+    // barrier that ended the previous step
+    if (st_i + 1 < nitems) issue(st_i + 1);
+    const char* prev = tiles + ((st_i + 2) % 3) * St::BYTES;  // item st_i - 1
+    const char* cur = tiles + (st_i % 3) * St::BYTES;
+    auto ldV = [&](int u, int mc) { return St::ldV(prev, u, mc); };
+    auto ldK = [&](int c, int ks) { return St::ldK(cur, c, ks); };
+    if (lag && st_i >= 1 && p_mine)
+      eng.template softmax<true, false>(sreg, p_kbase, p_lo, p_hi, a.sc2, bmax, bsum);
+    if (st_i >= 1 && p_mine) eng.pv(sreg, ldV);
+    if (st_i < nitems) {
+      if (st_i == nu) {
+        fold(gate0, true);
+        eng.reset();
       }
-    } else {
-      if (st_i >= 1 && p_mine) {
-        const char* buf = tiles + ((st_i - 1) % 3) * St::BYTES;
-        eng.template softmax_pv<true, false>(sreg, [&](int u, int mc) { return St::ldV(buf, u, mc); }, p_kbase,
-                                             p_lo, p_hi, a.sc2, bmax, bsum);
-      }
-      if (st_i < nitems) {
-        if (st_i == nu) {
-          fold(gate0, true);
-          eng.reset();
-        }
-        p_mine = item(st_i, p_kbase, p_lo, p_hi);
-        if (p_mine) {
-          const char* buf = tiles + (st_i % 3) * St::BYTES;
-          eng.qk([&](int c, int ks) { return St::ldK(buf, c, ks); }, sreg);
-        }
+      p_mine = item(st_i, p_kbase, p_lo, p_hi);
+      if (p_mine) {
+        eng.qk(ldK, sreg);
+        if (!lag) eng.template softmax<true, false>(sreg, p_kbase, p_lo, p_hi, a.sc2, bmax, bsum);
       }
     }
+    wait_vmem();
+    if (st_i + 1 < nitems) st.dma_fix(tiles + ((st_i + 1) % 3) * St::BYTES);
     __syncthreads();
   }
   if (nu == nitems) {
