@@ -466,7 +466,9 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
   extern __shared__ uint32_t dyn[];
 
   const int per = gridDim.x >> 3;
-  const int wgid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  // consecutive ids share an XCD; within an XCD the latest positions (the
+  // largest unions of selected blocks) are dispatched first
+  const int wgid = (blockIdx.x & 7) * per + (per - 1 - (blockIdx.x >> 3));
   const bool live = wgid < a.nwg;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -488,6 +490,64 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
   int* ulist = (int*)(S + PWG * nw32);
   int* nu_p = ulist + a.nblk;
 
+  // Items: first the window blocks of the group's positions (known at once),
+  // then the union of their selected blocks.
+  int jw0 = 0, nwin = 0;
+  if (live && a.W > 0) {
+    jw0 = max(0, t0 - a.W + 1) >> 6;
+    nwin = (min(T - 1, t0 + PWG - 1) >> 6) - jw0 + 1;
+  }
+
+  const int col = lane & 15;
+  const int hcol = g * G + col % G;
+  int pcol[NT], tcol[NT], hicol[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    pcol[nt] = nt * PT + col / G;
+    tcol[nt] = tw0 + pcol[nt];
+    hicol[nt] = tcol[nt] < T ? tcol[nt] : -1;
+  }
+  // query fragments, gates and the first window tile are in flight while the
+  // selection bitsets are built
+  Eng eng;
+  eng.reset();
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < Eng::NS; ++ks)
+      eng.qf[nt][ks] =
+          (live && tcol[nt] < T)
+              ? Tt::ld((const char*)a.q +
+                       (((size_t)(b * T + tcol[nt]) * a.Hq + hcol) * D + 32 * ks + 8 * (lane >> 4)) * ES)
+              : Tt::zero();
+  float gate0[NT], gate1[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    gate0[nt] = 1.f;
+    gate1[nt] = 1.f;
+    if (a.gates && live && tcol[nt] < T) {
+      const float2 gl = *(const float2*)(a.gates + ((size_t)(b * T + tcol[nt]) * a.Hq + hcol) * 2);
+      gate0[nt] = 1.f / (1.f + expf(-gl.x));
+      gate1[nt] = 1.f / (1.f + expf(-gl.y));
+    }
+  }
+  const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * T * D * ES;
+  const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
+  const char* ksg = (const char*)a.ks + (size_t)(b * a.Hkv + g) * T * D * ES;
+  const char* vsg = (const char*)a.vs + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
+  St st;
+  st.dma_init();
+  auto issue = [&](int i) {  // item i -> LDS buffer i % 3, in flight until wait_vmem
+    const bool win = i < nwin;
+    const int j = win ? jw0 + i : ulist[i - nwin];
+    st.dma(tiles + (i % 3) * St::BYTES, (win ? ksg : kg) + (size_t)64 * j * D * ES,
+           (win ? vsg : vg) + (size_t)j * D * 64 * ES, T - 64 * j);
+  };
+  if (nwin > 0) issue(0);
+
+  // selection bitsets: per position (S), per wave (Uw) and per group (U);
+  // positions own their words, the unions are OR-reductions (no contended
+  // atomics)
   for (int i = threadIdx.x; i < (1 + NW + PWG) * nw32; i += 64 * NW) U[i] = 0u;
   __syncthreads();
   if (live) {
@@ -496,14 +556,22 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
       const int t = t0 + p;
       if (t < T) {
         const int j = a.idx[((size_t)(b * a.Hkv + g) * T + t) * a.topk + (e % a.topk)];
-        if (j >= 0 && j < a.nblk && 64 * j <= t) {
-          const uint32_t bit = 1u << (j & 31);
-          atomicOr(&U[j >> 5], bit);
-          atomicOr(&Uw[(p / PW) * nw32 + (j >> 5)], bit);
-          atomicOr(&S[p * nw32 + (j >> 5)], bit);
-        }
+        if (j >= 0 && j < a.nblk && 64 * j <= t) atomicOr(&S[p * nw32 + (j >> 5)], 1u << (j & 31));
       }
     }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < NW * nw32; i += 64 * NW) {
+    const int ww = i / nw32, k = i % nw32;
+    uint32_t v = 0u;
+    for (int p = 0; p < PW; ++p) v |= S[(ww * PW + p) * nw32 + k];
+    Uw[i] = v;
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < nw32; k += 64 * NW) {
+    uint32_t v = 0u;
+    for (int ww = 0; ww < NW; ++ww) v |= Uw[ww * nw32 + k];
+    U[k] = v;
   }
   __syncthreads();
   if (threadIdx.x < 64) {
@@ -529,58 +597,9 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
   }
   __syncthreads();
   const int nu = live ? *nu_p : 0;
-  int jw0 = 0, nwin = 0;
-  if (live && a.W > 0) {
-    jw0 = max(0, t0 - a.W + 1) >> 6;
-    nwin = (min(T - 1, t0 + PWG - 1) >> 6) - jw0 + 1;
-  }
-  const int nitems = nu + nwin;
+  const int nitems = nwin + nu;
+  if (nwin == 0 && nitems > 0) issue(0);
 
-  const int col = lane & 15;
-  const int hcol = g * G + col % G;
-  int pcol[NT], tcol[NT], hicol[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    pcol[nt] = nt * PT + col / G;
-    tcol[nt] = tw0 + pcol[nt];
-    hicol[nt] = tcol[nt] < T ? tcol[nt] : -1;
-  }
-  Eng eng;
-  eng.reset();
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int ks = 0; ks < Eng::NS; ++ks)
-      eng.qf[nt][ks] =
-          (live && tcol[nt] < T)
-              ? Tt::ld((const char*)a.q +
-                       (((size_t)(b * T + tcol[nt]) * a.Hq + hcol) * D + 32 * ks + 8 * (lane >> 4)) * ES)
-              : Tt::zero();
-
-  const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * T * D * ES;
-  const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
-  const char* ksg = (const char*)a.ks + (size_t)(b * a.Hkv + g) * T * D * ES;
-  const char* vsg = (const char*)a.vs + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
-  St st;
-  st.dma_init();
-  auto issue = [&](int i) {  // item i -> LDS buffer i % 3, in flight until wait_vmem
-    const bool win = i >= nu;
-    const int j = win ? jw0 + (i - nu) : ulist[i];
-    st.dma(tiles + (i % 3) * St::BYTES, (win ? ksg : kg) + (size_t)64 * j * D * ES,
-           (win ? vsg : vg) + (size_t)j * D * 64 * ES, T - 64 * j);
-  };
-
-  float gate0[NT], gate1[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    gate0[nt] = 1.f;
-    gate1[nt] = 1.f;
-    if (a.gates && live && tcol[nt] < T) {
-      const float2 gl = *(const float2*)(a.gates + ((size_t)(b * T + tcol[nt]) * a.Hq + hcol) * 2);
-      gate0[nt] = 1.f / (1.f + expf(-gl.x));
-      gate1[nt] = 1.f / (1.f + expf(-gl.y));
-    }
-  }
   // Close a branch.  The first branch's gated output is parked in the output
   // rows themselves (in the output dtype) while the second branch runs and is
   // added back when that one closes: no registers hold it in between.
@@ -604,8 +623,8 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
   // item i: first key, per-column-tile key range, and whether this wave
   // computes it
   auto item = [&](int i, int& kbase, int* lo, int* hi) -> bool {
-    if (i < nu) {
-      const int j = ulist[i];
+    if (i >= nwin) {
+      const int j = ulist[i - nwin];
       kbase = 64 * j;
       const bool mine = (__builtin_amdgcn_readfirstlane(Uw[w * nw32 + (j >> 5)]) >> (j & 31)) & 1u;
 #pragma unroll
@@ -616,7 +635,7 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
       }
       return mine;
     }
-    const int j = jw0 + (i - nu);
+    const int j = jw0 + i;
     kbase = 64 * j;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -626,7 +645,6 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
     return tw0 < T && 64 * j <= tw0 + PW - 1 && 64 * j + 63 >= tw0 - a.W + 1;
   };
 
-  if (nitems > 0) issue(0);
   wait_vmem();
   if (nitems > 0) st.dma_fix(tiles);
   __syncthreads();
@@ -651,8 +669,8 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
       eng.template softmax<true, false>(sreg, p_kbase, p_lo, p_hi, a.sc2, bmax, bsum);
     if (st_i >= 1 && p_mine) eng.pv(sreg, ldV);
     if (st_i < nitems) {
-      if (st_i == nu) {
-        fold(gate0, true);
+      if (st_i == nwin) {  // window branch closed: park it
+        fold(gate1, true);
         eng.reset();
       }
       p_mine = item(st_i, p_kbase, p_lo, p_hi);
@@ -665,10 +683,10 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
     if (st_i + 1 < nitems) st.dma_fix(tiles + ((st_i + 1) % 3) * St::BYTES);
     __syncthreads();
   }
-  if (nu == nitems) {
-    fold(gate0, true);
+  if (nwin == nitems) {
+    fold(gate1, true);
   } else {
-    fold(gate1, false);
+    fold(gate0, false);
   }
 }
 
