@@ -123,6 +123,11 @@ template <> struct Tr<HS_BF16> {
   __device__ __forceinline__ static void store4(void* dst, float a, float b, float c, float d) {
     *reinterpret_cast<uint2*>(dst) = make_uint2(bf16x2_bits(a, b), bf16x2_bits(c, d));
   }
+  __device__ __forceinline__ static Frag ones() {
+    Frag f;
+    f.u = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
+    return f;
+  }
   // a lane's 16 probabilities (four f32x4) -> its two P fragments, stored in
   // place in x[0] and x[1]; p_frag reads fragment u back
   __device__ __forceinline__ static void pack_p(f32x4 (&x)[4]) {
@@ -186,6 +191,12 @@ template <> struct Tr<HS_F32> {
   }
   __device__ __forceinline__ static void store4(void* dst, float a, float b, float c, float d) {
     *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
+  }
+  __device__ __forceinline__ static Frag ones() {
+    Frag f;
+    f.a = make_float4(1.f, 1.f, 1.f, 1.f);
+    f.b = f.a;
+    return f;
   }
   // fp32 P fragments are the probabilities themselves
   __device__ __forceinline__ static void pack_p(f32x4 (&)[4]) {}
@@ -428,17 +439,26 @@ struct TileStage {
 // ------------------------------------------------------------- the engine
 // One wavefront, NT column tiles of 16 query columns each, head_dim D.
 // Online softmax state per column tile: running maximum m (log2 units, already
-// scaled), per-lane partial denominator l, and O^T accumulators
-// (o[nt][mc]: head_dim rows 16*mc + 4q .. +3 of the lane's column).
-template <int DT, int D, int NT>
+// scaled), the denominator, and O^T accumulators (o[nt][mc]: head_dim rows
+// 16*mc + 4q .. +3 of the lane's column).  The denominator is a per-lane
+// partial sum l of the fp32 probabilities, or, with LSUM, a column sum lacc
+// that the matrix unit accumulates from the packed P against an all-ones
+// fragment (two extra MFMAs per tile and column tile instead of 16 VALU adds
+// per lane; numerator and denominator then use the same rounded P).
+// softmax's `act` carries one bit per column tile; a clear bit (no live key
+// in the tile for any of its columns, wave-uniform) skips that tile's
+// softmax and sets its P to 0.
+template <int DT, int D, int NT, bool LSUM = false>
 struct WaveAttn {
   using T = Tr<DT>;
   using Frag = typename T::Frag;
   static constexpr int NS = D / 32;  // k-steps of S^T = K Q^T
   static constexpr int NM = D / 16;  // row chunks of O^T
+  static constexpr unsigned kAll = (1u << NT) - 1;
 
   Frag qf[NT][NS];
   f32x4 o[NT][NM];
+  f32x4 lacc[LSUM ? NT : 1];
   float m[NT], l[NT];
 
   __device__ __forceinline__ void reset() {
@@ -446,6 +466,7 @@ struct WaveAttn {
     for (int nt = 0; nt < NT; ++nt) {
       m[nt] = kNegBig;
       l[nt] = 0.f;
+      if (LSUM) lacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int mc = 0; mc < NM; ++mc) o[nt][mc] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -465,9 +486,7 @@ struct WaveAttn {
         const Frag a = ldK(c, ks);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          if (ks == 0) {
-            s[nt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
+          if (ks == 0) s[nt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
           T::mma(s[nt][c], a, qf[nt][ks]);
         }
       }
@@ -484,7 +503,7 @@ struct WaveAttn {
   // cover the whole tile.
   template <bool MASK, bool WANT_SUM, class HK = NoHook>
   __device__ __forceinline__ void softmax(f32x4 (&s)[NT][4], int kbase, const int* lo, const int* hi, float sc2,
-                                          float* bmax, float* bsum, const HK& hook = HK()) {
+                                          float* bmax, float* bsum, const HK& hook = HK(), unsigned act = kAll) {
     const int lane = lane_id();
     const int q4 = (lane >> 4) << 2;
     bool ranged = false, off = false;
@@ -501,6 +520,13 @@ struct WaveAttn {
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
+      if (!((act >> nt) & 1u)) {  // no live key for this column tile: P = 0
+        bmax[nt] = -INFINITY;
+        if (WANT_SUM) bsum[nt] = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) s[nt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        continue;
+      }
       // masking, exponentials and packing work in place on the logits
       f32x4(&x)[4] = s[nt];
       const bool en = !MASK || lo[nt] != kNoKey;
@@ -548,14 +574,15 @@ struct WaveAttn {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           x[c][i] = fast_exp2(__builtin_fmaf(x[c][i], sc2, nmn));
-          ps += x[c][i];
+          if (!LSUM || WANT_SUM) ps += x[c][i];
         }
-      l[nt] = l[nt] * alpha + ps;
+      if (!LSUM) l[nt] = l[nt] * alpha + ps;
       if (WANT_SUM) bsum[nt] = xlane_sum(ps);
       T::pack_p(x);
       if (__ballot(up) != 0ull) {
 #pragma unroll
         for (int mc = 0; mc < NM; ++mc) o[nt][mc] *= alpha;
+        if (LSUM) lacc[nt] *= alpha;
       }
     }
   }
@@ -570,6 +597,10 @@ struct WaveAttn {
         const Frag a = ldV(u, mc);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) T::mma(o[nt][mc], a, T::p_frag(s[nt], u));
+      }
+      if (LSUM) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) T::mma(lacc[nt], T::ones(), T::p_frag(s[nt], u));
       }
     }
   }
@@ -601,7 +632,7 @@ struct WaveAttn {
 
   // Column totals: 1/l (0 when the column saw no key) and the log2-domain LSE.
   __device__ __forceinline__ void finish(int nt, float& inv_l, float& lse2) const {
-    const float lt = xlane_sum(l[nt]);
+    const float lt = LSUM ? lacc[nt][0] : xlane_sum(l[nt]);
     inv_l = lt > 0.f ? 1.f / lt : 0.f;
     lse2 = lt > 0.f ? m[nt] + fast_log2(lt) : -INFINITY;
   }

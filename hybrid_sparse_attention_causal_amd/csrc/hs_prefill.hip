@@ -458,7 +458,7 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_prefill_kernel(SparsePrefil
 template <int DT, int D, int NT>
 __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefillArgs a) {
   using Tt = Tr<DT>;
-  using Eng = WaveAttn<DT, D, NT>;
+  using Eng = WaveAttn<DT, D, NT, true>;
   using St = TileStage<DT, D, 512>;
   constexpr int ES = Tt::ES;
   constexpr int NW = 8;
@@ -620,29 +620,26 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
       }
     }
   };
-  // item i: first key, per-column-tile key range, and whether this wave
-  // computes it
-  auto item = [&](int i, int& kbase, int* lo, int* hi) -> bool {
-    if (i >= nwin) {
-      const int j = ulist[i - nwin];
-      kbase = 64 * j;
-      const bool mine = (__builtin_amdgcn_readfirstlane(Uw[w * nw32 + (j >> 5)]) >> (j & 31)) & 1u;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const bool sel = (S[(w * PW + pcol[nt]) * nw32 + (j >> 5)] >> (j & 31)) & 1u;
-        lo[nt] = sel ? 0 : kNoKey;
-        hi[nt] = hicol[nt];
-      }
-      return mine;
-    }
-    const int j = jw0 + i;
+  // item i: first key, per-column-tile key range, and the column tiles of
+  // this wave that have a live key in it (0: the wave skips the item)
+  auto item = [&](int i, int& kbase, int* lo, int* hi) -> unsigned {
+    const bool win = i < nwin;
+    const int j = win ? jw0 + i : ulist[i - nwin];
     kbase = 64 * j;
+    unsigned act = 0;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      lo[nt] = tcol[nt] - a.W + 1;
+      if (win) {
+        lo[nt] = tcol[nt] - a.W + 1;
+      } else {
+        const bool sel = (S[(w * PW + pcol[nt]) * nw32 + (j >> 5)] >> (j & 31)) & 1u;
+        lo[nt] = sel ? 0 : kNoKey;
+      }
       hi[nt] = hicol[nt];
+      const bool live_col = max(lo[nt], kbase) <= min(hi[nt], kbase + 63);
+      act |= (__ballot(live_col) != 0ull ? 1u : 0u) << nt;
     }
-    return tw0 < T && 64 * j <= tw0 + PW - 1 && 64 * j + 63 >= tw0 - a.W + 1;
+    return act;
   };
 
   wait_vmem();
@@ -651,12 +648,15 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
 
   // Per step s, wave A (0-3) runs  P(s-1)V | QK(s) | softmax(s)  and wave B
   // (4-7) runs  softmax(s-1) | P(s-1)V | QK(s): one wave's matrix block
-  // (PV + QK, 64 MFMAs) overlaps its partner's exponentials.  Across the
+  // (PV + QK, 64 MFMAs) overlaps its partner's exponentials.  A wave raises
+  // its issue priority for its matrix block, so the partner's vector work
+  // fills the gaps between MFMAs instead of delaying them.  Across the
   // barrier A carries the packed P of item s, B its logits, both in sreg.
   float bmax[NT], bsum[NT];
   f32x4 sreg[NT][4];
   int p_kbase = 0, p_lo[NT], p_hi[NT];
-  bool p_mine = false;
+  unsigned p_act = 0;
+  const typename Eng::NoHook nohook;
   for (int st_i = 0; st_i <= nitems; ++st_i) {
     // the buffer of item st_i + 1 held item st_i - 2, last read before the
     // barrier that ended the previous step
@@ -665,20 +665,24 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
     const char* cur = tiles + (st_i % 3) * St::BYTES;
     auto ldV = [&](int u, int mc) { return St::ldV(prev, u, mc); };
     auto ldK = [&](int c, int ks) { return St::ldK(cur, c, ks); };
-    if (lag && st_i >= 1 && p_mine)
-      eng.template softmax<true, false>(sreg, p_kbase, p_lo, p_hi, a.sc2, bmax, bsum);
-    if (st_i >= 1 && p_mine) eng.pv(sreg, ldV);
+    if (lag && st_i >= 1 && p_act)
+      eng.template softmax<true, false>(sreg, p_kbase, p_lo, p_hi, a.sc2, bmax, bsum, nohook, p_act);
+    __builtin_amdgcn_s_setprio(1);
+    if (st_i >= 1 && p_act) eng.pv(sreg, ldV);
     if (st_i < nitems) {
       if (st_i == nwin) {  // window branch closed: park it
         fold(gate1, true);
         eng.reset();
       }
-      p_mine = item(st_i, p_kbase, p_lo, p_hi);
-      if (p_mine) {
+      p_act = item(st_i, p_kbase, p_lo, p_hi);
+      if (p_act) {
         eng.qk(ldK, sreg);
-        if (!lag) eng.template softmax<true, false>(sreg, p_kbase, p_lo, p_hi, a.sc2, bmax, bsum);
+        __builtin_amdgcn_s_setprio(0);
+        if (!lag)
+          eng.template softmax<true, false>(sreg, p_kbase, p_lo, p_hi, a.sc2, bmax, bsum, nohook, p_act);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     wait_vmem();
     if (st_i + 1 < nitems) st.dma_fix(tiles + ((st_i + 1) % 3) * St::BYTES);
     __syncthreads();
