@@ -78,10 +78,17 @@ __global__ __launch_bounds__(256, (DT == HS_F32 && D == 128) ? 1 : 2) void full_
       auto ldK = [&](int c, int ks) { return St::ldK(buf, c, ks); };
       auto ldV = [&](int u, int mc) { return St::ldV(buf, u, mc); };
       float bmax[NT], bsum[NT];
+      f32x4 s[NT][4];
+      __builtin_amdgcn_s_setprio(1);
+      eng.qk(ldK, s);
+      __builtin_amdgcn_s_setprio(0);
       if (64 * j + 63 > p0)
-        eng.template tile<true, SCORE_LSE != 0>(ldK, ldV, 64 * j, lo, hi, a.sc2, bmax, bsum);
+        eng.template softmax<true, SCORE_LSE != 0>(s, 64 * j, lo, hi, a.sc2, bmax, bsum);
       else
-        eng.template tile<false, SCORE_LSE != 0>(ldK, ldV, 64 * j, lo, hi, a.sc2, bmax, bsum);
+        eng.template softmax<false, SCORE_LSE != 0>(s, 64 * j, lo, hi, a.sc2, bmax, bsum);
+      __builtin_amdgcn_s_setprio(1);
+      eng.pv(s, ldV);
+      __builtin_amdgcn_s_setprio(0);
       if ((lane >> 4) == 0) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -462,7 +469,12 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
   using St = TileStage<DT, D, 512>;
   constexpr int ES = Tt::ES;
   constexpr int NW = 8;
-  __shared__ __attribute__((aligned(16))) char tiles[3 * St::BYTES];
+  // three tile buffers as separate arrays: with the step loop unrolled by
+  // three every access names its buffer, so the compiler can tell the
+  // in-flight transfer into one buffer from the reads of the other two
+  __shared__ __attribute__((aligned(16))) char tile0[St::BYTES];
+  __shared__ __attribute__((aligned(16))) char tile1[St::BYTES];
+  __shared__ __attribute__((aligned(16))) char tile2[St::BYTES];
   extern __shared__ uint32_t dyn[];
 
   const int per = gridDim.x >> 3;
@@ -537,13 +549,13 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
   const char* vsg = (const char*)a.vs + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
   St st;
   st.dma_init();
-  auto issue = [&](int i) {  // item i -> LDS buffer i % 3, in flight until wait_vmem
+  auto issue = [&](int i, char* buf) {  // item i -> buf (tile i % 3), in flight until wait_vmem
     const bool win = i < nwin;
     const int j = win ? jw0 + i : ulist[i - nwin];
-    st.dma(tiles + (i % 3) * St::BYTES, (win ? ksg : kg) + (size_t)64 * j * D * ES,
-           (win ? vsg : vg) + (size_t)j * D * 64 * ES, T - 64 * j);
+    st.dma(buf, (win ? ksg : kg) + (size_t)64 * j * D * ES, (win ? vsg : vg) + (size_t)j * D * 64 * ES,
+           T - 64 * j);
   };
-  if (nwin > 0) issue(0);
+  if (nwin > 0) issue(0, tile0);
 
   // selection bitsets: per position (S), per wave (Uw) and per group (U);
   // positions own their words, the unions are OR-reductions (no contended
@@ -598,7 +610,7 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
   __syncthreads();
   const int nu = live ? *nu_p : 0;
   const int nitems = nwin + nu;
-  if (nwin == 0 && nitems > 0) issue(0);
+  if (nwin == 0 && nitems > 0) issue(0, tile0);
 
   // Close a branch.  The first branch's gated output is parked in the output
   // rows themselves (in the output dtype) while the second branch runs and is
@@ -643,7 +655,7 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
   };
 
   wait_vmem();
-  if (nitems > 0) st.dma_fix(tiles);
+  if (nitems > 0) st.dma_fix(tile0);
   __syncthreads();
 
   // Per step s, wave A (0-3) runs  P(s-1)V | QK(s) | softmax(s)  and wave B
@@ -657,12 +669,16 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
   int p_kbase = 0, p_lo[NT], p_hi[NT];
   unsigned p_act = 0;
   const typename Eng::NoHook nohook;
-  for (int st_i = 0; st_i <= nitems; ++st_i) {
-    // the buffer of item st_i + 1 held item st_i - 2, last read before the
-    // barrier that ended the previous step
-    if (st_i + 1 < nitems) issue(st_i + 1);
-    const char* prev = tiles + ((st_i + 2) % 3) * St::BYTES;  // item st_i - 1
-    const char* cur = tiles + (st_i % 3) * St::BYTES;
+  // step st_i: item st_i - 1 in `prev`, item st_i in `cur`, item st_i + 1
+  // is transferred into `next` (the buffer of item st_i - 2, last read before
+  // the barrier that ended the previous step)
+  // All reads of the item lists and bitsets come before the step's transfer
+  // is issued (the compiler cannot tell them apart from it and would wait).
+  auto step = [&](int st_i, const char* prev, const char* cur, char* next) {
+    unsigned c_act = 0;
+    int c_kbase = 0, c_lo[NT], c_hi[NT];
+    if (st_i < nitems) c_act = item(st_i, c_kbase, c_lo, c_hi);
+    if (st_i + 1 < nitems) issue(st_i + 1, next);
     auto ldV = [&](int u, int mc) { return St::ldV(prev, u, mc); };
     auto ldK = [&](int c, int ks) { return St::ldK(cur, c, ks); };
     if (lag && st_i >= 1 && p_act)
@@ -674,18 +690,31 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
         fold(gate1, true);
         eng.reset();
       }
-      p_act = item(st_i, p_kbase, p_lo, p_hi);
-      if (p_act) {
+      if (c_act) {
         eng.qk(ldK, sreg);
         __builtin_amdgcn_s_setprio(0);
         if (!lag)
-          eng.template softmax<true, false>(sreg, p_kbase, p_lo, p_hi, a.sc2, bmax, bsum, nohook, p_act);
+          eng.template softmax<true, false>(sreg, c_kbase, c_lo, c_hi, a.sc2, bmax, bsum, nohook, c_act);
       }
     }
     __builtin_amdgcn_s_setprio(0);
+    p_act = c_act;
+    p_kbase = c_kbase;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      p_lo[nt] = c_lo[nt];
+      p_hi[nt] = c_hi[nt];
+    }
     wait_vmem();
-    if (st_i + 1 < nitems) st.dma_fix(tiles + ((st_i + 1) % 3) * St::BYTES);
+    if (st_i + 1 < nitems) st.dma_fix(next);
     __syncthreads();
+  };
+  for (int st_i = 0; st_i <= nitems; st_i += 3) {
+    step(st_i, tile2, tile0, tile1);
+    if (st_i + 1 > nitems) break;
+    step(st_i + 1, tile0, tile1, tile2);
+    if (st_i + 2 > nitems) break;
+    step(st_i + 2, tile1, tile2, tile0);
   }
   if (nwin == nitems) {
     fold(gate1, true);
