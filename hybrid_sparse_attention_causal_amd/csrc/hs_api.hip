@@ -99,8 +99,12 @@ int decode_nch(const hs_shape* s) {
 size_t decode_full_ws(const hs_shape* s) {
   return (size_t)s->batch * s->hq * decode_nch(s) * (s->head_dim + 2) * sizeof(float);
 }
+// keys [rows][C], histograms [rows][2 * 2048], counts [rows] (padded to 4),
+// candidates [rows][kTokCap] keys and ids
 size_t token_topk_ws(const hs_shape* s) {
-  return (size_t)s->batch * s->hkv * ((size_t)s->kv_len + 2048) * sizeof(uint32_t);
+  const size_t rows = (size_t)s->batch * s->hkv;
+  return rows * ((size_t)s->kv_len + 2 * 2048 + 2 * hs::kTokCap) * sizeof(uint32_t) +
+         ((rows + 3) / 4) * 4 * sizeof(uint32_t);
 }
 // Token mode (block = 1) runs on fp8 caches with position-major values; block
 // mode (block = 64) on bf16 caches with block-major values.
@@ -251,8 +255,11 @@ hs_status hs_block_topk(const hs_shape* s, const float* blk_raw, const float* ls
     a.gs = grp_score;
     a.idx = idx;
     a.lens = s->kv_lens;
+    const size_t rows = (size_t)s->batch * s->hkv;
     a.keys = (uint32_t*)ws;
-    a.hist = (uint32_t*)ws + (size_t)s->batch * s->hkv * s->kv_len;
+    a.hist = a.keys + rows * s->kv_len;
+    a.cand_key = a.hist + rows * 2 * 2048 + ((rows + 3) / 4) * 4;
+    a.cand_idx = (int32_t*)(a.cand_key + rows * hs::kTokCap);
     a.B = s->batch;
     a.Hq = s->hq;
     a.Hkv = s->hkv;

@@ -197,50 +197,55 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
   }
 }
 
-// One wave per (b, h): merge the nchb = ceil(L / (CH*64)) partials.
+// One work group of 4 waves per (b, h) merges the nchb = ceil(L / (CH*64))
+// partials: the group finds the common maximum, wave w sums the chunks
+// c = w, w+4, ... (independent loads, unrolled), and the four partial sums
+// are added through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeFullArgs a) {
-  const int lane = threadIdx.x & 63;
-  const long bh = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (bh >= (long)a.B * a.Hq) return;
+  constexpr int PER = D / 64;
+  __shared__ float red[4];
+  __shared__ float accs[4][D + 1];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const long bh = blockIdx.x;
   const int b = (int)(bh / a.Hq);
   const int L = a.lens[b];
   const int span = a.ch_blocks * 64;
   const int nchb = L > 0 ? (L + span - 1) / span : 0;
   const float* pp = a.part + (size_t)bh * a.nch * (D + 2);
   float M = kNegBig;
-  for (int c = lane; c < nchb; c += 64) M = fmaxf(M, pp[(size_t)c * (D + 2) + D]);
+  for (int c = threadIdx.x; c < nchb; c += 256) M = fmaxf(M, pp[(size_t)c * (D + 2) + D]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float lsum = 0.f;
-  for (int c = lane; c < nchb; c += 64) {
-    const float* p = pp + (size_t)c * (D + 2);
-    lsum += p[D + 1] * fast_exp2(p[D] - M);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
-  constexpr int PER = D / 64;
-  float acc[PER];
+  if (lane == 0) red[w] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float acc[PER], lsum = 0.f;
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  // lane c of a 64-chunk group holds that chunk's weight; the loads of the
-  // chunks are independent and unrolled
-  for (int c0 = 0; c0 < nchb; c0 += 64) {
-    const float wl = c0 + lane < nchb ? fast_exp2(pp[(size_t)(c0 + lane) * (D + 2) + D] - M) : 0.f;
-    const int n = min(64, nchb - c0);
-#pragma unroll 8
-    for (int c = 0; c < n; ++c) {
-      const float w = __shfl(wl, c);
-      const float* p = pp + (size_t)(c0 + c) * (D + 2);
+#pragma unroll 4
+  for (int c = w; c < nchb; c += 4) {
+    const float* p = pp + (size_t)c * (D + 2);
+    const float wt = fast_exp2(p[D] - M);
+    lsum += wt * p[D + 1];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] += w * p[lane + 64 * i];
-    }
+    for (int i = 0; i < PER; ++i) acc[i] += wt * p[lane + 64 * i];
   }
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  uint16_t* o = (uint16_t*)a.o + (size_t)bh * D;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) o[lane + 64 * i] = (uint16_t)bf16_bits(acc[i] * inv);
-  if (lane == 0) a.lse[bh] = lsum > 0.f ? (M + fast_log2(lsum)) * kLn2 : -INFINITY;
+  for (int i = 0; i < PER; ++i) accs[w][lane + 64 * i] = acc[i];
+  if (lane == 0) accs[w][D] = lsum;
+  __syncthreads();
+  if (w == 0) {
+    const float lt = accs[0][D] + accs[1][D] + accs[2][D] + accs[3][D];
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    uint16_t* o = (uint16_t*)a.o + (size_t)bh * D;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int d = lane + 64 * i;
+      o[d] = (uint16_t)bf16_bits((accs[0][d] + accs[1][d] + accs[2][d] + accs[3][d]) * inv);
+    }
+    if (lane == 0) a.lse[bh] = lt > 0.f ? (M + fast_log2(lt)) * kLn2 : -INFINITY;
+  }
 }
 
 // ============================================================ sparse layer
@@ -464,12 +469,136 @@ __device__ void find_bin(const uint32_t* h, int nb, int k, uint32_t* scan, int* 
   __syncthreads();
 }
 
+constexpr int kTokSeg = 16384;  // keys per work group in the histogram and candidate passes
+
+// grid (rows, ceil(C / kTokSeg)), 1024 threads: the level-2 histogram (bits
+// 20..10 of the keys whose top 11 bits are the level-1 threshold bin); every
+// group of a row finds that bin again from the level-1 histogram
+__global__ __launch_bounds__(1024) void token_hist2_kernel(TokenTopkArgs a) {
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t scan[1024];
+  __shared__ int res[2];
+  const int row = blockIdx.x, t = threadIdx.x;
+  const int L = a.lens[row / a.Hkv];
+  const int ncand = max(0, L - a.n_recent);
+  const int s0 = blockIdx.y * kTokSeg;
+  if (ncand <= a.kb || s0 >= ncand) return;  // uniform
+  const uint32_t* gh = a.hist + (size_t)row * 2048;
+  for (int i = t; i < 2048; i += 1024) hist[i] = gh[i];
+  __syncthreads();
+  find_bin(hist, 2048, a.kb, scan, res);
+  const uint32_t b1 = (uint32_t)res[0];
+  for (int i = t; i < 2048; i += 1024) hist[i] = 0u;
+  __syncthreads();
+  const uint32_t* keys = a.keys + (size_t)row * a.C;
+  const int s1 = min(ncand, s0 + kTokSeg);
+  for (int i = s0 + t; i < s1; i += 1024) {
+    const uint32_t k = keys[i];
+    if ((k >> 21) == b1) atomicAdd(&hist[(k >> 10) & 2047u], 1u);
+  }
+  __syncthreads();
+  uint32_t* h2 = a.hist + (size_t)a.B * a.Hkv * 2048 + (size_t)row * 2048;
+  for (int i = t; i < 2048; i += 1024)
+    if (hist[i]) atomicAdd(&h2[i], hist[i]);
+}
+
+// grid (rows, ceil(C / kTokSeg)), 1024 threads: compacts the candidates, the
+// keys whose top 22 bits are at least the level-2 threshold prefix (fewer
+// than kb above it plus that prefix's bin), as (key, token id) pairs in
+// arbitrary order; the count may exceed kTokCap (then only the count is kept)
+__global__ __launch_bounds__(1024) void token_cand_kernel(TokenTopkArgs a) {
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t scan[1024];
+  __shared__ int res[2];
+  __shared__ uint32_t base_s;
+  const int row = blockIdx.x, t = threadIdx.x;
+  const int L = a.lens[row / a.Hkv];
+  const int ncand = max(0, L - a.n_recent);
+  const int s0 = blockIdx.y * kTokSeg;
+  if (ncand <= a.kb || s0 >= ncand) return;  // uniform
+  const size_t rows = (size_t)a.B * a.Hkv;
+  for (int i = t; i < 2048; i += 1024) hist[i] = a.hist[(size_t)row * 2048 + i];
+  __syncthreads();
+  find_bin(hist, 2048, a.kb, scan, res);
+  const uint32_t b1 = (uint32_t)res[0];
+  const int need = a.kb - res[1];
+  for (int i = t; i < 2048; i += 1024) hist[i] = a.hist[rows * 2048 + (size_t)row * 2048 + i];
+  __syncthreads();
+  find_bin(hist, 2048, need, scan, res);
+  const uint32_t pfx = (b1 << 11) | (uint32_t)res[0];
+  const uint32_t* keys = a.keys + (size_t)row * a.C;
+  constexpr int PER = kTokSeg / 1024;
+  uint32_t flags = 0u, cnt = 0u;
+#pragma unroll
+  for (int n = 0; n < PER; ++n) {
+    const int i = s0 + t + 1024 * n;
+    if (i < ncand && (keys[i] >> 10) >= pfx) {
+      flags |= 1u << n;
+      ++cnt;
+    }
+  }
+  // block exclusive scan of the per-thread counts
+  scan[t] = cnt;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const uint32_t x = t >= off ? scan[t - off] : 0u;
+    __syncthreads();
+    scan[t] += x;
+    __syncthreads();
+  }
+  const uint32_t excl = scan[t] - cnt;
+  if (t == 1023) base_s = atomicAdd(a.hist + rows * 2 * 2048 + row, scan[1023]);
+  __syncthreads();
+  uint32_t pos = base_s + excl;
+  uint32_t* ck = a.cand_key + (size_t)row * kTokCap;
+  int32_t* ci = a.cand_idx + (size_t)row * kTokCap;
+#pragma unroll
+  for (int n = 0; n < PER; ++n) {
+    if ((flags >> n) & 1u) {
+      const int i = s0 + t + 1024 * n;
+      if (pos < (uint32_t)kTokCap) {
+        ck[pos] = keys[i];
+        ci[pos] = i;
+      }
+      ++pos;
+    }
+  }
+}
+
+// In-place bitonic sort of P (a power of two) LDS entries by `before`
+// (a strict total order); 1024 threads.
+template <class BF>
+__device__ void bitonic_sort(uint32_t* k, int32_t* v, int P, const BF& before) {
+  const int t = threadIdx.x;
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int e = t; e < P / 2; e += 1024) {
+        const int lo = 2 * e - (e & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const bool sw = up ? before(k[hi], v[hi], k[lo], v[lo]) : before(k[lo], v[lo], k[hi], v[hi]);
+        if (sw) {
+          const uint32_t tk = k[lo];
+          k[lo] = k[hi];
+          k[hi] = tk;
+          const int32_t tv = v[lo];
+          v[lo] = v[hi];
+          v[hi] = tv;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
 // one work group (1024 threads) per (sequence, kv group) row
 __global__ __launch_bounds__(1024) void token_select_kernel(TokenTopkArgs a) {
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t scan[1024];
   __shared__ int res[2];
   __shared__ uint32_t wsum[32];
+  __shared__ uint32_t cand_k[kTokCap];
+  __shared__ int32_t cand_i[kTokCap];
   const int row = blockIdx.x;
   const int b = row / a.Hkv;
   const int L = a.lens[b];
@@ -482,9 +611,35 @@ __global__ __launch_bounds__(1024) void token_select_kernel(TokenTopkArgs a) {
   int32_t* out = a.idx + (size_t)row * (kb + a.n_recent);
   int nsel;
 
+  const uint32_t ncnd = a.hist[(size_t)a.B * a.Hkv * 2 * 2048 + row];
   if (ncand <= kb) {
     for (int i = t; i < ncand; i += 1024) out[i] = i;
     nsel = ncand;
+  } else if (ncnd <= (uint32_t)kTokCap) {
+    // the candidates (at least kb, all keys above the threshold prefix):
+    // sort by key descending, ties to the smaller id, keep kb, then sort
+    // the kept ids ascending
+    uint32_t* sk = cand_k;
+    int32_t* si = cand_i;
+    int P = 64;
+    while (P < (int)ncnd) P <<= 1;
+    const uint32_t* ck = a.cand_key + (size_t)row * kTokCap;
+    const int32_t* ci = a.cand_idx + (size_t)row * kTokCap;
+    for (int e = t; e < P; e += 1024) {
+      sk[e] = e < (int)ncnd ? ck[e] : 0u;
+      si[e] = e < (int)ncnd ? ci[e] : 0x7fffffff;
+    }
+    __syncthreads();
+    bitonic_sort(sk, si, P, [](uint32_t ka, int32_t ia, uint32_t kb_, int32_t ib) {
+      return ka > kb_ || (ka == kb_ && ia < ib);
+    });
+    int Q = 64;
+    while (Q < kb) Q <<= 1;
+    for (int e = t; e < Q; e += 1024) sk[e] = e < kb ? (uint32_t)si[e] : 0xffffffffu;
+    __syncthreads();
+    bitonic_sort(sk, si, Q, [](uint32_t ka, int32_t, uint32_t kb_, int32_t) { return ka < kb_; });
+    for (int e = t; e < kb; e += 1024) out[e] = (int32_t)sk[e];
+    nsel = kb;
   } else {
     // level 1: the global histogram of the top 11 bits
     const uint32_t* gh = a.hist + (size_t)row * 2048;
@@ -671,7 +826,7 @@ hipError_t launch_decode_full(const DecodeFullArgs& a, int D, hipStream_t s) {
   else decode_full_dispatch<64>(a, grid, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 g2((unsigned)(((long)a.B * a.Hq + 3) / 4));
+  dim3 g2((unsigned)((long)a.B * a.Hq));
   if (D == 128) hipLaunchKernelGGL(decode_combine_kernel<128>, g2, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(decode_combine_kernel<64>, g2, dim3(256), 0, s, a);
   return hipGetLastError();
@@ -690,11 +845,18 @@ namespace hs {
 
 hipError_t launch_token_topk(const TokenTopkArgs& a, hipStream_t s) {
   const long rows = (long)a.B * a.Hkv;
-  hipLaunchKernelGGL(zero_u32_kernel, dim3(256), dim3(256), 0, s, a.hist, rows * 2048);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(256), dim3(256), 0, s, a.hist, rows * 2 * 2048 + rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(token_keys_kernel, dim3((unsigned)rows, (unsigned)((a.C + 4095) / 4096)), dim3(256), 0,
                      s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 seg((unsigned)rows, (unsigned)((a.C + kTokSeg - 1) / kTokSeg));
+  hipLaunchKernelGGL(token_hist2_kernel, seg, dim3(1024), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(token_cand_kernel, seg, dim3(1024), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(token_select_kernel, dim3((unsigned)rows), dim3(1024), 0, s, a);

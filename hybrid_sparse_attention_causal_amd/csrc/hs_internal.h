@@ -86,9 +86,15 @@ struct TokenTopkArgs {
   int32_t* idx;           // [B][Hkv][kb + n_recent]
   const int32_t* lens;
   uint32_t* keys;         // workspace [B*Hkv][C]
-  uint32_t* hist;         // workspace [B*Hkv][2048]
+  uint32_t* hist;         // workspace [B*Hkv][2048] level-1, then [B*Hkv][2048] level-2,
+                          // then [B*Hkv] candidate counts (zeroed together)
+  uint32_t* cand_key;     // workspace [B*Hkv][kTokCap]
+  int32_t* cand_idx;      // workspace [B*Hkv][kTokCap]
   int B, Hq, Hkv, C, kb, n_recent;
 };
+// candidates kept per row for the final exact selection (rows with more fall
+// back to a radix select over the whole row)
+constexpr int kTokCap = 8192;
 
 hipError_t launch_token_topk(const TokenTopkArgs& a, hipStream_t s);
 hipError_t launch_decode_sparse_token(const DecodeSparseArgs& a, int D, hipStream_t s);
