@@ -17,10 +17,10 @@ namespace hs {
 // Work group = 4 wavefronts.  With Gw = min(G, 4) query heads of one kv group
 // per work group, wave w takes head hb*Gw + w%Gw and 16*NT consecutive query
 // positions; all waves of a group share the same K/V tiles, staged through LDS
-// (double-buffered, K rows stored in S^T row order, V tiles copied d-major as
-// they are in memory).  Grid: x = head blocks (fast, so consecutive groups land
-// on the same XCD when Hq/Gw is a multiple of 8), y = position tiles, longest
-// (latest) first.
+// by direct global-to-LDS transfers (double-buffered, K rows stored in S^T row
+// order, V tiles d-major as they are in memory).  Grid: x = head blocks (fast,
+// so consecutive groups land on the same XCD when Hq/Gw is a multiple of 8),
+// y = position tiles, longest (latest) first.
 template <int DT, int D, int NT, int SCORE_LSE>
 __global__ __launch_bounds__(256, (DT == HS_F32 && D == 128) ? 1 : 2) void full_prefill_kernel(FullPrefillArgs a) {
   using Tt = Tr<DT>;
@@ -28,7 +28,11 @@ __global__ __launch_bounds__(256, (DT == HS_F32 && D == 128) ? 1 : 2) void full_
   using St = TileStage<DT, D, 256>;
   constexpr int ES = Tt::ES;
   constexpr int PWAVE = 16 * NT;
-  __shared__ __attribute__((aligned(16))) char smem[2 * St::BYTES];
+  // two tile buffers as separate arrays, the loop unrolled by two: every
+  // access names its buffer, so reads of one are not held up by the transfer
+  // in flight into the other
+  __shared__ __attribute__((aligned(16))) char buf0[St::BYTES];
+  __shared__ __attribute__((aligned(16))) char buf1[St::BYTES];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int G = a.Hq / a.Hkv;
@@ -49,7 +53,10 @@ __global__ __launch_bounds__(256, (DT == HS_F32 && D == 128) ? 1 : 2) void full_
   const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * T * D * ES;
   const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
   St st;
-  auto gload = [&](int j) { st.gload(kg + (size_t)64 * j * D * ES, vg + (size_t)j * D * 64 * ES, T - 64 * j); };
+  st.dma_init();
+  auto issue = [&](int j, char* buf) {
+    st.dma(buf, kg + (size_t)64 * j * D * ES, vg + (size_t)j * D * 64 * ES, T - 64 * j);
+  };
 
   Eng eng;
   eng.reset();
@@ -68,15 +75,15 @@ __global__ __launch_bounds__(256, (DT == HS_F32 && D == 128) ? 1 : 2) void full_
   }
 
   wait_vmem();
-  gload(0);
-  st.sstore(smem);
+  issue(0, buf0);
+  wait_vmem();
+  st.dma_fix(buf0);
   __syncthreads();
-  for (int j = 0; j <= jmax; ++j) {
-    const char* buf = smem + (j & 1) * St::BYTES;
-    if (j < jmax) gload(j + 1);
+  auto step = [&](int j, const char* cur, char* next) {
+    if (j < jmax) issue(j + 1, next);
     if (64 * j <= plast) {
-      auto ldK = [&](int c, int ks) { return St::ldK(buf, c, ks); };
-      auto ldV = [&](int u, int mc) { return St::ldV(buf, u, mc); };
+      auto ldK = [&](int c, int ks) { return St::ldK(cur, c, ks); };
+      auto ldV = [&](int u, int mc) { return St::ldV(cur, u, mc); };
       float bmax[NT], bsum[NT];
       f32x4 s[NT][4];
       __builtin_amdgcn_s_setprio(1);
@@ -100,8 +107,14 @@ __global__ __launch_bounds__(256, (DT == HS_F32 && D == 128) ? 1 : 2) void full_
         }
       }
     }
-    if (j < jmax) st.sstore(smem + ((j + 1) & 1) * St::BYTES);
+    wait_vmem();
+    if (j < jmax) st.dma_fix(next);
     __syncthreads();
+  };
+  for (int j = 0; j <= jmax; j += 2) {
+    step(j, buf0, buf1);
+    if (j + 1 > jmax) break;
+    step(j + 1, buf1, buf0);
   }
 
 #pragma unroll
