@@ -190,6 +190,8 @@ def bench_decode(cid: int, steps: int):
                        g=dev(lay["gates"]))
         layers.append(ent)
     stream = torch.cuda.current_stream()
+    nsel_ws = hb.workspace_size(hb.HS_FN_DECODE_SELECT, shape, blk)
+    ws_sel = torch.empty(max(16, nsel_ws), dtype=torch.uint8, device="cuda")
 
     def step():
         hb.decode_full_attn_scores(q, k, v, lens, o, lse, raw, block=blk, ws=ws_full,
@@ -199,7 +201,7 @@ def bench_decode(cid: int, steps: int):
         for l in layers:
             if token:
                 hb.decode_select_attn(l["q"], k, v, lens, idx, nsel, None, None, 0, None, l["o"],
-                                      block=1, kv_scale=scale, stream=stream)
+                                      block=1, kv_scale=scale, stream=stream, ws=ws_sel)
             else:
                 hb.decode_select_attn(l["q"], k, v, lens, idx, nsel, l["kr"], l["vr"], cfg.W, l["g"],
                                       l["o"], stream=stream)

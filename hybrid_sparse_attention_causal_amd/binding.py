@@ -195,14 +195,20 @@ def decode_block_topk(q, k, lens, raw, lse, topk, idx, grp_score=None, block=64,
 
 
 def decode_select_attn(q_sp, k, v, lens, idx, n_sel, k_ring, v_ring, window, gate_logits, o,
-                       block=64, kv_scale=None, scale=0.0, stream=None):
+                       block=64, kv_scale=None, scale=0.0, stream=None, ws=None):
     """One decode sparse layer.  q_sp/o [B,Hq,d]; idx [B,Hkv,n_sel];
-    k_ring [B,Hkv,W,d]; v_ring [B,Hkv,ceil(W/64),d,64]; gates [B,Hq,2] or None."""
+    k_ring [B,Hkv,W,d]; v_ring [B,Hkv,ceil(W/64),d,64]; gates [B,Hq,2] or None.
+    ws: uint8 device workspace (allocated here when None and one is needed)."""
     _contig(q_sp, k, v, lens, idx, k_ring, v_ring, gate_logits, o)
     s = decode_shape(q_sp, k, lens, kv_scale, scale)
+    if ws is None:
+        need = workspace_size(HS_FN_DECODE_SELECT, s, block)
+        ws = torch.empty(need, dtype=torch.uint8, device=q_sp.device) if need else None
     _check(load().hs_decode_select_attn(ctypes.byref(s), _ptr(q_sp), _ptr(k), _ptr(v), _ptr(idx),
                                         n_sel, block, _ptr(k_ring), _ptr(v_ring), window,
-                                        _ptr(gate_logits), _ptr(o), None, 0, _stream(stream)))
+                                        _ptr(gate_logits), _ptr(o), _ptr(ws),
+                                        0 if ws is None else ws.numel(), _stream(stream)))
+    return ws
 
 
 def version() -> int:

@@ -106,6 +106,12 @@ size_t token_topk_ws(const hs_shape* s) {
   return rows * ((size_t)s->kv_len + 2 * 2048 + 2 * hs::kTokCap) * sizeof(uint32_t) +
          ((rows + 3) / 4) * 4 * sizeof(uint32_t);
 }
+// token-mode sparse layer: partial states of up to kTokSplitMax work groups per
+// (sequence, group)
+size_t decode_select_ws(const hs_shape* s, int block) {
+  if (block != 1 || s->hkv <= 0) return 0;
+  return (size_t)s->batch * s->hkv * hs::kTokSplitMax * (s->hq / s->hkv) * (s->head_dim + 2) * sizeof(float);
+}
 // Token mode (block = 1) runs on fp8 caches with position-major values; block
 // mode (block = 64) on bf16 caches with block-major values.
 hs_status check_decode_block(const char* fn, const hs_shape* s, int block) {
@@ -142,6 +148,7 @@ size_t hs_workspace_size(int fn_id, const hs_shape* shape, int block, int topk, 
   if (!shape || shape->struct_size < sizeof(hs_shape) || !shape->kv_lens) return 0;
   if (fn_id == HS_FN_FULL_ATTN) return decode_full_ws(shape);
   if (fn_id == HS_FN_BLOCK_TOPK && block == 1) return token_topk_ws(shape);
+  if (fn_id == HS_FN_DECODE_SELECT) return decode_select_ws(shape, block);
   return 0;
 }
 
@@ -355,8 +362,6 @@ hs_status hs_decode_select_attn(const hs_shape* s, const void* q_sp, const void*
                                 const void* v_ring, int window, const float* gate_logits, void* o,
                                 void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "hs_decode_select_attn";
-  (void)ws;
-  (void)ws_bytes;
   hs_status st = check_decode(fn, s);
   if (st) return st;
   st = check_decode_block(fn, s, block);
@@ -397,7 +402,19 @@ hs_status hs_decode_select_attn(const hs_shape* s, const void* q_sp, const void*
   a.W = window;
   a.kv_scale = s->kv_scale;
   a.sc2 = scale_log2(s);
-  if (block == 1) return launched(fn, hs::launch_decode_sparse_token(a, s->head_dim, (hipStream_t)stream));
+  a.nsplit = 1;
+  if (block == 1) {
+    // with a workspace, each (sequence, group) is spread over several work
+    // groups (about eight 64-token tiles each) and merged by a second kernel
+    const int ntile = (n_sel + 63) / 64;
+    const int nsp = ntile / 8 < 1 ? 1 : (ntile / 8 > hs::kTokSplitMax ? hs::kTokSplitMax : ntile / 8);
+    if (nsp > 1 && ws && ws_bytes >= decode_select_ws(s, block)) {
+      if (!aligned16(ws)) return fail(HS_ERR_INVALID_ARG, "%s: ws not 16-byte aligned", fn);
+      a.part = (float*)ws;
+      a.nsplit = nsp;
+    }
+    return launched(fn, hs::launch_decode_sparse_token(a, s->head_dim, (hipStream_t)stream));
+  }
   return launched(fn, hs::launch_decode_sparse(a, s->head_dim, (hipStream_t)stream));
 }
 

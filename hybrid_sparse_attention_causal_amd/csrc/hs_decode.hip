@@ -750,7 +750,9 @@ __global__ __launch_bounds__(512) void decode_sparse_token_kernel(DecodeSparseAr
   float bmax[1], bsum[1];
   int lo[1], hi[1];
 
-  for (int it = w; it < ntile; it += NW) {
+  // work group blockIdx.y of gridDim.y takes every gridDim.y-th group of
+  // eight tiles
+  for (int it = blockIdx.y * NW + w; it < ntile; it += gridDim.y * NW) {
     const int s0 = 64 * it;
     int tok = s0 + lane < a.nsel ? il[s0 + lane] : -1;
     if (tok >= L) tok = -1;
@@ -802,6 +804,52 @@ __global__ __launch_bounds__(512) void decode_sparse_token_kernel(DecodeSparseAr
       const float wt = fast_exp2(sm_m[ww][c] - M);
       ls += wt * sm_l[ww][c];
       os += wt * sm_o[ww][c][d];
+    }
+    if (gridDim.y == 1) {
+      ((uint16_t*)a.o)[((size_t)b * a.Hq + g * G + c) * D + d] =
+          (uint16_t)bf16_bits(ls > 0.f ? sv * os / ls : 0.f);
+    } else {
+      // partial state of this work group: unnormalised o, then m and l
+      float* pp = a.part + (((size_t)bg * gridDim.y + blockIdx.y) * G + c) * (D + 2);
+      pp[d] = os;
+      if (d == 0) {
+        pp[D] = M;
+        pp[D + 1] = ls;
+      }
+    }
+  }
+}
+
+// one work group per (b, g): merges the nsplit partial states of the token
+// sparse layer
+template <int D>
+__global__ __launch_bounds__(1024) void decode_token_combine_kernel(DecodeSparseArgs a) {
+  const int bg = blockIdx.x;
+  const int g = bg % a.Hkv, b = bg / a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const float sv = a.kv_scale[a.Hkv + g];
+  for (int el = threadIdx.x; el < G * D; el += 1024) {
+    const int c = el / D, d = el % D;
+    const float* pp = a.part + ((size_t)bg * a.nsplit * G + c) * (D + 2);
+    const size_t st = (size_t)G * (D + 2);
+    // all loads of the (at most kTokSplitMax) partials are issued together
+    float m[kTokSplitMax], l[kTokSplitMax], x[kTokSplitMax];
+#pragma unroll
+    for (int sp = 0; sp < kTokSplitMax; ++sp) {
+      const bool in = sp < a.nsplit;
+      m[sp] = in ? pp[sp * st + D] : kNegBig;
+      l[sp] = in ? pp[sp * st + D + 1] : 0.f;
+      x[sp] = in ? pp[sp * st + d] : 0.f;
+    }
+    float M = kNegBig;
+#pragma unroll
+    for (int sp = 0; sp < kTokSplitMax; ++sp) M = fmaxf(M, m[sp]);
+    float ls = 0.f, os = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < kTokSplitMax; ++sp) {
+      const float wt = fast_exp2(m[sp] - M);
+      ls += wt * l[sp];
+      os += wt * x[sp];
     }
     ((uint16_t*)a.o)[((size_t)b * a.Hq + g * G + c) * D + d] = (uint16_t)bf16_bits(ls > 0.f ? sv * os / ls : 0.f);
   }
@@ -864,9 +912,14 @@ hipError_t launch_token_topk(const TokenTopkArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_decode_sparse_token(const DecodeSparseArgs& a, int D, hipStream_t s) {
-  dim3 grid((unsigned)(a.B * a.Hkv));
+  dim3 grid((unsigned)(a.B * a.Hkv), (unsigned)a.nsplit);
   if (D == 128) hipLaunchKernelGGL(decode_sparse_token_kernel<128>, grid, dim3(512), 0, s, a);
   else hipLaunchKernelGGL(decode_sparse_token_kernel<64>, grid, dim3(512), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  dim3 g2((unsigned)(a.B * a.Hkv));
+  if (D == 128) hipLaunchKernelGGL(decode_token_combine_kernel<128>, g2, dim3(1024), 0, s, a);
+  else hipLaunchKernelGGL(decode_token_combine_kernel<64>, g2, dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 

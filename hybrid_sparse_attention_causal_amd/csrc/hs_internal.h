@@ -75,9 +75,12 @@ struct DecodeSparseArgs {
   void* o;
   const int32_t* lens;
   const float* kv_scale;  // fp8 token mode: device [2][Hkv]
-  int B, Hq, Hkv, C, nsel, W;
+  float* part;            // token mode, nsplit > 1: workspace [B*Hkv][nsplit][G][D+2]
+  int B, Hq, Hkv, C, nsel, W, nsplit;
   float sc2;
 };
+// token-mode sparse decode: work groups per (sequence, group) at most
+constexpr int kTokSplitMax = 8;
 
 struct TokenTopkArgs {
   const float* raw;       // [B][Hq][C] per-token logits

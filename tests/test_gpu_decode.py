@@ -239,3 +239,26 @@ def test_config5_token_level_full_size_sampled():
     inp = gen.make_decode(gen.config(5), n_layers=2)
     run = TokenRun(inp)
     check_token_sequences(run, [0, 7, 15])
+
+
+def test_token_split_work_groups():
+    """Token-mode sparse layer spread over several work groups per (sequence,
+    group) (workspace given) against the oracle and against the one-group
+    path (no workspace), on ragged lengths with many empty tail tiles."""
+    say("[token split] fp8, C=16384, top-1500 + 100 recent, lens 1..16384")
+    cfg = gen.config(5, B=4, T=16384, Hq=8, Hkv=2, d=128, kb=1500, n_recent=100, N=1,
+                     L_lo=1, L_hi=16384)
+    inp = gen.make_decode(cfg)
+    inp.lens = np.array([3, 900, 7777, 16384], np.int32)
+    run = TokenRun(inp)
+    check_token_sequences(run, range(4))
+    lay = inp.layers[0]
+    B, Hq, d = cfg.B, cfg.Hq, cfg.d
+    o1 = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    tiny = torch.empty(16, dtype=torch.uint8, device="cuda")  # too small: one group per (b, g)
+    hb.decode_select_attn(dev(lay["q"]), run.k, run.v, run.lens, run.idx, cfg.kb + cfg.n_recent,
+                          None, None, 0, None, o1, block=1, kv_scale=run.scale, ws=tiny)
+    torch.cuda.synchronize()
+    a, b = host(run.outs[0]), host(o1)
+    say(f"  split vs one group max|dO|={np.abs(a - b).max():.3g}")
+    assert not np.isnan(b).any() and np.abs(a - b).max() <= 2e-2
