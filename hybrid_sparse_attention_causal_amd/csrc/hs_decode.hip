@@ -401,7 +401,9 @@ __global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* p, long n) {
   for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) p[i] = 0u;
 }
 
-// grid (rows, C/4096): keys for 4096 tokens and the level-1 histogram (top 11 bits)
+// grid (rows, C/4096): keys for 4096 tokens and the level-1 histogram (top 11
+// bits).  Thread t takes the token quads t, t + 256, t + 512, t + 768 of the
+// group's 4096 tokens: 16-byte loads of each head's logits, all in flight.
 __global__ __launch_bounds__(256) void token_keys_kernel(TokenTopkArgs a) {
   __shared__ uint32_t hist[2048];
   const int row = blockIdx.x;
@@ -412,24 +414,39 @@ __global__ __launch_bounds__(256) void token_keys_kernel(TokenTopkArgs a) {
   for (int i = threadIdx.x; i < 2048; i += 256) hist[i] = 0u;
   __syncthreads();
   const int base = blockIdx.y * 4096;
-  float ls[16];
-  for (int hh = 0; hh < G; ++hh) ls[hh] = a.lse[(size_t)b * a.Hq + g * G + hh];
   uint32_t* keys = a.keys + (size_t)row * a.C;
-  for (int n = 0; n < 16; ++n) {
-    const int i = base + threadIdx.x + 256 * n;
-    if (i >= a.C) break;
-    uint32_t key = 0u;
-    if (i < L) {
-      float x = -INFINITY;
-      for (int hh = 0; hh < G; ++hh)
-        x = fmaxf(x, a.raw[((size_t)b * a.Hq + g * G + hh) * a.C + i] - ls[hh]);
-      if (a.gs) a.gs[(size_t)row * a.C + i] = expf(x);
-      if (i < ncand) {
-        key = order_key_f(x);
-        atomicAdd(&hist[key >> 21], 1u);
+  const float* rg = a.raw + ((size_t)b * a.Hq + g * G) * a.C;
+  const float* lse = a.lse + (size_t)b * a.Hq + g * G;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int i0 = base + 4 * (threadIdx.x + 256 * n);
+    if (i0 >= a.C) break;  // C is a multiple of 64
+    float4 x = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    if (i0 < L) {
+      for (int hh = 0; hh < G; ++hh) {
+        const float4 r = *(const float4*)(rg + (size_t)hh * a.C + i0);
+        const float l = lse[hh];
+        x.x = fmaxf(x.x, r.x - l);
+        x.y = fmaxf(x.y, r.y - l);
+        x.z = fmaxf(x.z, r.z - l);
+        x.w = fmaxf(x.w, r.w - l);
       }
     }
-    keys[i] = key;
+    const float xs[4] = {x.x, x.y, x.z, x.w};
+    uint32_t kq[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = i0 + e;
+      kq[e] = 0u;
+      if (i < L) {
+        if (a.gs) a.gs[(size_t)row * a.C + i] = expf(xs[e]);
+        if (i < ncand) {
+          kq[e] = order_key_f(xs[e]);
+          atomicAdd(&hist[kq[e] >> 21], 1u);
+        }
+      }
+    }
+    *(uint4*)(keys + i0) = make_uint4(kq[0], kq[1], kq[2], kq[3]);
   }
   __syncthreads();
   uint32_t* gh = a.hist + (size_t)row * 2048;
