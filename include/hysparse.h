@@ -30,12 +30,15 @@
  *     (thread-local) describes the problem.  HS_ERR_LAUNCH reports a failed
  *     kernel launch.
  *   - Query head h belongs to kv head floor(h / G), G = hq / hkv (contiguous
- *     GQA grouping).  G must be a power of two <= 64; head_dim is 64 or 128.
- *   - Value caches use a block-major layout: each run of 64 consecutive
+ *     GQA grouping).  G must be a power of two <= 32 (<= 16 for the sparse
+ *     layers and for decode); head_dim is 64 or 128.
+ *   - Value tensors use a block-major layout: each run of 64 consecutive
  *     positions of one kv head is stored as a [head_dim][64] tile, i.e. a
- *     value tensor is [batch][hkv][ceil(len/64)][head_dim][64].  Key caches
- *     are position-major [batch][hkv][len][head_dim].  Tail entries of the
- *     last value tile (positions >= len) are never used and may hold anything.
+ *     value tensor is [batch][hkv][ceil(len/64)][head_dim][64].  The one
+ *     exception is the fp8 value cache of token-level decode, which is
+ *     position-major like the keys.  Key tensors are position-major
+ *     [batch][hkv][len][head_dim].  Tail entries of the last value tile
+ *     (positions >= len) are never used and may hold anything.
  *   - The softmax scale is shape.scale, or 1/sqrt(head_dim) when it is 0.
  */
 #ifndef HYSPARSE_H
@@ -102,12 +105,15 @@ typedef struct hs_shape {
  *     post-softmax score of the pages is exp(blk_raw - lse).  Entries
  *     j > floor(t/64) are not written.
  * Decode (kv_lens != NULL, q_len == 1), capacity C = kv_len (multiple of 64):
- *   q [batch][hq][head_dim] (dtype); k [batch][hkv][C][head_dim];
- *   v [batch][hkv][C/64][head_dim][64] (kv_dtype; fp8 needs kv_scale);
+ *   q [batch][hq][head_dim] (dtype, bf16); k [batch][hkv][C][head_dim];
+ *   block = 64: bf16 caches, v [batch][hkv][C/64][head_dim][64];
+ *   block = 1 (token-level variant): fp8 e4m3 caches with kv_scale,
+ *     v [batch][hkv][C][head_dim] (position-major);
  *   o [batch][hq][head_dim]; lse [batch][hq];
  *   blk_raw [batch][hq][C/block]: block = 64 gives block scores as above for
  *   j <= floor((L_b-1)/64); block = 1 gives every token's logit tau q.k_i for
- *   i < L_b (the token-level variant).  Needs a workspace.
+ *   i < L_b.  Needs a workspace of hs_workspace_size(HS_FN_FULL_ATTN, ...)
+ *   bytes (the split-K partial states).
  * `block` must be 64 in prefill and 64 or 1 in decode.
  */
 hs_status hs_full_attn_fwd_scores(const hs_shape* shape, const void* q, const void* k,
@@ -169,7 +175,14 @@ hs_status hs_sparse_attn_fwd(const hs_shape* shape, const void* q_sp, const void
  *   k_ring, v_ring: the layer's own window ring [batch][hkv][W][head_dim]
  *   and [batch][hkv][ceil(W/64)][head_dim][64] (slot = position mod W), or
  *   NULL with window == 0.  gate_logits [batch][hq][2] or NULL.
- *   o [batch][hq][head_dim] (out).  Needs a workspace.
+ *   o [batch][hq][head_dim] (out).
+ * Token mode (block = 1, fp8 caches as in hs_full_attn_fwd_scores) has no
+ * window branch and no gate (the newest tokens are part of idx).  Block mode
+ * takes no workspace.  Token mode takes an optional one: with
+ * ws_bytes >= hs_workspace_size(HS_FN_DECODE_SELECT, shape, 1, 0, 0) every
+ * (sequence, kv head) is spread over several work groups and merged by a
+ * second kernel; with less (or NULL) one work group handles it.  Results
+ * agree to rounding either way.
  */
 hs_status hs_decode_select_attn(const hs_shape* shape, const void* q_sp, const void* k,
                                 const void* v, const int32_t* idx, int n_sel, int block,
@@ -183,8 +196,11 @@ hs_status hs_decode_select_attn(const hs_shape* shape, const void* q_sp, const v
 #define HS_FN_SPARSE_ATTN 2
 #define HS_FN_DECODE_SELECT 3
 
-/* Workspace bytes the given entry point needs for this shape (0 if none).
- * `block`, `topk` and `window` are the values that will be passed to it. */
+/* Workspace bytes the given entry point needs (or, for token-mode
+ * hs_decode_select_attn, can use) for this shape; 0 if none.  `block`,
+ * `topk` and `window` are the values that will be passed to it.  The
+ * workspace is scratch: its contents need no initialisation and are not
+ * preserved. */
 size_t hs_workspace_size(int fn_id, const hs_shape* shape, int block, int topk, int window);
 
 /* Thread-local description of the last error of this thread ("" if none). */
