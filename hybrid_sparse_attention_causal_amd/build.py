@@ -54,6 +54,11 @@ def build_library(verbose: bool = False) -> str:
         outs = list(ex.map(compile_one, zip(srcs, objs)))
     tmp = LIB + ".tmp"
     outs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]))
+    # every kernel launch stub must be defined in the library itself
+    missing = [l.split()[-1] for l in _run(["nm", "-D", "--undefined-only", tmp]).splitlines()
+               if "__device_stub__" in l]
+    if missing:
+        raise RuntimeError(f"libhysparse.so leaves kernel launch stubs undefined: {missing[:4]}")
     os.replace(tmp, LIB)
     if verbose:
         for o in outs:

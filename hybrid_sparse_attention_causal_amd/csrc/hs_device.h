@@ -56,11 +56,13 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // Reductions over the four lanes {l, l^16, l^32, l^48} that hold one MFMA
 // column, with the gfx950 row-swap instructions (no LDS traffic).  Every
 // lane of the group gets the same result.
+// max(a, b) for non-NaN a, b as one v_med3_f32 (fmaxf adds NaN quieting)
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
 __device__ __forceinline__ float xlane_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  v = max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
   const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+  return max2(__uint_as_float(t[0]), __uint_as_float(t[1]));
 }
 __device__ __forceinline__ float xlane_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -357,7 +359,7 @@ struct TileStage {
   static_assert(NDMA * NWV * 1024 == BYTES && (KB / 1024) % NWV == 0, "tile does not split into wave chunks");
   static constexpr int NDK = KB / 1024 / NWV;  // instructions 0..NDK-1 are key rows
   int dkey[NDK > 0 ? NDK : 1];
-  int doff[NDMA];
+  uint32_t doff[NDMA];  // source byte offset in the tile (key rows: of the unclamped row)
   __device__ __forceinline__ void dma_init() {
     const int lane = lane_id(), w = threadIdx.x >> 6;
 #pragma unroll
@@ -366,21 +368,35 @@ struct TileStage {
       if (n < NDK) {
         const int r = off / KS, c = ((off % KS) >> 4) ^ (r & KSW);
         dkey[n] = tile_key(r >> 4, r & 15);
-        doff[n] = c * 16;
+        doff[n] = dkey[n] * KS + c * 16;
       } else {
         const int v = off - KB, dd = v / VS, c = ((v % VS) >> 4) ^ (dd & VSW);
         doff[n] = dd * VS + c * 16;
       }
     }
   }
+  // krows, vslab and nk must be wave-uniform
   __device__ __forceinline__ void dma(char* buf, const char* krows, const char* vslab, int nk) {
     nk_ = nk;
     const int w = threadIdx.x >> 6;
+    // (the source pointer goes through a named variable: passing the
+    // conditional expression straight to the builtin makes the host pass of
+    // this compiler drop the launch stubs of some kernel instantiations)
+    if (nk >= 64) {  // whole tile: scalar base + per-lane offset
 #pragma unroll
-    for (int n = 0; n < NDMA; ++n) {
-      const char* src = n < NDK ? krows + (size_t)min(dkey[n < NDK ? n : 0], nk - 1) * KS + doff[n] : vslab + doff[n];
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + (w + NWV * n) * 1024), 16,
-                                       0, 0);
+      for (int n = 0; n < NDMA; ++n) {
+        const char* src = n < NDK ? krows + doff[n] : vslab + doff[n];
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + (w + NWV * n) * 1024),
+                                         16, 0, 0);
+      }
+    } else {  // ragged last tile: key rows past nk read row nk-1 instead
+#pragma unroll
+      for (int n = 0; n < NDMA; ++n) {
+        const int kk = dkey[n < NDK ? n : 0];
+        const char* src = n < NDK ? krows + (doff[n] - (uint32_t)((kk - min(kk, nk - 1)) * KS)) : vslab + doff[n];
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + (w + NWV * n) * 1024),
+                                         16, 0, 0);
+      }
     }
   }
   // after this wave's transfers have landed (vmcnt 0): zero the value
@@ -391,7 +407,7 @@ struct TileStage {
     constexpr int EPW = 4 / ES;
 #pragma unroll
     for (int n = NDK; n < NDMA; ++n) {
-      const int k0 = ((doff[n] % VS) >> 4) * (16 / ES);
+      const int k0 = (((int)doff[n] % VS) >> 4) * (16 / ES);
       if (k0 + 16 / ES > nk_) {
         uint4* p = (uint4*)(buf + (w + NWV * n) * 1024 + 16 * lane);
         const uint4 x = *p;
@@ -505,7 +521,6 @@ struct WaveAttn {
   __device__ __forceinline__ void softmax(f32x4 (&s)[NT][4], int kbase, const int* lo, const int* hi, float sc2,
                                           float* bmax, float* bsum, const HK& hook = HK(), unsigned act = kAll) {
     const int lane = lane_id();
-    const int q4 = (lane >> 4) << 2;
     bool ranged = false, off = false;
     if (MASK) {
       bool part = false, dis = false;

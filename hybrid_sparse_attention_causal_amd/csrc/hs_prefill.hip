@@ -564,7 +564,7 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
   st.dma_init();
   auto issue = [&](int i, char* buf) {  // item i -> buf (tile i % 3), in flight until wait_vmem
     const bool win = i < nwin;
-    const int j = win ? jw0 + i : ulist[i - nwin];
+    const int j = __builtin_amdgcn_readfirstlane(win ? jw0 + i : ulist[i - nwin]);
     st.dma(buf, (win ? ksg : kg) + (size_t)64 * j * D * ES, (win ? vsg : vg) + (size_t)j * D * 64 * ES,
            T - 64 * j);
   };

@@ -22,6 +22,16 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(hs_[a-z_0-9]+)\s*\(", src)))
 
 
+def test_no_undefined_library_symbols():
+    """Every symbol of the library's own code (kernel launch stubs included)
+    is defined in it: an undefined one would only fail at its first launch."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", hb.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    own = [l.split()[-1] for l in out.splitlines() if "_ZN2hs" in l or l.split()[-1].startswith("hs_")]
+    assert not own, own[:5]
+
+
 def test_exports_every_declared_symbol():
     lib = hb.load()
     names = declared_functions()
