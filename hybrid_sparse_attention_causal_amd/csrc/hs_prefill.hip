@@ -134,6 +134,152 @@ __global__ __launch_bounds__(256, (DT == HS_F32 && D == 128) ? 1 : 2) void full_
   }
 }
 
+// Full layer, 8-wavefront ping-pong variant (G <= 16): the work group takes
+// 8*32/G consecutive positions of one kv group; wave w holds NT = 2 column
+// tiles of the G heads of 16/G positions each (as in the sparse layer), all
+// eight waves read the same K/V tile, staged by direct transfers into three
+// named LDS buffers one tile ahead, and waves w / w+4 run half a tile out of
+// phase (A: P(s-1)V | QK(s) | softmax(s), B: softmax(s-1) | P(s-1)V | QK(s)).
+// Block scores are written when a tile's softmax is done.
+template <int DT, int D, int SCORE_LSE>
+__global__ __launch_bounds__(512, 2) void full_prefill_pp_kernel(FullPrefillArgs a) {
+  constexpr int NT = 2;
+  using Tt = Tr<DT>;
+  using Eng = WaveAttn<DT, D, NT>;
+  using St = TileStage<DT, D, 512>;
+  constexpr int ES = Tt::ES;
+  constexpr int NW = 8;
+  __shared__ __attribute__((aligned(16))) char tile0[St::BYTES];
+  __shared__ __attribute__((aligned(16))) char tile1[St::BYTES];
+  __shared__ __attribute__((aligned(16))) char tile2[St::BYTES];
+
+  const int per = gridDim.x >> 3;
+  // consecutive ids share an XCD; within an XCD the latest positions (the
+  // most tiles) are dispatched first
+  const int wgid = (blockIdx.x & 7) * per + (per - 1 - (blockIdx.x >> 3));
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const bool lag = w >= 4;
+  const int T = a.T;
+  const int G = a.Hq / a.Hkv;
+  const int PT = 16 / G;
+  const int PW = NT * PT;
+  const int PWG = NW * PW;
+  const int nwg_bg = (T + PWG - 1) / PWG;
+  const bool live = wgid < a.B * a.Hkv * nwg_bg;
+  const int bg = wgid / nwg_bg;
+  const int g = bg % a.Hkv, b = bg / a.Hkv;
+  const int t0 = (wgid % nwg_bg) * PWG;
+  const int tw0 = t0 + w * PW;
+  const int nitems = live ? ((min(T, t0 + PWG) - 1) >> 6) + 1 : 0;
+
+  const int col = lane & 15;
+  const int hcol = g * G + col % G;
+  int tcol[NT], hicol[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    tcol[nt] = tw0 + nt * PT + col / G;
+    hicol[nt] = (live && tcol[nt] < T) ? tcol[nt] : -1;
+  }
+  Eng eng;
+  eng.reset();
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < Eng::NS; ++ks)
+      eng.qf[nt][ks] =
+          hicol[nt] >= 0
+              ? Tt::ld((const char*)a.q + (((size_t)(b * T + tcol[nt]) * a.Hq + hcol) * D + 32 * ks + 8 * (lane >> 4)) * ES)
+              : Tt::zero();
+  const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * T * D * ES;
+  const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
+  St st;
+  st.dma_init();
+  auto issue = [&](int j, char* buf) {
+    st.dma(buf, kg + (size_t)64 * j * D * ES, vg + (size_t)j * D * 64 * ES, T - 64 * j);
+  };
+  if (nitems > 0) issue(0, tile0);
+  wait_vmem();
+  if (nitems > 0) st.dma_fix(tile0);
+  __syncthreads();
+
+  // tile j for this wave: column tiles with a live key (key <= position)
+  auto act_of = [&](int j) -> unsigned {
+    unsigned act = 0;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) act |= (__ballot(hicol[nt] >= 64 * j) != 0ull ? 1u : 0u) << nt;
+    return act;
+  };
+  int lo[NT], hi[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    lo[nt] = 0;
+    hi[nt] = hicol[nt];
+  }
+  // block scores of tile j, once its softmax is done
+  auto scores = [&](int j, const float* bmax, const float* bsum) {
+    if ((lane >> 4) == 0) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        if (hicol[nt] >= 64 * j) {
+          const float r = SCORE_LSE ? eng.m[nt] + fast_log2(bsum[nt]) : bmax[nt];
+          a.raw[((size_t)(b * a.Hq + hcol) * T + tcol[nt]) * a.nblk + j] = r * kLn2;
+        }
+      }
+    }
+  };
+  float bmax[NT], bsum[NT];
+  f32x4 sreg[NT][4];
+  unsigned p_act = 0;
+  const typename Eng::NoHook nohook;
+  auto step = [&](int st_i, const char* prev, const char* cur, char* next) {
+    const unsigned c_act = st_i < nitems ? act_of(st_i) : 0u;
+    if (st_i + 1 < nitems) issue(st_i + 1, next);
+    auto ldV = [&](int u, int mc) { return St::ldV(prev, u, mc); };
+    auto ldK = [&](int c, int ks) { return St::ldK(cur, c, ks); };
+    if (lag && st_i >= 1 && p_act) {
+      eng.template softmax<true, SCORE_LSE != 0>(sreg, 64 * (st_i - 1), lo, hi, a.sc2, bmax, bsum, nohook, p_act);
+      scores(st_i - 1, bmax, bsum);
+    }
+    __builtin_amdgcn_s_setprio(1);
+    if (st_i >= 1 && p_act) eng.pv(sreg, ldV);
+    if (c_act) {
+      eng.qk(ldK, sreg);
+      __builtin_amdgcn_s_setprio(0);
+      if (!lag) {
+        eng.template softmax<true, SCORE_LSE != 0>(sreg, 64 * st_i, lo, hi, a.sc2, bmax, bsum, nohook, c_act);
+        scores(st_i, bmax, bsum);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    p_act = c_act;
+    wait_vmem();
+    if (st_i + 1 < nitems) st.dma_fix(next);
+    __syncthreads();
+  };
+  for (int st_i = 0; st_i <= nitems; st_i += 3) {
+    step(st_i, tile2, tile0, tile1);
+    if (st_i + 1 > nitems) break;
+    step(st_i + 1, tile0, tile1, tile2);
+    if (st_i + 2 > nitems) break;
+    step(st_i + 2, tile1, tile2, tile0);
+  }
+
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float inv, l2;
+    eng.finish(nt, inv, l2);
+    if (hicol[nt] >= 0) {
+      if ((lane >> 4) == 0) a.lse[(size_t)(b * a.Hq + hcol) * T + tcol[nt]] = l2 * kLn2;
+      char* op = (char*)a.o + (((size_t)(b * T + tcol[nt]) * a.Hq + hcol) * D + 4 * (lane >> 4)) * ES;
+#pragma unroll
+      for (int mc = 0; mc < Eng::NM; ++mc) {
+        const f32x4 v = eng.o[nt][mc];
+        Tt::store4(op + 16 * mc * ES, v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+      }
+    }
+  }
+}
+
 // ===================================================================== top-k
 // One wavefront per (sequence, kv group, query row).  Candidate j sits in lane
 // j % 64, slot j / 64.  The score of a candidate is x = max_h (raw - LSE_h),
@@ -741,6 +887,20 @@ template <int DT, int D>
 static hipError_t full_dispatch(const FullPrefillArgs& a, int score_lse, hipStream_t s) {
   constexpr int NT = 2;
   const int G = a.Hq / a.Hkv;
+  // the ping-pong kernel needs G <= 16 and three tile buffers in LDS
+  constexpr bool pingpong = 3 * TileStage<DT, D, 512>::BYTES <= 100 * 1024;
+  if constexpr (pingpong) {
+    if (G <= 16) {
+      const int PWG = 8 * (16 * NT / G);
+      const long nwg = (long)a.B * a.Hkv * ((a.T + PWG - 1) / PWG);
+      const unsigned per = (unsigned)((nwg + 7) / 8);
+      if (score_lse)
+        hipLaunchKernelGGL((full_prefill_pp_kernel<DT, D, 1>), dim3(8 * per), dim3(512), 0, s, a);
+      else
+        hipLaunchKernelGGL((full_prefill_pp_kernel<DT, D, 0>), dim3(8 * per), dim3(512), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   const int Gw = G < 4 ? G : 4;
   const int posw = (4 / Gw) * 16 * NT;
   dim3 grid(a.B * (a.Hq / Gw), (a.T + posw - 1) / posw);
