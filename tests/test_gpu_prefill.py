@@ -69,34 +69,33 @@ def oracle_rows(inp, pos, kb, W, score="max", include_diag=False, gates=True, b=
                                  pos, kb, W, include_diag=include_diag, score=score)
 
 
-def check_run(run, pos, score="max", include_diag=False, gates=True, layers=None):
+def check_run(run, pos, score="max", include_diag=False, gates=True, layers=None, b=0):
     cfg, inp = run.cfg, run.inp
     tol = TOL[cfg.dtype]
-    ref = oracle_rows(inp, pos, run.kb, run.W, score, include_diag, gates)
-    o = host(run.o)[0][pos]
+    ref = oracle_rows(inp, pos, run.kb, run.W, score, include_diag, gates, b=b)
+    o = host(run.o)[b][pos]
     err_o = np.abs(o - ref["o"]).max()
-    lse = host(run.lse)[0][:, pos]
+    lse = host(run.lse)[b][:, pos]
     err_lse = np.abs(lse - ref["lse"]).max()
-    raw = host(run.raw)[0][:, pos]
+    raw = host(run.raw)[b][:, pos]
     valid = ~np.isnan(ref["raw"])
     err_raw = np.abs(raw[valid] - ref["raw"][valid]).max()
     say(f"  full layer: max|dO|={err_o:.3g} max|dLSE|={err_lse:.3g} max|draw|={err_raw:.3g}")
     assert err_o <= tol and err_lse <= SIDE_TOL and err_raw <= SIDE_TOL
-    gs = host(run.gs)[0][:, pos]
+    gs = host(run.gs)[b][:, pos]
     vg = ~np.isnan(ref["Sg"])
     rel_gs = np.abs(gs[vg] - ref["Sg"][vg]).max() / np.abs(ref["Sg"][vg]).max()
-    gidx = host(run.idx)[0][:, pos]
+    gidx = host(run.idx)[b][:, pos]
     n, ties, fails = compare_indices(gidx, ref, pos, run.kb, include_diag)
     say(f"  selection: rows={n} near-tie={ties} failures={len(fails)} rel|dSg|={rel_gs:.3g}")
     assert not fails, fails[:5]
     assert rel_gs < 1e-4
-    b = 0
     k64, v64 = inp.f64("k")[b], inp.f64("v")[b]
     for l in range(len(inp.layers)) if layers is None else layers:
         gl = inp.f64("gates", l)[b][pos] if gates else None
         want = ora.sparse_layer_rows(inp.f64("q", l)[b][pos], pos, k64, v64, gidx,
                                      inp.f64("k", l)[b], inp.f64("v", l)[b], run.W, gl)
-        got = host(run.outs[l])[0][pos]
+        got = host(run.outs[l])[b][pos]
         err = np.abs(got - want).max()
         say(f"  sparse layer {l}: max|dO|={err:.3g}")
         assert err <= tol
@@ -241,3 +240,23 @@ def test_repeat_runs_are_bitwise_identical():
     a, b = Run(inp), Run(inp)
     for x, y in ((a.o, b.o), (a.raw, b.raw), (a.idx, b.idx), (a.outs[0], b.outs[0])):
         assert torch.equal(torch.nan_to_num(x.float(), 123.0), torch.nan_to_num(y.float(), 123.0))
+
+
+def test_batch2_group16_both_sequences():
+    """Two sequences, 16 query heads per kv head (the widest group of the
+    sparse layers): every row of both sequences."""
+    say("[batch 2, G=16] T=200 Hq=16 Hkv=1 d=64 bf16")
+    cfg = gen.config(1, B=2, T=200, Hq=16, Hkv=1, d=64, dtype="bf16", kb=2, W=40, N=2)
+    inp = gen.make_prefill(cfg)
+    run = Run(inp)
+    for b in range(2):
+        check_run(run, np.arange(cfg.T), b=b)
+
+
+def test_group32_full_layer_and_selection():
+    """G = 32 (full layer and selection only; the sparse layers take G <= 16)."""
+    say("[G=32] T=150 Hq=32 Hkv=1 d=128 bf16, full layer + top-k")
+    cfg = gen.config(1, T=150, Hq=32, Hkv=1, d=128, dtype="bf16", kb=1, W=0, N=0)
+    inp = gen.make_prefill(cfg, n_layers=0)
+    run = Run(inp)
+    check_run(run, np.arange(cfg.T))
