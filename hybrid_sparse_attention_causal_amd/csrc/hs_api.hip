@@ -90,10 +90,8 @@ hs_status check_decode(const char* fn, const hs_shape* s) {
   return HS_OK;
 }
 
-// split-K chunking of the decode full layer: 16 blocks (1024 keys) per chunk
-constexpr int kDecodeChunkBlocks = 16;
 int decode_nch(const hs_shape* s) {
-  const int span = 64 * kDecodeChunkBlocks;
+  const int span = 64 * hs::kDecodeChunkBlocks;
   return (s->kv_len + span - 1) / span;
 }
 size_t decode_full_ws(const hs_shape* s) {
@@ -193,7 +191,7 @@ hs_status hs_full_attn_fwd_scores(const hs_shape* s, const void* q, const void* 
     a.Hkv = s->hkv;
     a.C = s->kv_len;
     a.nch = decode_nch(s);
-    a.ch_blocks = kDecodeChunkBlocks;
+    a.ch_blocks = hs::kDecodeChunkBlocks;
     a.token = block == 1;
     a.kv_dtype = s->kv_dtype;
     a.kv_scale = s->kv_scale;

@@ -32,13 +32,15 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
   using Eng = WaveAttn<HS_BF16, D, 1>;
   constexpr int KES = KV == HS_FP8_E4M3 ? 1 : 2;  // cache bytes per element
   const int lane = threadIdx.x & 63;
-  const long unit = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // unit, sequence and length are wave-uniform; saying so keeps the tile loop
+  // a scalar loop
+  const long unit = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (unit >= (long)a.B * a.Hkv * a.nch) return;
   const int ch = (int)(unit % a.nch);
   const int bg = (int)(unit / a.nch);
   const int g = bg % a.Hkv, b = bg / a.Hkv;
-  const int L = a.lens[b];
-  const int span = a.ch_blocks * 64;
+  const int L = __builtin_amdgcn_readfirstlane(a.lens[b]);
+  const int span = kDecodeChunkBlocks * 64;
   const int kstart = ch * span;
   if (kstart >= L) return;
   const int kend = min(L, kstart + span);
@@ -55,10 +57,13 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
   int lo[1], hi[1];
   lo[0] = col < G ? 0 : kNoKey;
   hi[0] = L - 1;
+  // unconditional loads (columns past G read head g*G and are zeroed): a
+  // load under a branch would make the compiler drain every later wait
 #pragma unroll
-  for (int ks = 0; ks < Eng::NS; ++ks)
-    eng.qf[0][ks] = col < G ? Tt::ld((const char*)a.q + ((size_t)(b * a.Hq + h) * D + 32 * ks + q8) * 2)
-                            : Tt::zero();
+  for (int ks = 0; ks < Eng::NS; ++ks) {
+    const Frag f = Tt::ld((const char*)a.q + ((size_t)(b * a.Hq + (col < G ? h : g * G)) * D + 32 * ks + q8) * 2);
+    eng.qf[0][ks] = col < G ? f : Tt::zero();
+  }
   const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * a.C * D * KES;
   const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * a.C * D * KES;
   float* rawrow = a.raw + (size_t)(b * a.Hq + h) * (TOKEN ? a.C : a.C / 64);
@@ -66,34 +71,44 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
 
   // Raw fragments of one tile: bf16: 16 K and 16 V fragments of 16 bytes;
   // fp8: 16 K fragments of 8 bytes and 2x(D/64)x8 value dwords (decoded at
-  // use).  Two waves per SIMD keep two tiles in flight per SIMD.
+  // use).  The key and value halves of a tile are separate register sets, so
+  // the next tile's keys load while this tile's values are still in flight
+  // and consumed, and its values load during the next tile's QK^T.
   constexpr bool F8 = KV == HS_FP8_E4M3;
-  struct RawB {
+  struct RawKB {
     uint4 k[4][Eng::NS];
+  };
+  struct RawK8 {
+    uint2 k8[4][Eng::NS];
+  };
+  struct RawVB {
     uint4 v[2][Eng::NM];
   };
-  struct Raw8 {
-    uint2 k8[4][Eng::NS];
+  struct RawV8 {
     uint32_t v8[2][D / 64][8];
   };
-  struct Raw : std::conditional_t<F8, Raw8, RawB> {};
-  auto load = [&](int kb0, Raw& r) {
-    const bool partial = kb0 + 64 > L;
-    const int j = kb0 >> 6;
+  using RawK = std::conditional_t<F8, RawK8, RawKB>;
+  using RawV = std::conditional_t<F8, RawV8, RawVB>;
+  // Every load is unconditional: the capacity C is a multiple of 64, so a
+  // tile's rows all lie inside the cache even past L.  Keys at or past L are
+  // masked out of the logits by selects; values there are zeroed, since
+  // P = 0 times a stale non-finite value would not vanish.
+  auto loadK = [&](int kb0, RawK& r) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int key = kb0 + tile_key(c, r16);
-      const bool ok = !partial || key < L;
 #pragma unroll
       for (int ks = 0; ks < Eng::NS; ++ks) {
         if constexpr (F8) {
-          r.k8[c][ks] = ok ? *(const uint2*)(kg + (size_t)key * D + 32 * ks + q8) : make_uint2(0u, 0u);
+          r.k8[c][ks] = *(const uint2*)(kg + (size_t)key * D + 32 * ks + q8);
         } else {
-          r.k[c][ks] =
-              ok ? *(const uint4*)(kg + ((size_t)key * D + 32 * ks + q8) * 2) : make_uint4(0u, 0u, 0u, 0u);
+          r.k[c][ks] = *(const uint4*)(kg + ((size_t)key * D + 32 * ks + q8) * 2);
         }
       }
     }
+  };
+  auto loadV = [&](int kb0, RawV& r) {
+    const int j = kb0 >> 6;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int key0 = kb0 + 32 * u + q8;
@@ -101,42 +116,66 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
 #pragma unroll
         for (int hf = 0; hf < D / 64; ++hf)
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            r.v8[u][hf][e] = (!partial || key0 + e < L)
-                                 ? *(const uint32_t*)(vg + (size_t)(key0 + e) * D + 64 * hf + 4 * r16)
-                                 : 0u;
+          for (int e = 0; e < 8; ++e) r.v8[u][hf][e] = *(const uint32_t*)(vg + (size_t)(key0 + e) * D + 64 * hf + 4 * r16);
+      } else {
+#pragma unroll
+        for (int mc = 0; mc < Eng::NM; ++mc)
+          r.v[u][mc] = *(const uint4*)(vg + (((size_t)j * D + 16 * mc + r16) * 64 + 32 * u + q8) * 2);
+      }
+    }
+  };
+  // zero the value entries of keys >= L (last tile of a sequence only)
+  auto clipV = [&](int kb0, RawV& r) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int key0 = kb0 + 32 * u + q8;
+      if constexpr (F8) {
+#pragma unroll
+        for (int hf = 0; hf < D / 64; ++hf)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) r.v8[u][hf][e] = key0 + e < L ? r.v8[u][hf][e] : 0u;
       } else {
 #pragma unroll
         for (int mc = 0; mc < Eng::NM; ++mc) {
-          Frag f = Tt::ld(vg + (((size_t)j * D + 16 * mc + r16) * 64 + 32 * u + q8) * 2);
-          if (partial) f = Tt::keep(f, L - key0);
-          r.v[u][mc] = f.u;
+          Frag f;
+          f.u = r.v[u][mc];
+          r.v[u][mc] = Tt::keep(f, L - key0).u;
         }
       }
     }
   };
-  auto compute = [&](int kb0, const Raw& r) {
+  float bkeep[kDecodeChunkBlocks / 4];
+#pragma unroll
+  for (int r = 0; r < kDecodeChunkBlocks / 4; ++r) bkeep[r] = -INFINITY;
+  RawK rk;
+  RawV rv;
+  // One tile: QK^T on the keys in rk, the keys of tile nx are requested,
+  // softmax, PV with the values in rv, the values of tile nx are requested.
+  auto body = [&](int kb0, int nx) {
     const int j = kb0 >> 6;
-    Frag vc[4];
     auto ldK = [&](int c, int ks) {
       if constexpr (F8) {
-        return fp8x8_frag(r.k8[c][ks]);
+        return fp8x8_frag(rk.k8[c][ks]);
       } else {
         Frag f;
-        f.u = r.k[c][ks];
+        f.u = rk.k[c][ks];
         return f;
       }
     };
+    Frag vc[4];
     auto ldV = [&](int u, int mc) {
       if constexpr (F8) {
-        if ((mc & 3) == 0) fp8_vfrag4(r.v8[u][mc >> 2], vc);
+        if ((mc & 3) == 0) fp8_vfrag4(rv.v8[u][mc >> 2], vc);
         return vc[mc & 3];
       } else {
         Frag f;
-        f.u = r.v[u][mc];
+        f.u = rv.v[u][mc];
         return f;
       }
     };
+    f32x4 s[1][4];
+    eng.qk(ldK, s);
+    loadK(nx, rk);
     float bmax[1], bsum[1];
     if (TOKEN) {
       auto hook = [&](int, const float* x) {
@@ -155,18 +194,47 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
           }
         }
       };
-      eng.template tile<true, false>(ldK, ldV, kb0, lo, hi, sc2, bmax, bsum, hook);
+      eng.template softmax<true, false>(s, kb0, lo, hi, sc2, bmax, bsum, hook);
     } else {
-      eng.template tile<true, false>(ldK, ldV, kb0, lo, hi, sc2, bmax, bsum);
-      if (lane < 16 && col < G) rawrow[j] = bmax[0] * kLn2;
+      eng.template softmax<true, false>(s, kb0, lo, hi, sc2, bmax, bsum);
+      // block maxima are held until the chunk ends (lane group q keeps the
+      // chunk's tiles q, q + 4, ...): a store inside the loop would turn
+      // every wait for the next tile's loads into a full drain
+      const int tt = (kb0 - kstart) >> 6;
+#pragma unroll
+      for (int r = 0; r < kDecodeChunkBlocks / 4; ++r)
+        if (tt == 4 * r + (lane >> 4)) bkeep[r] = bmax[0];
+      (void)j;
     }
+    eng.pv(s, ldV);
+    loadV(nx, rv);
   };
-  // per tile, the key and value loads are issued together (one memory round
-  // trip per tile)
-  for (int kb0 = kstart; kb0 < kend; kb0 += 64) {
-    Raw r;
-    load(kb0, r);
-    compute(kb0, r);
+  // Full tiles in a loop whose loads are the same every iteration (the last
+  // full tile reloads itself when nothing follows it: an L2 hit), so the
+  // compiler's waits stay counts instead of drains; a partial last tile
+  // (keys past L) is peeled off below.
+  const int ntile = (kend - kstart + 63) >> 6;
+  const int nfull = (kend - kstart) >> 6;
+  if (ntile > 0) {
+    loadK(kstart, rk);
+    loadV(kstart, rv);
+  }
+  for (int t = 0; t < nfull; ++t) {
+    const int kb0 = kstart + 64 * t;
+    body(kb0, t + 1 < ntile ? kb0 + 64 : kb0);
+  }
+  if (nfull < ntile) {
+    const int kb0 = kstart + 64 * nfull;
+    clipV(kb0, rv);
+    body(kb0, kb0);
+  }
+
+  if (!TOKEN && col < G) {
+#pragma unroll
+    for (int r = 0; r < kDecodeChunkBlocks / 4; ++r) {
+      const int kb = kstart + 64 * (4 * r + (lane >> 4));
+      if (kb < kend) rawrow[kb >> 6] = bkeep[r] * kLn2;
+    }
   }
 
   // partial state: unnormalised o (head_dim floats, natural order), m (log2), l

@@ -45,6 +45,11 @@ struct SparsePrefillArgs {
   float sc2;
 };
 
+// split-K chunking of the decode full layer: 64-key tiles per chunk (the
+// kernel keeps one block maximum per tile in registers until the chunk ends)
+constexpr int kDecodeChunkBlocks = 16;
+static_assert(kDecodeChunkBlocks % 4 == 0, "chunk tiles are spread over four lane groups");
+
 struct DecodeFullArgs {
   const void* q;
   const void* k;
