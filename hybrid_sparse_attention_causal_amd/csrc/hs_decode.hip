@@ -317,111 +317,162 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeFullArgs a) {
 }
 
 // ============================================================ sparse layer
-// One work group (8 waves) per (b, g).  Work items: the n_sel selected blocks
-// of the shared cache, then the ceil(min(L, W)/64) tiles of the window ring;
-// item i goes to wave i % 8.  Each wave keeps one online-softmax state per
-// branch; the 8 partial states are merged through LDS and the two branches
-// combined with the gates.
+// One work group (8 waves) per (b, g).  Work items: the ceil(min(L, W)/64)
+// tiles of the window ring, then the n_sel selected blocks of the shared
+// cache; item i goes to wave i % 8, so each wave meets its window items
+// first.  A wave parks its window-branch state in LDS when it moves on to
+// the selected blocks and reuses the same registers for the sparse branch.
+// The 8 partial states of each branch are merged through LDS and the two
+// branches combined with the gates.
 template <int D>
 __global__ __launch_bounds__(512) void decode_sparse_kernel(DecodeSparseArgs a) {
   using Tt = Tr<HS_BF16>;
+  using Frag = typename Tt::Frag;
   using Eng = WaveAttn<HS_BF16, D, 1>;
   constexpr int ES = 2;
   constexpr int NW = 8;
   __shared__ float sm_m[NW][16], sm_l[NW][16];
   __shared__ __attribute__((aligned(16))) float sm_o[NW][16][D];
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int bg = blockIdx.x;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
-  const int L = a.lens[b];
+  const int L = __builtin_amdgcn_readfirstlane(a.lens[b]);
   const int G = a.Hq / a.Hkv;
   const int col = lane & 15;
   const int h = g * G + col;
   const int r16 = lane & 15, q8 = 8 * (lane >> 4), q4 = (lane >> 4) << 2;
   const int nring = a.W > 0 ? (min(L, a.W) + 63) / 64 : 0;
   const int nslots = min(L, a.W);
+  const int nitem = nring + a.nsel;
 
-  Eng sp, sw;
-  sp.reset();
-  sw.reset();
+  Eng eng;
+  eng.reset();
+  // Every global load below is unconditional: a load under a branch would
+  // turn the compiler's later waits into full drains.  Columns past G read
+  // head g*G and are zeroed.
 #pragma unroll
   for (int ks = 0; ks < Eng::NS; ++ks) {
-    sp.qf[0][ks] = col < G ? Tt::ld((const char*)a.q + ((size_t)(b * a.Hq + h) * D + 32 * ks + q8) * ES)
-                           : Tt::zero();
-    sw.qf[0][ks] = sp.qf[0][ks];
+    const Frag f = Tt::ld((const char*)a.q + ((size_t)(b * a.Hq + (col < G ? h : g * G)) * D + 32 * ks + q8) * ES);
+    eng.qf[0][ks] = col < G ? f : Tt::zero();
   }
   const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * a.C * D * ES;
   const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * (a.C / 64) * D * 64 * ES;
+  const char* krg = (const char*)a.kr + (size_t)(b * a.Hkv + g) * a.W * D * ES;
+  const char* vrg = (const char*)a.vr + (size_t)(b * a.Hkv + g) * ((a.W + 63) / 64) * D * 64 * ES;
   const int32_t* il = a.idx + (size_t)(b * a.Hkv + g) * a.nsel;
+
+  // Item it < nring: ring tile it (slots 64*it ..); otherwise selected block
+  // il[it - nring] (an invalid id reads block 0 with every column switched
+  // off).  All fields are wave-uniform, so one load path serves both kinds.
+  struct Item {
+    const char* kp;  // first key row of the tile
+    const char* vp;  // [D][64] value slab of the tile
+    int rows;        // key rows addressable from kp
+    int kbase;       // first key (cache position or ring slot)
+    int hi;          // last valid key
+    bool ring, on;
+  };
+  auto item = [&](int it) {
+    Item r;
+    r.ring = it < nring;
+    if (r.ring) {
+      r.on = true;
+      r.kp = krg + (size_t)64 * it * D * ES;
+      r.vp = vrg + (size_t)it * D * 64 * ES;
+      r.rows = a.W - 64 * it;  // the ring's last tile may be short
+      r.kbase = 64 * it;
+      r.hi = nslots - 1;
+    } else {
+      const int j0 = __builtin_amdgcn_readfirstlane(il[it - nring]);
+      r.on = j0 >= 0 && 64 * j0 < L;
+      const int j = r.on ? j0 : 0;
+      r.kp = kg + (size_t)64 * j * D * ES;
+      r.vp = vg + (size_t)j * D * 64 * ES;
+      r.rows = 64;
+      r.kbase = 64 * j;
+      r.hi = L - 1;
+    }
+    return r;
+  };
+  uint4 rk[4][Eng::NS], rv[2][Eng::NM];
+  auto loadK = [&](const Item& t) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int row = min(tile_key(c, r16), t.rows - 1);
+#pragma unroll
+      for (int ks = 0; ks < Eng::NS; ++ks) rk[c][ks] = *(const uint4*)(t.kp + ((size_t)row * D + 32 * ks + q8) * ES);
+    }
+  };
+  auto loadV = [&](const Item& t) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int mc = 0; mc < Eng::NM; ++mc)
+        rv[u][mc] = *(const uint4*)(t.vp + (((size_t)16 * mc + r16) * 64 + 32 * u + q8) * ES);
+  };
+  // a wave's partial state -> LDS slice w
+  auto park = [&]() {
+    const float lt = xlane_sum(eng.l[0]);
+    if (lane < 16) {
+      sm_m[w][col] = eng.m[0];
+      sm_l[w][col] = lt;
+    }
+#pragma unroll
+    for (int mc = 0; mc < Eng::NM; ++mc) *(float4*)&sm_o[w][col][16 * mc + q4] = *(const float4*)&eng.o[0][mc];
+  };
+
   float bmax[1], bsum[1];
   int lo[1], hi[1];
-
-  for (int it = w; it < a.nsel + nring; it += NW) {
-    if (it < a.nsel) {
-      const int j = il[it];
-      if (j < 0 || 64 * j >= L) continue;
-      const int kb0 = 64 * j;
-      const bool partial = kb0 + 64 > L;
-      lo[0] = col < G ? 0 : kNoKey;
-      hi[0] = L - 1;
-      // key and value fragments are loaded together (one round trip)
-      typename Tt::Frag kf[4][Eng::NS], vf[2][Eng::NM];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int key = kb0 + tile_key(c, r16);
-#pragma unroll
-        for (int ks = 0; ks < Eng::NS; ++ks)
-          kf[c][ks] = (!partial || key < L) ? Tt::ld(kg + ((size_t)key * D + 32 * ks + q8) * ES) : Tt::zero();
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int mc = 0; mc < Eng::NM; ++mc) {
-          const auto f = Tt::ld(vg + (((size_t)j * D + 16 * mc + r16) * 64 + 32 * u + q8) * ES);
-          vf[u][mc] = partial ? Tt::keep(f, L - (kb0 + 32 * u + q8)) : f;
-        }
-      auto ldK = [&](int c, int ks) { return kf[c][ks]; };
-      auto ldV = [&](int u, int mc) { return vf[u][mc]; };
-      sp.template tile<true, false>(ldK, ldV, kb0, lo, hi, a.sc2, bmax, bsum);
-    } else {
-      const int r = it - a.nsel;
-      const int s0 = 64 * r;
-      const char* krg = (const char*)a.kr + (size_t)(b * a.Hkv + g) * a.W * D * ES;
-      const char* vrg = (const char*)a.vr + (size_t)(b * a.Hkv + g) * ((a.W + 63) / 64) * D * 64 * ES;
-      lo[0] = col < G ? 0 : kNoKey;
-      hi[0] = nslots - 1;
-      auto ldK = [&](int c, int ks) {
-        const int s = s0 + tile_key(c, r16);
-        return s < nslots ? Tt::ld(krg + ((size_t)s * D + 32 * ks + q8) * ES) : Tt::zero();
-      };
-      auto ldV = [&](int u, int mc) {
-        const int s = s0 + 32 * u + q8;
-        if (s >= nslots) return Tt::zero();
-        const auto f = Tt::ld(vrg + (((size_t)r * D + 16 * mc + r16) * 64 + 32 * u + q8) * ES);
-        return s + 8 <= nslots ? f : Tt::keep(f, nslots - s);
-      };
-      sw.template tile<true, false>(ldK, ldV, s0, lo, hi, a.sc2, bmax, bsum);
+  bool parked = false;  // window branch of this wave already in LDS
+  Item cur = item(w < nitem ? w : 0);
+  if (w < nitem) {
+    loadK(cur);
+    loadV(cur);
+  }
+  for (int it = w; it < nitem; it += NW) {
+    if (!parked && !cur.ring) {  // first selected block: the window branch is complete
+      park();
+      eng.reset();
+      parked = true;
     }
+    // the next item of this wave (or this one again: an L2 hit that keeps
+    // the loads, and so the waits, the same every iteration)
+    const Item nxt = it + NW < nitem ? item(it + NW) : cur;
+    auto ldK = [&](int c, int ks) {
+      Frag f;
+      f.u = rk[c][ks];
+      return f;
+    };
+    auto ldV = [&](int u, int mc) {
+      Frag f;
+      f.u = rv[u][mc];
+      // values of keys past the last valid one are zeroed (selects only):
+      // P = 0 there, but a stale non-finite value would not vanish
+      return Tt::keep(f, cur.hi + 1 - (cur.kbase + 32 * u + q8));
+    };
+    f32x4 sx[1][4];
+    eng.qk(ldK, sx);
+    loadK(nxt);
+    lo[0] = col < G && cur.on ? 0 : kNoKey;
+    hi[0] = cur.hi;
+    eng.template softmax<true, false>(sx, cur.kbase, lo, hi, a.sc2, bmax, bsum);
+    eng.pv(sx, ldV);
+    loadV(nxt);
+    cur = nxt;
+  }
+  if (!parked) {  // no selected block reached this wave
+    park();
+    eng.reset();
   }
 
-  // merge the 8 partial states of each branch through LDS, one branch at a
-  // time; thread -> (head column, d) outputs
+  // Merge the partial states of one branch (the window branch sits in LDS
+  // now; the sparse branch follows); thread -> (head column, d) outputs.
   constexpr int PER = (16 * D + 64 * NW - 1) / (64 * NW);
   float out[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) out[i] = 0.f;
-#pragma unroll
-  for (int br = 0; br < 2; ++br) {
-    Eng& e = br ? sw : sp;
-    const float lt = xlane_sum(e.l[0]);
-    if (lane < 16) {
-      sm_m[w][col] = e.m[0];
-      sm_l[w][col] = lt;
-    }
-#pragma unroll
-    for (int mc = 0; mc < Eng::NM; ++mc) *(float4*)&sm_o[w][col][16 * mc + q4] = *(const float4*)&e.o[0][mc];
-    __syncthreads();
+  auto merge = [&](int br) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int el = threadIdx.x + 64 * NW * i;
@@ -442,8 +493,13 @@ __global__ __launch_bounds__(512) void decode_sparse_kernel(DecodeSparseArgs a) 
         out[i] += ls > 0.f ? gate * os / ls : 0.f;
       }
     }
-    __syncthreads();
-  }
+  };
+  __syncthreads();
+  merge(1);
+  __syncthreads();
+  park();
+  __syncthreads();
+  merge(0);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int el = threadIdx.x + 64 * NW * i;
