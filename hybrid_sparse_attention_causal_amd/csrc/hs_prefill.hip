@@ -882,6 +882,247 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
   }
 }
 
+// Sparse kernel for two resident work groups per CU (4 wavefronts each, NT
+// column tiles of 16 columns per wavefront).  Each wavefront runs QK^T ->
+// softmax -> PV on item s while item s+1 is transferred into the second of
+// two LDS tile buffers.  With two groups on a CU, one group's barrier waits,
+// selection set-up and closing writes overlap the other group's tiles.  Work
+// assignment, masking and the two branches are as in sparse_prefill_kernel;
+// column tile nt of wave w holds the G heads of the 16/G positions
+// tw0 + nt*16/G + col/G.
+template <int DT, int D, int NT>
+__global__ __launch_bounds__(256, 2) void sparse_prefill_dual_kernel(SparsePrefillArgs a) {
+  using Tt = Tr<DT>;
+  using Eng = WaveAttn<DT, D, NT, true>;
+  using St = TileStage<DT, D, 256>;
+  constexpr int ES = Tt::ES;
+  constexpr int NW = 4;
+  // two tile buffers as separate arrays: with the step loop unrolled by two
+  // every access names its buffer, so the compiler can tell the in-flight
+  // transfer into one buffer from the reads of the other
+  __shared__ __attribute__((aligned(16))) char tile0[St::BYTES];
+  __shared__ __attribute__((aligned(16))) char tile1[St::BYTES];
+  extern __shared__ uint32_t dyn[];
+
+  const int per = gridDim.x >> 3;
+  // consecutive ids share an XCD; within an XCD the latest positions (the
+  // largest unions of selected blocks) are dispatched first
+  const int wgid = (blockIdx.x & 7) * per + (per - 1 - (blockIdx.x >> 3));
+  const bool live = wgid < a.nwg;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int T = a.T;
+  const int G = a.Hq / a.Hkv;
+  const int PT = 16 / G;  // positions per column tile
+  const int PW = NT * PT;
+  const int PWG = NW * PW;
+  const int nwg_bg = (T + PWG - 1) / PWG;
+  const int bg = wgid / nwg_bg;
+  const int g = bg % a.Hkv, b = bg / a.Hkv;
+  const int t0 = (wgid % nwg_bg) * PWG;
+  const int tw0 = t0 + w * PW;
+  const int nw32 = (a.nblk + 31) >> 5;
+  uint32_t* U = dyn;
+  uint32_t* Uw = U + nw32;
+  uint32_t* S = Uw + NW * nw32;
+  int* ulist = (int*)(S + PWG * nw32);
+  int* nu_p = ulist + a.nblk;
+
+  // Items: first the window blocks of the group's positions (known at once),
+  // then the union of their selected blocks.
+  int jw0 = 0, nwin = 0;
+  if (live && a.W > 0) {
+    jw0 = max(0, t0 - a.W + 1) >> 6;
+    nwin = (min(T - 1, t0 + PWG - 1) >> 6) - jw0 + 1;
+  }
+
+  const int col = lane & 15;
+  const int hcol = g * G + col % G;
+  int pcol[NT], tcol[NT], hicol[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    pcol[nt] = nt * PT + col / G;
+    tcol[nt] = tw0 + pcol[nt];
+    hicol[nt] = tcol[nt] < T ? tcol[nt] : -1;
+  }
+  // query fragments, gates and the first window tile are in flight while the
+  // selection bitsets are built
+  Eng eng;
+  eng.reset();
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < Eng::NS; ++ks)
+      eng.qf[nt][ks] =
+          (live && tcol[nt] < T)
+              ? Tt::ld((const char*)a.q +
+                       (((size_t)(b * T + tcol[nt]) * a.Hq + hcol) * D + 32 * ks + 8 * (lane >> 4)) * ES)
+              : Tt::zero();
+  float gate0[NT], gate1[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    gate0[nt] = 1.f;
+    gate1[nt] = 1.f;
+    if (a.gates && live && tcol[nt] < T) {
+      const float2 gl = *(const float2*)(a.gates + ((size_t)(b * T + tcol[nt]) * a.Hq + hcol) * 2);
+      gate0[nt] = 1.f / (1.f + expf(-gl.x));
+      gate1[nt] = 1.f / (1.f + expf(-gl.y));
+    }
+  }
+  const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * T * D * ES;
+  const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
+  const char* ksg = (const char*)a.ks + (size_t)(b * a.Hkv + g) * T * D * ES;
+  const char* vsg = (const char*)a.vs + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
+  St st;
+  st.dma_init();
+  auto issue = [&](int i, char* buf) {  // item i -> buf (tile i % 2), in flight until wait_vmem
+    const bool win = i < nwin;
+    const int j = __builtin_amdgcn_readfirstlane(win ? jw0 + i : ulist[i - nwin]);
+    st.dma(buf, (win ? ksg : kg) + (size_t)64 * j * D * ES, (win ? vsg : vg) + (size_t)j * D * 64 * ES,
+           T - 64 * j);
+  };
+  if (nwin > 0) issue(0, tile0);
+
+  // selection bitsets: per position (S), per wave (Uw) and per group (U);
+  // positions own their words, the unions are OR-reductions (no contended
+  // atomics)
+  for (int i = threadIdx.x; i < (1 + NW + PWG) * nw32; i += 64 * NW) U[i] = 0u;
+  __syncthreads();
+  if (live) {
+    for (int e = threadIdx.x; e < PWG * a.topk; e += 64 * NW) {
+      const int p = e / a.topk;
+      const int t = t0 + p;
+      if (t < T) {
+        const int j = a.idx[((size_t)(b * a.Hkv + g) * T + t) * a.topk + (e % a.topk)];
+        if (j >= 0 && j < a.nblk && 64 * j <= t) atomicOr(&S[p * nw32 + (j >> 5)], 1u << (j & 31));
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < NW * nw32; i += 64 * NW) {
+    const int ww = i / nw32, k = i % nw32;
+    uint32_t v = 0u;
+    for (int p = 0; p < PW; ++p) v |= S[(ww * PW + p) * nw32 + k];
+    Uw[i] = v;
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < nw32; k += 64 * NW) {
+    uint32_t v = 0u;
+    for (int ww = 0; ww < NW; ++ww) v |= Uw[ww * nw32 + k];
+    U[k] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    int base = 0;
+    for (int w0 = 0; w0 < nw32; w0 += 64) {
+      const uint32_t word = w0 + lane < nw32 ? U[w0 + lane] : 0u;
+      const int cnt = __popc(word);
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+      }
+      int pos = base + incl - cnt;
+      uint32_t wd = word;
+      while (wd) {
+        ulist[pos++] = (w0 + lane) * 32 + __builtin_ctz(wd);
+        wd &= wd - 1;
+      }
+      base += __shfl(incl, 63);
+    }
+    if (lane == 0) *nu_p = base;
+  }
+  __syncthreads();
+  const int nu = live ? *nu_p : 0;
+  const int nitems = nwin + nu;
+  if (nwin == 0 && nitems > 0) issue(0, tile0);
+
+  // Close a branch.  The first branch's gated output is parked in the output
+  // rows themselves (in the output dtype) while the second branch runs and is
+  // added back when that one closes: no registers hold it in between.
+  auto fold = [&](const float* gate, bool first) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float inv, l2;
+      eng.finish(nt, inv, l2);
+      const float sc = inv * gate[nt];
+      if (live && tcol[nt] < T) {
+        char* op = (char*)a.o + (((size_t)(b * T + tcol[nt]) * a.Hq + hcol) * D + 4 * (lane >> 4)) * ES;
+#pragma unroll
+        for (int mc = 0; mc < Eng::NM; ++mc) {
+          f32x4 v = eng.o[nt][mc] * sc;
+          if (!first) v += Tt::load4(op + 16 * mc * ES);
+          Tt::store4(op + 16 * mc * ES, v[0], v[1], v[2], v[3]);
+        }
+      }
+    }
+  };
+  // item i: first key, per-column-tile key range, and the column tiles of
+  // this wave that have a live key in it (0: the wave skips the item)
+  auto item = [&](int i, int& kbase, int* lo, int* hi) -> unsigned {
+    const bool win = i < nwin;
+    const int j = win ? jw0 + i : ulist[i - nwin];
+    kbase = 64 * j;
+    unsigned act = 0;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      if (win) {
+        lo[nt] = tcol[nt] - a.W + 1;
+      } else {
+        const bool sel = (S[(w * PW + pcol[nt]) * nw32 + (j >> 5)] >> (j & 31)) & 1u;
+        lo[nt] = sel ? 0 : kNoKey;
+      }
+      hi[nt] = hicol[nt];
+      const bool live_col = max(lo[nt], kbase) <= min(hi[nt], kbase + 63);
+      act |= (__ballot(live_col) != 0ull ? 1u : 0u) << nt;
+    }
+    return act;
+  };
+
+  wait_vmem();
+  if (nitems > 0) st.dma_fix(tile0);
+  __syncthreads();
+
+  // Step s: item s is in `cur`; item s+1 goes into `next`, the buffer of
+  // item s-1, whose last reads came before the barrier that ended the
+  // previous step.  All reads of the item lists and bitsets come before the
+  // step's transfer is issued (the compiler cannot tell them apart from it
+  // and would wait).
+  f32x4 sreg[NT][4];
+  float bmax[NT], bsum[NT];
+  const typename Eng::NoHook nohook;
+  auto step = [&](int st_i, const char* cur, char* next) {
+    int kbase = 0, lo[NT], hi[NT];
+    const unsigned act = item(st_i, kbase, lo, hi);
+    if (st_i + 1 < nitems) issue(st_i + 1, next);
+    if (st_i == nwin) {  // window branch closed: park it
+      fold(gate1, true);
+      eng.reset();
+    }
+    if (act) {
+      auto ldK = [&](int c, int ks) { return St::ldK(cur, c, ks); };
+      auto ldV = [&](int u, int mc) { return St::ldV(cur, u, mc); };
+      eng.qk(ldK, sreg);
+      eng.template softmax<true, false>(sreg, kbase, lo, hi, a.sc2, bmax, bsum, nohook, act);
+      eng.pv(sreg, ldV);
+    }
+    wait_vmem();
+    if (st_i + 1 < nitems) st.dma_fix(next);
+    __syncthreads();
+  };
+  for (int st_i = 0; st_i < nitems; st_i += 2) {
+    step(st_i, tile0, tile1);
+    if (st_i + 1 >= nitems) break;
+    step(st_i + 1, tile1, tile0);
+  }
+  if (nwin == nitems) {
+    fold(gate1, true);
+  } else {
+    fold(gate0, false);
+  }
+}
+
 // ================================================================ launchers
 template <int DT, int D>
 static hipError_t full_dispatch(const FullPrefillArgs& a, int score_lse, hipStream_t s) {
@@ -937,12 +1178,26 @@ constexpr int kSparseStages = 2;
 
 template <int DT, int D>
 static hipError_t sparse_dispatch(SparsePrefillArgs a, hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  // two resident work groups of four waves per CU when two of them fit in LDS
+  constexpr bool dual = 2 * TileStage<DT, D, 256>::BYTES <= 64 * 1024;
+  if constexpr (dual) {
+    constexpr int NT = kSparseNT;
+    const int PWG = 4 * (16 * NT / G);
+    const int nw32 = (a.nblk + 31) / 32;
+    const size_t lds = ((size_t)(1 + 4 + PWG) * nw32 + a.nblk + 1) * sizeof(uint32_t);
+    if (lds <= 16 * 1024) {
+      a.nwg = a.B * a.Hkv * ((a.T + PWG - 1) / PWG);
+      const int per = (a.nwg + 7) / 8;
+      hipLaunchKernelGGL((sparse_prefill_dual_kernel<DT, D, NT>), dim3(8 * per), dim3(256), lds, s, a);
+      return hipGetLastError();
+    }
+  }
   constexpr int NW = kSparseWaves;
   // the ping-pong kernel needs three tile buffers in LDS (f32 with d = 128
   // does not fit and takes the one-column-tile kernel)
   constexpr bool pingpong = NW == 8 && 3 * TileStage<DT, D, 512>::BYTES <= 100 * 1024;
   constexpr int NT = pingpong ? kSparseNT : 1;
-  const int G = a.Hq / a.Hkv;
   const int PWG = NW * (16 * NT / G);
   a.nwg = a.B * a.Hkv * ((a.T + PWG - 1) / PWG);
   const int per = (a.nwg + 7) / 8;
