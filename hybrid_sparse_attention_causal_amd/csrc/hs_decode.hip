@@ -198,8 +198,8 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
     } else {
       eng.template softmax<true, false>(s, kb0, lo, hi, sc2, bmax, bsum);
       // block maxima are held until the chunk ends (lane group q keeps the
-      // chunk's tiles q, q + 4, ...): a store inside the loop would turn
-      // every wait for the next tile's loads into a full drain
+      // chunk's tiles q, q + 4, ...) and then written with one store per
+      // lane group instead of one per tile
       const int tt = (kb0 - kstart) >> 6;
 #pragma unroll
       for (int r = 0; r < kDecodeChunkBlocks / 4; ++r)
