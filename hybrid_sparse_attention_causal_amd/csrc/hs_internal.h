@@ -41,7 +41,7 @@ struct SparsePrefillArgs {
   const float* gates;
   void* o;
   int B, T, Hq, Hkv, nblk, topk, W;
-  int nwg;  // work groups before the XCD remap
+  int nwg;  // work groups (kv groups x position blocks)
   float sc2;
 };
 

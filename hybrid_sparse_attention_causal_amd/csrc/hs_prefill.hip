@@ -13,6 +13,27 @@
 
 namespace hs {
 
+// Work-group order for position-block kernels: block id i takes kv group
+// (sequence, group) bg = i % nbg and the rank-th latest position block, rank
+// = i / nbg.  Consecutive ids are dealt round-robin over the 8 XCDs, so with
+// nbg a multiple of 8 each XCD keeps to nbg/8 kv groups (their K/V stays in
+// its L2); with fewer groups a group's position blocks alternate over several
+// XCDs, and every XCD gets late (long) and early (short) blocks alike.  Each
+// XCD starts with the latest blocks.
+struct WgSlot {
+  int bg, pblk;
+  bool live;
+};
+__device__ __forceinline__ WgSlot wg_slot(int nbg, int npblk) {
+  const int i = blockIdx.x;
+  const int rank = i / nbg;
+  WgSlot w;
+  w.bg = i % nbg;
+  w.live = rank < npblk;
+  w.pblk = w.live ? npblk - 1 - rank : 0;
+  return w;
+}
+
 // ===================================================================== full
 // Work group = 4 wavefronts.  With Gw = min(G, 4) query heads of one kv group
 // per work group, wave w takes head hb*Gw + w%Gw and 16*NT consecutive query
@@ -153,10 +174,6 @@ __global__ __launch_bounds__(512, 2) void full_prefill_pp_kernel(FullPrefillArgs
   __shared__ __attribute__((aligned(16))) char tile1[St::BYTES];
   __shared__ __attribute__((aligned(16))) char tile2[St::BYTES];
 
-  const int per = gridDim.x >> 3;
-  // consecutive ids share an XCD; within an XCD the latest positions (the
-  // most tiles) are dispatched first
-  const int wgid = (blockIdx.x & 7) * per + (per - 1 - (blockIdx.x >> 3));
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const bool lag = w >= 4;
   const int T = a.T;
@@ -165,10 +182,11 @@ __global__ __launch_bounds__(512, 2) void full_prefill_pp_kernel(FullPrefillArgs
   const int PW = NT * PT;
   const int PWG = NW * PW;
   const int nwg_bg = (T + PWG - 1) / PWG;
-  const bool live = wgid < a.B * a.Hkv * nwg_bg;
-  const int bg = wgid / nwg_bg;
+  const WgSlot ws = wg_slot(a.B * a.Hkv, nwg_bg);
+  const bool live = ws.live;
+  const int bg = ws.bg;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
-  const int t0 = (wgid % nwg_bg) * PWG;
+  const int t0 = ws.pblk * PWG;
   const int tw0 = t0 + w * PW;
   const int nitems = live ? ((min(T, t0 + PWG) - 1) >> 6) + 1 : 0;
 
@@ -395,9 +413,6 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_prefill_kernel(SparsePrefil
 
   // XCD-aware remap: consecutive ids go round-robin over the 8 XCDs; give each
   // XCD a contiguous range of work groups (same kv group -> shared L2).
-  const int per = gridDim.x >> 3;
-  const int wgid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  const bool live = wgid < a.nwg;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int T = a.T;
@@ -405,9 +420,11 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_prefill_kernel(SparsePrefil
   const int PW = 16 * NT / G;
   const int PWG = NW * PW;
   const int nwg_bg = (T + PWG - 1) / PWG;
-  const int bg = wgid / nwg_bg;
+  const WgSlot ws = wg_slot(a.B * a.Hkv, nwg_bg);
+  const bool live = ws.live;
+  const int bg = ws.bg;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
-  const int t0 = (wgid % nwg_bg) * PWG;
+  const int t0 = ws.pblk * PWG;
   const int tw0 = t0 + w * PW;
   const int nw32 = (a.nblk + 31) >> 5;
   uint32_t* U = dyn;                      // union of the work group
@@ -636,11 +653,6 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
   __shared__ __attribute__((aligned(16))) char tile2[St::BYTES];
   extern __shared__ uint32_t dyn[];
 
-  const int per = gridDim.x >> 3;
-  // consecutive ids share an XCD; within an XCD the latest positions (the
-  // largest unions of selected blocks) are dispatched first
-  const int wgid = (blockIdx.x & 7) * per + (per - 1 - (blockIdx.x >> 3));
-  const bool live = wgid < a.nwg;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const bool lag = w >= 4;  // waves 4-7 run half a tile behind
@@ -650,9 +662,11 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
   const int PW = NT * PT;
   const int PWG = NW * PW;
   const int nwg_bg = (T + PWG - 1) / PWG;
-  const int bg = wgid / nwg_bg;
+  const WgSlot ws = wg_slot(a.B * a.Hkv, nwg_bg);
+  const bool live = ws.live;
+  const int bg = ws.bg;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
-  const int t0 = (wgid % nwg_bg) * PWG;
+  const int t0 = ws.pblk * PWG;
   const int tw0 = t0 + w * PW;
   const int nw32 = (a.nblk + 31) >> 5;
   uint32_t* U = dyn;
@@ -904,11 +918,6 @@ __global__ __launch_bounds__(256, 2) void sparse_prefill_dual_kernel(SparsePrefi
   __shared__ __attribute__((aligned(16))) char tile1[St::BYTES];
   extern __shared__ uint32_t dyn[];
 
-  const int per = gridDim.x >> 3;
-  // consecutive ids share an XCD; within an XCD the latest positions (the
-  // largest unions of selected blocks) are dispatched first
-  const int wgid = (blockIdx.x & 7) * per + (per - 1 - (blockIdx.x >> 3));
-  const bool live = wgid < a.nwg;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int T = a.T;
@@ -917,9 +926,11 @@ __global__ __launch_bounds__(256, 2) void sparse_prefill_dual_kernel(SparsePrefi
   const int PW = NT * PT;
   const int PWG = NW * PW;
   const int nwg_bg = (T + PWG - 1) / PWG;
-  const int bg = wgid / nwg_bg;
+  const WgSlot ws = wg_slot(a.B * a.Hkv, nwg_bg);
+  const bool live = ws.live;
+  const int bg = ws.bg;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
-  const int t0 = (wgid % nwg_bg) * PWG;
+  const int t0 = ws.pblk * PWG;
   const int tw0 = t0 + w * PW;
   const int nw32 = (a.nblk + 31) >> 5;
   uint32_t* U = dyn;
@@ -1133,12 +1144,11 @@ static hipError_t full_dispatch(const FullPrefillArgs& a, int score_lse, hipStre
   if constexpr (pingpong) {
     if (G <= 16) {
       const int PWG = 8 * (16 * NT / G);
-      const long nwg = (long)a.B * a.Hkv * ((a.T + PWG - 1) / PWG);
-      const unsigned per = (unsigned)((nwg + 7) / 8);
+      const unsigned nwg = (unsigned)((long)a.B * a.Hkv * ((a.T + PWG - 1) / PWG));
       if (score_lse)
-        hipLaunchKernelGGL((full_prefill_pp_kernel<DT, D, 1>), dim3(8 * per), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((full_prefill_pp_kernel<DT, D, 1>), dim3(nwg), dim3(512), 0, s, a);
       else
-        hipLaunchKernelGGL((full_prefill_pp_kernel<DT, D, 0>), dim3(8 * per), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((full_prefill_pp_kernel<DT, D, 0>), dim3(nwg), dim3(512), 0, s, a);
       return hipGetLastError();
     }
   }
@@ -1188,8 +1198,7 @@ static hipError_t sparse_dispatch(SparsePrefillArgs a, hipStream_t s) {
     const size_t lds = ((size_t)(1 + 4 + PWG) * nw32 + a.nblk + 1) * sizeof(uint32_t);
     if (lds <= 16 * 1024) {
       a.nwg = a.B * a.Hkv * ((a.T + PWG - 1) / PWG);
-      const int per = (a.nwg + 7) / 8;
-      hipLaunchKernelGGL((sparse_prefill_dual_kernel<DT, D, NT>), dim3(8 * per), dim3(256), lds, s, a);
+      hipLaunchKernelGGL((sparse_prefill_dual_kernel<DT, D, NT>), dim3(a.nwg), dim3(256), lds, s, a);
       return hipGetLastError();
     }
   }
@@ -1200,13 +1209,12 @@ static hipError_t sparse_dispatch(SparsePrefillArgs a, hipStream_t s) {
   constexpr int NT = pingpong ? kSparseNT : 1;
   const int PWG = NW * (16 * NT / G);
   a.nwg = a.B * a.Hkv * ((a.T + PWG - 1) / PWG);
-  const int per = (a.nwg + 7) / 8;
   const int nw32 = (a.nblk + 31) / 32;
   const size_t lds = ((size_t)(1 + NW + PWG) * nw32 + a.nblk + 1) * sizeof(uint32_t);
   if constexpr (pingpong)
-    hipLaunchKernelGGL((sparse_prefill_pp_kernel<DT, D, NT>), dim3(8 * per), dim3(512), lds, s, a);
+    hipLaunchKernelGGL((sparse_prefill_pp_kernel<DT, D, NT>), dim3(a.nwg), dim3(512), lds, s, a);
   else
-    hipLaunchKernelGGL((sparse_prefill_kernel<DT, D, NT, NW, kSparseStages>), dim3(8 * per), dim3(64 * NW), lds,
+    hipLaunchKernelGGL((sparse_prefill_kernel<DT, D, NT, NW, kSparseStages>), dim3(a.nwg), dim3(64 * NW), lds,
                        s, a);
   return hipGetLastError();
 }
