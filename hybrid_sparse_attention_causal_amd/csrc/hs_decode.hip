@@ -881,9 +881,10 @@ __global__ __launch_bounds__(512) void decode_sparse_token_kernel(DecodeSparseAr
   Eng eng;
   eng.reset();
 #pragma unroll
-  for (int ks = 0; ks < Eng::NS; ++ks)
-    eng.qf[0][ks] = col < G ? Tt::ld((const char*)a.q + ((size_t)(b * a.Hq + h) * D + 32 * ks + q8) * 2)
-                            : Tt::zero();
+  for (int ks = 0; ks < Eng::NS; ++ks) {
+    const Frag f = Tt::ld((const char*)a.q + ((size_t)(b * a.Hq + (col < G ? h : g * G)) * D + 32 * ks + q8) * 2);
+    eng.qf[0][ks] = col < G ? f : Tt::zero();
+  }
   const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * a.C * D;
   const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * a.C * D;
   const int32_t* il = a.idx + (size_t)(b * a.Hkv + g) * a.nsel;
@@ -892,30 +893,47 @@ __global__ __launch_bounds__(512) void decode_sparse_token_kernel(DecodeSparseAr
   int lo[1], hi[1];
 
   // work group blockIdx.y of gridDim.y takes every gridDim.y-th group of
-  // eight tiles
+  // eight tiles.  All of a tile's gathered rows are requested at once, with
+  // unconditional loads (a padding entry reads token 0; its logit is masked
+  // and its values zeroed by selects): a load under a per-lane branch would
+  // make the compiler wait for each one in turn.
   for (int it = blockIdx.y * NW + w; it < ntile; it += gridDim.y * NW) {
     const int s0 = 64 * it;
     int tok = s0 + lane < a.nsel ? il[s0 + lane] : -1;
     if (tok >= L) tok = -1;
     const int nvalid = __popcll(__ballot(tok >= 0));  // valid entries form a prefix
     if (nvalid == 0) continue;
+    const int tsafe = tok >= 0 ? tok : 0;
     lo[0] = col < G ? 0 : kNoKey;
     hi[0] = s0 + nvalid - 1;
-    Frag vc[4];
-    auto ldK = [&](int c, int ks) {
-      const int tk = __shfl(tok, tile_key(c, r16));
-      return tk >= 0 ? fp8x8_frag(*(const uint2*)(kg + (size_t)tk * D + 32 * ks + q8)) : Tt::zero();
-    };
-    auto ldV = [&](int u, int mc) {
-      if ((mc & 3) == 0) {
-        uint32_t wv[8];
+    uint2 kraw[4][Eng::NS];
+    uint32_t vraw[2][D / 64][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tk = __shfl(tok, 32 * u + q8 + e);
-          wv[e] = tk >= 0 ? *(const uint32_t*)(vg + (size_t)tk * D + 64 * (mc >> 2) + 4 * r16) : 0u;
-        }
-        fp8_vfrag4(wv, vc);
+    for (int c = 0; c < 4; ++c) {
+      const int tk = __shfl(tsafe, tile_key(c, r16));
+#pragma unroll
+      for (int ks = 0; ks < Eng::NS; ++ks) kraw[c][ks] = *(const uint2*)(kg + (size_t)tk * D + 32 * ks + q8);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tk = __shfl(tsafe, 32 * u + q8 + e);
+#pragma unroll
+        for (int hf = 0; hf < D / 64; ++hf) vraw[u][hf][e] = *(const uint32_t*)(vg + (size_t)tk * D + 64 * hf + 4 * r16);
       }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool ok = 32 * u + q8 + e < nvalid;
+#pragma unroll
+        for (int hf = 0; hf < D / 64; ++hf) vraw[u][hf][e] = ok ? vraw[u][hf][e] : 0u;
+      }
+    Frag vc[4];
+    auto ldK = [&](int c, int ks) { return fp8x8_frag(kraw[c][ks]); };
+    auto ldV = [&](int u, int mc) {
+      if ((mc & 3) == 0) fp8_vfrag4(vraw[u][mc >> 2], vc);
       return vc[mc & 3];
     };
     eng.template tile<true, false>(ldK, ldV, s0, lo, hi, sc2, bmax, bsum);
