@@ -99,9 +99,10 @@ size_t decode_full_ws(const hs_shape* s) {
 }
 // keys [rows][C], histograms [rows][2 * 2048], counts [rows] (padded to 4),
 // candidates [rows][kTokCap] keys and ids
+int token_nseg(const hs_shape* s) { return (s->kv_len + hs::kTokSeg - 1) / hs::kTokSeg; }
 size_t token_topk_ws(const hs_shape* s) {
   const size_t rows = (size_t)s->batch * s->hkv;
-  return rows * ((size_t)s->kv_len + 2 * 2048 + 2 * hs::kTokCap) * sizeof(uint32_t) +
+  return rows * ((size_t)s->kv_len + 2 * 2048 + 2 * hs::kTokCap + 2 * (size_t)token_nseg(s)) * sizeof(uint32_t) +
          ((rows + 3) / 4) * 4 * sizeof(uint32_t);
 }
 // token-mode sparse layer: partial states of up to kTokSplitMax work groups per
@@ -265,6 +266,8 @@ hs_status hs_block_topk(const hs_shape* s, const float* blk_raw, const float* ls
     a.hist = a.keys + rows * s->kv_len;
     a.cand_key = a.hist + rows * 2 * 2048 + ((rows + 3) / 4) * 4;
     a.cand_idx = (int32_t*)(a.cand_key + rows * hs::kTokCap);
+    a.nseg = token_nseg(s);
+    a.seg = (uint32_t*)(a.cand_idx + rows * hs::kTokCap);
     a.B = s->batch;
     a.Hq = s->hq;
     a.Hkv = s->hkv;

@@ -610,8 +610,6 @@ __device__ void find_bin(const uint32_t* h, int nb, int k, uint32_t* scan, int* 
   __syncthreads();
 }
 
-constexpr int kTokSeg = 16384;  // keys per work group in the histogram and candidate passes
-
 // grid (rows, ceil(C / kTokSeg)), 1024 threads: the level-2 histogram (bits
 // 20..10 of the keys whose top 11 bits are the level-1 threshold bin); every
 // group of a row finds that bin again from the level-1 histogram
@@ -645,8 +643,10 @@ __global__ __launch_bounds__(1024) void token_hist2_kernel(TokenTopkArgs a) {
 
 // grid (rows, ceil(C / kTokSeg)), 1024 threads: compacts the candidates, the
 // keys whose top 22 bits are at least the level-2 threshold prefix (fewer
-// than kb above it plus that prefix's bin), as (key, token id) pairs in
-// arbitrary order; the count may exceed kTokCap (then only the count is kept)
+// than kb above it plus that prefix's bin), as (key, token id) pairs; each
+// segment's candidates form one run in token order, the runs lie in arbitrary
+// order and seg records where each one went.  The count may exceed kTokCap
+// (then only the count is kept).
 __global__ __launch_bounds__(1024) void token_cand_kernel(TokenTopkArgs a) {
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t scan[1024];
@@ -668,12 +668,25 @@ __global__ __launch_bounds__(1024) void token_cand_kernel(TokenTopkArgs a) {
   find_bin(hist, 2048, need, scan, res);
   const uint32_t pfx = (b1 << 11) | (uint32_t)res[0];
   const uint32_t* keys = a.keys + (size_t)row * a.C;
+  // thread t takes the PER consecutive keys s0 + PER*t .. (16-byte loads),
+  // so the block's exclusive scan below keeps the candidates in token order
   constexpr int PER = kTokSeg / 1024;
+  static_assert(PER % 4 == 0, "keys are read four at a time");
+  uint32_t kv[PER];
+  const int i0 = s0 + PER * t;
+#pragma unroll
+  for (int n = 0; n < PER; n += 4) {
+    // a row holds C keys, C a multiple of 64, so a quad never leaves it
+    const uint4 q = i0 + n < ncand ? *(const uint4*)(keys + i0 + n) : make_uint4(0u, 0u, 0u, 0u);
+    kv[n] = q.x;
+    kv[n + 1] = q.y;
+    kv[n + 2] = q.z;
+    kv[n + 3] = q.w;
+  }
   uint32_t flags = 0u, cnt = 0u;
 #pragma unroll
   for (int n = 0; n < PER; ++n) {
-    const int i = s0 + t + 1024 * n;
-    if (i < ncand && (keys[i] >> 10) >= pfx) {
+    if (i0 + n < ncand && (kv[n] >> 10) >= pfx) {
       flags |= 1u << n;
       ++cnt;
     }
@@ -688,7 +701,12 @@ __global__ __launch_bounds__(1024) void token_cand_kernel(TokenTopkArgs a) {
     __syncthreads();
   }
   const uint32_t excl = scan[t] - cnt;
-  if (t == 1023) base_s = atomicAdd(a.hist + rows * 2 * 2048 + row, scan[1023]);
+  if (t == 1023) {
+    base_s = atomicAdd(a.hist + rows * 2 * 2048 + row, scan[1023]);
+    // this segment's run: its candidates in ascending token order
+    a.seg[((size_t)row * a.nseg + blockIdx.y) * 2] = base_s;
+    a.seg[((size_t)row * a.nseg + blockIdx.y) * 2 + 1] = scan[1023];
+  }
   __syncthreads();
   uint32_t pos = base_s + excl;
   uint32_t* ck = a.cand_key + (size_t)row * kTokCap;
@@ -696,38 +714,11 @@ __global__ __launch_bounds__(1024) void token_cand_kernel(TokenTopkArgs a) {
 #pragma unroll
   for (int n = 0; n < PER; ++n) {
     if ((flags >> n) & 1u) {
-      const int i = s0 + t + 1024 * n;
       if (pos < (uint32_t)kTokCap) {
-        ck[pos] = keys[i];
-        ci[pos] = i;
+        ck[pos] = kv[n];
+        ci[pos] = i0 + n;
       }
       ++pos;
-    }
-  }
-}
-
-// In-place bitonic sort of P (a power of two) LDS entries by `before`
-// (a strict total order); 1024 threads.
-template <class BF>
-__device__ void bitonic_sort(uint32_t* k, int32_t* v, int P, const BF& before) {
-  const int t = threadIdx.x;
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int e = t; e < P / 2; e += 1024) {
-        const int lo = 2 * e - (e & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const bool sw = up ? before(k[hi], v[hi], k[lo], v[lo]) : before(k[lo], v[lo], k[hi], v[hi]);
-        if (sw) {
-          const uint32_t tk = k[lo];
-          k[lo] = k[hi];
-          k[hi] = tk;
-          const int32_t tv = v[lo];
-          v[lo] = v[hi];
-          v[hi] = tv;
-        }
-      }
-      __syncthreads();
     }
   }
 }
@@ -752,34 +743,90 @@ __global__ __launch_bounds__(1024) void token_select_kernel(TokenTopkArgs a) {
   int32_t* out = a.idx + (size_t)row * (kb + a.n_recent);
   int nsel;
 
+  // Writes, in ascending order of position, the ids of the n entries whose
+  // key is above thr and of the first need_eq entries whose key equals thr.
+  // Wave w owns the contiguous entries [w*wseg, (w+1)*wseg) and walks them 64
+  // at a time; ballots give each lane its rank among the keys > thr and
+  // == thr of its wave, and the 16 waves' counts give every wave its first
+  // output slot and its first tie rank.
+  auto emit = [&](int n, uint32_t thr, int need_eq, auto key_of, auto id_of) {
+    const int wseg = ((n + 1023) / 1024) * 64;
+    const int i0 = min(n, w * wseg), i1 = min(n, i0 + wseg);
+    uint32_t ngt = 0, neq = 0;
+    for (int i = i0; i < i1; i += 64) {
+      const bool in = i + lane < i1;
+      const uint32_t k = in ? key_of(i + lane) : 0u;
+      ngt += __popcll(__ballot(in && k > thr));
+      neq += __popcll(__ballot(in && k == thr));
+    }
+    if (lane == 0) {
+      wsum[w] = ngt;
+      wsum[16 + w] = neq;
+    }
+    __syncthreads();
+    uint32_t gt_base = 0, eq_base = 0;
+    for (int v = 0; v < w; ++v) {
+      gt_base += wsum[v];
+      eq_base += wsum[16 + v];
+    }
+    uint32_t pos = gt_base + min(eq_base, (uint32_t)need_eq);
+    for (int i = i0; i < i1; i += 64) {
+      const bool in = i + lane < i1;
+      const uint32_t k = in ? key_of(i + lane) : 0u;
+      const uint64_t eqm = __ballot(in && k == thr);
+      const uint32_t eq_rank = eq_base + __popcll(eqm & lt_mask);
+      const bool take = in && (k > thr || (k == thr && eq_rank < (uint32_t)need_eq));
+      const uint64_t tm = __ballot(take);
+      if (take) out[pos + __popcll(tm & lt_mask)] = id_of(i + lane);
+      pos += __popcll(tm);
+      eq_base += __popcll(eqm);
+    }
+  };
+
   const uint32_t ncnd = a.hist[(size_t)a.B * a.Hkv * 2 * 2048 + row];
   if (ncand <= kb) {
     for (int i = t; i < ncand; i += 1024) out[i] = i;
     nsel = ncand;
   } else if (ncnd <= (uint32_t)kTokCap) {
-    // the candidates (at least kb, all keys above the threshold prefix):
-    // sort by key descending, ties to the smaller id, keep kb, then sort
-    // the kept ids ascending
-    uint32_t* sk = cand_k;
-    int32_t* si = cand_i;
-    int P = 64;
-    while (P < (int)ncnd) P <<= 1;
+    // the candidates (at least kb: all keys whose top 22 bits reach the
+    // level-2 threshold prefix): gathered in ascending token order (each key
+    // segment's run is in order, and runs follow their segments), then the
+    // last 10 bits decide inside the threshold prefix and ties go to the
+    // smaller token
+    const uint32_t* gh = a.hist + (size_t)row * 2048;
+    for (int i = t; i < 2048; i += 1024) hist[i] = gh[i];
+    __syncthreads();
+    find_bin(hist, 2048, kb, scan, res);
+    const uint32_t b1 = (uint32_t)res[0];
+    int need = kb - res[1];
+    const uint32_t* gh2 = a.hist + (size_t)a.B * a.Hkv * 2048 + (size_t)row * 2048;
+    for (int i = t; i < 2048; i += 1024) hist[i] = gh2[i];
+    __syncthreads();
+    find_bin(hist, 2048, need, scan, res);
+    const uint32_t pfx = (b1 << 11) | (uint32_t)res[0];
+    need -= res[1];
     const uint32_t* ck = a.cand_key + (size_t)row * kTokCap;
     const int32_t* ci = a.cand_idx + (size_t)row * kTokCap;
-    for (int e = t; e < P; e += 1024) {
-      sk[e] = e < (int)ncnd ? ck[e] : 0u;
-      si[e] = e < (int)ncnd ? ci[e] : 0x7fffffff;
+    const uint32_t* sg = a.seg + (size_t)row * a.nseg * 2;
+    const int nsg = (ncand + kTokSeg - 1) / kTokSeg;
+    int off = 0;
+    for (int q = 0; q < nsg; ++q) {
+      const int base = (int)sg[2 * q], cnt = (int)sg[2 * q + 1];
+      for (int e = t; e < cnt; e += 1024) {
+        cand_k[off + e] = ck[base + e];
+        cand_i[off + e] = ci[base + e];
+      }
+      off += cnt;
     }
+    for (int i = t; i < 1024; i += 1024) hist[i] = 0u;
     __syncthreads();
-    bitonic_sort(sk, si, P, [](uint32_t ka, int32_t ia, uint32_t kb_, int32_t ib) {
-      return ka > kb_ || (ka == kb_ && ia < ib);
-    });
-    int Q = 64;
-    while (Q < kb) Q <<= 1;
-    for (int e = t; e < Q; e += 1024) sk[e] = e < kb ? (uint32_t)si[e] : 0xffffffffu;
+    for (int e = t; e < (int)ncnd; e += 1024)
+      if ((cand_k[e] >> 10) == pfx) atomicAdd(&hist[cand_k[e] & 1023u], 1u);
     __syncthreads();
-    bitonic_sort(sk, si, Q, [](uint32_t ka, int32_t, uint32_t kb_, int32_t) { return ka < kb_; });
-    for (int e = t; e < kb; e += 1024) out[e] = (int32_t)sk[e];
+    find_bin(hist, 1024, need, scan, res);
+    const uint32_t thr = (pfx << 10) | (uint32_t)res[0];
+    const int need_eq = need - res[1];  // >= 1 candidates equal to thr are taken
+    emit(ncnd, thr, need_eq, [&](int i) { return cand_k[i]; }, [&](int i) { return cand_i[i]; });
     nsel = kb;
   } else {
     // level 1: the global histogram of the top 11 bits
@@ -811,42 +858,7 @@ __global__ __launch_bounds__(1024) void token_select_kernel(TokenTopkArgs a) {
     find_bin(hist, 1024, need, scan, res);
     const uint32_t thr = (p2 << 10) | (uint32_t)res[0];
     const int need_eq = need - res[1];  // >= 1 keys equal to thr are taken
-    // emit ascending: wave w owns the contiguous candidates
-    // [w*wseg, (w+1)*wseg) and walks them 64 at a time; ballots give each
-    // lane its rank among the keys > thr and == thr of its wave, and one
-    // exclusive scan over the 16 waves' counts gives every wave its first
-    // output slot and its first tie rank.
-    const int wseg = ((ncand + 1023) / 1024) * 64;
-    const int i0 = min(ncand, w * wseg), i1 = min(ncand, i0 + wseg);
-    uint32_t ngt = 0, neq = 0;
-    for (int i = i0; i < i1; i += 64) {
-      const uint32_t k = i + lane < i1 ? keys[i + lane] : 0u;
-      const bool in = i + lane < i1;
-      ngt += __popcll(__ballot(in && k > thr));
-      neq += __popcll(__ballot(in && k == thr));
-    }
-    if (lane == 0) {
-      wsum[w] = ngt;
-      wsum[16 + w] = neq;
-    }
-    __syncthreads();
-    uint32_t gt_base = 0, eq_base = 0;
-    for (int v = 0; v < w; ++v) {
-      gt_base += wsum[v];
-      eq_base += wsum[16 + v];
-    }
-    uint32_t pos = gt_base + min(eq_base, (uint32_t)need_eq);
-    for (int i = i0; i < i1; i += 64) {
-      const bool in = i + lane < i1;
-      const uint32_t k = in ? keys[i + lane] : 0u;
-      const uint64_t eqm = __ballot(in && k == thr);
-      const uint32_t eq_rank = eq_base + __popcll(eqm & lt_mask);
-      const bool take = in && (k > thr || (k == thr && eq_rank < (uint32_t)need_eq));
-      const uint64_t tm = __ballot(take);
-      if (take) out[pos + __popcll(tm & lt_mask)] = i + lane;
-      pos += __popcll(tm);
-      eq_base += __popcll(eqm);
-    }
+    emit(ncand, thr, need_eq, [&](int i) { return keys[i]; }, [](int i) { return i; });
     nsel = kb;
   }
   for (int r = t; r < nrec; r += 1024) out[nsel + r] = L - nrec + r;

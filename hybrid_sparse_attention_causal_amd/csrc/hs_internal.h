@@ -98,11 +98,15 @@ struct TokenTopkArgs {
                           // then [B*Hkv] candidate counts (zeroed together)
   uint32_t* cand_key;     // workspace [B*Hkv][kTokCap]
   int32_t* cand_idx;      // workspace [B*Hkv][kTokCap]
+  uint32_t* seg;          // workspace [B*Hkv][nseg][2]: (first slot, count) of each
+                          // key segment's candidates in cand_key / cand_idx
+  int nseg;               // key segments per row, ceil(C / kTokSeg)
   int B, Hq, Hkv, C, kb, n_recent;
 };
 // candidates kept per row for the final exact selection (rows with more fall
 // back to a radix select over the whole row)
 constexpr int kTokCap = 8192;
+constexpr int kTokSeg = 16384;  // keys per work group in the histogram and candidate passes
 
 hipError_t launch_token_topk(const TokenTopkArgs& a, hipStream_t s);
 hipError_t launch_decode_sparse_token(const DecodeSparseArgs& a, int D, hipStream_t s);
