@@ -581,20 +581,22 @@ __global__ __launch_bounds__(256) void token_keys_kernel(TokenTopkArgs a) {
 // Block-wide search in a histogram of nb bins (nb = 1024 or 2048, 1024 threads):
 // the bin b with count(> b) < k <= count(>= b); returns b and count(> b).
 __device__ void find_bin(const uint32_t* h, int nb, int k, uint32_t* scan, int* res) {
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int per = nb / 1024;
   // thread t owns bins [nb - (t+1)*per, nb - t*per), i.e. descending order
   uint32_t own = 0;
   for (int e = 0; e < per; ++e) own += h[nb - t * per - 1 - e];
-  scan[t] = own;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const uint32_t v = t >= off ? scan[t - off] : 0u;
-    __syncthreads();
-    scan[t] += v;
-    __syncthreads();
+  // inclusive scan: within the wave by shuffles, then over the 16 wave totals
+  uint32_t incl = own;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
   }
-  const uint32_t incl = scan[t], excl = incl - own;
+  if (lane == 63) scan[w] = incl;
+  __syncthreads();
+  for (int v = 0; v < w; ++v) incl += scan[v];
+  const uint32_t excl = incl - own;
   if (excl < (uint32_t)k && incl >= (uint32_t)k) {
     uint32_t above = excl;
     for (int e = 0; e < per; ++e) {
