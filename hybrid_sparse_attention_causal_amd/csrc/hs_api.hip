@@ -91,7 +91,7 @@ hs_status check_decode(const char* fn, const hs_shape* s) {
 }
 
 int decode_nch(const hs_shape* s) {
-  const int span = 64 * hs::kDecodeChunkBlocks;
+  const int span = 64 * hs::decode_chunk_blocks(s->kv_len);
   return (s->kv_len + span - 1) / span;
 }
 size_t decode_full_ws(const hs_shape* s) {
@@ -192,7 +192,7 @@ hs_status hs_full_attn_fwd_scores(const hs_shape* s, const void* q, const void* 
     a.Hkv = s->hkv;
     a.C = s->kv_len;
     a.nch = decode_nch(s);
-    a.ch_blocks = hs::kDecodeChunkBlocks;
+    a.ch_blocks = hs::decode_chunk_blocks(s->kv_len);
     a.token = block == 1;
     a.kv_dtype = s->kv_dtype;
     a.kv_scale = s->kv_scale;

@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
   const int bg = (int)(unit / a.nch);
   const int g = bg % a.Hkv, b = bg / a.Hkv;
   const int L = __builtin_amdgcn_readfirstlane(a.lens[b]);
-  const int span = kDecodeChunkBlocks * 64;
+  const int span = a.ch_blocks * 64;  // ch_blocks <= kDecodeChunkBlocksMax
   const int kstart = ch * span;
   if (kstart >= L) return;
   const int kend = min(L, kstart + span);
@@ -144,9 +144,9 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
       }
     }
   };
-  float bkeep[kDecodeChunkBlocks / 4];
+  float bkeep[kDecodeChunkBlocksMax / 4];
 #pragma unroll
-  for (int r = 0; r < kDecodeChunkBlocks / 4; ++r) bkeep[r] = -INFINITY;
+  for (int r = 0; r < kDecodeChunkBlocksMax / 4; ++r) bkeep[r] = -INFINITY;
   RawK rk;
   RawV rv;
   // One tile: QK^T on the keys in rk, the keys of tile nx are requested,
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
       // lane group instead of one per tile
       const int tt = (kb0 - kstart) >> 6;
 #pragma unroll
-      for (int r = 0; r < kDecodeChunkBlocks / 4; ++r)
+      for (int r = 0; r < kDecodeChunkBlocksMax / 4; ++r)
         if (tt == 4 * r + (lane >> 4)) bkeep[r] = bmax[0];
       (void)j;
     }
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
 
   if (!TOKEN && col < G) {
 #pragma unroll
-    for (int r = 0; r < kDecodeChunkBlocks / 4; ++r) {
+    for (int r = 0; r < kDecodeChunkBlocksMax / 4; ++r) {
       const int kb = kstart + 64 * (4 * r + (lane >> 4));
       if (kb < kend) rawrow[kb >> 6] = bkeep[r] * kLn2;
     }

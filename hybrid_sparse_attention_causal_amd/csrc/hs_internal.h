@@ -45,10 +45,12 @@ struct SparsePrefillArgs {
   float sc2;
 };
 
-// split-K chunking of the decode full layer: 64-key tiles per chunk (the
-// kernel keeps one block maximum per tile in registers until the chunk ends)
-constexpr int kDecodeChunkBlocks = 16;
-static_assert(kDecodeChunkBlocks % 4 == 0, "chunk tiles are spread over four lane groups");
+// split-K chunking of the decode full layer: at most this many 64-key tiles
+// per chunk (the kernel keeps one block maximum per tile in registers until
+// the chunk ends); the host picks 16 or 32 by context capacity
+constexpr int kDecodeChunkBlocksMax = 32;
+static_assert(kDecodeChunkBlocksMax % 4 == 0, "chunk tiles are spread over four lane groups");
+inline int decode_chunk_blocks(int capacity) { return capacity > 131072 ? 32 : 16; }
 
 struct DecodeFullArgs {
   const void* q;
