@@ -324,6 +324,9 @@ __global__ __launch_bounds__(256) void block_topk_kernel(TopkArgs a) {
   const int ncand = (t >> 6) + (a.diag ? 1 : 0);
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
+  // every load is unconditional (entries past the visible blocks read a
+  // clamped slot of the same row and are dropped by a select): loads under a
+  // per-lane branch would be waited for one by one
   float x[MAXI];
 #pragma unroll
   for (int i = 0; i < MAXI; ++i) x[i] = -INFINITY;
@@ -331,11 +334,11 @@ __global__ __launch_bounds__(256) void block_topk_kernel(TopkArgs a) {
     const int h = g * G + hh;
     const float* rp = a.raw + ((size_t)(b * a.Hq + h) * R + tr) * a.raw_stride;
     const float ls = a.lse[(size_t)(b * a.Hq + h) * R + tr];
+    float v[MAXI];
 #pragma unroll
-    for (int i = 0; i < MAXI; ++i) {
-      const int j = i * 64 + lane;
-      if (j < nvis) x[i] = fmaxf(x[i], rp[j] - ls);
-    }
+    for (int i = 0; i < MAXI; ++i) v[i] = rp[min(i * 64 + lane, a.raw_stride - 1)];
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) x[i] = i * 64 + lane < nvis ? fmaxf(x[i], v[i] - ls) : x[i];
   }
   const size_t orow = (size_t)(b * a.Hkv + g) * R + tr;
   if (a.gs) {
