@@ -363,7 +363,12 @@ __global__ __launch_bounds__(256) void block_topk_kernel(TopkArgs a) {
       int cnt = 0;
 #pragma unroll
       for (int i = 0; i < MAXI; ++i) cnt += __popcll(__ballot(u[i] >= c));
-      if (cnt >= kb) thr = c;
+      if (cnt >= kb) {
+        thr = c;
+        // exactly kb keys reach c: they are the selection whatever the lower
+        // bits (ties at thr are then all taken)
+        if (cnt == kb) break;
+      }
     }
     int gt = 0;
 #pragma unroll
