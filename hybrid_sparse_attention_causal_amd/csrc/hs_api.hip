@@ -293,8 +293,8 @@ hs_status hs_block_topk(const hs_shape* s, const float* blk_raw, const float* ls
     a.R = s->q_len;
     a.raw_stride = (s->q_len + 63) / 64;
   }
-  if (a.raw_stride > 1024)
-    return fail(HS_ERR_UNSUPPORTED, "%s: more than 1024 candidate blocks per row", fn);
+  if (a.raw_stride > 4096)
+    return fail(HS_ERR_UNSUPPORTED, "%s: more than 4096 candidate blocks per row", fn);
   if (s->batch == 0 || a.R == 0) return ok();
   REQUIRE_PTR(blk_raw);
   REQUIRE_PTR(lse);

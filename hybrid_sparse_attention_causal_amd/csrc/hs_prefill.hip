@@ -1184,7 +1184,9 @@ hipError_t launch_block_topk(const TopkArgs& a, int max_blocks, hipStream_t s) {
   else if (max_blocks <= 128) hipLaunchKernelGGL(block_topk_kernel<2>, grid, dim3(256), 0, s, a);
   else if (max_blocks <= 256) hipLaunchKernelGGL(block_topk_kernel<4>, grid, dim3(256), 0, s, a);
   else if (max_blocks <= 512) hipLaunchKernelGGL(block_topk_kernel<8>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(block_topk_kernel<16>, grid, dim3(256), 0, s, a);
+  else if (max_blocks <= 1024) hipLaunchKernelGGL(block_topk_kernel<16>, grid, dim3(256), 0, s, a);
+  else if (max_blocks <= 2048) hipLaunchKernelGGL(block_topk_kernel<32>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(block_topk_kernel<64>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -140,7 +140,9 @@ hs_status hs_full_attn_fwd_scores(const hs_shape* shape, const void* q, const vo
  *   the n_recent newest tokens are always added and do not count against
  *   topk; idx [batch][hkv][topk+n_recent] holds token ids, ascending, -1
  *   padded.  grp_score (nullable) [batch][hkv][C] receives S_g for i < L_b.
- * topk is 1..1024 in block mode and 1..4096 in token mode.
+ * topk is 1..1024 in block mode and 1..4096 in token mode.  Block mode takes
+ * at most 4096 blocks per row (T, or the cache capacity, up to 262144);
+ * longer rows return HS_ERR_UNSUPPORTED.
  */
 hs_status hs_block_topk(const hs_shape* shape, const float* blk_raw, const float* lse,
                         int block, int topk, int n_recent, int flags, float* grp_score,

@@ -111,6 +111,16 @@ def test_small_ragged(W, gates):
     check_sequences(run, range(6), gates=gates)
 
 
+def test_long_capacity_chunks():
+    """Capacity above 128K: the full layer's split-K chunks are 32 tiles long."""
+    say("[decode capacity 196608] B=2 Hq=8 Hkv=2 d=128")
+    cfg = gen.config(4, B=2, T=196608, Hq=8, Hkv=2, d=128, kb=8, W=128, N=1, L_lo=1, L_hi=196608)
+    inp = gen.make_decode(cfg)
+    inp.lens = np.array([150001, 196608], np.int32)
+    run = DecodeRun(inp)
+    check_sequences(run, range(2))
+
+
 def test_group_of_16_and_d64():
     say("[decode G=16 d=64]")
     cfg = gen.config(4, B=3, T=2048, Hq=16, Hkv=1, d=64, kb=5, W=128, N=1, L_lo=300, L_hi=2048)

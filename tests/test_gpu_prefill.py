@@ -234,6 +234,18 @@ def test_config3_80b_shaped_sampled():
     check_run(run, pos)
 
 
+def test_long_sequence_wide_bitsets():
+    """T = 53312 with one head per kv group: the selection bitsets of a
+    four-wave group would pass 16 KiB of LDS, so the sparse layer takes the
+    8-wave kernel with three tile buffers."""
+    say("[long] T=53312 Hq=2 Hkv=2 d=64 bf16, sampled rows")
+    cfg = gen.config(1, T=53312, Hq=2, Hkv=2, d=64, dtype="bf16", kb=8, W=64, N=1)
+    inp = gen.make_prefill(cfg)
+    run = Run(inp)
+    pos = sample_rows(53312, every=997, head=64, tail=64)
+    check_run(run, pos)
+
+
 def test_repeat_runs_are_bitwise_identical():
     say("[determinism]")
     inp = gen.make_prefill(gen.config(1, T=500, Hq=8, Hkv=2, d=128, dtype="bf16", N=1))
