@@ -1,13 +1,18 @@
 // hs_prefill.hip -- prefill kernels of the hybrid block on gfx950.
 //
-//  full_prefill_kernel   full causal GQA attention + per-64-block scores in one
-//                        pass (HySparse explainer 3.4.1, "Modified
-//                        FlashAttention Kernel"; paper 3.2)
-//  block_topk_kernel     exp(raw - LSE), GQA group maximum, top-k
-//                        (explainer 3.4.1 eq. S_g, 3.4.2; paper 3.2)
-//  sparse_prefill_kernel one sparse layer: gathered-block branch over the
-//                        shared K/V + sliding window over the layer's own K'/V'
-//                        + sigmoid gates (explainer 3.4.3; paper 3.1, 3.3)
+//  full layer: full causal GQA attention + per-64-block scores in one pass
+//  (HySparse explainer 3.4.1, "Modified FlashAttention Kernel"; paper 3.2)
+//    full_prefill_pp_kernel      8 waves, ping-pong schedule (G <= 16)
+//    full_prefill_kernel         4 waves (fp32 with d = 128, or G > 16)
+//  block_topk_kernel: exp(raw - LSE), GQA group maximum, top-k
+//  (explainer 3.4.1 eq. S_g, 3.4.2; paper 3.2)
+//  one sparse layer: gathered-block branch over the shared K/V + sliding
+//  window over the layer's own K'/V' + sigmoid gates (explainer 3.4.3; paper
+//  3.1, 3.3)
+//    sparse_prefill_dual_kernel  4 waves, two work groups per CU (default)
+//    sparse_prefill_pp_kernel    8 waves, ping-pong (selection bitsets too
+//                                large for two groups per CU)
+//    sparse_prefill_kernel       8 waves, one column tile each (fp32, d = 128)
 #include "hs_device.h"
 #include "hs_internal.h"
 
