@@ -8,9 +8,15 @@
 //                         partial (m, l, o) (HySparse explainer 3.4.1; HySparse2
 //                         explainer, decode_one_token: causal_scores(q, K))
 //  decode_combine_kernel  merges the partials into o and LSE
+//  token_*_kernel         token-level selection (HySparse2 explainer,
+//                         decode_one_token): order keys and a level-1
+//                         histogram, a level-2 histogram, candidate compaction,
+//                         the exact pick
 //  decode_sparse_kernel   one sparse layer: the selected blocks of the shared
 //                         cache plus the layer's own window ring, merged by the
 //                         sigmoid gates (explainer 3.4.3)
+//  decode_sparse_token_kernel + decode_token_combine_kernel
+//                         one token-level sparse layer over gathered fp8 rows
 #include <type_traits>
 
 #include "hs_device.h"
@@ -19,7 +25,8 @@
 namespace hs {
 
 // ======================================================== split-K full layer
-// Unit (b, g, ch) covers keys [ch*CH*64, min(L, (ch+1)*CH*64)).  MFMA columns
+// Unit (b, g, ch) covers keys [ch*CH*64, min(L, (ch+1)*CH*64)), CH =
+// ch_blocks (16 or 32 tiles, chosen by the host).  MFMA columns
 // 0..G-1 are the G query heads of kv group g (G <= 16).
 // KV = HS_BF16: key cache [C][D] and block-major value cache [C/64][D][64];
 // KV = HS_FP8_E4M3: position-major fp8 key and value caches [C][D] with one
