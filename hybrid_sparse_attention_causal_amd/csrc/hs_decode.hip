@@ -39,22 +39,50 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
   using Eng = WaveAttn<HS_BF16, D, 1>;
   constexpr int KES = KV == HS_FP8_E4M3 ? 1 : 2;  // cache bytes per element
   const int lane = threadIdx.x & 63;
-  // unit, sequence and length are wave-uniform; saying so keeps the tile loop
-  // a scalar loop
-  const long unit = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (unit >= (long)a.B * a.Hkv * a.nch) return;
-  const int ch = (int)(unit % a.nch);
-  const int bg = (int)(unit / a.nch);
-  const int g = bg % a.Hkv, b = bg / a.Hkv;
-  const int L = __builtin_amdgcn_readfirstlane(a.lens[b]);
   const int span = a.ch_blocks * 64;  // ch_blocks <= kDecodeChunkBlocksMax
+  // Wave id -> live unit: sequence b owns Hkv * ceil(L_b / span) consecutive
+  // ids in (b, g, ch) order, found by a wave prefix over the lengths.  The
+  // grid is sized for full caches; the ids past the live total exit at the
+  // end of the grid.  Numbering only live units keeps consecutive work groups
+  // busy, so the round-robin placement over the XCDs stays even whatever the
+  // length mix (numbering every (b, g, ch) and skipping dead ones leaves the
+  // low XCDs with the long sequences' extra chunks).  Unit, sequence and
+  // length are wave-uniform; saying so keeps the tile loop a scalar loop.
+  const int id = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int b = -1, base = 0, nchb = 1;
+  for (int b0 = 0, carry = 0; b0 < a.B; b0 += 64) {
+    const int bl = b0 + lane;
+    const int cnt = bl < a.B ? a.Hkv * ((ctx_len(a.lens, bl, a.C) + span - 1) / span) : 0;
+    int inc = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(inc, o);
+      if (lane >= o) inc += t;
+    }
+    const int ex = carry + inc - cnt;
+    const unsigned long long hit = __ballot(cnt > 0 && id >= ex && id < ex + cnt);
+    if (hit) {
+      const int src = __builtin_ctzll(hit);
+      b = b0 + src;
+      base = __shfl(ex, src);
+      nchb = __shfl(cnt, src) / a.Hkv;
+      break;
+    }
+    carry += __shfl(inc, 63);
+  }
+  b = __builtin_amdgcn_readfirstlane(b);
+  if (b < 0) return;
+  base = __builtin_amdgcn_readfirstlane(base);
+  nchb = __builtin_amdgcn_readfirstlane(nchb);
+  const int g = (id - base) / nchb, ch = (id - base) % nchb;
+  const int L = __builtin_amdgcn_readfirstlane(ctx_len(a.lens, b, a.C));
   const int kstart = ch * span;
-  if (kstart >= L) return;
   const int kend = min(L, kstart + span);
   const int G = a.Hq / a.Hkv;
   const int col = lane & 15;
-  const int h = g * G + col;
   const int r16 = lane & 15, q8 = 8 * (lane >> 4);
+  const int q4 = (lane >> 4) << 2;
+  const int h = g * G + col;
   const float sk = KV == HS_FP8_E4M3 ? a.kv_scale[g] : 1.f;
   const float sv = KV == HS_FP8_E4M3 ? a.kv_scale[a.Hkv + g] : 1.f;
   const float sc2 = a.sc2 * sk;
@@ -74,7 +102,6 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
   const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * a.C * D * KES;
   const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * a.C * D * KES;
   float* rawrow = a.raw + (size_t)(b * a.Hq + h) * (TOKEN ? a.C : a.C / 64);
-  const int q4 = (lane >> 4) << 2;
 
   // Raw fragments of one tile: bf16: 16 K and 16 V fragments of 16 bytes;
   // fp8: 16 K fragments of 8 bytes and 2x(D/64)x8 value dwords (decoded at
@@ -157,8 +184,10 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
   RawK rk;
   RawV rv;
   // One tile: QK^T on the keys in rk, the keys of tile nx are requested,
-  // softmax, PV with the values in rv, the values of tile nx are requested.
-  auto body = [&](int kb0, int nx) {
+  // softmax, PV with the values in rv, the values of tile nx are requested
+  // (no requests when `more` is false: the last tile).
+  auto body = [&](int kb0, int nx, auto more) {
+    constexpr bool MORE = decltype(more)::value;
     const int j = kb0 >> 6;
     auto ldK = [&](int c, int ks) {
       if constexpr (F8) {
@@ -182,7 +211,7 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
     };
     f32x4 s[1][4];
     eng.qk(ldK, s);
-    loadK(nx, rk);
+    if constexpr (MORE) loadK(nx, rk);
     float bmax[1], bsum[1];
     if (TOKEN) {
       auto hook = [&](int, const float* x) {
@@ -214,26 +243,25 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
       (void)j;
     }
     eng.pv(s, ldV);
-    loadV(nx, rv);
+    if constexpr (MORE) loadV(nx, rv);
   };
-  // Full tiles in a loop whose loads are the same every iteration (the last
-  // full tile reloads itself when nothing follows it: an L2 hit), so the
-  // compiler's waits stay counts instead of drains; a partial last tile
-  // (keys past L) is peeled off below.
+  // Every tile but the last in a loop whose loads are the same every
+  // iteration, so the compiler's waits stay counts instead of drains; the
+  // last tile (the only one that can hold keys past L) is peeled off and
+  // requests nothing.
   const int ntile = (kend - kstart + 63) >> 6;
-  const int nfull = (kend - kstart) >> 6;
   if (ntile > 0) {
     loadK(kstart, rk);
     loadV(kstart, rv);
   }
-  for (int t = 0; t < nfull; ++t) {
+  for (int t = 0; t + 1 < ntile; ++t) {
     const int kb0 = kstart + 64 * t;
-    body(kb0, t + 1 < ntile ? kb0 + 64 : kb0);
+    body(kb0, kb0 + 64, std::true_type{});
   }
-  if (nfull < ntile) {
-    const int kb0 = kstart + 64 * nfull;
+  if (ntile > 0) {
+    const int kb0 = kstart + 64 * (ntile - 1);
     clipV(kb0, rv);
-    body(kb0, kb0);
+    body(kb0, kb0, std::false_type{});
   }
 
   if (!TOKEN && col < G) {
@@ -284,7 +312,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeFullArgs a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const long bh = blockIdx.x;
   const int b = (int)(bh / a.Hq);
-  const int L = a.lens[b];
+  const int L = ctx_len(a.lens, b, a.C);
   const int span = a.ch_blocks * 64;
   const int nchb = L > 0 ? (L + span - 1) / span : 0;
   const float* pp = a.part + (size_t)bh * a.nch * (D + 2);
@@ -344,7 +372,7 @@ __global__ __launch_bounds__(512) void decode_sparse_kernel(DecodeSparseArgs a) 
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int bg = blockIdx.x;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
-  const int L = __builtin_amdgcn_readfirstlane(a.lens[b]);
+  const int L = __builtin_amdgcn_readfirstlane(ctx_len(a.lens, b, a.C));
   const int G = a.Hq / a.Hkv;
   const int col = lane & 15;
   const int h = g * G + col;
@@ -437,15 +465,17 @@ __global__ __launch_bounds__(512) void decode_sparse_kernel(DecodeSparseArgs a) 
     loadK(cur);
     loadV(cur);
   }
-  for (int it = w; it < nitem; it += NW) {
+  // One item: QK^T on rk, the next item's keys are requested, softmax, PV
+  // with rv, the next item's values are requested (none when `more` is
+  // false: this wave's last item).
+  auto step = [&](int it, auto more) {
+    constexpr bool MORE = decltype(more)::value;
     if (!parked && !cur.ring) {  // first selected block: the window branch is complete
       park();
       eng.reset();
       parked = true;
     }
-    // the next item of this wave (or this one again: an L2 hit that keeps
-    // the loads, and so the waits, the same every iteration)
-    const Item nxt = it + NW < nitem ? item(it + NW) : cur;
+    const Item nxt = MORE ? item(it + NW) : cur;
     auto ldK = [&](int c, int ks) {
       Frag f;
       f.u = rk[c][ks];
@@ -460,14 +490,19 @@ __global__ __launch_bounds__(512) void decode_sparse_kernel(DecodeSparseArgs a) 
     };
     f32x4 sx[1][4];
     eng.qk(ldK, sx);
-    loadK(nxt);
+    if constexpr (MORE) loadK(nxt);
     lo[0] = col < G && cur.on ? 0 : kNoKey;
     hi[0] = cur.hi;
     eng.template softmax<true, false>(sx, cur.kbase, lo, hi, a.sc2, bmax, bsum);
     eng.pv(sx, ldV);
-    loadV(nxt);
+    if constexpr (MORE) loadV(nxt);
     cur = nxt;
-  }
+  };
+  // every item but the last in a loop with the same loads each iteration
+  // (the compiler's waits stay counts), the last one peeled off
+  int it = w;
+  for (; it + NW < nitem; it += NW) step(it, std::true_type{});
+  if (it < nitem) step(it, std::false_type{});
   if (!parked) {  // no selected block reached this wave
     park();
     eng.reset();
@@ -539,7 +574,7 @@ __global__ __launch_bounds__(256) void token_keys_kernel(TokenTopkArgs a) {
   __shared__ uint32_t hist[2048];
   const int row = blockIdx.x;
   const int g = row % a.Hkv, b = row / a.Hkv;
-  const int L = a.lens[b];
+  const int L = ctx_len(a.lens, b, a.C);
   const int ncand = max(0, L - a.n_recent);
   const int G = a.Hq / a.Hkv;
   for (int i = threadIdx.x; i < 2048; i += 256) hist[i] = 0u;
@@ -627,7 +662,7 @@ __global__ __launch_bounds__(1024) void token_hist2_kernel(TokenTopkArgs a) {
   __shared__ uint32_t scan[1024];
   __shared__ int res[2];
   const int row = blockIdx.x, t = threadIdx.x;
-  const int L = a.lens[row / a.Hkv];
+  const int L = ctx_len(a.lens, row / a.Hkv, a.C);
   const int ncand = max(0, L - a.n_recent);
   const int s0 = blockIdx.y * kTokSeg;
   if (ncand <= a.kb || s0 >= ncand) return;  // uniform
@@ -662,7 +697,7 @@ __global__ __launch_bounds__(1024) void token_cand_kernel(TokenTopkArgs a) {
   __shared__ int res[2];
   __shared__ uint32_t base_s;
   const int row = blockIdx.x, t = threadIdx.x;
-  const int L = a.lens[row / a.Hkv];
+  const int L = ctx_len(a.lens, row / a.Hkv, a.C);
   const int ncand = max(0, L - a.n_recent);
   const int s0 = blockIdx.y * kTokSeg;
   if (ncand <= a.kb || s0 >= ncand) return;  // uniform
@@ -742,7 +777,7 @@ __global__ __launch_bounds__(1024) void token_select_kernel(TokenTopkArgs a) {
   __shared__ int32_t cand_i[kTokCap];
   const int row = blockIdx.x;
   const int b = row / a.Hkv;
-  const int L = a.lens[b];
+  const int L = ctx_len(a.lens, b, a.C);
   const int ncand = max(0, L - a.n_recent);
   const int nrec = min(L, a.n_recent);
   const int kb = a.kb;
@@ -891,7 +926,7 @@ __global__ __launch_bounds__(512) void decode_sparse_token_kernel(DecodeSparseAr
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int bg = blockIdx.x;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
-  const int L = a.lens[b];
+  const int L = ctx_len(a.lens, b, a.C);
   const int G = a.Hq / a.Hkv;
   const int col = lane & 15;
   const int h = g * G + col;
@@ -1048,7 +1083,7 @@ static void decode_full_dispatch(const DecodeFullArgs& a, dim3 grid, hipStream_t
 }
 
 hipError_t launch_decode_full(const DecodeFullArgs& a, int D, hipStream_t s) {
-  const long units = (long)a.B * a.Hkv * a.nch;
+  const long units = (long)a.B * a.Hkv * a.nch;  // upper bound of the live units
   dim3 grid((unsigned)((units + 3) / 4));
   if (D == 128) decode_full_dispatch<128>(a, grid, s);
   else decode_full_dispatch<64>(a, grid, s);

@@ -27,6 +27,10 @@
 
 namespace hs {
 
+// Context length of sequence b held to [0, C]: a length outside the cache
+// then cannot send a kernel outside its buffers.
+__device__ __forceinline__ int ctx_len(const int32_t* lens, int b, int C) { return min(max(lens[b], 0), C); }
+
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;

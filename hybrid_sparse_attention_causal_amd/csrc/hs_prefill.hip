@@ -323,7 +323,7 @@ __global__ __launch_bounds__(256) void block_topk_kernel(TopkArgs a) {
   const int tr = (int)(row % R);
   const int bg = (int)(row / R);
   const int g = bg % a.Hkv, b = bg / a.Hkv;
-  const int t = a.kv_lens ? a.kv_lens[b] - 1 : tr;
+  const int t = a.kv_lens ? ctx_len(a.kv_lens, b, 64 * a.raw_stride) - 1 : tr;
   const int G = a.Hq / a.Hkv;
   const int nvis = (t >> 6) + 1;
   const int ncand = (t >> 6) + (a.diag ? 1 : 0);

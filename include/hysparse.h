@@ -82,7 +82,9 @@ typedef struct hs_shape {
   int kv_dtype;           /* decode: hs_dtype of the caches; prefill: = dtype  */
   float scale;            /* softmax scale tau; 0 -> 1/sqrt(head_dim)          */
   const int32_t* kv_lens; /* decode: device [batch] context lengths L_b (the
-                             query sits at position L_b-1); NULL = prefill     */
+                             query sits at position L_b-1), 1 <= L_b <= C; the
+                             kernels hold a value outside [0, C] to that range
+                             rather than read past the caches.  NULL = prefill */
   const float* kv_scale;  /* fp8 caches: device [2][hkv] scales (K, V); value
                              = decoded code * scale.  NULL otherwise           */
 } hs_shape;
