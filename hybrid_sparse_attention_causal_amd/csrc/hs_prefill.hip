@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256, (DT == HS_F32 && D == 128) ? 1 : 2) void full_
 // eight waves read the same K/V tile, staged by direct transfers into three
 // named LDS buffers one tile ahead, and waves w / w+4 run half a tile out of
 // phase (A: P(s-1)V | QK(s) | softmax(s), B: softmax(s-1) | P(s-1)V | QK(s)).
-// Block scores are written when a tile's softmax is done.
+// Block scores are staged in LDS and written in runs of SPAN tiles.
 template <int DT, int D, int SCORE_LSE>
 __global__ __launch_bounds__(512, 2) void full_prefill_pp_kernel(FullPrefillArgs a) {
   constexpr int NT = 2;
@@ -178,6 +178,12 @@ __global__ __launch_bounds__(512, 2) void full_prefill_pp_kernel(FullPrefillArgs
   __shared__ __attribute__((aligned(16))) char tile0[St::BYTES];
   __shared__ __attribute__((aligned(16))) char tile1[St::BYTES];
   __shared__ __attribute__((aligned(16))) char tile2[St::BYTES];
+  // block scores of the last SPAN tiles, per wave and column (rows padded by 4
+  // floats: the per-tile writes of 16 columns fall in distinct banks); 16
+  // tiles with head_dim 64, so that two work groups still fit a CU
+  constexpr int SPAN = D >= 128 ? 32 : 16;
+  constexpr int SROW = SPAN + 4;
+  __shared__ __attribute__((aligned(16))) float sbuf[8][NT * 16][SROW];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const bool lag = w >= 4;
@@ -238,14 +244,46 @@ __global__ __launch_bounds__(512, 2) void full_prefill_pp_kernel(FullPrefillArgs
     lo[nt] = 0;
     hi[nt] = hicol[nt];
   }
-  // block scores of tile j, once its softmax is done
+  // Block scores of tile j, once its softmax is done, go to the wave's LDS
+  // rows; every SPAN tiles (and after the last) they are written out as whole
+  // runs of each score row.  One 4-byte store per tile and column left the
+  // rows' lines partly written in L2 for many tiles, and most of them were
+  // evicted and written back several times.
   auto scores = [&](int j, const float* bmax, const float* bsum) {
     if ((lane >> 4) == 0) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         if (hicol[nt] >= 64 * j) {
           const float r = SCORE_LSE ? eng.m[nt] + fast_log2(bsum[nt]) : bmax[nt];
-          a.raw[((size_t)(b * a.Hq + hcol) * T + tcol[nt]) * a.nblk + j] = r * kLn2;
+          sbuf[w][nt * 16 + col][j % SPAN] = r * kLn2;
+        }
+      }
+    }
+  };
+  // tiles j0 = j - j % SPAN .. j are scored: piece e of the NT*16*SPAN/4
+  // float4 pieces takes row e/(SPAN/4) (column tile, column) and tiles
+  // j0 + 4(e%(SPAN/4)) .. +3, those up to the row's last visible tile
+  const bool vec4 = (a.nblk & 3) == 0;
+  constexpr int QR = SPAN / 4;  // float4 pieces per row
+  auto flush = [&](int j) {
+    const int j0 = j - j % SPAN;
+#pragma unroll
+    for (int i = 0; i < NT * 16 * QR / 64; ++i) {
+      const int e = lane + 64 * i;
+      const int r = e / QR, c = r & 15, nt = r >> 4;
+      const int t = tw0 + nt * PT + c / G;
+      const int jj = j0 + 4 * (e % QR);
+      const int jl = live && t < T ? min(t >> 6, j) : -1;
+      if (jj <= jl) {
+        const float4 v = *(const float4*)&sbuf[w][r][4 * (e % QR)];
+        float* dst = a.raw + ((size_t)(b * a.Hq + g * G + c % G) * T + t) * a.nblk + jj;
+        if (vec4 && jj + 3 <= jl) {
+          *(float4*)dst = v;
+        } else {
+          dst[0] = v.x;
+          if (jj + 1 <= jl) dst[1] = v.y;
+          if (jj + 2 <= jl) dst[2] = v.z;
+          if (jj + 3 <= jl) dst[3] = v.w;
         }
       }
     }
@@ -263,6 +301,7 @@ __global__ __launch_bounds__(512, 2) void full_prefill_pp_kernel(FullPrefillArgs
       eng.template softmax<true, SCORE_LSE != 0>(sreg, 64 * (st_i - 1), lo, hi, a.sc2, bmax, bsum, nohook, p_act);
       scores(st_i - 1, bmax, bsum);
     }
+    if (lag && st_i >= 1 && (st_i - 1) % SPAN == SPAN - 1) flush(st_i - 1);
     __builtin_amdgcn_s_setprio(1);
     if (st_i >= 1 && p_act) eng.pv(sreg, ldV);
     if (c_act) {
@@ -274,6 +313,7 @@ __global__ __launch_bounds__(512, 2) void full_prefill_pp_kernel(FullPrefillArgs
       }
     }
     __builtin_amdgcn_s_setprio(0);
+    if (!lag && st_i < nitems && st_i % SPAN == SPAN - 1) flush(st_i);
     p_act = c_act;
     wait_vmem();
     if (st_i + 1 < nitems) st.dma_fix(next);
@@ -286,6 +326,7 @@ __global__ __launch_bounds__(512, 2) void full_prefill_pp_kernel(FullPrefillArgs
     if (st_i + 2 > nitems) break;
     step(st_i + 2, tile1, tile2, tile0);
   }
+  if (nitems > 0 && (nitems - 1) % SPAN != SPAN - 1) flush(nitems - 1);
 
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
