@@ -111,6 +111,20 @@ def test_small_ragged(W, gates):
     check_sequences(run, range(6), gates=gates)
 
 
+def test_many_sequences_unit_numbering():
+    """More than 128 sequences: the full layer numbers its live split-K units
+    with a prefix over the lengths taken 64 sequences at a time, so ids past
+    the first 64 and 128 sequences go through the carried part of the scan."""
+    say("[decode many sequences] B=150 C=2048 Hq=4 Hkv=2 d=64")
+    cfg = gen.config(4, B=150, T=2048, Hq=4, Hkv=2, d=64, kb=4, W=64, N=1, L_lo=1, L_hi=2048)
+    inp = gen.make_decode(cfg)
+    lens = np.random.default_rng(11).integers(1, 2049, size=150).astype(np.int32)
+    lens[[0, 63, 64, 127, 128, 149]] = [2048, 1, 1025, 64, 2047, 1024]
+    inp.lens = lens
+    run = DecodeRun(inp)
+    check_sequences(run, [0, 1, 62, 63, 64, 65, 100, 127, 128, 129, 140, 148, 149])
+
+
 def test_long_capacity_chunks():
     """Capacity above 128K: the full layer's split-K chunks are 32 tiles long."""
     say("[decode capacity 196608] B=2 Hq=8 Hkv=2 d=128")
