@@ -60,8 +60,15 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // Reductions over the four lanes {l, l^16, l^32, l^48} that hold one MFMA
 // column, with the gfx950 row-swap instructions (no LDS traffic).  Every
 // lane of the group gets the same result.
-// max(a, b) for non-NaN a, b as one v_med3_f32 (fmaxf adds NaN quieting)
-__device__ __forceinline__ float max2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
+// max of two floats that are never NaN here (logits, -inf for masked keys):
+// one v_max_f32.  The compiler's own max (maxnum) first quiets both inputs
+// with two more v_max_f32 in IEEE mode when it cannot prove them canonical,
+// as after a cross-lane swap.
+__device__ __forceinline__ float max2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float xlane_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   v = max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -593,7 +600,7 @@ struct WaveAttn {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           x[c][i] = fast_exp2(__builtin_fmaf(x[c][i], sc2, nmn));
-          if (!LSUM || WANT_SUM) ps += x[c][i];
+          if (!LSUM || WANT_SUM) ps = (c | i) ? ps + x[c][i] : x[c][i];  // no 0 + x
         }
       if (!LSUM) l[nt] = l[nt] * alpha + ps;
       if (WANT_SUM) bsum[nt] = xlane_sum(ps);
