@@ -373,18 +373,27 @@ __global__ __launch_bounds__(256) void block_topk_kernel(TopkArgs a) {
   // every load is unconditional (entries past the visible blocks read a
   // clamped slot of the same row and are dropped by a select): loads under a
   // per-lane branch would be waited for one by one
+  // HB heads' rows are requested together (one memory round trip per HB
+  // heads); a batch past the last head re-reads head G-1, which leaves the
+  // maximum unchanged
+  constexpr int HB = MAXI <= 4 ? 4 : (MAXI == 8 ? 2 : 1);
   float x[MAXI];
 #pragma unroll
   for (int i = 0; i < MAXI; ++i) x[i] = -INFINITY;
-  for (int hh = 0; hh < G; ++hh) {
-    const int h = g * G + hh;
-    const float* rp = a.raw + ((size_t)(b * a.Hq + h) * R + tr) * a.raw_stride;
-    const float ls = a.lse[(size_t)(b * a.Hq + h) * R + tr];
-    float v[MAXI];
+  for (int hh0 = 0; hh0 < G; hh0 += HB) {
+    float v[HB][MAXI], ls[HB];
 #pragma unroll
-    for (int i = 0; i < MAXI; ++i) v[i] = rp[min(i * 64 + lane, a.raw_stride - 1)];
+    for (int e = 0; e < HB; ++e) {
+      const int h = g * G + min(hh0 + e, G - 1);
+      const float* rp = a.raw + ((size_t)(b * a.Hq + h) * R + tr) * a.raw_stride;
+      ls[e] = a.lse[(size_t)(b * a.Hq + h) * R + tr];
 #pragma unroll
-    for (int i = 0; i < MAXI; ++i) x[i] = i * 64 + lane < nvis ? fmaxf(x[i], v[i] - ls) : x[i];
+      for (int i = 0; i < MAXI; ++i) v[e][i] = rp[min(i * 64 + lane, a.raw_stride - 1)];
+    }
+#pragma unroll
+    for (int e = 0; e < HB; ++e)
+#pragma unroll
+      for (int i = 0; i < MAXI; ++i) x[i] = i * 64 + lane < nvis ? fmaxf(x[i], v[e][i] - ls[e]) : x[i];
   }
   const size_t orow = (size_t)(b * a.Hkv + g) * R + tr;
   if (a.gs) {
