@@ -503,8 +503,28 @@ struct WaveAttn {
     __device__ __forceinline__ void operator()(int, const float*) const {}
   };
 
+  // Issue order for NR operand fragments read from LDS, each used by NPER
+  // matrix products (plus NTAIL more products at the end): the first LA reads,
+  // then one read after every NPER products, so LA reads stay in flight ahead
+  // of the products that need them.  Left to itself the compiler keeps about
+  // one read in flight and waits for it before every few products.  LA = 0
+  // leaves the order to the compiler (operands already in registers).
+  template <int LA, int NR, int NPER, int NTAIL>
+  __device__ __forceinline__ static void lds_mfma_order() {
+    if constexpr (LA > 0) {
+      __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);  // LDS reads
+#pragma unroll
+      for (int i = 0; i < NR - LA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NPER, 0);  // matrix products
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NPER * LA + NTAIL, 0);
+    }
+  }
+
   // S^T of one 64-key tile: s[nt][c] (rows = keys tile_key(c, 4q+i), column = lane's).
-  template <class LK>
+  // LA > 0: ldK reads LDS, ordered by lds_mfma_order.
+  template <int LA = 0, class LK>
   __device__ __forceinline__ void qk(const LK& ldK, f32x4 (&s)[NT][4]) const {
 #pragma unroll
     for (int ks = 0; ks < NS; ++ks) {
@@ -518,6 +538,7 @@ struct WaveAttn {
         }
       }
     }
+    lds_mfma_order<LA, 4 * NS, NT, 0>();
   }
 
   // Online-softmax update with the logits s of a tile, then O += P V.
@@ -614,7 +635,8 @@ struct WaveAttn {
   }
 
   // O += P V with the P fragments that softmax left in s.
-  template <class LV>
+  // LA > 0: ldV reads LDS, ordered by lds_mfma_order.
+  template <int LA = 0, class LV>
   __device__ __forceinline__ void pv(const f32x4 (&s)[NT][4], const LV& ldV) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -629,6 +651,7 @@ struct WaveAttn {
         for (int nt = 0; nt < NT; ++nt) T::mma(lacc[nt], T::ones(), T::p_frag(s[nt], u));
       }
     }
+    lds_mfma_order<LA, 2 * NM, NT, LSUM ? 2 * NT : 0>();
   }
 
   template <bool MASK, bool WANT_SUM, class LV, class HK = NoHook>
