@@ -111,6 +111,10 @@ SMALL = [
     (257, 2, 2, 64, "f32", 2, 64),
     (333, 32, 4, 128, "bf16", 4, 100),
     (640, 4, 1, 64, "f32", 8, 128),
+    # more than one run of staged block scores, ragged last run (34 blocks:
+    # rows not 16-byte aligned; 35 blocks with head_dim 64: runs of 16)
+    (2113, 8, 2, 128, "bf16", 4, 300),
+    (2200, 4, 1, 64, "bf16", 3, 100),
 ]
 
 
