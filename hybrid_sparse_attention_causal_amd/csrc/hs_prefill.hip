@@ -1139,21 +1139,31 @@ __global__ __launch_bounds__(256, 2) void sparse_prefill_dual_kernel(SparsePrefi
       }
     }
   };
+  // Item i's block and the selection-bitset word of each column tile's
+  // position for it, read one step ahead (the reads are in flight while the
+  // step before computes; window items read an unused word)
+  struct Pre {
+    int j;
+    uint32_t sw[NT];
+  };
+  auto fetch = [&](int i) {
+    Pre p;
+    const bool win = i < nwin;
+    p.j = __builtin_amdgcn_readfirstlane(win ? jw0 + i : ulist[i - nwin]);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) p.sw[nt] = S[(w * PW + pcol[nt]) * nw32 + (win ? 0 : p.j >> 5)];
+    return p;
+  };
   // item i: first key, per-column-tile key range, and the column tiles of
   // this wave that have a live key in it (0: the wave skips the item)
-  auto item = [&](int i, int& kbase, int* lo, int* hi) -> unsigned {
+  auto item = [&](int i, const Pre& p, int& kbase, int* lo, int* hi) -> unsigned {
     const bool win = i < nwin;
-    const int j = win ? jw0 + i : ulist[i - nwin];
-    kbase = 64 * j;
+    kbase = 64 * p.j;
     unsigned act = 0;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      if (win) {
-        lo[nt] = tcol[nt] - a.W + 1;
-      } else {
-        const bool sel = (S[(w * PW + pcol[nt]) * nw32 + (j >> 5)] >> (j & 31)) & 1u;
-        lo[nt] = sel ? 0 : kNoKey;
-      }
+      const bool sel = (p.sw[nt] >> (p.j & 31)) & 1u;
+      lo[nt] = win ? tcol[nt] - a.W + 1 : (sel ? 0 : kNoKey);
       hi[nt] = hicol[nt];
       const bool live_col = max(lo[nt], kbase) <= min(hi[nt], kbase + 63);
       act |= (__ballot(live_col) != 0ull ? 1u : 0u) << nt;
@@ -1173,10 +1183,16 @@ __global__ __launch_bounds__(256, 2) void sparse_prefill_dual_kernel(SparsePrefi
   f32x4 sreg[NT][4];
   float bmax[NT], bsum[NT];
   const typename Eng::NoHook nohook;
+  Pre pre{};
+  if (nitems > 0) pre = fetch(0);
   auto step = [&](int st_i, const char* cur, char* next) {
     int kbase = 0, lo[NT], hi[NT];
-    const unsigned act = item(st_i, kbase, lo, hi);
-    if (st_i + 1 < nitems) issue(st_i + 1, next);
+    const unsigned act = item(st_i, pre, kbase, lo, hi);
+    if (st_i + 1 < nitems) {
+      pre = fetch(st_i + 1);
+      st.dma(next, (st_i + 1 < nwin ? ksg : kg) + (size_t)64 * pre.j * D * ES,
+             (st_i + 1 < nwin ? vsg : vg) + (size_t)pre.j * D * 64 * ES, T - 64 * pre.j);
+    }
     if (st_i == nwin) {  // window branch closed: park it
       fold(gate1, true);
       eng.reset();
