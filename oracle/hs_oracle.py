@@ -44,6 +44,12 @@ design notes):
       older than the newest n_recent, which are always added and do not use
       the k budget; no window branch and no gate.  The group score is the
       same group-wise maximum of post-softmax weights.
+  R10 Sink biases ([P] 4.1, "Experiments Setup": per-head learnable sink
+      biases in the sparse and the window branch, following gpt-oss): each
+      branch's softmax takes one extra logit b_h, in the units of tau q.k,
+      that carries no value, o = sum_j e^{s_j} v_j / (sum_j e^{s_j} + e^{b_h}).
+      Sinks are optional ([2, Hq]: [0] sparse branch, [1] window branch;
+      token mode uses [0]); without them nothing changes.
 """
 from __future__ import annotations
 
@@ -58,23 +64,32 @@ def softmax_scale(d: int) -> float:
     return 1.0 / np.sqrt(d)
 
 
-def _attend(logits: np.ndarray, values: np.ndarray):
+def _attend(logits: np.ndarray, values: np.ndarray, sink=None):
     """Softmax over the last axis of `logits` ([..., n]) applied to values [n, d].
 
     Returns (o [..., d], lse [...]).  An empty key set (n == 0, or every logit
-    -inf) gives o = 0 and lse = -inf (reading R3).
+    -inf) gives o = 0 and lse = -inf (reading R3).  `sink` (broadcast to the
+    leading shape, or None) is one more logit per row with no value (reading
+    R10): it joins the maximum and the denominator, and the lse then
+    includes it.
     """
     lead = logits.shape[:-1]
     d = values.shape[-1]
+    b = None if sink is None else np.broadcast_to(np.asarray(sink, np.float64), lead)[..., None]
     if logits.shape[-1] == 0:
-        return np.zeros((*lead, d)), np.full(lead, -np.inf)
-    m = logits.max(axis=-1, keepdims=True)
+        m = np.full((*lead, 1), -np.inf)
+    else:
+        m = logits.max(axis=-1, keepdims=True)
+    if b is not None:
+        m = np.maximum(m, b)
     finite = np.isfinite(m)
     m_safe = np.where(finite, m, 0.0)
     e = np.exp(logits - m_safe)
     l = e.sum(axis=-1, keepdims=True)
+    if b is not None:
+        l = l + np.exp(b - m_safe)
     l_safe = np.where(l > 0, l, 1.0)
-    o = (e @ values) / l_safe
+    o = (e @ values) / l_safe if logits.shape[-1] else np.zeros((*lead, d))
     lse = np.where(finite & (l > 0), m_safe + np.log(l_safe), -np.inf)[..., 0]
     o = np.where(finite & (l > 0), o, 0.0)
     return o, lse
@@ -189,14 +204,15 @@ def select_with_recent(scores_row: np.ndarray, t: int, k: int, n_recent: int):
 # --------------------------------------------------------------- sparse layer
 def sparse_branch_rows(qs_rows: np.ndarray, pos: np.ndarray, k: np.ndarray,
                        v: np.ndarray, idx: np.ndarray, block: int = BLOCK,
-                       scale: float | None = None) -> np.ndarray:
+                       scale: float | None = None, sink=None) -> np.ndarray:
     """Block-sparse attention branch over the full layer's own K/V.
 
     K~, V~ = concat of the selected blocks (eq. K~,V~ of [X] 3.4.3, "Branch 1");
     o~_t = softmax(tau q'_t . K~) V~ (eq. o~_t).  Keys after t inside a selected
     diagonal block are excluded (causality).  idx [Hkv, R, n_sel] holds block
     ids (or token ids with block=1), -1 = unused; the order of the list does
-    not matter.  Returns o~ [R, Hq, d].
+    not matter.  sink [Hq] or None: the branch's sink logits (R10).
+    Returns o~ [R, Hq, d].
     """
     R, Hq, d = qs_rows.shape
     Hkv = k.shape[0]
@@ -212,15 +228,17 @@ def sparse_branch_rows(qs_rows: np.ndarray, pos: np.ndarray, k: np.ndarray,
             keys = (sel[:, None] * block + np.arange(block)[None, :]).reshape(-1)
             keys = keys[keys <= t]
             s = tau * (qs_rows[r, heads] @ k[g, keys].T)
-            out[r, heads], _ = _attend(s, v[g, keys])
+            out[r, heads], _ = _attend(s, v[g, keys], None if sink is None else sink[heads])
     return out
 
 
 def window_branch_rows(qs_rows: np.ndarray, pos: np.ndarray, ks: np.ndarray,
-                       vs: np.ndarray, W: int, scale: float | None = None) -> np.ndarray:
+                       vs: np.ndarray, W: int, scale: float | None = None,
+                       sink=None) -> np.ndarray:
     """Sliding-window branch with the layer's own K'/V' ([X] 3.4.3 "Branch 2",
     eq. o'_t): keys [t-W+1, t] (reading R6).  W = 0 gives 0.
-    ks, vs [Hkv, >=max(pos)+1, d].  Returns o' [R, Hq, d]."""
+    ks, vs [Hkv, >=max(pos)+1, d]; sink [Hq] or None (R10).
+    Returns o' [R, Hq, d]."""
     R, Hq, d = qs_rows.shape
     Hkv = ks.shape[0]
     G = Hq // Hkv
@@ -233,7 +251,7 @@ def window_branch_rows(qs_rows: np.ndarray, pos: np.ndarray, ks: np.ndarray,
             lo = max(0, t - W + 1)
             keys = np.arange(lo, t + 1) if W > 0 else np.arange(0)
             s = tau * (qs_rows[r, heads] @ ks[g, keys].T)
-            out[r, heads], _ = _attend(s, vs[g, keys])
+            out[r, heads], _ = _attend(s, vs[g, keys], None if sink is None else sink[heads])
     return out
 
 
@@ -271,12 +289,14 @@ def select_rows(raw: np.ndarray, lse: np.ndarray, pos: np.ndarray, Hkv: int, kb:
 
 
 def sparse_layer_rows(qs_rows, pos, k, v, idx, ks, vs, W, gates_rows,
-                      block: int = BLOCK, scale: float | None = None):
+                      block: int = BLOCK, scale: float | None = None, sinks=None):
     """One sparse layer ([X] 3.4.3, [P] 3.1/3.3): block-sparse branch over the
     shared K/V at the inherited indices, window branch over its own K'/V',
-    merged by the sigmoid gates."""
-    o_sp = sparse_branch_rows(qs_rows, pos, k, v, idx, block, scale)
-    o_sw = window_branch_rows(qs_rows, pos, ks, vs, W, scale)
+    merged by the sigmoid gates.  sinks [2, Hq] or None (R10)."""
+    o_sp = sparse_branch_rows(qs_rows, pos, k, v, idx, block, scale,
+                              None if sinks is None else sinks[0])
+    o_sw = window_branch_rows(qs_rows, pos, ks, vs, W, scale,
+                              None if sinks is None else sinks[1])
     return gated_fusion(o_sp, o_sw, gates_rows)
 
 
@@ -296,7 +316,7 @@ def hybrid_block_rows(q, k, v, layers, pos, kb, W, block=BLOCK,
     for lay in layers:
         gates = None if lay.get("gates") is None else lay["gates"][pos]
         outs.append(sparse_layer_rows(lay["q"][pos], pos, k, v, idx, lay["k"], lay["v"],
-                                      W, gates, block, scale))
+                                      W, gates, block, scale, lay.get("sinks")))
     return dict(o=o, lse=lse, raw=raw, Sg=Sg, idx=idx, ranked=ranked, layer_out=outs)
 
 
@@ -365,13 +385,16 @@ def decode_sparse_layer(lay, k, v, L, idx, W, block=BLOCK, kv_scale=None, scale=
     the selected blocks (block=64) or tokens (block=1) of the full layer's
     cache, the window branch over the layer's own ring, the sigmoid gates
     ([X] 3.4.3; [H2] decode_one_token).  idx [Hkv, n] (-1 = unused).
-    Token mode has no window and no gate (reading R9).  Returns o [Hq, d]."""
+    Token mode has no window and no gate (reading R9).  lay["sinks"] [2, Hq]
+    (optional, R10).  Returns o [Hq, d]."""
     if kv_scale is not None:
         k = decode_e4m3fn(k[:, :L]) * kv_scale[0][:, None, None]
         v = decode_e4m3fn(v[:, :L]) * kv_scale[1][:, None, None]
     pos = np.array([L - 1])
     qs = lay["q"][None]
-    o_sp = sparse_branch_rows(qs, pos, k, v, idx[:, None, :], block, scale)
+    sinks = lay.get("sinks")
+    o_sp = sparse_branch_rows(qs, pos, k, v, idx[:, None, :], block, scale,
+                              None if sinks is None else sinks[0])
     if block == 1:
         return o_sp[0]
     if W == 0 or lay.get("k_ring") is None:
@@ -379,6 +402,7 @@ def decode_sparse_layer(lay, k, v, L, idx, W, block=BLOCK, kv_scale=None, scale=
     else:
         kw, vw = window_from_ring(lay["k_ring"], lay["v_ring"], L, W)
         # window keys re-indexed 0..n-1 with the query at n-1
-        o_sw = window_branch_rows(qs, np.array([kw.shape[1] - 1]), kw, vw, W, scale)
+        o_sw = window_branch_rows(qs, np.array([kw.shape[1] - 1]), kw, vw, W, scale,
+                                  None if sinks is None else sinks[1])
     gates = lay.get("gates")
     return gated_fusion(o_sp, o_sw, None if gates is None else gates[None])[0]

@@ -155,6 +155,52 @@ def pin_window(o):
     return ok
 
 
+def pin_sinks(o):
+    """Sink biases (reading R10) against the gpt-oss form built from torch's
+    float64 SDPA: one extra key with zero key and value vectors whose logit
+    is the sink, added through SDPA's additive mask; both branches (the
+    sparse one with every block selected), a -inf sink changing nothing, an
+    empty selection staying 0, and with all logits 0 and equal values
+    o = n v / (n + e^b)."""
+    q, k, v = _rand(T=90, seed=7)
+    T, Hq, d = q.shape
+    Hkv = k.shape[0]
+    G = Hq // Hkv
+    pos = np.arange(T)
+    sink = np.random.default_rng(3).normal(1.0, 1.5, size=Hq)
+    i = np.arange(T)
+
+    def sdpa_sink(allowed):
+        Q = torch.from_numpy(q).permute(1, 0, 2)[None]
+        K = torch.from_numpy(np.concatenate([k, np.zeros((Hkv, 1, d))], 1)).repeat_interleave(G, 0)[None]
+        V = torch.from_numpy(np.concatenate([v, np.zeros((Hkv, 1, d))], 1)).repeat_interleave(G, 0)[None]
+        bias = np.broadcast_to(np.where(allowed, 0.0, -np.inf), (Hq, T, T))
+        col = np.broadcast_to(sink[:, None, None], (Hq, T, 1))
+        mask = torch.from_numpy(np.ascontiguousarray(np.concatenate([bias, col], 2)))[None]
+        out = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask)
+        return out[0].permute(1, 0, 2).numpy()
+
+    ok = True
+    for W in (1, 20, T + 5):
+        band = (i[None, :] <= i[:, None]) & (i[None, :] > i[:, None] - W)
+        got = o.window_branch_rows(q, pos, k, v, W, sink=sink)
+        ok = ok and np.abs(got - sdpa_sink(band)).max() < 1e-12
+    nblk = (T + 63) // 64
+    idx = np.broadcast_to(np.arange(nblk), (Hkv, T, nblk))
+    got = o.sparse_branch_rows(q, pos, k, v, idx, sink=sink)
+    ok = ok and np.abs(got - sdpa_sink(i[None, :] <= i[:, None])).max() < 1e-12
+    off = np.full(Hq, -np.inf)
+    ok = ok and np.array_equal(o.window_branch_rows(q, pos, k, v, 20, sink=off),
+                               o.window_branch_rows(q, pos, k, v, 20))
+    none = np.full((Hkv, T, 2), -1)
+    ok = ok and np.abs(o.sparse_branch_rows(q, pos, k, v, none, sink=sink)).max() == 0.0
+    vconst = np.broadcast_to(np.arange(1.0, d + 1.0), (Hkv, T, d)).copy()
+    got = o.window_branch_rows(np.zeros_like(q[10:]), pos[10:], k, vconst, 5, sink=sink)
+    want = (5.0 / (5.0 + np.exp(sink)))[:, None] * np.arange(1.0, d + 1.0)[None, :]
+    ok = ok and np.abs(got - want[None]).max() < 1e-12
+    return ok
+
+
 def pin_invariants(o):
     """Check (b): softmax rows sum to 1; max_j S = exp(max logit - LSE); LSE
     matches scipy's logsumexp; block masses (score='lse') sum to 1."""
@@ -306,6 +352,10 @@ def test_topk_ties_and_padding():
     assert pin_topk_ties(ora)
 
 
+def test_sinks():
+    assert pin_sinks(ora)
+
+
 def test_gates():
     assert pin_gates()
 
@@ -394,8 +444,8 @@ def _unnormalised_scores(raw, lse):          # forgets the -LSE of the rescale
     return np.exp(raw)
 
 
-def _window_off_by_one(qs, pos, ks, vs, W, scale=None):
-    return _orig_window(qs, pos, ks, vs, W + 1, scale)
+def _window_off_by_one(qs, pos, ks, vs, W, scale=None, sink=None):
+    return _orig_window(qs, pos, ks, vs, W + 1, scale, sink)
 
 
 def _gates_swapped(o_sparse, o_window, g):
@@ -420,10 +470,19 @@ def _fp8_bias8(codes):
     return _orig_fp8(codes) / 2.0
 
 
-def _no_diag_clip(qs_rows, pos, k, v, idx, block=64, scale=None):
-    return _orig_sparse(qs_rows, np.full_like(pos, k.shape[1] - 1), k, v, idx, block, scale)
+def _sink_ignored(logits, values, sink=None):
+    return _orig_attend(logits, values)
 
 
+def _sink_negated(logits, values, sink=None):
+    return _orig_attend(logits, values, None if sink is None else -np.asarray(sink))
+
+
+def _no_diag_clip(qs_rows, pos, k, v, idx, block=64, scale=None, sink=None):
+    return _orig_sparse(qs_rows, np.full_like(pos, k.shape[1] - 1), k, v, idx, block, scale, sink)
+
+
+_orig_attend = ora._attend
 _orig_window = ora.window_branch_rows
 _orig_fusion = ora.gated_fusion
 _orig_full = ora.full_attention_rows
@@ -440,6 +499,8 @@ _orig_sparse = ora.sparse_branch_rows
     ("ties to the higher index", dict(topk_select=_ties_high), [pin_topk_ties]),
     ("fp8 exponent bias", dict(decode_e4m3fn=_fp8_bias8), [pin_fp8]),
     ("diagonal block not clipped", dict(sparse_branch_rows=_no_diag_clip), [pin_dense_reduction]),
+    ("sink ignored", dict(_attend=_sink_ignored), [pin_sinks]),
+    ("sink sign flipped", dict(_attend=_sink_negated), [pin_sinks]),
 ])
 def test_planted_mistakes_fail_their_pins(name, repl, pins):
     with _Mutant(**repl) as m:
