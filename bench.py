@@ -142,7 +142,7 @@ def decode_bytes(inp) -> float:
     return float(full + N * per_layer)
 
 
-def bench_decode(cid: int, steps: int):
+def bench_decode(cid: int, steps: int, sinks: bool = False):
     """Time full decode steps of the 1:11 decode workload (block or token mode)
     on a cold cache; returns a dict for the JSON line."""
     import torch
@@ -183,8 +183,9 @@ def bench_decode(cid: int, steps: int):
     ws_full = torch.empty(max(16, hb.workspace_size(hb.HS_FN_FULL_ATTN, shape, blk)),
                           dtype=torch.uint8, device="cuda")
     layers = []
-    for lay in inp.layers:
-        ent = dict(q=dev(lay["q"]), o=torch.empty_like(o))
+    for li, lay in enumerate(inp.layers):
+        ent = dict(q=dev(lay["q"]), o=torch.empty_like(o),
+                   s=dev(gen.make_sinks(cfg, li)) if sinks else None)
         if not token:
             ent.update(kr=dev(lay["k_ring"]), vr=dev(gen.block_major(lay["v_ring"])),
                        g=dev(lay["gates"]))
@@ -201,10 +202,10 @@ def bench_decode(cid: int, steps: int):
         for l in layers:
             if token:
                 hb.decode_select_attn(l["q"], k, v, lens, idx, nsel, None, None, 0, None, l["o"],
-                                      block=1, kv_scale=scale, stream=stream, ws=ws_sel)
+                                      block=1, kv_scale=scale, stream=stream, ws=ws_sel, sinks=l["s"])
             else:
                 hb.decode_select_attn(l["q"], k, v, lens, idx, nsel, l["kr"], l["vr"], cfg.W, l["g"],
-                                      l["o"], stream=stream)
+                                      l["o"], stream=stream, sinks=l["s"])
 
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     for _ in range(2):
@@ -231,7 +232,7 @@ def bench_decode(cid: int, steps: int):
                          5: "token-level decode, 16 seqs x 262144, fp8 KV, top-2048 + 128 recent"}[cid],
             "ms_per_step_cold": ms, "ms_per_step_warm": warm0.elapsed_time(warm1) / steps,
             "algorithmic_bytes": nbytes, "GB_per_s": nbytes / (ms * 1e-3) / 1e9,
-            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM}
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM, "sinks": bool(sinks)}
 
 
 def main():
@@ -244,6 +245,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode", type=int, nargs="*", default=[4], choices=[4, 5],
                     help="decode workloads also measured (default: 4); pass none to skip")
+    ap.add_argument("--sinks", action="store_true",
+                    help="give every sparse layer per-head sink logits (not part of the workloads)")
     ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -283,8 +286,9 @@ def main():
     dt = hb.HS_BF16 if cfg.dtype == "bf16" else hb.HS_F32
     q, k, vb = dev(inp.q), dev(inp.k), dev(gen.block_major(inp.v))
     layers = [dict(q=dev(l["q"]), k=dev(l["k"]), v=dev(gen.block_major(l["v"])),
-                   g=dev(l["gates"]), o=torch.empty((B, T, Hq, d), dtype=tdt, device="cuda"))
-              for l in inp.layers]
+                   g=dev(l["gates"]), o=torch.empty((B, T, Hq, d), dtype=tdt, device="cuda"),
+                   s=dev(gen.make_sinks(cfg, i)) if args.sinks else None)
+              for i, l in enumerate(inp.layers)]
     o = torch.empty((B, T, Hq, d), dtype=tdt, device="cuda")
     lse = torch.empty((B, Hq, T), device="cuda")
     raw = torch.empty((B, Hq, T, cfg.nblk), device="cuda")
@@ -303,7 +307,7 @@ def main():
         mark(2)
         for i, l in enumerate(layers):
             hb.sparse_attn_fwd(l["q"], k, vb, idx, cfg.kb, l["k"], l["v"], cfg.W, l["g"], l["o"],
-                               stream=stream)
+                               stream=stream, sinks=l["s"])
             mark(3 + i)
 
     for _ in range(args.warmup):
@@ -351,7 +355,8 @@ def main():
                                 1: "tiny 1:3 hybrid block prefill"}[cfg.cid],
                    "batch": B, "seq_len": T, "hq": Hq, "hkv": Hkv, "head_dim": d,
                    "block": 64, "topk_blocks": cfg.kb, "window": cfg.W,
-                   "sparse_layers": len(layers), "parallelism": "single GPU"},
+                   "sparse_layers": len(layers), "sinks": bool(args.sinks),
+                   "parallelism": "single GPU"},
         "block_tflops": total_flops / (ms_step * 1e-3) / 1e12,
         "block_mfma_frac": total_flops / (ms_step * 1e-3) / 1e12 / peak,
         "kernel_ms": per,
@@ -361,7 +366,7 @@ def main():
     if args.decode:
         del layers, q, k, vb, o, lse, raw, idx
         torch.cuda.empty_cache()
-        out["decode"] = [bench_decode(c, max(3, min(args.steps, 10))) for c in args.decode]
+        out["decode"] = [bench_decode(c, max(3, min(args.steps, 10)), args.sinks) for c in args.decode]
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(out), flush=True)

@@ -71,8 +71,8 @@ def load() -> ctypes.CDLL:
     SP = ctypes.POINTER(Shape)
     lib.hs_full_attn_fwd_scores.argtypes = [SP, P, P, P, P, P, P, I, I, P, Z, P]
     lib.hs_block_topk.argtypes = [SP, P, P, I, I, I, I, P, P, P, Z, P]
-    lib.hs_sparse_attn_fwd.argtypes = [SP, P, P, P, P, I, P, P, I, P, P, P]
-    lib.hs_decode_select_attn.argtypes = [SP, P, P, P, P, I, I, P, P, I, P, P, P, Z, P]
+    lib.hs_sparse_attn_fwd.argtypes = [SP, P, P, P, P, I, P, P, I, P, P, P, P]
+    lib.hs_decode_select_attn.argtypes = [SP, P, P, P, P, I, I, P, P, I, P, P, P, P, Z, P]
     lib.hs_workspace_size.argtypes = [I, SP, I, I, I]
     lib.hs_workspace_size.restype = Z
     lib.hs_last_error.restype = ctypes.c_char_p
@@ -142,16 +142,17 @@ def block_topk(q_shape, blk_raw, lse, topk, idx, grp_score=None, include_diag=Fa
 
 
 def sparse_attn_fwd(q_sp, k, v_blk, idx, topk, k_swa, v_swa_blk, window, gate_logits, o,
-                    scale=0.0, stream=None):
+                    scale=0.0, stream=None, sinks=None):
     """One prefill sparse layer.  q_sp/o [B,T,Hq,d]; k [B,Hkv,T,d]; v_blk, v_swa_blk
-    [B,Hkv,nblk,d,64]; idx [B,Hkv,T,topk]; k_swa [B,Hkv,T,d]; gates [B,T,Hq,2] or None."""
-    _contig(q_sp, k, v_blk, idx, k_swa, v_swa_blk, gate_logits, o)
+    [B,Hkv,nblk,d,64]; idx [B,Hkv,T,topk]; k_swa [B,Hkv,T,d]; gates [B,T,Hq,2] or None;
+    sinks [2,Hq] fp32 (sparse, window branch) or None."""
+    _contig(q_sp, k, v_blk, idx, k_swa, v_swa_blk, gate_logits, sinks, o)
     B, T, Hq, d = q_sp.shape
     Hkv = (k if k is not None else k_swa).shape[1]
     s = make_shape(B, T, T, Hq, Hkv, d, dtype_code(q_sp), scale=scale)
     _check(load().hs_sparse_attn_fwd(ctypes.byref(s), _ptr(q_sp), _ptr(k), _ptr(v_blk),
                                      _ptr(idx), topk, _ptr(k_swa), _ptr(v_swa_blk), window,
-                                     _ptr(gate_logits), _ptr(o), _stream(stream)))
+                                     _ptr(gate_logits), _ptr(sinks), _ptr(o), _stream(stream)))
 
 
 # ------------------------------------------------------------------- decode
@@ -195,18 +196,19 @@ def decode_block_topk(q, k, lens, raw, lse, topk, idx, grp_score=None, block=64,
 
 
 def decode_select_attn(q_sp, k, v, lens, idx, n_sel, k_ring, v_ring, window, gate_logits, o,
-                       block=64, kv_scale=None, scale=0.0, stream=None, ws=None):
+                       block=64, kv_scale=None, scale=0.0, stream=None, ws=None, sinks=None):
     """One decode sparse layer.  q_sp/o [B,Hq,d]; idx [B,Hkv,n_sel];
-    k_ring [B,Hkv,W,d]; v_ring [B,Hkv,ceil(W/64),d,64]; gates [B,Hq,2] or None.
+    k_ring [B,Hkv,W,d]; v_ring [B,Hkv,ceil(W/64),d,64]; gates [B,Hq,2] or None;
+    sinks [2,Hq] fp32 or None (token mode uses row 0).
     ws: uint8 device workspace (allocated here when None and one is needed)."""
-    _contig(q_sp, k, v, lens, idx, k_ring, v_ring, gate_logits, o)
+    _contig(q_sp, k, v, lens, idx, k_ring, v_ring, gate_logits, sinks, o)
     s = decode_shape(q_sp, k, lens, kv_scale, scale)
     if ws is None:
         need = workspace_size(HS_FN_DECODE_SELECT, s, block)
         ws = torch.empty(need, dtype=torch.uint8, device=q_sp.device) if need else None
     _check(load().hs_decode_select_attn(ctypes.byref(s), _ptr(q_sp), _ptr(k), _ptr(v), _ptr(idx),
                                         n_sel, block, _ptr(k_ring), _ptr(v_ring), window,
-                                        _ptr(gate_logits), _ptr(o), _ptr(ws),
+                                        _ptr(gate_logits), _ptr(sinks), _ptr(o), _ptr(ws),
                                         0 if ws is None else ws.numel(), _stream(stream)))
     return ws
 

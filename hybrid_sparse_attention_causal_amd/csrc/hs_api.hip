@@ -315,7 +315,8 @@ hs_status hs_block_topk(const hs_shape* s, const float* blk_raw, const float* ls
 
 hs_status hs_sparse_attn_fwd(const hs_shape* s, const void* q_sp, const void* k, const void* v,
                              const int32_t* idx, int topk, const void* k_swa, const void* v_swa,
-                             int window, const float* gate_logits, void* o, void* stream) {
+                             int window, const float* gate_logits, const float* sinks, void* o,
+                             void* stream) {
   const char* fn = "hs_sparse_attn_fwd";
   hs_status st = check_prefill(fn, s);
   if (st) return st;
@@ -346,6 +347,7 @@ hs_status hs_sparse_attn_fwd(const hs_shape* s, const void* q_sp, const void* k,
   a.ks = k_swa;
   a.vs = v_swa;
   a.gates = gate_logits;
+  a.sinks = sinks;
   a.o = o;
   a.B = s->batch;
   a.T = s->q_len;
@@ -360,8 +362,9 @@ hs_status hs_sparse_attn_fwd(const hs_shape* s, const void* q_sp, const void* k,
 
 hs_status hs_decode_select_attn(const hs_shape* s, const void* q_sp, const void* k, const void* v,
                                 const int32_t* idx, int n_sel, int block, const void* k_ring,
-                                const void* v_ring, int window, const float* gate_logits, void* o,
-                                void* ws, size_t ws_bytes, void* stream) {
+                                const void* v_ring, int window, const float* gate_logits,
+                                const float* sinks, void* o, void* ws, size_t ws_bytes,
+                                void* stream) {
   const char* fn = "hs_decode_select_attn";
   hs_status st = check_decode(fn, s);
   if (st) return st;
@@ -393,6 +396,7 @@ hs_status hs_decode_select_attn(const hs_shape* s, const void* q_sp, const void*
   a.kr = k_ring;
   a.vr = v_ring;
   a.gates = gate_logits;
+  a.sinks = sinks;
   a.o = o;
   a.lens = s->kv_lens;
   a.B = s->batch;

@@ -520,10 +520,12 @@ __global__ __launch_bounds__(512) void decode_sparse_kernel(DecodeSparseArgs a) 
       const int el = threadIdx.x + 64 * NW * i;
       const int c = el / D, d = el % D;
       if (c < G) {
-        float M = kNegBig;
+        // the branch's sink logit (log2 units) joins the maximum and the sum
+        const float sk = a.sinks ? a.sinks[br * a.Hq + g * G + c] * kLog2e : -INFINITY;
+        float M = fmaxf(kNegBig, sk);
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww][c]);
-        float ls = 0.f, os = 0.f;
+        float ls = fast_exp2(sk - M), os = 0.f;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) {
           const float wt = fast_exp2(sm_m[ww][c] - M);
@@ -1010,10 +1012,13 @@ __global__ __launch_bounds__(512) void decode_sparse_token_kernel(DecodeSparseAr
   __syncthreads();
   for (int el = threadIdx.x; el < G * D; el += 64 * NW) {
     const int c = el / D, d = el % D;
-    float M = kNegBig;
+    // the sparse-branch sink joins here when this group writes o itself; the
+    // merge kernel adds it to split partials
+    const float sk = a.sinks && gridDim.y == 1 ? a.sinks[g * G + c] * kLog2e : -INFINITY;
+    float M = fmaxf(kNegBig, sk);
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww][c]);
-    float ls = 0.f, os = 0.f;
+    float ls = fast_exp2(sk - M), os = 0.f;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
       const float wt = fast_exp2(sm_m[ww][c] - M);
@@ -1056,10 +1061,11 @@ __global__ __launch_bounds__(1024) void decode_token_combine_kernel(DecodeSparse
       l[sp] = in ? pp[sp * st + D + 1] : 0.f;
       x[sp] = in ? pp[sp * st + d] : 0.f;
     }
-    float M = kNegBig;
+    const float sk = a.sinks ? a.sinks[g * G + c] * kLog2e : -INFINITY;  // sparse-branch sink
+    float M = fmaxf(kNegBig, sk);
 #pragma unroll
     for (int sp = 0; sp < kTokSplitMax; ++sp) M = fmaxf(M, m[sp]);
-    float ls = 0.f, os = 0.f;
+    float ls = fast_exp2(sk - M), os = 0.f;
 #pragma unroll
     for (int sp = 0; sp < kTokSplitMax; ++sp) {
       const float wt = fast_exp2(m[sp] - M);

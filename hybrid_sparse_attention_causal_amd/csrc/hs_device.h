@@ -680,10 +680,19 @@ struct WaveAttn {
   }
 
   // Column totals: 1/l (0 when the column saw no key) and the log2-domain LSE.
-  __device__ __forceinline__ void finish(int nt, float& inv_l, float& lse2) const {
-    const float lt = LSUM ? lacc[nt][0] : xlane_sum(l[nt]);
-    inv_l = lt > 0.f ? 1.f / lt : 0.f;
-    lse2 = lt > 0.f ? m[nt] + fast_log2(lt) : -INFINITY;
+  // sink2: an extra logit with no value (log2 units; -inf: none) joins the
+  // maximum and the denominator, so inv_l also carries the o rescale.
+  __device__ __forceinline__ void finish(int nt, float& inv_l, float& lse2, float sink2 = -INFINITY) const {
+    float lt = LSUM ? lacc[nt][0] : xlane_sum(l[nt]);
+    float mm = m[nt], sc = 1.f;
+    if (sink2 > -INFINITY) {
+      const float M = fmaxf(mm, sink2);
+      sc = fast_exp2(mm - M);
+      lt = lt * sc + fast_exp2(sink2 - M);
+      mm = M;
+    }
+    inv_l = lt > 0.f ? sc / lt : 0.f;
+    lse2 = lt > 0.f ? mm + fast_log2(lt) : -INFINITY;
   }
 };
 

@@ -39,6 +39,7 @@ struct SparsePrefillArgs {
   const void* ks;
   const void* vs;
   const float* gates;
+  const float* sinks;  // [2][Hq] sink logits (sparse, window branch) or NULL
   void* o;
   int B, T, Hq, Hkv, nblk, topk, W;
   int nwg;  // work groups (kv groups x position blocks)
@@ -79,6 +80,7 @@ struct DecodeSparseArgs {
   const void* kr;
   const void* vr;
   const float* gates;
+  const float* sinks;     // [2][Hq] sink logits (sparse, window branch) or NULL
   void* o;
   const int32_t* lens;
   const float* kv_scale;  // fp8 token mode: device [2][Hkv]

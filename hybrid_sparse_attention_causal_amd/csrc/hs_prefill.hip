@@ -594,11 +594,19 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_prefill_kernel(SparsePrefil
       gate1[nt] = 1.f / (1.f + expf(-gl.y));
     }
   }
-  auto fold = [&](const float* gate, bool first) {
+  // per-head sink logits of the sparse (0) and window (1) branch, log2
+  // units; -inf without sinks
+  float sink0[NT], sink1[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    sink0[nt] = a.sinks ? a.sinks[hcol[nt]] * kLog2e : -INFINITY;
+    sink1[nt] = a.sinks ? a.sinks[a.Hq + hcol[nt]] * kLog2e : -INFINITY;
+  }
+  auto fold = [&](const float* gate, const float* sink, bool first) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float inv, l2;
-      eng.finish(nt, inv, l2);
+      eng.finish(nt, inv, l2, sink[nt]);
       const float sc = inv * gate[nt];
 #pragma unroll
       for (int mc = 0; mc < Eng::NM; ++mc)
@@ -650,7 +658,7 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_prefill_kernel(SparsePrefil
     __syncthreads();
     auto step = [&](int i, St& ld_into, St& store_from) {
       if (i == nu) {
-        fold(gate0, true);
+        fold(gate0, sink0, true);
         eng.reset();
       }
       if (i + 2 < nitems) issue(ld_into, i + 2);
@@ -671,7 +679,7 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_prefill_kernel(SparsePrefil
     __syncthreads();
     for (int i = 0; i < nitems; ++i) {
       if (i == nu) {
-        fold(gate0, true);
+        fold(gate0, sink0, true);
         eng.reset();
       }
       if (i + 1 < nitems) issue(st, i + 1);
@@ -681,9 +689,9 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_prefill_kernel(SparsePrefil
     }
   }
   if (nu == nitems) {  // no window tiles: the sparse branch is still open
-    fold(gate0, true);
+    fold(gate0, sink0, true);
   } else {
-    fold(gate1, false);
+    fold(gate1, sink1, false);
   }
 
 #pragma unroll
@@ -786,6 +794,14 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
       gate1[nt] = 1.f / (1.f + expf(-gl.y));
     }
   }
+  // per-head sink logits of the sparse (0) and window (1) branch, log2
+  // units; -inf without sinks
+  float sink0[NT], sink1[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    sink0[nt] = a.sinks ? a.sinks[hcol] * kLog2e : -INFINITY;
+    sink1[nt] = a.sinks ? a.sinks[a.Hq + hcol] * kLog2e : -INFINITY;
+  }
   const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * T * D * ES;
   const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
   const char* ksg = (const char*)a.ks + (size_t)(b * a.Hkv + g) * T * D * ES;
@@ -858,11 +874,11 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
   // Close a branch.  The first branch's gated output is parked in the output
   // rows themselves (in the output dtype) while the second branch runs and is
   // added back when that one closes: no registers hold it in between.
-  auto fold = [&](const float* gate, bool first) {
+  auto fold = [&](const float* gate, const float* sink, bool first) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float inv, l2;
-      eng.finish(nt, inv, l2);
+      eng.finish(nt, inv, l2, sink[nt]);
       const float sc = inv * gate[nt];
       if (live && tcol[nt] < T) {
         char* op = (char*)a.o + (((size_t)(b * T + tcol[nt]) * a.Hq + hcol) * D + 4 * (lane >> 4)) * ES;
@@ -930,7 +946,7 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
     if (st_i >= 1 && p_act) eng.pv(sreg, ldV);
     if (st_i < nitems) {
       if (st_i == nwin) {  // window branch closed: park it
-        fold(gate1, true);
+        fold(gate1, sink1, true);
         eng.reset();
       }
       if (c_act) {
@@ -960,9 +976,9 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
     step(st_i + 2, tile1, tile2, tile0);
   }
   if (nwin == nitems) {
-    fold(gate1, true);
+    fold(gate1, sink1, true);
   } else {
-    fold(gate0, false);
+    fold(gate0, sink0, false);
   }
 }
 
@@ -1050,6 +1066,14 @@ __global__ __launch_bounds__(256, 2) void sparse_prefill_dual_kernel(SparsePrefi
       gate1[nt] = 1.f / (1.f + expf(-gl.y));
     }
   }
+  // per-head sink logits of the sparse (0) and window (1) branch, log2
+  // units; -inf without sinks
+  float sink0[NT], sink1[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    sink0[nt] = a.sinks ? a.sinks[hcol] * kLog2e : -INFINITY;
+    sink1[nt] = a.sinks ? a.sinks[a.Hq + hcol] * kLog2e : -INFINITY;
+  }
   const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * T * D * ES;
   const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
   const char* ksg = (const char*)a.ks + (size_t)(b * a.Hkv + g) * T * D * ES;
@@ -1122,11 +1146,11 @@ __global__ __launch_bounds__(256, 2) void sparse_prefill_dual_kernel(SparsePrefi
   // Close a branch.  The first branch's gated output is parked in the output
   // rows themselves (in the output dtype) while the second branch runs and is
   // added back when that one closes: no registers hold it in between.
-  auto fold = [&](const float* gate, bool first) {
+  auto fold = [&](const float* gate, const float* sink, bool first) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float inv, l2;
-      eng.finish(nt, inv, l2);
+      eng.finish(nt, inv, l2, sink[nt]);
       const float sc = inv * gate[nt];
       if (live && tcol[nt] < T) {
         char* op = (char*)a.o + (((size_t)(b * T + tcol[nt]) * a.Hq + hcol) * D + 4 * (lane >> 4)) * ES;
@@ -1194,7 +1218,7 @@ __global__ __launch_bounds__(256, 2) void sparse_prefill_dual_kernel(SparsePrefi
              (st_i + 1 < nwin ? vsg : vg) + (size_t)pre.j * D * 64 * ES, T - 64 * pre.j);
     }
     if (st_i == nwin) {  // window branch closed: park it
-      fold(gate1, true);
+      fold(gate1, sink1, true);
       eng.reset();
     }
     if (act) {
@@ -1214,9 +1238,9 @@ __global__ __launch_bounds__(256, 2) void sparse_prefill_dual_kernel(SparsePrefi
     step(st_i + 1, tile1, tile0);
   }
   if (nwin == nitems) {
-    fold(gate1, true);
+    fold(gate1, sink1, true);
   } else {
-    fold(gate0, false);
+    fold(gate0, sink0, false);
   }
 }
 

@@ -30,7 +30,12 @@ Storage formats: 'f32' -> float32 arrays, 'bf16' -> uint16 bit patterns (RNE),
 Random streams: numpy default_rng([seed, stream, *slab]) where seed is the
 configuration number, so any slab (one sequence, one kv head) can be
 regenerated on its own; stream ids: 0 Q, 1 K, 2 V, 3 c, 4 salient positions,
-5 sequence lengths, 10+l Q'_l, 30+l K'_l, 50+l V'_l, 70+l gates_l.
+5 sequence lengths, 10+l Q'_l, 30+l K'_l, 50+l V'_l, 70+l gates_l,
+90+l sinks_l.
+
+Sink logits (optional, not part of the five workloads): per layer, [2][Hq]
+float32 ~ N(2, 1.5^2), row 0 for the sparse and row 1 for the window branch,
+so that they sit near the typical largest logit and matter.
 """
 from __future__ import annotations
 
@@ -326,6 +331,12 @@ def _fp8_scales(cfg: Config, c: np.ndarray, lens: np.ndarray) -> np.ndarray:
             amax[0, g] = max(amax[0, g], ka)
             amax[1, g] = max(amax[1, g], va)
     return (amax / 448.0).astype(np.float32)
+
+
+def make_sinks(cfg: Config, layer: int = 0) -> np.ndarray:
+    """Sink logits [2, Hq] float32 of sparse layer `layer` (stream 90+layer)."""
+    r = _rng(cfg, 90 + layer)
+    return (2.0 + 1.5 * r.standard_normal((2, cfg.Hq))).astype(np.float32)
 
 
 def make_decode(cfg: Config, n_layers: int | None = None) -> DecodeInputs:

@@ -161,14 +161,20 @@ hs_status hs_block_topk(const hs_shape* shape, const float* blk_raw, const float
  *         the layer's own window cache (NULL together with window == 0)
  *   window   W >= 0: keys t-W+1 .. t of k_swa/v_swa
  *   gate_logits [batch][T][hq][2] fp32 (sparse, window) or NULL (both gates 1)
+ *   sinks [2][hq] fp32 device per-head sink logits (row 0: sparse branch,
+ *         row 1: window branch), in the units of tau q.k, or NULL (none)
  *   o     [batch][T][hq][head_dim] (out)
  * o_t = sigmoid(G0) o~_t + sigmoid(G1) o'_t; an empty selection gives o~ = 0.
- * Keys after t inside a selected block are excluded.
+ * Keys after t inside a selected block are excluded.  Sinks (paper 4.1,
+ * "Experiments Setup": per-head learnable sink biases in both branches,
+ * following gpt-oss): each branch's softmax takes one more logit b_h that
+ * carries no value, o = sum_j e^{s_j} v_j / (sum_j e^{s_j} + e^{b_h}).
  */
 hs_status hs_sparse_attn_fwd(const hs_shape* shape, const void* q_sp, const void* k,
                              const void* v, const int32_t* idx, int topk,
                              const void* k_swa, const void* v_swa, int window,
-                             const float* gate_logits, void* o, void* stream);
+                             const float* gate_logits, const float* sinks, void* o,
+                             void* stream);
 
 /*
  * One sparse layer at decode time, one query per sequence (explainer 3.4.3;
@@ -178,7 +184,8 @@ hs_status hs_sparse_attn_fwd(const hs_shape* shape, const void* q_sp, const void
  *   hs_block_topk (block ids for block = 64, token ids for block = 1).
  *   k_ring, v_ring: the layer's own window ring [batch][hkv][W][head_dim]
  *   and [batch][hkv][ceil(W/64)][head_dim][64] (slot = position mod W), or
- *   NULL with window == 0.  gate_logits [batch][hq][2] or NULL.
+ *   NULL with window == 0.  gate_logits [batch][hq][2] or NULL.  sinks
+ *   [2][hq] or NULL, as in hs_sparse_attn_fwd (token mode uses row 0).
  *   o [batch][hq][head_dim] (out).
  * Token mode (block = 1, fp8 caches as in hs_full_attn_fwd_scores) has no
  * window branch and no gate (the newest tokens are part of idx).  Block mode
@@ -191,8 +198,8 @@ hs_status hs_sparse_attn_fwd(const hs_shape* shape, const void* q_sp, const void
 hs_status hs_decode_select_attn(const hs_shape* shape, const void* q_sp, const void* k,
                                 const void* v, const int32_t* idx, int n_sel, int block,
                                 const void* k_ring, const void* v_ring, int window,
-                                const float* gate_logits, void* o, void* ws,
-                                size_t ws_bytes, void* stream);
+                                const float* gate_logits, const float* sinks, void* o,
+                                void* ws, size_t ws_bytes, void* stream);
 
 /* Function ids for hs_workspace_size */
 #define HS_FN_FULL_ATTN 0

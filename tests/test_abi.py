@@ -98,6 +98,6 @@ def test_topk_and_sparse_validation():
     assert lib.hs_block_topk(ctypes.byref(s), None, FAKE, 64, 4, 0, 0, None, FAKE, None, 0,
                              None) == hb.HS_ERR_INVALID_ARG
     assert lib.hs_sparse_attn_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 4, None, None, 16,
-                                  None, FAKE, None) == hb.HS_ERR_INVALID_ARG   # window w/o cache
+                                  None, None, FAKE, None) == hb.HS_ERR_INVALID_ARG   # window w/o cache
     assert lib.hs_sparse_attn_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, -1, None, None, 0,
-                                  None, FAKE, None) == hb.HS_ERR_INVALID_ARG
+                                  None, None, FAKE, None) == hb.HS_ERR_INVALID_ARG

@@ -22,7 +22,7 @@ def say(*a):
 
 
 class DecodeRun:
-    def __init__(self, inp, n_layers=None, gates=True, W=None):
+    def __init__(self, inp, n_layers=None, gates=True, W=None, sinks=False):
         cfg = inp.cfg
         self.cfg, self.inp = cfg, inp
         B, Hq, Hkv, C, d = cfg.B, cfg.Hq, cfg.Hkv, cfg.T, cfg.d
@@ -43,13 +43,15 @@ class DecodeRun:
         hb.decode_block_topk(q, self.k, self.lens, self.raw, self.lse, cfg.kb, self.idx, self.gs)
         self.outs = []
         layers = inp.layers if n_layers is None else inp.layers[:n_layers]
-        for lay in layers:
+        self.sinks = [gen.make_sinks(cfg, l) if sinks else None for l in range(len(layers))]
+        for l, lay in enumerate(layers):
             o = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
             kr = dev(lay["k_ring"]) if self.W else None
             vr = dev(gen.block_major(lay["v_ring"])) if self.W else None
             g = dev(lay["gates"]) if gates else None
+            sk = None if self.sinks[l] is None else dev(self.sinks[l])
             hb.decode_select_attn(dev(lay["q"]), self.k, self.v, self.lens, self.idx, cfg.kb,
-                                  kr, vr, self.W, g, o)
+                                  kr, vr, self.W, g, o, sinks=sk)
             self.outs.append(o)
         torch.cuda.synchronize()
 
@@ -71,11 +73,12 @@ def check_sequences(run, seqs, gates=True):
         ks, vs = zip(*(inp.kv_slab_f64(b, g) for g in range(cfg.Hkv)))
         k, v = np.stack(ks), np.stack(vs)
         layers = []
-        for lay in inp.layers[: len(run.outs)]:
+        for l, lay in enumerate(inp.layers[: len(run.outs)]):
             layers.append(dict(q=f64_bf16(lay["q"][b]),
                                k_ring=f64_bf16(lay["k_ring"][b]) if run.W else None,
                                v_ring=f64_bf16(lay["v_ring"][b]) if run.W else None,
-                               gates=lay["gates"][b].astype(np.float64) if gates else None))
+                               gates=lay["gates"][b].astype(np.float64) if gates else None,
+                               sinks=None if run.sinks[l] is None else run.sinks[l].astype(np.float64)))
         ref = ora.decode_step(f64_bf16(inp.q[b]), k, v, L, [], cfg.kb, run.W)
         nb = (L - 1) // 64 + 1
         worst["o"] = max(worst["o"], np.abs(o_g[b] - ref["o"]).max())
@@ -101,13 +104,14 @@ def check_sequences(run, seqs, gates=True):
     assert not np.isnan(o_g).any() and all(not np.isnan(x).any() for x in outs_g)
 
 
-@pytest.mark.parametrize("W,gates", [(100, True), (64, False), (0, True), (300, True)])
-def test_small_ragged(W, gates):
-    say(f"[decode small] W={W} gates={gates}")
+@pytest.mark.parametrize("W,gates,sinks", [(100, True, False), (64, False, False), (0, True, False),
+                                           (300, True, False), (100, True, True), (0, False, True)])
+def test_small_ragged(W, gates, sinks):
+    say(f"[decode small] W={W} gates={gates} sinks={sinks}")
     cfg = gen.config(4, B=6, T=1024, Hq=8, Hkv=2, d=128, kb=3, W=W, N=2, L_lo=1, L_hi=1024)
     inp = gen.make_decode(cfg)
     inp.lens = np.array([1, 63, 64, 65, 700, 1024], np.int32)
-    run = DecodeRun(inp, gates=gates)
+    run = DecodeRun(inp, gates=gates, sinks=sinks)
     check_sequences(run, range(6), gates=gates)
 
 
@@ -155,7 +159,7 @@ class TokenRun:
     """Token-level decode (fp8 e4m3 caches, position-major): full layer with
     per-token logits, top-k tokens + the newest n_recent, sparse layers."""
 
-    def __init__(self, inp, n_layers=None):
+    def __init__(self, inp, n_layers=None, sinks=False, ws=None):
         cfg = inp.cfg
         self.cfg, self.inp = cfg, inp
         B, Hq, Hkv, C, d = cfg.B, cfg.Hq, cfg.Hkv, cfg.T, cfg.d
@@ -178,10 +182,14 @@ class TokenRun:
         hb.decode_block_topk(q, self.k, self.lens, self.raw, self.lse, kb, self.idx, self.gs,
                              block=1, n_recent=R, kv_scale=self.scale)
         self.outs = []
-        for lay in (inp.layers if n_layers is None else inp.layers[:n_layers]):
+        layers = inp.layers if n_layers is None else inp.layers[:n_layers]
+        self.sinks = [gen.make_sinks(cfg, l) if sinks else None for l in range(len(layers))]
+        for l, lay in enumerate(layers):
             o = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+            sk = None if self.sinks[l] is None else dev(self.sinks[l])
             hb.decode_select_attn(dev(lay["q"]), self.k, self.v, self.lens, self.idx, kb + R,
-                                  None, None, 0, None, o, block=1, kv_scale=self.scale)
+                                  None, None, 0, None, o, block=1, kv_scale=self.scale,
+                                  sinks=sk, ws=ws)
             self.outs.append(o)
         torch.cuda.synchronize()
 
@@ -226,7 +234,8 @@ def check_token_sequences(run, seqs, rel=1e-4):
                     continue
             assert np.array_equal(row[:n_out], want[:n_out]), (b, g)
         for l in range(len(run.outs)):
-            lay = dict(q=f64_bf16(inp.layers[l]["q"][b]))
+            lay = dict(q=f64_bf16(inp.layers[l]["q"][b]),
+                       sinks=None if run.sinks[l] is None else run.sinks[l].astype(np.float64))
             want = ora.decode_sparse_layer(lay, k, v, L, idx_g[b].astype(np.int64), 0, block=1,
                                            kv_scale=inp.kv_scale.astype(np.float64))
             worst["layer"] = max(worst["layer"], np.abs(outs_g[l][b] - want).max())
@@ -246,6 +255,20 @@ def test_token_small_ragged():
     inp = gen.make_decode(cfg)
     inp.lens = np.array([1, 200, 300, 4096], np.int32)
     run = TokenRun(inp)
+    check_token_sequences(run, range(4))
+
+
+@pytest.mark.parametrize("split", [True, False])
+def test_token_sinks(split):
+    """Sink logits in the token-mode sparse layer, added by the merge kernel
+    (split work groups) or by the one group per (sequence, kv head)."""
+    say(f"[token sinks] split={split}")
+    cfg = gen.config(5, B=4, T=8192, Hq=8, Hkv=2, d=128, kb=700, n_recent=64, N=2,
+                     L_lo=1, L_hi=8192)
+    inp = gen.make_decode(cfg)
+    inp.lens = np.array([5, 1000, 6000, 8192], np.int32)
+    ws = None if split else torch.empty(16, dtype=torch.uint8, device="cuda")
+    run = TokenRun(inp, sinks=True, ws=ws)
     check_token_sequences(run, range(4))
 
 

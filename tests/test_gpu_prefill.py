@@ -30,7 +30,7 @@ class Run:
     """One prefill hybrid block on the GPU, with its buffers."""
 
     def __init__(self, inp, score=hb.HS_SCORE_MAX, include_diag=False, kb=None, W=None,
-                 gates=True):
+                 gates=True, sinks=False):
         cfg = inp.cfg
         self.cfg, self.inp = cfg, inp
         B, T, Hq, Hkv, d = cfg.B, cfg.T, cfg.Hq, cfg.Hkv, cfg.d
@@ -50,13 +50,15 @@ class Run:
         hb.block_topk((B, T, Hq, Hkv, d, dt), self.raw, self.lse, self.kb, self.idx, self.gs,
                       include_diag=include_diag)
         self.outs = []
-        for lay in inp.layers:
+        self.sinks = [gen.make_sinks(cfg, l) if sinks else None for l in range(len(inp.layers))]
+        for l, lay in enumerate(inp.layers):
             qs, ks = dev(lay["q"], cfg.dtype), dev(lay["k"], cfg.dtype)
             vsb = dev(gen.block_major(lay["v"]), cfg.dtype)
             g = dev(lay["gates"]) if gates else None
             o = torch.full((B, T, Hq, d), float("nan"), dtype=tdt, device="cuda")
+            sk = None if self.sinks[l] is None else dev(self.sinks[l])
             hb.sparse_attn_fwd(qs, k, vb, self.idx, self.kb, ks if self.W else None,
-                               vsb if self.W else None, self.W, g, o)
+                               vsb if self.W else None, self.W, g, o, sinks=sk)
             self.outs.append(o)
         torch.cuda.synchronize()
 
@@ -93,8 +95,9 @@ def check_run(run, pos, score="max", include_diag=False, gates=True, layers=None
     k64, v64 = inp.f64("k")[b], inp.f64("v")[b]
     for l in range(len(inp.layers)) if layers is None else layers:
         gl = inp.f64("gates", l)[b][pos] if gates else None
+        sk = None if run.sinks[l] is None else run.sinks[l].astype(np.float64)
         want = ora.sparse_layer_rows(inp.f64("q", l)[b][pos], pos, k64, v64, gidx,
-                                     inp.f64("k", l)[b], inp.f64("v", l)[b], run.W, gl)
+                                     inp.f64("k", l)[b], inp.f64("v", l)[b], run.W, gl, sinks=sk)
         got = host(run.outs[l])[b][pos]
         err = np.abs(got - want).max()
         say(f"  sparse layer {l}: max|dO|={err:.3g}")
@@ -125,6 +128,31 @@ def test_small_shapes_all_rows(T, Hq, Hkv, d, dtype, kb, W):
     inp = gen.make_prefill(cfg)
     run = Run(inp)
     check_run(run, np.arange(T))
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,d,dtype,kb,W", [
+    (333, 8, 2, 128, "bf16", 4, 100),   # two groups per CU
+    (257, 4, 2, 64, "f32", 2, 64),
+    (200, 8, 2, 128, "f32", 2, 50),     # fp32 head_dim 128: 8-wave one-column-tile kernel
+])
+def test_sinks_all_rows(T, Hq, Hkv, d, dtype, kb, W):
+    """Per-head sink logits in both branches (paper 4.1)."""
+    say(f"[sinks] T={T} Hq={Hq} Hkv={Hkv} d={d} {dtype} kb={kb} W={W}")
+    cfg = gen.config(1, T=T, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, kb=kb, W=W, N=2)
+    run = Run(gen.make_prefill(cfg), sinks=True)
+    check_run(run, np.arange(T))
+
+
+def test_window_shares_full_kv():
+    """Ablation of the paper's study 2: the window branch reads the full layer's
+    own K/V instead of a K'/V' of its own (no new kernel: the shared tensors go
+    in as the window cache)."""
+    say("[window shares the full layer's K/V]")
+    cfg = gen.config(1, T=300, Hq=8, Hkv=2, d=128, dtype="bf16", kb=3, W=90, N=1)
+    inp = gen.make_prefill(cfg)
+    inp.layers[0]["k"] = inp.k
+    inp.layers[0]["v"] = inp.v
+    check_run(Run(inp), np.arange(cfg.T))
 
 
 @pytest.mark.parametrize("score", ["max", "lse"])
@@ -238,14 +266,15 @@ def test_config3_80b_shaped_sampled():
     check_run(run, pos)
 
 
-def test_long_sequence_wide_bitsets():
+@pytest.mark.parametrize("sinks", [False, True])
+def test_long_sequence_wide_bitsets(sinks):
     """T = 53312 with one head per kv group: the selection bitsets of a
     four-wave group would pass 16 KiB of LDS, so the sparse layer takes the
     8-wave kernel with three tile buffers."""
-    say("[long] T=53312 Hq=2 Hkv=2 d=64 bf16, sampled rows")
+    say(f"[long] T=53312 Hq=2 Hkv=2 d=64 bf16, sampled rows, sinks={sinks}")
     cfg = gen.config(1, T=53312, Hq=2, Hkv=2, d=64, dtype="bf16", kb=8, W=64, N=1)
     inp = gen.make_prefill(cfg)
-    run = Run(inp)
+    run = Run(inp, sinks=sinks)
     pos = sample_rows(53312, every=997, head=64, tail=64)
     check_run(run, pos)
 
