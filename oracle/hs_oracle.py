@@ -44,7 +44,7 @@ design notes):
       older than the newest n_recent, which are always added and do not use
       the k budget; no window branch and no gate.  The group score is the
       same group-wise maximum of post-softmax weights.
-  R10 Sink biases ([P] 4.1, "Experiments Setup": per-head learnable sink
+  R14 Sink biases ([P] 4.1, "Experiments Setup": per-head learnable sink
       biases in the sparse and the window branch, following gpt-oss): each
       branch's softmax takes one extra logit b_h, in the units of tau q.k,
       that carries no value, o = sum_j e^{s_j} v_j / (sum_j e^{s_j} + e^{b_h}).
@@ -70,7 +70,7 @@ def _attend(logits: np.ndarray, values: np.ndarray, sink=None):
     Returns (o [..., d], lse [...]).  An empty key set (n == 0, or every logit
     -inf) gives o = 0 and lse = -inf (reading R3).  `sink` (broadcast to the
     leading shape, or None) is one more logit per row with no value (reading
-    R10): it joins the maximum and the denominator, and the lse then
+    R14): it joins the maximum and the denominator, and the lse then
     includes it.
     """
     lead = logits.shape[:-1]
@@ -211,7 +211,7 @@ def sparse_branch_rows(qs_rows: np.ndarray, pos: np.ndarray, k: np.ndarray,
     o~_t = softmax(tau q'_t . K~) V~ (eq. o~_t).  Keys after t inside a selected
     diagonal block are excluded (causality).  idx [Hkv, R, n_sel] holds block
     ids (or token ids with block=1), -1 = unused; the order of the list does
-    not matter.  sink [Hq] or None: the branch's sink logits (R10).
+    not matter.  sink [Hq] or None: the branch's sink logits (R14).
     Returns o~ [R, Hq, d].
     """
     R, Hq, d = qs_rows.shape
@@ -237,7 +237,7 @@ def window_branch_rows(qs_rows: np.ndarray, pos: np.ndarray, ks: np.ndarray,
                        sink=None) -> np.ndarray:
     """Sliding-window branch with the layer's own K'/V' ([X] 3.4.3 "Branch 2",
     eq. o'_t): keys [t-W+1, t] (reading R6).  W = 0 gives 0.
-    ks, vs [Hkv, >=max(pos)+1, d]; sink [Hq] or None (R10).
+    ks, vs [Hkv, >=max(pos)+1, d]; sink [Hq] or None (R14).
     Returns o' [R, Hq, d]."""
     R, Hq, d = qs_rows.shape
     Hkv = ks.shape[0]
@@ -292,7 +292,7 @@ def sparse_layer_rows(qs_rows, pos, k, v, idx, ks, vs, W, gates_rows,
                       block: int = BLOCK, scale: float | None = None, sinks=None):
     """One sparse layer ([X] 3.4.3, [P] 3.1/3.3): block-sparse branch over the
     shared K/V at the inherited indices, window branch over its own K'/V',
-    merged by the sigmoid gates.  sinks [2, Hq] or None (R10)."""
+    merged by the sigmoid gates.  sinks [2, Hq] or None (R14)."""
     o_sp = sparse_branch_rows(qs_rows, pos, k, v, idx, block, scale,
                               None if sinks is None else sinks[0])
     o_sw = window_branch_rows(qs_rows, pos, ks, vs, W, scale,
@@ -386,7 +386,7 @@ def decode_sparse_layer(lay, k, v, L, idx, W, block=BLOCK, kv_scale=None, scale=
     cache, the window branch over the layer's own ring, the sigmoid gates
     ([X] 3.4.3; [H2] decode_one_token).  idx [Hkv, n] (-1 = unused).
     Token mode has no window and no gate (reading R9).  lay["sinks"] [2, Hq]
-    (optional, R10).  Returns o [Hq, d]."""
+    (optional, R14).  Returns o [Hq, d]."""
     if kv_scale is not None:
         k = decode_e4m3fn(k[:, :L]) * kv_scale[0][:, None, None]
         v = decode_e4m3fn(v[:, :L]) * kv_scale[1][:, None, None]

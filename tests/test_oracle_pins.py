@@ -156,7 +156,7 @@ def pin_window(o):
 
 
 def pin_sinks(o):
-    """Sink biases (reading R10) against the gpt-oss form built from torch's
+    """Sink biases (reading R14) against the gpt-oss form built from torch's
     float64 SDPA: one extra key with zero key and value vectors whose logit
     is the sink, added through SDPA's additive mask; both branches (the
     sparse one with every block selected), a -inf sink changing nothing, an
