@@ -115,6 +115,13 @@ def _contig(*ts):
             raise ValueError("tensors passed to hysparse must be contiguous")
 
 
+def _check_f32(name, t, shape):
+    """fp32 side inputs read as raw floats by the kernels (gates, sinks)."""
+    if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != tuple(shape)):
+        raise ValueError(f"{name} must be a float32 tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+
+
 # ------------------------------------------------------------------ prefill
 def full_attn_fwd_scores(q, k, v_blk, o, lse, blk_raw, score=HS_SCORE_MAX, scale=0.0,
                          stream=None):
@@ -148,6 +155,8 @@ def sparse_attn_fwd(q_sp, k, v_blk, idx, topk, k_swa, v_swa_blk, window, gate_lo
     sinks [2,Hq] fp32 (sparse, window branch) or None."""
     _contig(q_sp, k, v_blk, idx, k_swa, v_swa_blk, gate_logits, sinks, o)
     B, T, Hq, d = q_sp.shape
+    _check_f32("gate_logits", gate_logits, (B, T, Hq, 2))
+    _check_f32("sinks", sinks, (2, Hq))
     Hkv = (k if k is not None else k_swa).shape[1]
     s = make_shape(B, T, T, Hq, Hkv, d, dtype_code(q_sp), scale=scale)
     _check(load().hs_sparse_attn_fwd(ctypes.byref(s), _ptr(q_sp), _ptr(k), _ptr(v_blk),
@@ -202,6 +211,8 @@ def decode_select_attn(q_sp, k, v, lens, idx, n_sel, k_ring, v_ring, window, gat
     sinks [2,Hq] fp32 or None (token mode uses row 0).
     ws: uint8 device workspace (allocated here when None and one is needed)."""
     _contig(q_sp, k, v, lens, idx, k_ring, v_ring, gate_logits, sinks, o)
+    _check_f32("gate_logits", gate_logits, (q_sp.shape[0], q_sp.shape[1], 2))
+    _check_f32("sinks", sinks, (2, q_sp.shape[1]))
     s = decode_shape(q_sp, k, lens, kv_scale, scale)
     if ws is None:
         need = workspace_size(HS_FN_DECODE_SELECT, s, block)

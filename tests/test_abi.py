@@ -101,3 +101,21 @@ def test_topk_and_sparse_validation():
                                   None, None, FAKE, None) == hb.HS_ERR_INVALID_ARG   # window w/o cache
     assert lib.hs_sparse_attn_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, -1, None, None, 0,
                                   None, None, FAKE, None) == hb.HS_ERR_INVALID_ARG
+
+
+def test_binding_rejects_bad_side_inputs():
+    """Gates and sinks are read as raw fp32 by the kernels: the binding checks
+    their dtype and shape before anything is launched."""
+    import torch
+
+    B, T, Hq, Hkv, d = 1, 64, 4, 2, 64
+    q = torch.zeros((B, T, Hq, d), dtype=torch.bfloat16)
+    k = torch.zeros((B, Hkv, T, d), dtype=torch.bfloat16)
+    v = torch.zeros((B, Hkv, 1, d, 64), dtype=torch.bfloat16)
+    idx = torch.zeros((B, Hkv, T, 2), dtype=torch.int32)
+    o = torch.zeros_like(q)
+    good_g = torch.zeros((B, T, Hq, 2))
+    for g, s in ((good_g.double(), None), (torch.zeros((B, T, Hq, 3)), None),
+                 (good_g, torch.zeros((2, Hq), dtype=torch.float64)), (good_g, torch.zeros((1, Hq)))):
+        with pytest.raises(ValueError):
+            hb.sparse_attn_fwd(q, k, v, idx, 2, None, None, 0, g, o, sinks=s)
