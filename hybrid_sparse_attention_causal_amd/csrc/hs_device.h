@@ -386,10 +386,12 @@ struct TileStage {
       }
     }
   }
-  // krows, vslab and nk must be wave-uniform
+  // krows, vslab and nk must be wave-uniform.  The wave index is made
+  // wave-uniform too, so each transfer's LDS destination (M0) is scalar
+  // arithmetic instead of a vector add and a readfirstlane.
   __device__ __forceinline__ void dma(char* buf, const char* krows, const char* vslab, int nk) {
     nk_ = nk;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // (the source pointer goes through a named variable: passing the
     // conditional expression straight to the builtin makes the host pass of
     // this compiler drop the launch stubs of some kernel instantiations)
