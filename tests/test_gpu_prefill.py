@@ -143,6 +143,20 @@ def test_sinks_all_rows(T, Hq, Hkv, d, dtype, kb, W):
     check_run(run, np.arange(T))
 
 
+def test_large_logits():
+    """Queries scaled by 24 (fp32 inputs): logits reach the hundreds and the
+    running maximum jumps by far more than the rescale slack between tiles;
+    every row of the full layer, the selection and the sparse layers (with
+    sinks) must still match."""
+    say("[large logits] T=400 Hq=4 Hkv=2 d=64 fp32, q x 24")
+    cfg = gen.config(1, T=400, Hq=4, Hkv=2, d=64, dtype="f32", kb=3, W=70, N=1)
+    inp = gen.make_prefill(cfg)
+    inp.q = (inp.q * 24.0).astype(np.float32)
+    inp.layers[0]["q"] = (inp.layers[0]["q"] * 24.0).astype(np.float32)
+    run = Run(inp, sinks=True)
+    check_run(run, np.arange(cfg.T))
+
+
 def test_window_shares_full_kv():
     """Ablation of the paper's study 2: the window branch reads the full layer's
     own K/V instead of a K'/V' of its own (no new kernel: the shared tensors go
