@@ -129,6 +129,21 @@ def test_many_sequences_unit_numbering():
     check_sequences(run, [0, 1, 62, 63, 64, 65, 100, 127, 128, 129, 140, 148, 149])
 
 
+def test_large_logits():
+    """Queries scaled by 24: logits reach the hundreds, so the split-K
+    partial states of one row carry maxima far apart and the merge must
+    rescale them exactly; sparse layers with sinks and the window."""
+    say("[decode large logits] q x 24")
+    cfg = gen.config(4, B=3, T=2048, Hq=8, Hkv=2, d=128, kb=4, W=100, N=1, L_lo=1, L_hi=2048)
+    inp = gen.make_decode(cfg)
+    inp.lens = np.array([70, 1500, 2048], np.int32)
+    up = lambda a: gen.f32_to_bf16_bits(gen.bf16_bits_to_f32(a) * 24.0)
+    inp.q = up(inp.q)
+    inp.layers[0]["q"] = up(inp.layers[0]["q"])
+    run = DecodeRun(inp, sinks=True)
+    check_sequences(run, range(3))
+
+
 def test_long_capacity_chunks():
     """Capacity above 128K: the full layer's split-K chunks are 32 tiles long."""
     say("[decode capacity 196608] B=2 Hq=8 Hkv=2 d=128")
