@@ -577,7 +577,7 @@ __global__ __launch_bounds__(64 * NW, 2) void sparse_prefill_kernel(SparsePrefil
   const char* vsg = (const char*)a.vs + (size_t)(b * a.Hkv + g) * a.nblk * D * 64 * ES;
   auto issue = [&](St& st, int i) {
     const bool win = i >= nu;
-    const int j = win ? jw0 + (i - nu) : ulist[i];
+    const int j = win ? jw0 + (i - nu) : ulist[min(i, a.nblk - 1)];
     st.gload((win ? ksg : kg) + (size_t)64 * j * D * ES, (win ? vsg : vg) + (size_t)j * D * 64 * ES,
              T - 64 * j);
   };
@@ -810,7 +810,7 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
   st.dma_init();
   auto issue = [&](int i, char* buf) {  // item i -> buf (tile i % 3), in flight until wait_vmem
     const bool win = i < nwin;
-    const int j = __builtin_amdgcn_readfirstlane(win ? jw0 + i : ulist[i - nwin]);
+    const int j = __builtin_amdgcn_readfirstlane(win ? jw0 + i : ulist[max(i - nwin, 0)]);
     st.dma(buf, (win ? ksg : kg) + (size_t)64 * j * D * ES, (win ? vsg : vg) + (size_t)j * D * 64 * ES,
            T - 64 * j);
   };
@@ -895,7 +895,7 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
   // this wave that have a live key in it (0: the wave skips the item)
   auto item = [&](int i, int& kbase, int* lo, int* hi) -> unsigned {
     const bool win = i < nwin;
-    const int j = win ? jw0 + i : ulist[i - nwin];
+    const int j = win ? jw0 + i : ulist[max(i - nwin, 0)];
     kbase = 64 * j;
     unsigned act = 0;
 #pragma unroll
@@ -1082,7 +1082,7 @@ __global__ __launch_bounds__(256, 2) void sparse_prefill_dual_kernel(SparsePrefi
   st.dma_init();
   auto issue = [&](int i, char* buf) {  // item i -> buf (tile i % 2), in flight until wait_vmem
     const bool win = i < nwin;
-    const int j = __builtin_amdgcn_readfirstlane(win ? jw0 + i : ulist[i - nwin]);
+    const int j = __builtin_amdgcn_readfirstlane(win ? jw0 + i : ulist[max(i - nwin, 0)]);
     st.dma(buf, (win ? ksg : kg) + (size_t)64 * j * D * ES, (win ? vsg : vg) + (size_t)j * D * 64 * ES,
            T - 64 * j);
   };
@@ -1173,7 +1173,7 @@ __global__ __launch_bounds__(256, 2) void sparse_prefill_dual_kernel(SparsePrefi
   auto fetch = [&](int i) {
     Pre p;
     const bool win = i < nwin;
-    p.j = __builtin_amdgcn_readfirstlane(win ? jw0 + i : ulist[i - nwin]);
+    p.j = __builtin_amdgcn_readfirstlane(win ? jw0 + i : ulist[max(i - nwin, 0)]);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) p.sw[nt] = S[(w * PW + pcol[nt]) * nw32 + (win ? 0 : p.j >> 5)];
     return p;
