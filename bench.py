@@ -262,9 +262,9 @@ def main():
         print(json.dumps({"copy_ref_bytes": n, "launches": 3}))
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the kernels shard by kv group with no exchange, see the design notes)",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: "
+              "this build has no multi-GPU path (prefill would shard by kv group with no "
+              "exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -19,8 +19,7 @@ Sources (cited by page title and section):
   [H2] HySparse2 explainer page (deep-reads), "Precise retrieval without a
        separate indexer" and the decode_one_token pseudocode.
 
-Readings where the pages leave a step open (each one also listed in the
-design notes):
+Readings where the pages leave a step open:
   R1  The block score is the post-softmax maximum (eq. S_t^i of [X] 3.4.1);
       the printed rescale of [X] "Modified FlashAttention Kernel" is read as
       exp(S - m)/l, i.e. exp(raw - LSE), which is the only form that makes the
