@@ -263,7 +263,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: "
-              "this build has no multi-GPU path (prefill would shard by kv group with no "
+              "the library has no multi-GPU path (prefill would shard by kv group with no "
               "exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
 
