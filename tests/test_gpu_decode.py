@@ -154,6 +154,17 @@ def test_long_capacity_chunks():
     check_sequences(run, range(2))
 
 
+def test_max_capacity_block_mode():
+    """Block mode at the largest capacity the selection takes (262144 slots,
+    4096 blocks per row), one sequence at the full length."""
+    say("[decode capacity 262144] B=2 Hq=4 Hkv=1 d=128")
+    cfg = gen.config(4, B=2, T=262144, Hq=4, Hkv=1, d=128, kb=16, W=128, N=1, L_lo=1, L_hi=262144)
+    inp = gen.make_decode(cfg)
+    inp.lens = np.array([100003, 262144], np.int32)
+    run = DecodeRun(inp)
+    check_sequences(run, range(2))
+
+
 def test_group_of_16_and_d64():
     say("[decode G=16 d=64]")
     cfg = gen.config(4, B=3, T=2048, Hq=16, Hkv=1, d=64, kb=5, W=128, N=1, L_lo=300, L_hi=2048)
