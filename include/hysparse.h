@@ -165,7 +165,10 @@ hs_status hs_block_topk(const hs_shape* shape, const float* blk_raw, const float
  *         row 1: window branch), in the units of tau q.k, or NULL (none)
  *   o     [batch][T][hq][head_dim] (out)
  * o_t = sigmoid(G0) o~_t + sigmoid(G1) o'_t; an empty selection gives o~ = 0.
- * Keys after t inside a selected block are excluded.  Sinks (paper 4.1,
+ * Keys after t inside a selected block are excluded.  The selection bitsets
+ * of one work group must fit 48 KiB of LDS: T <= 83968 for G = hq/hkv = 1,
+ * 147456 for G = 2, 239616 for G = 4, 262144 for G >= 8 (G <= 16); longer
+ * sequences return HS_ERR_UNSUPPORTED.  Sinks (paper 4.1,
  * "Experiments Setup": per-head learnable sink biases in both branches,
  * following gpt-oss): each branch's softmax takes one more logit b_h that
  * carries no value, o = sum_j e^{s_j} v_j / (sum_j e^{s_j} + e^{b_h}).

@@ -75,19 +75,20 @@ def check_run(run, pos, score="max", include_diag=False, gates=True, layers=None
     cfg, inp = run.cfg, run.inp
     tol = TOL[cfg.dtype]
     ref = oracle_rows(inp, pos, run.kb, run.W, score, include_diag, gates, b=b)
-    o = host(run.o)[b][pos]
+    dpos = torch.from_numpy(np.asarray(pos, np.int64)).cuda()  # rows picked on the device
+    o = host(run.o[b][dpos])
     err_o = np.abs(o - ref["o"]).max()
-    lse = host(run.lse)[b][:, pos]
+    lse = host(run.lse[b][:, dpos])
     err_lse = np.abs(lse - ref["lse"]).max()
-    raw = host(run.raw)[b][:, pos]
+    raw = host(run.raw[b][:, dpos])
     valid = ~np.isnan(ref["raw"])
     err_raw = np.abs(raw[valid] - ref["raw"][valid]).max()
     say(f"  full layer: max|dO|={err_o:.3g} max|dLSE|={err_lse:.3g} max|draw|={err_raw:.3g}")
     assert err_o <= tol and err_lse <= SIDE_TOL and err_raw <= SIDE_TOL
-    gs = host(run.gs)[b][:, pos]
+    gs = host(run.gs[b][:, dpos])
     vg = ~np.isnan(ref["Sg"])
     rel_gs = np.abs(gs[vg] - ref["Sg"][vg]).max() / np.abs(ref["Sg"][vg]).max()
-    gidx = host(run.idx)[b][:, pos]
+    gidx = host(run.idx[b][:, dpos])
     n, ties, fails = compare_indices(gidx, ref, pos, run.kb, include_diag)
     say(f"  selection: rows={n} near-tie={ties} failures={len(fails)} rel|dSg|={rel_gs:.3g}")
     assert not fails, fails[:5]
@@ -98,7 +99,7 @@ def check_run(run, pos, score="max", include_diag=False, gates=True, layers=None
         sk = None if run.sinks[l] is None else run.sinks[l].astype(np.float64)
         want = ora.sparse_layer_rows(inp.f64("q", l)[b][pos], pos, k64, v64, gidx,
                                      inp.f64("k", l)[b], inp.f64("v", l)[b], run.W, gl, sinks=sk)
-        got = host(run.outs[l])[b][pos]
+        got = host(run.outs[l][b][dpos])
         err = np.abs(got - want).max()
         say(f"  sparse layer {l}: max|dO|={err:.3g}")
         assert err <= tol
@@ -277,6 +278,18 @@ def test_config3_80b_shaped_sampled():
     inp = gen.make_prefill(gen.config(3), n_layers=2)
     run = Run(inp)
     pos = sample_rows(32768, every=409, head=96, tail=32)
+    check_run(run, pos)
+
+
+def test_longest_sequence_group4():
+    """T = 239616, the longest sequence the sparse layer takes with four heads
+    per kv group (its selection bitsets fill the 48 KiB allowed): every
+    kernel at its largest shape, sampled rows."""
+    say("[longest] T=239616 Hq=4 Hkv=1 d=64 bf16, sampled rows")
+    cfg = gen.config(1, T=239616, Hq=4, Hkv=1, d=64, dtype="bf16", kb=8, W=64, N=1)
+    inp = gen.make_prefill(cfg)
+    run = Run(inp, sinks=True)
+    pos = sample_rows(239616, every=4999, head=8, tail=8)
     check_run(run, pos)
 
 
