@@ -377,13 +377,14 @@ __global__ __launch_bounds__(256) void block_topk_kernel(TopkArgs a) {
   const int ncand = (t >> 6) + (a.diag ? 1 : 0);
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
-  // every load is unconditional (entries past the visible blocks read a
-  // clamped slot of the same row and are dropped by a select): loads under a
-  // per-lane branch would be waited for one by one
+  // every load is unconditional (entries past the visible blocks re-read the
+  // last visible one, a line the row fetches anyway, and are dropped by a
+  // select): loads under a per-lane branch would be waited for one by one
   // HB heads' rows are requested together (one memory round trip per HB
   // heads); a batch past the last head re-reads head G-1, which leaves the
   // maximum unchanged
   constexpr int HB = MAXI <= 4 ? 4 : (MAXI == 8 ? 2 : 1);
+  const int jlast = min(max(nvis - 1, 0), a.raw_stride - 1);
   float x[MAXI];
 #pragma unroll
   for (int i = 0; i < MAXI; ++i) x[i] = -INFINITY;
@@ -395,7 +396,7 @@ __global__ __launch_bounds__(256) void block_topk_kernel(TopkArgs a) {
       const float* rp = a.raw + ((size_t)(b * a.Hq + h) * R + tr) * a.raw_stride;
       ls[e] = a.lse[(size_t)(b * a.Hq + h) * R + tr];
 #pragma unroll
-      for (int i = 0; i < MAXI; ++i) v[e][i] = rp[min(i * 64 + lane, a.raw_stride - 1)];
+      for (int i = 0; i < MAXI; ++i) v[e][i] = rp[min(i * 64 + lane, jlast)];
     }
 #pragma unroll
     for (int e = 0; e < HB; ++e)
