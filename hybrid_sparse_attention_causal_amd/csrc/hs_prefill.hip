@@ -352,58 +352,24 @@ __global__ __launch_bounds__(512, 2) void full_prefill_pp_kernel(FullPrefillArgs
 }
 
 // ===================================================================== top-k
-// One wavefront per (sequence, kv group, query row).  Candidate j sits in lane
-// j % 64, slot j / 64.  The score of a candidate is x = max_h (raw - LSE_h),
-// the log of S_g; the k-th largest order key is found by a 32-step bitwise
-// search with wave ballots, equal keys are resolved towards smaller j, and the
-// selected ids are emitted in ascending order.
+// One wavefront per RW consecutive (sequence, kv group, query row) rows.
+// Candidate j sits in lane j % 64, slot j / 64.  The score of a candidate is
+// x = max_h (raw - LSE_h), the log of S_g; the k-th largest order key is found
+// by a bitwise search with wave ballots, equal keys are resolved towards
+// smaller j, and the selected ids are emitted in ascending order.
 __device__ __forceinline__ uint32_t order_key(float x) {
   const uint32_t u = __float_as_uint(x);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int MAXI>
-__global__ __launch_bounds__(256) void block_topk_kernel(TopkArgs a) {
-  const int lane = threadIdx.x & 63;
-  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int R = a.R;
-  if (row >= (long)a.B * a.Hkv * R) return;
-  const int tr = (int)(row % R);
-  const int bg = (int)(row / R);
-  const int g = bg % a.Hkv, b = bg / a.Hkv;
-  const int t = a.kv_lens ? ctx_len(a.kv_lens, b, 64 * a.raw_stride) - 1 : tr;
-  const int G = a.Hq / a.Hkv;
-  const int nvis = (t >> 6) + 1;
-  const int ncand = (t >> 6) + (a.diag ? 1 : 0);
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+// rows per wavefront: short rows are latency bound (one memory round trip per
+// row), so a wave requests two rows' scores together
+constexpr int topk_rows_per_wave(int maxi) { return maxi <= 4 ? 2 : 1; }
 
-  // every load is unconditional (entries past the visible blocks re-read the
-  // last visible one, a line the row fetches anyway, and are dropped by a
-  // select): loads under a per-lane branch would be waited for one by one
-  // HB heads' rows are requested together (one memory round trip per HB
-  // heads); a batch past the last head re-reads head G-1, which leaves the
-  // maximum unchanged
-  constexpr int HB = MAXI <= 4 ? 4 : (MAXI == 8 ? 2 : 1);
-  const int jlast = min(max(nvis - 1, 0), a.raw_stride - 1);
-  float x[MAXI];
-#pragma unroll
-  for (int i = 0; i < MAXI; ++i) x[i] = -INFINITY;
-  for (int hh0 = 0; hh0 < G; hh0 += HB) {
-    float v[HB][MAXI], ls[HB];
-#pragma unroll
-    for (int e = 0; e < HB; ++e) {
-      const int h = g * G + min(hh0 + e, G - 1);
-      const float* rp = a.raw + ((size_t)(b * a.Hq + h) * R + tr) * a.raw_stride;
-      ls[e] = a.lse[(size_t)(b * a.Hq + h) * R + tr];
-#pragma unroll
-      for (int i = 0; i < MAXI; ++i) v[e][i] = rp[min(i * 64 + lane, jlast)];
-    }
-#pragma unroll
-    for (int e = 0; e < HB; ++e)
-#pragma unroll
-      for (int i = 0; i < MAXI; ++i) x[i] = i * 64 + lane < nvis ? fmaxf(x[i], v[e][i] - ls[e]) : x[i];
-  }
-  const size_t orow = (size_t)(b * a.Hkv + g) * R + tr;
+// selection of one row from its candidates' log scores x (lane's slots)
+template <int MAXI>
+__device__ __forceinline__ void topk_emit(const TopkArgs& a, const float (&x)[MAXI], int nvis,
+                                          int ncand, size_t orow, int lane, uint64_t lt_mask) {
   if (a.gs) {
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
@@ -459,6 +425,72 @@ __global__ __launch_bounds__(256) void block_topk_kernel(TopkArgs a) {
     base += __popcll(sm);
   }
   for (int p = base + lane; p < kb; p += 64) out[p] = -1;
+}
+
+template <int MAXI>
+__global__ __launch_bounds__(256) void block_topk_kernel(TopkArgs a) {
+  constexpr int RW = topk_rows_per_wave(MAXI);
+  const int lane = threadIdx.x & 63;
+  const int R = a.R;
+  const long nrows = (long)a.B * a.Hkv * R;
+  const long row0 = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * RW;
+  if (row0 >= nrows) return;
+  const int G = a.Hq / a.Hkv;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+  // per row: a row past the last one repeats the last row's reads, and its
+  // selection is not emitted
+  int nvis[RW], ncand[RW], jlast[RW];
+  size_t orow[RW], rbase[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const long row = min(row0 + r, nrows - 1);
+    const int tr = (int)(row % R);
+    const int bg = (int)(row / R);
+    const int g = bg % a.Hkv, b = bg / a.Hkv;
+    const int t = a.kv_lens ? ctx_len(a.kv_lens, b, 64 * a.raw_stride) - 1 : tr;
+    nvis[r] = (t >> 6) + 1;
+    ncand[r] = (t >> 6) + (a.diag ? 1 : 0);
+    jlast[r] = min(max(nvis[r] - 1, 0), a.raw_stride - 1);
+    orow[r] = (size_t)(b * a.Hkv + g) * R + tr;
+    rbase[r] = (size_t)(b * a.Hq + g * G) * R + tr;   // (b, head g*G, row tr)
+  }
+
+  // every load is unconditional (entries past the visible blocks re-read the
+  // last visible one, a line the row fetches anyway, and are dropped by a
+  // select): loads under a per-lane branch would be waited for one by one.
+  // HB heads' rows of all RW rows are requested together (one memory round
+  // trip per HB heads); a batch past the last head re-reads head G-1, which
+  // leaves the maximum unchanged
+  constexpr int HB = MAXI <= 4 ? 4 : (MAXI == 8 ? 2 : 1);
+  float x[RW][MAXI];
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) x[r][i] = -INFINITY;
+  for (int hh0 = 0; hh0 < G; hh0 += HB) {
+    float v[RW][HB][MAXI], ls[RW][HB];
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int e = 0; e < HB; ++e) {
+        const size_t hr = rbase[r] + (size_t)min(hh0 + e, G - 1) * R;
+        const float* rp = a.raw + hr * a.raw_stride;
+        ls[r][e] = a.lse[hr];
+#pragma unroll
+        for (int i = 0; i < MAXI; ++i) v[r][e][i] = rp[min(i * 64 + lane, jlast[r])];
+      }
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int e = 0; e < HB; ++e)
+#pragma unroll
+        for (int i = 0; i < MAXI; ++i)
+          x[r][i] = i * 64 + lane < nvis[r] ? fmaxf(x[r][i], v[r][e][i] - ls[r][e]) : x[r][i];
+  }
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+    if (row0 + r < nrows) topk_emit<MAXI>(a, x[r], nvis[r], ncand[r], orow[r], lane, lt_mask);
 }
 
 // ==================================================================== sparse
@@ -1280,16 +1312,23 @@ hipError_t launch_full_prefill(const FullPrefillArgs& a, int dtype, int D, int s
   return D == 64 ? full_dispatch<HS_F32, 64>(a, score_lse, s) : full_dispatch<HS_F32, 128>(a, score_lse, s);
 }
 
-hipError_t launch_block_topk(const TopkArgs& a, int max_blocks, hipStream_t s) {
+// four waves per work group, topk_rows_per_wave(MAXI) rows per wave
+template <int MAXI>
+static void topk_launch(const TopkArgs& a, hipStream_t s) {
   const long rows = (long)a.B * a.Hkv * a.R;
-  dim3 grid((unsigned)((rows + 3) / 4));
-  if (max_blocks <= 64) hipLaunchKernelGGL(block_topk_kernel<1>, grid, dim3(256), 0, s, a);
-  else if (max_blocks <= 128) hipLaunchKernelGGL(block_topk_kernel<2>, grid, dim3(256), 0, s, a);
-  else if (max_blocks <= 256) hipLaunchKernelGGL(block_topk_kernel<4>, grid, dim3(256), 0, s, a);
-  else if (max_blocks <= 512) hipLaunchKernelGGL(block_topk_kernel<8>, grid, dim3(256), 0, s, a);
-  else if (max_blocks <= 1024) hipLaunchKernelGGL(block_topk_kernel<16>, grid, dim3(256), 0, s, a);
-  else if (max_blocks <= 2048) hipLaunchKernelGGL(block_topk_kernel<32>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(block_topk_kernel<64>, grid, dim3(256), 0, s, a);
+  const long per_wg = 4L * topk_rows_per_wave(MAXI);
+  hipLaunchKernelGGL(block_topk_kernel<MAXI>, dim3((unsigned)((rows + per_wg - 1) / per_wg)),
+                     dim3(256), 0, s, a);
+}
+
+hipError_t launch_block_topk(const TopkArgs& a, int max_blocks, hipStream_t s) {
+  if (max_blocks <= 64) topk_launch<1>(a, s);
+  else if (max_blocks <= 128) topk_launch<2>(a, s);
+  else if (max_blocks <= 256) topk_launch<4>(a, s);
+  else if (max_blocks <= 512) topk_launch<8>(a, s);
+  else if (max_blocks <= 1024) topk_launch<16>(a, s);
+  else if (max_blocks <= 2048) topk_launch<32>(a, s);
+  else topk_launch<64>(a, s);
   return hipGetLastError();
 }
 
