@@ -119,6 +119,9 @@ SMALL = [
     # rows not 16-byte aligned; 35 blocks with head_dim 64: runs of 16)
     (2113, 8, 2, 128, "bf16", 4, 300),
     (2200, 4, 1, 64, "bf16", 3, 100),
+    # 331 selection rows (8*41 + 3): the top-k kernel's last work group has a
+    # wave with one row of its two and two waves with none
+    (331, 4, 1, 64, "bf16", 3, 64),
 ]
 
 
