@@ -333,6 +333,25 @@ def decode_e4m3fn(codes: np.ndarray) -> np.ndarray:
     return s * val
 
 
+def dequantize_e4m3(codes: np.ndarray, scale, head_axis: int = 0) -> np.ndarray:
+    """Stored fp8 tensor -> values: decode_e4m3fn(code) * scale[h], with one
+    fp32 scale per head along `head_axis` (reading R10: "per-head fp32
+    scale")."""
+    c = np.asarray(codes)
+    s = np.asarray(scale, np.float64)
+    shape = [1] * c.ndim
+    shape[head_axis] = s.size
+    return decode_e4m3fn(c) * s.reshape(shape)
+
+
+def dequantize_kv(k: np.ndarray, v: np.ndarray, kv_scale, L: int | None = None):
+    """fp8 key and value caches [Hkv, C, d] -> values of the first L positions:
+    row 0 of kv_scale [2, Hkv] scales the keys, row 1 the values (R10)."""
+    kv_scale = np.asarray(kv_scale, np.float64)
+    return (dequantize_e4m3(k[:, :L], kv_scale[0], 0),
+            dequantize_e4m3(v[:, :L], kv_scale[1], 0))
+
+
 def window_from_ring(k_ring: np.ndarray, v_ring: np.ndarray, L: int, W: int):
     """Keys/values of the last min(L, W) positions, read from a W-slot ring
     where position p sits in slot p mod W (reading R8).  Returns them in
@@ -355,8 +374,7 @@ def decode_step(q, k, v, L, layers, kb, W, block=BLOCK, n_recent=0,
     """
     Hkv = k.shape[0]
     if kv_scale is not None:
-        k = decode_e4m3fn(k[:, :L]) * kv_scale[0][:, None, None]
-        v = decode_e4m3fn(v[:, :L]) * kv_scale[1][:, None, None]
+        k, v = dequantize_kv(k, v, kv_scale, L)
     pos = np.array([L - 1])
     o, lse, raw = full_attention_rows(q[None], pos, k, v, scale, block)
     Sg = group_max(block_scores(raw, lse), Hkv)          # [Hkv, 1, nblk]
@@ -387,8 +405,7 @@ def decode_sparse_layer(lay, k, v, L, idx, W, block=BLOCK, kv_scale=None, scale=
     Token mode has no window and no gate (reading R9).  lay["sinks"] [2, Hq]
     (optional, R14).  Returns o [Hq, d]."""
     if kv_scale is not None:
-        k = decode_e4m3fn(k[:, :L]) * kv_scale[0][:, None, None]
-        v = decode_e4m3fn(v[:, :L]) * kv_scale[1][:, None, None]
+        k, v = dequantize_kv(k, v, kv_scale, L)
     pos = np.array([L - 1])
     qs = lay["q"][None]
     sinks = lay.get("sinks")

@@ -318,6 +318,41 @@ def pin_fp8(o):
     return nan_ok and np.array_equal(ref[fin], mine[fin]) and int(np.isnan(mine).sum()) == 2
 
 
+def pin_fp8_scales(o):
+    """fp8 caches with one scale per (K|V, kv head): token-mode decode with
+    k >= L - n_recent selects every token, so the full layer and the sparse
+    layer both equal dense attention over the dequantised cache.  The
+    reference dequantises through torch's float8_e4m3fn and multiplies by the
+    scale itself; every K/V scale and every head's scale differs, so a
+    swapped scale row or a head slip changes the result."""
+    rng = np.random.default_rng(17)
+    L, Hq, Hkv, d, R = 300, 4, 2, 16, 16
+    kv_scale = np.array([[0.02, 0.5], [3.0, 0.07]])          # [K|V, kv head]
+    xk = rng.standard_normal((Hkv, L, d)) * 40.0
+    xv = rng.standard_normal((Hkv, L, d)) * 40.0
+    f8 = lambda x: torch.from_numpy(np.clip(x, -448, 448).astype(np.float32)).to(torch.float8_e4m3fn)
+    kc = np.stack([f8(xk[g]).view(torch.uint8).numpy() for g in range(Hkv)])
+    vc = np.stack([f8(xv[g]).view(torch.uint8).numpy() for g in range(Hkv)])
+    deq = lambda c, s: torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy() * s
+    kref = np.stack([deq(kc[g], kv_scale[0, g]) for g in range(Hkv)])
+    vref = np.stack([deq(vc[g], kv_scale[1, g]) for g in range(Hkv)])
+    q = rng.standard_normal((L, Hq, d))
+    qs = rng.standard_normal((L, Hq, d))
+    dec = o.decode_step(q[L - 1], kc, vc, L, [dict(q=qs[L - 1])], kb=L, W=0, block=1,
+                        n_recent=R, kv_scale=kv_scale)
+    ok = np.array_equal(dec["idx"][0], np.arange(L))
+    ok = ok and np.abs(dec["o"] - _sdpa(q, kref, vref, causal=True)[L - 1]).max() < 1e-12
+    ok = ok and np.abs(dec["layer_out"][0] - _sdpa(qs, kref, vref, causal=True)[L - 1]).max() < 1e-12
+    # the sparse layer on its own, over a hand-made subset of tokens
+    sel = np.array([[3, 7, 250, 299], [0, 1, 2, 299]])
+    got = o.decode_sparse_layer(dict(q=qs[L - 1]), kc, vc, L, sel, 0, block=1, kv_scale=kv_scale)
+    for g in range(Hkv):
+        heads = slice(g * 2, g * 2 + 2)
+        want = _sdpa(qs[L - 1:L, heads], kref[g:g + 1, sel[g]], vref[g:g + 1, sel[g]])[0]
+        ok = ok and np.abs(got[heads] - want).max() < 1e-12
+    return bool(ok)
+
+
 # ------------------------------------------------------------- the tests
 def test_e1_two_blocks():
     assert pin_e1(ora)
@@ -364,6 +399,10 @@ def test_fp8_table():
     assert pin_fp8(ora)
 
 
+def test_fp8_scales():
+    assert pin_fp8_scales(ora)
+
+
 def test_index_order_does_not_matter():
     q, k, v = _rand(T=256, Hq=4, Hkv=2, d=8, seed=5)
     pos = np.array([130, 200, 255])
@@ -372,6 +411,10 @@ def test_index_order_does_not_matter():
     a = ora.sparse_branch_rows(q[pos], pos, k, v, idx)
     b = ora.sparse_branch_rows(q[pos], pos, k, v, perm)
     assert np.abs(a - b).max() < 1e-14
+    # the list is a set: repeated ids and -1 anywhere in it change nothing
+    dup = np.array([[[2, -1, 0, 2, 1, 0]] * 3, [[-1, 1, 1, 0, -1, -1]] * 3])
+    c = ora.sparse_branch_rows(q[pos], pos, k, v, dup)
+    assert np.abs(a - c).max() < 1e-14
 
 
 def test_decode_equals_last_prefill_row():
@@ -482,6 +525,14 @@ def _no_diag_clip(qs_rows, pos, k, v, idx, block=64, scale=None, sink=None):
     return _orig_sparse(qs_rows, np.full_like(pos, k.shape[1] - 1), k, v, idx, block, scale, sink)
 
 
+def _kv_scale_rows_swapped(k, v, kv_scale, L=None):
+    return _orig_deq_kv(k, v, np.asarray(kv_scale)[::-1], L)
+
+
+def _scale_heads_reversed(codes, scale, head_axis=0):
+    return _orig_deq(codes, np.asarray(scale)[::-1], head_axis)
+
+
 _orig_attend = ora._attend
 _orig_window = ora.window_branch_rows
 _orig_fusion = ora.gated_fusion
@@ -489,6 +540,8 @@ _orig_full = ora.full_attention_rows
 _orig_topk = ora.topk_select
 _orig_fp8 = ora.decode_e4m3fn
 _orig_sparse = ora.sparse_branch_rows
+_orig_deq_kv = ora.dequantize_kv
+_orig_deq = ora.dequantize_e4m3
 
 
 @pytest.mark.parametrize("name,repl,pins", [
@@ -501,6 +554,8 @@ _orig_sparse = ora.sparse_branch_rows
     ("diagonal block not clipped", dict(sparse_branch_rows=_no_diag_clip), [pin_dense_reduction]),
     ("sink ignored", dict(_attend=_sink_ignored), [pin_sinks]),
     ("sink sign flipped", dict(_attend=_sink_negated), [pin_sinks]),
+    ("fp8 K and V scale rows swapped", dict(dequantize_kv=_kv_scale_rows_swapped), [pin_fp8_scales]),
+    ("fp8 scale taken from the wrong head", dict(dequantize_e4m3=_scale_heads_reversed), [pin_fp8_scales]),
 ])
 def test_planted_mistakes_fail_their_pins(name, repl, pins):
     with _Mutant(**repl) as m:
