@@ -1,7 +1,7 @@
-"""Benchmark of the hybrid-block prefill hot path on one MI355X.
+"""Benchmark of the hybrid-block attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--config 2] [--no-cpu]
-                    [--decode [4] [5]]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 30] [--config 3] [--extra 2]
+                    [--decode [4] [5]] [--no-cpu] [--sinks]
 
 One step = one whole hybrid block over one batch of synthetic input: the full
 causal GQA layer with block scores, the top-k selection, then the N sparse
@@ -9,8 +9,12 @@ layers (block-sparse branch over the shared K/V + sliding window + gates), all
 through the C ABI on the current torch stream.  Inputs are resident in HBM
 before the timed region starts.  Prints one JSON line.
 
-Workload (default, --config 2): the 7B-shaped 1:3 hybrid block, B=1, T=8192,
-Hq=32, Hkv=8, d=128, bf16, top-16 blocks of 64, window 512, 3 sparse layers.
+Workload (default, --config 3): the 80B-MoE-shaped 1:11 hybrid block, B=1,
+T=32768, Hq=32, Hkv=4, d=128, bf16, top-32 blocks of 64, window 128, 11
+sparse layers.  --extra 2 also times the 7B-shaped 1:3 block (T=8192) and
+reports it under "prefill_extra"; --decode 4 5 times one decode step of the
+64-sequence block-mode workload and of the 16 x 262144 fp8 token-level
+workload under "decode".
 
 Algorithmic work (counted, never the work actually issued): 4*d FLOP per
 (query head, key) pair, over the causal pairs of the full layer plus, per
@@ -50,21 +54,46 @@ def sparse_flops_per_layer(cfg, kb=None, W=None) -> float:
     return 4.0 * cfg.d * cfg.Hq * cfg.B * keys.sum()
 
 
-def kernel_source_hash() -> str:
+# the sources the prefill kernels are built from
+PREFILL_SOURCES = ("hs_prefill.hip", "hs_device.h", "hs_internal.h")
+TRAFFIC_FILES = {2: "sparse_prefill_7b_hbm_traffic.txt", 3: "sparse_prefill_32k_hbm_traffic.txt"}
+
+
+def kernel_source_hash(names=PREFILL_SOURCES) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "hybrid_sparse_attention_causal_amd", "csrc")
-    for n in sorted(os.listdir(csrc)):
+    for n in sorted(names):
         with open(os.path.join(csrc, n), "rb") as f:
             h.update(n.encode() + f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary
-    (profiles/sparse_prefill_7b_hbm_traffic.txt: FETCH_SIZE and WRITE_SIZE per
-    dispatch, scaled by a plain-copy calibration), if it was taken on the
-    current kernel sources and the same workload; else None."""
-    path = os.path.join(ROOT, "profiles", "sparse_prefill_7b_hbm_traffic.txt")
+def sparse_kernel_name(cfg) -> str:
+    """The kernel hs_sparse_attn_fwd launches for this shape (the library's
+    dispatch: two four-wave work groups per CU while their selection bitsets
+    fit 16 KiB of LDS, else the eight-wave ping-pong kernel; fp32 with
+    head_dim 128 takes the one-column-tile kernel)."""
+    if cfg.dtype == "f32" and cfg.d == 128:
+        return "sparse_prefill_kernel"
+    pwg = 4 * (32 // cfg.G)
+    nw32 = (cfg.nblk + 31) // 32
+    lds = ((1 + 4 + pwg) * nw32 + cfg.nblk + 1) * 4
+    return "sparse_prefill_dual_kernel" if lds <= 16 * 1024 else "sparse_prefill_pp_kernel"
+
+
+def full_kernel_name(cfg) -> str:
+    """The kernel hs_full_attn_fwd_scores launches in prefill."""
+    if cfg.G <= 16 and not (cfg.dtype == "f32" and cfg.d == 128):
+        return "full_prefill_pp_kernel"
+    return "full_prefill_kernel"
+
+
+def measured_traffic(cid: int, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary of
+    workload `cid` (FETCH_SIZE and WRITE_SIZE per dispatch, scaled by a
+    plain-copy calibration), if it was taken on the current prefill kernel
+    sources; else None."""
+    path = os.path.join(ROOT, "profiles", TRAFFIC_FILES.get(cid, "-"))
     if not os.path.exists(path):
         return None
     ent = {}
@@ -80,43 +109,88 @@ def measured_traffic(kernel: str):
         return None
 
 
-def cpu_baseline(inp, budget_s: float = 12.0):
-    """Time the fp64 oracle (as it stands, one BLAS thread) on a bounded sample of
-    query rows of the same workload and scale it by the algorithmic work."""
+_POOL_DATA = {}
+
+
+def _oracle_rows_worker(rows):
+    """One process-pool task: the oracle's whole hybrid block at `rows`.  The
+    stored inputs come from the parent (forked); float64 copies are made only
+    of the rows this task reads (np.zeros pages never written cost no memory)."""
     from threadpoolctl import threadpool_limits
 
+    from hybrid_sparse_attention_causal_amd import inputs as gen
     from oracle import hs_oracle as ora
+
+    inp, k64, v64 = _POOL_DATA["inp"], _POOL_DATA["k"], _POOL_DATA["v"]
+    cfg = inp.cfg
+    conv = lambda a: gen.to_f32(a, cfg.dtype).astype(np.float64)  # noqa: E731
+    rows = np.asarray(rows)
+    win = np.unique(np.concatenate([np.arange(max(0, t - cfg.W + 1), t + 1) for t in rows]))
+    with threadpool_limits(limits=1):
+        q = np.zeros((cfg.T, cfg.Hq, cfg.d))
+        q[rows] = conv(inp.q[0][rows])
+        layers = []
+        for lay in inp.layers:
+            ent = dict(q=np.zeros((cfg.T, cfg.Hq, cfg.d)), k=np.zeros((cfg.Hkv, cfg.T, cfg.d)),
+                       v=np.zeros((cfg.Hkv, cfg.T, cfg.d)), gates=np.zeros((cfg.T, cfg.Hq, 2)))
+            ent["q"][rows] = conv(lay["q"][0][rows])
+            ent["gates"][rows] = lay["gates"][0][rows]
+            ent["k"][:, win] = conv(lay["k"][0][:, win])
+            ent["v"][:, win] = conv(lay["v"][0][:, win])
+            layers.append(ent)
+        ora.hybrid_block_rows(q, k64, v64, layers, rows, cfg.kb, cfg.W)
+    return len(rows)
+
+
+def host_cores() -> int:
+    """Cores the baseline may use: this process's affinity set, capped at the
+    16-core CPU share of one GPU."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(inp, budget_s: float = 12.0):
+    """Time the fp64 oracle (as it stands) on a bounded random sample of query
+    rows of the same workload, on a process pool over the host cores (one BLAS
+    thread per process), and scale the wall time by the algorithmic work.
+    Call it before the GPU is touched: the pool is forked."""
+    import multiprocessing as mp
+
+    from hybrid_sparse_attention_causal_amd import inputs as gen
 
     cfg = inp.cfg
     T = cfg.T
-    rng = np.random.default_rng(12345)
-    order = rng.permutation(T)
-    f = lambda n, l=None: inp.f64(n, l)[0]
-    q, k, v = f("q"), f("k"), f("v")
-    layers = [dict(q=f("q", l), k=f("k", l), v=f("v", l), gates=f("gates", l))
-              for l in range(len(inp.layers))]
+    nl = len(inp.layers)
+    order = np.random.default_rng(12345).permutation(T)
+    chunks = [np.sort(order[i:i + 8]) for i in range(0, T, 8)]
 
     def row_work(t):
         sel = min(cfg.kb, t // 64) * 64 + min(t + 1, cfg.W)
-        return 4.0 * cfg.d * cfg.Hq * ((t + 1) + len(layers) * sel)
+        return 4.0 * cfg.d * cfg.Hq * ((t + 1) + nl * sel)
 
     total = sum(row_work(t) for t in range(T))
+    cores = host_cores()
+    conv = lambda a: gen.to_f32(a, cfg.dtype).astype(np.float64)  # noqa: E731
+    _POOL_DATA.update(inp=inp, k=conv(inp.k[0]), v=conv(inp.v[0]))
     done_w, n_rows = 0.0, 0
-    with threadpool_limits(limits=1):
+    with mp.get_context("fork").Pool(cores) as pool:
         t0 = time.perf_counter()
-        for i in range(0, T, 8):
-            rows = np.sort(order[i:i + 8])
-            ora.hybrid_block_rows(q, k, v, layers, rows, cfg.kb, cfg.W)
-            done_w += sum(row_work(int(t)) for t in rows)
-            n_rows += len(rows)
+        for i, n in enumerate(pool.imap(_oracle_rows_worker, chunks, chunksize=1)):
+            done_w += sum(row_work(int(t)) for t in chunks[i])
+            n_rows += n
             if time.perf_counter() - t0 > budget_s:
                 break
         el = time.perf_counter() - t0
+        pool.terminate()
+    _POOL_DATA.clear()
     block_s = el * total / done_w
-    return {"value": cfg.B * T / block_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": cfg.B * T / block_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{n_rows} random query rows of {T} (all heads, full layer, selection and "
-                      f"{len(layers)} sparse layers) in {el:.1f} s, scaled by algorithmic FLOPs "
-                      f"({done_w / total * 100:.2f}% of the block)"}
+                      f"{nl} sparse layers) in {el:.1f} s wall on a pool of {cores} processes, "
+                      f"scaled by algorithmic FLOPs ({done_w / total * 100:.2f}% of the block)"}
 
 
 def decode_bytes(inp) -> float:
@@ -235,46 +309,19 @@ def bench_decode(cid: int, steps: int, sinks: bool = False):
             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM, "sinks": bool(sinks)}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=30,
-                    help="untimed steps first; the GPU clock takes some 30 ms of load to settle")
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3])
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--decode", type=int, nargs="*", default=[4], choices=[4, 5],
-                    help="decode workloads also measured (default: 4); pass none to skip")
-    ap.add_argument("--sinks", action="store_true",
-                    help="give every sparse layer per-head sink logits (not part of the workloads)")
-    ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
-                    help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
-    args = ap.parse_args()
-    if args.copy_ref:
-        import torch
+WORKLOAD_NAMES = {1: "tiny 1:3 hybrid block prefill", 2: "7B-shaped 1:3 hybrid block prefill",
+                  3: "80B-MoE-shaped 1:11 hybrid block prefill"}
 
-        n = args.copy_ref << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_ref_bytes": n, "launches": 3}))
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: "
-              "the library has no multi-GPU path (prefill would shard by kv group with no "
-              "exchange between GPUs)", file=sys.stderr)
-        sys.exit(2)
 
+def bench_prefill(inp, steps: int, warmup: int, sinks: bool = False):
+    """Time whole prefill hybrid blocks of `inp` (inputs resident in HBM);
+    per-kernel HIP events on the launch stream inside the timed region."""
     import torch
 
     from hybrid_sparse_attention_causal_amd import binding as hb
     from hybrid_sparse_attention_causal_amd import inputs as gen
 
-    hb.load()
-    cfg = gen.config(args.config)
-    inp = gen.make_prefill(cfg)
+    cfg = inp.cfg
     B, T, Hq, Hkv, d = cfg.B, cfg.T, cfg.Hq, cfg.Hkv, cfg.d
 
     def dev(a):
@@ -287,7 +334,7 @@ def main():
     q, k, vb = dev(inp.q), dev(inp.k), dev(gen.block_major(inp.v))
     layers = [dict(q=dev(l["q"]), k=dev(l["k"]), v=dev(gen.block_major(l["v"])),
                    g=dev(l["gates"]), o=torch.empty((B, T, Hq, d), dtype=tdt, device="cuda"),
-                   s=dev(gen.make_sinks(cfg, i)) if args.sinks else None)
+                   s=dev(gen.make_sinks(cfg, i)) if sinks else None)
               for i, l in enumerate(inp.layers)]
     o = torch.empty((B, T, Hq, d), dtype=tdt, device="cuda")
     lse = torch.empty((B, Hq, T), device="cuda")
@@ -310,65 +357,126 @@ def main():
                                stream=stream, sinks=l["s"])
             mark(3 + i)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-           for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(evs[s])
+    for st in range(steps):
+        step(evs[st])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    per = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+    ms_step = wall * 1e3 / steps
+    per = {n: float(np.mean([evs[st][i].elapsed_time(evs[st][i + 1]) for st in range(steps)]))
            for i, n in enumerate(names)}
+    del layers, q, k, vb, o, lse, raw, idx
+    torch.cuda.empty_cache()
 
     ff = full_flops(cfg)
     fs = sparse_flops_per_layer(cfg)
-    total_flops = ff + len(layers) * fs
+    nl = len(inp.layers)
+    total_flops = ff + nl * fs
     peak = PEAK_BF16 if cfg.dtype == "bf16" else PEAK_F32
-    sparse_ms = float(np.mean([per[n] for n in names[2:]]))
-    # dominant kernel by time per step
-    if per["full_attn"] >= sparse_ms * len(layers):
-        dom, dom_ms, dom_flops, dom_kernel = "full_attn", per["full_attn"], ff, "full_prefill_kernel"
+    sparse_ms = float(np.mean([per[n] for n in names[2:]])) if nl else 0.0
+    # dominant kernel: the one taking most of the step
+    if per["full_attn"] >= sparse_ms * nl:
+        dom_ms, dom_flops, dom_kernel = per["full_attn"], ff, full_kernel_name(cfg)
     else:
-        dom, dom_ms, dom_flops, dom_kernel = "sparse_layer", sparse_ms, fs, "sparse_prefill_kernel"
+        dom_ms, dom_flops, dom_kernel = sparse_ms, fs, sparse_kernel_name(cfg)
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
-    traffic = measured_traffic(dom_kernel) if cfg.cid == 2 else None
+    return {
+        "ms_per_step": ms_step,
+        "tokens_per_s": B * T / (ms_step * 1e-3),
+        "config": {"workload": WORKLOAD_NAMES[cfg.cid],
+                   "batch": B, "seq_len": T, "hq": Hq, "hkv": Hkv, "head_dim": d,
+                   "block": 64, "topk_blocks": cfg.kb, "window": cfg.W,
+                   "sparse_layers": nl, "sinks": bool(sinks), "parallelism": "single GPU"},
+        "block_tflops": total_flops / (ms_step * 1e-3) / 1e12,
+        "block_mfma_frac": total_flops / (ms_step * 1e-3) / 1e12 / peak,
+        "kernel_ms": per,
+        "roofline": {"kernel": dom_kernel, "bound": "mfma", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": measured_traffic(cfg.cid, dom_kernel),
+                     "work_per_launch": dom_flops, "avg_launch_ms": dom_ms},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=30,
+                    help="untimed steps first; the GPU clock takes some 30 ms of load to settle")
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3])
+    ap.add_argument("--extra", type=int, nargs="*", default=[2], choices=[1, 2, 3],
+                    help="prefill workloads also timed and reported under prefill_extra")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--decode", type=int, nargs="*", default=[4, 5], choices=[4, 5],
+                    help="decode workloads also measured (default: 4 5); pass none to skip")
+    ap.add_argument("--sinks", action="store_true",
+                    help="give every sparse layer per-head sink logits (not part of the workloads)")
+    ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
+    args = ap.parse_args()
+    if args.copy_ref:
+        import torch
+
+        n = args.copy_ref << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_ref_bytes": n, "launches": 3}))
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: "
+              "the library has no multi-GPU path (prefill would shard by kv group with no "
+              "exchange between GPUs)", file=sys.stderr)
+        sys.exit(2)
+
+    from hybrid_sparse_attention_causal_amd import inputs as gen
+
+    inp = gen.make_prefill(gen.config(args.config))
+    # the oracle baseline forks a process pool: it runs before the GPU is touched
+    cpu = None if args.no_cpu else cpu_baseline(inp)
+
+    from hybrid_sparse_attention_causal_amd import binding as hb
+
+    hb.load()
+    res = bench_prefill(inp, args.steps, args.warmup, args.sinks)
+    del inp
+    cfg = gen.config(args.config)
     out = {
         "metric": METRIC,
-        "value": B * T / (ms_step * 1e-3),
+        "value": res["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded generator, planted salient keys)",
-        "config": {"workload": {2: "7B-shaped 1:3 hybrid block prefill",
-                                3: "80B-MoE-shaped 1:11 hybrid block prefill",
-                                1: "tiny 1:3 hybrid block prefill"}[cfg.cid],
-                   "batch": B, "seq_len": T, "hq": Hq, "hkv": Hkv, "head_dim": d,
-                   "block": 64, "topk_blocks": cfg.kb, "window": cfg.W,
-                   "sparse_layers": len(layers), "sinks": bool(args.sinks),
-                   "parallelism": "single GPU"},
-        "block_tflops": total_flops / (ms_step * 1e-3) / 1e12,
-        "block_mfma_frac": total_flops / (ms_step * 1e-3) / 1e12 / peak,
-        "kernel_ms": per,
-        "roofline": {"kernel": dom_kernel, "bound": "mfma", "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic},
+        "config": res["config"],
+        "block_tflops": res["block_tflops"],
+        "block_mfma_frac": res["block_mfma_frac"],
+        "kernel_ms": res["kernel_ms"],
+        "roofline": res["roofline"],
     }
+    extra = [c for c in args.extra if c != args.config]
+    if extra:
+        out["prefill_extra"] = []
+        for c in extra:
+            r = bench_prefill(gen.make_prefill(gen.config(c)), args.steps, args.warmup, args.sinks)
+            out["prefill_extra"].append(r)
     if args.decode:
-        del layers, q, k, vb, o, lse, raw, idx
-        torch.cuda.empty_cache()
         out["decode"] = [bench_decode(c, max(3, min(args.steps, 10)), args.sinks) for c in args.decode]
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(inp)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

@@ -351,6 +351,86 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeFullArgs a) {
   }
 }
 
+// ================================================= selection list as a set
+// The sparse branch attends the union of the selected blocks or tokens
+// (explainer 3.4.3 eq. K~,V~): the list is a set.  Every decode sparse work
+// group first copies its (sequence, kv head) list into LDS in a canonical
+// form: ids that are negative or not below `limit` are dropped, an id listed
+// twice counts once, and the input order does not matter.  The live ids end
+// up ascending in out[0 .. n), and n is returned to every thread.
+// hs_block_topk writes its lists ascending and duplicate-free; such a list
+// is only checked, anything else is sorted first (bitonic, in LDS).
+// buf and out hold `cap` words each, cap = the power of two >= nsel (at
+// least 64).  NTHR threads, all of which must call this.
+template <int NTHR>
+__device__ int canon_sel_list(const int32_t* il, int nsel, uint32_t limit, int cap, uint32_t* buf,
+                              uint32_t* out, int* sm_wtot) {
+  constexpr int NWV = NTHR / 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  bool unsorted = false;
+  for (int p = tid; p < cap; p += NTHR) {
+    uint32_t v = p < nsel ? (uint32_t)il[p] : 0xFFFFFFFFu;
+    buf[p] = v < limit ? v : 0xFFFFFFFFu;
+  }
+  __syncthreads();
+  for (int p = tid; p + 1 < nsel; p += NTHR) unsorted |= buf[p] > buf[p + 1];
+  if (__syncthreads_or(unsorted)) {
+    for (int k = 2; k <= cap; k <<= 1)
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < cap; i += NTHR) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const uint32_t x = buf[i], y = buf[ixj];
+            if ((x > y) == ((i & k) == 0)) {
+              buf[i] = y;
+              buf[ixj] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+  }
+  // compaction: thread tid owns entries [tid*per, tid*per + per)
+  const int per = (cap + NTHR - 1) / NTHR;
+  int cnt = 0;
+  for (int i = 0; i < per; ++i) {
+    const int p = tid * per + i;
+    if (p < cap) {
+      const uint32_t x = buf[p];
+      cnt += x != 0xFFFFFFFFu && (p == 0 || x != buf[p - 1]);
+    }
+  }
+  int inc = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(inc, o);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) sm_wtot[w] = inc;
+  __syncthreads();
+  int off = inc - cnt, n = 0;
+#pragma unroll
+  for (int ww = 0; ww < NWV; ++ww) {
+    off += ww < w ? sm_wtot[ww] : 0;
+    n += sm_wtot[ww];
+  }
+  for (int i = 0; i < per; ++i) {
+    const int p = tid * per + i;
+    if (p < cap) {
+      const uint32_t x = buf[p];
+      if (x != 0xFFFFFFFFu && (p == 0 || x != buf[p - 1])) out[off++] = x;
+    }
+  }
+  __syncthreads();
+  return n;
+}
+
+__host__ __device__ inline int sel_list_cap(int nsel) {
+  int c = 64;
+  while (c < nsel) c <<= 1;
+  return c;
+}
+
 // ============================================================ sparse layer
 // One work group (8 waves) per (b, g).  Work items: the ceil(min(L, W)/64)
 // tiles of the window ring, then the n_sel selected blocks of the shared
@@ -369,6 +449,9 @@ __global__ __launch_bounds__(512) void decode_sparse_kernel(DecodeSparseArgs a) 
   __shared__ float sm_m[NW][16], sm_l[NW][16];
   __shared__ __attribute__((aligned(16))) float sm_o[NW][16][D];
 
+  __shared__ int sm_wtot[NW];
+  extern __shared__ uint32_t dyn[];  // canonical selection list: 2 x cap words
+
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int bg = blockIdx.x;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
@@ -379,7 +462,13 @@ __global__ __launch_bounds__(512) void decode_sparse_kernel(DecodeSparseArgs a) 
   const int r16 = lane & 15, q8 = 8 * (lane >> 4), q4 = (lane >> 4) << 2;
   const int nring = a.W > 0 ? (min(L, a.W) + 63) / 64 : 0;
   const int nslots = min(L, a.W);
-  const int nitem = nring + a.nsel;
+  // live selected blocks: ids j with 64 j < L, each once, ascending
+  const int cap = sel_list_cap(a.nsel);
+  const uint32_t* sel = dyn + cap;
+  const int nlive = __builtin_amdgcn_readfirstlane(
+      canon_sel_list<64 * NW>(a.idx + (size_t)(b * a.Hkv + g) * a.nsel, a.nsel, (uint32_t)((L + 63) / 64), cap,
+                              dyn, dyn + cap, sm_wtot));
+  const int nitem = nring + nlive;
 
   Eng eng;
   eng.reset();
@@ -395,11 +484,10 @@ __global__ __launch_bounds__(512) void decode_sparse_kernel(DecodeSparseArgs a) 
   const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * (a.C / 64) * D * 64 * ES;
   const char* krg = (const char*)a.kr + (size_t)(b * a.Hkv + g) * a.W * D * ES;
   const char* vrg = (const char*)a.vr + (size_t)(b * a.Hkv + g) * ((a.W + 63) / 64) * D * 64 * ES;
-  const int32_t* il = a.idx + (size_t)(b * a.Hkv + g) * a.nsel;
 
-  // Item it < nring: ring tile it (slots 64*it ..); otherwise selected block
-  // il[it - nring] (an invalid id reads block 0 with every column switched
-  // off).  All fields are wave-uniform, so one load path serves both kinds.
+  // Item it < nring: ring tile it (slots 64*it ..); otherwise live selected
+  // block sel[it - nring].  All fields are wave-uniform, so one load path
+  // serves both kinds.
   struct Item {
     const char* kp;  // first key row of the tile
     const char* vp;  // [D][64] value slab of the tile
@@ -419,9 +507,9 @@ __global__ __launch_bounds__(512) void decode_sparse_kernel(DecodeSparseArgs a) 
       r.kbase = 64 * it;
       r.hi = nslots - 1;
     } else {
-      const int j0 = __builtin_amdgcn_readfirstlane(il[it - nring]);
-      r.on = j0 >= 0 && 64 * j0 < L;
-      const int j = r.on ? j0 : 0;
+      // it < nitem whenever the item is used; a clamped read otherwise
+      const int j = nlive > 0 ? __builtin_amdgcn_readfirstlane((int)sel[min(it - nring, nlive - 1)]) : 0;
+      r.on = nlive > 0;
       r.kp = kg + (size_t)64 * j * D * ES;
       r.vp = vg + (size_t)j * D * 64 * ES;
       r.rows = 64;
@@ -924,6 +1012,8 @@ __global__ __launch_bounds__(512) void decode_sparse_token_kernel(DecodeSparseAr
   constexpr int NW = 8;
   __shared__ float sm_m[NW][16], sm_l[NW][16];
   __shared__ __attribute__((aligned(16))) float sm_o[NW][16][D];
+  __shared__ int sm_wtot[NW];
+  extern __shared__ uint32_t dyn[];  // canonical selection list: 2 x cap words
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int bg = blockIdx.x;
@@ -935,6 +1025,11 @@ __global__ __launch_bounds__(512) void decode_sparse_token_kernel(DecodeSparseAr
   const int r16 = lane & 15, q8 = 8 * (lane >> 4), q4 = (lane >> 4) << 2;
   const float sk = a.kv_scale[g], sv = a.kv_scale[a.Hkv + g];
   const float sc2 = a.sc2 * sk;
+  // live selected tokens: ids i < L, each once, ascending
+  const int cap = sel_list_cap(a.nsel);
+  const uint32_t* sel = dyn + cap;
+  const int nlive = canon_sel_list<64 * NW>(a.idx + (size_t)(b * a.Hkv + g) * a.nsel, a.nsel, (uint32_t)L, cap,
+                                            dyn, dyn + cap, sm_wtot);
 
   Eng eng;
   eng.reset();
@@ -945,23 +1040,20 @@ __global__ __launch_bounds__(512) void decode_sparse_token_kernel(DecodeSparseAr
   }
   const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * a.C * D;
   const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * a.C * D;
-  const int32_t* il = a.idx + (size_t)(b * a.Hkv + g) * a.nsel;
-  const int ntile = (a.nsel + 63) / 64;
+  const int ntile = (nlive + 63) / 64;
   float bmax[1], bsum[1];
   int lo[1], hi[1];
 
   // work group blockIdx.y of gridDim.y takes every gridDim.y-th group of
-  // eight tiles.  All of a tile's gathered rows are requested at once, with
-  // unconditional loads (a padding entry reads token 0; its logit is masked
-  // and its values zeroed by selects): a load under a per-lane branch would
-  // make the compiler wait for each one in turn.
+  // eight tiles of the live list.  All of a tile's gathered rows are
+  // requested at once, with unconditional loads (an entry past the list
+  // reads token 0; its logit is masked and its values zeroed by selects): a
+  // load under a per-lane branch would make the compiler wait for each one
+  // in turn.
   for (int it = blockIdx.y * NW + w; it < ntile; it += gridDim.y * NW) {
     const int s0 = 64 * it;
-    int tok = s0 + lane < a.nsel ? il[s0 + lane] : -1;
-    if (tok >= L) tok = -1;
-    const int nvalid = __popcll(__ballot(tok >= 0));  // valid entries form a prefix
-    if (nvalid == 0) continue;
-    const int tsafe = tok >= 0 ? tok : 0;
+    const int nvalid = min(64, nlive - s0);  // entries s0 .. s0+nvalid-1 are live
+    const int tsafe = (int)sel[s0 + min(lane, nvalid - 1)];  // lanes past the list repeat a live token
     lo[0] = col < G ? 0 : kNoKey;
     hi[0] = s0 + nvalid - 1;
     uint2 kraw[4][Eng::NS];
@@ -1103,8 +1195,9 @@ hipError_t launch_decode_full(const DecodeFullArgs& a, int D, hipStream_t s) {
 
 hipError_t launch_decode_sparse(const DecodeSparseArgs& a, int D, hipStream_t s) {
   dim3 grid((unsigned)(a.B * a.Hkv));
-  if (D == 128) hipLaunchKernelGGL(decode_sparse_kernel<128>, grid, dim3(512), 0, s, a);
-  else hipLaunchKernelGGL(decode_sparse_kernel<64>, grid, dim3(512), 0, s, a);
+  const size_t lds = 2 * (size_t)sel_list_cap(a.nsel) * sizeof(uint32_t);
+  if (D == 128) hipLaunchKernelGGL(decode_sparse_kernel<128>, grid, dim3(512), lds, s, a);
+  else hipLaunchKernelGGL(decode_sparse_kernel<64>, grid, dim3(512), lds, s, a);
   return hipGetLastError();
 }
 
@@ -1134,8 +1227,9 @@ hipError_t launch_token_topk(const TokenTopkArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_sparse_token(const DecodeSparseArgs& a, int D, hipStream_t s) {
   dim3 grid((unsigned)(a.B * a.Hkv), (unsigned)a.nsplit);
-  if (D == 128) hipLaunchKernelGGL(decode_sparse_token_kernel<128>, grid, dim3(512), 0, s, a);
-  else hipLaunchKernelGGL(decode_sparse_token_kernel<64>, grid, dim3(512), 0, s, a);
+  const size_t lds = 2 * (size_t)sel_list_cap(a.nsel) * sizeof(uint32_t);
+  if (D == 128) hipLaunchKernelGGL(decode_sparse_token_kernel<128>, grid, dim3(512), lds, s, a);
+  else hipLaunchKernelGGL(decode_sparse_token_kernel<64>, grid, dim3(512), lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   dim3 g2((unsigned)(a.B * a.Hkv));

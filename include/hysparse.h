@@ -156,7 +156,9 @@ hs_status hs_block_topk(const hs_shape* shape, const float* blk_raw, const float
  * eq. o'_t, "Gated Fusion"; paper 3.1 and 3.3).
  *   q_sp  [batch][T][hq][head_dim]          the layer's own queries q'
  *   k, v  the full layer's K (position-major) and V (block-major), shared
- *   idx   [batch][hkv][T][topk] int32 block ids (any order, -1 = unused)
+ *   idx   [batch][hkv][T][topk] int32 block ids, read as a set per row (any
+ *         order; repeats count once; negative or j > floor(t/64) ids, and
+ *         -1 padding, are ignored)
  *   k_swa [batch][hkv][T][head_dim], v_swa [batch][hkv][nblk][head_dim][64]
  *         the layer's own window cache (NULL together with window == 0)
  *   window   W >= 0: keys t-W+1 .. t of k_swa/v_swa
@@ -185,6 +187,11 @@ hs_status hs_sparse_attn_fwd(const hs_shape* shape, const void* q_sp, const void
  *   q_sp [batch][hq][head_dim]; k, v: the full layer's caches as in
  *   hs_full_attn_fwd_scores decode mode; idx [batch][hkv][n_sel] from
  *   hs_block_topk (block ids for block = 64, token ids for block = 1).
+ *   Each idx row is read as a set (the sparse branch attends the union of
+ *   the selected blocks or tokens): the order does not matter, an id listed
+ *   more than once counts once, and ids that are negative or out of range
+ *   (block mode: 64*j >= L_b; token mode: i >= L_b) are ignored, wherever
+ *   they stand in the row.  idx may be NULL when n_sel == 0.
  *   k_ring, v_ring: the layer's own window ring [batch][hkv][W][head_dim]
  *   and [batch][hkv][ceil(W/64)][head_dim][64] (slot = position mod W), or
  *   NULL with window == 0.  gate_logits [batch][hq][2] or NULL.  sinks

@@ -119,3 +119,43 @@ def test_binding_rejects_bad_side_inputs():
                  (good_g, torch.zeros((2, Hq), dtype=torch.float64)), (good_g, torch.zeros((1, Hq)))):
         with pytest.raises(ValueError):
             hb.sparse_attn_fwd(q, k, v, idx, 2, None, None, 0, g, o, sinks=s)
+
+
+def _dshape(**kw):
+    """A decode shape whose kv_lens points at a fake (never read) address."""
+    args = dict(batch=2, q_len=1, kv_len=1024, hq=8, hkv=2, head_dim=128, dtype=hb.HS_BF16,
+                kv_lens=FAKE)
+    args.update(kw)
+    return hb.make_shape(**args)
+
+
+def _dsel(s, idx=FAKE, n_sel=4, block=64, ring=FAKE, window=64, gates=None, ptrs=FAKE, ws=None, ws_bytes=0):
+    lib = hb.load()
+    return lib.hs_decode_select_attn(ctypes.byref(s), ptrs, ptrs, ptrs, idx, n_sel, block, ring, ring,
+                                     window, gates, None, ptrs, ws, ws_bytes, None)
+
+
+def test_decode_select_validation():
+    """hs_decode_select_attn rejects bad arguments before any launch."""
+    s = _dshape()
+    assert _dsel(s, n_sel=-1) == hb.HS_ERR_INVALID_ARG
+    assert _dsel(s, n_sel=8193) == hb.HS_ERR_INVALID_ARG
+    assert _dsel(s, idx=None) == hb.HS_ERR_INVALID_ARG                 # n_sel > 0 needs idx
+    assert _dsel(s, ring=None) == hb.HS_ERR_INVALID_ARG                # window needs the ring
+    assert _dsel(s, window=-1) == hb.HS_ERR_INVALID_ARG
+    assert _dsel(s, window=2048) == hb.HS_ERR_INVALID_ARG              # window > capacity
+    assert _dsel(s, block=32) == hb.HS_ERR_INVALID_ARG
+    assert _dsel(s, block=1) == hb.HS_ERR_UNSUPPORTED                  # token mode needs fp8 caches
+    assert _dsel(s, gates=FAKE + 4) == hb.HS_ERR_INVALID_ARG           # gates misaligned
+    assert _dsel(s, ptrs=FAKE + 2) == hb.HS_ERR_INVALID_ARG            # q misaligned
+    assert _dsel(_dshape(kv_lens=None)) == hb.HS_ERR_INVALID_ARG       # decode needs kv_lens
+    assert _dsel(_dshape(kv_len=1000)) == hb.HS_ERR_INVALID_ARG        # capacity not a multiple of 64
+    assert _dsel(_dshape(q_len=2)) == hb.HS_ERR_INVALID_ARG
+    assert _dsel(_dshape(hq=64, hkv=2)) == hb.HS_ERR_UNSUPPORTED       # group of 32
+    f8 = _dshape(kv_dtype=hb.HS_FP8_E4M3, kv_scale=FAKE)
+    assert _dsel(f8, block=1, window=64) == hb.HS_ERR_INVALID_ARG      # token mode: no window
+    assert _dsel(f8, block=1, window=0, gates=FAKE) == hb.HS_ERR_INVALID_ARG  # token mode: no gate
+    assert _dsel(_dshape(kv_dtype=hb.HS_FP8_E4M3), block=1, window=0) == hb.HS_ERR_INVALID_ARG  # no scale
+    # nothing to do: no sequences
+    assert _dsel(_dshape(batch=0), ptrs=None, idx=None, ring=None) == hb.HS_OK
+    assert hb.load().hs_last_error().decode() == ""

@@ -60,15 +60,26 @@ def f64_bf16(a):
     return gen.bf16_bits_to_f32(a).astype(np.float64)
 
 
+def _pool_map(fn, items):
+    """Oracle checks of independent sequences on a thread pool (numpy releases
+    the GIL in its matrix products and random draws); one BLAS thread each."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1), ThreadPoolExecutor(min(16, len(items))) as ex:
+        return list(ex.map(fn, items))
+
+
 def check_sequences(run, seqs, gates=True):
     cfg, inp = run.cfg, run.inp
     tol = TOL["bf16"]
     o_g, lse_g, raw_g = host(run.o), host(run.lse), host(run.raw)
     idx_g, gs_g = host(run.idx), host(run.gs)
     outs_g = [host(o) for o in run.outs]
-    worst = dict(o=0.0, lse=0.0, raw=0.0, layer=0.0)
-    ties = 0
-    for b in seqs:
+
+    def one(b):
+        w = dict(o=0.0, lse=0.0, raw=0.0, layer=0.0, ties=0)
         L = int(inp.lens[b])
         ks, vs = zip(*(inp.kv_slab_f64(b, g) for g in range(cfg.Hkv)))
         k, v = np.stack(ks), np.stack(vs)
@@ -81,22 +92,27 @@ def check_sequences(run, seqs, gates=True):
                                sinks=None if run.sinks[l] is None else run.sinks[l].astype(np.float64)))
         ref = ora.decode_step(f64_bf16(inp.q[b]), k, v, L, [], cfg.kb, run.W)
         nb = (L - 1) // 64 + 1
-        worst["o"] = max(worst["o"], np.abs(o_g[b] - ref["o"]).max())
-        worst["lse"] = max(worst["lse"], np.abs(lse_g[b] - ref["lse"]).max())
-        worst["raw"] = max(worst["raw"], np.abs(raw_g[b][:, :nb] - ref["raw"][:, :nb]).max())
-        assert np.abs(gs_g[b][:, :nb] - ref["Sg"][:, :nb]).max() <= 1e-4 * ref["Sg"][:, :nb].max()
+        w["o"] = np.abs(o_g[b] - ref["o"]).max()
+        w["lse"] = np.abs(lse_g[b] - ref["lse"]).max()
+        w["raw"] = np.abs(raw_g[b][:, :nb] - ref["raw"][:, :nb]).max()
+        assert np.abs(gs_g[b][:, :nb] - ref["Sg"][:, :nb]).max() <= 1e-4 * ref["Sg"][:, :nb].max(), b
         for g in range(cfg.Hkv):
             ranked = ref["ranked"][g]
             ok, tie = check_index_row(idx_g[b, g], ref["idx"][g], ranked, cfg.kb)
             if tie:
-                ties += 1
+                w["ties"] += 1
                 cand = np.arange((L - 1) // 64)
                 ok = ok and check_index_set(idx_g[b, g], ref["Sg"][g], cand, cfg.kb, ranked)
             assert ok, (b, g, idx_g[b, g], ref["idx"][g])
         for l, lay in enumerate(layers):
             want = ora.decode_sparse_layer(lay, k, v, L, idx_g[b].astype(np.int64), run.W)
-            worst["layer"] = max(worst["layer"], np.abs(outs_g[l][b] - want).max())
-    say(f"  seqs={list(seqs)} max|dO|={worst['o']:.3g} max|dLSE|={worst['lse']:.3g} "
+            w["layer"] = max(w["layer"], np.abs(outs_g[l][b] - want).max())
+        return w
+
+    res = _pool_map(one, list(seqs))
+    worst = {key: max(r[key] for r in res) for key in ("o", "lse", "raw", "layer")}
+    ties = sum(r["ties"] for r in res)
+    say(f"  {len(res)} seqs max|dO|={worst['o']:.3g} max|dLSE|={worst['lse']:.3g} "
         f"max|draw|={worst['raw']:.3g} sparse max|dO|={worst['layer']:.3g} near-tie={ties}")
     assert worst["o"] <= tol and worst["layer"] <= tol
     assert worst["lse"] <= SIDE_TOL and worst["raw"] <= SIDE_TOL
@@ -173,11 +189,97 @@ def test_group_of_16_and_d64():
     check_sequences(run, range(3))
 
 
-def test_config4_full_size_sampled():
-    say("[config 4] 64 seqs, capacity 65536, L ~ U[32768, 65536], kb=32, W=128 (layers 0-1 of 11)")
+def test_config4_full_size_all_sequences():
+    say("[config 4] 64 seqs, capacity 65536, L ~ U[32768, 65536], kb=32, W=128 (layers 0-1 of 11), "
+        "every sequence")
     inp = gen.make_decode(gen.config(4), n_layers=2)
     run = DecodeRun(inp)
-    check_sequences(run, [0, 21, 42, 63])
+    check_sequences(run, range(64))
+
+
+def _messy_rows(clean, n_out, bad, seed):
+    """Index rows [B, Hkv, n_out] holding the same sets as `clean` (ids >= 0)
+    but shuffled, with some ids repeated and invalid ids (`bad(b)`: negative
+    or out of range) mixed in anywhere."""
+    rng = np.random.default_rng(seed)
+    B, Hkv, _ = clean.shape
+    out = np.empty((B, Hkv, n_out), np.int32)
+    for b in range(B):
+        for g in range(Hkv):
+            live = clean[b, g][clean[b, g] >= 0]
+            extra = [int(x) for x in rng.choice(live, size=min(3, live.size))] if live.size else []
+            row = list(live) + extra + list(bad(b))
+            row += [-1] * (n_out - len(row))
+            assert len(row) == n_out
+            out[b, g] = rng.permutation(np.array(row, np.int32))
+    return out
+
+
+def test_index_rows_are_sets_block_mode():
+    """The block-mode sparse layer reads each idx row as a set: a shuffled
+    row with repeated ids, -1 and out-of-range ids anywhere gives bit-for-bit
+    the output of the clean ascending row, and matches the oracle given the
+    messy row directly."""
+    say("[decode idx as a set] block mode")
+    cfg = gen.config(4, B=4, T=2048, Hq=8, Hkv=2, d=128, kb=6, W=100, N=1, L_lo=1, L_hi=2048)
+    inp = gen.make_decode(cfg)
+    inp.lens = np.array([40, 200, 1500, 2048], np.int32)
+    run = DecodeRun(inp)
+    clean = host(run.idx).astype(np.int32)
+    C = cfg.T
+    bad = lambda b: [-1, -5, (int(inp.lens[b]) + 63) // 64, C // 64 + 7, 1 << 30]
+    n_out = cfg.kb + 3 + 5 + 4
+    messy = _messy_rows(clean, n_out, bad, seed=3)
+    lay = inp.layers[0]
+    o2 = torch.full_like(run.outs[0], float("nan"))
+    hb.decode_select_attn(dev(lay["q"]), run.k, run.v, run.lens, dev(messy), n_out,
+                          dev(lay["k_ring"]), dev(gen.block_major(lay["v_ring"])), cfg.W,
+                          dev(lay["gates"]), o2)
+    torch.cuda.synchronize()
+    a, b2 = host(run.outs[0]), host(o2)
+    say(f"  messy vs clean rows: max|dO|={np.abs(a - b2).max():.3g}")
+    assert np.array_equal(a, b2)
+    for b in range(cfg.B):
+        L = int(inp.lens[b])
+        ks, vs = zip(*(inp.kv_slab_f64(b, g) for g in range(cfg.Hkv)))
+        want = ora.decode_sparse_layer(dict(q=f64_bf16(lay["q"][b]), k_ring=f64_bf16(lay["k_ring"][b]),
+                                            v_ring=f64_bf16(lay["v_ring"][b]),
+                                            gates=lay["gates"][b].astype(np.float64)),
+                                       np.stack(ks), np.stack(vs), L, messy[b].astype(np.int64), cfg.W)
+        assert np.abs(b2[b] - want).max() <= TOL["bf16"], b
+
+
+@pytest.mark.parametrize("W", [0, 100])
+def test_empty_selection_block_mode(W):
+    """n_sel = 0 with no index list at all: the sparse branch is empty, so
+    the layer output is the gated window branch (0 without a window)."""
+    say(f"[decode empty selection] W={W}")
+    cfg = gen.config(4, B=3, T=1024, Hq=8, Hkv=2, d=128, kb=4, W=W, N=1, L_lo=1, L_hi=1024)
+    inp = gen.make_decode(cfg)
+    inp.lens = np.array([1, 300, 1024], np.int32)
+    kc = np.empty((cfg.B, cfg.Hkv, cfg.T, cfg.d), np.uint16)
+    vc = np.empty((cfg.B, cfg.Hkv, cfg.T // 64, cfg.d, 64), np.uint16)
+    gen.fill_decode_cache(inp, kc, vc)
+    k, v = dev(kc), dev(vc)
+    lens = torch.from_numpy(inp.lens).cuda()
+    lay = inp.layers[0]
+    o = torch.full((cfg.B, cfg.Hq, cfg.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kr = dev(lay["k_ring"]) if W else None
+    vr = dev(gen.block_major(lay["v_ring"])) if W else None
+    hb.decode_select_attn(dev(lay["q"]), k, v, lens, None, 0, kr, vr, W, dev(lay["gates"]), o)
+    torch.cuda.synchronize()
+    got = host(o)
+    for b in range(cfg.B):
+        L = int(inp.lens[b])
+        want = ora.decode_sparse_layer(
+            dict(q=f64_bf16(lay["q"][b]), gates=lay["gates"][b].astype(np.float64),
+                 k_ring=f64_bf16(lay["k_ring"][b]) if W else None,
+                 v_ring=f64_bf16(lay["v_ring"][b]) if W else None),
+            np.zeros((cfg.Hkv, L, cfg.d)), np.zeros((cfg.Hkv, L, cfg.d)), L,
+            np.full((cfg.Hkv, 0), -1, np.int64), W)
+        assert np.abs(got[b] - want).max() <= TOL["bf16"], b
+    if W == 0:
+        assert np.all(got == 0)
 
 
 # --------------------------------------------------------------- token level
@@ -226,19 +328,18 @@ def check_token_sequences(run, seqs, rel=1e-4):
     o_g, lse_g, raw_g = host(run.o), host(run.lse), host(run.raw)
     idx_g, gs_g = host(run.idx), host(run.gs)
     outs_g = [host(o) for o in run.outs]
-    worst = dict(o=0.0, lse=0.0, raw=0.0, layer=0.0, gs=0.0)
-    ties = 0
-    for b in seqs:
+    scale = inp.kv_scale.astype(np.float64)
+
+    def one(b):
+        w = dict(o=0.0, lse=0.0, raw=0.0, layer=0.0, gs=0.0, ties=0)
         L = int(inp.lens[b])
         ks, vs = zip(*(inp.kv_slab(b, g) for g in range(cfg.Hkv)))
-        k, v = np.stack(ks), np.stack(vs)
-        ref = ora.decode_step(f64_bf16(inp.q[b]), k, v, L, [], kb, 0, block=1, n_recent=R,
-                              kv_scale=inp.kv_scale.astype(np.float64))
-        worst["o"] = max(worst["o"], np.abs(o_g[b] - ref["o"]).max())
-        worst["lse"] = max(worst["lse"], np.abs(lse_g[b] - ref["lse"]).max())
-        worst["raw"] = max(worst["raw"], np.abs(raw_g[b][:, :L] - ref["raw"][:, :L]).max())
-        worst["gs"] = max(worst["gs"], (np.abs(gs_g[b][:, :L] - ref["Sg"][:, :L]) /
-                                        ref["Sg"][:, :L].max()).max())
+        k, v = ora.dequantize_kv(np.stack(ks), np.stack(vs), scale, L)
+        ref = ora.decode_step(f64_bf16(inp.q[b]), k, v, L, [], kb, 0, block=1, n_recent=R)
+        w["o"] = np.abs(o_g[b] - ref["o"]).max()
+        w["lse"] = np.abs(lse_g[b] - ref["lse"]).max()
+        w["raw"] = np.abs(raw_g[b][:, :L] - ref["raw"][:, :L]).max()
+        w["gs"] = (np.abs(gs_g[b][:, :L] - ref["Sg"][:, :L]) / ref["Sg"][:, :L].max()).max()
         ncand = max(0, L - R)
         for g in range(cfg.Hkv):
             row = idx_g[b, g]
@@ -250,7 +351,7 @@ def check_token_sequences(run, seqs, rel=1e-4):
             if ncand > kb:
                 sk, sk1 = ranked[kb - 1], ranked[kb]
                 if (sk - sk1) / sk < rel:
-                    ties += 1
+                    w["ties"] += 1
                     got = row[: n_out - min(R, L)]
                     Sg = ref["Sg"][g]
                     cand = np.arange(ncand)
@@ -262,10 +363,14 @@ def check_token_sequences(run, seqs, rel=1e-4):
         for l in range(len(run.outs)):
             lay = dict(q=f64_bf16(inp.layers[l]["q"][b]),
                        sinks=None if run.sinks[l] is None else run.sinks[l].astype(np.float64))
-            want = ora.decode_sparse_layer(lay, k, v, L, idx_g[b].astype(np.int64), 0, block=1,
-                                           kv_scale=inp.kv_scale.astype(np.float64))
-            worst["layer"] = max(worst["layer"], np.abs(outs_g[l][b] - want).max())
-    say(f"  seqs={list(seqs)} max|dO|={worst['o']:.3g} max|dLSE|={worst['lse']:.3g} "
+            want = ora.decode_sparse_layer(lay, k, v, L, idx_g[b].astype(np.int64), 0, block=1)
+            w["layer"] = max(w["layer"], np.abs(outs_g[l][b] - want).max())
+        return w
+
+    res = _pool_map(one, list(seqs))
+    worst = {key: max(r[key] for r in res) for key in ("o", "lse", "raw", "layer", "gs")}
+    ties = sum(r["ties"] for r in res)
+    say(f"  {len(res)} seqs max|dO|={worst['o']:.3g} max|dLSE|={worst['lse']:.3g} "
         f"max|draw|={worst['raw']:.3g} rel|dSg|={worst['gs']:.3g} "
         f"sparse max|dO|={worst['layer']:.3g} near-tie={ties}")
     tol = TOL["fp8"]
@@ -307,11 +412,68 @@ def test_token_d64_group16():
     check_token_sequences(run, range(2))
 
 
-def test_config5_token_level_full_size_sampled():
-    say("[config 5] 16 seqs x 262144 fp8 tokens, top-2048 + 128 recent (layers 0-1 of 11)")
+def test_config5_token_level_full_size_all_sequences():
+    say("[config 5] 16 seqs x 262144 fp8 tokens, top-2048 + 128 recent (layers 0-1 of 11), "
+        "every sequence")
     inp = gen.make_decode(gen.config(5), n_layers=2)
     run = TokenRun(inp)
-    check_token_sequences(run, [0, 7, 15])
+    check_token_sequences(run, range(16))
+
+
+def test_token_many_tied_candidates():
+    """Every logit of one sequence equal (its query is zero): all old tokens
+    tie, far more than the 8192 candidates the threshold pass keeps, so the
+    pick takes the radix select over the whole row.  Ties go to the smaller
+    token id: the selection is tokens 0 .. k-1 plus the newest ones."""
+    say("[token ties] fp8, C=16384, top-2048 + 128 recent, one sequence with q = 0")
+    cfg = gen.config(5, B=2, T=16384, Hq=8, Hkv=2, d=128, kb=2048, n_recent=128, N=1,
+                     L_lo=16384, L_hi=16384)
+    inp = gen.make_decode(cfg)
+    inp.lens = np.array([16384, 12000], np.int32)
+    inp.q[0] = 0
+    run = TokenRun(inp)
+    idx = host(run.idx)
+    for g in range(cfg.Hkv):
+        want = np.concatenate([np.arange(2048), np.arange(16384 - 128, 16384)])
+        assert np.array_equal(idx[0, g], want), g
+    check_token_sequences(run, range(2))
+
+
+@pytest.mark.parametrize("split", [True, False])
+def test_index_rows_are_sets_token_mode(split):
+    """Token mode reads each idx row as a set too: shuffled, repeated,
+    negative and out-of-range (>= L) token ids give bit-for-bit the output
+    of the clean row, and match the oracle given the messy row."""
+    say(f"[decode idx as a set] token mode split={split}")
+    cfg = gen.config(5, B=3, T=8192, Hq=8, Hkv=2, d=128, kb=700, n_recent=64, N=1,
+                     L_lo=1, L_hi=8192)
+    inp = gen.make_decode(cfg)
+    inp.lens = np.array([50, 3000, 8192], np.int32)
+    ws = None if split else torch.empty(16, dtype=torch.uint8, device="cuda")
+    run = TokenRun(inp, ws=ws)
+    clean = host(run.idx).astype(np.int32)
+    bad = lambda b: [-1, -9, int(inp.lens[b]), int(inp.lens[b]) + 5, cfg.T + 100, 1 << 30]
+    n_out = cfg.kb + cfg.n_recent + 3 + 6 + 20
+    messy = _messy_rows(clean, n_out, bad, seed=4)
+    lay = inp.layers[0]
+    o2 = torch.full_like(run.outs[0], float("nan"))
+    hb.decode_select_attn(dev(lay["q"]), run.k, run.v, run.lens, dev(messy), n_out, None, None, 0,
+                          None, o2, block=1, kv_scale=run.scale, ws=ws)
+    torch.cuda.synchronize()
+    a, b2 = host(run.outs[0]), host(o2)
+    say(f"  messy vs clean rows: max|dO|={np.abs(a - b2).max():.3g}")
+    if split:
+        # the split over work groups follows the list length: equal to rounding
+        assert np.abs(a - b2).max() <= 1e-2
+    else:
+        assert np.array_equal(a, b2)
+    for b in range(cfg.B):
+        L = int(inp.lens[b])
+        ks, vs = zip(*(inp.kv_slab(b, g) for g in range(cfg.Hkv)))
+        want = ora.decode_sparse_layer(dict(q=f64_bf16(lay["q"][b])), np.stack(ks), np.stack(vs), L,
+                                       messy[b].astype(np.int64), 0, block=1,
+                                       kv_scale=inp.kv_scale.astype(np.float64))
+        assert np.abs(b2[b] - want).max() <= TOL["fp8"], b
 
 
 def test_token_split_work_groups():
