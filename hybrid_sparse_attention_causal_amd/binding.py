@@ -21,7 +21,9 @@ HS_SEL_FULLY_PAST, HS_SEL_INCLUDE_DIAG = 0, 2
 HS_FN_FULL_ATTN, HS_FN_BLOCK_TOPK, HS_FN_SPARSE_ATTN, HS_FN_DECODE_SELECT = range(4)
 
 EXPORTS = ("hs_full_attn_fwd_scores", "hs_block_topk", "hs_sparse_attn_fwd",
-           "hs_decode_select_attn", "hs_workspace_size", "hs_last_error", "hs_version")
+           "hs_decode_select_attn", "hs_decode_select_attn_static", "hs_workspace_size",
+           "hs_last_error", "hs_version")
+HS_STATIC_SCRATCH_BYTES = 8 << 20
 
 
 class HsError(RuntimeError):
@@ -73,12 +75,13 @@ def load() -> ctypes.CDLL:
     lib.hs_block_topk.argtypes = [SP, P, P, I, I, I, I, P, P, P, Z, P]
     lib.hs_sparse_attn_fwd.argtypes = [SP, P, P, P, P, I, P, P, I, P, P, P, P]
     lib.hs_decode_select_attn.argtypes = [SP, P, P, P, P, I, I, P, P, I, P, P, P, P, Z, P]
+    lib.hs_decode_select_attn_static.argtypes = [SP, P, P, P, P, I, I, P, P, I, P, P, P, P]
     lib.hs_workspace_size.argtypes = [I, SP, I, I, I]
     lib.hs_workspace_size.restype = Z
     lib.hs_last_error.restype = ctypes.c_char_p
     lib.hs_version.restype = I
     for name in ("hs_full_attn_fwd_scores", "hs_block_topk", "hs_sparse_attn_fwd",
-                 "hs_decode_select_attn"):
+                 "hs_decode_select_attn", "hs_decode_select_attn_static"):
         getattr(lib, name).restype = I
     del F
     _lib = lib
@@ -222,6 +225,19 @@ def decode_select_attn(q_sp, k, v, lens, idx, n_sel, k_ring, v_ring, window, gat
                                         _ptr(gate_logits), _ptr(sinks), _ptr(o), _ptr(ws),
                                         0 if ws is None else ws.numel(), _stream(stream)))
     return ws
+
+
+def decode_select_attn_static(q_sp, k, v, lens, idx, n_sel, k_ring, v_ring, window, gate_logits, o,
+                              block=64, kv_scale=None, scale=0.0, stream=None, sinks=None):
+    """hs_decode_select_attn_static: decode_select_attn with no workspace (the
+    library's fixed per-GPU scratch holds the token-mode split partials)."""
+    _contig(q_sp, k, v, lens, idx, k_ring, v_ring, gate_logits, sinks, o)
+    _check_f32("gate_logits", gate_logits, (q_sp.shape[0], q_sp.shape[1], 2))
+    _check_f32("sinks", sinks, (2, q_sp.shape[1]))
+    s = decode_shape(q_sp, k, lens, kv_scale, scale)
+    _check(load().hs_decode_select_attn_static(ctypes.byref(s), _ptr(q_sp), _ptr(k), _ptr(v), _ptr(idx),
+                                               n_sel, block, _ptr(k_ring), _ptr(v_ring), window,
+                                               _ptr(gate_logits), _ptr(sinks), _ptr(o), _stream(stream)))
 
 
 def version() -> int:

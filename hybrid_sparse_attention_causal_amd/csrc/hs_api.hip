@@ -4,10 +4,17 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <mutex>
 #include <string>
 
 #include "hs_internal.h"
 #include "hysparse.h"
+
+// Scratch of hs_decode_select_attn_static: a fixed device array, one copy per
+// GPU (each device loads its own copy of this code object).  Host code never
+// uses the array's name as an address: the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[HS_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -120,6 +127,33 @@ hs_status check_decode_block(const char* fn, const hs_shape* s, int block) {
   if (block == 1 && s->kv_dtype != HS_FP8_E4M3)
     return fail(HS_ERR_UNSUPPORTED, "%s: token mode needs HS_FP8_E4M3 caches", fn);
   return HS_OK;
+}
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[256];  // per device id; filled on the first call on that device
+
+hs_status static_scratch_ptr(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= 256)
+    return fail(HS_ERR_LAUNCH, "%s: no current HIP device (%s)", fn, hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(HS_ERR_LAUNCH, "%s: hipGetSymbolAddress of the static scratch failed on device %d: %s", fn,
+                  dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HS_OK;
+}
+
+// bytes of the token-mode split partial states for nsp work groups per
+// (sequence, kv head)
+size_t split_partials_bytes(const hs_shape* s, int nsp) {
+  return (size_t)s->batch * s->hkv * nsp * (s->hq / s->hkv) * (s->head_dim + 2) * sizeof(float);
 }
 
 float scale_log2(const hs_shape* s) {
@@ -360,12 +394,14 @@ hs_status hs_sparse_attn_fwd(const hs_shape* s, const void* q_sp, const void* k,
   return launched(fn, hs::launch_sparse_prefill(a, s->dtype, s->head_dim, (hipStream_t)stream));
 }
 
-hs_status hs_decode_select_attn(const hs_shape* s, const void* q_sp, const void* k, const void* v,
-                                const int32_t* idx, int n_sel, int block, const void* k_ring,
-                                const void* v_ring, int window, const float* gate_logits,
-                                const float* sinks, void* o, void* ws, size_t ws_bytes,
-                                void* stream) {
-  const char* fn = "hs_decode_select_attn";
+}  // extern "C"
+
+namespace {
+
+hs_status decode_select_impl(const char* fn, const hs_shape* s, const void* q_sp, const void* k, const void* v,
+                             const int32_t* idx, int n_sel, int block, const void* k_ring, const void* v_ring,
+                             int window, const float* gate_logits, const float* sinks, void* o, void* ws,
+                             size_t ws_bytes, bool static_scratch, void* stream) {
   hs_status st = check_decode(fn, s);
   if (st) return st;
   st = check_decode_block(fn, s, block);
@@ -413,7 +449,22 @@ hs_status hs_decode_select_attn(const hs_shape* s, const void* q_sp, const void*
     // groups (about eight 64-token tiles each) and merged by a second kernel
     const int ntile = (n_sel + 63) / 64;
     const int nsp = ntile / 8 < 1 ? 1 : (ntile / 8 > hs::kTokSplitMax ? hs::kTokSplitMax : ntile / 8);
-    if (nsp > 1 && ws && ws_bytes >= decode_select_ws(s, block)) {
+    if (static_scratch) {
+      // the split partial states go to this device's static scratch array
+      const size_t need = split_partials_bytes(s, nsp);
+      if (nsp > 1) {
+        if (need > HS_STATIC_SCRATCH_BYTES)
+          return fail(HS_ERR_WORKSPACE,
+                      "%s: this shape needs %zu bytes of scratch; the static scratch holds %zu "
+                      "(use hs_decode_select_attn with a workspace)",
+                      fn, need, (size_t)HS_STATIC_SCRATCH_BYTES);
+        void* scr = nullptr;
+        st = static_scratch_ptr(fn, &scr);
+        if (st) return st;
+        a.part = (float*)scr;
+        a.nsplit = nsp;
+      }
+    } else if (nsp > 1 && ws && ws_bytes >= decode_select_ws(s, block)) {
       if (!aligned16(ws)) return fail(HS_ERR_INVALID_ARG, "%s: ws not 16-byte aligned", fn);
       a.part = (float*)ws;
       a.nsplit = nsp;
@@ -421,6 +472,27 @@ hs_status hs_decode_select_attn(const hs_shape* s, const void* q_sp, const void*
     return launched(fn, hs::launch_decode_sparse_token(a, s->head_dim, (hipStream_t)stream));
   }
   return launched(fn, hs::launch_decode_sparse(a, s->head_dim, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+hs_status hs_decode_select_attn(const hs_shape* s, const void* q_sp, const void* k, const void* v,
+                                const int32_t* idx, int n_sel, int block, const void* k_ring,
+                                const void* v_ring, int window, const float* gate_logits,
+                                const float* sinks, void* o, void* ws, size_t ws_bytes,
+                                void* stream) {
+  return decode_select_impl("hs_decode_select_attn", s, q_sp, k, v, idx, n_sel, block, k_ring, v_ring,
+                            window, gate_logits, sinks, o, ws, ws_bytes, false, stream);
+}
+
+hs_status hs_decode_select_attn_static(const hs_shape* s, const void* q_sp, const void* k, const void* v,
+                                       const int32_t* idx, int n_sel, int block, const void* k_ring,
+                                       const void* v_ring, int window, const float* gate_logits,
+                                       const float* sinks, void* o, void* stream) {
+  return decode_select_impl("hs_decode_select_attn_static", s, q_sp, k, v, idx, n_sel, block, k_ring,
+                            v_ring, window, gate_logits, sinks, o, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

@@ -211,6 +211,27 @@ hs_status hs_decode_select_attn(const hs_shape* shape, const void* q_sp, const v
                                 const float* gate_logits, const float* sinks, void* o,
                                 void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * hs_decode_select_attn without a workspace, for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Arguments and
+ * results are those of hs_decode_select_attn.  The token-mode split partial
+ * states go to a fixed device array inside the library instead of a caller
+ * workspace: HS_STATIC_SCRATCH_BYTES per GPU, held until the process ends.
+ * Token-mode shapes whose split partials need more (about
+ * batch * hq * 8 * (head_dim + 2) * 4 bytes) return HS_ERR_WORKSPACE; block
+ * mode needs no scratch.  All calls on one GPU share that GPU's array, so
+ * calls that overlap in time on one GPU (on different streams) race; calls
+ * on one stream are ordered and safe.  The first call on a device looks up
+ * that device's copy of the array (no allocation).
+ */
+#define HS_STATIC_SCRATCH_BYTES (8u << 20)
+hs_status hs_decode_select_attn_static(const hs_shape* shape, const void* q_sp, const void* k,
+                                       const void* v, const int32_t* idx, int n_sel, int block,
+                                       const void* k_ring, const void* v_ring, int window,
+                                       const float* gate_logits, const float* sinks, void* o,
+                                       void* stream);
+
 /* Function ids for hs_workspace_size */
 #define HS_FN_FULL_ATTN 0
 #define HS_FN_BLOCK_TOPK 1
