@@ -309,6 +309,89 @@ def bench_decode(cid: int, steps: int, sinks: bool = False):
             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM, "sinks": bool(sinks)}
 
 
+PEAK_PCIE = 64.0  # GB/s, PCIe 5.0 x16 host link, one direction
+
+
+def bench_decode_offload(cid: int, steps: int, chunk: int = 8):
+    """One decode step of the block-mode workload with the full layer's cache
+    held in pinned host memory: the offload pipeline (chunked prefetch over
+    PCIe overlapped with the full layer, selection and gather of the previous
+    chunk) plus the N sparse layers on the compact cache of the selected
+    blocks.  Also times a plain host-to-device copy of the same live bytes."""
+    import torch
+
+    from hybrid_sparse_attention_causal_amd import binding as hb
+    from hybrid_sparse_attention_causal_amd import inputs as gen
+
+    cfg = gen.config(cid)
+    inp = gen.make_decode(cfg)
+    B, Hq, Hkv, C, d, kb = cfg.B, cfg.Hq, cfg.Hkv, cfg.T, cfg.d, cfg.kb
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    kt = torch.empty((B, Hkv, C, d), dtype=torch.int16, pin_memory=True)
+    vt = torch.empty((B, Hkv, C // 64, d, 64), dtype=torch.int16, pin_memory=True)
+    gen.fill_decode_cache(inp, kt.numpy().view(np.uint16), vt.numpy().view(np.uint16))
+    kt, vt = kt.view(torch.bfloat16), vt.view(torch.bfloat16)
+    lens_h = torch.from_numpy(inp.lens.astype(np.int32))
+    lens = lens_h.cuda()
+    q = dev(inp.q)
+    o = torch.empty((B, Hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq), device="cuda")
+    raw = torch.empty((B, Hq, C // 64), device="cuda")
+    idx = torch.empty((B, Hkv, kb), dtype=torch.int32, device="cuda")
+    k_sel = torch.empty((B, Hkv, kb * 64, d), dtype=torch.bfloat16, device="cuda")
+    v_sel = torch.empty((B, Hkv, kb, d, 64), dtype=torch.bfloat16, device="cuda")
+    idx_sel = torch.empty((B, Hkv, kb), dtype=torch.int32, device="cuda")
+    ws = torch.empty(hb.offload_workspace_size(q, kt, lens, chunk), dtype=torch.uint8, device="cuda")
+    layers = [dict(q=dev(l["q"]), kr=dev(l["k_ring"]), vr=dev(gen.block_major(l["v_ring"])), g=dev(l["gates"]),
+                   o=torch.empty_like(o)) for l in inp.layers]
+    stream = torch.cuda.current_stream()
+    copy_stream = torch.cuda.Stream()
+
+    def step():
+        hb.offload_full_select(q, kt, vt, lens, lens_h, o, lse, raw, kb, idx, k_sel, v_sel, idx_sel, chunk, ws,
+                               stream=stream, copy_stream=copy_stream)
+        for l in layers:
+            hb.decode_select_attn(l["q"], k_sel, v_sel, lens, idx_sel, kb, l["kr"], l["vr"], cfg.W, l["g"], l["o"],
+                                  stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    L = inp.lens.astype(np.float64)
+    live = float((L * d * 2 + np.ceil(L / 64) * 64 * d * 2).sum() * Hkv)  # live K rows + V blocks
+    # a plain copy of the same number of bytes, pinned host -> device
+    nbytes = int(live)
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    dst.copy_(src, non_blocking=True)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = c0.elapsed_time(c1)
+    resident = (k_sel.numel() + v_sel.numel()) * 2 + idx_sel.numel() * 4
+    return {"workload": "1:11 hybrid block decode, 64 seqs, L~U[32768,65536], top-32 blocks, W=128, "
+                        "full-layer cache in pinned host memory",
+            "chunk_seqs": chunk, "ms_per_step": ms, "pcie_bytes_per_step": live,
+            "pcie_GB_per_s": live / (ms * 1e-3) / 1e9, "pcie_frac": live / (ms * 1e-3) / 1e9 / PEAK_PCIE,
+            "plain_copy_GB_per_s": live / (copy_ms * 1e-3) / 1e9,
+            "gpu_bytes_selected_blocks": resident, "gpu_bytes_staging": ws.numel(),
+            "gpu_bytes_full_cache_if_resident": (kt.numel() + vt.numel()) * 2}
+
+
 WORKLOAD_NAMES = {1: "tiny 1:3 hybrid block prefill", 2: "7B-shaped 1:3 hybrid block prefill",
                   3: "80B-MoE-shaped 1:11 hybrid block prefill"}
 
@@ -414,6 +497,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode", type=int, nargs="*", default=[4, 5], choices=[4, 5],
                     help="decode workloads also measured (default: 4 5); pass none to skip")
+    ap.add_argument("--offload", type=int, nargs="*", default=[4], choices=[4],
+                    help="decode workloads also timed with the full-layer cache in host memory")
     ap.add_argument("--sinks", action="store_true",
                     help="give every sparse layer per-head sink logits (not part of the workloads)")
     ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
@@ -475,6 +560,8 @@ def main():
             out["prefill_extra"].append(r)
     if args.decode:
         out["decode"] = [bench_decode(c, max(3, min(args.steps, 10)), args.sinks) for c in args.decode]
+    if args.offload:
+        out["decode_offload"] = [bench_decode_offload(c, 3) for c in args.offload]
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)

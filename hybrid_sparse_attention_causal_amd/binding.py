@@ -21,7 +21,8 @@ HS_SEL_FULLY_PAST, HS_SEL_INCLUDE_DIAG = 0, 2
 HS_FN_FULL_ATTN, HS_FN_BLOCK_TOPK, HS_FN_SPARSE_ATTN, HS_FN_DECODE_SELECT = range(4)
 
 EXPORTS = ("hs_full_attn_fwd_scores", "hs_block_topk", "hs_sparse_attn_fwd",
-           "hs_decode_select_attn", "hs_decode_select_attn_static", "hs_workspace_size",
+           "hs_decode_select_attn", "hs_decode_select_attn_static", "hs_gather_blocks",
+           "hs_offload_full_select", "hs_offload_workspace_size", "hs_workspace_size",
            "hs_last_error", "hs_version")
 HS_STATIC_SCRATCH_BYTES = 8 << 20
 
@@ -76,12 +77,17 @@ def load() -> ctypes.CDLL:
     lib.hs_sparse_attn_fwd.argtypes = [SP, P, P, P, P, I, P, P, I, P, P, P, P]
     lib.hs_decode_select_attn.argtypes = [SP, P, P, P, P, I, I, P, P, I, P, P, P, P, Z, P]
     lib.hs_decode_select_attn_static.argtypes = [SP, P, P, P, P, I, I, P, P, I, P, P, P, P]
+    lib.hs_gather_blocks.argtypes = [SP, P, P, P, I, P, P, P, P]
+    lib.hs_offload_full_select.argtypes = [SP, P, P, P, P, P, P, P, I, P, P, P, P, I, P, Z, P, P]
+    lib.hs_offload_workspace_size.argtypes = [SP, I]
+    lib.hs_offload_workspace_size.restype = Z
     lib.hs_workspace_size.argtypes = [I, SP, I, I, I]
     lib.hs_workspace_size.restype = Z
     lib.hs_last_error.restype = ctypes.c_char_p
     lib.hs_version.restype = I
     for name in ("hs_full_attn_fwd_scores", "hs_block_topk", "hs_sparse_attn_fwd",
-                 "hs_decode_select_attn", "hs_decode_select_attn_static"):
+                 "hs_decode_select_attn", "hs_decode_select_attn_static", "hs_gather_blocks",
+                 "hs_offload_full_select"):
         getattr(lib, name).restype = I
     del F
     _lib = lib
@@ -238,6 +244,38 @@ def decode_select_attn_static(q_sp, k, v, lens, idx, n_sel, k_ring, v_ring, wind
     _check(load().hs_decode_select_attn_static(ctypes.byref(s), _ptr(q_sp), _ptr(k), _ptr(v), _ptr(idx),
                                                n_sel, block, _ptr(k_ring), _ptr(v_ring), window,
                                                _ptr(gate_logits), _ptr(sinks), _ptr(o), _stream(stream)))
+
+
+# ------------------------------------------------------------ KV offload
+def gather_blocks(k, v, lens, idx, n_sel, k_sel, v_sel, idx_sel, stream=None):
+    """Selected blocks of a block-mode cache into a compact cache.  k [B,Hkv,C,d],
+    v [B,Hkv,C/64,d,64]; idx [B,Hkv,n_sel]; k_sel [B,Hkv,n_sel*64,d],
+    v_sel [B,Hkv,n_sel,d,64], idx_sel [B,Hkv,n_sel] int32 (out)."""
+    _contig(k, v, lens, idx, k_sel, v_sel, idx_sel)
+    B, Hkv, C, d = k.shape
+    s = make_shape(B, 1, C, Hkv, Hkv, d, HS_BF16, HS_BF16, 0.0, lens, None)
+    _check(load().hs_gather_blocks(ctypes.byref(s), _ptr(k), _ptr(v), _ptr(idx), n_sel, _ptr(k_sel),
+                                   _ptr(v_sel), _ptr(idx_sel), _stream(stream)))
+
+
+def offload_workspace_size(q, k_host, lens, chunk) -> int:
+    return load().hs_offload_workspace_size(ctypes.byref(decode_shape(q, k_host, lens)), chunk)
+
+
+def offload_full_select(q, k_host, v_host, lens, lens_host, o, lse, raw, topk, idx, k_sel, v_sel, idx_sel,
+                        chunk, ws, stream=None, copy_stream=None, scale=0.0):
+    """Full layer + selection + gather over host-resident caches (pinned CPU
+    tensors k_host [B,Hkv,C,d], v_host [B,Hkv,C/64,d,64]); lens on the device
+    and lens_host (int32 CPU tensor) with the same values; ws a uint8 device
+    tensor of offload_workspace_size bytes."""
+    _contig(q, k_host, v_host, lens, lens_host, o, lse, raw, idx, k_sel, v_sel, idx_sel, ws)
+    if lens_host.dtype != torch.int32 or lens_host.device.type != "cpu":
+        raise ValueError("lens_host must be an int32 CPU tensor")
+    s = decode_shape(q, k_host, lens, None, scale)
+    cs = _stream(copy_stream) if copy_stream is not None else None
+    _check(load().hs_offload_full_select(ctypes.byref(s), _ptr(lens_host), _ptr(q), _ptr(k_host), _ptr(v_host),
+                                         _ptr(o), _ptr(lse), _ptr(raw), topk, _ptr(idx), _ptr(k_sel), _ptr(v_sel),
+                                         _ptr(idx_sel), chunk, _ptr(ws), ws.numel(), _stream(stream), cs))
 
 
 def version() -> int:

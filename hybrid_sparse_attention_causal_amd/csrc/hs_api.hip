@@ -156,6 +156,15 @@ size_t split_partials_bytes(const hs_shape* s, int nsp) {
   return (size_t)s->batch * s->hkv * nsp * (s->hq / s->hkv) * (s->head_dim + 2) * sizeof(float);
 }
 
+// workspace of hs_offload_full_select: two staging buffers of `chunk`
+// sequences at full capacity, then the split-K partials of one chunk
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+size_t offload_ws(const hs_shape* s, int chunk) {
+  hs_shape c = *s;
+  c.batch = chunk;
+  return 2 * align256(hs::offload_stage_bytes(chunk, s->hkv, s->kv_len, s->head_dim, 2)) + decode_full_ws(&c);
+}
+
 float scale_log2(const hs_shape* s) {
   const float tau = s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)s->head_dim);
   return tau * 1.4426950408889634f;
@@ -493,6 +502,116 @@ hs_status hs_decode_select_attn_static(const hs_shape* s, const void* q_sp, cons
                                        const float* sinks, void* o, void* stream) {
   return decode_select_impl("hs_decode_select_attn_static", s, q_sp, k, v, idx, n_sel, block, k_ring,
                             v_ring, window, gate_logits, sinks, o, nullptr, 0, true, stream);
+}
+
+hs_status hs_gather_blocks(const hs_shape* s, const void* k, const void* v, const int32_t* idx, int n_sel,
+                           void* k_sel, void* v_sel, int32_t* idx_sel, void* stream) {
+  const char* fn = "hs_gather_blocks";
+  hs_status st = check_decode(fn, s);
+  if (st) return st;
+  st = check_decode_block(fn, s, 64);
+  if (st) return st;
+  if (n_sel < 1 || n_sel > 8192) return fail(HS_ERR_INVALID_ARG, "%s: n_sel=%d (1..8192)", fn, n_sel);
+  if (s->batch == 0) return ok();
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(idx);
+  REQUIRE_PTR(k_sel);
+  REQUIRE_PTR(v_sel);
+  REQUIRE_PTR(idx_sel);
+  hs::GatherArgs g{};
+  g.k = k;
+  g.v = v;
+  g.idx = idx;
+  g.lens = s->kv_lens;
+  g.k_sel = k_sel;
+  g.v_sel = v_sel;
+  g.idx_sel = idx_sel;
+  g.B = s->batch;
+  g.Hkv = s->hkv;
+  g.C = s->kv_len;
+  g.D = s->head_dim;
+  g.nsel = n_sel;
+  g.es = 2;
+  return launched(fn, hs::launch_gather_blocks(g, (hipStream_t)stream));
+}
+
+size_t hs_offload_workspace_size(const hs_shape* shape, int chunk) {
+  if (!shape || shape->struct_size < sizeof(hs_shape) || chunk < 1 || shape->hkv <= 0) return 0;
+  return offload_ws(shape, chunk);
+}
+
+hs_status hs_offload_full_select(const hs_shape* s, const int32_t* lens_host, const void* q, const void* k_host,
+                                 const void* v_host, void* o, float* lse, float* blk_raw, int topk, int32_t* idx,
+                                 void* k_sel, void* v_sel, int32_t* idx_sel, int chunk, void* ws,
+                                 size_t ws_bytes, void* stream, void* copy_stream) {
+  const char* fn = "hs_offload_full_select";
+  hs_status st = check_decode(fn, s);
+  if (st) return st;
+  st = check_decode_block(fn, s, 64);
+  if (st) return st;
+  if (topk < 1 || topk > 1024) return fail(HS_ERR_INVALID_ARG, "%s: topk=%d (1..1024 blocks)", fn, topk);
+  if (s->kv_len / 64 > 4096) return fail(HS_ERR_UNSUPPORTED, "%s: more than 4096 candidate blocks per row", fn);
+  if (chunk < 1) return fail(HS_ERR_INVALID_ARG, "%s: chunk=%d", fn, chunk);
+  if (s->batch == 0) return ok();
+  if (!lens_host) return fail(HS_ERR_INVALID_ARG, "%s: lens_host is NULL", fn);
+  if (!k_host || !v_host) return fail(HS_ERR_INVALID_ARG, "%s: host caches are NULL", fn);
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(o);
+  REQUIRE_PTR(lse);
+  REQUIRE_PTR(blk_raw);
+  REQUIRE_PTR(idx);
+  REQUIRE_PTR(k_sel);
+  REQUIRE_PTR(v_sel);
+  REQUIRE_PTR(idx_sel);
+  if (chunk > s->batch) chunk = s->batch;
+  const size_t need = offload_ws(s, chunk);
+  if (!ws || ws_bytes < need)
+    return fail(HS_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, need, ws_bytes);
+  if (((uintptr_t)ws & 255u)) return fail(HS_ERR_INVALID_ARG, "%s: ws not 256-byte aligned", fn);
+  hs::OffloadArgs a{};
+  const size_t stage = align256(hs::offload_stage_bytes(chunk, s->hkv, s->kv_len, s->head_dim, 2));
+  a.stage[0] = ws;
+  a.stage[1] = (char*)ws + stage;
+  a.chunk = chunk;
+  a.lens_host = lens_host;
+  hs_shape cs = *s;
+  cs.batch = chunk;
+  a.full.q = q;
+  a.full.k = k_host;
+  a.full.v = v_host;
+  a.full.o = o;
+  a.full.lse = lse;
+  a.full.raw = blk_raw;
+  a.full.part = (float*)((char*)ws + 2 * stage);
+  a.full.lens = s->kv_lens;
+  a.full.B = s->batch;
+  a.full.Hq = s->hq;
+  a.full.Hkv = s->hkv;
+  a.full.C = s->kv_len;
+  a.full.nch = decode_nch(s);
+  a.full.ch_blocks = hs::decode_chunk_blocks(s->kv_len);
+  a.full.token = 0;
+  a.full.kv_dtype = HS_BF16;
+  a.full.sc2 = scale_log2(s);
+  a.topk.idx = idx;
+  a.topk.B = s->batch;
+  a.topk.Hq = s->hq;
+  a.topk.Hkv = s->hkv;
+  a.topk.R = 1;
+  a.topk.raw_stride = s->kv_len / 64;
+  a.topk.kb = topk;
+  a.topk.diag = 0;
+  a.gather.k_sel = k_sel;
+  a.gather.v_sel = v_sel;
+  a.gather.idx_sel = idx_sel;
+  a.gather.B = s->batch;
+  a.gather.Hkv = s->hkv;
+  a.gather.C = s->kv_len;
+  a.gather.D = s->head_dim;
+  a.gather.nsel = topk;
+  a.gather.es = 2;
+  return launched(fn, hs::offload_pipeline(a, s->head_dim, (hipStream_t)stream, (hipStream_t)copy_stream));
 }
 
 }  // extern "C"

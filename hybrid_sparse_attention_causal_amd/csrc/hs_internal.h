@@ -112,6 +112,36 @@ struct TokenTopkArgs {
 constexpr int kTokCap = 8192;
 constexpr int kTokSeg = 16384;  // keys per work group in the histogram and candidate passes
 
+// Gather of the selected 64-token blocks of a block-mode decode cache into a
+// compact per-(sequence, kv head) cache (explainer 3.4.3 eq. K~,V~).
+struct GatherArgs {
+  const void* k;          // [B][Hkv][C][D] keys
+  const void* v;          // [B][Hkv][C/64][D][64] values (block-major)
+  const int32_t* idx;     // [B][Hkv][nsel] block ids (read as a set)
+  const int32_t* lens;    // [B] context lengths
+  void* k_sel;            // [B][Hkv][nsel*64][D]
+  void* v_sel;            // [B][Hkv][nsel][D][64]
+  int32_t* idx_sel;       // [B][Hkv][nsel]: 0 .. n-1 for the live blocks, then -1
+  int B, Hkv, C, D, nsel;
+  int es;                 // bytes per cache element
+};
+hipError_t launch_gather_blocks(const GatherArgs& a, hipStream_t s);
+
+// One decode step's full layer over a cache held in host memory: chunks of
+// sequences are copied to one of two device staging buffers on copy_stream
+// while the full layer, the selection and the gather of the previous chunk
+// run on stream.
+struct OffloadArgs {
+  DecodeFullArgs full;    // the whole batch; k, v are the host caches, part the split-K workspace of a chunk
+  TopkArgs topk;          // the whole batch
+  GatherArgs gather;      // the whole batch; k, v are ignored (the staging buffers are read)
+  const int32_t* lens_host;
+  void* stage[2];         // each [chunk][Hkv][C][D] keys then [chunk][Hkv][C/64][D][64] values
+  int chunk;              // sequences per chunk
+};
+hipError_t offload_pipeline(const OffloadArgs& a, int D, hipStream_t s, hipStream_t copy_s);
+size_t offload_stage_bytes(int chunk, int Hkv, int C, int D, int es);
+
 hipError_t launch_token_topk(const TokenTopkArgs& a, hipStream_t s);
 hipError_t launch_decode_sparse_token(const DecodeSparseArgs& a, int D, hipStream_t s);
 

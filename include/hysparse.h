@@ -232,6 +232,51 @@ hs_status hs_decode_select_attn_static(const hs_shape* shape, const void* q_sp, 
                                        const float* gate_logits, const float* sinks, void* o,
                                        void* stream);
 
+/*
+ * Gather of the selected blocks (explainer 3.4.3 eq. K~,V~: the selected
+ * blocks' keys and values concatenated), block-mode decode caches:
+ *   k [batch][hkv][C][head_dim], v [batch][hkv][C/64][head_dim][64] (bf16),
+ *   idx [batch][hkv][n_sel] block ids, read as a set of fully-past blocks
+ *   (order free, repeats once; ids outside 0 <= j < floor((L_b-1)/64), the
+ *   block-mode decode candidates, are dropped: a gathered block is whole);
+ *   k_sel [batch][hkv][n_sel*64][head_dim], v_sel [batch][hkv][n_sel][head_dim][64]
+ *   (out): slot p < n holds the p-th live block in ascending id order;
+ *   idx_sel [batch][hkv][n_sel] (out): p for p < n, then -1.  Slots p >= n
+ *   are not written.
+ * The compact cache is a block-mode cache of capacity n_sel*64: a sparse
+ * layer over it is hs_decode_select_attn with shape.kv_len = 64*n_sel (which
+ * must be >= window), the same kv_lens, k_sel/v_sel and idx_sel, and gives
+ * the same result as over the full cache with idx.
+ */
+hs_status hs_gather_blocks(const hs_shape* shape, const void* k, const void* v, const int32_t* idx,
+                           int n_sel, void* k_sel, void* v_sel, int32_t* idx_sel, void* stream);
+
+/*
+ * One decode step's full layer, selection and gather over a full-layer cache
+ * held in host memory (paper section 5, "Potential of HySparse for Efficient
+ * KV Cache Offloading": the full layer's cache lives in external memory and
+ * is prefetched before the computation; only the selected blocks stay on
+ * the GPU for the sparse layers).  Block mode, bf16 caches.
+ *   lens_host [batch]: host copy of shape.kv_lens (sizes of the copies);
+ *   q, o, lse, blk_raw, idx: as hs_full_attn_fwd_scores + hs_block_topk in
+ *   decode mode (device); k_host, v_host: the caches in the decode layouts,
+ *   in pinned host memory; k_sel, v_sel, idx_sel: as hs_gather_blocks with
+ *   n_sel = topk (device).
+ * Sequences are processed in chunks of `chunk`: the live key rows and value
+ * blocks of chunk c+1 are copied (hipMemcpyAsync) on copy_stream into one of
+ * two device staging buffers while the full layer, the top-k and the gather
+ * of chunk c run on `stream`.  Results equal those of the device-resident
+ * calls.  ws: hs_offload_workspace_size(shape, chunk) bytes, 256-byte
+ * aligned.  copy_stream should be a second stream of default priority; all
+ * work is complete once `stream` reaches the end of what this call enqueued.
+ */
+size_t hs_offload_workspace_size(const hs_shape* shape, int chunk);
+hs_status hs_offload_full_select(const hs_shape* shape, const int32_t* lens_host, const void* q,
+                                 const void* k_host, const void* v_host, void* o, float* lse,
+                                 float* blk_raw, int topk, int32_t* idx, void* k_sel, void* v_sel,
+                                 int32_t* idx_sel, int chunk, void* ws, size_t ws_bytes, void* stream,
+                                 void* copy_stream);
+
 /* Function ids for hs_workspace_size */
 #define HS_FN_FULL_ATTN 0
 #define HS_FN_BLOCK_TOPK 1

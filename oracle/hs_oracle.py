@@ -422,3 +422,32 @@ def decode_sparse_layer(lay, k, v, L, idx, W, block=BLOCK, kv_scale=None, scale=
                                   None if sinks is None else sinks[1])
     gates = lay.get("gates")
     return gated_fusion(o_sp, o_sw, None if gates is None else gates[None])[0]
+
+
+# --------------------------------------------------------------- KV offload
+def gather_blocks(k: np.ndarray, v: np.ndarray, idx: np.ndarray, L: int, block: int = BLOCK):
+    """K~, V~ of [X] 3.4.3 ("Branch 1", eq. K~,V~) as a stored cache: the
+    selected blocks' keys and values concatenated, for one sequence.  This is
+    what stays on the GPU when the full layer's cache is offloaded ([P] 5,
+    "Potential of HySparse for Efficient KV Cache Offloading").
+
+    k, v [Hkv, >=L, d]; idx [Hkv, n] block ids, read as a set of fully-past
+    blocks, the decode candidates of reading R2 (ids 0 <= j < floor((L-1)/block),
+    each once, ascending; a gathered block is whole, so the partly visible
+    diagonal block is not kept).  Returns k_sel, v_sel [Hkv, n*block, d] (rows
+    past the live blocks are zero) and idx_sel [Hkv, n]: p for the p-th live
+    block, then -1.  A sparse branch over (k_sel, v_sel, idx_sel) at the query
+    position L-1 attends exactly the keys it attends over (k, v, idx).
+    """
+    Hkv, _, d = k.shape
+    n = idx.shape[1]
+    k_sel = np.zeros((Hkv, n * block, d))
+    v_sel = np.zeros((Hkv, n * block, d))
+    idx_sel = np.full((Hkv, n), -1, np.int64)
+    for g in range(Hkv):
+        live = np.unique(idx[g][(idx[g] >= 0) & (idx[g] < (L - 1) // block)])
+        for p, j in enumerate(live):
+            k_sel[g, p * block: (p + 1) * block] = k[g, j * block: (j + 1) * block]
+            v_sel[g, p * block: (p + 1) * block] = v[g, j * block: (j + 1) * block]
+        idx_sel[g, : live.size] = np.arange(live.size)
+    return k_sel, v_sel, idx_sel

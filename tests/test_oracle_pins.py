@@ -353,6 +353,34 @@ def pin_fp8_scales(o):
     return bool(ok)
 
 
+def pin_gather(o):
+    """The gathered cache of the selected blocks (eq. K~,V~) is what the
+    sparse branch attends: a decode sparse layer over (k_sel, v_sel, idx_sel)
+    equals the layer over the whole cache with the fully-past ids of a messy
+    list (shuffled, a repeat, -1, the diagonal block and out-of-range ids).
+    Also checked: each live block lands whole in its slot, and the slots after
+    the live ones stay 0."""
+    rng = np.random.default_rng(23)
+    Hkv, Hq, d, L, n = 2, 4, 8, 700, 9
+    k = rng.standard_normal((Hkv, L, d))
+    v = rng.standard_normal((Hkv, L, d))
+    idx = np.array([[7, 2, -1, 7, 10, 0, 3, 11, 5], [1, 4, 4, 4, -1, -1, 9, 200, 6]])
+    k_sel, v_sel, idx_sel = o.gather_blocks(k, v, idx, L)
+    lay = dict(q=rng.standard_normal((Hq, d)))
+    past = np.where(idx < (L - 1) // 64, idx, -1)     # block 10 holds the query: not fully past
+    a = ora.decode_sparse_layer(lay, k, v, L, past, 0)
+    b = ora.decode_sparse_layer(lay, k_sel, v_sel, L, idx_sel, 0)
+    ok = np.abs(a - b).max() < 1e-13
+    live = [[0, 2, 3, 5, 7], [1, 4, 6, 9]]            # ids with j < 10, each once
+    for g in range(Hkv):
+        ok = ok and list(idx_sel[g]) == list(range(len(live[g]))) + [-1] * (n - len(live[g]))
+        for p, j in enumerate(live[g]):
+            ok = ok and np.array_equal(k_sel[g, 64 * p: 64 * p + 64], k[g, 64 * j: 64 * j + 64])
+            ok = ok and np.array_equal(v_sel[g, 64 * p: 64 * p + 64], v[g, 64 * j: 64 * j + 64])
+        ok = ok and not k_sel[g, 64 * len(live[g]):].any()
+    return bool(ok)
+
+
 # ------------------------------------------------------------- the tests
 def test_e1_two_blocks():
     assert pin_e1(ora)
@@ -401,6 +429,10 @@ def test_fp8_table():
 
 def test_fp8_scales():
     assert pin_fp8_scales(ora)
+
+
+def test_gather():
+    assert pin_gather(ora)
 
 
 def test_index_order_does_not_matter():
@@ -533,6 +565,26 @@ def _scale_heads_reversed(codes, scale, head_axis=0):
     return _orig_deq(codes, np.asarray(scale)[::-1], head_axis)
 
 
+def _gather_keeps_repeats(k, v, idx, L, block=64):
+    # a repeated id gets a slot of its own (the list taken as a sequence, not a set)
+    Hkv, _, d = k.shape
+    n = idx.shape[1]
+    k_sel = np.zeros((Hkv, n * block, d))
+    v_sel = np.zeros((Hkv, n * block, d))
+    idx_sel = np.full((Hkv, n), -1, np.int64)
+    for g in range(Hkv):
+        live = np.sort(idx[g][(idx[g] >= 0) & (idx[g] < (L - 1) // block)])
+        for p, j in enumerate(live):
+            k_sel[g, p * block: (p + 1) * block] = k[g, j * block: (j + 1) * block]
+            v_sel[g, p * block: (p + 1) * block] = v[g, j * block: (j + 1) * block]
+        idx_sel[g, : live.size] = np.arange(live.size)
+    return k_sel, v_sel, idx_sel
+
+
+def _gather_shifted(k, v, idx, L, block=64):
+    return _orig_gather(k, v, np.where(idx >= 0, idx + 1, idx), L, block)
+
+
 _orig_attend = ora._attend
 _orig_window = ora.window_branch_rows
 _orig_fusion = ora.gated_fusion
@@ -542,6 +594,7 @@ _orig_fp8 = ora.decode_e4m3fn
 _orig_sparse = ora.sparse_branch_rows
 _orig_deq_kv = ora.dequantize_kv
 _orig_deq = ora.dequantize_e4m3
+_orig_gather = ora.gather_blocks
 
 
 @pytest.mark.parametrize("name,repl,pins", [
@@ -556,6 +609,8 @@ _orig_deq = ora.dequantize_e4m3
     ("sink sign flipped", dict(_attend=_sink_negated), [pin_sinks]),
     ("fp8 K and V scale rows swapped", dict(dequantize_kv=_kv_scale_rows_swapped), [pin_fp8_scales]),
     ("fp8 scale taken from the wrong head", dict(dequantize_e4m3=_scale_heads_reversed), [pin_fp8_scales]),
+    ("gather keeps a repeated block twice", dict(gather_blocks=_gather_keeps_repeats), [pin_gather]),
+    ("gather one block off", dict(gather_blocks=_gather_shifted), [pin_gather]),
 ])
 def test_planted_mistakes_fail_their_pins(name, repl, pins):
     with _Mutant(**repl) as m:
