@@ -23,6 +23,11 @@ paper's section 2.3):
   * Decode configuration 5: K, V ~ N(0,1) rounded to bf16, planted, then
     quantised to OCP fp8 e4m3 with one fp32 scale per (K or V, kv head)
     = amax/448 over that head's whole tensor.
+  * fp8 prefill (dtype 'fp8' on a prefill configuration): every tensor is
+    drawn and planted as for bf16, rounded to bf16, then quantised to e4m3
+    with one scale per head = amax/448 over that head's values: queries per
+    query head (q_scale [Hq]), K and V per kv head (kv_scale [2, Hkv]), each
+    layer's queries and window K'/V' likewise (q_scale, swa_scale).
 
 Storage formats: 'f32' -> float32 arrays, 'bf16' -> uint16 bit patterns (RNE),
 'fp8' -> uint8 e4m3fn codes plus float32 scales.
@@ -212,13 +217,30 @@ class PrefillInputs:
     k: np.ndarray                 # [B,Hkv,T,d] stored
     v: np.ndarray                 # [B,Hkv,T,d] stored
     layers: list = field(default_factory=list)  # per sparse layer dict q,k,v,gates
+                                                 # (+ q_scale, swa_scale for fp8)
     salient: list = field(default_factory=list)  # per batch index arrays
+    q_scale: np.ndarray | None = None   # fp8: [Hq] float32
+    kv_scale: np.ndarray | None = None  # fp8: [2, Hkv] float32
 
     def f64(self, name: str, layer: int | None = None) -> np.ndarray:
+        """Stored values as float64 (f32/bf16 storage; gates).  fp8 codes are
+        decoded by the oracle, with the scales, not here."""
         src = self.layers[layer][name] if layer is not None else getattr(self, name)
         if name == "gates":
             return src.astype(np.float64)
         return to_f32(src, self.cfg.dtype).astype(np.float64)
+
+
+def _fp8_per_head(x: np.ndarray, head_axis: int):
+    """Round float32 values to bf16, then quantise to e4m3 codes with one
+    scale per index of `head_axis` = amax/448 of that head's values."""
+    x = bf16_bits_to_f32(f32_to_bf16_bits(x))
+    axes = tuple(i for i in range(x.ndim) if i != head_axis)
+    amax = np.abs(x).max(axis=axes).astype(np.float64)
+    scale = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
+    shape = [1] * x.ndim
+    shape[head_axis] = -1
+    return encode_e4m3(x / scale.reshape(shape)), scale
 
 
 def _unit_vectors(cfg: Config) -> np.ndarray:
@@ -260,8 +282,19 @@ def make_prefill(cfg: Config, n_layers: int | None = None) -> PrefillInputs:
         kl = _normal_big(cfg, 30 + l, (B, Hkv, T, d))
         vl = _normal_big(cfg, 50 + l, (B, Hkv, T, d))
         gl = _normal_big(cfg, 70 + l, (B, T, cfg.Hq, 2))
-        layers.append(dict(q=store(ql, cfg.dtype), k=store(kl, cfg.dtype),
-                           v=store(vl, cfg.dtype), gates=gl))
+        if cfg.dtype == "fp8":
+            qc, qs = _fp8_per_head(ql, 2)
+            kc, ks = _fp8_per_head(kl, 1)
+            vc, vs = _fp8_per_head(vl, 1)
+            layers.append(dict(q=qc, k=kc, v=vc, gates=gl, q_scale=qs, swa_scale=np.stack([ks, vs])))
+        else:
+            layers.append(dict(q=store(ql, cfg.dtype), k=store(kl, cfg.dtype),
+                               v=store(vl, cfg.dtype), gates=gl))
+    if cfg.dtype == "fp8":
+        qc, qs = _fp8_per_head(q, 2)
+        kc, ks = _fp8_per_head(k, 1)
+        vc, vs = _fp8_per_head(v, 1)
+        return PrefillInputs(cfg, qc, kc, vc, layers, sal, qs, np.stack([ks, vs]))
     return PrefillInputs(cfg, store(q, cfg.dtype), store(k, cfg.dtype),
                          store(v, cfg.dtype), layers, sal)
 

@@ -43,6 +43,13 @@ Readings where the pages leave a step open:
       older than the newest n_recent, which are always added and do not use
       the k budget; no window branch and no gate.  The group score is the
       same group-wise maximum of post-softmax weights.
+  R15 fp8 prefill: the queries, keys and values of the full layer, and each
+      sparse layer's queries and window K'/V', may be stored as e4m3 codes
+      with one fp32 scale per head (queries per query head, keys and values
+      per kv head).  The path computes the same definitions on the values
+      code * scale (dequantize_e4m3); rounding the probabilities to fp8 for
+      the value product is the kernels' approximation, covered by the fp8
+      tolerance, not part of the definition.
   R14 Sink biases ([P] 4.1, "Experiments Setup": per-head learnable sink
       biases in the sparse and the window branch, following gpt-oss): each
       branch's softmax takes one extra logit b_h, in the units of tau q.k,

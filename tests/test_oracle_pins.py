@@ -381,6 +381,34 @@ def pin_gather(o):
     return bool(ok)
 
 
+def pin_fp8_prefill(o):
+    """fp8 prefill (reading R15): a full layer and a sparse layer over e4m3
+    codes with one scale per query head and per kv head equal torch SDPA on
+    the values torch's float8_e4m3fn decode gives, times the scales."""
+    rng = np.random.default_rng(29)
+    T, Hq, Hkv, d = 200, 4, 2, 16
+    f8 = lambda x: torch.from_numpy(np.clip(x, -448, 448).astype(np.float32)).to(torch.float8_e4m3fn)
+    deq = lambda c: torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    qs = np.array([0.01, 0.05, 0.2, 1.5])            # per query head
+    ks = np.array([0.03, 0.4])                        # per kv head
+    vs = np.array([2.0, 0.09])
+    qc = f8(rng.standard_normal((T, Hq, d)) * 30).view(torch.uint8).numpy()
+    kc = f8(rng.standard_normal((Hkv, T, d)) * 30).view(torch.uint8).numpy()
+    vc = f8(rng.standard_normal((Hkv, T, d)) * 30).view(torch.uint8).numpy()
+    qref = deq(qc) * qs[None, :, None]
+    kref = deq(kc) * ks[:, None, None]
+    vref = deq(vc) * vs[:, None, None]
+    q = o.dequantize_e4m3(qc, qs, head_axis=1)
+    k = o.dequantize_e4m3(kc, ks, head_axis=0)
+    v = o.dequantize_e4m3(vc, vs, head_axis=0)
+    pos = np.arange(T)
+    out, _, _ = o.full_attention_rows(q[pos], pos, k, v)
+    ok = np.abs(out - _sdpa(qref, kref, vref, causal=True)).max() < 1e-12
+    idx = np.tile(np.arange(4), (Hkv, T, 1))          # every block, diagonal included
+    sp = o.sparse_branch_rows(q[pos], pos, k, v, idx)
+    return bool(ok and np.abs(sp - _sdpa(qref, kref, vref, causal=True)).max() < 1e-12)
+
+
 # ------------------------------------------------------------- the tests
 def test_e1_two_blocks():
     assert pin_e1(ora)
@@ -429,6 +457,10 @@ def test_fp8_table():
 
 def test_fp8_scales():
     assert pin_fp8_scales(ora)
+
+
+def test_fp8_prefill():
+    assert pin_fp8_prefill(ora)
 
 
 def test_gather():
@@ -608,7 +640,8 @@ _orig_gather = ora.gather_blocks
     ("sink ignored", dict(_attend=_sink_ignored), [pin_sinks]),
     ("sink sign flipped", dict(_attend=_sink_negated), [pin_sinks]),
     ("fp8 K and V scale rows swapped", dict(dequantize_kv=_kv_scale_rows_swapped), [pin_fp8_scales]),
-    ("fp8 scale taken from the wrong head", dict(dequantize_e4m3=_scale_heads_reversed), [pin_fp8_scales]),
+    ("fp8 scale taken from the wrong head", dict(dequantize_e4m3=_scale_heads_reversed),
+     [pin_fp8_scales, pin_fp8_prefill]),
     ("gather keeps a repeated block twice", dict(gather_blocks=_gather_keeps_repeats), [pin_gather]),
     ("gather one block off", dict(gather_blocks=_gather_shifted), [pin_gather]),
 ])
