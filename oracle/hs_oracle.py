@@ -458,3 +458,106 @@ def gather_blocks(k: np.ndarray, v: np.ndarray, idx: np.ndarray, L: int, block: 
             v_sel[g, p * block: (p + 1) * block] = v[g, j * block: (j + 1) * block]
         idx_sel[g, : live.size] = np.arange(live.size)
     return k_sel, v_sel, idx_sel
+
+
+# ----------------------------------------------------------------- backward
+# Training backward of the hybrid block ([P] 4.1 "Experiments Setup": the
+# models are pretrained with this architecture; [X] 3.4 "Training Pipeline":
+# the sparse layers' gradients reach W_k, W_v through the shared K/V).  The
+# selection is a discrete choice taken in the forward pass: indices are
+# inputs here and get no gradient, nor do the block scores.  Each function
+# is the chain rule of the forward definitions above, for one query row at a
+# time; dO is the gradient of the loss with respect to a layer's output.
+def _attend_bwd(s, values, keys, q, do, tau, sink=None):
+    """Gradients of o = softmax([s, sink]) . values for one query row (s = tau
+    q.keys^T over n keys, sink an extra logit with no value).  Returns dq
+    [d], dkeys [n, d], dvalues [n, d], dsink (0 without a sink).  With
+    p = softmax and o = p values: dvalues = p^T do, dp = values do,
+    ds = p (dp - do.o), dq = tau ds keys, dkeys = tau ds^T q, and the sink's
+    logit gets -p_sink do.o."""
+    n, d = values.shape
+    if n == 0 and sink is None:
+        return np.zeros(q.shape[-1]), np.zeros((0, keys.shape[-1] if keys.ndim == 2 else 0)), np.zeros((0, d)), 0.0
+    m = s.max() if n else -np.inf
+    if sink is not None:
+        m = max(m, sink)
+    e = np.exp(s - m)
+    z = e.sum() + (np.exp(sink - m) if sink is not None else 0.0)
+    p = e / z
+    o = p @ values if n else np.zeros(d)
+    delta = float(do @ o)
+    dvalues = np.outer(p, do)
+    dp = values @ do
+    ds = p * (dp - delta)
+    dq = tau * (ds @ keys) if n else np.zeros(q.shape[-1])
+    dkeys = tau * np.outer(ds, q)
+    dsink = -float(np.exp(sink - m) / z) * delta if sink is not None else 0.0
+    return dq, dkeys, dvalues, dsink
+
+
+def full_attention_bwd(q, k, v, do, scale=None):
+    """Backward of the full causal layer (eq. o_t of [X] 3.4.1).
+    q, do [T, Hq, d]; k, v [Hkv, T, d].  Returns dq [T, Hq, d], dk, dv [Hkv, T, d]."""
+    T, Hq, d = q.shape
+    Hkv = k.shape[0]
+    G = Hq // Hkv
+    tau = softmax_scale(d) if scale is None else scale
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for t in range(T):
+        for h in range(Hq):
+            g = h // G
+            s = tau * (k[g, : t + 1] @ q[t, h])
+            a, b_, c, _ = _attend_bwd(s, v[g, : t + 1], k[g, : t + 1], q[t, h], do[t, h], tau)
+            dq[t, h] = a
+            dk[g, : t + 1] += b_
+            dv[g, : t + 1] += c
+    return dq, dk, dv
+
+
+def sparse_layer_bwd(qs, k, v, idx, ks, vs, W, gates, do, block=BLOCK, scale=None, sinks=None):
+    """Backward of one sparse layer ([X] 3.4.3: block-sparse branch over the
+    shared K/V at the inherited indices, window branch over the layer's own
+    K'/V', sigmoid gates; reading R14 sinks).
+    qs, do [T, Hq, d]; k, v, ks, vs [Hkv, T, d]; idx [Hkv, T, n] (read as a
+    set, as in the forward); gates [T, Hq, 2] or None; sinks [2, Hq] or None.
+    Returns dict(dq [T,Hq,d], dk, dv [Hkv,T,d] (the shared K/V's share from
+    this layer), dks, dvs [Hkv,T,d], dgates [T,Hq,2] or None, dsinks [2,Hq]
+    or None).  With o = s0 o~ + s1 o' (s = sigmoid of the gate logits):
+    do~ = s0 do, do' = s1 do, dG0 = s0 (1 - s0) do.o~, dG1 likewise."""
+    T, Hq, d = qs.shape
+    Hkv = k.shape[0]
+    G = Hq // Hkv
+    tau = softmax_scale(d) if scale is None else scale
+    out = dict(dq=np.zeros_like(qs), dk=np.zeros_like(k), dv=np.zeros_like(v), dks=np.zeros_like(ks),
+               dvs=np.zeros_like(vs), dgates=None if gates is None else np.zeros_like(gates),
+               dsinks=None if sinks is None else np.zeros_like(sinks))
+    for t in range(T):
+        for h in range(Hq):
+            g = h // G
+            sel = idx[g, t]
+            sel = np.unique(sel[sel >= 0])
+            keys = (sel[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+            keys = keys[keys <= t]
+            win = np.arange(max(0, t - W + 1), t + 1) if W > 0 else np.arange(0)
+            b0 = None if sinks is None else sinks[0, h]
+            b1 = None if sinks is None else sinks[1, h]
+            o_sp, _ = _attend(tau * (qs[t, h] @ k[g, keys].T), v[g, keys], b0)
+            o_sw, _ = _attend(tau * (qs[t, h] @ ks[g, win].T), vs[g, win], b1)
+            s0, s1 = (1.0, 1.0) if gates is None else (sigmoid(gates[t, h, 0]), sigmoid(gates[t, h, 1]))
+            if gates is not None:
+                out["dgates"][t, h, 0] = s0 * (1 - s0) * float(do[t, h] @ o_sp)
+                out["dgates"][t, h, 1] = s1 * (1 - s1) * float(do[t, h] @ o_sw)
+            for (kk, vv, idxs, dkey, dval, gsc, sk, br) in (
+                    (k, v, keys, "dk", "dv", s0, b0, 0), (ks, vs, win, "dks", "dvs", s1, b1, 1)):
+                if idxs.size == 0 and sk is None:
+                    continue
+                sc = tau * (kk[g, idxs] @ qs[t, h])
+                a, b_, c, dsk = _attend_bwd(sc, vv[g, idxs], kk[g, idxs], qs[t, h], gsc * do[t, h], tau, sk)
+                out["dq"][t, h] += a
+                np.add.at(out[dkey][g], idxs, b_)
+                np.add.at(out[dval][g], idxs, c)
+                if sinks is not None:
+                    out["dsinks"][br, h] += dsk
+    return out

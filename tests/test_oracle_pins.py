@@ -409,6 +409,77 @@ def pin_fp8_prefill(o):
     return bool(ok and np.abs(sp - _sdpa(qref, kref, vref, causal=True)).max() < 1e-12)
 
 
+def pin_bwd_full(o):
+    """Backward of the full layer equals torch autograd through float64 SDPA
+    (causal, GQA by repeated kv heads)."""
+    rng = np.random.default_rng(31)
+    T, Hq, Hkv, d = 90, 4, 2, 8
+    q, k, v, do = (rng.standard_normal((T, Hq, d)), rng.standard_normal((Hkv, T, d)),
+                   rng.standard_normal((Hkv, T, d)), rng.standard_normal((T, Hq, d)))
+    dq, dk, dv = o.full_attention_bwd(q, k, v, do)
+    Q, K, V = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(
+        Q.permute(1, 0, 2)[None], K.repeat_interleave(Hq // Hkv, 0)[None], V.repeat_interleave(Hq // Hkv, 0)[None],
+        is_causal=True)[0].permute(1, 0, 2)
+    (out * torch.from_numpy(do)).sum().backward()
+    return max(np.abs(dq - Q.grad.numpy()).max(), np.abs(dk - K.grad.numpy()).max(),
+               np.abs(dv - V.grad.numpy()).max()) < 1e-12
+
+
+def _sparse_case(seed=37):
+    rng = np.random.default_rng(seed)
+    T, Hq, Hkv, d, W = 150, 4, 2, 4, 20
+    x = dict(qs=rng.standard_normal((T, Hq, d)), k=rng.standard_normal((Hkv, T, d)),
+             v=rng.standard_normal((Hkv, T, d)), ks=rng.standard_normal((Hkv, T, d)),
+             vs=rng.standard_normal((Hkv, T, d)), gates=rng.standard_normal((T, Hq, 2)),
+             sinks=rng.standard_normal((2, Hq)))
+    idx = np.stack([np.stack([rng.choice(max(t // 64, 1), size=2) - (t < 64) for t in range(T)])
+                    for _ in range(Hkv)])                  # repeats and -1 included
+    return x, idx, W, rng.standard_normal((T, Hq, d))
+
+
+def pin_bwd_sparse(o):
+    """Backward of a sparse layer (both branches, gates, sinks) against central
+    finite differences of the forward oracle, along one random direction per
+    input: (L(x + e u) - L(x - e u)) / 2e = <dL/dx, u> with L = sum(dO * o)."""
+    x, idx, W, do = _sparse_case()
+    T = do.shape[0]
+    pos = np.arange(T)
+
+    def loss(y):
+        out = ora.sparse_layer_rows(y["qs"], pos, y["k"], y["v"], idx, y["ks"], y["vs"], W, y["gates"],
+                                    sinks=y["sinks"])
+        return float((out * do).sum())
+
+    g = o.sparse_layer_bwd(x["qs"], x["k"], x["v"], idx, x["ks"], x["vs"], W, x["gates"], do, sinks=x["sinks"])
+    names = dict(qs="dq", k="dk", v="dv", ks="dks", vs="dvs", gates="dgates", sinks="dsinks")
+    rng = np.random.default_rng(41)
+    eps = 1e-5
+    ok = True
+    for name, gname in names.items():
+        u = rng.standard_normal(x[name].shape)
+        yp = dict(x, **{name: x[name] + eps * u})
+        ym = dict(x, **{name: x[name] - eps * u})
+        fd = (loss(yp) - loss(ym)) / (2 * eps)
+        an = float((g[gname] * u).sum())
+        ok = ok and abs(fd - an) <= 1e-6 * max(1.0, abs(an))
+    return ok
+
+
+def pin_bwd_sparse_dense(o):
+    """Every block selected (diagonal included), no window, no gate, no sink:
+    the sparse layer is dense causal attention over the shared K/V, so its
+    gradients equal the full layer's (torch autograd is behind that one)."""
+    rng = np.random.default_rng(43)
+    T, Hq, Hkv, d = 130, 4, 2, 8
+    qs, k, v, do = (rng.standard_normal((T, Hq, d)), rng.standard_normal((Hkv, T, d)),
+                    rng.standard_normal((Hkv, T, d)), rng.standard_normal((T, Hq, d)))
+    idx = np.tile(np.arange(3), (Hkv, T, 1))
+    g = o.sparse_layer_bwd(qs, k, v, idx, k, v, 0, None, do)
+    dq, dk, dv = o.full_attention_bwd(qs, k, v, do)
+    return max(np.abs(g["dq"] - dq).max(), np.abs(g["dk"] - dk).max(), np.abs(g["dv"] - dv).max()) < 1e-12
+
+
 # ------------------------------------------------------------- the tests
 def test_e1_two_blocks():
     assert pin_e1(ora)
@@ -461,6 +532,18 @@ def test_fp8_scales():
 
 def test_fp8_prefill():
     assert pin_fp8_prefill(ora)
+
+
+def test_bwd_full():
+    assert pin_bwd_full(ora)
+
+
+def test_bwd_sparse_finite_differences():
+    assert pin_bwd_sparse(ora)
+
+
+def test_bwd_sparse_dense_case():
+    assert pin_bwd_sparse_dense(ora)
 
 
 def test_gather():
@@ -617,6 +700,29 @@ def _gather_shifted(k, v, idx, L, block=64):
     return _orig_gather(k, v, np.where(idx >= 0, idx + 1, idx), L, block)
 
 
+def _bwd_no_delta(s_, values, keys, q, do, tau, sink=None):
+    # forgets the -do.o term of ds = p (dp - do.o)
+    dq, dk, dv, dsk = _orig_attend_bwd(s_, values, keys, q, do, tau, sink)
+    n = values.shape[0]
+    if n == 0:
+        return dq, dk, dv, dsk
+    m = s_.max() if sink is None else max(s_.max(), sink)
+    e = np.exp(s_ - m)
+    z = e.sum() + (np.exp(sink - m) if sink is not None else 0.0)
+    p = e / z
+    ds = p * (values @ do)
+    return tau * (ds @ keys), tau * np.outer(ds, q), dv, dsk
+
+
+def _bwd_sparse_gate_sigma(qs, k, v, idx, ks, vs, W, gates, do, block=64, scale=None, sinks=None):
+    # gate derivative taken as sigma instead of sigma (1 - sigma)
+    out = _orig_sparse_bwd(qs, k, v, idx, ks, vs, W, gates, do, block, scale, sinks)
+    if gates is not None:
+        sg = 1.0 / (1.0 + np.exp(-gates))
+        out["dgates"] = out["dgates"] / (1.0 - sg)
+    return out
+
+
 _orig_attend = ora._attend
 _orig_window = ora.window_branch_rows
 _orig_fusion = ora.gated_fusion
@@ -627,6 +733,8 @@ _orig_sparse = ora.sparse_branch_rows
 _orig_deq_kv = ora.dequantize_kv
 _orig_deq = ora.dequantize_e4m3
 _orig_gather = ora.gather_blocks
+_orig_attend_bwd = ora._attend_bwd
+_orig_sparse_bwd = ora.sparse_layer_bwd
 
 
 @pytest.mark.parametrize("name,repl,pins", [
@@ -644,6 +752,8 @@ _orig_gather = ora.gather_blocks
      [pin_fp8_scales, pin_fp8_prefill]),
     ("gather keeps a repeated block twice", dict(gather_blocks=_gather_keeps_repeats), [pin_gather]),
     ("gather one block off", dict(gather_blocks=_gather_shifted), [pin_gather]),
+    ("backward without the -do.o term", dict(_attend_bwd=_bwd_no_delta), [pin_bwd_full, pin_bwd_sparse]),
+    ("gate derivative without (1 - sigma)", dict(sparse_layer_bwd=_bwd_sparse_gate_sigma), [pin_bwd_sparse]),
 ])
 def test_planted_mistakes_fail_their_pins(name, repl, pins):
     with _Mutant(**repl) as m:
