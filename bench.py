@@ -36,6 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16 = 2500.0  # TFLOP/s, MI355X dense bf16 MFMA
+PEAK_FP8 = 5000.0   # TFLOP/s, MI355X dense fp8 MFMA
 PEAK_F32 = 157.3    # TFLOP/s, MI355X fp32 matrix
 PEAK_HBM = 8000.0   # GB/s
 METRIC = "hybrid-block prefill tokens/s + % MFMA peak; sparse decode GB/s + % HBM peak"
@@ -73,6 +74,8 @@ def sparse_kernel_name(cfg) -> str:
     dispatch: two four-wave work groups per CU while their selection bitsets
     fit 16 KiB of LDS, else the eight-wave ping-pong kernel; fp32 with
     head_dim 128 takes the one-column-tile kernel)."""
+    if cfg.dtype == "fp8":
+        return "sparse_prefill_f8_kernel"
     if cfg.dtype == "f32" and cfg.d == 128:
         return "sparse_prefill_kernel"
     pwg = 4 * (32 // cfg.G)
@@ -83,6 +86,8 @@ def sparse_kernel_name(cfg) -> str:
 
 def full_kernel_name(cfg) -> str:
     """The kernel hs_full_attn_fwd_scores launches in prefill."""
+    if cfg.dtype == "fp8":
+        return "full_prefill_f8_kernel"
     if cfg.G <= 16 and not (cfg.dtype == "f32" and cfg.d == 128):
         return "full_prefill_pp_kernel"
     return "full_prefill_kernel"
@@ -412,12 +417,16 @@ def bench_prefill(inp, steps: int, warmup: int, sinks: bool = False):
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
-    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-    dt = hb.HS_BF16 if cfg.dtype == "bf16" else hb.HS_F32
+    f8 = cfg.dtype == "fp8"
+    tdt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    dt = {"bf16": hb.HS_BF16, "f32": hb.HS_F32, "fp8": hb.HS_FP8_E4M3}[cfg.dtype]
     q, k, vb = dev(inp.q), dev(inp.k), dev(gen.block_major(inp.v))
+    qsc = dev(inp.q_scale) if f8 else None
+    kvsc = dev(inp.kv_scale) if f8 else None
     layers = [dict(q=dev(l["q"]), k=dev(l["k"]), v=dev(gen.block_major(l["v"])),
                    g=dev(l["gates"]), o=torch.empty((B, T, Hq, d), dtype=tdt, device="cuda"),
-                   s=dev(gen.make_sinks(cfg, i)) if sinks else None)
+                   s=dev(gen.make_sinks(cfg, i)) if sinks else None,
+                   qs=dev(l["q_scale"]) if f8 else None, ss=dev(l["swa_scale"]) if f8 else None)
               for i, l in enumerate(inp.layers)]
     o = torch.empty((B, T, Hq, d), dtype=tdt, device="cuda")
     lse = torch.empty((B, Hq, T), device="cuda")
@@ -431,13 +440,13 @@ def bench_prefill(inp, steps: int, warmup: int, sinks: bool = False):
             if ev is not None:
                 ev[i].record(stream)
         mark(0)
-        hb.full_attn_fwd_scores(q, k, vb, o, lse, raw, stream=stream)
+        hb.full_attn_fwd_scores(q, k, vb, o, lse, raw, stream=stream, q_scale=qsc, kv_scale=kvsc)
         mark(1)
         hb.block_topk((B, T, Hq, Hkv, d, dt), raw, lse, cfg.kb, idx, stream=stream)
         mark(2)
         for i, l in enumerate(layers):
             hb.sparse_attn_fwd(l["q"], k, vb, idx, cfg.kb, l["k"], l["v"], cfg.W, l["g"], l["o"],
-                               stream=stream, sinks=l["s"])
+                               stream=stream, sinks=l["s"], q_scale=l["qs"], kv_scale=kvsc, swa_scale=l["ss"])
             mark(3 + i)
 
     for _ in range(warmup):
@@ -460,7 +469,7 @@ def bench_prefill(inp, steps: int, warmup: int, sinks: bool = False):
     fs = sparse_flops_per_layer(cfg)
     nl = len(inp.layers)
     total_flops = ff + nl * fs
-    peak = PEAK_BF16 if cfg.dtype == "bf16" else PEAK_F32
+    peak = {"bf16": PEAK_BF16, "f32": PEAK_F32, "fp8": PEAK_FP8}[cfg.dtype]
     sparse_ms = float(np.mean([per[n] for n in names[2:]])) if nl else 0.0
     # dominant kernel: the one taking most of the step
     if per["full_attn"] >= sparse_ms * nl:
@@ -471,12 +480,14 @@ def bench_prefill(inp, steps: int, warmup: int, sinks: bool = False):
     return {
         "ms_per_step": ms_step,
         "tokens_per_s": B * T / (ms_step * 1e-3),
-        "config": {"workload": WORKLOAD_NAMES[cfg.cid],
+        "dtype": cfg.dtype,
+        "config": {"workload": WORKLOAD_NAMES[cfg.cid] + (", fp8 e4m3 Q/K/V with per-head scales" if f8 else ""),
                    "batch": B, "seq_len": T, "hq": Hq, "hkv": Hkv, "head_dim": d,
                    "block": 64, "topk_blocks": cfg.kb, "window": cfg.W,
                    "sparse_layers": nl, "sinks": bool(sinks), "parallelism": "single GPU"},
         "block_tflops": total_flops / (ms_step * 1e-3) / 1e12,
         "block_mfma_frac": total_flops / (ms_step * 1e-3) / 1e12 / peak,
+        "mfma_peak_tflops": peak,
         "kernel_ms": per,
         "roofline": {"kernel": dom_kernel, "bound": "mfma", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak,
@@ -494,6 +505,8 @@ def main():
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3])
     ap.add_argument("--extra", type=int, nargs="*", default=[2], choices=[1, 2, 3],
                     help="prefill workloads also timed and reported under prefill_extra")
+    ap.add_argument("--fp8", type=int, nargs="*", default=[3], choices=[2, 3],
+                    help="prefill workloads also timed with fp8 e4m3 Q/K/V (fp8 matrix products)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode", type=int, nargs="*", default=[4, 5], choices=[4, 5],
                     help="decode workloads also measured (default: 4 5); pass none to skip")
@@ -558,6 +571,9 @@ def main():
         for c in extra:
             r = bench_prefill(gen.make_prefill(gen.config(c)), args.steps, args.warmup, args.sinks)
             out["prefill_extra"].append(r)
+    if args.fp8:
+        out["prefill_fp8"] = [bench_prefill(gen.make_prefill(gen.config(c, dtype="fp8")), args.steps,
+                                             args.warmup, args.sinks) for c in args.fp8]
     if args.decode:
         out["decode"] = [bench_decode(c, max(3, min(args.steps, 10)), args.sinks) for c in args.decode]
     if args.offload:

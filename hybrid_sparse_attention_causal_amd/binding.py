@@ -41,11 +41,12 @@ class Shape(ctypes.Structure):
         ("dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int),
         ("scale", ctypes.c_float),
         ("kv_lens", ctypes.c_void_p), ("kv_scale", ctypes.c_void_p),
+        ("q_scale", ctypes.c_void_p), ("swa_scale", ctypes.c_void_p),
     ]
 
 
 def make_shape(batch, q_len, kv_len, hq, hkv, head_dim, dtype, kv_dtype=None, scale=0.0,
-               kv_lens=None, kv_scale=None) -> Shape:
+               kv_lens=None, kv_scale=None, q_scale=None, swa_scale=None) -> Shape:
     s = Shape()
     s.struct_size = ctypes.sizeof(Shape)
     s.batch, s.q_len, s.kv_len = batch, q_len, kv_len
@@ -55,6 +56,8 @@ def make_shape(batch, q_len, kv_len, hq, hkv, head_dim, dtype, kv_dtype=None, sc
     s.scale = scale
     s.kv_lens = _ptr(kv_lens)
     s.kv_scale = _ptr(kv_scale)
+    s.q_scale = _ptr(q_scale)
+    s.swa_scale = _ptr(swa_scale)
     return s
 
 
@@ -133,13 +136,16 @@ def _check_f32(name, t, shape):
 
 # ------------------------------------------------------------------ prefill
 def full_attn_fwd_scores(q, k, v_blk, o, lse, blk_raw, score=HS_SCORE_MAX, scale=0.0,
-                         stream=None):
+                         stream=None, q_scale=None, kv_scale=None):
     """Prefill full layer.  q [B,T,Hq,d], k [B,Hkv,T,d], v_blk [B,Hkv,nblk,d,64];
-    outputs o [B,T,Hq,d], lse [B,Hq,T] fp32, blk_raw [B,Hq,T,nblk] fp32."""
-    _contig(q, k, v_blk, o, lse, blk_raw)
+    outputs o [B,T,Hq,d], lse [B,Hq,T] fp32, blk_raw [B,Hq,T,nblk] fp32.
+    fp8 (uint8 e4m3 codes): q_scale [Hq] and kv_scale [2,Hkv] fp32; o is bf16."""
+    _contig(q, k, v_blk, o, lse, blk_raw, q_scale, kv_scale)
     B, T, Hq, d = q.shape
     Hkv = k.shape[1]
-    s = make_shape(B, T, T, Hq, Hkv, d, dtype_code(q), scale=scale)
+    _check_f32("q_scale", q_scale, (Hq,))
+    _check_f32("kv_scale", kv_scale, (2, Hkv))
+    s = make_shape(B, T, T, Hq, Hkv, d, dtype_code(q), scale=scale, kv_scale=kv_scale, q_scale=q_scale)
     _check(load().hs_full_attn_fwd_scores(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v_blk),
                                           _ptr(o), _ptr(lse), _ptr(blk_raw), 64, score,
                                           None, 0, _stream(stream)))
@@ -158,16 +164,21 @@ def block_topk(q_shape, blk_raw, lse, topk, idx, grp_score=None, include_diag=Fa
 
 
 def sparse_attn_fwd(q_sp, k, v_blk, idx, topk, k_swa, v_swa_blk, window, gate_logits, o,
-                    scale=0.0, stream=None, sinks=None):
+                    scale=0.0, stream=None, sinks=None, q_scale=None, kv_scale=None, swa_scale=None):
     """One prefill sparse layer.  q_sp/o [B,T,Hq,d]; k [B,Hkv,T,d]; v_blk, v_swa_blk
     [B,Hkv,nblk,d,64]; idx [B,Hkv,T,topk]; k_swa [B,Hkv,T,d]; gates [B,T,Hq,2] or None;
-    sinks [2,Hq] fp32 (sparse, window branch) or None."""
-    _contig(q_sp, k, v_blk, idx, k_swa, v_swa_blk, gate_logits, sinks, o)
+    sinks [2,Hq] fp32 (sparse, window branch) or None.  fp8 codes: q_scale [Hq],
+    kv_scale [2,Hkv] (shared K, V), swa_scale [2,Hkv] (window K', V'); o is bf16."""
+    _contig(q_sp, k, v_blk, idx, k_swa, v_swa_blk, gate_logits, sinks, o, q_scale, kv_scale, swa_scale)
     B, T, Hq, d = q_sp.shape
     _check_f32("gate_logits", gate_logits, (B, T, Hq, 2))
     _check_f32("sinks", sinks, (2, Hq))
     Hkv = (k if k is not None else k_swa).shape[1]
-    s = make_shape(B, T, T, Hq, Hkv, d, dtype_code(q_sp), scale=scale)
+    _check_f32("q_scale", q_scale, (Hq,))
+    _check_f32("kv_scale", kv_scale, (2, Hkv))
+    _check_f32("swa_scale", swa_scale, (2, Hkv))
+    s = make_shape(B, T, T, Hq, Hkv, d, dtype_code(q_sp), scale=scale, kv_scale=kv_scale, q_scale=q_scale,
+                   swa_scale=swa_scale)
     _check(load().hs_sparse_attn_fwd(ctypes.byref(s), _ptr(q_sp), _ptr(k), _ptr(v_blk),
                                      _ptr(idx), topk, _ptr(k_swa), _ptr(v_swa_blk), window,
                                      _ptr(gate_logits), _ptr(sinks), _ptr(o), _stream(stream)))

@@ -2,6 +2,7 @@
 // argument validation (before anything is launched), error reporting and
 // dispatch to the kernel launchers.
 #include <math.h>
+#include <stddef.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <mutex>
@@ -44,11 +45,22 @@ bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
     if (!aligned16(p)) return fail(HS_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, #p); \
   } while (0)
 
+// hs_shape as first published ended after kv_scale; later fields are read
+// only when the caller's struct_size covers them
+constexpr size_t kShapeMinSize = offsetof(hs_shape, kv_scale) + sizeof(const float*);
+const float* shape_q_scale(const hs_shape* s) {
+  return s->struct_size >= offsetof(hs_shape, q_scale) + sizeof(const float*) ? s->q_scale : nullptr;
+}
+const float* shape_swa_scale(const hs_shape* s) {
+  return s->struct_size >= offsetof(hs_shape, swa_scale) + sizeof(const float*) ? s->swa_scale : nullptr;
+}
+bool aligned4(const void* p) { return p && ((uintptr_t)p & 3u) == 0; }
+
 // Common shape checks.  Returns HS_OK or an error (message set).
 hs_status check_shape(const char* fn, const hs_shape* s) {
   if (!s) return fail(HS_ERR_INVALID_ARG, "%s: shape is NULL", fn);
-  if (s->struct_size < sizeof(hs_shape))
-    return fail(HS_ERR_INVALID_ARG, "%s: shape.struct_size %zu < %zu", fn, s->struct_size, sizeof(hs_shape));
+  if (s->struct_size < kShapeMinSize)
+    return fail(HS_ERR_INVALID_ARG, "%s: shape.struct_size %zu < %zu", fn, s->struct_size, kShapeMinSize);
   if (s->batch < 0 || s->q_len < 0 || s->kv_len < 0)
     return fail(HS_ERR_INVALID_ARG, "%s: negative batch/q_len/kv_len", fn);
   if (s->hq <= 0 || s->hkv <= 0 || s->hq % s->hkv != 0)
@@ -72,10 +84,13 @@ hs_status check_prefill(const char* fn, const hs_shape* s) {
   if (s->kv_lens) return fail(HS_ERR_INVALID_ARG, "%s: prefill call with kv_lens set", fn);
   if (s->q_len != s->kv_len)
     return fail(HS_ERR_INVALID_ARG, "%s: prefill needs q_len == kv_len (got %d, %d)", fn, s->q_len, s->kv_len);
-  if (s->dtype != HS_F32 && s->dtype != HS_BF16)
-    return fail(HS_ERR_UNSUPPORTED, "%s: prefill dtype %d (supported: HS_F32, HS_BF16)", fn, s->dtype);
+  if (s->dtype != HS_F32 && s->dtype != HS_BF16 && s->dtype != HS_FP8_E4M3)
+    return fail(HS_ERR_UNSUPPORTED, "%s: prefill dtype %d (supported: HS_F32, HS_BF16, HS_FP8_E4M3)", fn,
+                s->dtype);
   if (s->kv_dtype != s->dtype)
     return fail(HS_ERR_UNSUPPORTED, "%s: prefill needs kv_dtype == dtype", fn);
+  if (s->dtype == HS_FP8_E4M3 && (s->head_dim != 128 || s->hq / s->hkv > 16))
+    return fail(HS_ERR_UNSUPPORTED, "%s: fp8 prefill needs head_dim 128 and hq/hkv <= 16", fn);
   return HS_OK;
 }
 
@@ -265,6 +280,13 @@ hs_status hs_full_attn_fwd_scores(const hs_shape* s, const void* q, const void* 
   a.Hkv = s->hkv;
   a.nblk = (s->q_len + 63) / 64;
   a.sc2 = scale_log2(s);
+  if (s->dtype == HS_FP8_E4M3) {
+    a.q_scale = shape_q_scale(s);
+    a.kv_scale = s->kv_scale;
+    if (!aligned4(a.q_scale) || !aligned4(a.kv_scale))
+      return fail(HS_ERR_INVALID_ARG, "%s: fp8 prefill needs shape.q_scale and shape.kv_scale", fn);
+    return launched(fn, hs::launch_full_prefill_f8(a, flags == HS_SCORE_LSE, (hipStream_t)stream));
+  }
   return launched(fn, hs::launch_full_prefill(a, s->dtype, s->head_dim, flags == HS_SCORE_LSE,
                                               (hipStream_t)stream));
 }
@@ -400,6 +422,17 @@ hs_status hs_sparse_attn_fwd(const hs_shape* s, const void* q_sp, const void* k,
   a.topk = topk;
   a.W = window;
   a.sc2 = scale_log2(s);
+  if (s->dtype == HS_FP8_E4M3) {
+    a.q_scale = shape_q_scale(s);
+    a.kv_scale = s->kv_scale;
+    a.swa_scale = shape_swa_scale(s);
+    if (!aligned4(a.q_scale)) return fail(HS_ERR_INVALID_ARG, "%s: fp8 prefill needs shape.q_scale", fn);
+    if (topk > 0 && !aligned4(a.kv_scale))
+      return fail(HS_ERR_INVALID_ARG, "%s: fp8 prefill with topk > 0 needs shape.kv_scale", fn);
+    if (window > 0 && !aligned4(a.swa_scale))
+      return fail(HS_ERR_INVALID_ARG, "%s: fp8 prefill with a window needs shape.swa_scale", fn);
+    return launched(fn, hs::launch_sparse_prefill_f8(a, (hipStream_t)stream));
+  }
   return launched(fn, hs::launch_sparse_prefill(a, s->dtype, s->head_dim, (hipStream_t)stream));
 }
 

@@ -698,4 +698,33 @@ struct WaveAttn {
   }
 };
 
+// ------------------------------------------------ prefill work-group order
+// LDS fragment reads kept in flight ahead of the matrix products that use
+// them (WaveAttn::lds_mfma_order), per kernel: the deepest that measured
+// fastest without register spills (full layer: 4 spills at 4, about 1 %
+// faster; sparse layer: 6, 7 % faster than the compiler's own order)
+constexpr int kFullLA = 3;
+constexpr int kSparseLA = 6;
+
+// Work-group order for position-block kernels: block id i takes kv group
+// (sequence, group) bg = i % nbg and the rank-th latest position block, rank
+// = i / nbg.  Consecutive ids are dealt round-robin over the 8 XCDs, so with
+// nbg a multiple of 8 each XCD keeps to nbg/8 kv groups (their K/V stays in
+// its L2); with fewer groups a group's position blocks alternate over several
+// XCDs, and every XCD gets late (long) and early (short) blocks alike.  Each
+// XCD starts with the latest blocks.
+struct WgSlot {
+  int bg, pblk;
+  bool live;
+};
+__device__ __forceinline__ WgSlot wg_slot(int nbg, int npblk) {
+  const int i = blockIdx.x;
+  const int rank = i / nbg;
+  WgSlot w;
+  w.bg = i % nbg;
+  w.live = rank < npblk;
+  w.pblk = w.live ? npblk - 1 - rank : 0;
+  return w;
+}
+
 }  // namespace hs

@@ -16,6 +16,8 @@ struct FullPrefillArgs {
   float* raw;
   int B, T, Hq, Hkv, nblk;
   float sc2;  // softmax scale * log2(e)
+  const float* q_scale;   // fp8: [Hq] query scales
+  const float* kv_scale;  // fp8: [2][Hkv] key and value scales
 };
 
 struct TopkArgs {
@@ -44,6 +46,9 @@ struct SparsePrefillArgs {
   int B, T, Hq, Hkv, nblk, topk, W;
   int nwg;  // work groups (kv groups x position blocks)
   float sc2;
+  const float* q_scale;    // fp8: [Hq] scales of the layer's queries
+  const float* kv_scale;   // fp8: [2][Hkv] scales of the shared K, V
+  const float* swa_scale;  // fp8: [2][Hkv] scales of the window K', V'
 };
 
 // split-K chunking of the decode full layer: at most this many 64-key tiles
@@ -150,6 +155,9 @@ hipError_t launch_decode_sparse(const DecodeSparseArgs& a, int D, hipStream_t s)
 
 hipError_t launch_full_prefill(const FullPrefillArgs& a, int dtype, int D, int score_lse,
                                hipStream_t s);
+// fp8 e4m3 Q, K, V (head_dim 128, G <= 16): bf16 O
+hipError_t launch_full_prefill_f8(const FullPrefillArgs& a, int score_lse, hipStream_t s);
+hipError_t launch_sparse_prefill_f8(const SparsePrefillArgs& a, hipStream_t s);
 hipError_t launch_block_topk(const TopkArgs& a, int max_blocks, hipStream_t s);
 hipError_t launch_sparse_prefill(const SparsePrefillArgs& a, int dtype, int D, hipStream_t s);
 // dynamic LDS of the sparse prefill kernel (bitsets + block list)

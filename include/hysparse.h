@@ -87,6 +87,12 @@ typedef struct hs_shape {
                              rather than read past the caches.  NULL = prefill */
   const float* kv_scale;  /* fp8 caches: device [2][hkv] scales (K, V); value
                              = decoded code * scale.  NULL otherwise           */
+  /* fields below were appended; a caller whose struct_size stops before one
+     of them is read as passing NULL there */
+  const float* q_scale;   /* fp8 prefill: device [hq] scales of the queries (q
+                             of the full layer, q_sp of a sparse layer)        */
+  const float* swa_scale; /* fp8 prefill sparse layer: device [2][hkv] scales
+                             of the window cache (k_swa, v_swa)               */
 } hs_shape;
 
 /*
@@ -98,7 +104,7 @@ typedef struct hs_shape {
  *   q  [batch][T][hq][head_dim]          dtype
  *   k  [batch][hkv][T][head_dim]         dtype
  *   v  [batch][hkv][nblk][head_dim][64]  dtype (block-major)
- *   o  [batch][T][hq][head_dim]          dtype (out)
+ *   o  [batch][T][hq][head_dim]          dtype (out; bf16 for fp8 inputs)
  *   lse     [batch][hq][T] fp32 (out): log sum_{i<=t} exp(tau q_t.k_i)
  *   blk_raw [batch][hq][T][nblk] fp32 (out): for j <= floor(t/64) only,
  *           HS_SCORE_MAX: max_{i in block j, i<=t} tau q_t.k_i
@@ -117,6 +123,12 @@ typedef struct hs_shape {
  *   i < L_b.  Needs a workspace of hs_workspace_size(HS_FN_FULL_ATTN, ...)
  *   bytes (the split-K partial states).
  * `block` must be 64 in prefill and 64 or 1 in decode.
+ * fp8 prefill (dtype = kv_dtype = HS_FP8_E4M3, head_dim 128, hq/hkv <= 16):
+ *   q, k, v hold OCP e4m3 codes; the values are code * scale with
+ *   shape.q_scale [hq] for the queries and shape.kv_scale [2][hkv] for the
+ *   keys and values.  Logits are exact in fp32; the probabilities are
+ *   rounded to e4m3 for the value product (lse and blk_raw are those of the
+ *   exact logits).  o is bf16.
  */
 hs_status hs_full_attn_fwd_scores(const hs_shape* shape, const void* q, const void* k,
                                   const void* v, void* o, float* lse, float* blk_raw,

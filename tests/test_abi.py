@@ -60,7 +60,10 @@ def _full(s, block=64, flags=0, ptrs=FAKE):
     (dict(hq=6, hkv=4), hb.HS_ERR_INVALID_ARG),
     (dict(hq=12, hkv=4), hb.HS_ERR_UNSUPPORTED),      # group of 3
     (dict(head_dim=96), hb.HS_ERR_UNSUPPORTED),
-    (dict(dtype=hb.HS_FP8_E4M3), hb.HS_ERR_UNSUPPORTED),
+    (dict(dtype=hb.HS_FP8_E4M3, head_dim=64), hb.HS_ERR_UNSUPPORTED),   # fp8 prefill: head_dim 128
+    (dict(dtype=hb.HS_FP8_E4M3, hq=64, hkv=2), hb.HS_ERR_UNSUPPORTED),  # fp8 prefill: groups <= 16
+    (dict(dtype=hb.HS_FP8_E4M3), hb.HS_ERR_INVALID_ARG),                # no q_scale / kv_scale
+    (dict(dtype=hb.HS_FP8_E4M3, kv_dtype=hb.HS_BF16), hb.HS_ERR_UNSUPPORTED),
     (dict(q_len=-1), hb.HS_ERR_INVALID_ARG),
     (dict(kv_len=64), hb.HS_ERR_INVALID_ARG),          # prefill needs q_len == kv_len
     (dict(scale=float("nan")), hb.HS_ERR_INVALID_ARG),
@@ -81,6 +84,19 @@ def test_full_attn_rejects_bad_args():
     assert _full(bad) == hb.HS_ERR_INVALID_ARG
     assert hb.load().hs_full_attn_fwd_scores(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 0,
                                              None, 0, None) == hb.HS_ERR_INVALID_ARG
+
+
+def test_shape_without_appended_fields():
+    """A caller built against the first hs_shape (ending after kv_scale) is
+    accepted: the appended fields are read as NULL."""
+    s = _shape()
+    s.struct_size = hb.Shape.kv_scale.offset + ctypes.sizeof(ctypes.c_void_p)
+    s.q_scale = FAKE + 3          # garbage past the caller's struct is not read
+    assert _full(s, ptrs=None) == hb.HS_ERR_INVALID_ARG   # fails on the null q, not the struct
+    assert "q is NULL" in hb.load().hs_last_error().decode()
+    s.struct_size -= 8
+    assert _full(s) == hb.HS_ERR_INVALID_ARG
+    assert "struct_size" in hb.load().hs_last_error().decode()
 
 
 def test_empty_problem_is_a_no_op():
