@@ -19,11 +19,12 @@ HS_F32, HS_BF16, HS_FP8_E4M3 = 0, 1, 2
 HS_SCORE_MAX, HS_SCORE_LSE = 0, 1
 HS_SEL_FULLY_PAST, HS_SEL_INCLUDE_DIAG = 0, 2
 HS_FN_FULL_ATTN, HS_FN_BLOCK_TOPK, HS_FN_SPARSE_ATTN, HS_FN_DECODE_SELECT = range(4)
+HS_FN_FULL_ATTN_BWD, HS_FN_SPARSE_ATTN_BWD = 4, 5
 
 EXPORTS = ("hs_full_attn_fwd_scores", "hs_block_topk", "hs_sparse_attn_fwd",
            "hs_decode_select_attn", "hs_decode_select_attn_static", "hs_gather_blocks",
-           "hs_offload_full_select", "hs_offload_workspace_size", "hs_workspace_size",
-           "hs_last_error", "hs_version")
+           "hs_offload_full_select", "hs_offload_workspace_size", "hs_sparse_attn_fwd_train",
+           "hs_full_attn_bwd", "hs_sparse_attn_bwd", "hs_workspace_size", "hs_last_error", "hs_version")
 HS_STATIC_SCRATCH_BYTES = 8 << 20
 
 
@@ -84,13 +85,17 @@ def load() -> ctypes.CDLL:
     lib.hs_offload_full_select.argtypes = [SP, P, P, P, P, P, P, P, I, P, P, P, P, I, P, Z, P, P]
     lib.hs_offload_workspace_size.argtypes = [SP, I]
     lib.hs_offload_workspace_size.restype = Z
+    lib.hs_sparse_attn_fwd_train.argtypes = [SP, P, P, P, P, I, P, P, I, P, P, P, P, P, P]
+    lib.hs_full_attn_bwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.hs_sparse_attn_bwd.argtypes = [SP, P, P, P, P, I, P, P, I, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
     lib.hs_workspace_size.argtypes = [I, SP, I, I, I]
     lib.hs_workspace_size.restype = Z
     lib.hs_last_error.restype = ctypes.c_char_p
     lib.hs_version.restype = I
     for name in ("hs_full_attn_fwd_scores", "hs_block_topk", "hs_sparse_attn_fwd",
                  "hs_decode_select_attn", "hs_decode_select_attn_static", "hs_gather_blocks",
-                 "hs_offload_full_select"):
+                 "hs_offload_full_select", "hs_sparse_attn_fwd_train", "hs_full_attn_bwd",
+                 "hs_sparse_attn_bwd"):
         getattr(lib, name).restype = I
     del F
     _lib = lib
@@ -255,6 +260,62 @@ def decode_select_attn_static(q_sp, k, v, lens, idx, n_sel, k_ring, v_ring, wind
     _check(load().hs_decode_select_attn_static(ctypes.byref(s), _ptr(q_sp), _ptr(k), _ptr(v), _ptr(idx),
                                                n_sel, block, _ptr(k_ring), _ptr(v_ring), window,
                                                _ptr(gate_logits), _ptr(sinks), _ptr(o), _stream(stream)))
+
+
+# ------------------------------------------------------------- training
+def sparse_attn_fwd_train(q_sp, k, v_blk, idx, topk, k_swa, v_swa_blk, window, gate_logits, o, o_branch,
+                          lse_branch, scale=0.0, stream=None, sinks=None):
+    """sparse_attn_fwd (bf16) that also writes each branch's output o_branch
+    [2,B,T,Hq,d] bf16 and LSE lse_branch [2,B,Hq,T] fp32 for the backward."""
+    _contig(q_sp, k, v_blk, idx, k_swa, v_swa_blk, gate_logits, sinks, o, o_branch, lse_branch)
+    B, T, Hq, d = q_sp.shape
+    _check_f32("gate_logits", gate_logits, (B, T, Hq, 2))
+    _check_f32("sinks", sinks, (2, Hq))
+    Hkv = (k if k is not None else k_swa).shape[1]
+    s = make_shape(B, T, T, Hq, Hkv, d, dtype_code(q_sp), scale=scale)
+    _check(load().hs_sparse_attn_fwd_train(ctypes.byref(s), _ptr(q_sp), _ptr(k), _ptr(v_blk), _ptr(idx), topk,
+                                           _ptr(k_swa), _ptr(v_swa_blk), window, _ptr(gate_logits), _ptr(sinks),
+                                           _ptr(o), _ptr(o_branch), _ptr(lse_branch), _stream(stream)))
+
+
+def _bwd_ws(fn_id, s, device, ws):
+    need = load().hs_workspace_size(fn_id, ctypes.byref(s), 64, 0, 0)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return ws
+
+
+def full_attn_bwd(q, k, v_blk, o, lse, dout, dq, dk, dv, ws=None, scale=0.0, stream=None):
+    """Backward of the full layer (bf16).  dq [B,T,Hq,d], dk/dv [B,Hkv,T,d] fp32
+    (overwritten).  ws: uint8 device workspace (allocated here when None or
+    too small); returned for reuse."""
+    _contig(q, k, v_blk, o, lse, dout, dq, dk, dv)
+    B, T, Hq, d = q.shape
+    s = make_shape(B, T, T, Hq, k.shape[1], d, dtype_code(q), scale=scale)
+    ws = _bwd_ws(HS_FN_FULL_ATTN_BWD, s, q.device, ws)
+    _check(load().hs_full_attn_bwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v_blk), _ptr(o), _ptr(lse), _ptr(dout),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream(stream)))
+    return ws
+
+
+def sparse_attn_bwd(q_sp, k, v_blk, idx, topk, k_swa, v_swa_blk, window, gate_logits, sinks, o_branch,
+                    lse_branch, dout, dq, dk, dv, dk_swa, dv_swa, dgate=None, dsinks=None, ws=None, scale=0.0,
+                    stream=None):
+    """Backward of one sparse layer (bf16).  dq [B,T,Hq,d] fp32 (out); dk/dv
+    [B,Hkv,T,d] fp32 receive this layer's share ADDED; dk_swa/dv_swa
+    [B,Hkv,T,d] fp32, dgate [B,T,Hq,2], dsinks [2,Hq] (out)."""
+    _contig(q_sp, k, v_blk, idx, k_swa, v_swa_blk, gate_logits, sinks, o_branch, lse_branch, dout, dq, dk, dv,
+            dk_swa, dv_swa, dgate, dsinks)
+    B, T, Hq, d = q_sp.shape
+    Hkv = (k if k is not None else k_swa).shape[1]
+    s = make_shape(B, T, T, Hq, Hkv, d, dtype_code(q_sp), scale=scale)
+    ws = _bwd_ws(HS_FN_SPARSE_ATTN_BWD, s, q_sp.device, ws)
+    _check(load().hs_sparse_attn_bwd(ctypes.byref(s), _ptr(q_sp), _ptr(k), _ptr(v_blk), _ptr(idx), topk,
+                                     _ptr(k_swa), _ptr(v_swa_blk), window, _ptr(gate_logits), _ptr(sinks),
+                                     _ptr(o_branch), _ptr(lse_branch), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                     _ptr(dk_swa), _ptr(dv_swa), _ptr(dgate), _ptr(dsinks), _ptr(ws), ws.numel(),
+                                     _stream(stream)))
+    return ws
 
 
 # ------------------------------------------------------------ KV offload

@@ -180,6 +180,40 @@ size_t offload_ws(const hs_shape* s, int chunk) {
   return 2 * align256(hs::offload_stage_bytes(chunk, s->hkv, s->kv_len, s->head_dim, 2)) + decode_full_ws(&c);
 }
 
+// backward workspace: layout copies, per-row terms, selection bitsets
+struct BwdWs {
+  size_t kb[2], vp[2], qT, doT, delta[2], sterm[2], bits, total;
+};
+int bwd_nc(const hs_shape* s) {
+  const long cols = (long)s->q_len * (s->hq / s->hkv) + 32;
+  return (int)((cols + 63) / 64 * 64);
+}
+BwdWs bwd_ws(const hs_shape* s, bool sparse) {
+  BwdWs w{};
+  const size_t B = s->batch, T = s->q_len, D = s->head_dim, Hkv = s->hkv, Hq = s->hq;
+  const size_t nblk = (T + 63) / 64, nw32 = (nblk + 31) / 32;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const int nbr = sparse ? 2 : 1;
+  for (int i = 0; i < nbr; ++i) {
+    w.kb[i] = take(B * Hkv * nblk * D * 64 * 2);
+    w.vp[i] = take(B * Hkv * nblk * 64 * D * 2);
+  }
+  w.qT = take(B * Hkv * D * bwd_nc(s) * 2);
+  w.doT = take(B * Hkv * D * bwd_nc(s) * 2);
+  for (int i = 0; i < nbr; ++i) w.delta[i] = take(B * Hq * T * 4);
+  if (sparse) {
+    for (int i = 0; i < 2; ++i) w.sterm[i] = take(B * Hq * T * 4);
+    w.bits = take(B * Hkv * T * nw32 * 4);
+  }
+  w.total = off;
+  return w;
+}
+
 float scale_log2(const hs_shape* s) {
   const float tau = s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)s->head_dim);
   return tau * 1.4426950408889634f;
@@ -202,7 +236,10 @@ size_t hs_workspace_size(int fn_id, const hs_shape* shape, int block, int topk, 
   (void)block;
   (void)topk;
   (void)window;
-  if (!shape || shape->struct_size < sizeof(hs_shape) || !shape->kv_lens) return 0;
+  if (!shape || shape->struct_size < kShapeMinSize || shape->hkv <= 0 || shape->hq <= 0) return 0;
+  if (!shape->kv_lens && (fn_id == HS_FN_FULL_ATTN_BWD || fn_id == HS_FN_SPARSE_ATTN_BWD))
+    return bwd_ws(shape, fn_id == HS_FN_SPARSE_ATTN_BWD).total;
+  if (!shape->kv_lens) return 0;
   if (fn_id == HS_FN_FULL_ATTN) return decode_full_ws(shape);
   if (fn_id == HS_FN_BLOCK_TOPK && block == 1) return token_topk_ws(shape);
   if (fn_id == HS_FN_DECODE_SELECT) return decode_select_ws(shape, block);
@@ -378,11 +415,13 @@ hs_status hs_block_topk(const hs_shape* s, const float* blk_raw, const float* ls
   return launched(fn, hs::launch_block_topk(a, a.raw_stride, (hipStream_t)stream));
 }
 
-hs_status hs_sparse_attn_fwd(const hs_shape* s, const void* q_sp, const void* k, const void* v,
-                             const int32_t* idx, int topk, const void* k_swa, const void* v_swa,
-                             int window, const float* gate_logits, const float* sinks, void* o,
-                             void* stream) {
-  const char* fn = "hs_sparse_attn_fwd";
+}  // extern "C"
+
+namespace {
+hs_status sparse_fwd_impl(const char* fn, const hs_shape* s, const void* q_sp, const void* k, const void* v,
+                          const int32_t* idx, int topk, const void* k_swa, const void* v_swa, int window,
+                          const float* gate_logits, const float* sinks, void* o, void* o_br, float* lse_br,
+                          void* stream) {
   hs_status st = check_prefill(fn, s);
   if (st) return st;
   if (topk < 0 || topk > 1024) return fail(HS_ERR_INVALID_ARG, "%s: topk=%d (0..1024)", fn, topk);
@@ -422,6 +461,8 @@ hs_status hs_sparse_attn_fwd(const hs_shape* s, const void* q_sp, const void* k,
   a.topk = topk;
   a.W = window;
   a.sc2 = scale_log2(s);
+  a.o_br = o_br;
+  a.lse_br = lse_br;
   if (s->dtype == HS_FP8_E4M3) {
     a.q_scale = shape_q_scale(s);
     a.kv_scale = s->kv_scale;
@@ -434,6 +475,17 @@ hs_status hs_sparse_attn_fwd(const hs_shape* s, const void* q_sp, const void* k,
     return launched(fn, hs::launch_sparse_prefill_f8(a, (hipStream_t)stream));
   }
   return launched(fn, hs::launch_sparse_prefill(a, s->dtype, s->head_dim, (hipStream_t)stream));
+}
+}  // namespace
+
+extern "C" {
+
+hs_status hs_sparse_attn_fwd(const hs_shape* s, const void* q_sp, const void* k, const void* v,
+                             const int32_t* idx, int topk, const void* k_swa, const void* v_swa,
+                             int window, const float* gate_logits, const float* sinks, void* o,
+                             void* stream) {
+  return sparse_fwd_impl("hs_sparse_attn_fwd", s, q_sp, k, v, idx, topk, k_swa, v_swa, window, gate_logits, sinks,
+                         o, nullptr, nullptr, stream);
 }
 
 }  // extern "C"
@@ -645,6 +697,289 @@ hs_status hs_offload_full_select(const hs_shape* s, const int32_t* lens_host, co
   a.gather.nsel = topk;
   a.gather.es = 2;
   return launched(fn, hs::offload_pipeline(a, s->head_dim, (hipStream_t)stream, (hipStream_t)copy_stream));
+}
+
+hs_status hs_sparse_attn_fwd_train(const hs_shape* s, const void* q_sp, const void* k, const void* v,
+                                   const int32_t* idx, int topk, const void* k_swa, const void* v_swa,
+                                   int window, const float* gate_logits, const float* sinks, void* o,
+                                   void* o_branch, float* lse_branch, void* stream) {
+  const char* fn = "hs_sparse_attn_fwd_train";
+  hs_status st = check_prefill(fn, s);
+  if (st) return st;
+  if (s->dtype != HS_BF16) return fail(HS_ERR_UNSUPPORTED, "%s: training forward takes bf16", fn);
+  if (s->batch == 0 || s->q_len == 0) return ok();
+  REQUIRE_PTR(o_branch);
+  REQUIRE_PTR(lse_branch);
+  hs::SparsePrefillArgs probe{};
+  probe.Hq = s->hq;
+  probe.Hkv = s->hkv;
+  probe.nblk = (s->q_len + 63) / 64;
+  if (!hs::sparse_prefill_dual_ok(probe, s->dtype, s->head_dim))
+    return fail(HS_ERR_UNSUPPORTED, "%s: sequence too long for the training forward", fn);
+  return sparse_fwd_impl(fn, s, q_sp, k, v, idx, topk, k_swa, v_swa, window, gate_logits, sinks, o, o_branch,
+                         lse_branch, stream);
+}
+
+hs_status hs_full_attn_bwd(const hs_shape* s, const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, float* dq, float* dk, float* dv, void* ws,
+                           size_t ws_bytes, void* stream) {
+  const char* fn = "hs_full_attn_bwd";
+  hs_status st = check_prefill(fn, s);
+  if (st) return st;
+  if (s->dtype != HS_BF16) return fail(HS_ERR_UNSUPPORTED, "%s: the backward takes bf16", fn);
+  if (s->hq / s->hkv > 16) return fail(HS_ERR_UNSUPPORTED, "%s: group size > 16", fn);
+  if (s->batch == 0 || s->q_len == 0) return ok();
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(o);
+  REQUIRE_PTR(lse);
+  REQUIRE_PTR(dout);
+  REQUIRE_PTR(dq);
+  REQUIRE_PTR(dk);
+  REQUIRE_PTR(dv);
+  const BwdWs w = bwd_ws(s, false);
+  if (!ws || ws_bytes < w.total)
+    return fail(HS_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, w.total, ws_bytes);
+  if ((uintptr_t)ws & 255u) return fail(HS_ERR_INVALID_ARG, "%s: ws not 256-byte aligned", fn);
+  if (hs::bwd_q_lds_bytes(s->q_len, s->hq / s->hkv) > 64 * 1024)
+    return fail(HS_ERR_UNSUPPORTED, "%s: sequence too long", fn);
+  char* W = (char*)ws;
+  hipStream_t strm = (hipStream_t)stream;
+  const int nblk = (s->q_len + 63) / 64;
+  hs::BwdLayoutArgs l{};
+  l.k[0] = k;
+  l.v[0] = v;
+  l.kb[0] = W + w.kb[0];
+  l.vp[0] = W + w.vp[0];
+  l.q = q;
+  l.dout = dout;
+  l.qT = W + w.qT;
+  l.doT = W + w.doT;
+  l.B = s->batch;
+  l.T = s->q_len;
+  l.Hq = s->hq;
+  l.Hkv = s->hkv;
+  l.nblk = nblk;
+  l.NC = bwd_nc(s);
+  hipError_t e = hs::launch_bwd_layouts(l, s->head_dim, strm);
+  if (e != hipSuccess) return launched(fn, e);
+  hs::BwdRowArgs r{};
+  r.o[0] = o;
+  r.dout = dout;
+  r.delta[0] = (float*)(W + w.delta[0]);
+  r.B = s->batch;
+  r.T = s->q_len;
+  r.Hq = s->hq;
+  r.D = s->head_dim;
+  r.nbr = 1;
+  e = hs::launch_bwd_rows(r, strm);
+  if (e != hipSuccess) return launched(fn, e);
+  const float tau = s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)s->head_dim);
+  hs::BwdKVArgs a{};
+  a.q = q;
+  a.dout = dout;
+  a.qT = l.qT;
+  a.doT = l.doT;
+  a.k = k;
+  a.vp = l.vp[0];
+  a.lse = lse;
+  a.delta = r.delta[0];
+  a.dk = dk;
+  a.dv = dv;
+  a.B = s->batch;
+  a.T = s->q_len;
+  a.Hq = s->hq;
+  a.Hkv = s->hkv;
+  a.nblk = nblk;
+  a.NC = l.NC;
+  a.sc2 = scale_log2(s);
+  a.tau = tau;
+  e = hs::launch_bwd_kv(a, 0, s->head_dim, strm);
+  if (e != hipSuccess) return launched(fn, e);
+  hs::BwdQArgs b{};
+  b.q = q;
+  b.dout = dout;
+  b.k0 = k;
+  b.kb0 = l.kb[0];
+  b.vp0 = l.vp[0];
+  b.lse0 = lse;
+  b.delta0 = r.delta[0];
+  b.dq = dq;
+  b.B = s->batch;
+  b.T = s->q_len;
+  b.Hq = s->hq;
+  b.Hkv = s->hkv;
+  b.nblk = nblk;
+  b.sc2 = a.sc2;
+  b.tau = tau;
+  return launched(fn, hs::launch_bwd_q(b, 0, s->head_dim, strm));
+}
+
+hs_status hs_sparse_attn_bwd(const hs_shape* s, const void* q_sp, const void* k, const void* v,
+                             const int32_t* idx, int topk, const void* k_swa, const void* v_swa, int window,
+                             const float* gate_logits, const float* sinks, const void* o_branch,
+                             const float* lse_branch, const void* dout, float* dq_sp, float* dk, float* dv,
+                             float* dk_swa, float* dv_swa, float* dgate, float* dsinks, void* ws, size_t ws_bytes,
+                             void* stream) {
+  const char* fn = "hs_sparse_attn_bwd";
+  hs_status st = check_prefill(fn, s);
+  if (st) return st;
+  if (s->dtype != HS_BF16) return fail(HS_ERR_UNSUPPORTED, "%s: the backward takes bf16", fn);
+  if (s->hq / s->hkv > 16) return fail(HS_ERR_UNSUPPORTED, "%s: group size > 16", fn);
+  if (topk < 0 || topk > 1024) return fail(HS_ERR_INVALID_ARG, "%s: topk=%d (0..1024)", fn, topk);
+  if (window < 0) return fail(HS_ERR_INVALID_ARG, "%s: window < 0", fn);
+  if (s->batch == 0 || s->q_len == 0) return ok();
+  REQUIRE_PTR(q_sp);
+  REQUIRE_PTR(o_branch);
+  REQUIRE_PTR(lse_branch);
+  REQUIRE_PTR(dout);
+  REQUIRE_PTR(dq_sp);
+  if (topk > 0) {
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(idx);
+    REQUIRE_PTR(dk);
+    REQUIRE_PTR(dv);
+  }
+  if (window > 0) {
+    REQUIRE_PTR(k_swa);
+    REQUIRE_PTR(v_swa);
+    REQUIRE_PTR(dk_swa);
+    REQUIRE_PTR(dv_swa);
+  }
+  if (gate_logits && !dgate) return fail(HS_ERR_INVALID_ARG, "%s: gate_logits given without dgate", fn);
+  if (sinks && !dsinks) return fail(HS_ERR_INVALID_ARG, "%s: sinks given without dsinks", fn);
+  const BwdWs w = bwd_ws(s, true);
+  if (!ws || ws_bytes < w.total)
+    return fail(HS_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, w.total, ws_bytes);
+  if ((uintptr_t)ws & 255u) return fail(HS_ERR_INVALID_ARG, "%s: ws not 256-byte aligned", fn);
+  if (hs::bwd_q_lds_bytes(s->q_len, s->hq / s->hkv) > 64 * 1024)
+    return fail(HS_ERR_UNSUPPORTED, "%s: sequence too long", fn);
+  char* W = (char*)ws;
+  hipStream_t strm = (hipStream_t)stream;
+  const int T = s->q_len, nblk = (T + 63) / 64;
+  const size_t brs = (size_t)s->batch * T * s->hq;  // rows of one branch
+  hs::BwdLayoutArgs l{};
+  if (topk > 0) {
+    l.k[0] = k;
+    l.v[0] = v;
+  }
+  if (window > 0) {
+    l.k[1] = k_swa;
+    l.v[1] = v_swa;
+  }
+  for (int i = 0; i < 2; ++i) {
+    l.kb[i] = W + w.kb[i];
+    l.vp[i] = W + w.vp[i];
+  }
+  l.q = q_sp;
+  l.dout = dout;
+  l.qT = W + w.qT;
+  l.doT = W + w.doT;
+  l.B = s->batch;
+  l.T = T;
+  l.Hq = s->hq;
+  l.Hkv = s->hkv;
+  l.nblk = nblk;
+  l.NC = bwd_nc(s);
+  hipError_t e = hs::launch_bwd_layouts(l, s->head_dim, strm);
+  if (e != hipSuccess) return launched(fn, e);
+  uint32_t* bits = (uint32_t*)(W + w.bits);
+  if (topk > 0) {
+    e = hs::launch_selbits(idx, bits, s->batch, s->hkv, T, topk, nblk, strm);
+    if (e != hipSuccess) return launched(fn, e);
+  }
+  hs::BwdRowArgs r{};
+  r.o[0] = o_branch;
+  r.o[1] = (const char*)o_branch + brs * s->head_dim * 2;
+  r.dout = dout;
+  r.lse[0] = lse_branch;
+  r.lse[1] = lse_branch + brs;
+  r.gates = gate_logits;
+  r.sinks = sinks;
+  r.delta[0] = (float*)(W + w.delta[0]);
+  r.delta[1] = (float*)(W + w.delta[1]);
+  r.dgates = dgate;
+  r.sterm[0] = (float*)(W + w.sterm[0]);
+  r.sterm[1] = (float*)(W + w.sterm[1]);
+  r.dsinks = dsinks;
+  r.B = s->batch;
+  r.T = T;
+  r.Hq = s->hq;
+  r.D = s->head_dim;
+  r.nbr = 2;
+  e = hs::launch_bwd_rows(r, strm);
+  if (e != hipSuccess) return launched(fn, e);
+  const float tau = s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)s->head_dim);
+  hs::BwdKVArgs a{};
+  a.q = q_sp;
+  a.dout = dout;
+  a.qT = l.qT;
+  a.doT = l.doT;
+  a.gates = gate_logits;
+  a.B = s->batch;
+  a.T = T;
+  a.Hq = s->hq;
+  a.Hkv = s->hkv;
+  a.nblk = nblk;
+  a.W = window;
+  a.nw32 = (nblk + 31) / 32;
+  a.NC = l.NC;
+  a.sc2 = scale_log2(s);
+  a.tau = tau;
+  if (topk > 0) {  // the sparse branch adds into the shared K/V's gradients
+    a.k = k;
+    a.vp = l.vp[0];
+    a.lse = r.lse[0];
+    a.delta = r.delta[0];
+    a.selbits = bits;
+    a.dk = dk;
+    a.dv = dv;
+    a.br = 0;
+    a.accumulate = 1;
+    e = hs::launch_bwd_kv(a, 2, s->head_dim, strm);
+    if (e != hipSuccess) return launched(fn, e);
+  }
+  if (window > 0) {
+    a.k = k_swa;
+    a.vp = l.vp[1];
+    a.lse = r.lse[1];
+    a.delta = r.delta[1];
+    a.selbits = nullptr;
+    a.dk = dk_swa;
+    a.dv = dv_swa;
+    a.br = 1;
+    a.accumulate = 0;
+    e = hs::launch_bwd_kv(a, 1, s->head_dim, strm);
+    if (e != hipSuccess) return launched(fn, e);
+  }
+  hs::BwdQArgs b{};
+  b.q = q_sp;
+  b.dout = dout;
+  b.k0 = k;
+  b.kb0 = l.kb[0];
+  b.vp0 = l.vp[0];
+  b.k1 = k_swa;
+  b.kb1 = l.kb[1];
+  b.vp1 = l.vp[1];
+  b.lse0 = r.lse[0];
+  b.lse1 = r.lse[1];
+  b.delta0 = r.delta[0];
+  b.delta1 = r.delta[1];
+  b.gates = gate_logits;
+  b.idx = idx;
+  b.topk = topk;
+  b.dq = dq_sp;
+  b.B = s->batch;
+  b.T = T;
+  b.Hq = s->hq;
+  b.Hkv = s->hkv;
+  b.nblk = nblk;
+  b.W = window;
+  b.sc2 = a.sc2;
+  b.tau = tau;
+  return launched(fn, hs::launch_bwd_q(b, 1, s->head_dim, strm));
 }
 
 }  // extern "C"

@@ -1,0 +1,603 @@
+// hs_backward.hip -- backward pass of the hybrid block (bf16 inputs, fp32
+// gradients).  The models of the pages are trained with this architecture
+// (HySparse paper 4.1 "Experiments Setup"); the sparse layers' gradients
+// reach the shared K/V (explainer 3.4 "Training Pipeline").  The selection is
+// a discrete choice of the forward pass: indices are inputs, block scores
+// get no gradient.
+//
+// For one attention branch with p = softmax(tau q.k) and o = p v, given dO:
+//   dV = p^T dO~,  dP = dO~ . v,  dS = p (dP - dO~ . o),
+//   dQ = tau dS K,  dK = tau dS^T Q,  with dO~ = sigma(gate) dO
+// (sigma = 1 for the full layer and ungated layers).
+//
+// Every matrix product reads its operands in the order the MFMA wants, from
+// layout copies made first (memory-bound transposes):
+//   Kb  keys block-major [..][nblk][D][64]   (A operand of dQ^T = K^T dS^T)
+//   Vp  values position-major [..][T][D]     (dP = dO V^T, both orientations)
+//   QT, dOT  queries / output gradients d-major per kv group [..][D][T*G]
+//            (A operands of dK^T = Q^T dS and dV^T = dO^T P)
+//
+//  bwd_kv_kernel  key side: one work group per (sequence, kv group, 64-key
+//                 tile), wave w owning keys 16w..16w+15; loops over the
+//                 query tiles (32 columns = 32/G positions x G heads) that
+//                 can attend the tile: S = Q K^T and dP = dO V^T with the
+//                 queries as M rows (lane = key, 8 consecutive columns), so
+//                 P and dS are directly the B operands of dV^T += dO^T P and
+//                 dK^T += Q^T dS.  Modes: full layer (causal), window branch
+//                 (t - W < key <= t), sparse branch (the positions that
+//                 selected the block; query tiles where none did are
+//                 skipped).
+//  bwd_q_kernel   query side: work groups of 4*16/G positions as in the
+//                 forward; per item (key tile) S^T = K Q^T and dP^T = V dO^T
+//                 (K rows and V rows staged in LDS), dS^T elementwise, then
+//                 dQ^T += K^T dS^T with the block-major K tile, as the
+//                 forward's P V.  Sparse layers: window items (branch 1)
+//                 then the union of the selected blocks (branch 0), each
+//                 with its own LSE, dO.o and gate.
+#include "hs_device.h"
+#include "hs_internal.h"
+
+namespace hs {
+
+// ================================================== layout conversions
+// K [B*Hkv][T][D] -> Kb [B*Hkv][nblk][D][64], zero past T
+template <int D>
+__global__ __launch_bounds__(256) void k_to_blockmajor_kernel(const uint16_t* k, uint16_t* kb, int T, int nblk) {
+  __shared__ uint16_t tl[64][D + 2];
+  const int j = blockIdx.x % nblk;
+  const size_t bg = blockIdx.x / nblk;
+  for (int e = threadIdx.x; e < 64 * D / 8; e += 256) {
+    const int r = e / (D / 8), c = e % (D / 8), t = 64 * j + r;
+    const uint4 x = t < T ? *(const uint4*)(k + (bg * T + t) * D + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tl[r][8 * c + 2 * i] = (uint16_t)(w[i] & 0xffffu);
+      tl[r][8 * c + 2 * i + 1] = (uint16_t)(w[i] >> 16);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < D * 8; e += 256) {
+    const int dd = e / 8, c = e % 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)tl[8 * c + 2 * i][dd] | ((uint32_t)tl[8 * c + 2 * i + 1][dd] << 16);
+    *(uint4*)(kb + ((bg * nblk + j) * D + dd) * 64 + 8 * c) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// V [B*Hkv][nblk][D][64] -> Vp [B*Hkv][nblk*64][D], zero past T (the tail of
+// the last value tile may hold anything)
+template <int D>
+__global__ __launch_bounds__(256) void v_to_posmajor_kernel(const uint16_t* v, uint16_t* vp, int T, int nblk) {
+  __shared__ uint16_t tl[D][64 + 2];
+  const int j = blockIdx.x % nblk;
+  const size_t bg = blockIdx.x / nblk;
+  for (int e = threadIdx.x; e < D * 8; e += 256) {
+    const int dd = e / 8, c = e % 8;
+    const uint4 x = *(const uint4*)(v + ((bg * nblk + j) * D + dd) * 64 + 8 * c);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tl[dd][8 * c + 2 * i] = (uint16_t)(w[i] & 0xffffu);
+      tl[dd][8 * c + 2 * i + 1] = (uint16_t)(w[i] >> 16);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 64 * D / 8; e += 256) {
+    const int r = e / (D / 8), c = e % (D / 8);
+    const bool in = 64 * j + r < T;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = in ? ((uint32_t)tl[8 * c + 2 * i][r] | ((uint32_t)tl[8 * c + 2 * i + 1][r] << 16)) : 0u;
+    *(uint4*)(vp + (bg * nblk * 64 + 64 * j + r) * D + 8 * c) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// X [B][T][Hq][D] -> XT [B*Hkv][D][NC]: column c = t*G + hh holds head
+// g*G + hh of position t; zero for c >= T*G.  One work group per 64 columns.
+template <int D>
+__global__ __launch_bounds__(256) void rows_to_dmajor_kernel(const uint16_t* x, uint16_t* xt, int T, int Hq, int Hkv,
+                                                             int NC) {
+  __shared__ uint16_t tl[64][D + 2];
+  const int nch = NC / 64;
+  const int ch = blockIdx.x % nch;
+  const int bg = blockIdx.x / nch;
+  const int g = bg % Hkv, b = bg / Hkv, G = Hq / Hkv;
+  for (int e = threadIdx.x; e < 64 * D / 8; e += 256) {
+    const int r = e / (D / 8), c = e % (D / 8);
+    const int col = 64 * ch + r, t = col / G, hh = col % G;
+    const uint4 v = t < T ? *(const uint4*)(x + (((size_t)b * T + t) * Hq + g * G + hh) * D + 8 * c)
+                          : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tl[r][8 * c + 2 * i] = (uint16_t)(w[i] & 0xffffu);
+      tl[r][8 * c + 2 * i + 1] = (uint16_t)(w[i] >> 16);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < D * 8; e += 256) {
+    const int dd = e / 8, c = e % 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)tl[8 * c + 2 * i][dd] | ((uint32_t)tl[8 * c + 2 * i + 1][dd] << 16);
+    *(uint4*)(xt + ((size_t)bg * D + dd) * NC + 64 * ch + 8 * c) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// ===================================================== per-row preparation
+// One row per 16 lanes: delta[br] = dO . o_br (bf16 rows), and for gated
+// layers dG_br = s (1 - s) delta_br; with sinks the row's sink term
+// -exp(b - lse_br) s delta_br (summed per head by bwd_sink_reduce_kernel).
+__global__ __launch_bounds__(256) void bwd_rows_kernel(BwdRowArgs a) {
+  const int lane = threadIdx.x & 63;
+  const long row = ((long)blockIdx.x * 256 + threadIdx.x) / 16;  // (b, t, h)
+  const int sub = lane & 15;
+  const long nrows = (long)a.B * a.T * a.Hq;
+  const bool in = row < nrows;
+  const long rr = in ? row : 0;
+  const int h = (int)(rr % a.Hq);
+  const long bt = rr / a.Hq;
+  const int t = (int)(bt % a.T), b = (int)(bt / a.T);
+  const int per = a.D / 16;  // elements per lane
+  for (int br = 0; br < a.nbr; ++br) {
+    const uint16_t* o = (const uint16_t*)a.o[br] + rr * a.D;
+    const uint16_t* d = (const uint16_t*)a.dout + rr * a.D;
+    float acc = 0.f;
+    for (int i = 0; i < per; ++i) {
+      const int e = sub * per + i;
+      acc += __uint_as_float((uint32_t)o[e] << 16) * __uint_as_float((uint32_t)d[e] << 16);
+    }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
+    if (in && sub == 0) {
+      const size_t ri = ((size_t)b * a.Hq + h) * a.T + t;
+      a.delta[br][ri] = acc;
+      const float s = a.gates ? 1.f / (1.f + expf(-a.gates[(size_t)rr * 2 + br])) : 1.f;
+      if (a.dgates) a.dgates[(size_t)rr * 2 + br] = s * (1.f - s) * acc;
+      if (a.sinks) a.sterm[br][ri] = -expf(a.sinks[br * a.Hq + h] - a.lse[br][ri]) * s * acc;
+    }
+  }
+}
+
+// dsinks[br][h] = sum over (b, t) of the sink terms; one work group per (br, h)
+__global__ __launch_bounds__(256) void bwd_sink_reduce_kernel(BwdRowArgs a) {
+  __shared__ float part[4];
+  const int br = blockIdx.x / a.Hq, h = blockIdx.x % a.Hq;
+  float acc = 0.f;
+  for (long i = threadIdx.x; i < (long)a.B * a.T; i += 256) {
+    const int b = (int)(i / a.T), t = (int)(i % a.T);
+    acc += a.sterm[br][((size_t)b * a.Hq + h) * a.T + t];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) a.dsinks[br * a.Hq + h] = part[0] + part[1] + part[2] + part[3];
+}
+
+// selection bitsets [B*Hkv][T][nw32]: bit j of row t set when the row's list
+// holds j with 0 <= j < nblk and 64 j <= t (the forward's rule)
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, long n) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) p[i] = 0u;
+}
+__global__ __launch_bounds__(256) void selbits_kernel(const int32_t* idx, uint32_t* bits, long n, int T, int topk,
+                                                      int nblk, int nw32) {
+  const long e = (long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  const long rowi = e / topk;  // (bg, t)
+  const int t = (int)(rowi % T);
+  const int j = idx[e];
+  if (j >= 0 && j < nblk && 64 * j <= t) atomicOr(&bits[rowi * nw32 + (j >> 5)], 1u << (j & 31));
+}
+
+// ============================================================ key side
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void bwd_kv_kernel(BwdKVArgs a) {
+  using Tt = Tr<HS_BF16>;
+  using Frag = Tt::Frag;
+  constexpr int NS = D / 32, NM = D / 16;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int j = blockIdx.x % a.nblk;
+  const int bg = blockIdx.x / a.nblk;
+  const int g = bg % a.Hkv, b = bg / a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int T = a.T;
+  const int key = 64 * j + 16 * w + r16;
+  const int keyc = min(key, T - 1);
+  Frag kf[NS], vf[NS];
+  const char* krow = (const char*)a.k + ((size_t)bg * T + keyc) * D * 2;
+  const char* vrow = (const char*)a.vp + ((size_t)bg * a.nblk * 64 + key) * D * 2;
+#pragma unroll
+  for (int ks = 0; ks < NS; ++ks) {
+    kf[ks] = Tt::ld(krow + (32 * ks + 8 * q4) * 2);
+    vf[ks] = Tt::ld(vrow + (32 * ks + 8 * q4) * 2);
+  }
+  f32x4 dkT[NM], dvT[NM];
+#pragma unroll
+  for (int mc = 0; mc < NM; ++mc) {
+    dkT[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dvT[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int PQ = 32 / G;  // positions per query tile
+  const int t_lo = 64 * j;
+  const int t_hi = MODE == 1 ? min(T - 1, 64 * j + 63 + a.W - 1) : T - 1;
+  const char* qT = (const char*)a.qT + (size_t)bg * D * a.NC * 2;
+  const char* doT = (const char*)a.doT + (size_t)bg * D * a.NC * 2;
+  for (int tile = t_lo / PQ; tile <= t_hi / PQ; ++tile) {
+    const int tq0 = tile * PQ;
+    if (MODE == 2) {  // no position of the tile selected the block: skip
+      bool sel = false;
+      if (lane < PQ && tq0 + lane < T)
+        sel = (a.selbits[((size_t)bg * T + tq0 + lane) * a.nw32 + (j >> 5)] >> (j & 31)) & 1u;
+      if (__ballot(sel) == 0ull) continue;
+    }
+    // S, dP: chunk e holds columns 8(rho/4) + 4e + rho%4 as M rows
+    f32x4 S[2], dP[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int c = 8 * (r16 >> 2) + 4 * e + (r16 & 3);
+      const int tc = min(tq0 + c / G, T - 1), h = g * G + c % G;
+      const char* qrow = (const char*)a.q + (((size_t)b * T + tc) * a.Hq + h) * D * 2;
+      const char* drow = (const char*)a.dout + (((size_t)b * T + tc) * a.Hq + h) * D * 2;
+      S[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dP[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NS; ++ks) {
+        Tt::mma(S[e], Tt::ld(qrow + (32 * ks + 8 * q4) * 2), kf[ks]);
+        Tt::mma(dP[e], Tt::ld(drow + (32 * ks + 8 * q4) * 2), vf[ks]);
+      }
+    }
+    // the lane holds key `key` and columns 8q4 .. 8q4+7
+    float ps[8], ds[8];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 8 * q4 + 4 * e + i;
+        const int t = tq0 + c / G, h = g * G + c % G;
+        const int tc = min(t, T - 1);
+        const size_t ri = ((size_t)b * a.Hq + h) * T + tc;
+        bool valid = t < T && key <= t;
+        if (MODE == 1) valid = valid && key > t - a.W;
+        if (MODE == 2)
+          valid = valid && ((a.selbits[((size_t)bg * T + tc) * a.nw32 + (j >> 5)] >> (j & 31)) & 1u);
+        const float sg = a.gates ? 1.f / (1.f + expf(-a.gates[(((size_t)b * T + tc) * a.Hq + h) * 2 + a.br])) : 1.f;
+        const float p = valid ? fast_exp2(S[e][i] * a.sc2 - a.lse[ri] * kLog2e) : 0.f;
+        ps[4 * e + i] = p * sg;
+        ds[4 * e + i] = p * sg * (dP[e][i] - a.delta[ri]);
+      }
+    const Frag pf = Tt::pack(ps), dsf = Tt::pack(ds);
+#pragma unroll
+    for (int mc = 0; mc < NM; ++mc) {
+      const size_t off = ((size_t)(16 * mc + r16) * a.NC + (size_t)tq0 * G + 8 * q4) * 2;
+      Tt::mma(dvT[mc], Tt::ld(doT + off), pf);
+      Tt::mma(dkT[mc], Tt::ld(qT + off), dsf);
+    }
+  }
+  if (key < T) {
+    float* dkp = a.dk + ((size_t)bg * T + key) * D + 4 * q4;
+    float* dvp = a.dv + ((size_t)bg * T + key) * D + 4 * q4;
+#pragma unroll
+    for (int mc = 0; mc < NM; ++mc) {
+      float4 x = make_float4(a.tau * dkT[mc][0], a.tau * dkT[mc][1], a.tau * dkT[mc][2], a.tau * dkT[mc][3]);
+      float4 y = make_float4(dvT[mc][0], dvT[mc][1], dvT[mc][2], dvT[mc][3]);
+      if (a.accumulate) {
+        const float4 x0 = *(const float4*)(dkp + 16 * mc), y0 = *(const float4*)(dvp + 16 * mc);
+        x = make_float4(x.x + x0.x, x.y + x0.y, x.z + x0.z, x.w + x0.w);
+        y = make_float4(y.x + y0.x, y.y + y0.y, y.z + y0.z, y.w + y0.w);
+      }
+      *(float4*)(dkp + 16 * mc) = x;
+      *(float4*)(dvp + 16 * mc) = y;
+    }
+  }
+}
+
+// ========================================================== query side
+// Rows-only LDS staging (K or V rows of a 64-key tile, in S^T row order,
+// chunk-swizzled as TileStage's key rows), direct global -> LDS.
+template <int D, int NTHR>
+struct RowStage {
+  static constexpr int KS = D * 2;
+  static constexpr int KCH = KS / 16;
+  static constexpr int KSW = (KCH < 16 ? KCH : 16) - 1;
+  static constexpr int BYTES = 64 * KS;
+  static constexpr int NWV = NTHR / 64;
+  static constexpr int NDMA = BYTES / 1024 / NWV;
+  static_assert(NDMA * NWV * 1024 == BYTES, "tile does not split into wave chunks");
+  int dkey[NDMA];
+  uint32_t doff[NDMA];
+  __device__ __forceinline__ static int k_lds(int row, int chunk) { return row * KS + ((chunk ^ (row & KSW)) << 4); }
+  __device__ __forceinline__ void dma_init() {
+    const int lane = lane_id(), w = threadIdx.x >> 6;
+#pragma unroll
+    for (int n = 0; n < NDMA; ++n) {
+      const int off = (w + NWV * n) * 1024 + 16 * lane;
+      const int r = off / KS, c = ((off % KS) >> 4) ^ (r & KSW);
+      dkey[n] = tile_key(r >> 4, r & 15);
+      doff[n] = dkey[n] * KS + c * 16;
+    }
+  }
+  // rows: row 0 of the tile; rows past nk read row nk-1
+  __device__ __forceinline__ void dma(char* buf, const char* rows, int nk) {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int n = 0; n < NDMA; ++n) {
+      const int kk = dkey[n];
+      const char* src = rows + (doff[n] - (uint32_t)((kk - min(kk, nk - 1)) * KS));
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + (w + NWV * n) * 1024), 16,
+                                       0, 0);
+    }
+  }
+  __device__ __forceinline__ static Tr<HS_BF16>::Frag ldK(const char* buf, int c, int ks) {
+    const int lane = lane_id();
+    const int row = 16 * c + (lane & 15);
+    const int ch = (32 * ks + 8 * (lane >> 4)) * 2 / 16;
+    return Tr<HS_BF16>::ld(buf + k_lds(row, ch));
+  }
+};
+
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void bwd_q_kernel(BwdQArgs a) {
+  using Tt = Tr<HS_BF16>;
+  using Eng = WaveAttn<HS_BF16, D, 1>;
+  using StK = TileStage<HS_BF16, D, 256>;  // K rows + the block-major K tile
+  using StV = RowStage<D, 256>;            // V rows
+  constexpr int NW = 4;
+  __shared__ __attribute__((aligned(16))) char kt0[StK::BYTES];
+  __shared__ __attribute__((aligned(16))) char kt1[StK::BYTES];
+  __shared__ __attribute__((aligned(16))) char vt0[StV::BYTES];
+  __shared__ __attribute__((aligned(16))) char vt1[StV::BYTES];
+  extern __shared__ uint32_t dyn[];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int T = a.T;
+  const int G = a.Hq / a.Hkv;
+  const int PT = 16 / G;
+  const int PWG = NW * PT;
+  const int nwg_bg = (T + PWG - 1) / PWG;
+  const WgSlot ws = wg_slot(a.B * a.Hkv, nwg_bg);
+  const bool live = ws.live;
+  const int bg = ws.bg;
+  const int g = bg % a.Hkv, b = bg / a.Hkv;
+  const int t0 = ws.pblk * PWG;
+  const int col = lane & 15;
+  const int h = g * G + col % G;
+  const int tcol = t0 + w * PT + col / G;
+  const int hicol = live && tcol < T ? tcol : -1;
+  const int tc = min(tcol, T - 1);
+
+  Eng eq, ed;  // eq: Q fragments and the dQ^T accumulators; ed: dO fragments
+  eq.reset();
+#pragma unroll
+  for (int ks = 0; ks < Eng::NS; ++ks) {
+    const size_t off = ((((size_t)b * T + tc) * a.Hq + h) * D + 32 * ks + 8 * (lane >> 4)) * 2;
+    eq.qf[0][ks] = Tt::ld((const char*)a.q + off);
+    ed.qf[0][ks] = Tt::ld((const char*)a.dout + off);
+  }
+  // per-branch column statistics (log2-unit LSE, dO.o, gate)
+  const size_t ri = ((size_t)b * a.Hq + h) * T + tc;
+  float lse2[2], dl[2], sg[2];
+#pragma unroll
+  for (int br = 0; br < 2; ++br) {
+    const float* L = br ? a.lse1 : a.lse0;
+    const float* Dl = br ? a.delta1 : a.delta0;
+    lse2[br] = L ? L[ri] * kLog2e : 0.f;
+    dl[br] = Dl ? Dl[ri] : 0.f;
+    sg[br] = a.gates ? 1.f / (1.f + expf(-a.gates[(((size_t)b * T + tc) * a.Hq + h) * 2 + br])) : 1.f;
+  }
+
+  // items: MODE 0 the causal tiles 0 .. of the group's last position; MODE 1
+  // the window tiles (branch 1, the layer's own cache) then the union of the
+  // positions' selected blocks (branch 0, the shared cache)
+  const int nw32 = (a.nblk + 31) >> 5;
+  uint32_t* S = dyn;                 // [PWG][nw32] per position
+  uint32_t* U = S + PWG * nw32;      // [nw32] union
+  int* ulist = (int*)(U + nw32);     // [nblk]
+  int* nu_p = ulist + a.nblk;
+  int jw0 = 0, nwin = 0, nu = 0;
+  if (MODE == 0) {
+    nu = live ? ((min(T, t0 + PWG) - 1) >> 6) + 1 : 0;
+  } else {
+    if (live && a.W > 0) {
+      jw0 = max(0, t0 - a.W + 1) >> 6;
+      nwin = (min(T - 1, t0 + PWG - 1) >> 6) - jw0 + 1;
+    }
+    for (int i = threadIdx.x; i < (PWG + 1) * nw32; i += 64 * NW) S[i] = 0u;
+    __syncthreads();
+    if (live) {
+      for (int e = threadIdx.x; e < PWG * a.topk; e += 64 * NW) {
+        const int p = e / a.topk, t = t0 + p;
+        if (t < T) {
+          const int j = a.idx[((size_t)bg * T + t) * a.topk + (e % a.topk)];
+          if (j >= 0 && j < a.nblk && 64 * j <= t) atomicOr(&S[p * nw32 + (j >> 5)], 1u << (j & 31));
+        }
+      }
+    }
+    __syncthreads();
+    for (int k = threadIdx.x; k < nw32; k += 64 * NW) {
+      uint32_t v = 0u;
+      for (int p = 0; p < PWG; ++p) v |= S[p * nw32 + k];
+      U[k] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      int base = 0;
+      for (int w0 = 0; w0 < nw32; w0 += 64) {
+        const uint32_t word = w0 + lane < nw32 ? U[w0 + lane] : 0u;
+        const int cnt = __popc(word);
+        int incl = cnt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int v = __shfl_up(incl, off);
+          if (lane >= off) incl += v;
+        }
+        int pos = base + incl - cnt;
+        uint32_t wd = word;
+        while (wd) {
+          ulist[pos++] = (w0 + lane) * 32 + __builtin_ctz(wd);
+          wd &= wd - 1;
+        }
+        base += __shfl(incl, 63);
+      }
+      if (lane == 0) *nu_p = base;
+    }
+    __syncthreads();
+    nu = live ? *nu_p : 0;
+  }
+  const int nitems = nwin + nu;
+
+  StK sk;
+  StV sv;
+  sk.dma_init();
+  sv.dma_init();
+  auto blk = [&](int i) {
+    return __builtin_amdgcn_readfirstlane(MODE == 0 ? i : (i < nwin ? jw0 + i : ulist[max(i - nwin, 0)]));
+  };
+  auto issue = [&](int i, char* kb, char* vb) {
+    const bool win = MODE == 1 && i < nwin;
+    const int j = blk(i);
+    const char* kr = (const char*)(win ? a.k1 : a.k0) + ((size_t)bg * T + 64 * j) * D * 2;
+    const char* kbs = (const char*)(win ? a.kb1 : a.kb0) + ((size_t)bg * a.nblk + j) * D * 64 * 2;
+    const char* vr = (const char*)(win ? a.vp1 : a.vp0) + ((size_t)bg * a.nblk * 64 + 64 * j) * D * 2;
+    sk.dma(kb, kr, kbs, T - 64 * j);
+    sv.dma(vb, vr, T - 64 * j);
+  };
+  if (nitems > 0) issue(0, kt0, vt0);
+  wait_vmem();
+  __syncthreads();
+
+  auto step = [&](int i, const char* kc, const char* vc, char* kn, char* vn) {
+    const bool win = MODE == 1 && i < nwin;
+    const int j = blk(i);
+    if (i + 1 < nitems) issue(i + 1, kn, vn);
+    const int kbase = 64 * j;
+    int lo, hi = hicol;
+    if (MODE == 0) {
+      lo = 0;
+    } else if (win) {
+      lo = tcol - a.W + 1;
+    } else {
+      const bool sel = hicol >= 0 && ((S[(w * PT + col / G) * nw32 + (j >> 5)] >> (j & 31)) & 1u);
+      lo = sel ? 0 : kNoKey;
+    }
+    const bool livecol = hicol >= 0 && lo != kNoKey && max(lo, kbase) <= min(hi, kbase + 63);
+    if (__ballot(livecol) != 0ull) {
+      f32x4 s[1][4], dp[1][4];
+      eq.qk([&](int c, int ks) { return StK::ldK(kc, c, ks); }, s);
+      ed.qk([&](int c, int ks) { return StV::ldK(vc, c, ks); }, dp);
+      const int br = win ? 1 : 0;
+      const float l2 = br ? lse2[1] : lse2[0], d0 = br ? dl[1] : dl[0], s0 = br ? sg[1] : sg[0];
+      const int kb8 = kbase + 8 * (lane >> 4);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+          const int k = kb8 + 32 * (c >> 1) + 4 * (c & 1) + i2;
+          const bool valid = livecol && k >= lo && k <= hi;
+          const float p = valid ? fast_exp2(s[0][c][i2] * a.sc2 - l2) : 0.f;
+          s[0][c][i2] = p * s0 * (dp[0][c][i2] - d0);
+        }
+      Tt::pack_p(s[0]);
+      eq.pv(s, [&](int u, int mc) { return StK::ldV(kc, u, mc); });
+    }
+    wait_vmem();
+    __syncthreads();
+  };
+  for (int i = 0; i < nitems; i += 2) {
+    step(i, kt0, vt0, kt1, vt1);
+    if (i + 1 >= nitems) break;
+    step(i + 1, kt1, vt1, kt0, vt0);
+  }
+  if (hicol >= 0) {
+    float* op = a.dq + (((size_t)b * T + tcol) * a.Hq + h) * D + 4 * (lane >> 4);
+#pragma unroll
+    for (int mc = 0; mc < Eng::NM; ++mc) {
+      const f32x4 v = eq.o[0][mc];
+      *(float4*)(op + 16 * mc) = make_float4(a.tau * v[0], a.tau * v[1], a.tau * v[2], a.tau * v[3]);
+    }
+  }
+}
+
+// ============================================================= launchers
+template <int D>
+static hipError_t layouts(const BwdLayoutArgs& l, hipStream_t s) {
+  const unsigned nkb = (unsigned)((long)l.B * l.Hkv * l.nblk);
+  for (int i = 0; i < 2; ++i) {
+    if (l.k[i]) hipLaunchKernelGGL(k_to_blockmajor_kernel<D>, dim3(nkb), dim3(256), 0, s, (const uint16_t*)l.k[i],
+                                   (uint16_t*)l.kb[i], l.T, l.nblk);
+    if (l.v[i]) hipLaunchKernelGGL(v_to_posmajor_kernel<D>, dim3(nkb), dim3(256), 0, s, (const uint16_t*)l.v[i],
+                                   (uint16_t*)l.vp[i], l.T, l.nblk);
+  }
+  const unsigned nrt = (unsigned)((long)l.B * l.Hkv * (l.NC / 64));
+  hipLaunchKernelGGL(rows_to_dmajor_kernel<D>, dim3(nrt), dim3(256), 0, s, (const uint16_t*)l.q, (uint16_t*)l.qT,
+                     l.T, l.Hq, l.Hkv, l.NC);
+  hipLaunchKernelGGL(rows_to_dmajor_kernel<D>, dim3(nrt), dim3(256), 0, s, (const uint16_t*)l.dout,
+                     (uint16_t*)l.doT, l.T, l.Hq, l.Hkv, l.NC);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_layouts(const BwdLayoutArgs& l, int D, hipStream_t s) {
+  return D == 128 ? layouts<128>(l, s) : layouts<64>(l, s);
+}
+
+hipError_t launch_bwd_rows(const BwdRowArgs& a, hipStream_t s) {
+  const long rows = (long)a.B * a.T * a.Hq;
+  hipLaunchKernelGGL(bwd_rows_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !a.sinks) return e;
+  hipLaunchKernelGGL(bwd_sink_reduce_kernel, dim3((unsigned)(a.nbr * a.Hq)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_selbits(const int32_t* idx, uint32_t* bits, int B, int Hkv, int T, int topk, int nblk,
+                          hipStream_t s) {
+  const int nw32 = (nblk + 31) / 32;
+  const long nw = (long)B * Hkv * T * nw32;
+  hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, s, bits, nw);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long n = (long)B * Hkv * T * topk;
+  if (n > 0)
+    hipLaunchKernelGGL(selbits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx, bits, n, T, topk,
+                       nblk, nw32);
+  return hipGetLastError();
+}
+
+template <int D>
+static void kv_dispatch(const BwdKVArgs& a, int mode, hipStream_t s) {
+  const dim3 grid((unsigned)((long)a.B * a.Hkv * a.nblk));
+  if (mode == 0) hipLaunchKernelGGL((bwd_kv_kernel<D, 0>), grid, dim3(256), 0, s, a);
+  else if (mode == 1) hipLaunchKernelGGL((bwd_kv_kernel<D, 1>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((bwd_kv_kernel<D, 2>), grid, dim3(256), 0, s, a);
+}
+hipError_t launch_bwd_kv(const BwdKVArgs& a, int mode, int D, hipStream_t s) {
+  if (D == 128) kv_dispatch<128>(a, mode, s);
+  else kv_dispatch<64>(a, mode, s);
+  return hipGetLastError();
+}
+
+size_t bwd_q_lds_bytes(int T, int G) {
+  const int nblk = (T + 63) / 64, nw32 = (nblk + 31) / 32, PWG = 4 * (16 / G);
+  return ((size_t)(PWG + 1) * nw32 + nblk + 1) * sizeof(uint32_t);
+}
+
+template <int D>
+static void q_dispatch(const BwdQArgs& a, int mode, hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  const int PWG = 4 * (16 / G);
+  const dim3 grid((unsigned)((long)a.B * a.Hkv * ((a.T + PWG - 1) / PWG)));
+  const size_t lds = bwd_q_lds_bytes(a.T, G);
+  if (mode == 0) hipLaunchKernelGGL((bwd_q_kernel<D, 0>), grid, dim3(256), lds, s, a);
+  else hipLaunchKernelGGL((bwd_q_kernel<D, 1>), grid, dim3(256), lds, s, a);
+}
+hipError_t launch_bwd_q(const BwdQArgs& a, int mode, int D, hipStream_t s) {
+  if (D == 128) q_dispatch<128>(a, mode, s);
+  else q_dispatch<64>(a, mode, s);
+  return hipGetLastError();
+}
+
+}  // namespace hs

@@ -49,7 +49,15 @@ struct SparsePrefillArgs {
   const float* q_scale;    // fp8: [Hq] scales of the layer's queries
   const float* kv_scale;   // fp8: [2][Hkv] scales of the shared K, V
   const float* swa_scale;  // fp8: [2][Hkv] scales of the window K', V'
+  // training forward (optional): each branch's ungated output [2][B][T][Hq][D]
+  // (0: sparse branch, 1: window branch, output dtype) and its LSE
+  // [2][B][Hq][T] (natural log, sink included)
+  void* o_br;
+  float* lse_br;
 };
+// whether hs_sparse_attn_fwd runs sparse_prefill_dual_kernel for this shape
+// (the kernel that also writes the training-forward branch outputs)
+bool sparse_prefill_dual_ok(const SparsePrefillArgs& a, int dtype, int D);
 
 // split-K chunking of the decode full layer: at most this many 64-key tiles
 // per chunk (the kernel keeps one block maximum per tile in registers until
@@ -146,6 +154,75 @@ struct OffloadArgs {
 };
 hipError_t offload_pipeline(const OffloadArgs& a, int D, hipStream_t s, hipStream_t copy_s);
 size_t offload_stage_bytes(int chunk, int Hkv, int C, int D, int es);
+
+// ------------------------------------------------------------ backward
+// layout copies for the backward (hs_backward.hip)
+struct BwdLayoutArgs {
+  const void* k[2];  // key caches [B][Hkv][T][D] (NULL: skip)
+  const void* v[2];  // block-major value caches [B][Hkv][nblk][D][64]
+  void* kb[2];       // out: keys block-major [B][Hkv][nblk][D][64]
+  void* vp[2];       // out: values position-major [B][Hkv][nblk*64][D]
+  const void* q;     // [B][T][Hq][D]
+  const void* dout;
+  void* qT;          // out: [B][Hkv][D][NC]
+  void* doT;
+  int B, T, Hq, Hkv, nblk, NC;
+};
+struct BwdRowArgs {
+  const void* o[2];     // branch outputs [B][T][Hq][D] bf16 (the layer output for the full layer)
+  const void* dout;
+  const float* lse[2];  // [B][Hq][T] (sinks only)
+  const float* gates;   // [B][T][Hq][2] or NULL
+  const float* sinks;   // [2][Hq] or NULL
+  float* delta[2];      // out: [B][Hq][T] dO . o_br
+  float* dgates;        // out (gated layers): [B][T][Hq][2]
+  float* sterm[2];      // scratch (sinks): [B][Hq][T]
+  float* dsinks;        // out (sinks): [2][Hq]
+  int B, T, Hq, D, nbr;
+};
+struct BwdKVArgs {
+  const void* q;
+  const void* dout;
+  const void* qT;
+  const void* doT;
+  const void* k;        // this branch's keys [B][Hkv][T][D]
+  const void* vp;       // this branch's values, position-major
+  const float* lse;     // this branch's LSE [B][Hq][T]
+  const float* delta;   // dO . o_br
+  const float* gates;
+  const uint32_t* selbits;  // sparse branch: [B][Hkv][T][nw32]
+  float* dk;
+  float* dv;
+  int B, T, Hq, Hkv, nblk, W, nw32, NC, br, accumulate;
+  float sc2, tau;
+};
+struct BwdQArgs {
+  const void* q;
+  const void* dout;
+  const void* k0;   // branch 0 (full layer / sparse branch): keys, keys block-major, values position-major
+  const void* kb0;
+  const void* vp0;
+  const void* k1;   // branch 1 (window): the layer's own cache
+  const void* kb1;
+  const void* vp1;
+  const float* lse0;
+  const float* lse1;
+  const float* delta0;
+  const float* delta1;
+  const float* gates;
+  const int32_t* idx;
+  int topk;
+  float* dq;
+  int B, T, Hq, Hkv, nblk, W;
+  float sc2, tau;
+};
+hipError_t launch_bwd_layouts(const BwdLayoutArgs& l, int D, hipStream_t s);
+hipError_t launch_bwd_rows(const BwdRowArgs& a, hipStream_t s);
+hipError_t launch_selbits(const int32_t* idx, uint32_t* bits, int B, int Hkv, int T, int topk, int nblk,
+                          hipStream_t s);
+hipError_t launch_bwd_kv(const BwdKVArgs& a, int mode, int D, hipStream_t s);  // mode 0 full, 1 window, 2 sparse
+hipError_t launch_bwd_q(const BwdQArgs& a, int mode, int D, hipStream_t s);    // mode 0 full, 1 sparse layer
+size_t bwd_q_lds_bytes(int T, int G);
 
 hipError_t launch_token_topk(const TokenTopkArgs& a, hipStream_t s);
 hipError_t launch_decode_sparse_token(const DecodeSparseArgs& a, int D, hipStream_t s);

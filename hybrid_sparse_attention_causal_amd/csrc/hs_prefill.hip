@@ -1152,6 +1152,17 @@ __global__ __launch_bounds__(256, 2) void sparse_prefill_dual_kernel(SparsePrefi
   // Close a branch.  The first branch's gated output is parked in the output
   // rows themselves (in the output dtype) while the second branch runs and is
   // added back when that one closes: no registers hold it in between.
+  // training forward: the branch's own (ungated) output and LSE
+  auto branch_out = [&](int nt, float inv, float l2, int br) {
+    const size_t row = (size_t)(b * T + tcol[nt]) * a.Hq + hcol;
+    char* bp = (char*)a.o_br + (((size_t)br * a.B * T * a.Hq + row) * D + 4 * (lane >> 4)) * ES;
+#pragma unroll
+    for (int mc = 0; mc < Eng::NM; ++mc) {
+      const f32x4 v = eng.o[nt][mc] * inv;
+      Tt::store4(bp + 16 * mc * ES, v[0], v[1], v[2], v[3]);
+    }
+    if ((lane >> 4) == 0) a.lse_br[((size_t)br * a.B * a.Hq + b * a.Hq + hcol) * T + tcol[nt]] = l2 * kLn2;
+  };
   auto fold = [&](const float* gate, const float* sink, bool first) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -1166,6 +1177,7 @@ __global__ __launch_bounds__(256, 2) void sparse_prefill_dual_kernel(SparsePrefi
           if (!first) v += Tt::load4(op + 16 * mc * ES);
           Tt::store4(op + 16 * mc * ES, v[0], v[1], v[2], v[3]);
         }
+        if (a.o_br) branch_out(nt, inv, l2, first ? 1 : 0);
       }
     }
   };
@@ -1245,6 +1257,15 @@ __global__ __launch_bounds__(256, 2) void sparse_prefill_dual_kernel(SparsePrefi
   }
   if (nwin == nitems) {
     fold(gate1, sink1, true);
+    if (a.o_br) {  // no selected block: the sparse branch is empty (its sink alone)
+      eng.reset();
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float inv, l2;
+        eng.finish(nt, inv, l2, sink0[nt]);
+        if (live && tcol[nt] < T) branch_out(nt, inv, l2, 0);
+      }
+    }
   } else {
     fold(gate0, sink0, false);
   }
@@ -1342,6 +1363,14 @@ static hipError_t sparse_dispatch(SparsePrefillArgs a, hipStream_t s) {
     hipLaunchKernelGGL((sparse_prefill_kernel<DT, D, NT, NW, kSparseStages>), dim3(a.nwg), dim3(64 * NW), lds,
                        s, a);
   return hipGetLastError();
+}
+
+bool sparse_prefill_dual_ok(const SparsePrefillArgs& a, int dtype, int D) {
+  if (dtype == HS_F32 && D == 128) return false;
+  const int G = a.Hq / a.Hkv;
+  const int PWG = 4 * (16 * kSparseNT / G);
+  const int nw32 = (a.nblk + 31) / 32;
+  return ((size_t)(1 + 4 + PWG) * nw32 + a.nblk + 1) * sizeof(uint32_t) <= 16 * 1024;
 }
 
 // dynamic LDS of the widest sparse launch shape (an upper bound for all)

@@ -289,11 +289,75 @@ hs_status hs_offload_full_select(const hs_shape* shape, const int32_t* lens_host
                                  int32_t* idx_sel, int chunk, void* ws, size_t ws_bytes, void* stream,
                                  void* copy_stream);
 
+/*
+ * Training forward of one sparse layer: hs_sparse_attn_fwd (bf16), plus what
+ * its backward needs, each branch's own ungated output and LSE:
+ *   o_branch   [2][batch][T][hq][head_dim] bf16 (out): [0] the block-sparse
+ *              branch o~, [1] the window branch o' (explainer 3.4.3)
+ *   lse_branch [2][batch][hq][T] fp32 (out): log of each branch's softmax
+ *              denominator, its sink included (-inf for an empty branch
+ *              without a sink)
+ * Takes the shapes the default sparse kernel serves (selection bitsets of a
+ * work group within 16 KiB of LDS: T <= 32768 for G = 1, more for larger
+ * groups); longer sequences return HS_ERR_UNSUPPORTED.
+ */
+hs_status hs_sparse_attn_fwd_train(const hs_shape* shape, const void* q_sp, const void* k,
+                                   const void* v, const int32_t* idx, int topk, const void* k_swa,
+                                   const void* v_swa, int window, const float* gate_logits,
+                                   const float* sinks, void* o, void* o_branch, float* lse_branch,
+                                   void* stream);
+
+/*
+ * Backward pass of the full layer (bf16 prefill, head_dim 64/128, hq/hkv <=
+ * 16).  The paper trains this architecture (section 4.1); gradients follow
+ * the chain rule of eq. o_t (explainer 3.4.1):
+ *   dV = P^T dO, dP = dO V^T, dS = P (dP - rowsum(dO o)), dQ = tau dS K,
+ *   dK = tau dS^T Q.
+ *   q, o, dout [batch][T][hq][head_dim]; k, v as hs_full_attn_fwd_scores;
+ *   lse [batch][hq][T] from the forward;
+ *   dq [batch][T][hq][head_dim], dk, dv [batch][hkv][T][head_dim] fp32
+ *   (out, overwritten; dv is position-major).
+ * ws: hs_workspace_size(HS_FN_FULL_ATTN_BWD, shape, 64, 0, 0) bytes,
+ * 256-byte aligned (layout copies of K, V, Q and dO; row terms).
+ */
+hs_status hs_full_attn_bwd(const hs_shape* shape, const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, const void* dout, float* dq, float* dk,
+                           float* dv, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward pass of one sparse layer (bf16): the block-sparse branch over the
+ * shared K/V at the forward's indices (read as in the forward; they get no
+ * gradient), the window branch over the layer's own K'/V', the sigmoid gates
+ * (explainer 3.4.3), the sink logits (paper 4.1).  With s = sigmoid(G):
+ * each branch sees dO~ = s dO; dG = s (1 - s) dO.o_branch; a sink gets
+ * -sum_t p_sink dO~.o_branch.
+ *   q_sp, dout [batch][T][hq][head_dim]; k, v, idx, topk, k_swa, v_swa,
+ *   window, gate_logits, sinks: as in the forward call;
+ *   o_branch, lse_branch: from hs_sparse_attn_fwd_train;
+ *   dq_sp [batch][T][hq][head_dim] fp32 (out);
+ *   dk, dv [batch][hkv][T][head_dim] fp32: the shared K/V's gradients, to
+ *     which this layer's share is ADDED (pass those of the full layer's
+ *     backward, then every sparse layer's in turn);
+ *   dk_swa, dv_swa [batch][hkv][T][head_dim] fp32 (out; with window > 0);
+ *   dgate [batch][T][hq][2] fp32 (out; with gate_logits); dsinks [2][hq]
+ *   fp32 (out; with sinks).
+ * ws: hs_workspace_size(HS_FN_SPARSE_ATTN_BWD, shape, 64, topk, window)
+ * bytes, 256-byte aligned.
+ */
+hs_status hs_sparse_attn_bwd(const hs_shape* shape, const void* q_sp, const void* k, const void* v,
+                             const int32_t* idx, int topk, const void* k_swa, const void* v_swa,
+                             int window, const float* gate_logits, const float* sinks,
+                             const void* o_branch, const float* lse_branch, const void* dout,
+                             float* dq_sp, float* dk, float* dv, float* dk_swa, float* dv_swa,
+                             float* dgate, float* dsinks, void* ws, size_t ws_bytes, void* stream);
+
 /* Function ids for hs_workspace_size */
 #define HS_FN_FULL_ATTN 0
 #define HS_FN_BLOCK_TOPK 1
 #define HS_FN_SPARSE_ATTN 2
 #define HS_FN_DECODE_SELECT 3
+#define HS_FN_FULL_ATTN_BWD 4   /* prefill shape (kv_lens NULL) */
+#define HS_FN_SPARSE_ATTN_BWD 5 /* prefill shape (kv_lens NULL) */
 
 /* Workspace bytes the given entry point needs (or, for token-mode
  * hs_decode_select_attn, can use) for this shape; 0 if none.  `block`,
