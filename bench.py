@@ -397,6 +397,93 @@ def bench_decode_offload(cid: int, steps: int, chunk: int = 8):
             "gpu_bytes_full_cache_if_resident": (kt.numel() + vt.numel()) * 2}
 
 
+def bench_training(cid: int, steps: int, warmup: int):
+    """One training step of a prefill hybrid block (bf16): the forward (full
+    layer, selection, N sparse layers writing their branch outputs) and the
+    backward (full layer, then every sparse layer adding its share into the
+    shared dK/dV).  Algorithmic FLOPs: the forward's count, plus 2.5 times it
+    for the backward (per attended pair: S, dP, dV, dK, dQ at 2d each)."""
+    import torch
+
+    from hybrid_sparse_attention_causal_amd import binding as hb
+    from hybrid_sparse_attention_causal_amd import inputs as gen
+
+    cfg = gen.config(cid)
+    inp = gen.make_prefill(cfg)
+    B, T, Hq, Hkv, d, kb, W = cfg.B, cfg.T, cfg.Hq, cfg.Hkv, cfg.d, cfg.kb, cfg.W
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    q, k, vb = dev(inp.q), dev(inp.k), dev(gen.block_major(inp.v))
+    o = torch.empty((B, T, Hq, d), **bf)
+    lse = torch.empty((B, Hq, T), **f32)
+    raw = torch.empty((B, Hq, T, cfg.nblk), **f32)
+    idx = torch.empty((B, Hkv, T, kb), dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(77)
+    mk_do = lambda: dev(gen.f32_to_bf16_bits(rng.standard_normal((B, T, Hq, d)).astype(np.float32)))
+    do_full = mk_do()
+    dq = torch.empty((B, T, Hq, d), **f32)
+    dk = torch.empty((B, Hkv, T, d), **f32)
+    dv = torch.empty((B, Hkv, T, d), **f32)
+    layers = [dict(q=dev(l["q"]), k=dev(l["k"]), v=dev(gen.block_major(l["v"])), g=dev(l["gates"]),
+                   o=torch.empty((B, T, Hq, d), **bf), ob=torch.empty((2, B, T, Hq, d), **bf),
+                   lb=torch.empty((2, B, Hq, T), **f32), do=mk_do(), dq=torch.empty((B, T, Hq, d), **f32),
+                   dks=torch.empty((B, Hkv, T, d), **f32), dvs=torch.empty((B, Hkv, T, d), **f32),
+                   dg=torch.empty((B, T, Hq, 2), **f32)) for l in inp.layers]
+    ws = [None]
+    stream = torch.cuda.current_stream()
+    names = ["fwd_full", "fwd_topk"] + [f"fwd_sparse_{i}" for i in range(len(layers))] + ["bwd_full"] + \
+            [f"bwd_sparse_{i}" for i in range(len(layers))]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        hb.full_attn_fwd_scores(q, k, vb, o, lse, raw, stream=stream)
+        mark(1)
+        hb.block_topk((B, T, Hq, Hkv, d, hb.HS_BF16), raw, lse, kb, idx, stream=stream)
+        mark(2)
+        for i, l in enumerate(layers):
+            hb.sparse_attn_fwd_train(l["q"], k, vb, idx, kb, l["k"], l["v"], W, l["g"], l["o"], l["ob"], l["lb"],
+                                     stream=stream)
+            mark(3 + i)
+        n0 = 3 + len(layers)
+        ws[0] = hb.full_attn_bwd(q, k, vb, o, lse, do_full, dq, dk, dv, ws=ws[0], stream=stream)
+        mark(n0)
+        for i, l in enumerate(layers):
+            ws[0] = hb.sparse_attn_bwd(l["q"], k, vb, idx, kb, l["k"], l["v"], W, l["g"], None, l["ob"], l["lb"],
+                                       l["do"], l["dq"], dk, dv, l["dks"], l["dvs"], l["dg"], None, ws=ws[0],
+                                       stream=stream)
+            mark(n0 + 1 + i)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for st in range(steps):
+        step(evs[st])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    per = {n: float(np.mean([evs[st][i].elapsed_time(evs[st][i + 1]) for st in range(steps)]))
+           for i, n in enumerate(names)}
+    fwd = full_flops(cfg) + len(layers) * sparse_flops_per_layer(cfg)
+    total = 3.5 * fwd
+    bwd_full_flops = 2.5 * full_flops(cfg)
+    return {"workload": WORKLOAD_NAMES[cid] + ", training step (forward + backward)",
+            "ms_per_step": ms_step, "tokens_per_s": B * T / (ms_step * 1e-3),
+            "algorithmic_tflop": total / 1e12, "tflops": total / (ms_step * 1e-3) / 1e12,
+            "mfma_frac": total / (ms_step * 1e-3) / 1e12 / PEAK_BF16,
+            "bwd_full_tflops": bwd_full_flops / (per["bwd_full"] * 1e-3) / 1e12,
+            "kernel_ms": per}
+
+
 WORKLOAD_NAMES = {1: "tiny 1:3 hybrid block prefill", 2: "7B-shaped 1:3 hybrid block prefill",
                   3: "80B-MoE-shaped 1:11 hybrid block prefill"}
 
@@ -507,6 +594,8 @@ def main():
                     help="prefill workloads also timed and reported under prefill_extra")
     ap.add_argument("--fp8", type=int, nargs="*", default=[3], choices=[2, 3],
                     help="prefill workloads also timed with fp8 e4m3 Q/K/V (fp8 matrix products)")
+    ap.add_argument("--train", type=int, nargs="*", default=[2], choices=[1, 2, 3],
+                    help="prefill workloads also timed as a training step (forward + backward)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode", type=int, nargs="*", default=[4, 5], choices=[4, 5],
                     help="decode workloads also measured (default: 4 5); pass none to skip")
@@ -574,6 +663,8 @@ def main():
     if args.fp8:
         out["prefill_fp8"] = [bench_prefill(gen.make_prefill(gen.config(c, dtype="fp8")), args.steps,
                                              args.warmup, args.sinks) for c in args.fp8]
+    if args.train:
+        out["training"] = [bench_training(c, max(3, min(args.steps, 10)), 3) for c in args.train]
     if args.decode:
         out["decode"] = [bench_decode(c, max(3, min(args.steps, 10)), args.sinks) for c in args.decode]
     if args.offload:

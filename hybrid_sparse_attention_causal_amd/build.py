@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import glob
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -33,12 +34,37 @@ CFLAGS = [
 ]
 
 
+# Kernels allowed to use per-lane scratch (register spills). Spills on the hot
+# kernels cost several times their run time, so any other kernel that spills
+# fails the build. Only fp32-input variants, which are correctness paths and
+# not tuned, are listed.
+SCRATCH_ALLOWED = {
+    "_ZN2hs24sparse_prefill_pp_kernelILi0ELi64ELi2EEEvNS_17SparsePrefillArgsE",
+    "_ZN2hs21sparse_prefill_kernelILi0ELi128ELi1ELi8ELi2EEEvNS_17SparsePrefillArgsE",
+}
+_REMARK = "kernel-resource-usage"
+
+
 def _run(cmd):
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
     return out
+
+
+def _spills(remarks: str) -> dict:
+    """Kernel name -> scratch bytes per lane, from the resource-usage remarks."""
+    found, name = {}, None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and int(m.group(1)):
+            found[name] = int(m.group(1))
+    return found
 
 
 def build_library(verbose: bool = False) -> str:
@@ -48,7 +74,12 @@ def build_library(verbose: bool = False) -> str:
 
     def compile_one(so):
         src, obj = so
-        return _run([HIPCC, *CFLAGS, "-c", src, "-o", obj])
+        out = _run([HIPCC, *CFLAGS, f"-Rpass-analysis={_REMARK}", "-c", src, "-o", obj])
+        spills = {k: v for k, v in _spills(out).items() if k not in SCRATCH_ALLOWED}
+        if spills:
+            raise RuntimeError(f"{os.path.basename(src)}: kernels spill to scratch "
+                               f"(bytes/lane): {spills}")
+        return "\n".join(l for l in out.splitlines() if _REMARK not in l)
 
     with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
         outs = list(ex.map(compile_one, zip(srcs, objs)))

@@ -996,7 +996,7 @@ __global__ __launch_bounds__(512, 2) void sparse_prefill_pp_kernel(SparsePrefill
 // assignment, masking and the two branches are as in sparse_prefill_kernel;
 // column tile nt of wave w holds the G heads of the 16/G positions
 // tw0 + nt*16/G + col/G.
-template <int DT, int D, int NT>
+template <int DT, int D, int NT, bool TRAIN>
 __global__ __launch_bounds__(256, 2) void sparse_prefill_dual_kernel(SparsePrefillArgs a) {
   using Tt = Tr<DT>;
   using Eng = WaveAttn<DT, D, NT, true>;
@@ -1151,33 +1151,33 @@ __global__ __launch_bounds__(256, 2) void sparse_prefill_dual_kernel(SparsePrefi
 
   // Close a branch.  The first branch's gated output is parked in the output
   // rows themselves (in the output dtype) while the second branch runs and is
-  // added back when that one closes: no registers hold it in between.
-  // training forward: the branch's own (ungated) output and LSE
-  auto branch_out = [&](int nt, float inv, float l2, int br) {
-    const size_t row = (size_t)(b * T + tcol[nt]) * a.Hq + hcol;
-    char* bp = (char*)a.o_br + (((size_t)br * a.B * T * a.Hq + row) * D + 4 * (lane >> 4)) * ES;
-#pragma unroll
-    for (int mc = 0; mc < Eng::NM; ++mc) {
-      const f32x4 v = eng.o[nt][mc] * inv;
-      Tt::store4(bp + 16 * mc * ES, v[0], v[1], v[2], v[3]);
-    }
-    if ((lane >> 4) == 0) a.lse_br[((size_t)br * a.B * a.Hq + b * a.Hq + hcol) * T + tcol[nt]] = l2 * kLn2;
-  };
-  auto fold = [&](const float* gate, const float* sink, bool first) {
+  // added back when that one closes: no registers hold it in between.  The
+  // training forward also writes the branch's own (ungated) output and LSE.
+  auto fold = [&](const float* gate, const float* sink, bool first) __attribute__((always_inline)) {
+    const int br = first ? 1 : 0;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float inv, l2;
       eng.finish(nt, inv, l2, sink[nt]);
       const float sc = inv * gate[nt];
       if (live && tcol[nt] < T) {
-        char* op = (char*)a.o + (((size_t)(b * T + tcol[nt]) * a.Hq + hcol) * D + 4 * (lane >> 4)) * ES;
+        const size_t row = (size_t)(b * T + tcol[nt]) * a.Hq + hcol;
+        char* op = (char*)a.o + (row * D + 4 * (lane >> 4)) * ES;
 #pragma unroll
         for (int mc = 0; mc < Eng::NM; ++mc) {
           f32x4 v = eng.o[nt][mc] * sc;
           if (!first) v += Tt::load4(op + 16 * mc * ES);
           Tt::store4(op + 16 * mc * ES, v[0], v[1], v[2], v[3]);
         }
-        if (a.o_br) branch_out(nt, inv, l2, first ? 1 : 0);
+        if constexpr (TRAIN) {
+          char* bp = (char*)a.o_br + (((size_t)br * a.B * T * a.Hq + row) * D + 4 * (lane >> 4)) * ES;
+#pragma unroll
+          for (int mc = 0; mc < Eng::NM; ++mc) {
+            const f32x4 v = eng.o[nt][mc] * inv;
+            Tt::store4(bp + 16 * mc * ES, v[0], v[1], v[2], v[3]);
+          }
+          if ((lane >> 4) == 0) a.lse_br[((size_t)br * a.B * a.Hq + b * a.Hq + hcol) * T + tcol[nt]] = l2 * kLn2;
+        }
       }
     }
   };
@@ -1257,13 +1257,17 @@ __global__ __launch_bounds__(256, 2) void sparse_prefill_dual_kernel(SparsePrefi
   }
   if (nwin == nitems) {
     fold(gate1, sink1, true);
-    if (a.o_br) {  // no selected block: the sparse branch is empty (its sink alone)
-      eng.reset();
+    if constexpr (TRAIN) {  // no selected block: the sparse branch is empty (its sink alone)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        float inv, l2;
-        eng.finish(nt, inv, l2, sink0[nt]);
-        if (live && tcol[nt] < T) branch_out(nt, inv, l2, 0);
+        if (live && tcol[nt] < T) {
+          const float l2 = sink0[nt] > -INFINITY ? sink0[nt] : -INFINITY;  // log2 of the sink's weight alone
+          const size_t row = (size_t)(b * T + tcol[nt]) * a.Hq + hcol;
+          char* bp = (char*)a.o_br + (row * D + 4 * (lane >> 4)) * ES;
+#pragma unroll
+          for (int mc = 0; mc < Eng::NM; ++mc) Tt::store4(bp + 16 * mc * ES, 0.f, 0.f, 0.f, 0.f);
+          if ((lane >> 4) == 0) a.lse_br[((size_t)b * a.Hq + hcol) * T + tcol[nt]] = l2 * kLn2;
+        }
       }
     }
   } else {
@@ -1344,7 +1348,10 @@ static hipError_t sparse_dispatch(SparsePrefillArgs a, hipStream_t s) {
     const size_t lds = ((size_t)(1 + 4 + PWG) * nw32 + a.nblk + 1) * sizeof(uint32_t);
     if (lds <= 16 * 1024) {
       a.nwg = a.B * a.Hkv * ((a.T + PWG - 1) / PWG);
-      hipLaunchKernelGGL((sparse_prefill_dual_kernel<DT, D, NT>), dim3(a.nwg), dim3(256), lds, s, a);
+      if (a.o_br)
+        hipLaunchKernelGGL((sparse_prefill_dual_kernel<DT, D, NT, true>), dim3(a.nwg), dim3(256), lds, s, a);
+      else
+        hipLaunchKernelGGL((sparse_prefill_dual_kernel<DT, D, NT, false>), dim3(a.nwg), dim3(256), lds, s, a);
       return hipGetLastError();
     }
   }

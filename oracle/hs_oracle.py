@@ -495,9 +495,11 @@ def _attend_bwd(s, values, keys, q, do, tau, sink=None):
     return dq, dkeys, dvalues, dsink
 
 
-def full_attention_bwd(q, k, v, do, scale=None):
+def full_attention_bwd(q, k, v, do, scale=None, rows=None):
     """Backward of the full causal layer (eq. o_t of [X] 3.4.1).
-    q, do [T, Hq, d]; k, v [Hkv, T, d].  Returns dq [T, Hq, d], dk, dv [Hkv, T, d]."""
+    q, do [T, Hq, d]; k, v [Hkv, T, d].  Returns dq [T, Hq, d], dk, dv [Hkv, T, d].
+    rows: query positions to take (default all); dq is then exact at those
+    rows, and dk, dv hold only those rows' contributions."""
     T, Hq, d = q.shape
     Hkv = k.shape[0]
     G = Hq // Hkv
@@ -505,7 +507,7 @@ def full_attention_bwd(q, k, v, do, scale=None):
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    for t in range(T):
+    for t in (range(T) if rows is None else rows):
         for h in range(Hq):
             g = h // G
             s = tau * (k[g, : t + 1] @ q[t, h])
@@ -516,7 +518,7 @@ def full_attention_bwd(q, k, v, do, scale=None):
     return dq, dk, dv
 
 
-def sparse_layer_bwd(qs, k, v, idx, ks, vs, W, gates, do, block=BLOCK, scale=None, sinks=None):
+def sparse_layer_bwd(qs, k, v, idx, ks, vs, W, gates, do, block=BLOCK, scale=None, sinks=None, rows=None):
     """Backward of one sparse layer ([X] 3.4.3: block-sparse branch over the
     shared K/V at the inherited indices, window branch over the layer's own
     K'/V', sigmoid gates; reading R14 sinks).
@@ -525,7 +527,8 @@ def sparse_layer_bwd(qs, k, v, idx, ks, vs, W, gates, do, block=BLOCK, scale=Non
     Returns dict(dq [T,Hq,d], dk, dv [Hkv,T,d] (the shared K/V's share from
     this layer), dks, dvs [Hkv,T,d], dgates [T,Hq,2] or None, dsinks [2,Hq]
     or None).  With o = s0 o~ + s1 o' (s = sigmoid of the gate logits):
-    do~ = s0 do, do' = s1 do, dG0 = s0 (1 - s0) do.o~, dG1 likewise."""
+    do~ = s0 do, do' = s1 do, dG0 = s0 (1 - s0) do.o~, dG1 likewise.
+    rows: as in full_attention_bwd."""
     T, Hq, d = qs.shape
     Hkv = k.shape[0]
     G = Hq // Hkv
@@ -533,7 +536,7 @@ def sparse_layer_bwd(qs, k, v, idx, ks, vs, W, gates, do, block=BLOCK, scale=Non
     out = dict(dq=np.zeros_like(qs), dk=np.zeros_like(k), dv=np.zeros_like(v), dks=np.zeros_like(ks),
                dvs=np.zeros_like(vs), dgates=None if gates is None else np.zeros_like(gates),
                dsinks=None if sinks is None else np.zeros_like(sinks))
-    for t in range(T):
+    for t in (range(T) if rows is None else rows):
         for h in range(Hq):
             g = h // G
             sel = idx[g, t]

@@ -145,3 +145,100 @@ def test_sparse_layer_backward(T, Hq, Hkv, d, kb, W, gates, sinks):
         close("dgates", host(dg)[0], ref["dgates"])
     if sinks:
         close("dsinks", host(dsk), ref["dsinks"])
+
+
+def _block_backward(inp, cfg, kb, W, seed_do=11):
+    """Training forward and backward of a whole hybrid block on the GPU:
+    full layer + selection + N sparse layers, then the full layer's backward
+    and every sparse layer's, the latter adding into the shared dK/dV."""
+    B, T, Hq, Hkv, d = cfg.B, cfg.T, cfg.Hq, cfg.Hkv, cfg.d
+    q, k, vb = dev(inp.q), dev(inp.k), dev(gen.block_major(inp.v))
+    o = torch.empty((B, T, Hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq, T), device="cuda")
+    raw = torch.empty((B, Hq, T, cfg.nblk), device="cuda")
+    hb.full_attn_fwd_scores(q, k, vb, o, lse, raw)
+    idx = torch.empty((B, Hkv, T, kb), dtype=torch.int32, device="cuda")
+    hb.block_topk((B, T, Hq, Hkv, d, hb.HS_BF16), raw, lse, kb, idx)
+    r = np.random.default_rng(seed_do)
+    do_full = gen.f32_to_bf16_bits(r.standard_normal((B, T, Hq, d)).astype(np.float32))
+    dq = torch.empty((B, T, Hq, d), device="cuda")
+    dk = torch.empty((B, Hkv, T, d), device="cuda")
+    dv = torch.empty((B, Hkv, T, d), device="cuda")
+    ws = hb.full_attn_bwd(q, k, vb, o, lse, dev(do_full), dq, dk, dv)
+    layers = []
+    for lay in inp.layers:
+        qs, ks, vs, g = dev(lay["q"]), dev(lay["k"]), dev(gen.block_major(lay["v"])), dev(lay["gates"])
+        os_ = torch.empty((B, T, Hq, d), dtype=torch.bfloat16, device="cuda")
+        ob = torch.empty((2, B, T, Hq, d), dtype=torch.bfloat16, device="cuda")
+        lb = torch.empty((2, B, Hq, T), device="cuda")
+        hb.sparse_attn_fwd_train(qs, k, vb, idx, kb, ks, vs, W, g, os_, ob, lb)
+        do_l = gen.f32_to_bf16_bits(r.standard_normal((B, T, Hq, d)).astype(np.float32))
+        dql = torch.empty((B, T, Hq, d), device="cuda")
+        dks = torch.empty((B, Hkv, T, d), device="cuda")
+        dvs = torch.empty((B, Hkv, T, d), device="cuda")
+        dg = torch.empty((B, T, Hq, 2), device="cuda")
+        ws = hb.sparse_attn_bwd(qs, k, vb, idx, kb, ks, vs, W, g, None, ob, lb, dev(do_l), dql, dk, dv, dks, dvs,
+                                dg, None, ws=ws)
+        layers.append(dict(do=do_l, dq=dql, dks=dks, dvs=dvs, dg=dg, ob=ob))
+    torch.cuda.synchronize()
+    return dict(idx=idx, do=do_full, dq=dq, dk=dk, dv=dv, o=o, layers=layers)
+
+
+def test_hybrid_block_backward_accumulates():
+    """T = 1024 (16 tiles), two sparse layers: the shared dK/dV equal the full
+    layer's gradient plus both sparse layers' shares (oracle, all rows)."""
+    say("[bwd hybrid block] T=1024 Hq=8 Hkv=2 d=128 kb=4 W=128, 2 sparse layers")
+    cfg = gen.config(1, T=1024, Hq=8, Hkv=2, d=128, dtype="bf16", kb=4, W=128, N=2)
+    inp = gen.make_prefill(cfg)
+    res = _block_backward(inp, cfg, cfg.kb, cfg.W)
+    f = lambda n, l=None: inp.f64(n, l)[0]
+    up = lambda bits: gen.bf16_bits_to_f32(bits[0]).astype(np.float64)
+    rq, rk, rv = ora.full_attention_bwd(f("q"), f("k"), f("v"), up(res["do"]))
+    idx = host(res["idx"])[0].astype(np.int64)
+    for l, lay in enumerate(res["layers"]):
+        g = ora.sparse_layer_bwd(f("q", l), f("k"), f("v"), idx, f("k", l), f("v", l), cfg.W, f("gates", l),
+                                 up(lay["do"]))
+        rk = rk + g["dk"]
+        rv = rv + g["dv"]
+        close(f"layer {l} dq", host(lay["dq"])[0], g["dq"])
+        close(f"layer {l} dk window", host(lay["dks"])[0], g["dks"])
+        close(f"layer {l} dgates", host(lay["dg"])[0], g["dgates"])
+    close("full dq", host(res["dq"])[0], rq)
+    close("shared dk (full + 2 sparse)", host(res["dk"])[0], rk)
+    close("shared dv (full + 2 sparse)", host(res["dv"])[0], rv)
+
+
+def test_backward_7b_shape_sampled():
+    """The 7B-shaped block (T = 8192, 32/8 heads, 3 sparse layers): dQ of the
+    full layer and of sparse layer 0 on sampled rows against the oracle's
+    row-local backward; the shared dK/dV through two identities that hold at
+    any size: for every kv group, the dV rows sum to the gated dO summed over
+    the queries that reach a key ((sum_i p_ti) = 1 per branch with keys),
+    and the dK rows sum to zero (sum_i dS_ti = 0 per row)."""
+    say("[bwd 7B-shaped] T=8192 Hq=32 Hkv=8 d=128, 3 sparse layers")
+    cfg = gen.config(2)
+    inp = gen.make_prefill(cfg)
+    res = _block_backward(inp, cfg, cfg.kb, cfg.W)
+    f = lambda n, l=None: inp.f64(n, l)[0]
+    up = lambda bits: gen.bf16_bits_to_f32(bits[0]).astype(np.float64)
+    rows = np.array([0, 1, 63, 64, 1000, 4095, 4096, 6000, 8190, 8191])
+    rq, _, _ = ora.full_attention_bwd(f("q"), f("k"), f("v"), up(res["do"]), rows=rows)
+    close("full dq (sampled rows)", host(res["dq"])[0][rows], rq[rows])
+    idx = host(res["idx"])[0].astype(np.int64)
+    lay0 = res["layers"][0]
+    g = ora.sparse_layer_bwd(f("q", 0), f("k"), f("v"), idx, f("k", 0), f("v", 0), cfg.W, f("gates", 0),
+                             up(lay0["do"]), rows=rows)
+    close("layer 0 dq (sampled rows)", host(lay0["dq"])[0][rows], g["dq"][rows])
+    close("layer 0 dgates (sampled rows)", host(lay0["dg"])[0][rows], g["dgates"][rows])
+    # identities: sum over keys of dV = sum over (t, h in g) of dO~ of every
+    # branch that reaches keys of this cache; sum over keys of dK = 0
+    G = cfg.G
+    want = up(res["do"]).reshape(cfg.T, cfg.Hkv, G, cfg.d).sum(axis=(0, 2))      # full layer
+    sig = lambda x: 1.0 / (1.0 + np.exp(-x))
+    for l, lay in enumerate(res["layers"]):
+        s0 = sig(f("gates", l)[..., 0])[..., None]                                # [T, Hq, 1]
+        has = (idx >= 0).any(axis=2).T[:, :, None].repeat(G, axis=1)              # [T, Hq, 1] any selected block
+        dob = up(lay["do"]) * s0 * has
+        want = want + dob.reshape(cfg.T, cfg.Hkv, G, cfg.d).sum(axis=(0, 2))
+    close("sum_i dV (shared)", host(res["dv"])[0].sum(axis=1), want)
+    close("sum_i dK (shared) = 0", host(res["dk"])[0].sum(axis=1), np.zeros((cfg.Hkv, cfg.d)))
