@@ -278,8 +278,8 @@ def sparse_attn_fwd_train(q_sp, k, v_blk, idx, topk, k_swa, v_swa_blk, window, g
                                            _ptr(o), _ptr(o_branch), _ptr(lse_branch), _stream(stream)))
 
 
-def _bwd_ws(fn_id, s, device, ws):
-    need = load().hs_workspace_size(fn_id, ctypes.byref(s), 64, 0, 0)
+def _bwd_ws(fn_id, s, device, ws, topk=0):
+    need = load().hs_workspace_size(fn_id, ctypes.byref(s), 64, topk, 0)
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
     return ws
@@ -309,7 +309,7 @@ def sparse_attn_bwd(q_sp, k, v_blk, idx, topk, k_swa, v_swa_blk, window, gate_lo
     B, T, Hq, d = q_sp.shape
     Hkv = (k if k is not None else k_swa).shape[1]
     s = make_shape(B, T, T, Hq, Hkv, d, dtype_code(q_sp), scale=scale)
-    ws = _bwd_ws(HS_FN_SPARSE_ATTN_BWD, s, q_sp.device, ws)
+    ws = _bwd_ws(HS_FN_SPARSE_ATTN_BWD, s, q_sp.device, ws, topk)
     _check(load().hs_sparse_attn_bwd(ctypes.byref(s), _ptr(q_sp), _ptr(k), _ptr(v_blk), _ptr(idx), topk,
                                      _ptr(k_swa), _ptr(v_swa_blk), window, _ptr(gate_logits), _ptr(sinks),
                                      _ptr(o_branch), _ptr(lse_branch), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),

@@ -180,15 +180,16 @@ size_t offload_ws(const hs_shape* s, int chunk) {
   return 2 * align256(hs::offload_stage_bytes(chunk, s->hkv, s->kv_len, s->head_dim, 2)) + decode_full_ws(&c);
 }
 
-// backward workspace: layout copies, per-row terms, selection bitsets
+// backward workspace: layout copies, per-row terms, per-column statistics,
+// the sparse branch's position lists
 struct BwdWs {
-  size_t kb[2], vp[2], qT, doT, delta[2], sterm[2], bits, total;
+  size_t kb[2], vp[2], qT, doT, delta[2], sterm[2], cstat[2], colbits, plist, pcnt, poff, total;
 };
 int bwd_nc(const hs_shape* s) {
-  const long cols = (long)s->q_len * (s->hq / s->hkv) + 32;
+  const long cols = (long)s->q_len * hs::bwd_gp(s->hq / s->hkv) + 32;
   return (int)((cols + 63) / 64 * 64);
 }
-BwdWs bwd_ws(const hs_shape* s, bool sparse) {
+BwdWs bwd_ws(const hs_shape* s, bool sparse, int topk) {
   BwdWs w{};
   const size_t B = s->batch, T = s->q_len, D = s->head_dim, Hkv = s->hkv, Hq = s->hq;
   const size_t nblk = (T + 63) / 64, nw32 = (nblk + 31) / 32;
@@ -206,9 +207,14 @@ BwdWs bwd_ws(const hs_shape* s, bool sparse) {
   w.qT = take(B * Hkv * D * bwd_nc(s) * 2);
   w.doT = take(B * Hkv * D * bwd_nc(s) * 2);
   for (int i = 0; i < nbr; ++i) w.delta[i] = take(B * Hq * T * 4);
+  for (int i = 0; i < nbr; ++i) w.cstat[i] = take(B * Hkv * 3 * (size_t)bwd_nc(s) * 4);
   if (sparse) {
+    (void)nw32;
     for (int i = 0; i < 2; ++i) w.sterm[i] = take(B * Hq * T * 4);
-    w.bits = take(B * Hkv * T * nw32 * 4);
+    w.colbits = take(B * Hkv * nblk * ((T + 31) / 32) * 4);
+    w.plist = take(B * Hkv * T * (size_t)(topk > 0 ? topk : 1) * 4);
+    w.pcnt = take(B * Hkv * nblk * 4);
+    w.poff = take(B * Hkv * nblk * 4);
   }
   w.total = off;
   return w;
@@ -234,11 +240,10 @@ const char* hs_last_error(void) { return g_err.c_str(); }
 
 size_t hs_workspace_size(int fn_id, const hs_shape* shape, int block, int topk, int window) {
   (void)block;
-  (void)topk;
   (void)window;
   if (!shape || shape->struct_size < kShapeMinSize || shape->hkv <= 0 || shape->hq <= 0) return 0;
   if (!shape->kv_lens && (fn_id == HS_FN_FULL_ATTN_BWD || fn_id == HS_FN_SPARSE_ATTN_BWD))
-    return bwd_ws(shape, fn_id == HS_FN_SPARSE_ATTN_BWD).total;
+    return bwd_ws(shape, fn_id == HS_FN_SPARSE_ATTN_BWD, topk < 0 ? 0 : topk).total;
   if (!shape->kv_lens) return 0;
   if (fn_id == HS_FN_FULL_ATTN) return decode_full_ws(shape);
   if (fn_id == HS_FN_BLOCK_TOPK && block == 1) return token_topk_ws(shape);
@@ -738,7 +743,7 @@ hs_status hs_full_attn_bwd(const hs_shape* s, const void* q, const void* k, cons
   REQUIRE_PTR(dq);
   REQUIRE_PTR(dk);
   REQUIRE_PTR(dv);
-  const BwdWs w = bwd_ws(s, false);
+  const BwdWs w = bwd_ws(s, false, 0);
   if (!ws || ws_bytes < w.total)
     return fail(HS_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, w.total, ws_bytes);
   if ((uintptr_t)ws & 255u) return fail(HS_ERR_INVALID_ARG, "%s: ws not 256-byte aligned", fn);
@@ -762,15 +767,21 @@ hs_status hs_full_attn_bwd(const hs_shape* s, const void* q, const void* k, cons
   l.Hkv = s->hkv;
   l.nblk = nblk;
   l.NC = bwd_nc(s);
+  l.Gp = hs::bwd_gp(s->hq / s->hkv);
   hipError_t e = hs::launch_bwd_layouts(l, s->head_dim, strm);
   if (e != hipSuccess) return launched(fn, e);
   hs::BwdRowArgs r{};
   r.o[0] = o;
   r.dout = dout;
   r.delta[0] = (float*)(W + w.delta[0]);
+  r.lse_col[0] = lse;
+  r.cstat[0] = (float*)(W + w.cstat[0]);
   r.B = s->batch;
   r.T = s->q_len;
   r.Hq = s->hq;
+  r.Hkv = s->hkv;
+  r.Gp = l.Gp;
+  r.NC = l.NC;
   r.D = s->head_dim;
   r.nbr = 1;
   e = hs::launch_bwd_rows(r, strm);
@@ -783,8 +794,7 @@ hs_status hs_full_attn_bwd(const hs_shape* s, const void* q, const void* k, cons
   a.doT = l.doT;
   a.k = k;
   a.vp = l.vp[0];
-  a.lse = lse;
-  a.delta = r.delta[0];
+  a.cstat = r.cstat[0];
   a.dk = dk;
   a.dv = dv;
   a.B = s->batch;
@@ -793,6 +803,7 @@ hs_status hs_full_attn_bwd(const hs_shape* s, const void* q, const void* k, cons
   a.Hkv = s->hkv;
   a.nblk = nblk;
   a.NC = l.NC;
+  a.Gp = l.Gp;
   a.sc2 = scale_log2(s);
   a.tau = tau;
   e = hs::launch_bwd_kv(a, 0, s->head_dim, strm);
@@ -850,7 +861,7 @@ hs_status hs_sparse_attn_bwd(const hs_shape* s, const void* q_sp, const void* k,
   }
   if (gate_logits && !dgate) return fail(HS_ERR_INVALID_ARG, "%s: gate_logits given without dgate", fn);
   if (sinks && !dsinks) return fail(HS_ERR_INVALID_ARG, "%s: sinks given without dsinks", fn);
-  const BwdWs w = bwd_ws(s, true);
+  const BwdWs w = bwd_ws(s, true, topk);
   if (!ws || ws_bytes < w.total)
     return fail(HS_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, w.total, ws_bytes);
   if ((uintptr_t)ws & 255u) return fail(HS_ERR_INVALID_ARG, "%s: ws not 256-byte aligned", fn);
@@ -883,11 +894,15 @@ hs_status hs_sparse_attn_bwd(const hs_shape* s, const void* q_sp, const void* k,
   l.Hkv = s->hkv;
   l.nblk = nblk;
   l.NC = bwd_nc(s);
+  l.Gp = hs::bwd_gp(s->hq / s->hkv);
   hipError_t e = hs::launch_bwd_layouts(l, s->head_dim, strm);
   if (e != hipSuccess) return launched(fn, e);
-  uint32_t* bits = (uint32_t*)(W + w.bits);
+  int32_t* plist = (int32_t*)(W + w.plist);
+  int32_t* pcnt = (int32_t*)(W + w.pcnt);
+  int32_t* poff = (int32_t*)(W + w.poff);
   if (topk > 0) {
-    e = hs::launch_selbits(idx, bits, s->batch, s->hkv, T, topk, nblk, strm);
+    e = hs::launch_pos_lists(idx, (uint32_t*)(W + w.colbits), plist, pcnt, poff, s->batch, s->hkv, T, topk, nblk,
+                             strm);
     if (e != hipSuccess) return launched(fn, e);
   }
   hs::BwdRowArgs r{};
@@ -904,9 +919,16 @@ hs_status hs_sparse_attn_bwd(const hs_shape* s, const void* q_sp, const void* k,
   r.sterm[0] = (float*)(W + w.sterm[0]);
   r.sterm[1] = (float*)(W + w.sterm[1]);
   r.dsinks = dsinks;
+  r.lse_col[0] = r.lse[0];
+  r.lse_col[1] = r.lse[1];
+  if (topk > 0) r.cstat[0] = (float*)(W + w.cstat[0]);
+  if (window > 0) r.cstat[1] = (float*)(W + w.cstat[1]);
   r.B = s->batch;
   r.T = T;
   r.Hq = s->hq;
+  r.Hkv = s->hkv;
+  r.Gp = l.Gp;
+  r.NC = l.NC;
   r.D = s->head_dim;
   r.nbr = 2;
   e = hs::launch_bwd_rows(r, strm);
@@ -917,26 +939,26 @@ hs_status hs_sparse_attn_bwd(const hs_shape* s, const void* q_sp, const void* k,
   a.dout = dout;
   a.qT = l.qT;
   a.doT = l.doT;
-  a.gates = gate_logits;
   a.B = s->batch;
   a.T = T;
   a.Hq = s->hq;
   a.Hkv = s->hkv;
   a.nblk = nblk;
   a.W = window;
-  a.nw32 = (nblk + 31) / 32;
   a.NC = l.NC;
+  a.Gp = l.Gp;
+  a.topk = topk;
   a.sc2 = scale_log2(s);
   a.tau = tau;
   if (topk > 0) {  // the sparse branch adds into the shared K/V's gradients
     a.k = k;
     a.vp = l.vp[0];
-    a.lse = r.lse[0];
-    a.delta = r.delta[0];
-    a.selbits = bits;
+    a.cstat = r.cstat[0];
+    a.plist = plist;
+    a.pcnt = pcnt;
+    a.poff = poff;
     a.dk = dk;
     a.dv = dv;
-    a.br = 0;
     a.accumulate = 1;
     e = hs::launch_bwd_kv(a, 2, s->head_dim, strm);
     if (e != hipSuccess) return launched(fn, e);
@@ -944,12 +966,10 @@ hs_status hs_sparse_attn_bwd(const hs_shape* s, const void* q_sp, const void* k,
   if (window > 0) {
     a.k = k_swa;
     a.vp = l.vp[1];
-    a.lse = r.lse[1];
-    a.delta = r.delta[1];
-    a.selbits = nullptr;
+    a.cstat = r.cstat[1];
+    a.plist = nullptr;
     a.dk = dk_swa;
     a.dv = dv_swa;
-    a.br = 1;
     a.accumulate = 0;
     e = hs::launch_bwd_kv(a, 1, s->head_dim, strm);
     if (e != hipSuccess) return launched(fn, e);

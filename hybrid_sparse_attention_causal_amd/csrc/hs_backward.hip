@@ -18,15 +18,20 @@
 //            (A operands of dK^T = Q^T dS and dV^T = dO^T P)
 //
 //  bwd_kv_kernel  key side: one work group per (sequence, kv group, 64-key
-//                 tile), wave w owning keys 16w..16w+15; loops over the
-//                 query tiles (32 columns = 32/G positions x G heads) that
-//                 can attend the tile: S = Q K^T and dP = dO V^T with the
-//                 queries as M rows (lane = key, 8 consecutive columns), so
-//                 P and dS are directly the B operands of dV^T += dO^T P and
-//                 dK^T += Q^T dS.  Modes: full layer (causal), window branch
-//                 (t - W < key <= t), sparse branch (the positions that
-//                 selected the block; query tiles where none did are
-//                 skipped).
+//                 block), wave w owning keys 16w..16w+15 (K and V rows in
+//                 registers).  It walks the positions that attend the block
+//                 in tiles of 32 columns (32/Gp positions x Gp heads): the
+//                 tile's Q and dO rows, its Q^T and dO^T columns and its
+//                 per-column statistics are staged in LDS by direct
+//                 transfers, one tile ahead, and shared by the four waves.
+//                 S = Q K^T and dP = dO V^T take the queries as M rows (lane
+//                 = key, 8 consecutive columns), so P and dS are directly the
+//                 B operands of dV^T += dO^T P and dK^T += Q^T dS.  Positions:
+//                 full layer t >= 64j (causal), window branch t in
+//                 [64j, 64j + 63 + W - 1], sparse branch the ascending list of
+//                 the positions that selected the block (built from the
+//                 indices first, so no tile without a selecting position is
+//                 visited).
 //  bwd_q_kernel   query side: work groups of 4*16/G positions as in the
 //                 forward; per item (key tile) S^T = K Q^T and dP^T = V dO^T
 //                 (K rows and V rows staged in LDS), dS^T elementwise, then
@@ -95,11 +100,12 @@ __global__ __launch_bounds__(256) void v_to_posmajor_kernel(const uint16_t* v, u
   }
 }
 
-// X [B][T][Hq][D] -> XT [B*Hkv][D][NC]: column c = t*G + hh holds head
-// g*G + hh of position t; zero for c >= T*G.  One work group per 64 columns.
+// X [B][T][Hq][D] -> XT [B*Hkv][D][NC]: column c = t*Gp + hh holds head
+// g*G + hh of position t; zero for hh >= G and for c >= T*Gp.  One work group
+// per 64 columns.
 template <int D>
 __global__ __launch_bounds__(256) void rows_to_dmajor_kernel(const uint16_t* x, uint16_t* xt, int T, int Hq, int Hkv,
-                                                             int NC) {
+                                                             int NC, int Gp) {
   __shared__ uint16_t tl[64][D + 2];
   const int nch = NC / 64;
   const int ch = blockIdx.x % nch;
@@ -107,9 +113,9 @@ __global__ __launch_bounds__(256) void rows_to_dmajor_kernel(const uint16_t* x, 
   const int g = bg % Hkv, b = bg / Hkv, G = Hq / Hkv;
   for (int e = threadIdx.x; e < 64 * D / 8; e += 256) {
     const int r = e / (D / 8), c = e % (D / 8);
-    const int col = 64 * ch + r, t = col / G, hh = col % G;
-    const uint4 v = t < T ? *(const uint4*)(x + (((size_t)b * T + t) * Hq + g * G + hh) * D + 8 * c)
-                          : make_uint4(0u, 0u, 0u, 0u);
+    const int col = 64 * ch + r, t = col / Gp, hh = col % Gp;
+    const uint4 v = (t < T && hh < G) ? *(const uint4*)(x + (((size_t)b * T + t) * Hq + g * G + hh) * D + 8 * c)
+                                      : make_uint4(0u, 0u, 0u, 0u);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -158,6 +164,13 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdRowArgs a) {
       const float s = a.gates ? 1.f / (1.f + expf(-a.gates[(size_t)rr * 2 + br])) : 1.f;
       if (a.dgates) a.dgates[(size_t)rr * 2 + br] = s * (1.f - s) * acc;
       if (a.sinks) a.sterm[br][ri] = -expf(a.sinks[br * a.Hq + h] - a.lse[br][ri]) * s * acc;
+      if (a.cstat[br]) {  // the key side's per-column copy (column t*Gp + hh of the kv group)
+        const int G = a.Hq / a.Hkv;
+        float* cs = a.cstat[br] + ((size_t)b * a.Hkv + h / G) * 3 * a.NC + (size_t)t * a.Gp + h % G;
+        cs[0] = a.lse_col[br][ri] * kLog2e;
+        cs[a.NC] = acc;
+        cs[2 * (size_t)a.NC] = s;
+      }
     }
   }
 }
@@ -178,43 +191,155 @@ __global__ __launch_bounds__(256) void bwd_sink_reduce_kernel(BwdRowArgs a) {
   if (threadIdx.x == 0) a.dsinks[br * a.Hq + h] = part[0] + part[1] + part[2] + part[3];
 }
 
-// selection bitsets [B*Hkv][T][nw32]: bit j of row t set when the row's list
-// holds j with 0 <= j < nblk and 64 j <= t (the forward's rule)
+// Position lists of the sparse branch.  colbits [B*Hkv][nblk][nwt] (nwt =
+// ceil(T/32)): bit t of block j's row is set when position t's list holds j
+// with 0 <= j < nblk and 64 j <= t (the forward's rule; duplicates count
+// once).
 __global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, long n) {
   for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) p[i] = 0u;
 }
-__global__ __launch_bounds__(256) void selbits_kernel(const int32_t* idx, uint32_t* bits, long n, int T, int topk,
-                                                      int nblk, int nw32) {
+__global__ __launch_bounds__(256) void colbits_kernel(const int32_t* idx, uint32_t* bits, long n, int T, int topk,
+                                                      int nblk, int nwt) {
   const long e = (long)blockIdx.x * 256 + threadIdx.x;
   if (e >= n) return;
-  const long rowi = e / topk;  // (bg, t)
+  const long rowi = e / topk;  // bg * T + t
   const int t = (int)(rowi % T);
+  const long bg = rowi / T;
   const int j = idx[e];
-  if (j >= 0 && j < nblk && 64 * j <= t) atomicOr(&bits[rowi * nw32 + (j >> 5)], 1u << (j & 31));
+  if (j >= 0 && j < nblk && 64 * j <= t) atomicOr(&bits[(bg * nblk + j) * nwt + (t >> 5)], 1u << (t & 31));
+}
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+// one wave per (kv group, block): list length
+__global__ __launch_bounds__(256) void pos_count_kernel(const uint32_t* bits, int32_t* pcnt, int nbj, int nblk,
+                                                        int nwt) {
+  const int wv = (int)(((long)blockIdx.x * 256 + threadIdx.x) >> 6), lane = threadIdx.x & 63;
+  if (wv >= nbj) return;  // wave-uniform
+  const uint32_t* row = bits + (size_t)wv * nwt;
+  int c = 0;
+  for (int w = 2 * (wv % nblk) + lane; w < nwt; w += 64) c += __popc(row[w]);
+  c = wave_sum(c);
+  if (lane == 0) pcnt[wv] = c;
+}
+// one wave per (kv group, block): its offset (the lengths of the group's
+// earlier blocks) and its positions, ascending
+__global__ __launch_bounds__(256) void pos_write_kernel(const uint32_t* bits, const int32_t* pcnt, int32_t* poff,
+                                                        int32_t* plist, int nbj, int nblk, int nwt, long cap) {
+  const int wv = (int)(((long)blockIdx.x * 256 + threadIdx.x) >> 6), lane = threadIdx.x & 63;
+  if (wv >= nbj) return;  // wave-uniform
+  const int bg = wv / nblk, j = wv % nblk;
+  int off = 0;
+  for (int jj = lane; jj < j; jj += 64) off += pcnt[bg * nblk + jj];
+  off = wave_sum(off);
+  if (lane == 0) poff[wv] = off;
+  int32_t* out = plist + bg * cap + off;
+  const uint32_t* row = bits + (size_t)wv * nwt;
+  int base = 0;
+  for (int w0 = 2 * j; w0 < nwt; w0 += 64) {
+    const int w = w0 + lane;
+    uint32_t word = w < nwt ? row[w] : 0u;
+    const int cnt = __popc(word);
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    int pos = base + incl - cnt;
+    while (word) {
+      out[pos++] = 32 * w + __builtin_ctz(word);
+      word &= word - 1u;
+    }
+    base += __shfl(incl, 63);
+  }
 }
 
 // ============================================================ key side
+// LDS layout of one staged query tile (32 columns) of the key side.  Column
+// slot c of the tile is (position slot c / Gp, head c % Gp).
+//   rows   Q and dO rows, row R holding column colmap(R) (so that the A
+//          fragments of S chunk e are rows 16e .. 16e+15); the 16-byte chunk
+//          p of row R sits at p ^ (R & KSW)
+//   dmaj   Q^T and dO^T: D rows of 32 columns (64 bytes); chunk p of row R at
+//          p ^ ((R >> 2) & 3)
+//   stat   lse*log2(e), dO.o, sigma(gate) of the 32 columns (transferred,
+//          with 128 bytes of padding)
+template <int D>
+struct KvStage {
+  static constexpr int KS = D * 2;
+  static constexpr int KCH = KS / 16;
+  static constexpr int KSW = (KCH < 16 ? KCH : 16) - 1;
+  static constexpr int QB = 32 * KS;
+  static constexpr int TB = D * 64;
+  static constexpr int OQ = 0, OD = QB, OQT = 2 * QB, ODT = 2 * QB + TB, OS = 2 * QB + 2 * TB;
+  static constexpr int BYTES = OS + 512;
+  static constexpr int NQI = QB / 1024;  // row-tile transfers of 16 bytes per lane
+  static constexpr int NTI = TB / 256;   // d-major transfers of 4 bytes per lane
+  static_assert(NQI % 4 == 0 && NTI % 4 == 0, "transfers do not split over four waves");
+  __device__ __forceinline__ static int colmap(int R) {
+    return 8 * ((R & 15) >> 2) + 4 * (R >> 4) + (R & 3);
+  }
+};
+constexpr int kPosChunk = 256;  // positions staged in LDS at a time
+
 template <int D, int MODE>
-__global__ __launch_bounds__(256) void bwd_kv_kernel(BwdKVArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdKVArgs a) {
   using Tt = Tr<HS_BF16>;
   using Frag = Tt::Frag;
+  using KS_ = KvStage<D>;
   constexpr int NS = D / 32, NM = D / 16;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) char buf0[KS_::BYTES];
+  __shared__ __attribute__((aligned(16))) char buf1[KS_::BYTES];
+  __shared__ int posl[kPosChunk];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, q4 = lane >> 4;
-  const int j = blockIdx.x % a.nblk;
-  const int bg = blockIdx.x / a.nblk;
+  const int nbg = a.B * a.Hkv;
+  const int bg = blockIdx.x % nbg, j = blockIdx.x / nbg;  // early (long) blocks first
   const int g = bg % a.Hkv, b = bg / a.Hkv;
-  const int G = a.Hq / a.Hkv;
+  const int G = a.Hq / a.Hkv, Gp = a.Gp;
+  const int lgGp = 31 - __clz(Gp);
+  const int PQ = 32 >> lgGp;  // positions per tile
   const int T = a.T;
   const int key = 64 * j + 16 * w + r16;
-  const int keyc = min(key, T - 1);
-  Frag kf[NS], vf[NS];
-  const char* krow = (const char*)a.k + ((size_t)bg * T + keyc) * D * 2;
-  const char* vrow = (const char*)a.vp + ((size_t)bg * a.nblk * 64 + key) * D * 2;
+
+  int npos, pbase = 64 * j;
+  if (MODE == 2) {
+    npos = a.pcnt[bg * a.nblk + j];
+    pbase = a.poff[bg * a.nblk + j];
+  } else if (MODE == 1) {
+    npos = min(T - 1, 64 * j + 63 + a.W - 1) - 64 * j + 1;
+  } else {
+    npos = T - 64 * j;
+  }
+  float* dkp = a.dk + ((size_t)bg * T + key) * D + 4 * q4;
+  float* dvp = a.dv + ((size_t)bg * T + key) * D + 4 * q4;
+  if (npos <= 0) {  // nothing attends the block (sparse branch): its share is 0
+    if (!a.accumulate && key < T) {
 #pragma unroll
-  for (int ks = 0; ks < NS; ++ks) {
-    kf[ks] = Tt::ld(krow + (32 * ks + 8 * q4) * 2);
-    vf[ks] = Tt::ld(vrow + (32 * ks + 8 * q4) * 2);
+      for (int mc = 0; mc < NM; ++mc) {
+        *(float4*)(dkp + 16 * mc) = make_float4(0.f, 0.f, 0.f, 0.f);
+        *(float4*)(dvp + 16 * mc) = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    return;
+  }
+
+  // the wave's 16 keys and values as B operands (lane: key r16, 8 dims)
+  Frag kf[NS], vf[NS];
+  {
+    const int keyc = min(key, T - 1);
+    const char* krow = (const char*)a.k + ((size_t)bg * T + keyc) * D * 2;
+    const char* vrow = (const char*)a.vp + ((size_t)bg * a.nblk * 64 + key) * D * 2;
+#pragma unroll
+    for (int ks = 0; ks < NS; ++ks) {
+      kf[ks] = Tt::ld(krow + (32 * ks + 8 * q4) * 2);
+      vf[ks] = Tt::ld(vrow + (32 * ks + 8 * q4) * 2);
+    }
   }
   f32x4 dkT[NM], dvT[NM];
 #pragma unroll
@@ -222,65 +347,136 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdKVArgs a) {
     dkT[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
     dvT[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const int PQ = 32 / G;  // positions per query tile
-  const int t_lo = 64 * j;
-  const int t_hi = MODE == 1 ? min(T - 1, 64 * j + 63 + a.W - 1) : T - 1;
-  const char* qT = (const char*)a.qT + (size_t)bg * D * a.NC * 2;
-  const char* doT = (const char*)a.doT + (size_t)bg * D * a.NC * 2;
-  for (int tile = t_lo / PQ; tile <= t_hi / PQ; ++tile) {
-    const int tq0 = tile * PQ;
-    if (MODE == 2) {  // no position of the tile selected the block: skip
-      bool sel = false;
-      if (lane < PQ && tq0 + lane < T)
-        sel = (a.selbits[((size_t)bg * T + tq0 + lane) * a.nw32 + (j >> 5)] >> (j & 31)) & 1u;
-      if (__ballot(sel) == 0ull) continue;
+  const char* qg = (const char*)a.q + (size_t)b * T * a.Hq * D * 2;
+  const char* dg = (const char*)a.dout + (size_t)b * T * a.Hq * D * 2;
+  const char* qTg = (const char*)a.qT + (size_t)bg * D * a.NC * 2;
+  const char* dTg = (const char*)a.doT + (size_t)bg * D * a.NC * 2;
+  const float* csg = a.cstat + (size_t)bg * 3 * a.NC;
+
+  int nc = 0;  // positions in the current chunk
+  // tile `it` of the chunk (positions posl[it*PQ ..]) -> buf
+  auto issue = [&](int it, char* buf) {
+    const int pb = it * PQ;
+#pragma unroll
+    for (int k = 0; k < KS_::NQI / 4; ++k) {
+      const int n = w + 4 * k;
+      const int o = 1024 * n + 16 * lane;
+      const int R = o / KS_::KS, lc = ((o % KS_::KS) >> 4) ^ (R & KS_::KSW);
+      const int c = KS_::colmap(R);
+      const int t = posl[pb + (c >> lgGp)];
+      const int hh = min(c & (Gp - 1), G - 1);
+      const size_t ro = (((size_t)t * a.Hq + g * G + hh) * D) * 2 + 16 * lc;
+      const char* s1 = qg + ro;
+      const char* s2 = dg + ro;
+      __builtin_amdgcn_global_load_lds(s1, (__attribute__((address_space(3))) void*)(buf + KS_::OQ + 1024 * n), 16,
+                                       0, 0);
+      __builtin_amdgcn_global_load_lds(s2, (__attribute__((address_space(3))) void*)(buf + KS_::OD + 1024 * n), 16,
+                                       0, 0);
     }
-    // S, dP: chunk e holds columns 8(rho/4) + 4e + rho%4 as M rows
+#pragma unroll
+    for (int k = 0; k < KS_::NTI / 4; ++k) {
+      const int n = w + 4 * k;
+      const int R = 4 * n + (lane >> 4), pdw = lane & 15;
+      const int ldw = 4 * ((pdw >> 2) ^ ((R >> 2) & 3)) + (pdw & 3);
+      const int c = 2 * ldw;
+      const int t = posl[pb + (c >> lgGp)];
+      const size_t to = ((size_t)R * a.NC + (size_t)t * Gp + (c & (Gp - 1))) * 2;
+      const char* s1 = qTg + to;
+      const char* s2 = dTg + to;
+      __builtin_amdgcn_global_load_lds(s1, (__attribute__((address_space(3))) void*)(buf + KS_::OQT + 256 * n), 4,
+                                       0, 0);
+      __builtin_amdgcn_global_load_lds(s2, (__attribute__((address_space(3))) void*)(buf + KS_::ODT + 256 * n), 4,
+                                       0, 0);
+    }
+    if (w < 2) {  // statistics: 96 floats, lanes past them reload the last array into the padding
+      const int ix = 64 * w + lane;
+      const int arr = min(ix >> 5, 2), c = ix & 31;
+      const int t = posl[pb + (c >> lgGp)];
+      const float* s1 = csg + (size_t)arr * a.NC + (size_t)t * Gp + (c & (Gp - 1));
+      __builtin_amdgcn_global_load_lds(s1, (__attribute__((address_space(3))) void*)(buf + KS_::OS + 256 * w), 4, 0,
+                                       0);
+    }
+  };
+
+  auto compute = [&](int it, const char* cur) {
     f32x4 S[2], dP[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int c = 8 * (r16 >> 2) + 4 * e + (r16 & 3);
-      const int tc = min(tq0 + c / G, T - 1), h = g * G + c % G;
-      const char* qrow = (const char*)a.q + (((size_t)b * T + tc) * a.Hq + h) * D * 2;
-      const char* drow = (const char*)a.dout + (((size_t)b * T + tc) * a.Hq + h) * D * 2;
       S[e] = f32x4{0.f, 0.f, 0.f, 0.f};
       dP[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < NS; ++ks) {
-        Tt::mma(S[e], Tt::ld(qrow + (32 * ks + 8 * q4) * 2), kf[ks]);
-        Tt::mma(dP[e], Tt::ld(drow + (32 * ks + 8 * q4) * 2), vf[ks]);
-      }
     }
-    // the lane holds key `key` and columns 8q4 .. 8q4+7
+#pragma unroll
+    for (int ks = 0; ks < NS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int R = 16 * e + r16;
+        const int off = R * KS_::KS + 16 * ((4 * ks + q4) ^ (R & KS_::KSW));
+        Tt::mma(S[e], Tt::ld(cur + KS_::OQ + off), kf[ks]);
+        Tt::mma(dP[e], Tt::ld(cur + KS_::OD + off), vf[ks]);
+      }
+    // the lane's columns 8 q4 .. 8 q4 + 7: element 4e + i is column 8 q4 + 4e + i
+    const float* st = (const float*)(cur + KS_::OS) + 8 * q4;
+    const float4 l0 = *(const float4*)st, l1 = *(const float4*)(st + 4);
+    const float4 d0 = *(const float4*)(st + 32), d1 = *(const float4*)(st + 36);
+    const float4 g0 = *(const float4*)(st + 64), g1 = *(const float4*)(st + 68);
+    const float lse2[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+    const float dl[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+    const float sg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    // each column's position: -1 past the chunk's positions or for a padding head
+    int tp[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int c = 8 * q4 + k, slot = it * PQ + (c >> lgGp);
+      tp[k] = (slot < nc && (c & (Gp - 1)) < G) ? posl[slot] : -1;
+    }
     float ps[8], ds[8];
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int c = 8 * q4 + 4 * e + i;
-        const int t = tq0 + c / G, h = g * G + c % G;
-        const int tc = min(t, T - 1);
-        const size_t ri = ((size_t)b * a.Hq + h) * T + tc;
-        bool valid = t < T && key <= t;
-        if (MODE == 1) valid = valid && key > t - a.W;
-        if (MODE == 2)
-          valid = valid && ((a.selbits[((size_t)bg * T + tc) * a.nw32 + (j >> 5)] >> (j & 31)) & 1u);
-        const float sg = a.gates ? 1.f / (1.f + expf(-a.gates[(((size_t)b * T + tc) * a.Hq + h) * 2 + a.br])) : 1.f;
-        const float p = valid ? fast_exp2(S[e][i] * a.sc2 - a.lse[ri] * kLog2e) : 0.f;
-        ps[4 * e + i] = p * sg;
-        ds[4 * e + i] = p * sg * (dP[e][i] - a.delta[ri]);
+        const int k = 4 * e + i;
+        bool valid = tp[k] >= 0 && key <= tp[k] && key < T;
+        if (MODE == 1) valid = valid && key > tp[k] - a.W;
+        const float p = fast_exp2(S[e][i] * a.sc2 - lse2[k]) * sg[k];
+        ps[k] = valid ? p : 0.f;
+        ds[k] = valid ? p * (dP[e][i] - dl[k]) : 0.f;
       }
     const Frag pf = Tt::pack(ps), dsf = Tt::pack(ds);
 #pragma unroll
     for (int mc = 0; mc < NM; ++mc) {
-      const size_t off = ((size_t)(16 * mc + r16) * a.NC + (size_t)tq0 * G + 8 * q4) * 2;
-      Tt::mma(dvT[mc], Tt::ld(doT + off), pf);
-      Tt::mma(dkT[mc], Tt::ld(qT + off), dsf);
+      const int R = 16 * mc + r16;
+      const int off = R * 64 + 16 * (q4 ^ ((R >> 2) & 3));
+      Tt::mma(dvT[mc], Tt::ld(cur + KS_::ODT + off), pf);
+      Tt::mma(dkT[mc], Tt::ld(cur + KS_::OQT + off), dsf);
+    }
+  };
+
+  int nit = 0;
+  auto step = [&](int it, const char* cur, char* next) {
+    if (it + 1 < nit) issue(it + 1, next);
+    compute(it, cur);
+    wait_vmem();
+    __syncthreads();
+  };
+  for (int c0 = 0; c0 < npos; c0 += kPosChunk) {
+    nc = min(kPosChunk, npos - c0);
+    __syncthreads();  // the previous chunk's tiles and positions are no longer read
+    {
+      const int i = min((int)threadIdx.x, nc - 1);
+      posl[threadIdx.x] = MODE == 2 ? a.plist[(size_t)bg * T * a.topk + pbase + c0 + i] : pbase + c0 + i;
+    }
+    __syncthreads();
+    nit = (nc + PQ - 1) / PQ;
+    issue(0, buf0);
+    wait_vmem();
+    __syncthreads();
+    for (int it = 0; it < nit; it += 2) {
+      step(it, buf0, buf1);
+      if (it + 1 >= nit) break;
+      step(it + 1, buf1, buf0);
     }
   }
   if (key < T) {
-    float* dkp = a.dk + ((size_t)bg * T + key) * D + 4 * q4;
-    float* dvp = a.dv + ((size_t)bg * T + key) * D + 4 * q4;
 #pragma unroll
     for (int mc = 0; mc < NM; ++mc) {
       float4 x = make_float4(a.tau * dkT[mc][0], a.tau * dkT[mc][1], a.tau * dkT[mc][2], a.tau * dkT[mc][3]);
@@ -534,9 +730,9 @@ static hipError_t layouts(const BwdLayoutArgs& l, hipStream_t s) {
   }
   const unsigned nrt = (unsigned)((long)l.B * l.Hkv * (l.NC / 64));
   hipLaunchKernelGGL(rows_to_dmajor_kernel<D>, dim3(nrt), dim3(256), 0, s, (const uint16_t*)l.q, (uint16_t*)l.qT,
-                     l.T, l.Hq, l.Hkv, l.NC);
+                     l.T, l.Hq, l.Hkv, l.NC, l.Gp);
   hipLaunchKernelGGL(rows_to_dmajor_kernel<D>, dim3(nrt), dim3(256), 0, s, (const uint16_t*)l.dout,
-                     (uint16_t*)l.doT, l.T, l.Hq, l.Hkv, l.NC);
+                     (uint16_t*)l.doT, l.T, l.Hq, l.Hkv, l.NC, l.Gp);
   return hipGetLastError();
 }
 
@@ -553,17 +749,21 @@ hipError_t launch_bwd_rows(const BwdRowArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_selbits(const int32_t* idx, uint32_t* bits, int B, int Hkv, int T, int topk, int nblk,
-                          hipStream_t s) {
-  const int nw32 = (nblk + 31) / 32;
-  const long nw = (long)B * Hkv * T * nw32;
-  hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, s, bits, nw);
+hipError_t launch_pos_lists(const int32_t* idx, uint32_t* colbits, int32_t* plist, int32_t* pcnt, int32_t* poff,
+                            int B, int Hkv, int T, int topk, int nblk, hipStream_t s) {
+  const int nwt = (T + 31) / 32;
+  const int nbj = B * Hkv * nblk;
+  hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, s, colbits, (long)nbj * nwt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long n = (long)B * Hkv * T * topk;
   if (n > 0)
-    hipLaunchKernelGGL(selbits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx, bits, n, T, topk,
-                       nblk, nw32);
+    hipLaunchKernelGGL(colbits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx, colbits, n, T, topk,
+                       nblk, nwt);
+  const unsigned nwg = (unsigned)((nbj + 3) / 4);
+  hipLaunchKernelGGL(pos_count_kernel, dim3(nwg), dim3(256), 0, s, colbits, pcnt, nbj, nblk, nwt);
+  hipLaunchKernelGGL(pos_write_kernel, dim3(nwg), dim3(256), 0, s, colbits, pcnt, poff, plist, nbj, nblk, nwt,
+                     (long)T * topk);
   return hipGetLastError();
 }
 

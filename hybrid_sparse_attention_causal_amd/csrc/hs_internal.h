@@ -164,10 +164,13 @@ struct BwdLayoutArgs {
   void* vp[2];       // out: values position-major [B][Hkv][nblk*64][D]
   const void* q;     // [B][T][Hq][D]
   const void* dout;
-  void* qT;          // out: [B][Hkv][D][NC]
+  void* qT;          // out: [B][Hkv][D][NC], column t*Gp + hh (zero for hh >= G)
   void* doT;
-  int B, T, Hq, Hkv, nblk, NC;
+  int B, T, Hq, Hkv, nblk, NC, Gp;
 };
+// columns per position in the d-major copies: the group size, at least 2, so
+// that one position's piece of a d-row is a whole number of dwords
+inline int bwd_gp(int G) { return G < 2 ? 2 : G; }
 struct BwdRowArgs {
   const void* o[2];     // branch outputs [B][T][Hq][D] bf16 (the layer output for the full layer)
   const void* dout;
@@ -178,7 +181,11 @@ struct BwdRowArgs {
   float* dgates;        // out (gated layers): [B][T][Hq][2]
   float* sterm[2];      // scratch (sinks): [B][Hq][T]
   float* dsinks;        // out (sinks): [2][Hq]
-  int B, T, Hq, D, nbr;
+  // per-column statistics for the key side, in the column order of the
+  // d-major copies: [B*Hkv][3][NC] = lse * log2(e), dO . o_br, sigma(gate)
+  const float* lse_col[2];  // the branch's row LSE [B][Hq][T] (natural log)
+  float* cstat[2];
+  int B, T, Hq, D, nbr, Hkv, Gp, NC;
 };
 struct BwdKVArgs {
   const void* q;
@@ -187,13 +194,13 @@ struct BwdKVArgs {
   const void* doT;
   const void* k;        // this branch's keys [B][Hkv][T][D]
   const void* vp;       // this branch's values, position-major
-  const float* lse;     // this branch's LSE [B][Hq][T]
-  const float* delta;   // dO . o_br
-  const float* gates;
-  const uint32_t* selbits;  // sparse branch: [B][Hkv][T][nw32]
+  const float* cstat;   // this branch's per-column statistics (BwdRowArgs::cstat)
+  const int32_t* plist; // sparse branch: positions that selected each block, ascending
+  const int32_t* pcnt;  // [B*Hkv][nblk] list lengths
+  const int32_t* poff;  // [B*Hkv][nblk] list offsets within the kv group's T*topk slots
   float* dk;
   float* dv;
-  int B, T, Hq, Hkv, nblk, W, nw32, NC, br, accumulate;
+  int B, T, Hq, Hkv, nblk, W, NC, Gp, topk, accumulate;
   float sc2, tau;
 };
 struct BwdQArgs {
@@ -218,8 +225,11 @@ struct BwdQArgs {
 };
 hipError_t launch_bwd_layouts(const BwdLayoutArgs& l, int D, hipStream_t s);
 hipError_t launch_bwd_rows(const BwdRowArgs& a, hipStream_t s);
-hipError_t launch_selbits(const int32_t* idx, uint32_t* bits, int B, int Hkv, int T, int topk, int nblk,
-                          hipStream_t s);
+// per (kv group, block) lists of the positions that selected the block (the
+// forward's rule), ascending: colbits [B*Hkv][nblk][ceil(T/32)] scratch,
+// plist [B*Hkv][T*topk], pcnt and poff [B*Hkv][nblk]
+hipError_t launch_pos_lists(const int32_t* idx, uint32_t* colbits, int32_t* plist, int32_t* pcnt, int32_t* poff,
+                            int B, int Hkv, int T, int topk, int nblk, hipStream_t s);
 hipError_t launch_bwd_kv(const BwdKVArgs& a, int mode, int D, hipStream_t s);  // mode 0 full, 1 window, 2 sparse
 hipError_t launch_bwd_q(const BwdQArgs& a, int mode, int D, hipStream_t s);    // mode 0 full, 1 sparse layer
 size_t bwd_q_lds_bytes(int T, int G);
