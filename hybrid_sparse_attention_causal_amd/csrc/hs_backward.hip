@@ -365,7 +365,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdKVArgs a) {
       const int c = KS_::colmap(R);
       const int t = posl[pb + (c >> lgGp)];
       const int hh = min(c & (Gp - 1), G - 1);
-      const size_t ro = (((size_t)t * a.Hq + g * G + hh) * D) * 2 + 16 * lc;
+      const uint32_t ro = (uint32_t)((t * a.Hq + g * G + hh) * D) * 2u + 16u * lc;
       const char* s1 = qg + ro;
       const char* s2 = dg + ro;
       __builtin_amdgcn_global_load_lds(s1, (__attribute__((address_space(3))) void*)(buf + KS_::OQ + 1024 * n), 16,
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdKVArgs a) {
       const int ldw = 4 * ((pdw >> 2) ^ ((R >> 2) & 3)) + (pdw & 3);
       const int c = 2 * ldw;
       const int t = posl[pb + (c >> lgGp)];
-      const size_t to = ((size_t)R * a.NC + (size_t)t * Gp + (c & (Gp - 1))) * 2;
+      const uint32_t to = (uint32_t)(R * a.NC + t * Gp + (c & (Gp - 1))) * 2u;
       const char* s1 = qTg + to;
       const char* s2 = dTg + to;
       __builtin_amdgcn_global_load_lds(s1, (__attribute__((address_space(3))) void*)(buf + KS_::OQT + 256 * n), 4,
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdKVArgs a) {
       const int ix = 64 * w + lane;
       const int arr = min(ix >> 5, 2), c = ix & 31;
       const int t = posl[pb + (c >> lgGp)];
-      const float* s1 = csg + (size_t)arr * a.NC + (size_t)t * Gp + (c & (Gp - 1));
+      const float* s1 = csg + (uint32_t)(arr * a.NC + t * Gp + (c & (Gp - 1)));
       __builtin_amdgcn_global_load_lds(s1, (__attribute__((address_space(3))) void*)(buf + KS_::OS + 256 * w), 4, 0,
                                        0);
     }
@@ -415,32 +415,29 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdKVArgs a) {
         Tt::mma(dP[e], Tt::ld(cur + KS_::OD + off), vf[ks]);
       }
     // the lane's columns 8 q4 .. 8 q4 + 7: element 4e + i is column 8 q4 + 4e + i
+    // (statistics and positions taken four columns at a time)
     const float* st = (const float*)(cur + KS_::OS) + 8 * q4;
-    const float4 l0 = *(const float4*)st, l1 = *(const float4*)(st + 4);
-    const float4 d0 = *(const float4*)(st + 32), d1 = *(const float4*)(st + 36);
-    const float4 g0 = *(const float4*)(st + 64), g1 = *(const float4*)(st + 68);
-    const float lse2[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-    const float dl[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-    const float sg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    // each column's position: -1 past the chunk's positions or for a padding head
-    int tp[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int c = 8 * q4 + k, slot = it * PQ + (c >> lgGp);
-      tp[k] = (slot < nc && (c & (Gp - 1)) < G) ? posl[slot] : -1;
-    }
     float ps[8], ds[8];
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
+    for (int e = 0; e < 2; ++e) {
+      const float4 l4 = *(const float4*)(st + 4 * e);
+      const float4 d4 = *(const float4*)(st + 32 + 4 * e);
+      const float4 g4 = *(const float4*)(st + 64 + 4 * e);
+      const float lse2[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+      const float sg[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int k = 4 * e + i;
-        bool valid = tp[k] >= 0 && key <= tp[k] && key < T;
-        if (MODE == 1) valid = valid && key > tp[k] - a.W;
-        const float p = fast_exp2(S[e][i] * a.sc2 - lse2[k]) * sg[k];
-        ps[k] = valid ? p : 0.f;
-        ds[k] = valid ? p * (dP[e][i] - dl[k]) : 0.f;
+        // the column's position; none past the chunk's positions or for a padding head
+        const int c = 8 * q4 + 4 * e + i, slot = it * PQ + (c >> lgGp);
+        const int tp = posl[slot];
+        bool valid = slot < nc && (c & (Gp - 1)) < G && key <= tp && key < T;
+        if (MODE == 1) valid = valid && key > tp - a.W;
+        const float p = fast_exp2(S[e][i] * a.sc2 - lse2[i]) * sg[i];
+        ps[4 * e + i] = valid ? p : 0.f;
+        ds[4 * e + i] = valid ? p * (dP[e][i] - dl[i]) : 0.f;
       }
+    }
     const Frag pf = Tt::pack(ps), dsf = Tt::pack(ds);
 #pragma unroll
     for (int mc = 0; mc < NM; ++mc) {
@@ -451,14 +448,20 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdKVArgs a) {
     }
   };
 
+  // Tiles are visited from the latest positions down: the work groups that
+  // start together (one kv group per XCD, successive blocks) then read the
+  // same query tiles at about the same time, so most of their transfers hit
+  // in L2.
   int nit = 0;
-  auto step = [&](int it, const char* cur, char* next) {
-    if (it + 1 < nit) issue(it + 1, next);
-    compute(it, cur);
+  auto step = [&](int k, const char* cur, char* next) {  // k-th tile visited: nit - 1 - k
+    if (k + 1 < nit) issue(nit - 2 - k, next);
+    compute(nit - 1 - k, cur);
     wait_vmem();
     __syncthreads();
   };
-  for (int c0 = 0; c0 < npos; c0 += kPosChunk) {
+  const int nch = (npos + kPosChunk - 1) / kPosChunk;
+  for (int ci = nch - 1; ci >= 0; --ci) {
+    const int c0 = ci * kPosChunk;
     nc = min(kPosChunk, npos - c0);
     __syncthreads();  // the previous chunk's tiles and positions are no longer read
     {
@@ -467,13 +470,13 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdKVArgs a) {
     }
     __syncthreads();
     nit = (nc + PQ - 1) / PQ;
-    issue(0, buf0);
+    issue(nit - 1, buf0);
     wait_vmem();
     __syncthreads();
-    for (int it = 0; it < nit; it += 2) {
-      step(it, buf0, buf1);
-      if (it + 1 >= nit) break;
-      step(it + 1, buf1, buf0);
+    for (int k = 0; k < nit; k += 2) {
+      step(k, buf0, buf1);
+      if (k + 1 >= nit) break;
+      step(k + 1, buf1, buf0);
     }
   }
   if (key < T) {
