@@ -55,8 +55,9 @@ def sparse_flops_per_layer(cfg, kb=None, W=None) -> float:
     return 4.0 * cfg.d * cfg.Hq * cfg.B * keys.sum()
 
 
-# the sources the prefill kernels are built from
-PREFILL_SOURCES = ("hs_prefill.hip", "hs_device.h", "hs_internal.h")
+# the sources the prefill kernels are built from (their argument structs are
+# declared next to the kernels' other interfaces, which change more often)
+PREFILL_SOURCES = ("hs_prefill.hip", "hs_device.h")
 TRAFFIC_FILES = {2: "sparse_prefill_7b_hbm_traffic.txt", 3: "sparse_prefill_32k_hbm_traffic.txt"}
 
 
