@@ -50,6 +50,18 @@ Readings where the pages leave a step open:
       code * scale (dequantize_e4m3); rounding the probabilities to fp8 for
       the value product is the kernels' approximation, covered by the fp8
       tolerance, not part of the definition.
+  R16 Backward ([P] 4.1 trains the architecture end to end; [X] 3.4 shares
+      the full layer's K/V with every sparse layer): the selection is a
+      discrete choice of the forward pass, so indices and block scores get no
+      gradient; each branch is a softmax attention with its own LSE; with
+      o = s0 o~ + s1 o' (s = sigmoid of the gate logits), do~ = s0 do,
+      do' = s1 do and dG_b = s_b (1 - s_b) do.o_b; the sparse branch's dK/dV
+      is this layer's share of the shared K/V's gradient.
+  R17 Offloaded cache ([P] 5, KV offloading): the compact cache holds whole
+      fully-past selected blocks (the decode candidates of R2), each once,
+      ascending (gather_blocks).
+  R18 Index rows are sets: any order, duplicates once, -1 and out-of-range
+      ids ignored anywhere in a row (K~, V~ of [X] 3.4.3 is a union).
   R14 Sink biases ([P] 4.1, "Experiments Setup": per-head learnable sink
       biases in the sparse and the window branch, following gpt-oss): each
       branch's softmax takes one extra logit b_h, in the units of tau q.k,
