@@ -180,10 +180,10 @@ size_t offload_ws(const hs_shape* s, int chunk) {
   return 2 * align256(hs::offload_stage_bytes(chunk, s->hkv, s->kv_len, s->head_dim, 2)) + decode_full_ws(&c);
 }
 
-// backward workspace: layout copies, per-row terms, per-column statistics,
-// the sparse branch's position lists
+// backward workspace: layout copies of K and V, per-row terms, per-column
+// statistics, the sparse branch's position lists
 struct BwdWs {
-  size_t kb[2], vp[2], qT, doT, delta[2], sterm[2], cstat[2], colbits, plist, pcnt, poff, total;
+  size_t kb[2], vp[2], delta[2], sterm[2], cstat[2], colbits, plist, pcnt, poff, total;
 };
 int bwd_nc(const hs_shape* s) {
   const long cols = (long)s->q_len * hs::bwd_gp(s->hq / s->hkv) + 32;
@@ -204,8 +204,6 @@ BwdWs bwd_ws(const hs_shape* s, bool sparse, int topk) {
     w.kb[i] = take(B * Hkv * nblk * D * 64 * 2);
     w.vp[i] = take(B * Hkv * nblk * 64 * D * 2);
   }
-  w.qT = take(B * Hkv * D * bwd_nc(s) * 2);
-  w.doT = take(B * Hkv * D * bwd_nc(s) * 2);
   for (int i = 0; i < nbr; ++i) w.delta[i] = take(B * Hq * T * 4);
   for (int i = 0; i < nbr; ++i) w.cstat[i] = take(B * Hkv * 3 * (size_t)bwd_nc(s) * 4);
   if (sparse) {
@@ -757,17 +755,12 @@ hs_status hs_full_attn_bwd(const hs_shape* s, const void* q, const void* k, cons
   l.v[0] = v;
   l.kb[0] = W + w.kb[0];
   l.vp[0] = W + w.vp[0];
-  l.q = q;
-  l.dout = dout;
-  l.qT = W + w.qT;
-  l.doT = W + w.doT;
   l.B = s->batch;
   l.T = s->q_len;
   l.Hq = s->hq;
   l.Hkv = s->hkv;
   l.nblk = nblk;
-  l.NC = bwd_nc(s);
-  l.Gp = hs::bwd_gp(s->hq / s->hkv);
+  const int NC = bwd_nc(s), Gp = hs::bwd_gp(s->hq / s->hkv);
   hipError_t e = hs::launch_bwd_layouts(l, s->head_dim, strm);
   if (e != hipSuccess) return launched(fn, e);
   hs::BwdRowArgs r{};
@@ -780,8 +773,8 @@ hs_status hs_full_attn_bwd(const hs_shape* s, const void* q, const void* k, cons
   r.T = s->q_len;
   r.Hq = s->hq;
   r.Hkv = s->hkv;
-  r.Gp = l.Gp;
-  r.NC = l.NC;
+  r.Gp = Gp;
+  r.NC = NC;
   r.D = s->head_dim;
   r.nbr = 1;
   e = hs::launch_bwd_rows(r, strm);
@@ -790,8 +783,6 @@ hs_status hs_full_attn_bwd(const hs_shape* s, const void* q, const void* k, cons
   hs::BwdKVArgs a{};
   a.q = q;
   a.dout = dout;
-  a.qT = l.qT;
-  a.doT = l.doT;
   a.k = k;
   a.vp = l.vp[0];
   a.cstat = r.cstat[0];
@@ -802,8 +793,8 @@ hs_status hs_full_attn_bwd(const hs_shape* s, const void* q, const void* k, cons
   a.Hq = s->hq;
   a.Hkv = s->hkv;
   a.nblk = nblk;
-  a.NC = l.NC;
-  a.Gp = l.Gp;
+  a.NC = NC;
+  a.Gp = Gp;
   a.sc2 = scale_log2(s);
   a.tau = tau;
   e = hs::launch_bwd_kv(a, 0, s->head_dim, strm);
@@ -884,17 +875,12 @@ hs_status hs_sparse_attn_bwd(const hs_shape* s, const void* q_sp, const void* k,
     l.kb[i] = W + w.kb[i];
     l.vp[i] = W + w.vp[i];
   }
-  l.q = q_sp;
-  l.dout = dout;
-  l.qT = W + w.qT;
-  l.doT = W + w.doT;
   l.B = s->batch;
   l.T = T;
   l.Hq = s->hq;
   l.Hkv = s->hkv;
   l.nblk = nblk;
-  l.NC = bwd_nc(s);
-  l.Gp = hs::bwd_gp(s->hq / s->hkv);
+  const int NC = bwd_nc(s), Gp = hs::bwd_gp(s->hq / s->hkv);
   hipError_t e = hs::launch_bwd_layouts(l, s->head_dim, strm);
   if (e != hipSuccess) return launched(fn, e);
   int32_t* plist = (int32_t*)(W + w.plist);
@@ -927,8 +913,8 @@ hs_status hs_sparse_attn_bwd(const hs_shape* s, const void* q_sp, const void* k,
   r.T = T;
   r.Hq = s->hq;
   r.Hkv = s->hkv;
-  r.Gp = l.Gp;
-  r.NC = l.NC;
+  r.Gp = Gp;
+  r.NC = NC;
   r.D = s->head_dim;
   r.nbr = 2;
   e = hs::launch_bwd_rows(r, strm);
@@ -937,16 +923,14 @@ hs_status hs_sparse_attn_bwd(const hs_shape* s, const void* q_sp, const void* k,
   hs::BwdKVArgs a{};
   a.q = q_sp;
   a.dout = dout;
-  a.qT = l.qT;
-  a.doT = l.doT;
   a.B = s->batch;
   a.T = T;
   a.Hq = s->hq;
   a.Hkv = s->hkv;
   a.nblk = nblk;
   a.W = window;
-  a.NC = l.NC;
-  a.Gp = l.Gp;
+  a.NC = NC;
+  a.Gp = Gp;
   a.topk = topk;
   a.sc2 = scale_log2(s);
   a.tau = tau;

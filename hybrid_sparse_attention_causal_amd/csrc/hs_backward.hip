@@ -11,11 +11,10 @@
 // (sigma = 1 for the full layer and ungated layers).
 //
 // Every matrix product reads its operands in the order the MFMA wants, from
-// layout copies made first (memory-bound transposes):
+// layout copies made first (memory-bound transposes) or, for the queries and
+// output gradients, from transposing LDS reads:
 //   Kb  keys block-major [..][nblk][D][64]   (A operand of dQ^T = K^T dS^T)
 //   Vp  values position-major [..][T][D]     (dP = dO V^T, both orientations)
-//   QT, dOT  queries / output gradients d-major per kv group [..][D][T*G]
-//            (A operands of dK^T = Q^T dS and dV^T = dO^T P)
 //
 //  bwd_kv_kernel  key side: one work group per (sequence, kv group, 64-key
 //                 block), wave w owning keys 16w..16w+15 (K and V rows in
@@ -43,6 +42,8 @@
 #include "hs_internal.h"
 
 namespace hs {
+
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 
 // ================================================== layout conversions
 // K [B*Hkv][T][D] -> Kb [B*Hkv][nblk][D][64], zero past T
@@ -97,39 +98,6 @@ __global__ __launch_bounds__(256) void v_to_posmajor_kernel(const uint16_t* v, u
     for (int i = 0; i < 4; ++i)
       w[i] = in ? ((uint32_t)tl[8 * c + 2 * i][r] | ((uint32_t)tl[8 * c + 2 * i + 1][r] << 16)) : 0u;
     *(uint4*)(vp + (bg * nblk * 64 + 64 * j + r) * D + 8 * c) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
-// X [B][T][Hq][D] -> XT [B*Hkv][D][NC]: column c = t*Gp + hh holds head
-// g*G + hh of position t; zero for hh >= G and for c >= T*Gp.  One work group
-// per 64 columns.
-template <int D>
-__global__ __launch_bounds__(256) void rows_to_dmajor_kernel(const uint16_t* x, uint16_t* xt, int T, int Hq, int Hkv,
-                                                             int NC, int Gp) {
-  __shared__ uint16_t tl[64][D + 2];
-  const int nch = NC / 64;
-  const int ch = blockIdx.x % nch;
-  const int bg = blockIdx.x / nch;
-  const int g = bg % Hkv, b = bg / Hkv, G = Hq / Hkv;
-  for (int e = threadIdx.x; e < 64 * D / 8; e += 256) {
-    const int r = e / (D / 8), c = e % (D / 8);
-    const int col = 64 * ch + r, t = col / Gp, hh = col % Gp;
-    const uint4 v = (t < T && hh < G) ? *(const uint4*)(x + (((size_t)b * T + t) * Hq + g * G + hh) * D + 8 * c)
-                                      : make_uint4(0u, 0u, 0u, 0u);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tl[r][8 * c + 2 * i] = (uint16_t)(w[i] & 0xffffu);
-      tl[r][8 * c + 2 * i + 1] = (uint16_t)(w[i] >> 16);
-    }
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < D * 8; e += 256) {
-    const int dd = e / 8, c = e % 8;
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)tl[8 * c + 2 * i][dd] | ((uint32_t)tl[8 * c + 2 * i + 1][dd] << 16);
-    *(uint4*)(xt + ((size_t)bg * D + dd) * NC + 64 * ch + 8 * c) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -258,32 +226,42 @@ __global__ __launch_bounds__(256) void pos_write_kernel(const uint32_t* bits, co
 }
 
 // ============================================================ key side
-// LDS layout of one staged query tile (32 columns) of the key side.  Column
-// slot c of the tile is (position slot c / Gp, head c % Gp).
-//   rows   Q and dO rows, row R holding column colmap(R) (so that the A
-//          fragments of S chunk e are rows 16e .. 16e+15); the 16-byte chunk
-//          p of row R sits at p ^ (R & KSW)
-//   dmaj   Q^T and dO^T: D rows of 32 columns (64 bytes); chunk p of row R at
-//          p ^ ((R >> 2) & 3)
-//   stat   lse*log2(e), dO.o, sigma(gate) of the 32 columns (transferred,
-//          with 128 bytes of padding)
+// LDS layout of one staged query tile (32 columns) of the key side.  Column c
+// of the tile is (position slot c / Gp, head c % Gp); row c of the row tiles
+// holds column c's Q (or dO) row, its 16-byte chunk p at p ^ swz(c).  The
+// swizzle keeps both readers free of bank conflicts: the A fragments of S
+// (rows 8(r/4) + 4e + r%4, r = 0..15, one chunk) and the transposing reads
+// that build the A fragments of dO^T and Q^T (4 rows x 2 chunks per 16
+// lanes).  The statistics (lse*log2(e), dO.o, sigma(gate) of the 32 columns)
+// follow, transferred with padding to 1 KiB.
 template <int D>
 struct KvStage {
   static constexpr int KS = D * 2;
   static constexpr int KCH = KS / 16;
-  static constexpr int KSW = (KCH < 16 ? KCH : 16) - 1;
   static constexpr int QB = 32 * KS;
-  static constexpr int TB = D * 64;
-  static constexpr int OQ = 0, OD = QB, OQT = 2 * QB, ODT = 2 * QB + TB, OS = 2 * QB + 2 * TB;
-  static constexpr int BYTES = OS + 512;
-  static constexpr int NQI = QB / 1024;  // row-tile transfers of 16 bytes per lane
-  static constexpr int NTI = TB / 256;   // d-major transfers of 4 bytes per lane
-  static_assert(NQI % 4 == 0 && NTI % 4 == 0, "transfers do not split over four waves");
-  __device__ __forceinline__ static int colmap(int R) {
-    return 8 * ((R & 15) >> 2) + 4 * (R >> 4) + (R & 3);
+  static constexpr int OQ = 0, OD = QB, OS = 2 * QB;
+  static constexpr int BYTES = OS + 1024;
+  static constexpr int NQI = QB / 1024;   // row-tile transfers of 16 bytes per lane
+  static constexpr int NDMA = NQI / 2 + 1;  // transfers per wave and tile (Q, dO rows; statistics)
+  static_assert(NQI % 4 == 0 || NQI == 4, "row tiles do not split over four waves");
+  // D = 128 (16 chunks per row, one bank sweep): the S reads of 16 lanes take
+  // rows 8a + 4e + b (a, b = 0..3) and get chunks 4b + (2 (a&1) + a/2) ^ ...,
+  // all distinct; the transposing reads of 32 lanes (row groups q = 0, 1 or
+  // 2, 3; 4 rows and 2 chunks each) get 16 distinct chunks as well
+  __device__ __forceinline__ static int swz(int c) {
+    return KCH >= 16 ? (((c & 3) << 2) | (((c >> 3) & 1) << 1) | ((c >> 4) & 1))
+                     : ((((c & 3) << 1) | ((c >> 3) & 1)) & (KCH - 1));
   }
 };
-constexpr int kPosChunk = 256;  // positions staged in LDS at a time
+constexpr int kPosChunk = 512;  // positions staged in LDS at a time
+constexpr int kKvBufs = 4;      // tile buffers per work group (three tiles in flight)
+
+// s_waitcnt with vmcnt = n (n < 64), the other counters not waited on
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 template <int D, int MODE>
 __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdKVArgs a) {
@@ -291,8 +269,11 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdKVArgs a) {
   using Frag = Tt::Frag;
   using KS_ = KvStage<D>;
   constexpr int NS = D / 32, NM = D / 16;
+  constexpr int ND = KS_::NDMA;
   __shared__ __attribute__((aligned(16))) char buf0[KS_::BYTES];
   __shared__ __attribute__((aligned(16))) char buf1[KS_::BYTES];
+  __shared__ __attribute__((aligned(16))) char buf2[KS_::BYTES];
+  __shared__ __attribute__((aligned(16))) char buf3[KS_::BYTES];
   __shared__ int posl[kPosChunk];
 
   const int lane = threadIdx.x & 63;
@@ -349,20 +330,19 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdKVArgs a) {
   }
   const char* qg = (const char*)a.q + (size_t)b * T * a.Hq * D * 2;
   const char* dg = (const char*)a.dout + (size_t)b * T * a.Hq * D * 2;
-  const char* qTg = (const char*)a.qT + (size_t)bg * D * a.NC * 2;
-  const char* dTg = (const char*)a.doT + (size_t)bg * D * a.NC * 2;
   const float* csg = a.cstat + (size_t)bg * 3 * a.NC;
 
   int nc = 0;  // positions in the current chunk
-  // tile `it` of the chunk (positions posl[it*PQ ..]) -> buf
+  // tile `it` of the chunk (positions posl[it*PQ ..]) -> buf: every wave
+  // issues ND transfers (its share of the two row tiles, one of the four
+  // 256-byte pieces of the statistics)
   auto issue = [&](int it, char* buf) {
     const int pb = it * PQ;
 #pragma unroll
     for (int k = 0; k < KS_::NQI / 4; ++k) {
       const int n = w + 4 * k;
       const int o = 1024 * n + 16 * lane;
-      const int R = o / KS_::KS, lc = ((o % KS_::KS) >> 4) ^ (R & KS_::KSW);
-      const int c = KS_::colmap(R);
+      const int c = o / KS_::KS, lc = ((o % KS_::KS) >> 4) ^ KS_::swz(c);
       const int t = posl[pb + (c >> lgGp)];
       const int hh = min(c & (Gp - 1), G - 1);
       const uint32_t ro = (uint32_t)((t * a.Hq + g * G + hh) * D) * 2u + 16u * lc;
@@ -373,22 +353,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdKVArgs a) {
       __builtin_amdgcn_global_load_lds(s2, (__attribute__((address_space(3))) void*)(buf + KS_::OD + 1024 * n), 16,
                                        0, 0);
     }
-#pragma unroll
-    for (int k = 0; k < KS_::NTI / 4; ++k) {
-      const int n = w + 4 * k;
-      const int R = 4 * n + (lane >> 4), pdw = lane & 15;
-      const int ldw = 4 * ((pdw >> 2) ^ ((R >> 2) & 3)) + (pdw & 3);
-      const int c = 2 * ldw;
-      const int t = posl[pb + (c >> lgGp)];
-      const uint32_t to = (uint32_t)(R * a.NC + t * Gp + (c & (Gp - 1))) * 2u;
-      const char* s1 = qTg + to;
-      const char* s2 = dTg + to;
-      __builtin_amdgcn_global_load_lds(s1, (__attribute__((address_space(3))) void*)(buf + KS_::OQT + 256 * n), 4,
-                                       0, 0);
-      __builtin_amdgcn_global_load_lds(s2, (__attribute__((address_space(3))) void*)(buf + KS_::ODT + 256 * n), 4,
-                                       0, 0);
-    }
-    if (w < 2) {  // statistics: 96 floats, lanes past them reload the last array into the padding
+    {  // statistics: 96 floats; lanes past them reload the last array into the padding
       const int ix = 64 * w + lane;
       const int arr = min(ix >> 5, 2), c = ix & 31;
       const int t = posl[pb + (c >> lgGp)];
@@ -405,17 +370,17 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdKVArgs a) {
       S[e] = f32x4{0.f, 0.f, 0.f, 0.f};
       dP[e] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // S = Q K^T, dP = dO V^T: chunk e's A row r16 is column 8(r16/4) + 4e + r16%4,
+    // so that a lane of the result holds columns 8 q4 .. 8 q4 + 7
 #pragma unroll
     for (int ks = 0; ks < NS; ++ks)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int R = 16 * e + r16;
-        const int off = R * KS_::KS + 16 * ((4 * ks + q4) ^ (R & KS_::KSW));
+        const int c = 8 * (r16 >> 2) + 4 * e + (r16 & 3);
+        const int off = c * KS_::KS + 16 * ((4 * ks + q4) ^ KS_::swz(c));
         Tt::mma(S[e], Tt::ld(cur + KS_::OQ + off), kf[ks]);
         Tt::mma(dP[e], Tt::ld(cur + KS_::OD + off), vf[ks]);
       }
-    // the lane's columns 8 q4 .. 8 q4 + 7: element 4e + i is column 8 q4 + 4e + i
-    // (statistics and positions taken four columns at a time)
     const float* st = (const float*)(cur + KS_::OS) + 8 * q4;
     float ps[8], ds[8];
 #pragma unroll
@@ -439,24 +404,47 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdKVArgs a) {
       }
     }
     const Frag pf = Tt::pack(ps), dsf = Tt::pack(ds);
+    // dV^T += dO^T P and dK^T += Q^T dS.  The A fragment (head_dim rows
+    // 16 mc + r16, columns 8 q4 .. 8 q4 + 7) is two transposing reads: lane L
+    // points at 4 dims (16 mc + 4 (L%4) ..) of row 8 (L/16) + 4 h + (L%16)/4
+    // and receives one dim of 4 rows.
+    const int tr_c = 8 * q4 + (r16 >> 2);
 #pragma unroll
     for (int mc = 0; mc < NM; ++mc) {
-      const int R = 16 * mc + r16;
-      const int off = R * 64 + 16 * (q4 ^ ((R >> 2) & 3));
-      Tt::mma(dvT[mc], Tt::ld(cur + KS_::ODT + off), pf);
-      Tt::mma(dkT[mc], Tt::ld(cur + KS_::OQT + off), dsf);
+      uint2 hq[2], hd[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = tr_c + 4 * h;
+        const int byte = 32 * mc + 8 * (r16 & 3);
+        const int off = c * KS_::KS + (((byte >> 4) ^ KS_::swz(c)) << 4) + (byte & 15);
+        hd[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                             (__attribute__((address_space(3))) bf16x4_t*)(cur + KS_::OD + off)));
+        hq[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                             (__attribute__((address_space(3))) bf16x4_t*)(cur + KS_::OQ + off)));
+      }
+      Frag fd, fq;
+      fd.u = make_uint4(hd[0].x, hd[0].y, hd[1].x, hd[1].y);
+      fq.u = make_uint4(hq[0].x, hq[0].y, hq[1].x, hq[1].y);
+      Tt::mma(dvT[mc], fd, pf);
+      Tt::mma(dkT[mc], fq, dsf);
     }
   };
 
   // Tiles are visited from the latest positions down: the work groups that
   // start together (one kv group per XCD, successive blocks) then read the
   // same query tiles at about the same time, so most of their transfers hit
-  // in L2.
+  // in L2.  Step k computes tile nit-1-k from buffer k % 4 and issues tile
+  // nit-4-k into the buffer of tile nit-k, read in the previous step.
   int nit = 0;
-  auto step = [&](int k, const char* cur, char* next) {  // k-th tile visited: nit - 1 - k
-    if (k + 1 < nit) issue(nit - 2 - k, next);
+  auto step = [&](int k, const char* cur, char* ahead) {
+    if (k + 3 < nit) issue(nit - 4 - k, ahead);
     compute(nit - 1 - k, cur);
-    wait_vmem();
+    // the next tile has landed (this wave's transfers: in order); up to two
+    // more may stay in flight
+    const int later = min(2, nit - 2 - k);
+    if (later >= 2) wait_vmcnt<2 * ND>();
+    else if (later == 1) wait_vmcnt<ND>();
+    else wait_vmem();
     __syncthreads();
   };
   const int nch = (npos + kPosChunk - 1) / kPosChunk;
@@ -464,19 +452,27 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdKVArgs a) {
     const int c0 = ci * kPosChunk;
     nc = min(kPosChunk, npos - c0);
     __syncthreads();  // the previous chunk's tiles and positions are no longer read
-    {
-      const int i = min((int)threadIdx.x, nc - 1);
-      posl[threadIdx.x] = MODE == 2 ? a.plist[(size_t)bg * T * a.topk + pbase + c0 + i] : pbase + c0 + i;
+    for (int i = threadIdx.x; i < kPosChunk; i += 256) {
+      const int ii = min(i, nc - 1);
+      posl[i] = MODE == 2 ? a.plist[(size_t)bg * T * a.topk + pbase + c0 + ii] : pbase + c0 + ii;
     }
     __syncthreads();
     nit = (nc + PQ - 1) / PQ;
     issue(nit - 1, buf0);
-    wait_vmem();
+    if (nit > 1) issue(nit - 2, buf1);
+    if (nit > 2) issue(nit - 3, buf2);
+    if (nit > 2) wait_vmcnt<2 * ND>();
+    else if (nit > 1) wait_vmcnt<ND>();
+    else wait_vmem();
     __syncthreads();
-    for (int k = 0; k < nit; k += 2) {
-      step(k, buf0, buf1);
+    for (int k = 0; k < nit; k += 4) {
+      step(k, buf0, buf3);
       if (k + 1 >= nit) break;
       step(k + 1, buf1, buf0);
+      if (k + 2 >= nit) break;
+      step(k + 2, buf2, buf1);
+      if (k + 3 >= nit) break;
+      step(k + 3, buf3, buf2);
     }
   }
   if (key < T) {
@@ -731,11 +727,6 @@ static hipError_t layouts(const BwdLayoutArgs& l, hipStream_t s) {
     if (l.v[i]) hipLaunchKernelGGL(v_to_posmajor_kernel<D>, dim3(nkb), dim3(256), 0, s, (const uint16_t*)l.v[i],
                                    (uint16_t*)l.vp[i], l.T, l.nblk);
   }
-  const unsigned nrt = (unsigned)((long)l.B * l.Hkv * (l.NC / 64));
-  hipLaunchKernelGGL(rows_to_dmajor_kernel<D>, dim3(nrt), dim3(256), 0, s, (const uint16_t*)l.q, (uint16_t*)l.qT,
-                     l.T, l.Hq, l.Hkv, l.NC, l.Gp);
-  hipLaunchKernelGGL(rows_to_dmajor_kernel<D>, dim3(nrt), dim3(256), 0, s, (const uint16_t*)l.dout,
-                     (uint16_t*)l.doT, l.T, l.Hq, l.Hkv, l.NC, l.Gp);
   return hipGetLastError();
 }
 

@@ -162,15 +162,15 @@ struct BwdLayoutArgs {
   const void* v[2];  // block-major value caches [B][Hkv][nblk][D][64]
   void* kb[2];       // out: keys block-major [B][Hkv][nblk][D][64]
   void* vp[2];       // out: values position-major [B][Hkv][nblk*64][D]
-  const void* q;     // [B][T][Hq][D]
-  const void* dout;
-  void* qT;          // out: [B][Hkv][D][NC], column t*Gp + hh (zero for hh >= G)
-  void* doT;
-  int B, T, Hq, Hkv, nblk, NC, Gp;
+  int B, T, Hq, Hkv, nblk;
 };
-// columns per position in the d-major copies: the group size, at least 2, so
-// that one position's piece of a d-row is a whole number of dwords
-inline int bwd_gp(int G) { return G < 2 ? 2 : G; }
+// query columns per position on the key side: the group size rounded up to a
+// power of two (columns of the extra heads are switched off)
+inline int bwd_gp(int G) {
+  int p = 1;
+  while (p < G) p <<= 1;
+  return p;
+}
 struct BwdRowArgs {
   const void* o[2];     // branch outputs [B][T][Hq][D] bf16 (the layer output for the full layer)
   const void* dout;
@@ -190,8 +190,6 @@ struct BwdRowArgs {
 struct BwdKVArgs {
   const void* q;
   const void* dout;
-  const void* qT;
-  const void* doT;
   const void* k;        // this branch's keys [B][Hkv][T][D]
   const void* vp;       // this branch's values, position-major
   const float* cstat;   // this branch's per-column statistics (BwdRowArgs::cstat)
