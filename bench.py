@@ -273,12 +273,21 @@ def bench_decode(cid: int, steps: int, sinks: bool = False):
     stream = torch.cuda.current_stream()
     nsel_ws = hb.workspace_size(hb.HS_FN_DECODE_SELECT, shape, blk)
     ws_sel = torch.empty(max(16, nsel_ws), dtype=torch.uint8, device="cuda")
+    ws_tsel = None
+    if token:
+        ws_tsel = torch.empty(max(16, hb.workspace_size(hb.HS_FN_DECODE_TOKEN_SELECT, shape, 1, cfg.kb)),
+                              dtype=torch.uint8, device="cuda")
 
-    def step():
-        hb.decode_full_attn_scores(q, k, v, lens, o, lse, raw, block=blk, ws=ws_full,
-                                   kv_scale=scale, stream=stream)
-        hb.decode_block_topk(q, k, lens, raw, lse, cfg.kb, idx, block=blk, n_recent=cfg.n_recent,
-                             kv_scale=scale, stream=stream)
+    def step(two_call=False):
+        if token and not two_call:
+            # full layer + token selection in one call (bounds, exact rescoring)
+            hb.decode_token_select(q, k, v, lens, o, lse, cfg.kb, cfg.n_recent, idx, scale, ws=ws_tsel,
+                                   stream=stream)
+        else:
+            hb.decode_full_attn_scores(q, k, v, lens, o, lse, raw, block=blk, ws=ws_full,
+                                       kv_scale=scale, stream=stream)
+            hb.decode_block_topk(q, k, lens, raw, lse, cfg.kb, idx, block=blk, n_recent=cfg.n_recent,
+                                 kv_scale=scale, stream=stream)
         for l in layers:
             if token:
                 hb.decode_select_attn(l["q"], k, v, lens, idx, nsel, None, None, 0, None, l["o"],
@@ -290,29 +299,42 @@ def bench_decode(cid: int, steps: int, sinks: bool = False):
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     for _ in range(2):
         step()
+        if token:
+            step(True)
     torch.cuda.synchronize()
-    times = []
-    for _ in range(steps):
-        scrub.fill_(1)  # evicts L2 and the MALL; outside the timed events
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
+
+    def cold(two_call=False):
+        times = []
+        for _ in range(steps):
+            scrub.fill_(1)  # evicts L2 and the MALL; outside the timed events
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step(two_call)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return float(np.median(times))
+
+    ms = cold()
+    ms_two = cold(True) if token else None
     warm0, warm1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     warm0.record(stream)
     for _ in range(steps):
         step()
     warm1.record(stream)
     torch.cuda.synchronize()
-    ms = float(np.median(times))
     nbytes = decode_bytes(inp)
-    return {"workload": {4: "1:11 hybrid block decode, 64 seqs, L~U[32768,65536], top-32 blocks, W=128",
-                         5: "token-level decode, 16 seqs x 262144, fp8 KV, top-2048 + 128 recent"}[cid],
-            "ms_per_step_cold": ms, "ms_per_step_warm": warm0.elapsed_time(warm1) / steps,
-            "algorithmic_bytes": nbytes, "GB_per_s": nbytes / (ms * 1e-3) / 1e9,
-            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM, "sinks": bool(sinks)}
+    res = {"workload": {4: "1:11 hybrid block decode, 64 seqs, L~U[32768,65536], top-32 blocks, W=128",
+                        5: "token-level decode, 16 seqs x 262144, fp8 KV, top-2048 + 128 recent"}[cid],
+           "ms_per_step_cold": ms, "ms_per_step_warm": warm0.elapsed_time(warm1) / steps,
+           "algorithmic_bytes": nbytes, "GB_per_s": nbytes / (ms * 1e-3) / 1e9,
+           "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM, "sinks": bool(sinks)}
+    if token:
+        # the step through hs_decode_token_select; the two-call step (per-token
+        # logits written and read back) for comparison
+        res["selection"] = "hs_decode_token_select (bounds + exact rescoring)"
+        res["ms_per_step_cold_two_call"] = ms_two
+    return res
 
 
 PEAK_PCIE = 64.0  # GB/s, PCIe 5.0 x16 host link, one direction

@@ -20,11 +20,13 @@ HS_SCORE_MAX, HS_SCORE_LSE = 0, 1
 HS_SEL_FULLY_PAST, HS_SEL_INCLUDE_DIAG = 0, 2
 HS_FN_FULL_ATTN, HS_FN_BLOCK_TOPK, HS_FN_SPARSE_ATTN, HS_FN_DECODE_SELECT = range(4)
 HS_FN_FULL_ATTN_BWD, HS_FN_SPARSE_ATTN_BWD = 4, 5
+HS_FN_DECODE_TOKEN_SELECT = 6
 
 EXPORTS = ("hs_full_attn_fwd_scores", "hs_block_topk", "hs_sparse_attn_fwd",
            "hs_decode_select_attn", "hs_decode_select_attn_static", "hs_gather_blocks",
            "hs_offload_full_select", "hs_offload_workspace_size", "hs_sparse_attn_fwd_train",
-           "hs_full_attn_bwd", "hs_sparse_attn_bwd", "hs_workspace_size", "hs_last_error", "hs_version")
+           "hs_full_attn_bwd", "hs_sparse_attn_bwd", "hs_decode_token_select", "hs_workspace_size",
+           "hs_last_error", "hs_version")
 HS_STATIC_SCRATCH_BYTES = 8 << 20
 
 
@@ -88,6 +90,7 @@ def load() -> ctypes.CDLL:
     lib.hs_sparse_attn_fwd_train.argtypes = [SP, P, P, P, P, I, P, P, I, P, P, P, P, P, P]
     lib.hs_full_attn_bwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, Z, P]
     lib.hs_sparse_attn_bwd.argtypes = [SP, P, P, P, P, I, P, P, I, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.hs_decode_token_select.argtypes = [SP, P, P, P, P, P, I, I, P, P, Z, P]
     lib.hs_workspace_size.argtypes = [I, SP, I, I, I]
     lib.hs_workspace_size.restype = Z
     lib.hs_last_error.restype = ctypes.c_char_p
@@ -95,7 +98,7 @@ def load() -> ctypes.CDLL:
     for name in ("hs_full_attn_fwd_scores", "hs_block_topk", "hs_sparse_attn_fwd",
                  "hs_decode_select_attn", "hs_decode_select_attn_static", "hs_gather_blocks",
                  "hs_offload_full_select", "hs_sparse_attn_fwd_train", "hs_full_attn_bwd",
-                 "hs_sparse_attn_bwd"):
+                 "hs_sparse_attn_bwd", "hs_decode_token_select"):
         getattr(lib, name).restype = I
     del F
     _lib = lib
@@ -227,6 +230,21 @@ def decode_block_topk(q, k, lens, raw, lse, topk, idx, grp_score=None, block=64,
     _check(load().hs_block_topk(ctypes.byref(s), _ptr(raw), _ptr(lse), block, topk, n_recent,
                                 HS_SEL_FULLY_PAST, _ptr(grp_score), _ptr(idx), _ptr(ws),
                                 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def decode_token_select(q, k, v, lens, o, lse, topk, n_recent, idx, kv_scale, ws=None, stream=None):
+    """Token-level decode: the full layer's o [B,Hq,d], lse [B,Hq] and the
+    token selection idx [B,Hkv,topk+n_recent] in one call, without per-token
+    logits (fp8 caches k, v [B,Hkv,C,d] uint8 with kv_scale [2,Hkv]).  ws:
+    uint8 device workspace (allocated here when None or too small); returned."""
+    _contig(q, k, v, o, lse, idx)
+    s = decode_shape(q, k, lens, kv_scale)
+    need = workspace_size(HS_FN_DECODE_TOKEN_SELECT, s, 1, topk)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(load().hs_decode_token_select(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), topk,
+                                         n_recent, _ptr(idx), _ptr(ws), ws.numel(), _stream(stream)))
+    return ws
 
 
 def decode_select_attn(q_sp, k, v, lens, idx, n_sel, k_ring, v_ring, window, gate_logits, o,

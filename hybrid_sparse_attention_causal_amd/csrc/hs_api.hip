@@ -127,6 +127,28 @@ size_t token_topk_ws(const hs_shape* s) {
   return rows * ((size_t)s->kv_len + 2 * 2048 + 2 * hs::kTokCap + 2 * (size_t)token_nseg(s)) * sizeof(uint32_t) +
          ((rows + 3) / 4) * 4 * sizeof(uint32_t);
 }
+// hs_decode_token_select: split-K partials, the bounds (z per token, offsets
+// per tile and head, widths per tile) and the token selection's workspace
+struct TokenSelWs {
+  size_t part, zb, ab, wb, topk, total;
+};
+TokenSelWs token_select_ws(const hs_shape* s) {
+  TokenSelWs w{};
+  const size_t rows = (size_t)s->batch * s->hkv, ntl = (size_t)s->kv_len / 64;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  w.part = take(decode_full_ws(s));
+  w.zb = take(rows * s->kv_len * sizeof(float));
+  w.ab = take(rows * ntl * (size_t)(s->hq / s->hkv) * sizeof(float));
+  w.wb = take(rows * ntl * sizeof(float));
+  w.topk = take(token_topk_ws(s));
+  w.total = off;
+  return w;
+}
 // token-mode sparse layer: partial states of up to kTokSplitMax work groups per
 // (sequence, group)
 size_t decode_select_ws(const hs_shape* s, int block) {
@@ -245,6 +267,7 @@ size_t hs_workspace_size(int fn_id, const hs_shape* shape, int block, int topk, 
   if (!shape->kv_lens) return 0;
   if (fn_id == HS_FN_FULL_ATTN) return decode_full_ws(shape);
   if (fn_id == HS_FN_BLOCK_TOPK && block == 1) return token_topk_ws(shape);
+  if (fn_id == HS_FN_DECODE_TOKEN_SELECT) return token_select_ws(shape).total;
   if (fn_id == HS_FN_DECODE_SELECT) return decode_select_ws(shape, block);
   return 0;
 }
@@ -329,6 +352,81 @@ hs_status hs_full_attn_fwd_scores(const hs_shape* s, const void* q, const void* 
   }
   return launched(fn, hs::launch_full_prefill(a, s->dtype, s->head_dim, flags == HS_SCORE_LSE,
                                               (hipStream_t)stream));
+}
+
+hs_status hs_decode_token_select(const hs_shape* s, const void* q, const void* k, const void* v, void* o,
+                                 float* lse, int topk, int n_recent, int32_t* idx, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  const char* fn = "hs_decode_token_select";
+  hs_status st = check_decode(fn, s);
+  if (st) return st;
+  st = check_decode_block(fn, s, 1);
+  if (st) return st;
+  if (topk < 1 || topk > 4096) return fail(HS_ERR_INVALID_ARG, "%s: topk=%d (1..4096 tokens)", fn, topk);
+  if (n_recent < 0 || n_recent > 4096) return fail(HS_ERR_INVALID_ARG, "%s: n_recent=%d (0..4096)", fn, n_recent);
+  if (s->batch == 0) return ok();
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(o);
+  REQUIRE_PTR(lse);
+  REQUIRE_PTR(idx);
+  if (!aligned16(k)) return fail(HS_ERR_INVALID_ARG, "%s: k not 16-byte aligned", fn);
+  const TokenSelWs w = token_select_ws(s);
+  if (!ws || ws_bytes < w.total)
+    return fail(HS_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, w.total, ws_bytes);
+  if (!aligned16(ws)) return fail(HS_ERR_INVALID_ARG, "%s: ws not 16-byte aligned", fn);
+  char* W = (char*)ws;
+  hipStream_t strm = (hipStream_t)stream;
+  hs::DecodeFullArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.raw = nullptr;
+  a.part = (float*)(W + w.part);
+  a.lens = s->kv_lens;
+  a.B = s->batch;
+  a.Hq = s->hq;
+  a.Hkv = s->hkv;
+  a.C = s->kv_len;
+  a.nch = decode_nch(s);
+  a.ch_blocks = hs::decode_chunk_blocks(s->kv_len);
+  a.token = 2;
+  a.kv_dtype = s->kv_dtype;
+  a.kv_scale = s->kv_scale;
+  a.sc2 = scale_log2(s);
+  a.zb = (float*)(W + w.zb);
+  a.ab = (float*)(W + w.ab);
+  hipError_t e = hs::launch_decode_full(a, s->head_dim, strm);
+  if (e != hipSuccess) return launched(fn, e);
+  hs::TokenTopkArgs t{};
+  t.lse = lse;
+  t.idx = idx;
+  t.lens = s->kv_lens;
+  const size_t rows = (size_t)s->batch * s->hkv;
+  t.keys = (uint32_t*)(W + w.topk);
+  t.hist = t.keys + rows * s->kv_len;
+  t.cand_key = t.hist + rows * 2 * 2048 + ((rows + 3) / 4) * 4;
+  t.cand_idx = (int32_t*)(t.cand_key + rows * hs::kTokCap);
+  t.nseg = token_nseg(s);
+  t.seg = (uint32_t*)(t.cand_idx + rows * hs::kTokCap);
+  t.B = s->batch;
+  t.Hq = s->hq;
+  t.Hkv = s->hkv;
+  t.C = s->kv_len;
+  t.kb = topk;
+  t.n_recent = n_recent;
+  t.zb = a.zb;
+  t.ab = a.ab;
+  t.wb = (float*)(W + w.wb);
+  t.q = q;
+  t.k = (const uint8_t*)k;
+  t.kv_scale = s->kv_scale;
+  t.sc2 = a.sc2;
+  t.D = s->head_dim;
+  return launched(fn, hs::launch_token_topk_bounds(t, strm));
 }
 
 hs_status hs_block_topk(const hs_shape* s, const float* blk_raw, const float* lse, int block,

@@ -25,6 +25,17 @@
 
 namespace hs {
 
+// Maximum over the 16 lanes of a row (lanes 16r .. 16r+15), every lane of the
+// row getting it: swaps within pairs and quads, then the half-row and row
+// mirrors (DPP, no LDS).
+__device__ __forceinline__ float row16_max(float v) {
+  v = max2(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = max2(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = max2(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = max2(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+
 // ======================================================== split-K full layer
 // Unit (b, g, ch) covers keys [ch*CH*64, min(L, (ch+1)*CH*64)), CH =
 // ch_blocks (16 or 32 tiles, chosen by the host).  MFMA columns
@@ -102,7 +113,7 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
   }
   const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * a.C * D * KES;
   const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * a.C * D * KES;
-  float* rawrow = a.raw + (size_t)(b * a.Hq + h) * (TOKEN ? a.C : a.C / 64);
+  float* rawrow = TOKEN == 2 ? nullptr : a.raw + (size_t)(b * a.Hq + h) * (TOKEN ? a.C : a.C / 64);
 
   // Raw fragments of one tile: bf16: 16 K and 16 V fragments of 16 bytes;
   // fp8: 16 K fragments of 8 bytes and 2x(D/64)x8 value dwords (decoded at
@@ -214,7 +225,38 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
     eng.qk(ldK, s);
     if constexpr (MORE) loadK(nx, rk);
     float bmax[1], bsum[1];
-    if (TOKEN) {
+    if constexpr (TOKEN == 2) {
+      // Selection bounds instead of logits.  The tile's offset per head is the
+      // chunk's LSE over its earlier tiles (m + log2 l of the running state,
+      // before this tile joins it), or the tile's own maximum for the
+      // chunk's first tile; z of a key is the maximum over the group's heads
+      // of (logit - offset).  With the heads' final LSEs, every token's score
+      // max_h (logit - LSE_h) then lies in [z - max_h d_h, z - min_h d_h],
+      // d_h = LSE_h - offset_h.
+      auto hook = [&](int, const float* x) {
+        float off;
+        if (kb0 == kstart) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = max2(mx, x[e]);
+          off = xlane_max(mx);
+        } else {
+          off = eng.m[0] + fast_log2(xlane_sum(eng.l[0]));
+        }
+        float z[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) z[e] = row16_max(col < G ? x[e] - off : -INFINITY);
+        const size_t brow = (size_t)b * a.Hkv + g;
+        if (col == 0) {
+          float* zr = a.zb + brow * a.C;
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            *(float4*)(zr + kb0 + tile_key(c, q4)) = make_float4(z[4 * c], z[4 * c + 1], z[4 * c + 2], z[4 * c + 3]);
+        }
+        if (lane < G) a.ab[(brow * (a.C / 64) + (kb0 >> 6)) * G + lane] = off;
+      };
+      eng.template softmax<true, false>(s, kb0, lo, hi, sc2, bmax, bsum, hook);
+    } else if constexpr (TOKEN == 1) {
       auto hook = [&](int, const float* x) {
         if (col < G) {
 #pragma unroll
@@ -574,6 +616,29 @@ __device__ __forceinline__ uint32_t order_key_f(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// the float of an order key, and the slack of the selection from bounds
+// (below, token_zkeys_kernel)
+__device__ __forceinline__ float inv_order_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+constexpr float kBoundSlack = 1e-3f;
+
+// hist[bin] += 1 for every active lane, one LDS atomic per distinct bin of the
+// wave: the scores of a row are close together, so most lanes of a wave share
+// a handful of bins and per-lane atomics would queue on the same addresses
+__device__ __forceinline__ void wave_hist_add(uint32_t* hist, uint32_t bin, bool act) {
+  const int lane = lane_id();
+  for (;;) {
+    const uint64_t am = __ballot(act);
+    if (!am) break;
+    const int leader = __builtin_ctzll(am);
+    const uint32_t lb = (uint32_t)__shfl((int)bin, leader);
+    const uint64_t m = __ballot(act && bin == lb);
+    if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(m));
+    act = act && bin != lb;
+  }
+}
+
 __global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* p, long n) {
   for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) p[i] = 0u;
 }
@@ -617,12 +682,11 @@ __global__ __launch_bounds__(256) void token_keys_kernel(TokenTopkArgs a) {
       kq[e] = 0u;
       if (i < L) {
         if (a.gs) a.gs[(size_t)row * a.C + i] = expf(xs[e]);
-        if (i < ncand) {
-          kq[e] = order_key_f(xs[e]);
-          atomicAdd(&hist[kq[e] >> 21], 1u);
-        }
+        if (i < ncand) kq[e] = order_key_f(xs[e]);
       }
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wave_hist_add(hist, kq[e] >> 21, i0 + e < ncand);
     *(uint4*)(keys + i0) = make_uint4(kq[0], kq[1], kq[2], kq[3]);
   }
   __syncthreads();
@@ -688,6 +752,8 @@ __global__ __launch_bounds__(1024) void token_hist2_kernel(TokenTopkArgs a) {
   const int s1 = min(ncand, s0 + kTokSeg);
   for (int i = s0 + t; i < s1; i += 1024) {
     const uint32_t k = keys[i];
+    // (plain atomics: inside the threshold bin the next 11 bits spread over
+    // many bins, where the per-bin ballot loop of wave_hist_add runs long)
     if ((k >> 21) == b1) atomicAdd(&hist[(k >> 10) & 2047u], 1u);
   }
   __syncthreads();
@@ -722,6 +788,10 @@ __global__ __launch_bounds__(1024) void token_cand_kernel(TokenTopkArgs a) {
   __syncthreads();
   find_bin(hist, 2048, need, scan, res);
   const uint32_t pfx = (b1 << 11) | (uint32_t)res[0];
+  // from bounds (wb set): the keys are those of lo, and the candidates are the
+  // tokens whose hi = lo + width reaches the lower edge of the threshold bin
+  const bool bounds = a.wb != nullptr;
+  const float lo_thr = bounds ? inv_order_key(pfx << 10) - kBoundSlack : 0.f;
   const uint32_t* keys = a.keys + (size_t)row * a.C;
   // thread t takes the PER consecutive keys s0 + PER*t .. (16-byte loads),
   // so the block's exclusive scan below keeps the candidates in token order
@@ -738,10 +808,13 @@ __global__ __launch_bounds__(1024) void token_cand_kernel(TokenTopkArgs a) {
     kv[n + 2] = q.z;
     kv[n + 3] = q.w;
   }
+  // the PER keys lie in one 64-token tile (PER divides 64)
+  const float width = bounds && i0 < ncand ? a.wb[(size_t)row * (a.C / 64) + (i0 >> 6)] : 0.f;
   uint32_t flags = 0u, cnt = 0u;
 #pragma unroll
   for (int n = 0; n < PER; ++n) {
-    if (i0 + n < ncand && (kv[n] >> 10) >= pfx) {
+    const bool cand = bounds ? inv_order_key(kv[n]) + width >= lo_thr : (kv[n] >> 10) >= pfx;
+    if (i0 + n < ncand && cand) {
       flags |= 1u << n;
       ++cnt;
     }
@@ -778,6 +851,50 @@ __global__ __launch_bounds__(1024) void token_cand_kernel(TokenTopkArgs a) {
   }
 }
 
+// Writes, in ascending order of position, the ids of the n entries whose key
+// is above thr and of the first need_eq entries whose key equals thr (1024
+// threads).  Wave w owns the contiguous entries [w*wseg, (w+1)*wseg) and walks
+// them 64 at a time; ballots give each lane its rank among the keys > thr and
+// == thr of its wave, and the 16 waves' counts give every wave its first
+// output slot and its first tie rank.
+template <class KF, class IF>
+__device__ void emit_selected(int n, uint32_t thr, int need_eq, const KF& key_of, const IF& id_of, int32_t* out,
+                              uint32_t* wsum) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const uint64_t lt_mask = lane ? (~0ull >> (64 - lane)) : 0ull;
+  const int wseg = ((n + 1023) / 1024) * 64;
+  const int i0 = min(n, w * wseg), i1 = min(n, i0 + wseg);
+  uint32_t ngt = 0, neq = 0;
+  for (int i = i0; i < i1; i += 64) {
+    const bool in = i + lane < i1;
+    const uint32_t k = in ? key_of(i + lane) : 0u;
+    ngt += __popcll(__ballot(in && k > thr));
+    neq += __popcll(__ballot(in && k == thr));
+  }
+  if (lane == 0) {
+    wsum[w] = ngt;
+    wsum[16 + w] = neq;
+  }
+  __syncthreads();
+  uint32_t gt_base = 0, eq_base = 0;
+  for (int v = 0; v < w; ++v) {
+    gt_base += wsum[v];
+    eq_base += wsum[16 + v];
+  }
+  uint32_t pos = gt_base + min(eq_base, (uint32_t)need_eq);
+  for (int i = i0; i < i1; i += 64) {
+    const bool in = i + lane < i1;
+    const uint32_t k = in ? key_of(i + lane) : 0u;
+    const uint64_t eqm = __ballot(in && k == thr);
+    const uint32_t eq_rank = eq_base + __popcll(eqm & lt_mask);
+    const bool take = in && (k > thr || (k == thr && eq_rank < (uint32_t)need_eq));
+    const uint64_t tm = __ballot(take);
+    if (take) out[pos + __popcll(tm & lt_mask)] = id_of(i + lane);
+    pos += __popcll(tm);
+    eq_base += __popcll(eqm);
+  }
+}
+
 // one work group (1024 threads) per (sequence, kv group) row
 __global__ __launch_bounds__(1024) void token_select_kernel(TokenTopkArgs a) {
   __shared__ uint32_t hist[2048];
@@ -792,51 +909,10 @@ __global__ __launch_bounds__(1024) void token_select_kernel(TokenTopkArgs a) {
   const int ncand = max(0, L - a.n_recent);
   const int nrec = min(L, a.n_recent);
   const int kb = a.kb;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const uint64_t lt_mask = lane ? (~0ull >> (64 - lane)) : 0ull;
+  const int t = threadIdx.x;
   const uint32_t* keys = a.keys + (size_t)row * a.C;
   int32_t* out = a.idx + (size_t)row * (kb + a.n_recent);
   int nsel;
-
-  // Writes, in ascending order of position, the ids of the n entries whose
-  // key is above thr and of the first need_eq entries whose key equals thr.
-  // Wave w owns the contiguous entries [w*wseg, (w+1)*wseg) and walks them 64
-  // at a time; ballots give each lane its rank among the keys > thr and
-  // == thr of its wave, and the 16 waves' counts give every wave its first
-  // output slot and its first tie rank.
-  auto emit = [&](int n, uint32_t thr, int need_eq, auto key_of, auto id_of) {
-    const int wseg = ((n + 1023) / 1024) * 64;
-    const int i0 = min(n, w * wseg), i1 = min(n, i0 + wseg);
-    uint32_t ngt = 0, neq = 0;
-    for (int i = i0; i < i1; i += 64) {
-      const bool in = i + lane < i1;
-      const uint32_t k = in ? key_of(i + lane) : 0u;
-      ngt += __popcll(__ballot(in && k > thr));
-      neq += __popcll(__ballot(in && k == thr));
-    }
-    if (lane == 0) {
-      wsum[w] = ngt;
-      wsum[16 + w] = neq;
-    }
-    __syncthreads();
-    uint32_t gt_base = 0, eq_base = 0;
-    for (int v = 0; v < w; ++v) {
-      gt_base += wsum[v];
-      eq_base += wsum[16 + v];
-    }
-    uint32_t pos = gt_base + min(eq_base, (uint32_t)need_eq);
-    for (int i = i0; i < i1; i += 64) {
-      const bool in = i + lane < i1;
-      const uint32_t k = in ? key_of(i + lane) : 0u;
-      const uint64_t eqm = __ballot(in && k == thr);
-      const uint32_t eq_rank = eq_base + __popcll(eqm & lt_mask);
-      const bool take = in && (k > thr || (k == thr && eq_rank < (uint32_t)need_eq));
-      const uint64_t tm = __ballot(take);
-      if (take) out[pos + __popcll(tm & lt_mask)] = id_of(i + lane);
-      pos += __popcll(tm);
-      eq_base += __popcll(eqm);
-    }
-  };
 
   const uint32_t ncnd = a.hist[(size_t)a.B * a.Hkv * 2 * 2048 + row];
   if (ncand <= kb) {
@@ -881,7 +957,8 @@ __global__ __launch_bounds__(1024) void token_select_kernel(TokenTopkArgs a) {
     find_bin(hist, 1024, need, scan, res);
     const uint32_t thr = (pfx << 10) | (uint32_t)res[0];
     const int need_eq = need - res[1];  // >= 1 candidates equal to thr are taken
-    emit(ncnd, thr, need_eq, [&](int i) { return cand_k[i]; }, [&](int i) { return cand_i[i]; });
+    emit_selected((int)ncnd, thr, need_eq, [&](int i) { return cand_k[i]; }, [&](int i) { return cand_i[i]; }, out,
+                  wsum);
     nsel = kb;
   } else {
     // level 1: the global histogram of the top 11 bits
@@ -913,7 +990,242 @@ __global__ __launch_bounds__(1024) void token_select_kernel(TokenTopkArgs a) {
     find_bin(hist, 1024, need, scan, res);
     const uint32_t thr = (p2 << 10) | (uint32_t)res[0];
     const int need_eq = need - res[1];  // >= 1 keys equal to thr are taken
-    emit(ncand, thr, need_eq, [&](int i) { return keys[i]; }, [](int i) { return i; });
+    emit_selected(ncand, thr, need_eq, [&](int i) { return keys[i]; }, [](int i) { return i; }, out, wsum);
+    nsel = kb;
+  }
+  for (int r = t; r < nrec; r += 1024) out[nsel + r] = L - nrec + r;
+  for (int r = nsel + nrec + t; r < kb + a.n_recent; r += 1024) out[r] = -1;
+}
+
+// ---------------------------------------- token-level top-k from bounds
+// The full layer run with token == 2 leaves, per token, z = max_h (logit_h -
+// off_h) and, per tile, the offsets off_h.  With the heads' LSEs (log2 units),
+// d_h = LSE_h - off_h gives lo = z - max_h d_h <= x <= z - min_h d_h = hi for
+// the token's score x = max_h (logit_h - LSE_h).  The k-th largest lo (found
+// by the histogram passes on the keys of lo, taken at the lower edge of its
+// 22-bit bin) is at most the k-th largest score, so every token of the top k,
+// ties included, has hi >= it: those tokens are the candidates.  Their scores
+// are then computed exactly from their key rows, and the exact selection runs
+// on them alone.  A slack of kBoundSlack (log2 units) on both tests covers the
+// rounding of the bounds and of the rescoring (kBoundSlack, with the order
+// keys, is defined with them above).
+
+// grid (rows, C/4096): keys of lo for 4096 tokens, the level-1 histogram,
+// and each tile's bound width max_h d_h - min_h d_h.  Thread t takes the
+// token quads t, t + 256, t + 512, t + 768.
+__global__ __launch_bounds__(256) void token_zkeys_kernel(TokenTopkArgs a) {
+  __shared__ uint32_t hist[2048];
+  __shared__ float lse2[16];
+  const int row = blockIdx.x;
+  const int g = row % a.Hkv, b = row / a.Hkv;
+  const int L = ctx_len(a.lens, b, a.C);
+  const int ncand = max(0, L - a.n_recent);
+  const int G = a.Hq / a.Hkv;
+  for (int i = threadIdx.x; i < 2048; i += 256) hist[i] = 0u;
+  if (threadIdx.x < G) lse2[threadIdx.x] = a.lse[(size_t)b * a.Hq + g * G + threadIdx.x] * kLog2e;
+  __syncthreads();
+  const int base = blockIdx.y * 4096;
+  const int ntl = a.C / 64;
+  uint32_t* keys = a.keys + (size_t)row * a.C;
+  const float* zr = a.zb + (size_t)row * a.C;
+  const float* ar = a.ab + (size_t)row * ntl * G;
+  float* wr = a.wb + (size_t)row * ntl;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int i0 = base + 4 * (threadIdx.x + 256 * n);
+    // C is a multiple of 64: a lane past it leaves (the histogram's ballots
+    // take the lanes still running)
+    if (i0 >= a.C) break;
+    uint32_t kq[4] = {0u, 0u, 0u, 0u};
+    if (i0 < L) {
+      const int tl = i0 >> 6;
+      float dmax = -INFINITY, dmin = INFINITY;
+      for (int hh = 0; hh < G; ++hh) {
+        const float d = lse2[hh] - ar[tl * G + hh];
+        dmax = fmaxf(dmax, d);
+        dmin = fminf(dmin, d);
+      }
+      if ((i0 & 63) == 0) wr[tl] = dmax - dmin;
+      const float4 z = *(const float4*)(zr + i0);
+      const float zs[4] = {z.x, z.y, z.z, z.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (i0 + e < ncand) kq[e] = order_key_f(zs[e] - dmax);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wave_hist_add(hist, kq[e] >> 21, i0 + e < ncand);
+    *(uint4*)(keys + i0) = make_uint4(kq[0], kq[1], kq[2], kq[3]);
+  }
+  __syncthreads();
+  uint32_t* gh = a.hist + (size_t)row * 2048;
+  for (int i = threadIdx.x; i < 2048; i += 256)
+    if (hist[i]) atomicAdd(&gh[i], hist[i]);
+}
+
+// The exact score (log2 units) of token i of row (b, g): max over the group's
+// heads of sc2 * k_scale * q_h . k_i - LSE_h, from the fp8 key row; qs holds
+// the group's queries (fp32, [G][D]) and lse2 the heads' LSEs (log2 units).
+template <int D>
+__device__ float exact_token_score(const uint8_t* krow, const float* qs, const float* lse2, int G, float sck) {
+  float acc[16];
+#pragma unroll
+  for (int hh = 0; hh < 16; ++hh) acc[hh] = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    const uint4 w = *(const uint4*)(krow + 16 * c);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    float kv[16];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f32x2 lo2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[e], false);
+      const f32x2 hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[e], true);
+      kv[4 * e] = lo2[0];
+      kv[4 * e + 1] = lo2[1];
+      kv[4 * e + 2] = hi2[0];
+      kv[4 * e + 3] = hi2[1];
+    }
+#pragma unroll
+    for (int hh = 0; hh < 16; ++hh) {
+      if (hh >= G) break;
+      const float4* qp = (const float4*)(qs + hh * D + 16 * c);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const float4 qv = qp[f];
+        acc[hh] = __builtin_fmaf(qv.x, kv[4 * f], acc[hh]);
+        acc[hh] = __builtin_fmaf(qv.y, kv[4 * f + 1], acc[hh]);
+        acc[hh] = __builtin_fmaf(qv.z, kv[4 * f + 2], acc[hh]);
+        acc[hh] = __builtin_fmaf(qv.w, kv[4 * f + 3], acc[hh]);
+      }
+    }
+  }
+  float x = -INFINITY;
+#pragma unroll
+  for (int hh = 0; hh < 16; ++hh)
+    if (hh < G) x = fmaxf(x, acc[hh] * sck - lse2[hh]);
+  return x;
+}
+
+// Radix select over n keys (in LDS or global memory, read through key_of):
+// the key thr of the k-th largest and how many entries equal to thr are
+// taken (need_eq >= 1), three levels of 11, 11 and 10 bits.
+template <class KF>
+__device__ void radix_kth(int n, int k, const KF& key_of, uint32_t* hist, uint32_t* scan, int* res, uint32_t* thr,
+                          int* need_eq) {
+  const int t = threadIdx.x;
+  int need = k;
+  uint32_t pfx = 0u;
+#pragma unroll 1
+  for (int lvl = 0; lvl < 3; ++lvl) {
+    const int shift = lvl == 0 ? 21 : (lvl == 1 ? 10 : 0);
+    const int nb = lvl == 2 ? 1024 : 2048;
+    for (int i = t; i < 2048; i += 1024) hist[i] = 0u;
+    __syncthreads();
+    for (int i = t; i < n; i += 1024) {
+      const uint32_t kk = key_of(i);
+      const bool in = lvl == 0 || (lvl == 1 ? (kk >> 21) == pfx : (kk >> 10) == pfx);
+      if (in) atomicAdd(&hist[(kk >> shift) & (uint32_t)(nb - 1)], 1u);
+    }
+    __syncthreads();
+    find_bin(hist, nb, need, scan, res);
+    pfx = lvl == 0 ? (uint32_t)res[0] : ((pfx << (lvl == 1 ? 11 : 10)) | (uint32_t)res[0]);
+    need -= res[1];
+  }
+  *thr = pfx;
+  *need_eq = need;
+}
+
+// grid (rows, kTokCap / 256): the exact key of every candidate (in place of
+// its lower-bound key), one candidate per thread; rows with more candidates
+// than the store holds are left to token_zselect_kernel
+template <int D>
+__global__ __launch_bounds__(256) void token_rescore_kernel(TokenTopkArgs a) {
+  __shared__ __attribute__((aligned(16))) float qs[16 * D];
+  __shared__ float lse2[16];
+  const int row = blockIdx.x;
+  const int b = row / a.Hkv, g = row % a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const uint32_t ncnd = a.hist[(size_t)a.B * a.Hkv * 2 * 2048 + row];
+  if (ncnd > (uint32_t)kTokCap || blockIdx.y * 256u >= ncnd) return;  // uniform
+  const int t = threadIdx.x;
+  const uint16_t* qg = (const uint16_t*)a.q + ((size_t)b * a.Hq + g * G) * D;
+  for (int i = t; i < G * D; i += 256) qs[i] = __uint_as_float((uint32_t)qg[i] << 16);
+  if (t < G) lse2[t] = a.lse[(size_t)b * a.Hq + g * G + t] * kLog2e;
+  __syncthreads();
+  const uint32_t e = blockIdx.y * 256u + t;
+  if (e >= ncnd) return;
+  const int id = a.cand_idx[(size_t)row * kTokCap + e];
+  const uint8_t* kr = a.k + (((size_t)b * a.Hkv + g) * a.C + id) * D;
+  a.cand_key[(size_t)row * kTokCap + e] =
+      order_key_f(exact_token_score<D>(kr, qs, lse2, G, a.sc2 * a.kv_scale[g]));
+}
+
+// one work group (1024 threads) per (sequence, kv group) row: the exact
+// selection among the candidates (rescored by token_rescore_kernel), then the
+// newest tokens
+template <int D>
+__global__ __launch_bounds__(1024) void token_zselect_kernel(TokenTopkArgs a) {
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t scan[1024];
+  __shared__ int res[2];
+  __shared__ uint32_t wsum[32];
+  __shared__ uint32_t cand_k[kTokCap];
+  __shared__ int32_t cand_i[kTokCap];
+  __shared__ __attribute__((aligned(16))) float qs[16 * D];
+  __shared__ float lse2[16];
+  const int row = blockIdx.x;
+  const int b = row / a.Hkv, g = row % a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int L = ctx_len(a.lens, b, a.C);
+  const int ncand = max(0, L - a.n_recent);
+  const int nrec = min(L, a.n_recent);
+  const int kb = a.kb;
+  const int t = threadIdx.x;
+  int32_t* out = a.idx + (size_t)row * (kb + a.n_recent);
+  const uint16_t* qg = (const uint16_t*)a.q + ((size_t)b * a.Hq + g * G) * D;
+  for (int i = t; i < G * D; i += 1024) qs[i] = __uint_as_float((uint32_t)qg[i] << 16);
+  if (t < G) lse2[t] = a.lse[(size_t)b * a.Hq + g * G + t] * kLog2e;
+  __syncthreads();
+  const float sck = a.sc2 * a.kv_scale[g];
+  const uint8_t* kr = a.k + ((size_t)b * a.Hkv + g) * a.C * D;
+  int nsel;
+  const uint32_t ncnd = a.hist[(size_t)a.B * a.Hkv * 2 * 2048 + row];
+  if (ncand <= kb) {
+    for (int i = t; i < ncand; i += 1024) out[i] = i;
+    nsel = ncand;
+  } else if (ncnd <= (uint32_t)kTokCap) {
+    // the candidates and their exact keys in ascending token order (each
+    // segment's run is in order, and runs follow their segments)
+    const int32_t* ci = a.cand_idx + (size_t)row * kTokCap;
+    const uint32_t* ck = a.cand_key + (size_t)row * kTokCap;
+    const uint32_t* sg = a.seg + (size_t)row * a.nseg * 2;
+    const int nsg = (ncand + kTokSeg - 1) / kTokSeg;
+    int off = 0;
+    for (int q = 0; q < nsg; ++q) {
+      const int base = (int)sg[2 * q], cnt = (int)sg[2 * q + 1];
+      for (int e = t; e < cnt; e += 1024) {
+        cand_i[off + e] = ci[base + e];
+        cand_k[off + e] = ck[base + e];
+      }
+      off += cnt;
+    }
+    __syncthreads();
+    uint32_t thr;
+    int need_eq;
+    radix_kth((int)ncnd, kb, [&](int i) { return cand_k[i]; }, hist, scan, res, &thr, &need_eq);
+    emit_selected((int)ncnd, thr, need_eq, [&](int i) { return cand_k[i]; }, [&](int i) { return cand_i[i]; }, out,
+                  wsum);
+    nsel = kb;
+  } else {
+    // too many candidates: exact keys for the whole row, then the same select
+    uint32_t* keys = a.keys + (size_t)row * a.C;
+    for (int i = t; i < ncand; i += 1024)
+      keys[i] = order_key_f(exact_token_score<D>(kr + (size_t)i * D, qs, lse2, G, sck));
+    __threadfence_block();
+    __syncthreads();
+    uint32_t thr;
+    int need_eq;
+    radix_kth(ncand, kb, [&](int i) { return keys[i]; }, hist, scan, res, &thr, &need_eq);
+    emit_selected(ncand, thr, need_eq, [&](int i) { return keys[i]; }, [](int i) { return i; }, out, wsum);
     nsel = kb;
   }
   for (int r = t; r < nrec; r += 1024) out[nsel + r] = L - nrec + r;
@@ -1093,7 +1405,8 @@ __global__ __launch_bounds__(1024) void decode_token_combine_kernel(DecodeSparse
 template <int D>
 static void decode_full_dispatch(const DecodeFullArgs& a, dim3 grid, hipStream_t s) {
   if (a.kv_dtype == HS_FP8_E4M3) {
-    if (a.token) hipLaunchKernelGGL((decode_full_kernel<D, 1, HS_FP8_E4M3>), grid, dim3(256), 0, s, a);
+    if (a.token == 2) hipLaunchKernelGGL((decode_full_kernel<D, 2, HS_FP8_E4M3>), grid, dim3(256), 0, s, a);
+    else if (a.token) hipLaunchKernelGGL((decode_full_kernel<D, 1, HS_FP8_E4M3>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((decode_full_kernel<D, 0, HS_FP8_E4M3>), grid, dim3(256), 0, s, a);
   } else {
     if (a.token) hipLaunchKernelGGL((decode_full_kernel<D, 1, HS_BF16>), grid, dim3(256), 0, s, a);
@@ -1143,6 +1456,32 @@ hipError_t launch_token_topk(const TokenTopkArgs& a, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(token_select_kernel, dim3((unsigned)rows), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_token_topk_bounds(const TokenTopkArgs& a, hipStream_t s) {
+  const long rows = (long)a.B * a.Hkv;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(256), dim3(256), 0, s, a.hist, rows * 2 * 2048 + rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(token_zkeys_kernel, dim3((unsigned)rows, (unsigned)((a.C + 4095) / 4096)), dim3(256), 0,
+                     s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 seg((unsigned)rows, (unsigned)((a.C + kTokSeg - 1) / kTokSeg));
+  hipLaunchKernelGGL(token_hist2_kernel, seg, dim3(1024), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(token_cand_kernel, seg, dim3(1024), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 rs((unsigned)rows, (unsigned)(kTokCap / 256));
+  if (a.D == 128) hipLaunchKernelGGL(token_rescore_kernel<128>, rs, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(token_rescore_kernel<64>, rs, dim3(256), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.D == 128) hipLaunchKernelGGL(token_zselect_kernel<128>, dim3((unsigned)rows), dim3(1024), 0, s, a);
+  else hipLaunchKernelGGL(token_zselect_kernel<64>, dim3((unsigned)rows), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 

@@ -79,10 +79,17 @@ struct DecodeFullArgs {
   int C;                  // cache capacity per sequence (multiple of 64)
   int nch;                // chunks per sequence at capacity
   int ch_blocks;          // 64-key blocks per chunk
-  int token;              // 1: raw holds per-token logits; 0: per-block maxima
+  int token;              // 1: raw holds per-token logits; 0: per-block maxima;
+                          // 2: selection bounds in zb / ab (raw unused)
   int kv_dtype;           // HS_BF16 (block-major V) or HS_FP8_E4M3 (position-major V)
   const float* kv_scale;  // fp8: device [2][Hkv]
   float sc2;
+  // token == 2: per (sequence, kv group) row, zb [rows][C] = max over the
+  // group's heads of (logit - a) and ab [rows][C/64][G] = the offsets a of
+  // each tile and head (log2 units; a is the chunk's LSE over its earlier
+  // tiles, or the tile's own maximum for a chunk's first tile)
+  float* zb;
+  float* ab;
 };
 
 struct DecodeSparseArgs {
@@ -119,6 +126,17 @@ struct TokenTopkArgs {
                           // key segment's candidates in cand_key / cand_idx
   int nseg;               // key segments per row, ceil(C / kTokSeg)
   int B, Hq, Hkv, C, kb, n_recent;
+  // selection from bounds (raw unused): zb, ab as written by the full layer
+  // with token == 2, wb [rows][C/64] scratch (per-tile bound widths), and
+  // what the exact rescoring of the candidates reads
+  const float* zb;
+  const float* ab;
+  float* wb;
+  const void* q;          // [B][Hq][D] bf16
+  const uint8_t* k;       // [B][Hkv][C][D] fp8 e4m3 key cache
+  const float* kv_scale;  // [2][Hkv]
+  float sc2;              // softmax scale * log2(e)
+  int D;
 };
 // candidates kept per row for the final exact selection (rows with more fall
 // back to a radix select over the whole row)
@@ -233,6 +251,8 @@ hipError_t launch_bwd_q(const BwdQArgs& a, int mode, int D, hipStream_t s);    /
 size_t bwd_q_lds_bytes(int T, int G);
 
 hipError_t launch_token_topk(const TokenTopkArgs& a, hipStream_t s);
+// the same selection from the bounds of a token == 2 full layer
+hipError_t launch_token_topk_bounds(const TokenTopkArgs& a, hipStream_t s);
 hipError_t launch_decode_sparse_token(const DecodeSparseArgs& a, int D, hipStream_t s);
 
 hipError_t launch_decode_full(const DecodeFullArgs& a, int D, hipStream_t s);

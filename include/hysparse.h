@@ -290,6 +290,34 @@ hs_status hs_offload_full_select(const hs_shape* shape, const int32_t* lens_host
                                  void* copy_stream);
 
 /*
+ * Token-level decode step's full layer and selection in one call, without the
+ * per-token logits (HySparse2 explainer, "Precise retrieval without a
+ * separate indexer" and the decode_one_token pseudocode).  o, lse and idx are
+ * those of hs_full_attn_fwd_scores + hs_block_topk with block = 1 and no
+ * grp_score: the same selection rule (top-k older tokens by
+ * x_i = max_h (logit_hi - LSE_h), ties to the smaller token id, then the
+ * n_recent newest tokens), and the same full-layer arithmetic for o and lse.
+ * Instead of every head's logit, the full layer leaves one value per token and
+ * kv group plus one offset per 64-token tile and head, which bound x_i from
+ * both sides once the LSEs are known; the tokens whose bounds reach the k-th
+ * largest lower bound are rescored exactly from their key rows, and the
+ * selection runs on them.  The scores are therefore rounded differently from
+ * the two-call path (both within fp32 rounding of the exact value), so rows
+ * whose k-th and (k+1)-th scores differ by rounding only may pick different
+ * tokens among those ties.
+ *   shape: decode (kv_lens set), fp8 e4m3 caches with kv_scale, head_dim 64
+ *   or 128, group size <= 16; q [batch][hq][head_dim] bf16; k, v the
+ *   position-major fp8 caches; o [batch][hq][head_dim] bf16 and lse
+ *   [batch][hq] (out); idx [batch][hkv][topk + n_recent] int32 (out),
+ *   topk 1..4096, n_recent 0..4096.
+ * ws: hs_workspace_size(HS_FN_DECODE_TOKEN_SELECT, shape, 1, topk, 0) bytes,
+ * 16-byte aligned.
+ */
+hs_status hs_decode_token_select(const hs_shape* shape, const void* q, const void* k, const void* v,
+                                 void* o, float* lse, int topk, int n_recent, int32_t* idx, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/*
  * Training forward of one sparse layer: hs_sparse_attn_fwd (bf16), plus what
  * its backward needs, each branch's own ungated output and LSE:
  *   o_branch   [2][batch][T][hq][head_dim] bf16 (out): [0] the block-sparse
@@ -358,6 +386,7 @@ hs_status hs_sparse_attn_bwd(const hs_shape* shape, const void* q_sp, const void
 #define HS_FN_DECODE_SELECT 3
 #define HS_FN_FULL_ATTN_BWD 4   /* prefill shape (kv_lens NULL) */
 #define HS_FN_SPARSE_ATTN_BWD 5 /* prefill shape (kv_lens NULL) */
+#define HS_FN_DECODE_TOKEN_SELECT 6
 
 /* Workspace bytes the given entry point needs (or, for token-mode
  * hs_decode_select_attn, can use) for this shape; 0 if none.  `block`,

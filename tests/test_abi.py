@@ -175,3 +175,30 @@ def test_decode_select_validation():
     # nothing to do: no sequences
     assert _dsel(_dshape(batch=0), ptrs=None, idx=None, ring=None) == hb.HS_OK
     assert hb.load().hs_last_error().decode() == ""
+
+
+def _tsel(s, topk=64, n_recent=8, ptrs=FAKE, idx=FAKE, ws=None, ws_bytes=0):
+    lib = hb.load()
+    return lib.hs_decode_token_select(ctypes.byref(s), ptrs, ptrs, ptrs, ptrs, ptrs, topk, n_recent, idx, ws,
+                                      ws_bytes, None)
+
+
+def test_decode_token_select_validation():
+    """hs_decode_token_select rejects bad arguments before any launch, and
+    sizes its workspace through hs_workspace_size."""
+    f8 = _dshape(kv_dtype=hb.HS_FP8_E4M3, kv_scale=FAKE)
+    need = hb.workspace_size(hb.HS_FN_DECODE_TOKEN_SELECT, f8, 1, 64)
+    # split-K partials + bounds (z per token and group, offsets per tile and head, widths) + selection
+    assert need >= 2 * 2 * 1024 * 4 + 2 * 2 * 16 * 4 * 4
+    assert _tsel(f8) == hb.HS_ERR_WORKSPACE                                  # no workspace
+    assert _tsel(f8, ws=FAKE, ws_bytes=need - 1) == hb.HS_ERR_WORKSPACE
+    assert _tsel(f8, ws=FAKE + 4, ws_bytes=need) == hb.HS_ERR_INVALID_ARG    # misaligned workspace
+    assert _tsel(f8, topk=0, ws=FAKE, ws_bytes=need) == hb.HS_ERR_INVALID_ARG
+    assert _tsel(f8, topk=4097, ws=FAKE, ws_bytes=need) == hb.HS_ERR_INVALID_ARG
+    assert _tsel(f8, n_recent=-1, ws=FAKE, ws_bytes=need) == hb.HS_ERR_INVALID_ARG
+    assert _tsel(f8, idx=None, ws=FAKE, ws_bytes=need) == hb.HS_ERR_INVALID_ARG
+    assert _tsel(_dshape(), ws=FAKE, ws_bytes=need) == hb.HS_ERR_UNSUPPORTED          # needs fp8 caches
+    assert _tsel(_dshape(kv_dtype=hb.HS_FP8_E4M3), ws=FAKE, ws_bytes=need) == hb.HS_ERR_INVALID_ARG  # no scale
+    assert _tsel(_dshape(kv_dtype=hb.HS_FP8_E4M3, kv_scale=FAKE, kv_lens=None),
+                 ws=FAKE, ws_bytes=need) == hb.HS_ERR_INVALID_ARG                     # decode needs kv_lens
+    assert _tsel(_dshape(kv_dtype=hb.HS_FP8_E4M3, kv_scale=FAKE, batch=0), ptrs=None, idx=None) == hb.HS_OK

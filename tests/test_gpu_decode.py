@@ -322,6 +322,32 @@ class TokenRun:
         torch.cuda.synchronize()
 
 
+def token_idx_row_ok(row, ref, g, L, kb, R, rel, where):
+    """One (sequence, kv group) row of a token selection against the oracle:
+    ascending, -1 padded, the newest tokens last; equal to the oracle's row
+    unless its k-th and (k+1)-th scores are within rel (then every token
+    clearly above the k-th is in and none clearly below).  Returns 1 for a
+    near-tie row."""
+    ncand = max(0, L - R)
+    want = ref["idx"][g]
+    n_out = min(kb, ncand) + min(R, L)
+    assert np.all(row[n_out:] == -1) and np.all(np.diff(row[:n_out]) > 0), where
+    assert np.array_equal(row[n_out - min(R, L):n_out], np.arange(L - min(R, L), L)), where
+    ranked = ref["ranked"][g]
+    if ncand > kb:
+        sk, sk1 = ranked[kb - 1], ranked[kb]
+        if (sk - sk1) / sk < rel:
+            got = row[: n_out - min(R, L)]
+            Sg = ref["Sg"][g]
+            cand = np.arange(ncand)
+            must = cand[Sg[cand] > sk * (1 + rel)]
+            banned = cand[Sg[cand] < sk * (1 - rel)]
+            assert np.all(np.isin(must, got)) and not np.any(np.isin(banned, got)), where
+            return 1
+    assert np.array_equal(row[:n_out], want[:n_out]), where
+    return 0
+
+
 def check_token_sequences(run, seqs, rel=1e-4):
     cfg, inp = run.cfg, run.inp
     R, kb = cfg.n_recent, cfg.kb
@@ -340,26 +366,8 @@ def check_token_sequences(run, seqs, rel=1e-4):
         w["lse"] = np.abs(lse_g[b] - ref["lse"]).max()
         w["raw"] = np.abs(raw_g[b][:, :L] - ref["raw"][:, :L]).max()
         w["gs"] = (np.abs(gs_g[b][:, :L] - ref["Sg"][:, :L]) / ref["Sg"][:, :L].max()).max()
-        ncand = max(0, L - R)
         for g in range(cfg.Hkv):
-            row = idx_g[b, g]
-            want = ref["idx"][g]
-            n_out = min(kb, ncand) + min(R, L)
-            assert np.all(row[n_out:] == -1) and np.all(np.diff(row[:n_out]) > 0), (b, g)
-            assert np.array_equal(row[n_out - min(R, L):n_out], np.arange(L - min(R, L), L))
-            ranked = ref["ranked"][g]
-            if ncand > kb:
-                sk, sk1 = ranked[kb - 1], ranked[kb]
-                if (sk - sk1) / sk < rel:
-                    w["ties"] += 1
-                    got = row[: n_out - min(R, L)]
-                    Sg = ref["Sg"][g]
-                    cand = np.arange(ncand)
-                    must = cand[Sg[cand] > sk * (1 + rel)]
-                    banned = cand[Sg[cand] < sk * (1 - rel)]
-                    assert np.all(np.isin(must, got)) and not np.any(np.isin(banned, got)), (b, g)
-                    continue
-            assert np.array_equal(row[:n_out], want[:n_out]), (b, g)
+            w["ties"] += token_idx_row_ok(idx_g[b, g], ref, g, L, kb, R, rel, (b, g))
         for l in range(len(run.outs)):
             lay = dict(q=f64_bf16(inp.layers[l]["q"][b]),
                        sinks=None if run.sinks[l] is None else run.sinks[l].astype(np.float64))
@@ -410,6 +418,82 @@ def test_token_d64_group16():
     inp = gen.make_decode(cfg)
     run = TokenRun(inp)
     check_token_sequences(run, range(2))
+
+
+# ------------------------------------- token level, selection from bounds
+class TokenSelectRun:
+    """hs_decode_token_select (the full layer and the token selection in one
+    call, the selection from bounds and exact rescoring) beside the two-call
+    path on the same inputs."""
+
+    def __init__(self, inp):
+        cfg = inp.cfg
+        self.cfg, self.inp = cfg, inp
+        self.base = TokenRun(inp, n_layers=0)
+        B, Hq, Hkv, d = cfg.B, cfg.Hq, cfg.Hkv, cfg.d
+        self.o = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.full((B, Hq), float("nan"), device="cuda")
+        self.idx = torch.full((B, Hkv, cfg.kb + cfg.n_recent), -7, dtype=torch.int32, device="cuda")
+        hb.decode_token_select(dev(inp.q), self.base.k, self.base.v, self.base.lens, self.o, self.lse, cfg.kb,
+                               cfg.n_recent, self.idx, self.base.scale)
+        torch.cuda.synchronize()
+
+
+def check_token_select(run, seqs, rel=1e-4):
+    cfg, inp = run.cfg, run.inp
+    R, kb = cfg.n_recent, cfg.kb
+    # the full layer's arithmetic is the same: o and lse bit for bit
+    assert torch.equal(run.o, run.base.o) and torch.equal(run.lse, run.base.lse)
+    idx_g = host(run.idx)
+    scale = inp.kv_scale.astype(np.float64)
+
+    def one(b):
+        L = int(inp.lens[b])
+        ks, vs = zip(*(inp.kv_slab(b, g) for g in range(cfg.Hkv)))
+        k, v = ora.dequantize_kv(np.stack(ks), np.stack(vs), scale, L)
+        ref = ora.decode_step(f64_bf16(inp.q[b]), k, v, L, [], kb, 0, block=1, n_recent=R)
+        return sum(token_idx_row_ok(idx_g[b, g], ref, g, L, kb, R, rel, (b, g)) for g in range(cfg.Hkv))
+
+    ties = sum(_pool_map(one, list(seqs)))
+    say(f"  {len(list(seqs))} seqs: selection from bounds matches the oracle (near-tie rows {ties})")
+
+
+def test_token_select_small_ragged():
+    say("[token select] fp8, C=4096, top-256 + 16 recent, lengths 1 .. 4096")
+    cfg = gen.config(5, B=4, T=4096, Hq=8, Hkv=2, d=128, kb=256, n_recent=16, N=0, L_lo=1, L_hi=4096)
+    inp = gen.make_decode(cfg)
+    inp.lens = np.array([1, 200, 300, 4096], np.int32)
+    check_token_select(TokenSelectRun(inp), range(4))
+
+
+def test_token_select_d64_group16():
+    say("[token select] d=64, G=16")
+    cfg = gen.config(5, B=2, T=8192, Hq=16, Hkv=1, d=64, kb=100, n_recent=128, N=0, L_lo=5000, L_hi=8192)
+    check_token_select(TokenSelectRun(gen.make_decode(cfg)), range(2))
+
+
+def test_token_select_all_tied_takes_the_whole_row():
+    """All logits of one sequence equal (q = 0): every old token is a
+    candidate, far past the candidate store, so the scores of the whole row
+    are computed exactly and selected there; ties go to the smaller id."""
+    say("[token select ties] fp8, C=16384, top-2048 + 128 recent, one sequence with q = 0")
+    cfg = gen.config(5, B=2, T=16384, Hq=8, Hkv=2, d=128, kb=2048, n_recent=128, N=0,
+                     L_lo=16384, L_hi=16384)
+    inp = gen.make_decode(cfg)
+    inp.lens = np.array([16384, 12000], np.int32)
+    inp.q[0] = 0
+    run = TokenSelectRun(inp)
+    idx = host(run.idx)
+    for g in range(cfg.Hkv):
+        want = np.concatenate([np.arange(2048), np.arange(16384 - 128, 16384)])
+        assert np.array_equal(idx[0, g], want), g
+    check_token_select(run, range(2))
+
+
+def test_token_select_config5_full_size_all_sequences():
+    say("[token select, config 5] 16 seqs x 262144 fp8 tokens, top-2048 + 128 recent, every sequence")
+    inp = gen.make_decode(gen.config(5), n_layers=0)
+    check_token_select(TokenSelectRun(inp), range(16))
 
 
 def test_config5_token_level_full_size_all_sequences():
