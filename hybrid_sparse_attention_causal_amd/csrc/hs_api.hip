@@ -5,6 +5,7 @@
 #include <stddef.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -185,6 +186,22 @@ hs_status static_scratch_ptr(const char* fn, void** out) {
   }
   *out = g_scratch_ptr[dev];
   return HS_OK;
+}
+
+std::mutex g_cu_mu;
+int g_cu_count[256];  // per device id; filled on the first query on that device
+
+// compute units of the current device (256 if it cannot be queried)
+int device_cu_count() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return 256;
+  std::lock_guard<std::mutex> lock(g_cu_mu);
+  if (!g_cu_count[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    g_cu_count[dev] = n;
+  }
+  return g_cu_count[dev];
 }
 
 // bytes of the token-mode split partial states for nsp work groups per
@@ -641,9 +658,12 @@ hs_status decode_select_impl(const char* fn, const hs_shape* s, const void* q_sp
   a.nsplit = 1;
   if (block == 1) {
     // with a workspace, each (sequence, group) is spread over several work
-    // groups (about eight 64-token tiles each) and merged by a second kernel
+    // groups of eight waves, about one 64-token tile per wave, and merged by
+    // a second kernel.  One such group takes a compute unit's registers, so
+    // there are no more groups than compute units: all run at once.
     const int ntile = (n_sel + 63) / 64;
-    const int nsp = ntile / 8 < 1 ? 1 : (ntile / 8 > hs::kTokSplitMax ? hs::kTokSplitMax : ntile / 8);
+    int nsp = std::min(hs::kTokSplitMax, std::max(1, (ntile + 7) / 8));
+    while (nsp > 1 && (long)s->batch * s->hkv * nsp > device_cu_count()) --nsp;
     if (static_scratch) {
       // the split partial states go to this device's static scratch array
       const size_t need = split_partials_bytes(s, nsp);

@@ -36,6 +36,36 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
+// Maximum over the 16 lanes of a row for 16 values at once, scattered: lane
+// i of the row returns max over the row of v[i].  Four exchange steps halve
+// the values a lane holds, each lane keeping the half whose next index bit
+// matches its own (partners: row mirror, half-row mirror, then swaps within
+// quads; each flips that bit and keeps the bits already settled): 15 moves
+// instead of 16 full reductions of 4 moves each.
+__device__ __forceinline__ float row16_max_scatter(const float (&v)[16], int i) {
+#define HS_DPP_MOVE(x, ctrl) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xF, 0xF, false))
+  float w8[8], w4[4], w2[2];
+  const bool b3 = i & 8, b2 = i & 4, b1 = i & 2, b0 = i & 1;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float keep = b3 ? v[8 + e] : v[e], send = b3 ? v[e] : v[8 + e];
+    w8[e] = max2(keep, HS_DPP_MOVE(send, 0x140));  // row mirror: lane 15 - i
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float keep = b2 ? w8[4 + e] : w8[e], send = b2 ? w8[e] : w8[4 + e];
+    w4[e] = max2(keep, HS_DPP_MOVE(send, 0x141));  // half-row mirror: lane i ^ 7
+  }
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const float keep = b1 ? w4[2 + e] : w4[e], send = b1 ? w4[e] : w4[2 + e];
+    w2[e] = max2(keep, HS_DPP_MOVE(send, 0x4E));  // lane i ^ 2
+  }
+  const float keep = b0 ? w2[1] : w2[0], send = b0 ? w2[0] : w2[1];
+  return max2(keep, HS_DPP_MOVE(send, 0xB1));  // lane i ^ 1
+#undef HS_DPP_MOVE
+}
+
 // ======================================================== split-K full layer
 // Unit (b, g, ch) covers keys [ch*CH*64, min(L, (ch+1)*CH*64)), CH =
 // ch_blocks (16 or 32 tiles, chosen by the host).  MFMA columns
@@ -45,7 +75,7 @@ __device__ __forceinline__ float row16_max(float v) {
 // scale per (K|V, kv head); the value fragments are byte-transposed in
 // registers (fp8_vfrag4), so their head_dim rows come in fp8_vrow_d order.
 template <int D, int TOKEN, int KV>
-__global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
+__global__ __launch_bounds__(256, KV == HS_FP8_E4M3 ? 3 : 2) void decode_full_kernel(DecodeFullArgs a) {
   using Tt = Tr<HS_BF16>;
   using Frag = Tt::Frag;
   using Eng = WaveAttn<HS_BF16, D, 1>;
@@ -105,10 +135,13 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
   lo[0] = col < G ? 0 : kNoKey;
   hi[0] = L - 1;
   // unconditional loads (columns past G read head g*G and are zeroed): a
-  // load under a branch would make the compiler drain every later wait
+  // load under a branch would make the compiler drain every later wait.
+  // The fp8 path takes head_dim in the order of fp8_kdim (keys and queries
+  // alike, so the logits are unchanged).
 #pragma unroll
   for (int ks = 0; ks < Eng::NS; ++ks) {
-    const Frag f = Tt::ld((const char*)a.q + ((size_t)(b * a.Hq + (col < G ? h : g * G)) * D + 32 * ks + q8) * 2);
+    const int dq = KV == HS_FP8_E4M3 ? fp8_kdim<D>(lane, ks) : 32 * ks + q8;
+    const Frag f = Tt::ld((const char*)a.q + ((size_t)(b * a.Hq + (col < G ? h : g * G)) * D + dq) * 2);
     eng.qf[0][ks] = col < G ? f : Tt::zero();
   }
   const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * a.C * D * KES;
@@ -116,8 +149,8 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
   float* rawrow = TOKEN == 2 ? nullptr : a.raw + (size_t)(b * a.Hq + h) * (TOKEN ? a.C : a.C / 64);
 
   // Raw fragments of one tile: bf16: 16 K and 16 V fragments of 16 bytes;
-  // fp8: 16 K fragments of 8 bytes and 2x(D/64)x8 value dwords (decoded at
-  // use).  The key and value halves of a tile are separate register sets, so
+  // fp8: 4 x D/64 K loads of 16 bytes (two fragments each) and 2x(D/64)x8
+  // value dwords (decoded at use).  The key and value halves of a tile are separate register sets, so
   // the next tile's keys load while this tile's values are still in flight
   // and consumed, and its values load during the next tile's QK^T.
   constexpr bool F8 = KV == HS_FP8_E4M3;
@@ -125,7 +158,7 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
     uint4 k[4][Eng::NS];
   };
   struct RawK8 {
-    uint2 k8[4][Eng::NS];
+    uint4 k8[4][Eng::NS / 2];
   };
   struct RawVB {
     uint4 v[2][Eng::NM];
@@ -143,13 +176,14 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int key = kb0 + tile_key(c, r16);
+      if constexpr (F8) {
 #pragma unroll
-      for (int ks = 0; ks < Eng::NS; ++ks) {
-        if constexpr (F8) {
-          r.k8[c][ks] = *(const uint2*)(kg + (size_t)key * D + 32 * ks + q8);
-        } else {
+        for (int j = 0; j < Eng::NS / 2; ++j)
+          r.k8[c][j] = *(const uint4*)(kg + (size_t)key * D + fp8_kdim<D>(lane, 2 * j));
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < Eng::NS; ++ks)
           r.k[c][ks] = *(const uint4*)(kg + ((size_t)key * D + 32 * ks + q8) * 2);
-        }
       }
     }
   };
@@ -203,7 +237,7 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
     const int j = kb0 >> 6;
     auto ldK = [&](int c, int ks) {
       if constexpr (F8) {
-        return fp8x8_frag(rk.k8[c][ks]);
+        return fp8x8_frag(half_u4(rk.k8[c][ks >> 1], ks & 1));
       } else {
         Frag f;
         f.u = rk.k[c][ks];
@@ -243,17 +277,20 @@ __global__ __launch_bounds__(256, 2) void decode_full_kernel(DecodeFullArgs a) {
         } else {
           off = eng.m[0] + fast_log2(xlane_sum(eng.l[0]));
         }
-        float z[16];
+        // x[e] is the logit of key tile_key(e / 4, q4 + e % 4); lane (q, i)
+        // ends up with z of e = i, and the wave stores the tile's 64 z in one
+        // instruction
+        float xm[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) z[e] = row16_max(col < G ? x[e] - off : -INFINITY);
+        for (int e = 0; e < 16; ++e) xm[e] = col < G ? x[e] - off : -INFINITY;
+        const float z = row16_max_scatter(xm, col);
         const size_t brow = (size_t)b * a.Hkv + g;
-        if (col == 0) {
-          float* zr = a.zb + brow * a.C;
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            *(float4*)(zr + kb0 + tile_key(c, q4)) = make_float4(z[4 * c], z[4 * c + 1], z[4 * c + 2], z[4 * c + 3]);
-        }
-        if (lane < G) a.ab[(brow * (a.C / 64) + (kb0 >> 6)) * G + lane] = off;
+        a.zb[brow * a.C + kb0 + tile_key(col >> 2, q4 + (col & 3))] = z;
+        // every lane stores (columns past G repeat head G-1's offset to its
+        // slot): a store under a lane branch would make the compiler count
+        // it as maybe absent and wait one load longer at every later wait
+        const float offs = col < G ? off : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(off), G - 1));
+        a.ab[(brow * (a.C / 64) + (kb0 >> 6)) * G + min(col, G - 1)] = offs;
       };
       eng.template softmax<true, false>(s, kb0, lo, hi, sc2, bmax, bsum, hook);
     } else if constexpr (TOKEN == 1) {
@@ -410,7 +447,9 @@ __global__ __launch_bounds__(512) void decode_sparse_kernel(DecodeSparseArgs a) 
   constexpr int ES = 2;
   constexpr int NW = 8;
   __shared__ float sm_m[NW][16], sm_l[NW][16];
-  __shared__ __attribute__((aligned(16))) float sm_o[NW][16][D];
+  // rows padded by 16 bytes: a 16-byte store of the 64 lanes then takes the
+  // minimum four passes instead of one per column
+  __shared__ __attribute__((aligned(16))) float sm_o[NW][16][D + 4];
 
   __shared__ int sm_wtot[NW];
   extern __shared__ uint32_t dyn[];  // canonical selection list: 2 x cap words
@@ -1244,9 +1283,10 @@ __global__ __launch_bounds__(512) void decode_sparse_token_kernel(DecodeSparseAr
   using Eng = WaveAttn<HS_BF16, D, 1>;
   constexpr int NW = 8;
   __shared__ float sm_m[NW][16], sm_l[NW][16];
-  __shared__ __attribute__((aligned(16))) float sm_o[NW][16][D];
   __shared__ int sm_wtot[NW];
-  extern __shared__ uint32_t dyn[];  // canonical selection list: 2 x cap words
+  // canonical selection list (2 x cap words); after the tile loop the same
+  // memory holds the waves' partial outputs [NW][G][D] for the merge
+  extern __shared__ uint32_t dyn[];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int bg = blockIdx.x;
@@ -1258,44 +1298,34 @@ __global__ __launch_bounds__(512) void decode_sparse_token_kernel(DecodeSparseAr
   const int r16 = lane & 15, q8 = 8 * (lane >> 4), q4 = (lane >> 4) << 2;
   const float sk = a.kv_scale[g], sv = a.kv_scale[a.Hkv + g];
   const float sc2 = a.sc2 * sk;
-  // live selected tokens: ids i < L, each once, ascending
-  const int cap = sel_list_cap(a.nsel);
-  const uint32_t* sel = dyn + cap;
-  const int nlive = canon_sel_list<64 * NW>(a.idx + (size_t)(b * a.Hkv + g) * a.nsel, a.nsel, (uint32_t)L, cap,
-                                            dyn, dyn + cap, sm_wtot);
-
   Eng eng;
   eng.reset();
+  // the query fragments are requested first, so that their latency overlaps
+  // the list canonicalisation; head_dim is taken in the order of fp8_kdim
 #pragma unroll
   for (int ks = 0; ks < Eng::NS; ++ks) {
-    const Frag f = Tt::ld((const char*)a.q + ((size_t)(b * a.Hq + (col < G ? h : g * G)) * D + 32 * ks + q8) * 2);
+    const Frag f = Tt::ld((const char*)a.q + ((size_t)(b * a.Hq + (col < G ? h : g * G)) * D + fp8_kdim<D>(lane, ks)) * 2);
     eng.qf[0][ks] = col < G ? f : Tt::zero();
   }
   const char* kg = (const char*)a.k + (size_t)(b * a.Hkv + g) * a.C * D;
   const char* vg = (const char*)a.v + (size_t)(b * a.Hkv + g) * a.C * D;
-  const int ntile = (nlive + 63) / 64;
   float bmax[1], bsum[1];
   int lo[1], hi[1];
 
-  // work group blockIdx.y of gridDim.y takes every gridDim.y-th group of
-  // eight tiles of the live list.  All of a tile's gathered rows are
-  // requested at once, with unconditional loads (an entry past the list
-  // reads token 0; its logit is masked and its values zeroed by selects): a
-  // load under a per-lane branch would make the compiler wait for each one
-  // in turn.
-  for (int it = blockIdx.y * NW + w; it < ntile; it += gridDim.y * NW) {
-    const int s0 = 64 * it;
-    const int nvalid = min(64, nlive - s0);  // entries s0 .. s0+nvalid-1 are live
-    const int tsafe = (int)sel[s0 + min(lane, nvalid - 1)];  // lanes past the list repeat a live token
-    lo[0] = col < G ? 0 : kNoKey;
-    hi[0] = s0 + nvalid - 1;
-    uint2 kraw[4][Eng::NS];
-    uint32_t vraw[2][D / 64][8];
+  // A tile's gathered rows are all requested at once, with unconditional
+  // loads (lanes past the list repeat a live token; their logits are masked
+  // and their values zeroed by selects): a load under a per-lane branch would
+  // make the compiler wait for each one in turn.
+  struct TileRaw {
+    uint4 k[4][Eng::NS / 2];
+    uint32_t v[2][D / 64][8];
+  };
+  auto issue = [&](int tsafe, TileRaw& r) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int tk = __shfl(tsafe, tile_key(c, r16));
 #pragma unroll
-      for (int ks = 0; ks < Eng::NS; ++ks) kraw[c][ks] = *(const uint2*)(kg + (size_t)tk * D + 32 * ks + q8);
+      for (int j = 0; j < Eng::NS / 2; ++j) r.k[c][j] = *(const uint4*)(kg + (size_t)tk * D + fp8_kdim<D>(lane, 2 * j));
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -1303,36 +1333,84 @@ __global__ __launch_bounds__(512) void decode_sparse_token_kernel(DecodeSparseAr
       for (int e = 0; e < 8; ++e) {
         const int tk = __shfl(tsafe, 32 * u + q8 + e);
 #pragma unroll
-        for (int hf = 0; hf < D / 64; ++hf) vraw[u][hf][e] = *(const uint32_t*)(vg + (size_t)tk * D + 64 * hf + 4 * r16);
+        for (int hf = 0; hf < D / 64; ++hf) r.v[u][hf][e] = *(const uint32_t*)(vg + (size_t)tk * D + 64 * hf + 4 * r16);
       }
+  };
+  // entries s0 .. s0+nvalid-1 of the live list are the tile's keys
+  auto compute = [&](int s0, int nvalid, TileRaw& r) {
+    lo[0] = col < G ? 0 : kNoKey;
+    hi[0] = s0 + nvalid - 1;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const bool ok = 32 * u + q8 + e < nvalid;
 #pragma unroll
-        for (int hf = 0; hf < D / 64; ++hf) vraw[u][hf][e] = ok ? vraw[u][hf][e] : 0u;
+        for (int hf = 0; hf < D / 64; ++hf) r.v[u][hf][e] = ok ? r.v[u][hf][e] : 0u;
       }
     Frag vc[4];
-    auto ldK = [&](int c, int ks) { return fp8x8_frag(kraw[c][ks]); };
+    auto ldK = [&](int c, int ks) { return fp8x8_frag(half_u4(r.k[c][ks >> 1], ks & 1)); };
     auto ldV = [&](int u, int mc) {
-      if ((mc & 3) == 0) fp8_vfrag4(vraw[u][mc >> 2], vc);
+      if ((mc & 3) == 0) fp8_vfrag4(r.v[u][mc >> 2], vc);
       return vc[mc & 3];
     };
     eng.template tile<true, false>(ldK, ldV, s0, lo, hi, sc2, bmax, bsum);
+  };
+
+  // Work group blockIdx.y of gridDim.y takes every gridDim.y-th group of
+  // eight tiles of the live list; wave w starts at tile it0.  The list's
+  // first entries arrive in registers, where this thread's entry of tile it0
+  // is v[blockIdx.y]; the wave requests that tile's rows before the list is
+  // in LDS.  If the list then proves canonical (live ids ascending, padding
+  // at the end, as the selection writes it) those are the tile's rows.
+  static_assert(kTokSplitMax <= kSelU, "a work group's first tiles lie in the requested entries");
+  const int32_t* il = a.idx + (size_t)(b * a.Hkv + g) * a.nsel;
+  uint32_t lv[kSelU];
+  sel_list_request<64 * NW>(il, a.nsel, lv);
+  const int it0 = blockIdx.y * NW + w;
+  uint32_t e = lv[0];
+#pragma unroll
+  for (int u = 1; u < kSelU; ++u) e = (int)blockIdx.y == u ? lv[u] : e;
+  const uint32_t e0 = (uint32_t)__shfl((int)e, 0);
+  TileRaw rs;
+  issue(e < (uint32_t)L ? (int)e : (e0 < (uint32_t)L ? (int)e0 : 0), rs);
+
+  // live selected tokens: ids i < L, each once, ascending
+  const int cap = sel_list_cap(a.nsel);
+  const uint32_t* sel = dyn + cap;
+  bool canonical;
+  const int nlive = canon_sel_list_from<64 * NW>(lv, il, a.nsel, (uint32_t)L, cap, dyn, dyn + cap, sm_wtot, canonical);
+  const int ntile = (nlive + 63) / 64;
+  int it = it0;
+  if (canonical && it0 < ntile) {
+    compute(64 * it0, min(64, nlive - 64 * it0), rs);
+    it += gridDim.y * NW;
+  }
+  for (; it < ntile; it += gridDim.y * NW) {
+    const int s0 = 64 * it;
+    const int nvalid = min(64, nlive - s0);
+    TileRaw r;
+    issue((int)sel[s0 + min(lane, nvalid - 1)], r);
+    compute(s0, nvalid, r);
   }
 
   const float lt = xlane_sum(eng.l[0]);
+  __syncthreads();  // every wave is done with the list: its memory takes sm_o
+  // [NW][G][D + 1]: with the odd row stride the 32 stores of each lane below
+  // hit 64 distinct banks
+  float* sm_o = (float*)dyn;
   if (lane < 16) {
     sm_m[w][col] = eng.m[0];
     sm_l[w][col] = lt;
   }
+  if (col < G) {
 #pragma unroll
-  for (int hf = 0; hf < D / 64; ++hf) {
+    for (int hf = 0; hf < D / 64; ++hf) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+      for (int k = 0; k < 4; ++k)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm_o[w][col][fp8_vrow_d(4 * hf + k, q4 + i)] = eng.o[0][4 * hf + k][i];
+        for (int i = 0; i < 4; ++i) sm_o[(w * G + col) * (D + 1) + fp8_vrow_d(4 * hf + k, q4 + i)] = eng.o[0][4 * hf + k][i];
+    }
   }
   __syncthreads();
   for (int el = threadIdx.x; el < G * D; el += 64 * NW) {
@@ -1348,7 +1426,7 @@ __global__ __launch_bounds__(512) void decode_sparse_token_kernel(DecodeSparseAr
     for (int ww = 0; ww < NW; ++ww) {
       const float wt = fast_exp2(sm_m[ww][c] - M);
       ls += wt * sm_l[ww][c];
-      os += wt * sm_o[ww][c][d];
+      os += wt * sm_o[(ww * G + c) * (D + 1) + d];
     }
     if (gridDim.y == 1) {
       ((uint16_t*)a.o)[((size_t)b * a.Hq + g * G + c) * D + d] =
@@ -1487,7 +1565,9 @@ hipError_t launch_token_topk_bounds(const TokenTopkArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_sparse_token(const DecodeSparseArgs& a, int D, hipStream_t s) {
   dim3 grid((unsigned)(a.B * a.Hkv), (unsigned)a.nsplit);
-  const size_t lds = 2 * (size_t)sel_list_cap(a.nsel) * sizeof(uint32_t);
+  // the selection list, or the eight waves' partial outputs after it
+  const size_t lds =
+      std::max(2 * (size_t)sel_list_cap(a.nsel), (size_t)8 * (a.Hq / a.Hkv) * (D + 1)) * sizeof(uint32_t);
   if (D == 128) hipLaunchKernelGGL(decode_sparse_token_kernel<128>, grid, dim3(512), lds, s, a);
   else hipLaunchKernelGGL(decode_sparse_token_kernel<64>, grid, dim3(512), lds, s, a);
   hipError_t e = hipGetLastError();

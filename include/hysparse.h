@@ -213,9 +213,10 @@ hs_status hs_sparse_attn_fwd(const hs_shape* shape, const void* q_sp, const void
  * window branch and no gate (the newest tokens are part of idx).  Block mode
  * takes no workspace.  Token mode takes an optional one: with
  * ws_bytes >= hs_workspace_size(HS_FN_DECODE_SELECT, shape, 1, 0, 0) every
- * (sequence, kv head) is spread over several work groups and merged by a
- * second kernel; with less (or NULL) one work group handles it.  Results
- * agree to rounding either way.
+ * (sequence, kv head) is spread over several work groups (about one 64-token
+ * tile per wave, and no more work groups in all than the device has compute
+ * units) and merged by a second kernel; with less (or NULL) one work group
+ * handles it.  Results agree to rounding either way.
  */
 hs_status hs_decode_select_attn(const hs_shape* shape, const void* q_sp, const void* k,
                                 const void* v, const int32_t* idx, int n_sel, int block,
@@ -230,9 +231,11 @@ hs_status hs_decode_select_attn(const hs_shape* shape, const void* q_sp, const v
  * results are those of hs_decode_select_attn.  The token-mode split partial
  * states go to a fixed device array inside the library instead of a caller
  * workspace: HS_STATIC_SCRATCH_BYTES per GPU, held until the process ends.
- * Token-mode shapes whose split partials need more (about
- * batch * hq * 8 * (head_dim + 2) * 4 bytes) return HS_ERR_WORKSPACE; block
- * mode needs no scratch.  All calls on one GPU share that GPU's array, so
+ * The split uses at most as many work groups as the device has compute
+ * units, so its partials take at most (compute units) * 16 * (head_dim + 2)
+ * * 4 bytes: 2.1 MB on a 256-CU device.  A shape whose split partials need
+ * more than HS_STATIC_SCRATCH_BYTES returns HS_ERR_WORKSPACE; block mode
+ * needs no scratch.  All calls on one GPU share that GPU's array, so
  * calls that overlap in time on one GPU (on different streams) race; calls
  * on one stream are ordered and safe.  The first call on a device looks up
  * that device's copy of the array (no allocation).
