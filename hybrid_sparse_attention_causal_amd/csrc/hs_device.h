@@ -245,21 +245,6 @@ __device__ __forceinline__ Tr<HS_BF16>::Frag fp8x8_frag(uint2 c) {
   return f;
 }
 
-// head_dim order of the QK^T operands from a position-major fp8 cache: lane
-// group q = lane/16 holds, at k-step ks, head_dim (D/4) q + 8 ks .. +7, so a
-// lane's keys over all k-steps are one contiguous D/4-byte run of the row
-// (16-byte loads, two k-steps each) and every load touches 64 bytes of each
-// of its 16 rows.  The queries are read in the same order; the dot products
-// are the same sums.
-template <int D>
-__device__ __forceinline__ int fp8_kdim(int lane, int ks) {
-  return (D / 4) * (lane >> 4) + 8 * ks;
-}
-// the 8 bytes of k-step 2j + hi from a 16-byte load
-__device__ __forceinline__ uint2 half_u4(uint4 v, int hi) {
-  return hi ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
-}
-
 // Value fragments from a position-major fp8 cache.  Lane (q, r) of key step u
 // loads the dword w[e] = V[key0 + e][dbase + 4r .. +3] of 8 consecutive keys
 // (key0 = kbase + 32u + 8q).  A 4x4 byte transpose of w[0..3] and of w[4..7]
