@@ -416,15 +416,21 @@ hs_status hs_decode_token_select(const hs_shape* s, const void* q, const void* k
   a.sc2 = scale_log2(s);
   a.zb = (float*)(W + w.zb);
   a.ab = (float*)(W + w.ab);
+  const size_t rows = (size_t)s->batch * s->hkv;
+  uint32_t* keys = (uint32_t*)(W + w.topk);
+  uint32_t* hist = keys + rows * s->kv_len;
+  // the merge kernel of the full layer clears the selection's two histograms
+  // per row and its per-row counters
+  a.clear = hist;
+  a.nclear = (long)rows * 2 * 2048 + (long)rows;
   hipError_t e = hs::launch_decode_full(a, s->head_dim, strm);
   if (e != hipSuccess) return launched(fn, e);
   hs::TokenTopkArgs t{};
   t.lse = lse;
   t.idx = idx;
   t.lens = s->kv_lens;
-  const size_t rows = (size_t)s->batch * s->hkv;
-  t.keys = (uint32_t*)(W + w.topk);
-  t.hist = t.keys + rows * s->kv_len;
+  t.keys = keys;
+  t.hist = hist;
   t.cand_key = t.hist + rows * 2 * 2048 + ((rows + 3) / 4) * 4;
   t.cand_idx = (int32_t*)(t.cand_key + rows * hs::kTokCap);
   t.nseg = token_nseg(s);

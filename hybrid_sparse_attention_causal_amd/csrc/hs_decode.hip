@@ -51,6 +51,30 @@ __device__ __forceinline__ uint2 half_u4(uint4 v, int hi) {
   return hi ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
 }
 
+// Value rows from a position-major fp8 cache: lane (q, r) of key step u loads
+// the D/16 bytes V[key0 + e][(D/16) r ..] of 8 consecutive keys (key0 =
+// kbase + 32u + 8q), one load per key: 16 lanes cover a whole row.  A 4x4
+// byte transpose of each dword column (fp8_vfrag4) gives the A fragments of
+// O^T row chunks mc = 4h + k (h: which dword), whose row m is head_dim
+// fp8_vrow_dv(mc, m); that order is undone when storing.
+template <int D>
+using Fp8VRow = std::conditional_t<D == 128, uint2, uint32_t>;
+template <int D>
+__host__ __device__ __forceinline__ int fp8_vrow_dv(int mc, int m) {
+  return (D / 16) * m + 4 * (mc >> 2) + (mc & 3);
+}
+// the 4 fragments of chunks 4h .. 4h+3 from the 8 keys' rows
+template <int D>
+__device__ __forceinline__ void fp8_vfrag4_rows(const Fp8VRow<D> (&v)[8], int h, Tr<HS_BF16>::Frag* out) {
+  uint32_t w[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if constexpr (D == 128) w[e] = h ? v[e].y : v[e].x;
+    else w[e] = v[e];
+  }
+  fp8_vfrag4(w, out);
+}
+
 // Maximum over the 16 lanes of a row for 16 values at once, scattered: lane
 // i of the row returns max over the row of v[i].  Four exchange steps halve
 // the values a lane holds, each lane keeping the half whose next index bit
@@ -179,7 +203,7 @@ __global__ __launch_bounds__(256, KV == HS_FP8_E4M3 ? 3 : 2) void decode_full_ke
     uint4 v[2][Eng::NM];
   };
   struct RawV8 {
-    uint32_t v8[2][D / 64][8];
+    Fp8VRow<D> v8[2][8];
   };
   using RawK = std::conditional_t<F8, RawK8, RawKB>;
   using RawV = std::conditional_t<F8, RawV8, RawVB>;
@@ -209,9 +233,7 @@ __global__ __launch_bounds__(256, KV == HS_FP8_E4M3 ? 3 : 2) void decode_full_ke
       const int key0 = kb0 + 32 * u + q8;
       if constexpr (F8) {
 #pragma unroll
-        for (int hf = 0; hf < D / 64; ++hf)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) r.v8[u][hf][e] = *(const uint32_t*)(vg + (size_t)(key0 + e) * D + 64 * hf + 4 * r16);
+        for (int e = 0; e < 8; ++e) r.v8[u][e] = *(const Fp8VRow<D>*)(vg + (size_t)(key0 + e) * D + (D / 16) * r16);
       } else {
 #pragma unroll
         for (int mc = 0; mc < Eng::NM; ++mc)
@@ -226,9 +248,7 @@ __global__ __launch_bounds__(256, KV == HS_FP8_E4M3 ? 3 : 2) void decode_full_ke
       const int key0 = kb0 + 32 * u + q8;
       if constexpr (F8) {
 #pragma unroll
-        for (int hf = 0; hf < D / 64; ++hf)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) r.v8[u][hf][e] = key0 + e < L ? r.v8[u][hf][e] : 0u;
+        for (int e = 0; e < 8; ++e) r.v8[u][e] = key0 + e < L ? r.v8[u][e] : Fp8VRow<D>{};
       } else {
 #pragma unroll
         for (int mc = 0; mc < Eng::NM; ++mc) {
@@ -262,7 +282,7 @@ __global__ __launch_bounds__(256, KV == HS_FP8_E4M3 ? 3 : 2) void decode_full_ke
     Frag vc[4];
     auto ldV = [&](int u, int mc) {
       if constexpr (F8) {
-        if ((mc & 3) == 0) fp8_vfrag4(rv.v8[u][mc >> 2], vc);
+        if ((mc & 3) == 0) fp8_vfrag4_rows<D>(rv.v8[u], mc >> 2, vc);
         return vc[mc & 3];
       } else {
         Frag f;
@@ -372,18 +392,16 @@ __global__ __launch_bounds__(256, KV == HS_FP8_E4M3 ? 3 : 2) void decode_full_ke
   if (col < G) {
     float* pp = a.part + ((size_t)(b * a.Hq + h) * a.nch + ch) * (D + 2);
     if (KV == HS_FP8_E4M3) {
-      // rows 4q+i of chunk mc hold head_dim 64*(mc>>2) + 16q + 4i + (mc&3)
+      // rows 4q+i of chunk mc hold head_dim fp8_vrow_dv(mc, 4q+i): this
+      // lane's D/4 values are the contiguous run from (D/4) q
+      float v[D / 4];
 #pragma unroll
-      for (int hf = 0; hf < D / 64; ++hf) {
-        float v[16];
+      for (int mc = 0; mc < Eng::NM; ++mc)
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int i = 0; i < 4; ++i) v[fp8_vrow_dv<D>(mc, i)] = eng.o[0][mc][i] * sv;
+      float4* dst = (float4*)(pp + (D / 4) * (lane >> 4));
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[4 * i + k] = eng.o[0][4 * hf + k][i] * sv;
-        float4* dst = (float4*)(pp + 64 * hf + 4 * q4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-      }
+      for (int j = 0; j < D / 16; ++j) dst[j] = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
     } else {
 #pragma unroll
       for (int mc = 0; mc < Eng::NM; ++mc) *(float4*)(pp + 16 * mc + q4) = *(const float4*)&eng.o[0][mc];
@@ -405,33 +423,55 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeFullArgs a) {
   __shared__ float red[4];
   __shared__ float accs[4][D + 1];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < a.nclear; i += (long)gridDim.x * 256) a.clear[i] = 0u;
   const long bh = blockIdx.x;
   const int b = (int)(bh / a.Hq);
   const int L = ctx_len(a.lens, b, a.C);
   const int span = a.ch_blocks * 64;
   const int nchb = L > 0 ? (L + span - 1) / span : 0;
   const float* pp = a.part + (size_t)bh * a.nch * (D + 2);
-  float M = kNegBig;
-  for (int c = threadIdx.x; c < nchb; c += 256) M = fmaxf(M, pp[(size_t)c * (D + 2) + D]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (lane == 0) red[w] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float acc[PER], lsum = 0.f;
+  // One pass: wave w takes chunks w, w + 4, ... with a running maximum, U
+  // chunks' loads in flight at a time (every load unconditional: chunks past
+  // the sequence reread chunk w and are weighted 0); the four waves' states
+  // are then merged through LDS.
+  constexpr int U = 8;
+  float mw = kNegBig, lsum = 0.f, acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-#pragma unroll 4
-  for (int c = w; c < nchb; c += 4) {
-    const float* p = pp + (size_t)c * (D + 2);
-    const float wt = fast_exp2(p[D] - M);
-    lsum += wt * p[D + 1];
+  for (int c0 = w; c0 < nchb; c0 += 4 * U) {
+    float pm[U], pl[U], po[U][PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += wt * p[lane + 64 * i];
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 4 * u < nchb ? c0 + 4 * u : c0;
+      const float* p = pp + (size_t)c * (D + 2);
+      pm[u] = p[D];
+      pl[u] = p[D + 1];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) po[u][i] = p[lane + 64 * i];
+    }
+    float mn = mw;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mn = c0 + 4 * u < nchb ? fmaxf(mn, pm[u]) : mn;
+    const float sc = fast_exp2(mw - mn);
+    lsum *= sc;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] *= sc;
+    mw = mn;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float wt = c0 + 4 * u < nchb ? fast_exp2(pm[u] - mn) : 0.f;
+      lsum += wt * pl[u];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] += wt * po[u][i];
+    }
   }
+  if (lane == 0) red[w] = mw;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sw = fast_exp2(mw - M);
 #pragma unroll
-  for (int i = 0; i < PER; ++i) accs[w][lane + 64 * i] = acc[i];
-  if (lane == 0) accs[w][D] = lsum;
+  for (int i = 0; i < PER; ++i) accs[w][lane + 64 * i] = acc[i] * sw;
+  if (lane == 0) accs[w][D] = lsum * sw;
   __syncthreads();
   if (w == 0) {
     const float lt = accs[0][D] + accs[1][D] + accs[2][D] + accs[3][D];
@@ -1333,7 +1373,7 @@ __global__ __launch_bounds__(512) void decode_sparse_token_kernel(DecodeSparseAr
   // make the compiler wait for each one in turn.
   struct TileRaw {
     uint4 k[4][Eng::NS / 2];
-    uint32_t v[2][D / 64][8];
+    Fp8VRow<D> v[2][8];
   };
   auto issue = [&](int tsafe, TileRaw& r) {
 #pragma unroll
@@ -1347,8 +1387,7 @@ __global__ __launch_bounds__(512) void decode_sparse_token_kernel(DecodeSparseAr
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int tk = __shfl(tsafe, 32 * u + q8 + e);
-#pragma unroll
-        for (int hf = 0; hf < D / 64; ++hf) r.v[u][hf][e] = *(const uint32_t*)(vg + (size_t)tk * D + 64 * hf + 4 * r16);
+        r.v[u][e] = *(const Fp8VRow<D>*)(vg + (size_t)tk * D + (D / 16) * r16);
       }
   };
   // entries s0 .. s0+nvalid-1 of the live list are the tile's keys
@@ -1360,13 +1399,12 @@ __global__ __launch_bounds__(512) void decode_sparse_token_kernel(DecodeSparseAr
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const bool ok = 32 * u + q8 + e < nvalid;
-#pragma unroll
-        for (int hf = 0; hf < D / 64; ++hf) r.v[u][hf][e] = ok ? r.v[u][hf][e] : 0u;
+        r.v[u][e] = ok ? r.v[u][e] : Fp8VRow<D>{};
       }
     Frag vc[4];
     auto ldK = [&](int c, int ks) { return fp8x8_frag(half_u4(r.k[c][ks >> 1], ks & 1)); };
     auto ldV = [&](int u, int mc) {
-      if ((mc & 3) == 0) fp8_vfrag4(r.v[u][mc >> 2], vc);
+      if ((mc & 3) == 0) fp8_vfrag4_rows<D>(r.v[u], mc >> 2, vc);
       return vc[mc & 3];
     };
     eng.template tile<true, false>(ldK, ldV, s0, lo, hi, sc2, bmax, bsum);
@@ -1420,12 +1458,9 @@ __global__ __launch_bounds__(512) void decode_sparse_token_kernel(DecodeSparseAr
   }
   if (col < G) {
 #pragma unroll
-    for (int hf = 0; hf < D / 64; ++hf) {
+    for (int mc = 0; mc < Eng::NM; ++mc)
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm_o[(w * G + col) * (D + 1) + fp8_vrow_d(4 * hf + k, q4 + i)] = eng.o[0][4 * hf + k][i];
-    }
+      for (int i = 0; i < 4; ++i) sm_o[(w * G + col) * (D + 1) + fp8_vrow_dv<D>(mc, q4 + i)] = eng.o[0][mc][i];
   }
   __syncthreads();
   for (int el = threadIdx.x; el < G * D; el += 64 * NW) {
@@ -1497,13 +1532,13 @@ __global__ __launch_bounds__(1024) void decode_token_combine_kernel(DecodeSparse
 // ================================================================ launchers
 template <int D>
 static void decode_full_dispatch(const DecodeFullArgs& a, dim3 grid, hipStream_t s) {
+  // token mode (logits or bounds) runs on fp8 caches and block mode on bf16
+  // caches; the host has checked the pairing
   if (a.kv_dtype == HS_FP8_E4M3) {
     if (a.token == 2) hipLaunchKernelGGL((decode_full_kernel<D, 2, HS_FP8_E4M3>), grid, dim3(256), 0, s, a);
-    else if (a.token) hipLaunchKernelGGL((decode_full_kernel<D, 1, HS_FP8_E4M3>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((decode_full_kernel<D, 0, HS_FP8_E4M3>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((decode_full_kernel<D, 1, HS_FP8_E4M3>), grid, dim3(256), 0, s, a);
   } else {
-    if (a.token) hipLaunchKernelGGL((decode_full_kernel<D, 1, HS_BF16>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((decode_full_kernel<D, 0, HS_BF16>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_full_kernel<D, 0, HS_BF16>), grid, dim3(256), 0, s, a);
   }
 }
 
@@ -1552,11 +1587,10 @@ hipError_t launch_token_topk(const TokenTopkArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// the histograms and counters were cleared by the full layer's merge kernel
 hipError_t launch_token_topk_bounds(const TokenTopkArgs& a, hipStream_t s) {
   const long rows = (long)a.B * a.Hkv;
-  hipLaunchKernelGGL(zero_u32_kernel, dim3(256), dim3(256), 0, s, a.hist, rows * 2 * 2048 + rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
   hipLaunchKernelGGL(token_zkeys_kernel, dim3((unsigned)rows, (unsigned)((a.C + 4095) / 4096)), dim3(256), 0,
                      s, a);
   e = hipGetLastError();

@@ -90,6 +90,10 @@ struct DecodeFullArgs {
   // tiles, or the tile's own maximum for a chunk's first tile)
   float* zb;
   float* ab;
+  // nclear words at clear are set to zero by the merge kernel (the fused
+  // selection's histograms and counters, which the next kernel accumulates)
+  uint32_t* clear;
+  long nclear;
 };
 
 struct DecodeSparseArgs {
