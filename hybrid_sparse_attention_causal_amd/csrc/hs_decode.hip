@@ -710,11 +710,7 @@ __device__ __forceinline__ uint32_t order_key_f(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// the float of an order key, and the slack of the selection from bounds
-// (below, token_zkeys_kernel)
-__device__ __forceinline__ float inv_order_key(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
+// the slack of the selection from bounds (below, token_zcand_kernel)
 constexpr float kBoundSlack = 1e-3f;
 
 // hist[bin] += 1 for every active lane, one LDS atomic per distinct bin of the
@@ -882,10 +878,6 @@ __global__ __launch_bounds__(1024) void token_cand_kernel(TokenTopkArgs a) {
   __syncthreads();
   find_bin(hist, 2048, need, scan, res);
   const uint32_t pfx = (b1 << 11) | (uint32_t)res[0];
-  // from bounds (wb set): the keys are those of lo, and the candidates are the
-  // tokens whose hi = lo + width reaches the lower edge of the threshold bin
-  const bool bounds = a.wb != nullptr;
-  const float lo_thr = bounds ? inv_order_key(pfx << 10) - kBoundSlack : 0.f;
   const uint32_t* keys = a.keys + (size_t)row * a.C;
   // thread t takes the PER consecutive keys s0 + PER*t .. (16-byte loads),
   // so the block's exclusive scan below keeps the candidates in token order
@@ -902,13 +894,10 @@ __global__ __launch_bounds__(1024) void token_cand_kernel(TokenTopkArgs a) {
     kv[n + 2] = q.z;
     kv[n + 3] = q.w;
   }
-  // the PER keys lie in one 64-token tile (PER divides 64)
-  const float width = bounds && i0 < ncand ? a.wb[(size_t)row * (a.C / 64) + (i0 >> 6)] : 0.f;
   uint32_t flags = 0u, cnt = 0u;
 #pragma unroll
   for (int n = 0; n < PER; ++n) {
-    const bool cand = bounds ? inv_order_key(kv[n]) + width >= lo_thr : (kv[n] >> 10) >= pfx;
-    if (i0 + n < ncand && cand) {
+    if (i0 + n < ncand && (kv[n] >> 10) >= pfx) {
       flags |= 1u << n;
       ++cnt;
     }
@@ -1096,18 +1085,28 @@ __global__ __launch_bounds__(1024) void token_select_kernel(TokenTopkArgs a) {
 // off_h) and, per tile, the offsets off_h.  With the heads' LSEs (log2 units),
 // d_h = LSE_h - off_h gives lo = z - max_h d_h <= x <= z - min_h d_h = hi for
 // the token's score x = max_h (logit_h - LSE_h).  The k-th largest lo (found
-// by the histogram passes on the keys of lo, taken at the lower edge of its
-// 22-bit bin) is at most the k-th largest score, so every token of the top k,
-// ties included, has hi >= it: those tokens are the candidates.  Their scores
-// are then computed exactly from their key rows, and the exact selection runs
-// on them alone.  A slack of kBoundSlack (log2 units) on both tests covers the
-// rounding of the bounds and of the rescoring (kBoundSlack, with the order
-// keys, is defined with them above).
+// from a histogram of lo, taken at the lower edge of its bin) is at most the
+// k-th largest score, so every token of the top k, ties included, has hi >=
+// it: those tokens are the candidates.  Their scores are then computed
+// exactly from their key rows, and the exact selection runs on them alone.
+// A slack of kBoundSlack (log2 units) on the test covers the rounding of the
+// bounds and of the rescoring.
 
-// grid (rows, C/4096): keys of lo for 4096 tokens, the level-1 histogram,
-// and each tile's bound width max_h d_h - min_h d_h.  Thread t takes the
-// token quads t, t + 256, t + 512, t + 768.
-__global__ __launch_bounds__(256) void token_zkeys_kernel(TokenTopkArgs a) {
+// Fixed-point bins of the lower bounds.  Exact scores are log2 weights, so
+// x <= 0 and lo <= x: bin 2047 - j (j < 2047) holds lo in (-(j+1)/64, -j/64],
+// bin 0 everything at or below -2047/64.  One histogram then places the k-th
+// largest lower bound within 1/64.
+constexpr float kZBinScale = 64.f;
+__device__ __forceinline__ uint32_t zbin(float lo) {
+  const float j = fminf(fmaxf(floorf(-lo * kZBinScale), 0.f), 2047.f);
+  return 2047u - (uint32_t)j;
+}
+
+// grid (rows, ceil(C / 4096)), 256 threads: per tile, the bound terms of the
+// group's heads (d_h = LSE_h - offset_h; lo = z - max_h d_h, hi = z - min_h
+// d_h), min_h d_h stored for the candidate pass; the histogram of the
+// candidates' lower bounds (plain LDS atomics: the bins of one wave are many)
+__global__ __launch_bounds__(256) void token_zhist_kernel(TokenTopkArgs a) {
   __shared__ uint32_t hist[2048];
   __shared__ float lse2[16];
   const int row = blockIdx.x;
@@ -1120,18 +1119,13 @@ __global__ __launch_bounds__(256) void token_zkeys_kernel(TokenTopkArgs a) {
   __syncthreads();
   const int base = blockIdx.y * 4096;
   const int ntl = a.C / 64;
-  uint32_t* keys = a.keys + (size_t)row * a.C;
   const float* zr = a.zb + (size_t)row * a.C;
   const float* ar = a.ab + (size_t)row * ntl * G;
   float* wr = a.wb + (size_t)row * ntl;
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const int i0 = base + 4 * (threadIdx.x + 256 * n);
-    // C is a multiple of 64: a lane past it leaves (the histogram's ballots
-    // take the lanes still running)
-    if (i0 >= a.C) break;
-    uint32_t kq[4] = {0u, 0u, 0u, 0u};
-    if (i0 < L) {
+    if (i0 < min(L, a.C)) {
       const int tl = i0 >> 6;
       float dmax = -INFINITY, dmin = INFINITY;
       for (int hh = 0; hh < G; ++hh) {
@@ -1139,21 +1133,93 @@ __global__ __launch_bounds__(256) void token_zkeys_kernel(TokenTopkArgs a) {
         dmax = fmaxf(dmax, d);
         dmin = fminf(dmin, d);
       }
-      if ((i0 & 63) == 0) wr[tl] = dmax - dmin;
+      if ((i0 & 63) == 0) wr[tl] = dmin;
       const float4 z = *(const float4*)(zr + i0);
       const float zs[4] = {z.x, z.y, z.z, z.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (i0 + e < ncand) kq[e] = order_key_f(zs[e] - dmax);
+        if (i0 + e < ncand) atomicAdd(&hist[zbin(zs[e] - dmax)], 1u);
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) wave_hist_add(hist, kq[e] >> 21, i0 + e < ncand);
-    *(uint4*)(keys + i0) = make_uint4(kq[0], kq[1], kq[2], kq[3]);
   }
   __syncthreads();
   uint32_t* gh = a.hist + (size_t)row * 2048;
   for (int i = threadIdx.x; i < 2048; i += 256)
     if (hist[i]) atomicAdd(&gh[i], hist[i]);
+}
+
+// grid (rows, ceil(C / kTokSeg)), 1024 threads: the candidates of one row
+// segment.  The bin of the k-th largest lower bound gives T, its lower edge
+// (at least k scores lie above T); a token is a candidate when its upper
+// bound reaches T - kBoundSlack.  The k-th bound in the open bottom bin
+// leaves T = -inf: every token is a candidate, more than the candidate
+// buffer holds, and the pick takes exact scores of the whole row.
+__global__ __launch_bounds__(1024) void token_zcand_kernel(TokenTopkArgs a) {
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t scan[1024];
+  __shared__ int res[2];
+  __shared__ uint32_t base_s;
+  const int row = blockIdx.x, t = threadIdx.x;
+  const int L = ctx_len(a.lens, row / a.Hkv, a.C);
+  const int ncand = max(0, L - a.n_recent);
+  const int s0 = blockIdx.y * kTokSeg;
+  if (ncand <= a.kb || s0 >= ncand) return;  // uniform
+  const size_t rows = (size_t)a.B * a.Hkv;
+  for (int i = t; i < 2048; i += 1024) hist[i] = a.hist[(size_t)row * 2048 + i];
+  __syncthreads();
+  find_bin(hist, 2048, a.kb, scan, res);
+  const int bk = res[0];
+  const float thr = bk > 0 ? -(float)(2048 - bk) / kZBinScale - kBoundSlack : -INFINITY;
+  const float* zr = a.zb + (size_t)row * a.C;
+  // thread t takes the PER consecutive tokens s0 + PER*t .. (16-byte loads),
+  // so the block's exclusive scan below keeps the candidates in token order
+  constexpr int PER = kTokSeg / 1024;
+  static_assert(PER % 4 == 0 && 64 % PER == 0, "four z per load; a thread's tokens lie in one tile");
+  float zv[PER];
+  const int i0 = s0 + PER * t;
+#pragma unroll
+  for (int n = 0; n < PER; n += 4) {
+    // a row holds C values, C a multiple of 64, so a quad never leaves it
+    const float4 q = i0 + n < ncand ? *(const float4*)(zr + i0 + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+    zv[n] = q.x;
+    zv[n + 1] = q.y;
+    zv[n + 2] = q.z;
+    zv[n + 3] = q.w;
+  }
+  const float dmin = i0 < ncand ? a.wb[(size_t)row * (a.C / 64) + (i0 >> 6)] : 0.f;
+  uint32_t flags = 0u, cnt = 0u;
+#pragma unroll
+  for (int n = 0; n < PER; ++n) {
+    if (i0 + n < ncand && zv[n] - dmin >= thr) {
+      flags |= 1u << n;
+      ++cnt;
+    }
+  }
+  // block exclusive scan of the per-thread counts
+  scan[t] = cnt;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const uint32_t x = t >= off ? scan[t - off] : 0u;
+    __syncthreads();
+    scan[t] += x;
+    __syncthreads();
+  }
+  const uint32_t excl = scan[t] - cnt;
+  if (t == 1023) {
+    base_s = atomicAdd(a.hist + rows * 2 * 2048 + row, scan[1023]);
+    // this segment's run: its candidates in ascending token order
+    a.seg[((size_t)row * a.nseg + blockIdx.y) * 2] = base_s;
+    a.seg[((size_t)row * a.nseg + blockIdx.y) * 2 + 1] = scan[1023];
+  }
+  __syncthreads();
+  uint32_t pos = base_s + excl;
+  int32_t* ci = a.cand_idx + (size_t)row * kTokCap;
+#pragma unroll
+  for (int n = 0; n < PER; ++n) {
+    if ((flags >> n) & 1u) {
+      if (pos < (uint32_t)kTokCap) ci[pos] = i0 + n;
+      ++pos;
+    }
+  }
 }
 
 // The exact score (log2 units) of token i of row (b, g): max over the group's
@@ -1591,15 +1657,12 @@ hipError_t launch_token_topk(const TokenTopkArgs& a, hipStream_t s) {
 hipError_t launch_token_topk_bounds(const TokenTopkArgs& a, hipStream_t s) {
   const long rows = (long)a.B * a.Hkv;
   hipError_t e;
-  hipLaunchKernelGGL(token_zkeys_kernel, dim3((unsigned)rows, (unsigned)((a.C + 4095) / 4096)), dim3(256), 0,
+  hipLaunchKernelGGL(token_zhist_kernel, dim3((unsigned)rows, (unsigned)((a.C + 4095) / 4096)), dim3(256), 0,
                      s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 seg((unsigned)rows, (unsigned)((a.C + kTokSeg - 1) / kTokSeg));
-  hipLaunchKernelGGL(token_hist2_kernel, seg, dim3(1024), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(token_cand_kernel, seg, dim3(1024), 0, s, a);
+  hipLaunchKernelGGL(token_zcand_kernel, seg, dim3(1024), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 rs((unsigned)rows, (unsigned)(kTokCap / 256));

@@ -123,7 +123,8 @@ struct TokenTopkArgs {
   const int32_t* lens;
   uint32_t* keys;         // workspace [B*Hkv][C]
   uint32_t* hist;         // workspace [B*Hkv][2048] level-1, then [B*Hkv][2048] level-2,
-                          // then [B*Hkv] candidate counts (zeroed together)
+                          // then [B*Hkv] candidate counts (zeroed together); from
+                          // bounds, the first part holds the lower bounds' bins
   uint32_t* cand_key;     // workspace [B*Hkv][kTokCap]
   int32_t* cand_idx;      // workspace [B*Hkv][kTokCap]
   uint32_t* seg;          // workspace [B*Hkv][nseg][2]: (first slot, count) of each
@@ -131,8 +132,8 @@ struct TokenTopkArgs {
   int nseg;               // key segments per row, ceil(C / kTokSeg)
   int B, Hq, Hkv, C, kb, n_recent;
   // selection from bounds (raw unused): zb, ab as written by the full layer
-  // with token == 2, wb [rows][C/64] scratch (per-tile bound widths), and
-  // what the exact rescoring of the candidates reads
+  // with token == 2, wb [rows][C/64] scratch (per tile, min over the heads of
+  // LSE_h - offset_h: hi = z - wb), and what the exact rescoring reads
   const float* zb;
   const float* ab;
   float* wb;
