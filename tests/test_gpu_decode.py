@@ -490,6 +490,21 @@ def test_token_select_all_tied_takes_the_whole_row():
     check_token_select(run, range(2))
 
 
+def test_token_select_peaked_scores_open_bin():
+    """One sequence's queries scaled by 40: its scores spread over hundreds of
+    log2 units, so fewer than k lower bounds lie within 32 of zero.  The k-th
+    bound falls in the open bottom bin, every old token is a candidate (more
+    than the candidate store holds), and the pick takes exact scores of the
+    whole row.  The second sequence is unscaled."""
+    say("[token select peaked] fp8, C=16384, top-2048 + 128 recent, one sequence with q x 40")
+    cfg = gen.config(5, B=2, T=16384, Hq=8, Hkv=2, d=128, kb=2048, n_recent=128, N=0,
+                     L_lo=16384, L_hi=16384)
+    inp = gen.make_decode(cfg)
+    inp.lens = np.array([16384, 9000], np.int32)
+    inp.q[0] = gen.f32_to_bf16_bits(gen.bf16_bits_to_f32(inp.q[0]) * 40.0)
+    check_token_select(TokenSelectRun(inp), range(2))
+
+
 def test_token_select_config5_full_size_all_sequences():
     say("[token select, config 5] 16 seqs x 262144 fp8 tokens, top-2048 + 128 recent, every sequence")
     inp = gen.make_decode(gen.config(5), n_layers=0)
