@@ -129,7 +129,8 @@ size_t token_topk_ws(const hs_shape* s) {
          ((rows + 3) / 4) * 4 * sizeof(uint32_t);
 }
 // hs_decode_token_select: split-K partials, the bounds (z per token, offsets
-// per tile and head, widths per tile) and the token selection's workspace
+// per tile and head, the upper-bound term per tile) and the token selection's
+// workspace (its key array serves the whole-row fallback)
 struct TokenSelWs {
   size_t part, zb, ab, wb, topk, total;
 };
