@@ -119,6 +119,11 @@ __global__ __launch_bounds__(256, KV == HS_FP8_E4M3 ? 3 : 2) void decode_full_ke
   using Frag = Tt::Frag;
   using Eng = WaveAttn<HS_BF16, D, 1>;
   constexpr int KES = KV == HS_FP8_E4M3 ? 1 : 2;  // cache bytes per element
+  // bounds (TOKEN == 2): each wave's z and offsets of its chunk are gathered
+  // here and written out when the chunk ends, in wide contiguous stores
+  // instead of small stores interleaved with the cache reads
+  __shared__ __attribute__((aligned(16))) float zst[TOKEN == 2 ? 4 * kDecodeChunkBlocksMax * 64 : 1];
+  __shared__ float ast[TOKEN == 2 ? 4 * kDecodeChunkBlocksMax * 16 : 1];
   const int lane = threadIdx.x & 63;
   const int span = a.ch_blocks * 64;  // ch_blocks <= kDecodeChunkBlocksMax
   // Wave id -> live unit: sequence b owns Hkv * ceil(L_b / span) consecutive
@@ -319,13 +324,9 @@ __global__ __launch_bounds__(256, KV == HS_FP8_E4M3 ? 3 : 2) void decode_full_ke
 #pragma unroll
         for (int e = 0; e < 16; ++e) xm[e] = col < G ? x[e] - off : -INFINITY;
         const float z = row16_max_scatter(xm, col);
-        const size_t brow = (size_t)b * a.Hkv + g;
-        a.zb[brow * a.C + kb0 + tile_key(col >> 2, q4 + (col & 3))] = z;
-        // every lane stores (columns past G repeat head G-1's offset to its
-        // slot): a store under a lane branch would make the compiler count
-        // it as maybe absent and wait one load longer at every later wait
-        const float offs = col < G ? off : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(off), G - 1));
-        a.ab[(brow * (a.C / 64) + (kb0 >> 6)) * G + min(col, G - 1)] = offs;
+        const int slot = (threadIdx.x >> 6) * kDecodeChunkBlocksMax + ((kb0 - kstart) >> 6);
+        zst[slot * 64 + tile_key(col >> 2, q4 + (col & 3))] = z;
+        if (col < G) ast[slot * 16 + col] = off;
       };
       eng.template softmax<true, false>(s, kb0, lo, hi, sc2, bmax, bsum, hook);
     } else if constexpr (TOKEN == 1) {
@@ -379,6 +380,17 @@ __global__ __launch_bounds__(256, KV == HS_FP8_E4M3 ? 3 : 2) void decode_full_ke
     body(kb0, kb0, std::false_type{});
   }
 
+  if constexpr (TOKEN == 2) {
+    // the chunk's bounds: z of its keys (contiguous in the row) and the
+    // offsets of its tiles, from this wave's staging rows
+    const size_t brow = (size_t)b * a.Hkv + g;
+    const int w4 = threadIdx.x >> 6;
+    float4* zg = (float4*)(a.zb + brow * a.C + kstart);
+    const float4* zs = (const float4*)(zst + w4 * kDecodeChunkBlocksMax * 64);
+    for (int i = lane; i < ntile * 16; i += 64) zg[i] = zs[i];
+    float* ag = a.ab + (brow * (a.C / 64) + (kstart >> 6)) * G;
+    for (int i = lane; i < ntile * G; i += 64) ag[i] = ast[(w4 * kDecodeChunkBlocksMax + i / G) * 16 + i % G];
+  }
   if (!TOKEN && col < G) {
 #pragma unroll
     for (int r = 0; r < kDecodeChunkBlocksMax / 4; ++r) {
