@@ -1,7 +1,8 @@
 """HIP graph capture of whole hybrid blocks through the C ABI: the library
 allocates nothing and records no memory-set nodes, so a prefill block and a
 decode step (block mode with window, gates and sinks; token mode with split
-work groups) can be captured once and replayed.  Every replay must reproduce
+work groups, selected in two calls or in the fused call) can be captured once
+and replayed.  Every replay must reproduce
 the eager results bit for bit, with eager work and synchronisations between
 replays and the outputs poisoned before each one."""
 import sys
@@ -78,9 +79,10 @@ def test_prefill_block_graph():
     _replay_matches(step, [o, lse, idx] + [l["o"] for l in layers])
 
 
-@pytest.mark.parametrize("token", [False, True])
-def test_decode_step_graph(token):
-    say(f"[graph] decode step, token mode={token}")
+@pytest.mark.parametrize("mode", ["block", "token", "token_fused"])
+def test_decode_step_graph(mode):
+    say(f"[graph] decode step, {mode}")
+    token = mode != "block"
     if token:
         cfg = gen.config(5, B=3, T=8192, Hq=8, Hkv=2, d=128, kb=600, n_recent=32, N=2,
                          L_lo=100, L_hi=8192)
@@ -113,6 +115,10 @@ def test_decode_step_graph(token):
                           dtype=torch.uint8, device="cuda")
     ws_sel = torch.empty(max(16, hb.workspace_size(hb.HS_FN_DECODE_SELECT, shape, blk)),
                          dtype=torch.uint8, device="cuda")
+    ws_tsel = None
+    if mode == "token_fused":
+        ws_tsel = torch.empty(hb.workspace_size(hb.HS_FN_DECODE_TOKEN_SELECT, shape, 1, cfg.kb),
+                              dtype=torch.uint8, device="cuda")
     layers = []
     for i, lay in enumerate(inp.layers):
         ent = dict(q=dev(lay["q"]), s=dev(gen.make_sinks(cfg, i)), o=torch.empty_like(o))
@@ -122,9 +128,13 @@ def test_decode_step_graph(token):
         layers.append(ent)
 
     def step():
-        hb.decode_full_attn_scores(q, k, v, lens, o, lse, raw, block=blk, ws=ws_full, kv_scale=scale)
-        hb.decode_block_topk(q, k, lens, raw, lse, cfg.kb, idx, block=blk, n_recent=cfg.n_recent,
-                             kv_scale=scale)
+        if mode == "token_fused":
+            # full layer and token selection in one call (bounds, rescoring)
+            hb.decode_token_select(q, k, v, lens, o, lse, cfg.kb, cfg.n_recent, idx, scale, ws=ws_tsel)
+        else:
+            hb.decode_full_attn_scores(q, k, v, lens, o, lse, raw, block=blk, ws=ws_full, kv_scale=scale)
+            hb.decode_block_topk(q, k, lens, raw, lse, cfg.kb, idx, block=blk, n_recent=cfg.n_recent,
+                                 kv_scale=scale)
         for l in layers:
             if token:
                 hb.decode_select_attn(l["q"], k, v, lens, idx, nsel, None, None, 0, None, l["o"],
