@@ -223,7 +223,7 @@ size_t offload_ws(const hs_shape* s, int chunk) {
 // backward workspace: layout copies of K and V, per-row terms, per-column
 // statistics, the sparse branch's position lists
 struct BwdWs {
-  size_t kb[2], vp[2], delta[2], sterm[2], cstat[2], colbits, plist, pcnt, poff, total;
+  size_t vp[2], delta[2], sterm[2], cstat[2], colbits, plist, pcnt, poff, total;
 };
 int bwd_nc(const hs_shape* s) {
   const long cols = (long)s->q_len * hs::bwd_gp(s->hq / s->hkv) + 32;
@@ -241,7 +241,6 @@ BwdWs bwd_ws(const hs_shape* s, bool sparse, int topk) {
   };
   const int nbr = sparse ? 2 : 1;
   for (int i = 0; i < nbr; ++i) {
-    w.kb[i] = take(B * Hkv * nblk * D * 64 * 2);
     w.vp[i] = take(B * Hkv * nblk * 64 * D * 2);
   }
   for (int i = 0; i < nbr; ++i) w.delta[i] = take(B * Hq * T * 4);
@@ -876,9 +875,7 @@ hs_status hs_full_attn_bwd(const hs_shape* s, const void* q, const void* k, cons
   hipStream_t strm = (hipStream_t)stream;
   const int nblk = (s->q_len + 63) / 64;
   hs::BwdLayoutArgs l{};
-  l.k[0] = k;
   l.v[0] = v;
-  l.kb[0] = W + w.kb[0];
   l.vp[0] = W + w.vp[0];
   l.B = s->batch;
   l.T = s->q_len;
@@ -928,7 +925,6 @@ hs_status hs_full_attn_bwd(const hs_shape* s, const void* q, const void* k, cons
   b.q = q;
   b.dout = dout;
   b.k0 = k;
-  b.kb0 = l.kb[0];
   b.vp0 = l.vp[0];
   b.lse0 = lse;
   b.delta0 = r.delta[0];
@@ -989,15 +985,12 @@ hs_status hs_sparse_attn_bwd(const hs_shape* s, const void* q_sp, const void* k,
   const size_t brs = (size_t)s->batch * T * s->hq;  // rows of one branch
   hs::BwdLayoutArgs l{};
   if (topk > 0) {
-    l.k[0] = k;
     l.v[0] = v;
   }
   if (window > 0) {
-    l.k[1] = k_swa;
     l.v[1] = v_swa;
   }
   for (int i = 0; i < 2; ++i) {
-    l.kb[i] = W + w.kb[i];
     l.vp[i] = W + w.vp[i];
   }
   l.B = s->batch;
@@ -1087,10 +1080,8 @@ hs_status hs_sparse_attn_bwd(const hs_shape* s, const void* q_sp, const void* k,
   b.q = q_sp;
   b.dout = dout;
   b.k0 = k;
-  b.kb0 = l.kb[0];
   b.vp0 = l.vp[0];
   b.k1 = k_swa;
-  b.kb1 = l.kb[1];
   b.vp1 = l.vp[1];
   b.lse0 = r.lse[0];
   b.lse1 = r.lse[1];

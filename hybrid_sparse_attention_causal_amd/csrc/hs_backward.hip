@@ -11,9 +11,8 @@
 // (sigma = 1 for the full layer and ungated layers).
 //
 // Every matrix product reads its operands in the order the MFMA wants, from
-// layout copies made first (memory-bound transposes) or, for the queries and
-// output gradients, from transposing LDS reads:
-//   Kb  keys block-major [..][nblk][D][64]   (A operand of dQ^T = K^T dS^T)
+// a layout copy made first (a memory-bound transpose) or from transposing
+// LDS reads (queries, output gradients, and K^T for dQ^T = K^T dS^T):
 //   Vp  values position-major [..][T][D]     (dP = dO V^T, both orientations)
 //
 //  bwd_kv_kernel  key side: one work group per (sequence, kv group, 64-key
@@ -34,8 +33,8 @@
 //  bwd_q_kernel   query side: work groups of 4*16/G positions as in the
 //                 forward; per item (key tile) S^T = K Q^T and dP^T = V dO^T
 //                 (K rows and V rows staged in LDS), dS^T elementwise, then
-//                 dQ^T += K^T dS^T with the block-major K tile, as the
-//                 forward's P V.  Sparse layers: window items (branch 1)
+//                 dQ^T += K^T dS^T reading K^T from the staged K rows by
+//                 transposing LDS reads, as the forward's P V.  Sparse layers: window items (branch 1)
 //                 then the union of the selected blocks (branch 0), each
 //                 with its own LSE, dO.o and gate.
 #include "hs_device.h"
@@ -46,32 +45,6 @@ namespace hs {
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 
 // ================================================== layout conversions
-// K [B*Hkv][T][D] -> Kb [B*Hkv][nblk][D][64], zero past T
-template <int D>
-__global__ __launch_bounds__(256) void k_to_blockmajor_kernel(const uint16_t* k, uint16_t* kb, int T, int nblk) {
-  __shared__ uint16_t tl[64][D + 2];
-  const int j = blockIdx.x % nblk;
-  const size_t bg = blockIdx.x / nblk;
-  for (int e = threadIdx.x; e < 64 * D / 8; e += 256) {
-    const int r = e / (D / 8), c = e % (D / 8), t = 64 * j + r;
-    const uint4 x = t < T ? *(const uint4*)(k + (bg * T + t) * D + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tl[r][8 * c + 2 * i] = (uint16_t)(w[i] & 0xffffu);
-      tl[r][8 * c + 2 * i + 1] = (uint16_t)(w[i] >> 16);
-    }
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < D * 8; e += 256) {
-    const int dd = e / 8, c = e % 8;
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)tl[8 * c + 2 * i][dd] | ((uint32_t)tl[8 * c + 2 * i + 1][dd] << 16);
-    *(uint4*)(kb + ((bg * nblk + j) * D + dd) * 64 + 8 * c) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
 // V [B*Hkv][nblk][D][64] -> Vp [B*Hkv][nblk*64][D], zero past T (the tail of
 // the last value tile may hold anything)
 template <int D>
@@ -533,14 +506,35 @@ struct RowStage {
     const int ch = (32 * ks + 8 * (lane >> 4)) * 2 / 16;
     return Tr<HS_BF16>::ld(buf + k_lds(row, ch));
   }
+  // The transposed tile as an A fragment: head_dim rows 16 mc + r16, keys
+  // 32 u + 8 q .. +7 (the P.V key order).  Two transposing reads: lane L of
+  // each 16-lane group points at 4 dims (16 mc + 4 (L%4) ..) of the row of
+  // key 32 u + 8 q + 4 h + (L%16)/4 and receives one dim of 4 keys.
+  __device__ __forceinline__ static Tr<HS_BF16>::Frag ldKT(const char* buf, int u, int mc) {
+    const int lane = lane_id(), r16 = lane & 15;
+    const int byte = 32 * mc + 8 * (r16 & 3);
+    uint2 hh[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = tile_row(32 * u + 8 * (lane >> 4) + 4 * h + (r16 >> 2));
+      const int off = k_lds(row, byte >> 4) + (byte & 15);
+      hh[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                           (__attribute__((address_space(3))) bf16x4_t*)(buf + off)));
+    }
+    Tr<HS_BF16>::Frag f;
+    f.u = make_uint4(hh[0].x, hh[0].y, hh[1].x, hh[1].y);
+    return f;
+  }
 };
 
 template <int D, int MODE>
-__global__ __launch_bounds__(256) void bwd_q_kernel(BwdQArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_q_kernel(BwdQArgs a) {
   using Tt = Tr<HS_BF16>;
   using Eng = WaveAttn<HS_BF16, D, 1>;
-  using StK = TileStage<HS_BF16, D, 256>;  // K rows + the block-major K tile
-  using StV = RowStage<D, 256>;            // V rows
+  // K rows (S^T = K Q^T reads them as they are, dQ^T += K^T dS^T through
+  // transposing reads) and V rows: 64 KiB of tiles, two work groups per CU
+  using StK = RowStage<D, 256>;
+  using StV = RowStage<D, 256>;
   constexpr int NW = 4;
   __shared__ __attribute__((aligned(16))) char kt0[StK::BYTES];
   __shared__ __attribute__((aligned(16))) char kt1[StK::BYTES];
@@ -656,9 +650,8 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdQArgs a) {
     const bool win = MODE == 1 && i < nwin;
     const int j = blk(i);
     const char* kr = (const char*)(win ? a.k1 : a.k0) + ((size_t)bg * T + 64 * j) * D * 2;
-    const char* kbs = (const char*)(win ? a.kb1 : a.kb0) + ((size_t)bg * a.nblk + j) * D * 64 * 2;
     const char* vr = (const char*)(win ? a.vp1 : a.vp0) + ((size_t)bg * a.nblk * 64 + 64 * j) * D * 2;
-    sk.dma(kb, kr, kbs, T - 64 * j);
+    sk.dma(kb, kr, T - 64 * j);
     sv.dma(vb, vr, T - 64 * j);
   };
   if (nitems > 0) issue(0, kt0, vt0);
@@ -697,7 +690,7 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdQArgs a) {
           s[0][c][i2] = p * s0 * (dp[0][c][i2] - d0);
         }
       Tt::pack_p(s[0]);
-      eq.pv(s, [&](int u, int mc) { return StK::ldV(kc, u, mc); });
+      eq.pv(s, [&](int u, int mc) { return StK::ldKT(kc, u, mc); });
     }
     wait_vmem();
     __syncthreads();
@@ -722,8 +715,6 @@ template <int D>
 static hipError_t layouts(const BwdLayoutArgs& l, hipStream_t s) {
   const unsigned nkb = (unsigned)((long)l.B * l.Hkv * l.nblk);
   for (int i = 0; i < 2; ++i) {
-    if (l.k[i]) hipLaunchKernelGGL(k_to_blockmajor_kernel<D>, dim3(nkb), dim3(256), 0, s, (const uint16_t*)l.k[i],
-                                   (uint16_t*)l.kb[i], l.T, l.nblk);
     if (l.v[i]) hipLaunchKernelGGL(v_to_posmajor_kernel<D>, dim3(nkb), dim3(256), 0, s, (const uint16_t*)l.v[i],
                                    (uint16_t*)l.vp[i], l.T, l.nblk);
   }

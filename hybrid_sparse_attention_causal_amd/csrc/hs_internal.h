@@ -181,9 +181,7 @@ size_t offload_stage_bytes(int chunk, int Hkv, int C, int D, int es);
 // ------------------------------------------------------------ backward
 // layout copies for the backward (hs_backward.hip)
 struct BwdLayoutArgs {
-  const void* k[2];  // key caches [B][Hkv][T][D] (NULL: skip)
-  const void* v[2];  // block-major value caches [B][Hkv][nblk][D][64]
-  void* kb[2];       // out: keys block-major [B][Hkv][nblk][D][64]
+  const void* v[2];  // block-major value caches [B][Hkv][nblk][D][64] (NULL: skip)
   void* vp[2];       // out: values position-major [B][Hkv][nblk*64][D]
   int B, T, Hq, Hkv, nblk;
 };
@@ -227,11 +225,9 @@ struct BwdKVArgs {
 struct BwdQArgs {
   const void* q;
   const void* dout;
-  const void* k0;   // branch 0 (full layer / sparse branch): keys, keys block-major, values position-major
-  const void* kb0;
+  const void* k0;   // branch 0 (full layer / sparse branch): keys [B][Hkv][T][D], values position-major
   const void* vp0;
   const void* k1;   // branch 1 (window): the layer's own cache
-  const void* kb1;
   const void* vp1;
   const float* lse0;
   const float* lse1;
