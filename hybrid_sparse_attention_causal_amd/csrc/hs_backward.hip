@@ -88,15 +88,31 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdRowArgs a) {
   const int h = (int)(rr % a.Hq);
   const long bt = rr / a.Hq;
   const int t = (int)(bt % a.T), b = (int)(bt / a.T);
-  const int per = a.D / 16;  // elements per lane
-  for (int br = 0; br < a.nbr; ++br) {
-    const uint16_t* o = (const uint16_t*)a.o[br] + rr * a.D;
-    const uint16_t* d = (const uint16_t*)a.dout + rr * a.D;
-    float acc = 0.f;
-    for (int i = 0; i < per; ++i) {
-      const int e = sub * per + i;
-      acc += __uint_as_float((uint32_t)o[e] << 16) * __uint_as_float((uint32_t)d[e] << 16);
+  // a lane's D/16 elements (8 or 4 bf16) of a row in one vector load
+  auto ld = [&](const void* base, float* x) {
+    const char* p = (const char*)base + (rr * a.D + sub * (a.D / 16)) * 2;
+    uint32_t u[4];
+    if (a.D == 128) {
+      const uint4 v = *(const uint4*)p;
+      u[0] = v.x, u[1] = v.y, u[2] = v.z, u[3] = v.w;
+    } else {
+      const uint2 v = *(const uint2*)p;
+      u[0] = v.x, u[1] = v.y, u[2] = 0u, u[3] = 0u;
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(u[i] << 16);
+      x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  };
+  float dx[8];
+  ld(a.dout, dx);
+  for (int br = 0; br < a.nbr; ++br) {
+    float ox[8];
+    ld(a.o[br], ox);
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc += ox[i] * dx[i];
 #pragma unroll
     for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
     if (in && sub == 0) {
@@ -136,18 +152,29 @@ __global__ __launch_bounds__(256) void bwd_sink_reduce_kernel(BwdRowArgs a) {
 // ceil(T/32)): bit t of block j's row is set when position t's list holds j
 // with 0 <= j < nblk and 64 j <= t (the forward's rule; duplicates count
 // once).
-__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, long n) {
-  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) p[i] = 0u;
-}
-__global__ __launch_bounds__(256) void colbits_kernel(const int32_t* idx, uint32_t* bits, long n, int T, int topk,
-                                                      int nblk, int nwt) {
-  const long e = (long)blockIdx.x * 256 + threadIdx.x;
-  if (e >= n) return;
-  const long rowi = e / topk;  // bg * T + t
-  const int t = (int)(rowi % T);
-  const long bg = rowi / T;
-  const int j = idx[e];
-  if (j >= 0 && j < nblk && 64 * j <= t) atomicOr(&bits[(bg * nblk + j) * nwt + (t >> 5)], 1u << (t & 31));
+// One work group per (kv group, run of nword words of positions): the
+// group's bits are gathered in LDS ([nblk][nword] words, atomics in LDS only)
+// and every word of the run is written, zero or not.
+__global__ __launch_bounds__(256) void colbits_kernel(const int32_t* idx, uint32_t* bits, int T, int topk, int nblk,
+                                                      int nwt, int nword) {
+  extern __shared__ uint32_t sb[];
+  const int bg = blockIdx.y;
+  const int w0 = blockIdx.x * nword;
+  const int nw = min(nword, nwt - w0);
+  for (int i = threadIdx.x; i < nblk * nword; i += 256) sb[i] = 0u;
+  __syncthreads();
+  const int t0 = 32 * w0, tn = min(T, t0 + 32 * nw);
+  const int32_t* ir = idx + ((size_t)bg * T + t0) * topk;
+  for (int e = threadIdx.x; e < (tn - t0) * topk; e += 256) {
+    const int t = t0 + e / topk;
+    const int j = ir[e];
+    if (j >= 0 && j < nblk && 64 * j <= t) atomicOr(&sb[j * nword + ((t - t0) >> 5)], 1u << (t & 31));
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nblk * nw; i += 256) {
+    const int j = i / nw, w = i % nw;
+    bits[((size_t)bg * nblk + j) * nwt + w0 + w] = sb[j * nword + w];
+  }
 }
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
@@ -738,13 +765,13 @@ hipError_t launch_pos_lists(const int32_t* idx, uint32_t* colbits, int32_t* plis
                             int B, int Hkv, int T, int topk, int nblk, hipStream_t s) {
   const int nwt = (T + 31) / 32;
   const int nbj = B * Hkv * nblk;
-  hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, s, colbits, (long)nbj * nwt);
+  // 8 words (256 positions) per work group, fewer when nblk x 8 words would
+  // pass 32 KiB of LDS
+  const int nword = std::max(1, std::min(8, 8192 / nblk));
+  hipLaunchKernelGGL(colbits_kernel, dim3((unsigned)((nwt + nword - 1) / nword), (unsigned)(B * Hkv)), dim3(256),
+                     (size_t)nblk * nword * sizeof(uint32_t), s, idx, colbits, T, topk, nblk, nwt, nword);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long n = (long)B * Hkv * T * topk;
-  if (n > 0)
-    hipLaunchKernelGGL(colbits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx, colbits, n, T, topk,
-                       nblk, nwt);
   const unsigned nwg = (unsigned)((nbj + 3) / 4);
   hipLaunchKernelGGL(pos_count_kernel, dim3(nwg), dim3(256), 0, s, colbits, pcnt, nbj, nblk, nwt);
   hipLaunchKernelGGL(pos_write_kernel, dim3(nwg), dim3(256), 0, s, colbits, pcnt, poff, plist, nbj, nblk, nwt,
