@@ -25,17 +25,6 @@
 
 namespace hs {
 
-// Maximum over the 16 lanes of a row (lanes 16r .. 16r+15), every lane of the
-// row getting it: swaps within pairs and quads, then the half-row and row
-// mirrors (DPP, no LDS).
-__device__ __forceinline__ float row16_max(float v) {
-  v = max2(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = max2(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  v = max2(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
-  v = max2(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
-  return v;
-}
-
 // head_dim order of the QK^T operands from a position-major fp8 cache: lane
 // group q = lane/16 holds, at k-step ks, head_dim (D/4) q + 8 ks .. +7, so a
 // lane's keys over all k-steps are one contiguous D/4-byte run of the row

@@ -66,9 +66,8 @@ __device__ __forceinline__ F8x32 f8_zero() {
   return f;
 }
 
-// key held in row (16c + rho) of the fp8 S^T tile, and the inverse
+// key held in row (16c + rho) of the fp8 S^T tile
 __host__ __device__ __forceinline__ int f8_tile_key(int c, int rho) { return ((rho >> 2) << 4) | (c << 2) | (rho & 3); }
-__host__ __device__ __forceinline__ int f8_tile_row(int kk) { return (((kk >> 2) & 3) << 4) | ((kk >> 4) << 2) | (kk & 3); }
 
 // four floats -> four e4m3 codes (RNE), one dword, byte e = element e
 __device__ __forceinline__ uint32_t f8x4_bits(float a, float b, float c, float d) {
