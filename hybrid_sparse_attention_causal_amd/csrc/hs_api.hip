@@ -223,7 +223,7 @@ size_t offload_ws(const hs_shape* s, int chunk) {
 // backward workspace: layout copies of K and V, per-row terms, per-column
 // statistics, the sparse branch's position lists
 struct BwdWs {
-  size_t vp[2], delta[2], sterm[2], cstat[2], colbits, plist, pcnt, poff, total;
+  size_t vp[2], delta[2], sterm[2], cstat[2], colbits, plist, pcnt, poff, utab, ucount, soff, pbuf, total;
 };
 int bwd_nc(const hs_shape* s) {
   const long cols = (long)s->q_len * hs::bwd_gp(s->hq / s->hkv) + 32;
@@ -252,6 +252,11 @@ BwdWs bwd_ws(const hs_shape* s, bool sparse, int topk) {
     w.plist = take(B * Hkv * T * (size_t)(topk > 0 ? topk : 1) * 4);
     w.pcnt = take(B * Hkv * nblk * 4);
     w.poff = take(B * Hkv * nblk * 4);
+    const int tk = topk > 0 ? topk : 1;
+    w.utab = take(B * Hkv * (size_t)hs::kv_umax((int)nblk, (int)T, tk) * 4);
+    w.ucount = take(B * Hkv * 4);
+    w.soff = take(B * Hkv * nblk * 4);
+    w.pbuf = take(B * Hkv * (size_t)hs::kv_smax((int)T, tk) * 2 * 64 * D * 4);
   }
   w.total = off;
   return w;
@@ -1008,6 +1013,9 @@ hs_status hs_sparse_attn_bwd(const hs_shape* s, const void* q_sp, const void* k,
     e = hs::launch_pos_lists(idx, (uint32_t*)(W + w.colbits), plist, pcnt, poff, s->batch, s->hkv, T, topk, nblk,
                              strm);
     if (e != hipSuccess) return launched(fn, e);
+    e = hs::launch_kv_units(pcnt, (int32_t*)(W + w.utab), (int32_t*)(W + w.ucount), (int32_t*)(W + w.soff),
+                            s->batch * s->hkv, nblk, hs::kv_umax(nblk, T, topk), strm);
+    if (e != hipSuccess) return launched(fn, e);
   }
   hs::BwdRowArgs r{};
   r.o[0] = o_branch;
@@ -1059,6 +1067,12 @@ hs_status hs_sparse_attn_bwd(const hs_shape* s, const void* q_sp, const void* k,
     a.plist = plist;
     a.pcnt = pcnt;
     a.poff = poff;
+    a.utab = (const int32_t*)(W + w.utab);
+    a.ucount = (const int32_t*)(W + w.ucount);
+    a.soff = (const int32_t*)(W + w.soff);
+    a.pbuf = (float*)(W + w.pbuf);
+    a.umax = hs::kv_umax(nblk, T, topk);
+    a.smax = hs::kv_smax(T, topk);
     a.dk = dk;
     a.dv = dv;
     a.accumulate = 1;

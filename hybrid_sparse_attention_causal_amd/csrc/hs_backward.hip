@@ -280,7 +280,15 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdKVArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, q4 = lane >> 4;
   const int nbg = a.B * a.Hkv;
-  const int bg = blockIdx.x % nbg, j = blockIdx.x / nbg;  // early (long) blocks first
+  const int bg = blockIdx.x % nbg;
+  int j = blockIdx.x / nbg, part = 0, nparts = 1;  // early (long) blocks first
+  if (MODE == 2) {  // work unit u of the kv group: part `part` of block j's list
+    const int u = blockIdx.x / nbg;
+    if (u >= a.ucount[bg]) return;
+    const int code = a.utab[(size_t)bg * a.umax + u];
+    j = code >> 16;
+    part = code & 0xffff;
+  }
   const int g = bg % a.Hkv, b = bg / a.Hkv;
   const int G = a.Hq / a.Hkv, Gp = a.Gp;
   const int lgGp = 31 - __clz(Gp);
@@ -290,17 +298,27 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdKVArgs a) {
 
   int npos, pbase = 64 * j;
   if (MODE == 2) {
-    npos = a.pcnt[bg * a.nblk + j];
-    pbase = a.poff[bg * a.nblk + j];
+    const int cnt = a.pcnt[bg * a.nblk + j];
+    nparts = max(1, (cnt + kUnitPos - 1) / kUnitPos);
+    npos = min(kUnitPos, cnt - part * kUnitPos);
+    pbase = a.poff[bg * a.nblk + j] + part * kUnitPos;
   } else if (MODE == 1) {
     npos = min(T - 1, 64 * j + 63 + a.W - 1) - 64 * j + 1;
   } else {
     npos = T - 64 * j;
   }
+  // a block split over several units writes each part's share to its own
+  // slot; kv_part_sum_kernel adds them up in part order
+  const bool split = MODE == 2 && nparts > 1;
+  const bool accumulate = a.accumulate && !split;
   float* dkp = a.dk + ((size_t)bg * T + key) * D + 4 * q4;
   float* dvp = a.dv + ((size_t)bg * T + key) * D + 4 * q4;
+  if (split) {
+    dkp = a.pbuf + ((size_t)bg * a.smax + a.soff[bg * a.nblk + j] + part) * 2 * 64 * D + (16 * w + r16) * D + 4 * q4;
+    dvp = dkp + 64 * D;
+  }
   if (npos <= 0) {  // nothing attends the block (sparse branch): its share is 0
-    if (!a.accumulate && key < T) {
+    if (!accumulate && key < T) {
 #pragma unroll
       for (int mc = 0; mc < NM; ++mc) {
         *(float4*)(dkp + 16 * mc) = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -480,7 +498,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdKVArgs a) {
     for (int mc = 0; mc < NM; ++mc) {
       float4 x = make_float4(a.tau * dkT[mc][0], a.tau * dkT[mc][1], a.tau * dkT[mc][2], a.tau * dkT[mc][3]);
       float4 y = make_float4(dvT[mc][0], dvT[mc][1], dvT[mc][2], dvT[mc][3]);
-      if (a.accumulate) {
+      if (accumulate) {
         const float4 x0 = *(const float4*)(dkp + 16 * mc), y0 = *(const float4*)(dvp + 16 * mc);
         x = make_float4(x.x + x0.x, x.y + x0.y, x.z + x0.z, x.w + x0.w);
         y = make_float4(y.x + y0.x, y.y + y0.y, y.z + y0.z, y.w + y0.w);
@@ -779,12 +797,101 @@ hipError_t launch_pos_lists(const int32_t* idx, uint32_t* colbits, int32_t* plis
   return hipGetLastError();
 }
 
+// Work units of the sparse branch's key side, one work group per kv group:
+// block j gets max(1, ceil(n_j / kUnitPos)) units (n_j: its list length),
+// numbered in block order; a block of several parts gets as many partial slots.
+__global__ __launch_bounds__(256) void kv_units_kernel(const int32_t* pcnt, int32_t* utab, int32_t* ucount,
+                                                       int32_t* soff, int nblk, int umax) {
+  __shared__ int wsum[2][4];
+  const int bg = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int ubase = 0, sbase = 0;
+  for (int j0 = 0; j0 < nblk; j0 += 256) {
+    const int jj = j0 + (int)threadIdx.x;
+    const int cnt = jj < nblk ? pcnt[(size_t)bg * nblk + jj] : 0;
+    const int np = jj < nblk ? max(1, (cnt + kUnitPos - 1) / kUnitPos) : 0;
+    const int ns = np > 1 ? np : 0;
+    int iu = np, is = ns;  // inclusive wave scans
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int vu = __shfl_up(iu, off), vs = __shfl_up(is, off);
+      if (lane >= off) {
+        iu += vu;
+        is += vs;
+      }
+    }
+    if (lane == 63) {
+      wsum[0][w] = iu;
+      wsum[1][w] = is;
+    }
+    __syncthreads();
+    int pu = 0, ps = 0, tu = 0, ts = 0;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      if (ww < w) {
+        pu += wsum[0][ww];
+        ps += wsum[1][ww];
+      }
+      tu += wsum[0][ww];
+      ts += wsum[1][ww];
+    }
+    __syncthreads();  // wsum is rewritten by the next round
+    if (jj < nblk) {
+      const int uo = ubase + pu + iu - np;
+      soff[(size_t)bg * nblk + jj] = sbase + ps + is - ns;
+      for (int p = 0; p < np; ++p) utab[(size_t)bg * umax + uo + p] = (jj << 16) | p;
+    }
+    ubase += tu;
+    sbase += ts;
+  }
+  if (threadIdx.x == 0) ucount[bg] = ubase;
+}
+
+// dK and dV of the blocks split over several units: the parts' shares summed
+// in part order, then added to (or written as) the gradient; kPartSlices work
+// groups per (block, kv group), each a slice of the 2 x 64 x D entries
+constexpr int kPartSlices = 16;
+template <int D>
+__global__ __launch_bounds__(256) void kv_part_sum_kernel(BwdKVArgs a) {
+  const int j = blockIdx.x, bg = blockIdx.y;
+  const int np = (a.pcnt[(size_t)bg * a.nblk + j] + kUnitPos - 1) / kUnitPos;
+  if (np <= 1) return;
+  const float* pp = a.pbuf + ((size_t)bg * a.smax + a.soff[(size_t)bg * a.nblk + j]) * 2 * 64 * D;
+  const int nk = min(64, a.T - 64 * j);
+  const int per = nk * D / 4;  // float4 pieces of one gradient
+  for (int e = blockIdx.z * 256 + threadIdx.x; e < 2 * per; e += kPartSlices * 256) {
+    const int kv = e / per, r = e % per;
+    const float* src = pp + (size_t)kv * 64 * D + 4 * r;
+    float4 x = *(const float4*)src;
+    for (int p = 1; p < np; ++p) {
+      const float4 y = *(const float4*)(src + (size_t)p * 2 * 64 * D);
+      x = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
+    }
+    float* dst = (kv ? a.dv : a.dk) + ((size_t)bg * a.T + 64 * j) * D + 4 * r;
+    if (a.accumulate) {
+      const float4 y = *(const float4*)dst;
+      x = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
+    }
+    *(float4*)dst = x;
+  }
+}
+
+hipError_t launch_kv_units(const int32_t* pcnt, int32_t* utab, int32_t* ucount, int32_t* soff, int nbg, int nblk,
+                           int umax, hipStream_t s) {
+  hipLaunchKernelGGL(kv_units_kernel, dim3((unsigned)nbg), dim3(256), 0, s, pcnt, utab, ucount, soff, nblk, umax);
+  return hipGetLastError();
+}
+
 template <int D>
 static void kv_dispatch(const BwdKVArgs& a, int mode, hipStream_t s) {
-  const dim3 grid((unsigned)((long)a.B * a.Hkv * a.nblk));
+  const long nbg = (long)a.B * a.Hkv;
+  const dim3 grid((unsigned)(nbg * a.nblk));
   if (mode == 0) hipLaunchKernelGGL((bwd_kv_kernel<D, 0>), grid, dim3(256), 0, s, a);
   else if (mode == 1) hipLaunchKernelGGL((bwd_kv_kernel<D, 1>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((bwd_kv_kernel<D, 2>), grid, dim3(256), 0, s, a);
+  else {
+    hipLaunchKernelGGL((bwd_kv_kernel<D, 2>), dim3((unsigned)(nbg * a.umax)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((kv_part_sum_kernel<D>), dim3((unsigned)a.nblk, (unsigned)nbg, kPartSlices), dim3(256), 0, s,
+                       a);
+  }
 }
 hipError_t launch_bwd_kv(const BwdKVArgs& a, int mode, int D, hipStream_t s) {
   if (D == 128) kv_dispatch<128>(a, mode, s);

@@ -217,11 +217,29 @@ struct BwdKVArgs {
   const int32_t* plist; // sparse branch: positions that selected each block, ascending
   const int32_t* pcnt;  // [B*Hkv][nblk] list lengths
   const int32_t* poff;  // [B*Hkv][nblk] list offsets within the kv group's T*topk slots
+  // sparse branch: work units of at most kUnitPos list entries.  utab
+  // [B*Hkv][umax]: unit u of a kv group is part (code & 0xffff) of block
+  // (code >> 16); ucount [B*Hkv] units per kv group; soff [B*Hkv][nblk] the
+  // first partial slot of a block of several parts; pbuf [B*Hkv][smax][2][64][D]
+  // the parts' dK (times tau) and dV, summed in part order by kv_part_sum_kernel
+  const int32_t* utab;
+  const int32_t* ucount;
+  const int32_t* soff;
+  float* pbuf;
+  int umax, smax;
   float* dk;
   float* dv;
   int B, T, Hq, Hkv, nblk, W, NC, Gp, topk, accumulate;
   float sc2, tau;
 };
+// list entries per work unit of the sparse branch's key side: a block selected
+// by more positions is split over several work groups
+constexpr int kUnitPos = 1024;
+inline int kv_umax(int nblk, int T, int topk) { return nblk + (int)((long)T * topk / kUnitPos) + 1; }
+inline int kv_smax(int T, int topk) { return (int)(2L * T * topk / kUnitPos) + 1; }
+// units of the sparse branch from the list lengths
+hipError_t launch_kv_units(const int32_t* pcnt, int32_t* utab, int32_t* ucount, int32_t* soff, int nbg, int nblk,
+                           int umax, hipStream_t s);
 struct BwdQArgs {
   const void* q;
   const void* dout;

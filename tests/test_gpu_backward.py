@@ -208,6 +208,53 @@ def test_hybrid_block_backward_accumulates():
     close("shared dv (full + 2 sparse)", host(res["dv"])[0], rv)
 
 
+def test_sparse_backward_split_lists():
+    """A block selected by more positions than one key-side work unit takes
+    (block 0 here: every position past the first block selects it, 2536 per
+    kv group, so three units) is split over several work groups whose shares
+    are summed afterwards, in a fixed order, into the existing gradient. Every
+    key's dK and dV against the oracle, with nonzero gradients already in place."""
+    T, Hq, Hkv, d, W = 2600, 8, 2, 64, 64
+    say(f"[bwd sparse, split lists] T={T} Hq={Hq} Hkv={Hkv} d={d} W={W}")
+    cfg = gen.config(1, T=T, Hq=Hq, Hkv=Hkv, d=d, dtype="bf16", kb=3, W=W, N=1)
+    inp = gen.make_prefill(cfg)
+    B, kb = 1, 3
+    idx_np = np.full((B, Hkv, T, kb), -1, np.int32)
+    for g in range(Hkv):
+        for t in range(64, T):
+            past = t // 64  # fully-past blocks 0 .. past-1
+            sel = sorted({0, past - 1, (7 * t + 3 * g) % past})
+            idx_np[0, g, t, :len(sel)] = sel
+    idx = dev(idx_np)
+    lay = inp.layers[0]
+    k, vb = dev(inp.k), dev(gen.block_major(inp.v))
+    qs, ks, vs, g = dev(lay["q"]), dev(lay["k"]), dev(gen.block_major(lay["v"])), dev(lay["gates"])
+    os_ = torch.empty((B, T, Hq, d), dtype=torch.bfloat16, device="cuda")
+    ob = torch.empty((2, B, T, Hq, d), dtype=torch.bfloat16, device="cuda")
+    lb = torch.empty((2, B, Hq, T), device="cuda")
+    hb.sparse_attn_fwd_train(qs, k, vb, idx, kb, ks, vs, W, g, os_, ob, lb)
+    do_bits = bf16_dout(cfg, 11, (B, T, Hq, d))
+    r = np.random.default_rng(3)
+    dk0 = r.standard_normal((B, Hkv, T, d)).astype(np.float32)
+    dv0 = r.standard_normal((B, Hkv, T, d)).astype(np.float32)
+    dq = torch.empty((B, T, Hq, d), device="cuda")
+    dk, dv = dev(dk0), dev(dv0)
+    dks = torch.empty((B, Hkv, T, d), device="cuda")
+    dvs = torch.empty((B, Hkv, T, d), device="cuda")
+    dg = torch.empty((B, T, Hq, 2), device="cuda")
+    hb.sparse_attn_bwd(qs, k, vb, idx, kb, ks, vs, W, g, None, ob, lb, dev(do_bits), dq, dk, dv, dks, dvs, dg)
+    torch.cuda.synchronize()
+    f = lambda n, l=None: inp.f64(n, l)[0]
+    do64 = gen.bf16_bits_to_f32(do_bits[0]).astype(np.float64)
+    ref = ora.sparse_layer_bwd(f("q", 0), f("k"), f("v"), idx_np[0].astype(np.int64), f("k", 0), f("v", 0), W,
+                               f("gates", 0), do64)
+    close("dq", host(dq)[0], ref["dq"])
+    close("dk (shared, added to what was there)", host(dk)[0] - dk0[0], ref["dk"])
+    close("dv (shared, added to what was there)", host(dv)[0] - dv0[0], ref["dv"])
+    close("dk (window)", host(dks)[0], ref["dks"])
+    close("dv (window)", host(dvs)[0], ref["dvs"])
+
+
 def test_backward_7b_shape_sampled():
     """The 7B-shaped block (T = 8192, 32/8 heads, 3 sparse layers): dQ of the
     full layer and of sparse layer 0 on sampled rows against the oracle's
