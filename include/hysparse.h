@@ -373,7 +373,8 @@ hs_status hs_full_attn_bwd(const hs_shape* shape, const void* q, const void* k, 
  *   dgate [batch][T][hq][2] fp32 (out; with gate_logits); dsinks [2][hq]
  *   fp32 (out; with sinks).
  * ws: hs_workspace_size(HS_FN_SPARSE_ATTN_BWD, shape, 64, topk, window)
- * bytes, 256-byte aligned.
+ * bytes, 256-byte aligned.  Gradients are sums taken in a fixed order (no
+ * atomics), so a call repeated on the same inputs gives the same bits.
  */
 hs_status hs_sparse_attn_bwd(const hs_shape* shape, const void* q_sp, const void* k, const void* v,
                              const int32_t* idx, int topk, const void* k_swa, const void* v_swa,
