@@ -253,6 +253,11 @@ def test_sparse_backward_split_lists():
     close("dv (shared, added to what was there)", host(dv)[0] - dv0[0], ref["dv"])
     close("dk (window)", host(dks)[0], ref["dks"])
     close("dv (window)", host(dvs)[0], ref["dvs"])
+    # a second call on the same inputs gives the same bits (sums in a fixed order)
+    dq2, dk2, dv2 = torch.empty_like(dq), dev(dk0), dev(dv0)
+    hb.sparse_attn_bwd(qs, k, vb, idx, kb, ks, vs, W, g, None, ob, lb, dev(do_bits), dq2, dk2, dv2, dks, dvs, dg)
+    torch.cuda.synchronize()
+    assert torch.equal(dk2, dk) and torch.equal(dv2, dv) and torch.equal(dq2, dq)
 
 
 def test_backward_7b_shape_sampled():
