@@ -16,6 +16,10 @@ reports it under "prefill_extra"; --decode 4 5 times one decode step of the
 64-sequence block-mode workload and of the 16 x 262144 fp8 token-level
 workload under "decode".
 
+Progress lines go to stderr, one per finished part; stdout carries only the
+JSON line.  The CPU oracle baseline runs first, in a child process of its own
+(cpu_baseline_isolated), before this process touches the GPU.
+
 Algorithmic work (counted, never the work actually issued): 4*d FLOP per
 (query head, key) pair, over the causal pairs of the full layer plus, per
 sparse layer and query, min(kb, floor(t/64))*64 selected keys and
@@ -40,6 +44,14 @@ PEAK_FP8 = 5000.0   # TFLOP/s, MI355X dense fp8 MFMA
 PEAK_F32 = 157.3    # TFLOP/s, MI355X fp32 matrix
 PEAK_HBM = 8000.0   # GB/s
 METRIC = "hybrid-block prefill tokens/s + % MFMA peak; sparse decode GB/s + % HBM peak"
+
+
+_T0 = time.perf_counter()
+
+
+def progress(msg: str) -> None:
+    """One line per finished part on stderr (stdout carries only the JSON line)."""
+    print(f"[bench {time.perf_counter() - _T0:7.1f} s] {msg}", file=sys.stderr, flush=True)
 
 
 def full_flops(cfg) -> float:
@@ -162,7 +174,7 @@ def cpu_baseline(inp, budget_s: float = 12.0):
     """Time the fp64 oracle (as it stands) on a bounded random sample of query
     rows of the same workload, on a process pool over the host cores (one BLAS
     thread per process), and scale the wall time by the algorithmic work.
-    Call it before the GPU is touched: the pool is forked."""
+    Call it in a process that has not touched the GPU: the pool is forked."""
     import multiprocessing as mp
 
     from hybrid_sparse_attention_causal_amd import inputs as gen
@@ -182,9 +194,19 @@ def cpu_baseline(inp, budget_s: float = 12.0):
     conv = lambda a: gen.to_f32(a, cfg.dtype).astype(np.float64)  # noqa: E731
     _POOL_DATA.update(inp=inp, k=conv(inp.k[0]), v=conv(inp.v[0]))
     done_w, n_rows = 0.0, 0
+    stalled = False
     with mp.get_context("fork").Pool(cores) as pool:
         t0 = time.perf_counter()
-        for i, n in enumerate(pool.imap(_oracle_rows_worker, chunks, chunksize=1)):
+        it = pool.imap(_oracle_rows_worker, chunks, chunksize=1)
+        for i in range(len(chunks)):
+            try:
+                # a worker that does not finish a few rows in this long is
+                # stuck (a forked process can inherit a held lock): the
+                # baseline then stops with what was done, not the benchmark
+                n = it.next(timeout=budget_s + 60.0)
+            except mp.TimeoutError:
+                stalled = True
+                break
             done_w += sum(row_work(int(t)) for t in chunks[i])
             n_rows += n
             if time.perf_counter() - t0 > budget_s:
@@ -192,11 +214,14 @@ def cpu_baseline(inp, budget_s: float = 12.0):
         el = time.perf_counter() - t0
         pool.terminate()
     _POOL_DATA.clear()
+    if done_w == 0.0:
+        return None
     block_s = el * total / done_w
     return {"value": cfg.B * T / block_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{n_rows} random query rows of {T} (all heads, full layer, selection and "
                       f"{nl} sparse layers) in {el:.1f} s wall on a pool of {cores} processes, "
-                      f"scaled by algorithmic FLOPs ({done_w / total * 100:.2f}% of the block)"}
+                      f"scaled by algorithmic FLOPs ({done_w / total * 100:.2f}% of the block)"
+                      + (", stopped early: a worker stalled" if stalled else "")}
 
 
 def decode_bytes(inp) -> float:
@@ -606,6 +631,31 @@ def bench_prefill(inp, steps: int, warmup: int, sinks: bool = False):
     }
 
 
+def cpu_baseline_isolated(cid: int, timeout_s: float = 180.0):
+    """cpu_baseline of workload `cid` in a child process of its own session
+    (it builds its own inputs and forks its own pool), so that a stuck pool
+    can neither hang nor outlive the benchmark: past `timeout_s` the whole
+    process group is killed and the baseline is reported as missing."""
+    import signal
+    import subprocess
+
+    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-only", str(cid)]
+    proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True,
+                            start_new_session=True)
+    try:
+        out, err = proc.communicate(timeout=timeout_s)
+    except subprocess.TimeoutExpired:
+        os.killpg(proc.pid, signal.SIGKILL)
+        proc.communicate()
+        progress(f"CPU oracle baseline: no result within {timeout_s:.0f} s, process group killed")
+        return None
+    lines = [l for l in out.splitlines() if l.startswith("{")]
+    if proc.returncode != 0 or not lines:
+        progress(f"CPU oracle baseline failed (exit {proc.returncode}): {err.strip()[-300:]}")
+        return None
+    return json.loads(lines[-1])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -628,7 +678,14 @@ def main():
                     help="give every sparse layer per-head sink logits (not part of the workloads)")
     ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
+    ap.add_argument("--cpu-baseline-only", type=int, default=0, metavar="CONFIG",
+                    help=argparse.SUPPRESS)  # the child process of cpu_baseline_isolated
     args = ap.parse_args()
+    if args.cpu_baseline_only:
+        from hybrid_sparse_attention_causal_amd import inputs as gen
+
+        print(json.dumps(cpu_baseline(gen.make_prefill(gen.config(args.cpu_baseline_only)))), flush=True)
+        return
     if args.copy_ref:
         import torch
 
@@ -648,14 +705,20 @@ def main():
 
     from hybrid_sparse_attention_causal_amd import inputs as gen
 
+    # the oracle baseline runs first, in a child process, so that the GPU
+    # work does not share the host cores with it
+    cpu = None if args.no_cpu else cpu_baseline_isolated(args.config)
+    if cpu is not None:
+        progress("CPU oracle baseline done")
+    progress(f"prefill workload {args.config}: preparing inputs")
     inp = gen.make_prefill(gen.config(args.config))
-    # the oracle baseline forks a process pool: it runs before the GPU is touched
-    cpu = None if args.no_cpu else cpu_baseline(inp)
+    progress(f"inputs of workload {args.config} ready")
 
     from hybrid_sparse_attention_causal_amd import binding as hb
 
     hb.load()
     res = bench_prefill(inp, args.steps, args.warmup, args.sinks)
+    progress(f"prefill workload {args.config}: {res['ms_per_step']:.3f} ms per block")
     del inp
     cfg = gen.config(args.config)
     out = {
@@ -681,17 +744,35 @@ def main():
     if extra:
         out["prefill_extra"] = []
         for c in extra:
+            progress(f"prefill workload {c}: preparing inputs")
             r = bench_prefill(gen.make_prefill(gen.config(c)), args.steps, args.warmup, args.sinks)
             out["prefill_extra"].append(r)
+            progress(f"prefill workload {c}: {r['ms_per_step']:.3f} ms per block")
     if args.fp8:
-        out["prefill_fp8"] = [bench_prefill(gen.make_prefill(gen.config(c, dtype="fp8")), args.steps,
-                                             args.warmup, args.sinks) for c in args.fp8]
+        out["prefill_fp8"] = []
+        for c in args.fp8:
+            progress(f"fp8 prefill workload {c}: preparing inputs")
+            out["prefill_fp8"].append(bench_prefill(gen.make_prefill(gen.config(c, dtype="fp8")), args.steps,
+                                                    args.warmup, args.sinks))
+            progress(f"fp8 prefill workload {c} done")
     if args.train:
-        out["training"] = [bench_training(c, max(3, min(args.steps, 10)), 3) for c in args.train]
+        out["training"] = []
+        for c in args.train:
+            progress(f"training step of workload {c}: preparing inputs")
+            out["training"].append(bench_training(c, max(3, min(args.steps, 10)), 3))
+            progress(f"training step of workload {c} done")
     if args.decode:
-        out["decode"] = [bench_decode(c, max(3, min(args.steps, 10)), args.sinks) for c in args.decode]
+        out["decode"] = []
+        for c in args.decode:
+            progress(f"decode workload {c}: preparing inputs")
+            out["decode"].append(bench_decode(c, max(3, min(args.steps, 10)), args.sinks))
+            progress(f"decode workload {c} done")
     if args.offload:
-        out["decode_offload"] = [bench_decode_offload(c, 3) for c in args.offload]
+        out["decode_offload"] = []
+        for c in args.offload:
+            progress(f"offloaded decode workload {c}: preparing inputs")
+            out["decode_offload"].append(bench_decode_offload(c, 3))
+            progress(f"offloaded decode workload {c} done")
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
