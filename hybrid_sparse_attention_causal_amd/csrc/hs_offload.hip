@@ -67,7 +67,11 @@ size_t offload_stage_bytes(int chunk, int Hkv, int C, int D, int es) {
 
 namespace {
 
-// events of the pipeline, created once per device and reused
+// events of the pipeline, created once per device and reused.  A stream's
+// wait on an event binds to the event's latest record at the time the wait
+// is enqueued, so calls that enqueue one after another may share them; the
+// pipeline holds g_ev_mu while it enqueues, so calls from several host
+// threads do not interleave their records and waits.
 struct PipeEvents {
   hipEvent_t entry, ready[2], free_[2];
   bool made = false;
@@ -75,12 +79,12 @@ struct PipeEvents {
 std::mutex g_ev_mu;
 PipeEvents g_ev[256];
 
+// called with g_ev_mu held
 hipError_t pipe_events(PipeEvents** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 256) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(g_ev_mu);
   PipeEvents& p = g_ev[dev];
   if (!p.made) {
     hipEvent_t* all[5] = {&p.entry, &p.ready[0], &p.ready[1], &p.free_[0], &p.free_[1]};
@@ -103,6 +107,7 @@ hipError_t pipe_events(PipeEvents** out) {
 }  // namespace
 
 hipError_t offload_pipeline(const OffloadArgs& a, int D, hipStream_t s, hipStream_t cs) {
+  std::lock_guard<std::mutex> lock(g_ev_mu);
   PipeEvents* ev = nullptr;
   HS_TRY(pipe_events(&ev));
   const int B = a.full.B, Hkv = a.full.Hkv, Hq = a.full.Hq, C = a.full.C, es = a.gather.es;

@@ -284,6 +284,9 @@ hs_status hs_gather_blocks(const hs_shape* shape, const void* k, const void* v, 
  * calls.  ws: hs_offload_workspace_size(shape, chunk) bytes, 256-byte
  * aligned.  copy_stream should be a second stream of default priority; all
  * work is complete once `stream` reaches the end of what this call enqueued.
+ * The library keeps one set of events per device for the pipeline and
+ * enqueues each call's work under a lock, so calls may come from several
+ * host threads (each with its own workspace).
  */
 size_t hs_offload_workspace_size(const hs_shape* shape, int chunk);
 hs_status hs_offload_full_select(const hs_shape* shape, const int32_t* lens_host, const void* q,

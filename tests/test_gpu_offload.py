@@ -172,3 +172,63 @@ def test_offload_config4_full_size():
     inp = gen.make_decode(gen.config(4), n_layers=2)
     run = OffloadRun(inp, 8, n_layers=2)
     run.check(oracle_seqs=[0, 63])
+
+
+def test_offload_concurrent_host_threads():
+    """Two host threads run the offload pipeline at the same time, each on its
+    own compute and copy streams with its own workspace and outputs: the
+    library enqueues each call under a lock (its events are shared per
+    device), and every result equals the device-resident step bit for bit."""
+    import threading
+
+    say("[offload, two host threads] B=7 C=4096 Hq=8 Hkv=2 kb=5 chunk=2, 4 calls each")
+    cfg = gen.config(4, B=7, T=4096, Hq=8, Hkv=2, d=128, kb=5, W=100, N=0, L_lo=1, L_hi=4096)
+    inp = gen.make_decode(cfg, n_layers=0)
+    inp.lens = np.array([1, 63, 64, 65, 130, 4000, 4096], np.int32)
+    B, Hq, Hkv, C, d, kb = cfg.B, cfg.Hq, cfg.Hkv, cfg.T, cfg.d, cfg.kb
+    kt, vt = _pinned_caches(inp)
+    k, v = kt.cuda(), vt.cuda()
+    lens_h = torch.from_numpy(inp.lens.astype(np.int32))
+    lens = lens_h.cuda()
+    q = dev(inp.q)
+
+    def outs():
+        return (torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda"),
+                torch.full((B, Hq), float("nan"), device="cuda"),
+                torch.full((B, Hq, C // 64), float("nan"), device="cuda"),
+                torch.full((B, Hkv, kb), -7, dtype=torch.int32, device="cuda"))
+
+    want = outs()
+    hb.decode_full_attn_scores(q, k, v, lens, *want[:3])
+    hb.decode_block_topk(q, k, lens, want[2], want[1], kb, want[3])
+    torch.cuda.synchronize()
+    results, errors = {}, []
+
+    def worker(i):
+        try:
+            torch.cuda.set_device(0)
+            s, cs = torch.cuda.Stream(), torch.cuda.Stream()
+            got = outs()
+            k_sel = torch.empty((B, Hkv, kb * 64, d), dtype=torch.bfloat16, device="cuda")
+            v_sel = torch.empty((B, Hkv, kb, d, 64), dtype=torch.bfloat16, device="cuda")
+            idx_sel = torch.empty((B, Hkv, kb), dtype=torch.int32, device="cuda")
+            ws = torch.empty(hb.offload_workspace_size(q, kt, lens, 2), dtype=torch.uint8, device="cuda")
+            torch.cuda.synchronize()
+            for _ in range(4):
+                hb.offload_full_select(q, kt, vt, lens, lens_h, *got[:3], kb, got[3], k_sel, v_sel, idx_sel, 2, ws,
+                                       stream=s, copy_stream=cs)
+            s.synchronize()
+            results[i] = got
+        except Exception as e:  # reported by the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    assert sorted(results) == [0, 1]
+    for i in range(2):
+        for name, x, y in zip(("o", "lse", "raw", "idx"), want, results[i]):
+            assert torch.equal(torch.nan_to_num(x.float(), 7.0), torch.nan_to_num(y.float(), 7.0)), (i, name)
